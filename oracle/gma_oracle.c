@@ -1,0 +1,218 @@
+/*
+ * Plain fp64 CPU oracle for the Gaussian Mixture Attention (GMA) forward mixer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or load
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * use it.  It shares no code, header, table or constant with the HIP kernels.
+ *
+ * Source: "Gaussian Mixture Attention: Linear-Time Sequence Mixing via
+ * Probabilistic Latent Routing" (Huang, Raza; arXiv 2606.18283), as summarised on
+ * gist.science (ja/de pages, section "Core mechanism") and in the arXiv abstract.
+ *
+ * What is computed, per batch element b and head h (parameters are per head):
+ *   var_kd   = softplus(var_raw_kd) + var_floor            (Core mechanism 3:
+ *                                                          softplus keeps variances valid)
+ *   log pi_k = p_k - logsumexp_j p_j                       (Core mechanism 3: softmax priors)
+ *   l_k(x)   = log pi_k + log N(x; mu_k, diag var_k)       (Core mechanism 1: standard
+ *                                                          GMM posterior p(z=k|x))
+ *   gamma_k  = exp(l_k - max l) / sum_j exp(l_j - max l)
+ *   Bidirectional (Core mechanism 2, write/read equations):
+ *     Vt = Gamma_K^T V,  Z = Gamma_K^T 1,  O = Gamma_Q Vt / (Gamma_Q Z + eps)
+ *   Causal (Core mechanism 3): prefix sums of the memory and the normaliser, so that
+ *     O_i uses only positions j <= i (inclusive of i).
+ *
+ * Readings of points the pages leave open: the log-density keeps every constant
+ * (log 2 pi and the prior's log-sum-exp); eps is added once per output row after
+ * the product Gamma_Q Z; softplus is the exact log1p(exp(r)) with no linear
+ * threshold; the same K Gaussians serve queries and keys of one head.
+ *
+ * Everything is double precision, sums run in ascending index order, and the loops
+ * follow the definitions directly: no blocking, fusion or reordering.  OpenMP only
+ * spreads independent (b, h) slices and independent rows over threads.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG (-1)
+#define ORACLE_NO_MEM (-2)
+
+static const double LOG_2PI = 1.8378770664093454835606594728112; /* log(2*pi) */
+
+/* softplus(r) = log(1 + e^r), written in the overflow-free form max(r,0)+log1p(e^-|r|). */
+static double softplus(double r) { return fmax(r, 0.0) + log1p(exp(-fabs(r))); }
+
+int gma_oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Log joint l_k(x_i) = log pi_k + log N(x_i; mu_k, diag(var_k)) for the N rows of x.
+ *   x            [N, d]   routing vectors of one head
+ *   mu, var_raw  [K, d]   parameters of that head
+ *   prior_logits [K]
+ *   out          [N, K]
+ */
+int gma_oracle_log_joint(const double* x, int N, int d, const double* mu,
+                         const double* var_raw, const double* prior_logits, int K,
+                         double var_floor, double* out) {
+    if (!x || !mu || !var_raw || !prior_logits || !out || N < 0 || d < 1 || K < 1)
+        return ORACLE_BAD_ARG;
+    double* var = (double*)malloc(sizeof(double) * (size_t)K * d);
+    double* logpi = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!var || !logpi) { free(var); free(logpi); return ORACLE_NO_MEM; }
+
+    for (int k = 0; k < K; ++k)
+        for (int j = 0; j < d; ++j)
+            var[(size_t)k * d + j] = softplus(var_raw[(size_t)k * d + j]) + var_floor;
+
+    /* log softmax of the prior logits */
+    double pmax = prior_logits[0];
+    for (int k = 1; k < K; ++k) pmax = fmax(pmax, prior_logits[k]);
+    double psum = 0.0;
+    for (int k = 0; k < K; ++k) psum += exp(prior_logits[k] - pmax);
+    double lse = pmax + log(psum);
+    for (int k = 0; k < K; ++k) logpi[k] = prior_logits[k] - lse;
+
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < N; ++i) {
+        const double* xi = x + (size_t)i * d;
+        for (int k = 0; k < K; ++k) {
+            const double* mk = mu + (size_t)k * d;
+            const double* vk = var + (size_t)k * d;
+            double quad = 0.0;
+            for (int j = 0; j < d; ++j) {
+                double diff = xi[j] - mk[j];
+                quad += LOG_2PI + log(vk[j]) + diff * diff / vk[j];
+            }
+            out[(size_t)i * K + k] = logpi[k] - 0.5 * quad;
+        }
+    }
+    free(var);
+    free(logpi);
+    return ORACLE_OK;
+}
+
+/* Posterior responsibilities gamma [N, K] = row-wise softmax of the log joint. */
+int gma_oracle_responsibilities(const double* x, int N, int d, const double* mu,
+                                const double* var_raw, const double* prior_logits, int K,
+                                double var_floor, double* gamma) {
+    int st = gma_oracle_log_joint(x, N, d, mu, var_raw, prior_logits, K, var_floor, gamma);
+    if (st != ORACLE_OK) return st;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < N; ++i) {
+        double* row = gamma + (size_t)i * K;
+        double m = row[0];
+        for (int k = 1; k < K; ++k) m = fmax(m, row[k]);
+        double s = 0.0;
+        for (int k = 0; k < K; ++k) { row[k] = exp(row[k] - m); s += row[k]; }
+        for (int k = 0; k < K; ++k) row[k] /= s;
+    }
+    return ORACLE_OK;
+}
+
+/* Bidirectional write then read for one head: gq, gk [N, K], v [N, dv] -> o [N, dv]. */
+static int mix_bidirectional(const double* gq, const double* gk, const double* v, int N, int K,
+                             int dv, double eps, double* o) {
+    double* vt = (double*)calloc((size_t)K * dv, sizeof(double)); /* Gamma_K^T V */
+    double* z = (double*)calloc((size_t)K, sizeof(double));       /* Gamma_K^T 1 */
+    if (!vt || !z) { free(vt); free(z); return ORACLE_NO_MEM; }
+    for (int j = 0; j < N; ++j)
+        for (int k = 0; k < K; ++k) {
+            double g = gk[(size_t)j * K + k];
+            z[k] += g;
+            for (int c = 0; c < dv; ++c) vt[(size_t)k * dv + c] += g * v[(size_t)j * dv + c];
+        }
+    for (int i = 0; i < N; ++i) {
+        double den = 0.0;
+        for (int k = 0; k < K; ++k) den += gq[(size_t)i * K + k] * z[k];
+        for (int c = 0; c < dv; ++c) {
+            double num = 0.0;
+            for (int k = 0; k < K; ++k) num += gq[(size_t)i * K + k] * vt[(size_t)k * dv + c];
+            o[(size_t)i * dv + c] = num / (den + eps);
+        }
+    }
+    free(vt);
+    free(z);
+    return ORACLE_OK;
+}
+
+/* Causal variant for one head: inclusive prefix sums S_i = sum_{j<=i} gk_j v_j^T,
+ * z_i = sum_{j<=i} gk_j, and O_i = gq_i S_i / (gq_i . z_i + eps). */
+static int mix_causal(const double* gq, const double* gk, const double* v, int N, int K, int dv,
+                      double eps, double* o) {
+    double* s = (double*)calloc((size_t)K * dv, sizeof(double));
+    double* z = (double*)calloc((size_t)K, sizeof(double));
+    if (!s || !z) { free(s); free(z); return ORACLE_NO_MEM; }
+    for (int i = 0; i < N; ++i) {
+        for (int k = 0; k < K; ++k) {
+            double g = gk[(size_t)i * K + k];
+            z[k] += g;
+            for (int c = 0; c < dv; ++c) s[(size_t)k * dv + c] += g * v[(size_t)i * dv + c];
+        }
+        double den = 0.0;
+        for (int k = 0; k < K; ++k) den += gq[(size_t)i * K + k] * z[k];
+        for (int c = 0; c < dv; ++c) {
+            double num = 0.0;
+            for (int k = 0; k < K; ++k) num += gq[(size_t)i * K + k] * s[(size_t)k * dv + c];
+            o[(size_t)i * dv + c] = num / (den + eps);
+        }
+    }
+    free(s);
+    free(z);
+    return ORACLE_OK;
+}
+
+/*
+ * Full forward.  All arrays are contiguous double:
+ *   qr, kr [B,H,N,d_r]; v, out [B,H,N,d_v]; mu, var_raw [H,K,d_r]; prior_logits [H,K];
+ *   gamma_q, gamma_k (each nullable) [B,H,N,K].
+ * Slices (b, h) are independent and run in parallel; inside a slice everything is
+ * sequential in index order.
+ */
+int gma_oracle_forward(const double* qr, const double* kr, const double* v, const double* mu,
+                       const double* var_raw, const double* prior_logits, int B, int H, int N,
+                       int d_r, int d_v, int K, int causal, double eps, double var_floor,
+                       double* out, double* gamma_q, double* gamma_k) {
+    if (!qr || !kr || !v || !mu || !var_raw || !prior_logits || !out) return ORACLE_BAD_ARG;
+    if (B < 1 || H < 1 || N < 0 || d_r < 1 || d_v < 1 || K < 1) return ORACLE_BAD_ARG;
+    if (causal != 0 && causal != 1) return ORACLE_BAD_ARG;
+    const size_t nk = (size_t)N * K;
+    int status = ORACLE_OK;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int h = bh % H;
+        const size_t xoff = (size_t)bh * N * d_r;
+        const size_t voff = (size_t)bh * N * d_v;
+        double* gq = gamma_q ? gamma_q + (size_t)bh * nk : (double*)malloc(sizeof(double) * (nk ? nk : 1));
+        double* gk = gamma_k ? gamma_k + (size_t)bh * nk : (double*)malloc(sizeof(double) * (nk ? nk : 1));
+        int st = (gq && gk) ? ORACLE_OK : ORACLE_NO_MEM;
+        const double* mu_h = mu + (size_t)h * K * d_r;
+        const double* vr_h = var_raw + (size_t)h * K * d_r;
+        const double* p_h = prior_logits + (size_t)h * K;
+        if (st == ORACLE_OK)
+            st = gma_oracle_responsibilities(qr + xoff, N, d_r, mu_h, vr_h, p_h, K, var_floor, gq);
+        if (st == ORACLE_OK)
+            st = gma_oracle_responsibilities(kr + xoff, N, d_r, mu_h, vr_h, p_h, K, var_floor, gk);
+        if (st == ORACLE_OK)
+            st = causal ? mix_causal(gq, gk, v + voff, N, K, d_v, eps, out + voff)
+                        : mix_bidirectional(gq, gk, v + voff, N, K, d_v, eps, out + voff);
+        if (!gamma_q) free(gq);
+        if (!gamma_k) free(gk);
+        if (st != ORACLE_OK) {
+#pragma omp critical
+            status = st;
+        }
+    }
+    return status;
+}

@@ -1,0 +1,130 @@
+"""ctypes front end of the plain-C fp64 oracle (``gma_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the benchmark's
+CPU-baseline leg, never by the product path.
+
+Inputs may be numpy arrays or CPU torch tensors of any float dtype; they are
+up-cast exactly to float64 (bf16 and fp32 values are exactly representable) and
+made contiguous before the call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gma_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def build(force: bool = True) -> str:
+    """Compile ``gma_oracle.c`` with gcc (-O2, OpenMP, strict IEEE: no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               "-Wextra", "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        d = ctypes.c_double
+        lib.gma_oracle_log_joint.argtypes = [dp, i, i, dp, dp, dp, i, d, dp]
+        lib.gma_oracle_log_joint.restype = i
+        lib.gma_oracle_responsibilities.argtypes = [dp, i, i, dp, dp, dp, i, d, dp]
+        lib.gma_oracle_responsibilities.restype = i
+        lib.gma_oracle_forward.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, i, d, d,
+                                           dp, dp, dp]
+        lib.gma_oracle_forward.restype = i
+        lib.gma_oracle_num_threads.argtypes = []
+        lib.gma_oracle_num_threads.restype = i
+        _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor (CPU)
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    return int(_load().gma_oracle_num_threads())
+
+
+def log_joint(x, mu, var_raw, prior_logits, var_floor: float) -> np.ndarray:
+    """log pi_k + log N(x_i; mu_k, diag var_k) for rows x [N, d] of one head -> [N, K]."""
+    x, mu, vr, p = _f64(x), _f64(mu), _f64(var_raw), _f64(prior_logits)
+    N, d = x.shape
+    K = mu.shape[0]
+    out = np.empty((N, K), dtype=np.float64)
+    st = _load().gma_oracle_log_joint(_ptr(x), N, d, _ptr(mu), _ptr(vr), _ptr(p), K,
+                                      float(var_floor), _ptr(out))
+    if st != 0:
+        raise RuntimeError(f"gma_oracle_log_joint failed: {st}")
+    return out
+
+
+def responsibilities(x, mu, var_raw, prior_logits, var_floor: float) -> np.ndarray:
+    """GMM posterior p(z=k | x_i) for rows x [N, d] of one head -> [N, K]."""
+    x, mu, vr, p = _f64(x), _f64(mu), _f64(var_raw), _f64(prior_logits)
+    N, d = x.shape
+    K = mu.shape[0]
+    out = np.empty((N, K), dtype=np.float64)
+    st = _load().gma_oracle_responsibilities(_ptr(x), N, d, _ptr(mu), _ptr(vr), _ptr(p), K,
+                                             float(var_floor), _ptr(out))
+    if st != 0:
+        raise RuntimeError(f"gma_oracle_responsibilities failed: {st}")
+    return out
+
+
+def forward(qr, kr, v, mu, var_raw, prior_logits, causal: bool, eps: float,
+            var_floor: float, return_gamma: bool = False
+            ) -> np.ndarray | Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """fp64 GMA forward.  qr, kr [B,H,N,d_r]; v [B,H,N,d_v]; mu, var_raw [H,K,d_r];
+    prior_logits [H,K].  Returns out [B,H,N,d_v] (and Gamma_Q, Gamma_K [B,H,N,K])."""
+    qr, kr, v = _f64(qr), _f64(kr), _f64(v)
+    mu, vr, p = _f64(mu), _f64(var_raw), _f64(prior_logits)
+    B, H, N, d_r = qr.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    if kr.shape != qr.shape or v.shape[:3] != qr.shape[:3]:
+        raise ValueError("shape mismatch")
+    if mu.shape != (H, K, d_r) or vr.shape != (H, K, d_r) or p.shape != (H, K):
+        raise ValueError("parameter shape mismatch")
+    out = np.empty((B, H, N, d_v), dtype=np.float64)
+    gq = np.empty((B, H, N, K), dtype=np.float64) if return_gamma else None
+    gk = np.empty((B, H, N, K), dtype=np.float64) if return_gamma else None
+    st = _load().gma_oracle_forward(_ptr(qr), _ptr(kr), _ptr(v), _ptr(mu), _ptr(vr), _ptr(p),
+                                    B, H, N, d_r, d_v, K, 1 if causal else 0, float(eps),
+                                    float(var_floor), _ptr(out), _ptr(gq), _ptr(gk))
+    if st != 0:
+        raise RuntimeError(f"gma_oracle_forward failed: {st}")
+    if return_gamma:
+        return out, gq, gk
+    return out

@@ -1,0 +1,309 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Source: "Gaussian Mixture Attention" (arXiv 2606.18283), gist.science summaries,
+section "Core mechanism": responsibilities are standard GMM posteriors with
+diagonal covariances (item 1); the write/read equations and the associativity
+argument (item 2); softplus variances, softmax priors and the causal prefix-sum
+variant (item 3).  Section "Contributions", theoretical analysis: the induced
+affinity is non-negative with rank <= K.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped constant,
+a sign, a swapped operand, an off-by-one in the causal boundary, softplus on the
+wrong quantity) fails at least one of them:
+  * log joint vs scipy's multivariate normal log-pdf  (constants, signs, softplus)
+  * posteriors vs scikit-learn's diagonal GaussianMixture.predict_proba
+  * 1-D two-component posterior vs the textbook logistic / quadratic discriminant
+  * mixing vs an independent N x N brute force (associativity, causal mask)
+  * closed forms: K = 1 mean / prefix mean, identical components
+  * invariants: rows on the simplex, rank(A) <= K, semiseparable causal rank,
+    bound by max|v|, linearity in V, prior shift invariance, permutation
+    equivariance, exact causality.
+"""
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+import oracle
+from tests import metrics
+
+
+def _params(rng, K, d, mu_std=1.0, vr_std=0.5, p_std=1.0):
+    mu = rng.normal(0.0, mu_std, size=(K, d))
+    vr = rng.normal(0.0, vr_std, size=(K, d))
+    p = rng.normal(0.0, p_std, size=(K,))
+    return mu, vr, p
+
+
+def _var(vr, floor):
+    # softplus through numpy's logaddexp(0, r) = log(1 + e^r): a route independent of the oracle
+    return np.logaddexp(0.0, vr) + floor
+
+
+# ---------------------------------------------------------------- responsibilities
+
+@pytest.mark.parametrize("K,d,floor", [(1, 1, 1e-3), (7, 5, 1e-3), (16, 16, 1e-2), (3, 64, 1e-3)])
+def test_log_joint_matches_scipy_logpdf(K, d, floor):
+    rng = np.random.default_rng(11 + K + d)
+    mu, vr, p = _params(rng, K, d)
+    x = rng.normal(size=(40, d))
+    got = oracle.log_joint(x, mu, vr, p, floor)
+    var = _var(vr, floor)
+    logpi = scipy.special.log_softmax(p)
+    for k in range(K):
+        ref = scipy.stats.multivariate_normal(mean=mu[k], cov=np.diag(var[k])).logpdf(x)
+        ref = np.atleast_1d(ref) + logpi[k]
+        np.testing.assert_allclose(got[:, k], ref, rtol=1e-10, atol=1e-10)
+
+
+def test_softplus_extremes_are_stable():
+    # var_raw far in both tails: softplus(r) -> r for r >> 0 and -> e^r for r << 0
+    K, d, floor = 4, 3, 1e-3
+    mu = np.zeros((K, d))
+    vr = np.array([[40.0, -40.0, 0.0], [700.0, -700.0, 1.0], [5.0, -5.0, 2.0], [20.0, -20.0, -1.0]])
+    p = np.zeros(K)
+    x = np.full((1, d), 0.5)
+    got = oracle.log_joint(x, mu, vr, p, floor)
+    var = _var(vr, floor)
+    assert np.all(np.isfinite(got))
+    for k in range(K):
+        ref = scipy.stats.multivariate_normal(mean=mu[k], cov=np.diag(var[k])).logpdf(x)
+        np.testing.assert_allclose(got[0, k], ref + np.log(1.0 / K), rtol=1e-12)
+
+
+@pytest.mark.parametrize("K,d,floor,seed", [(2, 1, 1e-3, 0), (8, 16, 1e-3, 1), (32, 8, 1e-2, 2),
+                                            (128, 64, 1e-3, 3)])
+def test_responsibilities_match_sklearn(K, d, floor, seed):
+    from sklearn.mixture import GaussianMixture
+
+    rng = np.random.default_rng(seed)
+    mu, vr, p = _params(rng, K, d)
+    x = rng.normal(size=(200, d))
+    var = _var(vr, floor)
+    gm = GaussianMixture(n_components=K, covariance_type="diag")
+    gm.weights_ = scipy.special.softmax(p)
+    gm.means_ = mu
+    gm.covariances_ = var
+    gm.precisions_cholesky_ = 1.0 / np.sqrt(var)
+    ref = gm.predict_proba(x)
+    got = oracle.responsibilities(x, mu, vr, p, floor)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_two_component_equal_variance_is_logistic():
+    # 1-D, K=2, shared variance s2: p(z=1|x) = sigmoid(w x + b) with
+    # w = (m1 - m2)/s2, b = (m2^2 - m1^2)/(2 s2) + log(pi1/pi2)   (linear discriminant)
+    m1, m2, r, floor = 0.7, -1.3, 0.2, 1e-3
+    s2 = np.logaddexp(0.0, r) + floor
+    p = np.array([0.4, -0.9])
+    x = np.linspace(-4, 4, 33)[:, None]
+    g = oracle.responsibilities(x, np.array([[m1], [m2]]), np.array([[r], [r]]), p, floor)
+    logratio = np.log(scipy.special.softmax(p)[0] / scipy.special.softmax(p)[1])
+    w = (m1 - m2) / s2
+    b = (m2 ** 2 - m1 ** 2) / (2 * s2) + logratio
+    np.testing.assert_allclose(g[:, 0], scipy.special.expit(w * x[:, 0] + b), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(g.sum(1), 1.0, atol=1e-15)
+
+
+def test_two_component_unequal_variance_is_quadratic_discriminant():
+    # 1-D, K=2: log-odds = log(pi1/pi2) - 0.5 log(s1/s2) - (x-m1)^2/(2 s1) + (x-m2)^2/(2 s2)
+    m1, m2, r1, r2, floor = -0.2, 1.1, -0.8, 1.3, 1e-2
+    s1 = np.logaddexp(0.0, r1) + floor
+    s2 = np.logaddexp(0.0, r2) + floor
+    p = np.array([1.2, 0.3])
+    x = np.linspace(-3, 3, 25)[:, None]
+    g = oracle.responsibilities(x, np.array([[m1], [m2]]), np.array([[r1], [r2]]), p, floor)
+    lo = (p[0] - p[1]) - 0.5 * np.log(s1 / s2) - (x[:, 0] - m1) ** 2 / (2 * s1) \
+        + (x[:, 0] - m2) ** 2 / (2 * s2)
+    np.testing.assert_allclose(g[:, 0], scipy.special.expit(lo), rtol=0, atol=1e-14)
+
+
+def test_identical_components_give_prior():
+    rng = np.random.default_rng(5)
+    K, d = 6, 4
+    mu = np.tile(rng.normal(size=(1, d)), (K, 1))
+    vr = np.tile(rng.normal(size=(1, d)), (K, 1))
+    p = rng.normal(size=K)
+    x = rng.normal(size=(17, d))
+    g = oracle.responsibilities(x, mu, vr, p, 1e-3)
+    np.testing.assert_allclose(g, np.tile(scipy.special.softmax(p), (17, 1)), atol=1e-15)
+
+
+def test_prior_logit_shift_invariance():
+    rng = np.random.default_rng(6)
+    mu, vr, p = _params(rng, 9, 5)
+    x = rng.normal(size=(30, 5))
+    g1 = oracle.responsibilities(x, mu, vr, p, 1e-3)
+    g2 = oracle.responsibilities(x, mu, vr, p + 3.75, 1e-3)
+    np.testing.assert_allclose(g1, g2, atol=1e-14)
+
+
+# ---------------------------------------------------------------- mixing
+
+def _brute(gq, gk, v, eps, causal):
+    """Independent N x N brute force: materialise A = Gamma_Q Gamma_K^T (lower-triangular
+    incl. the diagonal when causal) and row-normalise A [V, 1]."""
+    A = gq @ gk.T
+    if causal:
+        A = np.tril(A)
+    return (A @ v) / (A.sum(axis=1, keepdims=True) + eps)
+
+
+def _random_problem(rng, B, H, N, dr, dv, K, mu_std=1.0, x_std=1.0):
+    qr = rng.normal(0, x_std, size=(B, H, N, dr))
+    kr = rng.normal(0, x_std, size=(B, H, N, dr))
+    v = rng.normal(size=(B, H, N, dv))
+    mu = rng.normal(0, mu_std, size=(H, K, dr))
+    vr = rng.normal(0, 0.5, size=(H, K, dr))
+    p = rng.normal(size=(H, K))
+    return qr, kr, v, mu, vr, p
+
+
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(N=st.integers(1, 96), K=st.integers(1, 24), dr=st.integers(1, 12), dv=st.integers(1, 12),
+       causal=st.booleans(), seed=st.integers(0, 2 ** 31 - 1),
+       eps=st.sampled_from([1e-6, 1e-3, 0.5]))
+def test_forward_matches_bruteforce(N, K, dr, dv, causal, seed, eps):
+    rng = np.random.default_rng(seed)
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 2, N, dr, dv, K)
+    out, gq, gk = oracle.forward(qr, kr, v, mu, vr, p, causal, eps, 1e-3, return_gamma=True)
+    for h in range(2):
+        ref = _brute(gq[0, h], gk[0, h], v[0, h], eps, causal)
+        assert metrics.rowrel(out[0, h][None, None], ref[None, None]) < 1e-12
+
+
+def test_forward_gamma_matches_sklearn_path():
+    # the Gamma returned by the full forward is the same posterior sklearn computes
+    from sklearn.mixture import GaussianMixture
+
+    rng = np.random.default_rng(9)
+    qr, kr, v, mu, vr, p = _random_problem(rng, 2, 3, 50, 6, 5, 10)
+    _, gq, gk = oracle.forward(qr, kr, v, mu, vr, p, False, 1e-6, 1e-3, return_gamma=True)
+    for h in range(3):
+        var = _var(vr[h], 1e-3)
+        gm = GaussianMixture(n_components=10, covariance_type="diag")
+        gm.weights_, gm.means_, gm.covariances_ = scipy.special.softmax(p[h]), mu[h], var
+        gm.precisions_cholesky_ = 1.0 / np.sqrt(var)
+        for b in range(2):
+            np.testing.assert_allclose(gq[b, h], gm.predict_proba(qr[b, h]), atol=1e-12)
+            np.testing.assert_allclose(gk[b, h], gm.predict_proba(kr[b, h]), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_component_is_mean_or_prefix_mean(causal):
+    rng = np.random.default_rng(3)
+    N, eps = 37, 1e-3
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 1, N, 4, 6, 1)
+    out = oracle.forward(qr, kr, v, mu, vr, p, causal, eps, 1e-3)[0, 0]
+    vv = v[0, 0]
+    if causal:
+        ref = np.cumsum(vv, axis=0) / (np.arange(1, N + 1)[:, None] + eps)
+    else:
+        ref = np.tile(vv.sum(0) / (N + eps), (N, 1))
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_components_closed_form(causal):
+    # gamma = pi for every token: A_ij = |pi|^2, so O_i = sum v / (n_i + eps/|pi|^2)
+    rng = np.random.default_rng(4)
+    N, K, d, eps = 23, 5, 3, 0.01
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 1, N, d, 4, K)
+    mu[0] = mu[0, :1]
+    vr[0] = vr[0, :1]
+    out = oracle.forward(qr, kr, v, mu, vr, p, causal, eps, 1e-3)[0, 0]
+    pi2 = float((scipy.special.softmax(p[0]) ** 2).sum())
+    vv = v[0, 0]
+    if causal:
+        ref = np.cumsum(vv, axis=0) / (np.arange(1, N + 1)[:, None] + eps / pi2)
+    else:
+        ref = np.tile(vv.sum(0) / (N + eps / pi2), (N, 1))
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_affinity_rank_at_most_K_and_semiseparable():
+    rng = np.random.default_rng(8)
+    N, K = 120, 7
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 1, N, 5, 3, K)
+    _, gq, gk = oracle.forward(qr, kr, v, mu, vr, p, True, 1e-6, 1e-3, return_gamma=True)
+    A = gq[0, 0] @ gk[0, 0].T
+    s = np.linalg.svd(A, compute_uv=False)
+    assert s[K] <= 1e-10 * s[0]
+    assert np.all(A >= 0)
+    # any block strictly below the diagonal of tril(A) is a block of A: rank <= K
+    L = np.tril(A)
+    for split in (20, 60, 100):
+        blk = L[split:, :split]
+        sb = np.linalg.svd(blk, compute_uv=False)
+        assert len(sb) <= K or sb[K] <= 1e-10 * sb[0]
+
+
+def test_responsibility_rows_on_simplex():
+    rng = np.random.default_rng(12)
+    qr, kr, v, mu, vr, p = _random_problem(rng, 2, 2, 64, 8, 4, 33, mu_std=2.0)
+    _, gq, gk = oracle.forward(qr, kr, v, mu, vr, p, False, 1e-6, 1e-3, return_gamma=True)
+    for g in (gq, gk):
+        assert np.all(g >= 0)
+        np.testing.assert_allclose(g.sum(-1), 1.0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_output_bounded_linear_and_equivariant(causal):
+    rng = np.random.default_rng(13)
+    N = 48
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 1, N, 6, 5, 9)
+    o1 = oracle.forward(qr, kr, v, mu, vr, p, causal, 1e-6, 1e-3)
+    # convex combination scaled by A1/(A1+eps) < 1
+    assert np.all(np.abs(o1) <= np.abs(v).max(axis=2, keepdims=True) + 1e-12)
+    # linear in V
+    v2 = rng.normal(size=v.shape)
+    o2 = oracle.forward(qr, kr, v2, mu, vr, p, causal, 1e-6, 1e-3)
+    o12 = oracle.forward(qr, kr, 2.0 * v - 3.0 * v2, mu, vr, p, causal, 1e-6, 1e-3)
+    np.testing.assert_allclose(o12, 2.0 * o1 - 3.0 * o2, atol=1e-12)
+    if not causal:
+        # permuting keys with their values changes nothing; permuting queries permutes rows
+        perm = rng.permutation(N)
+        o3 = oracle.forward(qr[:, :, perm], kr[:, :, perm], v[:, :, perm], mu, vr, p, False,
+                            1e-6, 1e-3)
+        np.testing.assert_allclose(o3, o1[:, :, perm], atol=1e-13)
+
+
+def test_causal_outputs_ignore_the_future_exactly():
+    rng = np.random.default_rng(14)
+    N, cut = 40, 17
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 2, N, 4, 3, 6)
+    o1 = oracle.forward(qr, kr, v, mu, vr, p, True, 1e-6, 1e-3)
+    qr2, kr2, v2 = qr.copy(), kr.copy(), v.copy()
+    qr2[:, :, cut + 1:] = rng.normal(size=qr2[:, :, cut + 1:].shape)
+    kr2[:, :, cut + 1:] = rng.normal(size=kr2[:, :, cut + 1:].shape)
+    v2[:, :, cut + 1:] = 100 * rng.normal(size=v2[:, :, cut + 1:].shape)
+    o2 = oracle.forward(qr2, kr2, v2, mu, vr, p, True, 1e-6, 1e-3)
+    assert np.array_equal(o1[:, :, :cut + 1], o2[:, :, :cut + 1])
+    assert not np.allclose(o1[:, :, cut + 1:], o2[:, :, cut + 1:])
+    # and the last position of the causal variant equals the bidirectional row
+    ob = oracle.forward(qr, kr, v, mu, vr, p, False, 1e-6, 1e-3)
+    np.testing.assert_allclose(o1[:, :, -1], ob[:, :, -1], atol=1e-13)
+
+
+def test_empty_sequence():
+    rng = np.random.default_rng(15)
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 1, 0, 4, 3, 5)
+    for causal in (False, True):
+        out = oracle.forward(qr, kr, v, mu, vr, p, causal, 1e-6, 1e-3)
+        assert out.shape == (1, 1, 0, 3)
+
+
+def test_golden_fixture_regression():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_gma.json")
+    fx = json.load(open(path))
+    inp = {k: np.asarray(v) for k, v in fx["inputs"].items()}
+    for key, causal in (("bidirectional", False), ("causal", True)):
+        out, gq, gk = oracle.forward(inp["qr"], inp["kr"], inp["v"], inp["mu"], inp["var_raw"],
+                                     inp["prior_logits"], causal, fx["eps"], fx["var_floor"],
+                                     return_gamma=True)
+        np.testing.assert_allclose(out, np.asarray(fx[key]["out"]), rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(gq, np.asarray(fx[key]["gamma_q"]), rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(gk, np.asarray(fx[key]["gamma_k"]), rtol=1e-14, atol=1e-15)
