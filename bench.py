@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the GMA forward mixer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+
+A step is one full forward (parameter prep, responsibilities, write and read -- or the
+causal scan) over one batch of seeded synthetic inputs already resident in HBM.  W
+untimed warm-up steps, then exactly K timed steps bracketed by torch.cuda.synchronize()
+on both sides.  Each timed step runs through gma_forward_timed, which records a HIP
+event pair on the launch stream around every kernel, so per-kernel durations come from
+the same timed region.  Prints one JSON line.
+
+value = whole-job throughput in token-heads/s (B*H*N / seconds per step).  The
+default workload is the bidirectional bf16 K=128 workload (B=8, H=8, N=4096,
+d_r=d_v=64); the causal LM-shaped workload (B=16, H=8, N=2048, K=256) is measured the
+same way and reported under "causal".
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+
+def metric_name() -> str:
+    try:
+        return json.load(open(os.path.join(ROOT, "BASELINE.json")))["metric"]
+    except Exception:
+        return "GMA forward tokens/s per head-layer"
+
+
+def algorithmic(w, kernel: str):
+    """Algorithmic bytes and flops of one launch of `kernel` on workload `w`.
+
+    Per token-head the whole forward must read q, k, v once and write out once:
+    s_in*(2 d_r + d_v) + s_out*d_v bytes; it must do 4K(2d_r+1) flops for the Q and K
+    log-density contractions and 4K(d_v+1) for the write and read of [Vt | Z].  A kernel
+    that does one side of that work is charged that side only.
+    """
+    s = 4 if w.dtype == "f32" else 2
+    th = w.B * w.H * w.N
+    K, dr, dv = w.K, w.d_r, w.d_v
+    side_flops = 2 * K * (2 * dr + 1) + 2 * K * (dv + 1)
+    if "write" in kernel:      # reads k and v, forms Gamma_K and Gamma_K^T [V, 1]
+        return th * s * (dr + dv), th * side_flops
+    if "read" in kernel:       # reads q, forms Gamma_Q, Gamma_Q [Vt, Z], writes out
+        return th * s * (dr + dv), th * side_flops
+    if "resp" in kernel:       # responsibilities of both sides
+        return th * s * 2 * dr, th * 4 * K * (2 * dr + 1)
+    # whole forward (a fused or scan kernel)
+    return th * s * (2 * dr + 2 * dv), th * 2 * side_flops
+
+
+def hip_events(n):
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = (ctypes.c_void_p * n)()
+    for i in range(n):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        evs[i] = e
+    return hip, evs
+
+
+def elapsed_ms(hip, a, b) -> float:
+    t = ctypes.c_float(0.0)
+    if hip.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return float(t.value)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gaussian_mixture_sequence_resp_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(p)).get(f"{workload}:{kernel}")
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run_workload(w, steps, warmup):
+    import torch
+    import gaussian_mixture_sequence_resp_amd as gma
+    from gaussian_mixture_sequence_resp_amd.inputs import make_inputs
+
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    d = {k: v.to(dev) for k, v in inp.items()}
+    out = torch.empty((w.B, w.H, w.N, w.d_v), dtype=d["qr"].dtype, device=dev)
+    desc = gma.make_desc(w.B, w.H, w.N, w.d_r, w.d_v, w.K, w.dtype, w.var_floor)
+    need = gma.workspace_size(desc, w.causal)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    max_k = 8
+    hip, evs = hip_events(2 * max_k * steps)
+    names = (ctypes.c_char_p * max_k)()
+
+    def step(i=None):
+        if i is None:
+            gma.forward(d["qr"], d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"],
+                        causal=w.causal, eps=w.eps, var_floor=w.var_floor, out=out, workspace=ws,
+                        stream=stream)
+            return
+        sub = (ctypes.c_void_p * (2 * max_k)).from_buffer(evs, ctypes.sizeof(ctypes.c_void_p) * 2 * max_k * i)
+        gma.forward(d["qr"], d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"],
+                    causal=w.causal, eps=w.eps, var_floor=w.var_floor, out=out, workspace=ws,
+                    stream=stream, events=sub, names=names)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nk = gma.forward.last_kernel_count
+    per_kernel = {}
+    for j in range(min(nk, max_k)):
+        name = names[j].decode()
+        ts = [elapsed_ms(hip, evs[2 * max_k * i + 2 * j], evs[2 * max_k * i + 2 * j + 1]) for i in range(steps)]
+        per_kernel[name] = sum(ts) / len(ts)
+    # the same K steps without event recording, for reference
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for e in evs:
+        hip.hipEventDestroy(e)
+    return {"ms_per_step": (t1 - t0) * 1e3 / steps,
+            "ms_per_step_no_events": (t3 - t2) * 1e3 / steps,
+            "per_kernel_ms": per_kernel,
+            "workspace_bytes": need,
+            "inputs": inp}
+
+
+def roofline_for(w, per_kernel):
+    name = max(per_kernel, key=per_kernel.get)
+    ms = per_kernel[name]
+    nbytes, nflops = algorithmic(w, name)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    peak_flops = (FP32_VALU_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS) * 1e12
+    t_mfma = nflops / peak_flops
+    if t_hbm >= t_mfma:
+        ach = nbytes / (ms * 1e-3) / 1e9
+        rl = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = nflops / (ms * 1e-3) / 1e12
+        pk = FP32_VALU_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS
+        rl = {"bound": "mfma", "achieved": round(ach, 3), "peak": pk, "unit": "TFLOP/s",
+              "frac": round(ach / pk, 4)}
+    rl["kernel"] = name
+    rl["kernel_ms"] = round(ms, 5)
+    rl["traffic"] = traffic_from_profiles(name, w.name)
+    return rl
+
+
+def cpu_baseline(w, inp, budget_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of (b, h) slices of the same
+    workload, timed on this host's cores."""
+    import oracle
+    threads = oracle.num_threads()
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def run(hs):
+        t = time.perf_counter()
+        for b in sorted(set(b for b, _ in hs)):
+            hh = [h for bb, h in hs if bb == b]
+            lo, hi = min(hh), max(hh) + 1
+            oracle.forward(inp["qr"][b:b + 1, lo:hi], inp["kr"][b:b + 1, lo:hi], inp["v"][b:b + 1, lo:hi],
+                           inp["mu"][lo:hi], inp["var_raw"][lo:hi], inp["prior_logits"][lo:hi],
+                           w.causal, w.eps, w.var_floor)
+        return time.perf_counter() - t
+
+    # probe with one slice, then size the sample to the time budget (whole rows of heads)
+    t1 = run(heads[:1])
+    per = max(t1, 1e-6)
+    n = int(min(len(heads), max(1, budget_s * threads / per)))
+    n = min(len(heads), max(1, (n // w.H) * w.H if n >= w.H else n))
+    sample = heads[:n]
+    t = run(sample)
+    used = min(threads, n if n < w.H else w.H)
+    return {"value": round(n * w.N / t, 1), "unit": "token-heads/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{n} of {len(heads)} (b,h) slices x N={w.N} (fp64 C oracle, OpenMP over "
+                      f"slices, {t:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-causal", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the GMA forward here has no multi-GPU path "
+              "(the (b, h) slices shard with no communication; see DESIGN.md). Run --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    from gaussian_mixture_sequence_resp_amd.inputs import WORKLOADS
+    w = WORKLOADS[args.workload]
+    r = run_workload(w, args.steps, args.warmup)
+    th = w.token_heads
+    value = th / (r["ms_per_step"] * 1e-3)
+    line = {
+        "metric": metric_name(),
+        "value": round(value, 1),
+        "unit": "token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal draws, see gaussian_mixture_sequence_resp_amd/inputs.py)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d_r": w.d_r, "d_v": w.d_v,
+                   "K": w.K, "causal": w.causal, "global_batch": w.B, "seq_len": w.N,
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_step_no_events": round(r["ms_per_step_no_events"], 5),
+        "per_kernel_ms": {k: round(v, 5) for k, v in r["per_kernel_ms"].items()},
+        "workspace_bytes": r["workspace_bytes"],
+        "roofline": roofline_for(w, r["per_kernel_ms"]),
+    }
+    nbytes, nflops = algorithmic(w, "step")
+    line["step_roofline"] = {"hbm_frac": round(nbytes / (r["ms_per_step"] * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                             "mfma_frac": round(nflops / (r["ms_per_step"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+    if not args.no_causal and args.workload == 2:
+        wc = WORKLOADS[3]
+        rc = run_workload(wc, max(5, args.steps // 2), max(2, args.warmup // 2))
+        line["causal"] = {"workload": wc.name, "ms_per_step": round(rc["ms_per_step"], 5),
+                          "value": round(wc.token_heads / (rc["ms_per_step"] * 1e-3), 1),
+                          "per_kernel_ms": {k: round(v, 5) for k, v in rc["per_kernel_ms"].items()},
+                          "roofline": roofline_for(wc, rc["per_kernel_ms"])}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, r["inputs"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

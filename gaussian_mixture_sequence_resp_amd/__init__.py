@@ -1,0 +1,15 @@
+"""Gaussian Mixture Attention (GMA) forward mixer for MI355X (gfx950).
+
+The compute runs in ``libgma.so`` (hand-written HIP kernels behind the C ABI of
+``include/gma.h``); this package only binds it (``binding``), builds it
+(``build``) and draws seeded synthetic inputs (``inputs``).
+"""
+from .binding import (  # noqa: F401
+    GMAError,
+    forward,
+    load_library,
+    make_desc,
+    strerror,
+    version,
+    workspace_size,
+)

@@ -1,0 +1,138 @@
+"""Thin ctypes binding of libgma.so (declared in include/gma.h).
+
+Argument marshalling only: every step of the forward runs in the library's HIP
+kernels.  PyTorch supplies device memory (``torch.empty``) and the current HIP
+stream (``torch.cuda.current_stream().cuda_stream``).  If the library is missing
+or cannot be loaded every call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgma.so")
+
+GMA_OK = 0
+GMA_F32, GMA_BF16 = 0, 1
+ALGO = {"auto": 0, "simt": 1, "mfma": 2}
+
+_lib = None
+
+
+class GMAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"gma error {code}: {msg}")
+        self.code = code
+
+
+class GmaDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d_r", ctypes.c_int32), ("d_v", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("algo", ctypes.c_int32), ("var_floor", ctypes.c_float)]
+
+
+def load_library(path: Optional[str] = None):
+    """Load libgma.so (built in-tree by ``gaussian_mixture_sequence_resp_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    # torch ships its own HIP runtime (SONAME libamdhip64.so.7); loading torch first makes
+    # libgma.so bind to that same runtime instead of pulling in a second copy.
+    import torch  # noqa: F401
+    if not os.path.exists(p):
+        raise GMAError(-100, f"HIP library not built: {p} is missing "
+                             "(run __graft_entry__.build() or python -m "
+                             "gaussian_mixture_sequence_resp_amd.build)")
+    lib = ctypes.CDLL(p)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.gma_workspace_size.argtypes = [ctypes.POINTER(GmaDesc), ctypes.c_int]
+    lib.gma_workspace_size.restype = sz
+    lib.gma_forward.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp,
+                                ctypes.POINTER(GmaDesc), vp, sz, vp]
+    lib.gma_forward.restype = ctypes.c_int
+    lib.gma_forward_timed.argtypes = lib.gma_forward.argtypes + [
+        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+        ctypes.POINTER(ctypes.c_int)]
+    lib.gma_forward_timed.restype = ctypes.c_int
+    lib.gma_strerror.argtypes = [ctypes.c_int]
+    lib.gma_strerror.restype = ctypes.c_char_p
+    lib.gma_version.argtypes = []
+    lib.gma_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().gma_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return int(load_library().gma_version())
+
+
+def make_desc(B, H, N, d_r, d_v, K, dtype: str, var_floor: float, algo: str = "auto") -> GmaDesc:
+    dt = {"f32": GMA_F32, "bf16": GMA_BF16}[dtype]
+    return GmaDesc(int(B), int(H), int(N), int(d_r), int(d_v), int(K), dt, ALGO[algo],
+                   float(var_floor))
+
+
+def workspace_size(desc: GmaDesc, causal: bool) -> int:
+    return int(load_library().gma_workspace_size(ctypes.byref(desc), 1 if causal else 0))
+
+
+def _dtype_name(t) -> str:
+    import torch
+    if t.dtype == torch.float32:
+        return "f32"
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    raise GMAError(-3, f"unsupported dtype {t.dtype}")
+
+
+def forward(qr, kr, v, mu, var_raw, prior_logits, causal: bool = False, eps: float = 1e-6,
+            var_floor: float = 1e-3, out=None, gamma_out=None, workspace=None,
+            algo: str = "auto", stream=None, events=None, names=None):
+    """GMA forward on the current HIP device.
+
+    qr, kr [B,H,N,d_r] and v [B,H,N,d_v] (float32 or bfloat16, contiguous, on the GPU);
+    mu, var_raw [H,K,d_r] and prior_logits [H,K] float32.  Returns ``out`` [B,H,N,d_v] in
+    the input dtype.  ``gamma_out`` (optional, float32 [2,B,H,N,K]) receives Gamma_Q and
+    Gamma_K.  ``workspace`` (optional, uint8 device tensor) is allocated if not given.
+    """
+    import torch
+    lib = load_library()
+    B, H, N, d_r = qr.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    dt = _dtype_name(qr)
+    desc = make_desc(B, H, N, d_r, d_v, K, dt, var_floor, algo)
+    if out is None:
+        out = torch.empty((B, H, N, d_v), dtype=qr.dtype, device=qr.device)
+    need = int(lib.gma_workspace_size(ctypes.byref(desc), 1 if causal else 0))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qr.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(qr.device).cuda_stream
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    args = (ptr(qr), ptr(kr), ptr(v), ptr(mu), ptr(var_raw), ptr(prior_logits),
+            1 if causal else 0, float(eps), ptr(out), ptr(gamma_out),
+            ctypes.byref(desc), ws_ptr, ws_bytes, stream)
+    if events is None:
+        st = lib.gma_forward(*args)
+    else:
+        # events: ctypes array of hipEvent_t handles; names: ctypes array of c_char_p
+        nk = ctypes.c_int(0)
+        st = lib.gma_forward_timed(*args, events, len(events), names, ctypes.byref(nk))
+        forward.last_kernel_count = nk.value
+    if st != GMA_OK:
+        raise GMAError(st, strerror(st))
+    return out

@@ -1,0 +1,154 @@
+// Host side of libgma.so: argument validation, workspace sizing and dispatch.
+// Every check runs before the first HIP call, so an invalid call enqueues nothing.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "gma_internal.h"
+
+namespace {
+
+using gma::Args;
+
+int check_desc(const gma_desc* d) {
+    if (!d) return GMA_ERR_NULL_ARG;
+    if (d->B < 0 || d->H < 0 || d->N < 0 || d->d_r < 1 || d->d_v < 1 || d->K < 1) return GMA_ERR_BAD_SHAPE;
+    if (d->dtype != GMA_F32 && d->dtype != GMA_BF16) return GMA_ERR_UNSUPPORTED;
+    if (d->algo != GMA_ALGO_AUTO && d->algo != GMA_ALGO_SIMT && d->algo != GMA_ALGO_MFMA) return GMA_ERR_UNSUPPORTED;
+    if (d->K > GMA_MAX_K || d->d_r > GMA_MAX_DR || d->d_v > GMA_MAX_DV) return GMA_ERR_UNSUPPORTED;
+    // element counts: B*H*N rows must index with int32, tensors with int64
+    const int64_t rows = (int64_t)d->B * d->H * d->N;
+    if ((int64_t)d->B * d->H > INT32_MAX || rows > INT32_MAX) return GMA_ERR_BAD_SHAPE;
+    if (d->algo == GMA_ALGO_MFMA && d->dtype != GMA_BF16) return GMA_ERR_UNSUPPORTED;
+    if (!(d->var_floor >= 0.0f) || !isfinite(d->var_floor)) return GMA_ERR_BAD_SCALAR;
+    return GMA_OK;
+}
+
+// Resolve AUTO: the MFMA family for bf16 shapes it covers, SIMT otherwise.
+int resolve_algo(const gma_desc& d, int causal) {
+    if (d.algo == GMA_ALGO_SIMT) return GMA_ALGO_SIMT;
+    if (d.algo == GMA_ALGO_MFMA) return gma::mfma_supported(d, causal) ? GMA_ALGO_MFMA : -1;
+    return (d.dtype == GMA_BF16 && gma::mfma_supported(d, causal)) ? GMA_ALGO_MFMA : GMA_ALGO_SIMT;
+}
+
+size_t workspace_for(const gma_desc& d, int causal) {
+    const int algo = resolve_algo(d, causal);
+    if (algo == GMA_ALGO_MFMA) return gma::mfma_workspace(d, causal);
+    if (algo == GMA_ALGO_SIMT) return gma::simt_workspace(d, causal);
+    return 0;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gma_workspace_size(const gma_desc* desc, int causal) {
+    if (check_desc(desc) != GMA_OK || (causal != 0 && causal != 1)) return 0;
+    if ((int64_t)desc->B * desc->H * desc->N == 0) return 0;
+    return workspace_for(*desc, causal);
+}
+
+static int forward_impl(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                        const float* prior_logits, int causal, float eps, void* out, float* gamma_out,
+                        const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream,
+                        gma::Recorder* rec) {
+    int st = check_desc(desc);
+    if (st != GMA_OK) return st;
+    const gma_desc d = *desc;
+    if (causal != 0 && causal != 1) return GMA_ERR_BAD_SCALAR;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return GMA_ERR_BAD_SCALAR;
+    const size_t rows = (size_t)d.B * d.H * d.N;
+    if (rows == 0) return GMA_OK;  // empty sequence or batch: nothing to compute
+    if (!qr || !kr || !v || !mu || !var_raw || !prior_logits || !out) return GMA_ERR_NULL_ARG;
+    const size_t esz = d.dtype == GMA_F32 ? 4 : 2;
+    const size_t nx = rows * d.d_r * esz, nv = rows * d.d_v * esz;
+    const size_t np = (size_t)d.H * d.K * d.d_r * 4, npr = (size_t)d.H * d.K * 4;
+    const size_t ng = 2 * rows * d.K * 4;
+    if (misaligned(qr, 16) || misaligned(kr, 16) || misaligned(v, 16) || misaligned(out, 16))
+        return GMA_ERR_ALIGN;
+    if (misaligned(mu, 4) || misaligned(var_raw, 4) || misaligned(prior_logits, 4) ||
+        (gamma_out && misaligned(gamma_out, 4)))
+        return GMA_ERR_ALIGN;
+    if (workspace && misaligned(workspace, gma::kWsAlign)) return GMA_ERR_ALIGN;
+    const void* ins[6] = {qr, kr, v, mu, var_raw, prior_logits};
+    const size_t ins_n[6] = {nx, nx, nv, np, np, npr};
+    for (int i = 0; i < 6; ++i) {
+        if (overlaps(out, nv, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
+        if (gamma_out && overlaps(gamma_out, ng, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
+    }
+    if (gamma_out && overlaps(out, nv, gamma_out, ng)) return GMA_ERR_ALIAS;
+    const int algo = resolve_algo(d, causal);
+    if (algo < 0) return GMA_ERR_UNSUPPORTED;
+    const size_t need = workspace_for(d, causal);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GMA_ERR_WORKSPACE;
+    if (workspace && (overlaps(workspace, need, out, nv) || (gamma_out && overlaps(workspace, need, gamma_out, ng))))
+        return GMA_ERR_ALIAS;
+    for (int i = 0; i < 6; ++i)
+        if (workspace && overlaps(workspace, need, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
+
+    Args a;
+    a.qr = qr;
+    a.kr = kr;
+    a.v = v;
+    a.mu = mu;
+    a.var_raw = var_raw;
+    a.prior = prior_logits;
+    a.causal = causal;
+    a.eps = eps;
+    a.out = out;
+    a.gamma_out = gamma_out;
+    a.d = d;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.ws_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    a.rec = rec;
+    const hipError_t e = (algo == GMA_ALGO_MFMA) ? gma::mfma_forward(a) : gma::simt_forward(a);
+    return e == hipSuccess ? GMA_OK : GMA_ERR_HIP;
+}
+
+int gma_forward(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                const float* prior_logits, int causal, float eps, void* out, float* gamma_out,
+                const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_impl(qr, kr, v, mu, var_raw, prior_logits, causal, eps, out, gamma_out, desc, workspace,
+                        workspace_bytes, stream, nullptr);
+}
+
+int gma_forward_timed(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                      const float* prior_logits, int causal, float eps, void* out, float* gamma_out,
+                      const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* events, int n_events, const char** names, int* n_kernels) {
+    if (n_kernels) *n_kernels = 0;
+    if (n_events < 0 || (n_events > 0 && !events)) return GMA_ERR_NULL_ARG;
+    gma::Recorder rec{events, n_events, names, 0};
+    const int st = forward_impl(qr, kr, v, mu, var_raw, prior_logits, causal, eps, out, gamma_out, desc,
+                                workspace, workspace_bytes, stream, &rec);
+    if (n_kernels) *n_kernels = rec.count;
+    return st;
+}
+
+const char* gma_strerror(int status) {
+    switch (status) {
+        case GMA_OK: return "success";
+        case GMA_ERR_NULL_ARG: return "a required pointer argument is NULL";
+        case GMA_ERR_BAD_SHAPE: return "invalid shape (B, H, N must be >= 0; d_r, d_v, K >= 1; sizes too large)";
+        case GMA_ERR_UNSUPPORTED: return "unsupported configuration (K, d_r, d_v above the limits, dtype or algorithm)";
+        case GMA_ERR_ALIGN: return "misaligned pointer (tensors 16 B, parameters 4 B, workspace 256 B)";
+        case GMA_ERR_BAD_SCALAR: return "invalid scalar (eps/var_floor must be finite and >= 0; causal 0 or 1)";
+        case GMA_ERR_WORKSPACE: return "workspace missing or smaller than gma_workspace_size()";
+        case GMA_ERR_ALIAS: return "an output overlaps an input, the workspace or the other output";
+        case GMA_ERR_HIP: return "a HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int gma_version(void) { return GMA_VERSION; }
+
+}  // extern "C"

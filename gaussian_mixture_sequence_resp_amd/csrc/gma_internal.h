@@ -1,0 +1,73 @@
+// Internal interfaces of libgma.so shared by the host API and the kernel families.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gma.h"
+
+namespace gma {
+
+// Optional per-kernel event recording (gma_forward_timed).
+struct Recorder {
+    void* const* events;
+    int n_events;
+    const char** names;
+    int count;
+};
+
+struct Args {
+    const void* qr;
+    const void* kr;
+    const void* v;
+    const float* mu;
+    const float* var_raw;
+    const float* prior;
+    int causal;
+    float eps;
+    void* out;
+    float* gamma_out;
+    gma_desc d;
+    unsigned char* ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+    Recorder* rec;
+};
+
+// Bracket the next kernel launch with events when recording; no-ops otherwise.
+inline void rec_begin(const Args& a, const char* name) {
+    Recorder* r = a.rec;
+    if (r && 2 * r->count + 1 < r->n_events) {
+        (void)hipEventRecord(static_cast<hipEvent_t>(r->events[2 * r->count]), a.stream);
+        if (r->names) r->names[r->count] = name;
+    }
+}
+inline void rec_end(const Args& a) {
+    Recorder* r = a.rec;
+    if (!r) return;
+    if (2 * r->count + 1 < r->n_events)
+        (void)hipEventRecord(static_cast<hipEvent_t>(r->events[2 * r->count + 1]), a.stream);
+    r->count++;
+}
+
+// Round a byte count up to the workspace region alignment.
+constexpr size_t kWsAlign = 256;
+inline size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// SIMT family: plain fp32 arithmetic, one thread per output element.
+size_t simt_workspace(const gma_desc& d, int causal);
+hipError_t simt_forward(const Args& a);
+// Responsibilities only, written as float32 [2,B,H,N,K]; used for gamma_out by every family.
+hipError_t simt_gamma(const Args& a, float* gamma, const float* lam, const float* cst);
+// Parameter prep of the SIMT family: lam = 1/var [H,K,d_r], cst [H,K] (log prior minus half
+// the log-determinant), both float32.
+hipError_t simt_params(const Args& a, float* lam, float* cst);
+size_t simt_param_bytes(const gma_desc& d);
+
+// MFMA family (bf16 inputs): fused matrix-core kernels.
+size_t mfma_workspace(const gma_desc& d, int causal);
+bool mfma_supported(const gma_desc& d, int causal);
+hipError_t mfma_forward(const Args& a);
+
+}  // namespace gma

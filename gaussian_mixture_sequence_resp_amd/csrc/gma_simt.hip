@@ -1,0 +1,287 @@
+// SIMT family of the GMA forward: plain fp32 arithmetic, one thread per output element.
+//
+// Method: Gaussian Mixture Attention (arXiv 2606.18283), "Core mechanism" items 1-3:
+// GMM posterior responsibilities with softplus variances and softmax priors, the write
+// phase Vt = Gamma_K^T V, Z = Gamma_K^T 1, the read phase O = Gamma_Q Vt / (Gamma_Q Z + eps)
+// and the causal variant built on inclusive prefix sums.
+//
+// This family serves float32 inputs and any supported shape.  The log-density is taken in
+// its direct form, l_k(x) = c_k - 1/2 sum_d (x_d - mu_kd)^2 / var_kd with
+// c_k = log pi_k - 1/2 sum_d log var_kd; the constant (d/2) log 2 pi is the same for every
+// component of a row and cancels in the softmax, so it is not computed.  Responsibilities
+// are materialised in the workspace (float32 [2,B,H,N,K]), then the write and read phases
+// (or the causal scan) consume them.  Every sum runs in ascending index order, so results
+// are deterministic.
+#include <math.h>
+
+#include "gma_internal.h"
+#include "gma_numeric.h"
+
+namespace gma {
+namespace {
+
+constexpr int kBlock = 256;
+
+// One block per head: lam[h,k,d] = 1/var, cst[h,k] = log pi_k - 1/2 sum_d log var_kd.
+// Computed in double, stored as float.
+__global__ void __launch_bounds__(kBlock) params_kernel(const float* __restrict__ mu,
+                                                        const float* __restrict__ var_raw,
+                                                        const float* __restrict__ prior, int K,
+                                                        int dr, float var_floor,
+                                                        float* __restrict__ lam,
+                                                        float* __restrict__ cst) {
+    (void)mu;
+    const int h = blockIdx.x;
+    __shared__ double red[kBlock];
+    // log-sum-exp of the prior logits of this head (softmax priors)
+    double pmax = -INFINITY;
+    for (int k = threadIdx.x; k < K; k += kBlock) pmax = fmax(pmax, (double)prior[(size_t)h * K + k]);
+    red[threadIdx.x] = pmax;
+    __syncthreads();
+    for (int s = kBlock / 2; s > 0; s >>= 1) {
+        if (threadIdx.x < s) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + s]);
+        __syncthreads();
+    }
+    pmax = red[0];
+    __syncthreads();
+    double psum = 0.0;
+    for (int k = threadIdx.x; k < K; k += kBlock) psum += exp((double)prior[(size_t)h * K + k] - pmax);
+    red[threadIdx.x] = psum;
+    __syncthreads();
+    for (int s = kBlock / 2; s > 0; s >>= 1) {
+        if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    const double lse = pmax + log(red[0]);
+    for (int k = threadIdx.x; k < K; k += kBlock) {
+        double half_logdet = 0.0;
+        for (int d = 0; d < dr; ++d) {
+            const size_t i = ((size_t)h * K + k) * dr + d;
+            const double r = var_raw[i];
+            const double var = fmax(r, 0.0) + log1p(exp(-fabs(r))) + (double)var_floor;
+            lam[i] = (float)(1.0 / var);
+            half_logdet += 0.5 * log(var);
+        }
+        cst[(size_t)h * K + k] = (float)((double)prior[(size_t)h * K + k] - lse - half_logdet);
+    }
+}
+
+// One thread per routing row (side, b, h, n): gamma[side,b,h,n,:] = softmax_k l_k(x).
+template <typename T>
+__global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
+                                                      const T* __restrict__ kr,
+                                                      const float* __restrict__ mu,
+                                                      const float* __restrict__ lam,
+                                                      const float* __restrict__ cst,
+                                                      float* __restrict__ gamma, int BH, int H,
+                                                      int N, int dr, int K, int nblk) {
+    const int side = blockIdx.y;
+    const int bh = blockIdx.x / nblk;
+    const int n = (blockIdx.x % nblk) * kBlock + threadIdx.x;
+    if (n >= N) return;
+    const int h = bh % H;
+    const T* x = (side == 0 ? qr : kr) + ((size_t)bh * N + n) * dr;
+    float* g = gamma + (((size_t)side * BH + bh) * N + n) * K;
+    const float* mu_h = mu + (size_t)h * K * dr;
+    const float* lam_h = lam + (size_t)h * K * dr;
+    float m = -INFINITY;
+    for (int k = 0; k < K; ++k) {
+        float q = 0.0f;
+        for (int d = 0; d < dr; ++d) {
+            const float diff = Elem<T>::load(x, d) - mu_h[(size_t)k * dr + d];
+            q = fmaf(lam_h[(size_t)k * dr + d] * diff, diff, q);
+        }
+        const float l = cst[(size_t)h * K + k] - 0.5f * q;
+        g[k] = l;
+        m = fmaxf(m, l);
+    }
+    float s = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const float e = expf(g[k] - m);
+        g[k] = e;
+        s += e;
+    }
+    const float inv = 1.0f / s;
+    for (int k = 0; k < K; ++k) g[k] *= inv;
+}
+
+// Bidirectional write: mem[b,h,k,c] = sum_n gamma_K[n,k] * [v[n,c] | 1], c in [0, d_v].
+template <typename T>
+__global__ void __launch_bounds__(kBlock) write_kernel(const float* __restrict__ gk,
+                                                       const T* __restrict__ v,
+                                                       float* __restrict__ mem, int N, int K,
+                                                       int dv, int nblk) {
+    const int bh = blockIdx.x / nblk;
+    const int idx = (blockIdx.x % nblk) * kBlock + threadIdx.x;
+    const int W = dv + 1;
+    if (idx >= K * W) return;
+    const int k = idx / W, c = idx % W;
+    const float* g = gk + (size_t)bh * N * K;
+    const T* vv = v + (size_t)bh * N * dv;
+    float acc = 0.0f;
+    if (c < dv) {
+        for (int n = 0; n < N; ++n) acc = fmaf(g[(size_t)n * K + k], Elem<T>::load(vv, (size_t)n * dv + c), acc);
+    } else {
+        for (int n = 0; n < N; ++n) acc += g[(size_t)n * K + k];
+    }
+    mem[((size_t)bh * K + k) * W + c] = acc;
+}
+
+// Bidirectional read: out[b,h,n,c] = sum_k gq[n,k] mem[k,c] / (sum_k gq[n,k] mem[k,dv] + eps).
+template <typename T>
+__global__ void __launch_bounds__(kBlock) read_kernel(const float* __restrict__ gq,
+                                                      const float* __restrict__ mem,
+                                                      T* __restrict__ out, int N, int K, int dv,
+                                                      float eps, int nblk) {
+    const int bh = blockIdx.x / nblk;
+    const size_t idx = (size_t)(blockIdx.x % nblk) * kBlock + threadIdx.x;
+    if (idx >= (size_t)N * dv) return;
+    const int n = (int)(idx / dv), c = (int)(idx % dv);
+    const int W = dv + 1;
+    const float* g = gq + ((size_t)bh * N + n) * K;
+    const float* m = mem + (size_t)bh * K * W;
+    float num = 0.0f, den = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        num = fmaf(g[k], m[(size_t)k * W + c], num);
+        den = fmaf(g[k], m[(size_t)k * W + dv], den);
+    }
+    Elem<T>::store(out, ((size_t)bh * N + n) * dv + c, num / (den + eps));
+}
+
+// Causal scan, one block per (b, h).  The state [S | z] (K x (d_v+1), float32) lives in LDS;
+// for each position i: state += gamma_K[i] (x) [v_i | 1] (inclusive), then
+// out_i = gamma_Q[i] . S / (gamma_Q[i] . z + eps).
+template <typename T>
+__global__ void __launch_bounds__(kBlock) causal_kernel(const float* __restrict__ gq,
+                                                        const float* __restrict__ gk,
+                                                        const T* __restrict__ v,
+                                                        T* __restrict__ out, int N, int K,
+                                                        int dv, float eps) {
+    extern __shared__ float smem[];
+    const int W = dv + 1;
+    float* state = smem;             // [K][W]
+    float* res = smem + (size_t)K * W;  // [W]
+    const int bh = blockIdx.x;
+    const float* gqh = gq + (size_t)bh * N * K;
+    const float* gkh = gk + (size_t)bh * N * K;
+    const T* vh = v + (size_t)bh * N * dv;
+    T* oh = out + (size_t)bh * N * dv;
+    for (int i = threadIdx.x; i < K * W; i += kBlock) state[i] = 0.0f;
+    __syncthreads();
+    for (int n = 0; n < N; ++n) {
+        for (int i = threadIdx.x; i < K * W; i += kBlock) {
+            const int k = i / W, c = i % W;
+            const float g = gkh[(size_t)n * K + k];
+            state[i] = (c < dv) ? fmaf(g, Elem<T>::load(vh, (size_t)n * dv + c), state[i]) : state[i] + g;
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < W; c += kBlock) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) acc = fmaf(gqh[(size_t)n * K + k], state[(size_t)k * W + c], acc);
+            res[c] = acc;
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < dv; c += kBlock)
+            Elem<T>::store(oh, (size_t)n * dv + c, res[c] / (res[dv] + eps));
+        __syncthreads();
+    }
+}
+
+struct SimtLayout {
+    size_t lam, cst, gamma, mem, total;
+};
+
+SimtLayout simt_layout(const gma_desc& d) {
+    SimtLayout L;
+    const size_t BH = (size_t)d.B * d.H;
+    size_t off = 0;
+    L.lam = off;
+    off += align_up((size_t)d.H * d.K * d.d_r * sizeof(float));
+    L.cst = off;
+    off += align_up((size_t)d.H * d.K * sizeof(float));
+    L.gamma = off;
+    off += align_up(2 * BH * d.N * d.K * sizeof(float));
+    L.mem = off;
+    off += align_up(BH * d.K * (d.d_v + 1) * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+hipError_t simt_forward_t(const Args& a) {
+    const gma_desc& d = a.d;
+    const SimtLayout L = simt_layout(d);
+    float* lam = reinterpret_cast<float*>(a.ws + L.lam);
+    float* cst = reinterpret_cast<float*>(a.ws + L.cst);
+    float* gamma = a.gamma_out ? a.gamma_out : reinterpret_cast<float*>(a.ws + L.gamma);
+    float* mem = reinterpret_cast<float*>(a.ws + L.mem);
+    const int BH = d.B * d.H;
+    hipError_t e = simt_params(a, lam, cst);
+    if (e != hipSuccess) return e;
+    e = simt_gamma(a, gamma, lam, cst);
+    if (e != hipSuccess) return e;
+    const float* gq = gamma;
+    const float* gk = gamma + (size_t)BH * d.N * d.K;
+    const T* v = static_cast<const T*>(a.v);
+    T* out = static_cast<T*>(a.out);
+    if (!a.causal) {
+        const int wblk = (d.K * (d.d_v + 1) + kBlock - 1) / kBlock;
+        rec_begin(a, "simt_write");
+        write_kernel<T><<<dim3(BH * wblk), dim3(kBlock), 0, a.stream>>>(gk, v, mem, d.N, d.K, d.d_v, wblk);
+        rec_end(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int rblk = (int)(((size_t)d.N * d.d_v + kBlock - 1) / kBlock);
+        rec_begin(a, "simt_read");
+        read_kernel<T><<<dim3(BH * rblk), dim3(kBlock), 0, a.stream>>>(gq, mem, out, d.N, d.K, d.d_v, a.eps, rblk);
+        rec_end(a);
+        return hipGetLastError();
+    }
+    const size_t lds = ((size_t)d.K * (d.d_v + 1) + (d.d_v + 1)) * sizeof(float);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&causal_kernel<T>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    rec_begin(a, "simt_causal_scan");
+    causal_kernel<T><<<dim3(BH), dim3(kBlock), lds, a.stream>>>(gq, gk, v, out, d.N, d.K, d.d_v, a.eps);
+    rec_end(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t simt_param_bytes(const gma_desc& d) {
+    return align_up((size_t)d.H * d.K * d.d_r * sizeof(float)) + align_up((size_t)d.H * d.K * sizeof(float));
+}
+
+size_t simt_workspace(const gma_desc& d, int /*causal*/) { return simt_layout(d).total; }
+
+hipError_t simt_params(const Args& a, float* lam, float* cst) {
+    rec_begin(a, "simt_params");
+    params_kernel<<<dim3(a.d.H), dim3(kBlock), 0, a.stream>>>(a.mu, a.var_raw, a.prior, a.d.K, a.d.d_r,
+                                                              a.d.var_floor, lam, cst);
+    rec_end(a);
+    return hipGetLastError();
+}
+
+hipError_t simt_gamma(const Args& a, float* gamma, const float* lam, const float* cst) {
+    const gma_desc& d = a.d;
+    const int BH = d.B * d.H;
+    const int nblk = (d.N + kBlock - 1) / kBlock;
+    dim3 grid(BH * nblk, 2);
+    rec_begin(a, "simt_responsibilities");
+    if (d.dtype == GMA_F32)
+        resp_kernel<float><<<grid, dim3(kBlock), 0, a.stream>>>(
+            static_cast<const float*>(a.qr), static_cast<const float*>(a.kr), a.mu, lam, cst, gamma, BH,
+            d.H, d.N, d.d_r, d.K, nblk);
+    else
+        resp_kernel<bf16_t><<<grid, dim3(kBlock), 0, a.stream>>>(
+            static_cast<const bf16_t*>(a.qr), static_cast<const bf16_t*>(a.kr), a.mu, lam, cst, gamma, BH,
+            d.H, d.N, d.d_r, d.K, nblk);
+    rec_end(a);
+    return hipGetLastError();
+}
+
+hipError_t simt_forward(const Args& a) {
+    return a.d.dtype == GMA_F32 ? simt_forward_t<float>(a) : simt_forward_t<bf16_t>(a);
+}
+
+}  // namespace gma

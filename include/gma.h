@@ -1,0 +1,149 @@
+/*
+ * gma.h -- C ABI of libgma.so, the MI355X (gfx950) forward mixer of Gaussian Mixture
+ * Attention (GMA).
+ *
+ * Method: "Gaussian Mixture Attention: Linear-Time Sequence Mixing via Probabilistic
+ * Latent Routing" (Huang, Raza; arXiv 2606.18283), gist.science summary, section "Core
+ * mechanism":
+ *   item 1  -- queries and keys are routed to K learned diagonal Gaussians; the
+ *              responsibility gamma_{i,k} = p(z=k | x_i) is the standard GMM posterior
+ *              with means mu_k, diagonal covariances Sigma_k and mixture priors pi_k,
+ *              giving the non-negative maps Gamma_Q, Gamma_K (N x K);
+ *   item 2  -- write phase Vt = Gamma_K^T V, Z = Gamma_K^T 1 (a K-slot latent memory),
+ *              read phase O = Gamma_Q Vt / (Gamma_Q Z + eps); the N x N affinity
+ *              Gamma_Q Gamma_K^T is never formed;
+ *   item 3  -- bidirectional and causal variants (the causal one uses prefix sums of
+ *              the memory and the normaliser so O_i depends on positions j <= i only);
+ *              variances are reparameterised with softplus, priors with softmax.
+ *
+ * Conventions of this library (the pages leave them open):
+ *   var_kd = softplus(var_raw_kd) + var_floor  (softplus acts on the variance);
+ *   pi     = softmax(prior_logits) over the K components of a head;
+ *   one set of K Gaussians per head, shared by the queries and keys of that head and by
+ *   every batch element;
+ *   eps is added once per output row after the product Gamma_Q Z;
+ *   the causal sum is inclusive: O_i uses keys/values j = 0..i.
+ *
+ * Layouts (all row-major, contiguous, device memory):
+ *   qr, kr        [B, H, N, d_r]  dtype (GMA_F32 or GMA_BF16)
+ *   v, out        [B, H, N, d_v]  dtype
+ *   mu, var_raw   [H, K, d_r]     float32
+ *   prior_logits  [H, K]          float32
+ *   gamma_out     [2, B, H, N, K] float32, optional: Gamma_Q then Gamma_K
+ *
+ * Ownership: the caller owns every buffer, including the workspace; the library never
+ * allocates, frees or retains device memory and keeps no mutable global state.  `out`
+ * and `gamma_out` must not alias any input or each other.
+ *
+ * Execution: every call enqueues kernels on `stream` (a hipStream_t; NULL means the
+ * legacy default stream) and returns without synchronising.  Results are valid once the
+ * stream has been synchronised.  Concurrent calls are safe if they use distinct
+ * workspaces and outputs.
+ *
+ * Errors: every argument is checked on the host before any HIP call; on error nothing is
+ * enqueued and a negative status is returned.  Input values are not scanned: NaN or Inf
+ * in the inputs propagate.  No C++ exception crosses this interface.
+ */
+#ifndef GMA_H
+#define GMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GMA_VERSION 10000 /* 1.0.0 */
+
+/* Limits of this build. */
+#define GMA_MAX_K 256
+#define GMA_MAX_DR 128
+#define GMA_MAX_DV 128
+
+typedef enum {
+    GMA_OK = 0,
+    GMA_ERR_NULL_ARG = -1,    /* a required pointer is NULL                                 */
+    GMA_ERR_BAD_SHAPE = -2,   /* B, H or N < 0; d_r, d_v or K < 1; element counts too large  */
+    GMA_ERR_UNSUPPORTED = -3, /* K > GMA_MAX_K, d_r > GMA_MAX_DR, d_v > GMA_MAX_DV, unknown
+                                 dtype or algorithm, or an algorithm that cannot run this
+                                 dtype                                                        */
+    GMA_ERR_ALIGN = -4,       /* qr, kr, v, out not 16-byte aligned; parameters or gamma_out
+                                 not 4-byte aligned; workspace not 256-byte aligned           */
+    GMA_ERR_BAD_SCALAR = -5,  /* eps or var_floor negative or not finite; causal not 0 or 1  */
+    GMA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than gma_workspace_size()         */
+    GMA_ERR_ALIAS = -7,       /* out or gamma_out overlaps an input or each other            */
+    GMA_ERR_HIP = -8          /* a kernel launch reported an error                           */
+} gma_status;
+
+typedef enum { GMA_F32 = 0, GMA_BF16 = 1 } gma_dtype;
+
+/* Kernel family.  AUTO picks MFMA for bf16 and SIMT for fp32.  SIMT is the plain
+ * one-thread-per-element fp32 path (any supported shape, both dtypes); MFMA is the fused
+ * matrix-core path (bf16 only). */
+typedef enum { GMA_ALGO_AUTO = 0, GMA_ALGO_SIMT = 1, GMA_ALGO_MFMA = 2 } gma_algo;
+
+typedef struct {
+    int32_t B, H, N;     /* batch, heads, sequence length (0 gives an empty call)  */
+    int32_t d_r, d_v, K; /* routing dim, value dim, number of Gaussian components  */
+    int32_t dtype;       /* gma_dtype of qr, kr, v and out                         */
+    int32_t algo;        /* gma_algo                                               */
+    float var_floor;     /* added to softplus(var_raw); >= 0 and finite            */
+} gma_desc;
+
+/*
+ * Bytes of device workspace that gma_forward needs for this descriptor and variant
+ * (`causal` 0 or 1).  Pure host arithmetic, no HIP call.  Returns 0 when the descriptor
+ * is invalid (gma_forward then reports why) or when no workspace is needed.
+ */
+size_t gma_workspace_size(const gma_desc* desc, int causal);
+
+/*
+ * GMA forward (responsibilities, write, read; or the causal prefix form).
+ *   qr, kr, v      inputs, layout above, dtype = desc->dtype
+ *   mu, var_raw    [H,K,d_r] float32 Gaussian means and pre-softplus variances
+ *   prior_logits   [H,K] float32 pre-softmax mixture weights
+ *   causal         0 = bidirectional (write/read of "Core mechanism" item 2),
+ *                  1 = causal prefix-sum variant (item 3)
+ *   eps            normaliser floor, >= 0
+ *   out            [B,H,N,d_v] output in desc->dtype (round to nearest even for bf16)
+ *   gamma_out      NULL, or [2,B,H,N,K] float32 that receives Gamma_Q and Gamma_K
+ *                  (diagnostic; an extra kernel, not part of the fused path)
+ *   workspace      device scratch of at least gma_workspace_size(desc, causal) bytes,
+ *                  256-byte aligned (may be NULL if that size is 0); contents on entry
+ *                  are ignored and on return are unspecified
+ *   stream         hipStream_t to enqueue on, NULL for the default stream
+ * Returns GMA_OK or a negative gma_status.
+ */
+int gma_forward(const void* qr, const void* kr, const void* v, const float* mu,
+                const float* var_raw, const float* prior_logits, int causal, float eps,
+                void* out, float* gamma_out, const gma_desc* desc, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * Profiling variant of gma_forward: identical arguments and kernels, plus a pair of HIP
+ * events recorded on `stream` around every kernel the call launches, so a caller can time
+ * each kernel of one forward without a profiler.  `events` holds `n_events` hipEvent_t
+ * handles created by the caller (hipEventCreate); kernel i is bracketed by events[2i] and
+ * events[2i+1].  On return *n_kernels (if non-NULL) is the number of kernels launched and
+ * names[i] (if `names` is non-NULL, room for n_events/2 entries) points to a static name of
+ * kernel i.  Kernels beyond n_events/2 run unbracketed.  Nothing is synchronised; read the
+ * times with hipEventElapsedTime once the stream is done.
+ */
+int gma_forward_timed(const void* qr, const void* kr, const void* v, const float* mu,
+                      const float* var_raw, const float* prior_logits, int causal, float eps,
+                      void* out, float* gamma_out, const gma_desc* desc, void* workspace,
+                      size_t workspace_bytes, void* stream, void* const* events, int n_events,
+                      const char** names, int* n_kernels);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gma_strerror(int status);
+
+/* GMA_VERSION of the loaded library. */
+int gma_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMA_H */

@@ -68,12 +68,15 @@ int gma_oracle_log_joint(const double* x, int N, int d, const double* mu,
     if (!x || !mu || !var_raw || !prior_logits || !out || N < 0 || d < 1 || K < 1)
         return ORACLE_BAD_ARG;
     double* var = (double*)malloc(sizeof(double) * (size_t)K * d);
+    double* logvar = (double*)malloc(sizeof(double) * (size_t)K * d);
     double* logpi = (double*)malloc(sizeof(double) * (size_t)K);
-    if (!var || !logpi) { free(var); free(logpi); return ORACLE_NO_MEM; }
+    if (!var || !logvar || !logpi) { free(var); free(logvar); free(logpi); return ORACLE_NO_MEM; }
 
     for (int k = 0; k < K; ++k)
-        for (int j = 0; j < d; ++j)
+        for (int j = 0; j < d; ++j) {
             var[(size_t)k * d + j] = softplus(var_raw[(size_t)k * d + j]) + var_floor;
+            logvar[(size_t)k * d + j] = log(var[(size_t)k * d + j]);
+        }
 
     /* log softmax of the prior logits */
     double pmax = prior_logits[0];
@@ -89,15 +92,17 @@ int gma_oracle_log_joint(const double* x, int N, int d, const double* mu,
         for (int k = 0; k < K; ++k) {
             const double* mk = mu + (size_t)k * d;
             const double* vk = var + (size_t)k * d;
+            const double* lvk = logvar + (size_t)k * d;
             double quad = 0.0;
             for (int j = 0; j < d; ++j) {
                 double diff = xi[j] - mk[j];
-                quad += LOG_2PI + log(vk[j]) + diff * diff / vk[j];
+                quad += LOG_2PI + lvk[j] + diff * diff / vk[j];
             }
             out[(size_t)i * K + k] = logpi[k] - 0.5 * quad;
         }
     }
     free(var);
+    free(logvar);
     free(logpi);
     return ORACLE_OK;
 }

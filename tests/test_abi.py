@@ -1,0 +1,126 @@
+"""CPU-only checks of the C ABI (include/gma.h): the library loads, exports every
+declared entry point, and rejects invalid calls with the documented status codes
+before any HIP call (so these run on a machine without a GPU).  Pointers below are
+fake, aligned, non-overlapping addresses: every case fails validation, so none is
+ever dereferenced and no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gma.h")
+
+binding = pytest.importorskip("gaussian_mixture_sequence_resp_amd.binding")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libgma.so is not built; run __graft_entry__.build()")
+    return binding.load_library()
+
+
+def _header_text():
+    return open(HEADER).read()
+
+
+def _codes():
+    txt = _header_text()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(GMA_OK|GMA_ERR_[A-Z_]+)\s*=\s*(-?\d+)", txt)}
+
+
+def test_exports_every_declared_symbol(lib):
+    txt = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    names = set(re.findall(r"\b(gma_[a-z_]+)\s*\(", txt))
+    assert names == {"gma_workspace_size", "gma_forward", "gma_forward_timed", "gma_strerror",
+                     "gma_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror(lib):
+    m = re.search(r"#define GMA_VERSION (\d+)", _header_text())
+    assert lib.gma_version() == int(m.group(1))
+    for code in _codes().values():
+        s = binding.strerror(code)
+        assert s and s != "unknown status"
+    assert binding.strerror(-999) == "unknown status"
+
+
+class Call:
+    """A valid-looking call with fake device addresses; tests perturb one field."""
+    BASE = 1 << 32
+
+    def __init__(self, **kw):
+        self.desc = binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "simt")
+        for k in ("B", "H", "N", "d_r", "d_v", "K", "dtype", "algo", "var_floor"):
+            if k in kw:
+                setattr(self.desc, k, kw.pop(k))
+        step = 1 << 24
+        self.ptr = {n: self.BASE + i * step for i, n in enumerate(
+            ["qr", "kr", "v", "mu", "var_raw", "prior", "out", "gamma", "ws"])}
+        self.ptr["gamma"] = None
+        self.causal, self.eps = 0, 1e-6
+        self.ws_bytes = 1 << 40
+        for k, val in kw.items():
+            if k in self.ptr:
+                self.ptr[k] = val
+            else:
+                setattr(self, k, val)
+
+    def run(self, lib, desc_null=False):
+        p = self.ptr
+        d = None if desc_null else ctypes.byref(self.desc)
+        return lib.gma_forward(p["qr"], p["kr"], p["v"], p["mu"], p["var_raw"], p["prior"],
+                               self.causal, self.eps, p["out"], p["gamma"], d, p["ws"],
+                               self.ws_bytes, None)
+
+
+C = _codes()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), "GMA_ERR_BAD_SHAPE"), (dict(K=0), "GMA_ERR_BAD_SHAPE"),
+    (dict(d_r=0), "GMA_ERR_BAD_SHAPE"), (dict(d_v=0), "GMA_ERR_BAD_SHAPE"),
+    (dict(B=1 << 16, H=1 << 16), "GMA_ERR_BAD_SHAPE"),
+    (dict(K=257), "GMA_ERR_UNSUPPORTED"), (dict(d_r=129), "GMA_ERR_UNSUPPORTED"),
+    (dict(d_v=129), "GMA_ERR_UNSUPPORTED"), (dict(dtype=7), "GMA_ERR_UNSUPPORTED"),
+    (dict(algo=9), "GMA_ERR_UNSUPPORTED"), (dict(algo=2, dtype=0), "GMA_ERR_UNSUPPORTED"),
+    (dict(var_floor=float("nan")), "GMA_ERR_BAD_SCALAR"), (dict(var_floor=-1.0), "GMA_ERR_BAD_SCALAR"),
+    (dict(eps=-1.0), "GMA_ERR_BAD_SCALAR"), (dict(eps=float("inf")), "GMA_ERR_BAD_SCALAR"),
+    (dict(eps=float("nan")), "GMA_ERR_BAD_SCALAR"), (dict(causal=2), "GMA_ERR_BAD_SCALAR"),
+    (dict(qr=None), "GMA_ERR_NULL_ARG"), (dict(out=None), "GMA_ERR_NULL_ARG"),
+    (dict(prior=None), "GMA_ERR_NULL_ARG"),
+    (dict(qr=Call.BASE + 8), "GMA_ERR_ALIGN"), (dict(out=Call.BASE + 6 * (1 << 24) + 4), "GMA_ERR_ALIGN"),
+    (dict(mu=Call.BASE + 3 * (1 << 24) + 2), "GMA_ERR_ALIGN"),
+    (dict(ws=Call.BASE + 8 * (1 << 24) + 128), "GMA_ERR_ALIGN"),
+    (dict(out=Call.BASE), "GMA_ERR_ALIAS"), (dict(gamma=Call.BASE + (1 << 24)), "GMA_ERR_ALIAS"),
+    (dict(ws=Call.BASE + 2 * (1 << 24)), "GMA_ERR_ALIAS"),
+    (dict(ws_bytes=16), "GMA_ERR_WORKSPACE"), (dict(ws=None), "GMA_ERR_WORKSPACE"),
+])
+def test_invalid_calls_return_documented_codes(lib, kw, code):
+    assert Call(**kw).run(lib) == C[code]
+
+
+def test_null_descriptor(lib):
+    assert Call().run(lib, desc_null=True) == C["GMA_ERR_NULL_ARG"]
+
+
+def test_empty_problem_is_ok_without_launch(lib):
+    # N = 0 (or B = 0): a valid no-op, returns before touching any pointer or the GPU
+    assert Call(N=0, qr=None, ws=None).run(lib) == C["GMA_OK"]
+    assert Call(B=0).run(lib) == C["GMA_OK"]
+
+
+def test_workspace_size(lib):
+    d = binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "simt")
+    n = binding.workspace_size(d, False)
+    assert n > 0 and n % 256 == 0
+    # SIMT materialises both responsibility maps: at least 2*B*H*N*K floats
+    assert n >= 2 * 2 * 3 * 64 * 12 * 4
+    bad = binding.make_desc(2, 3, 64, 16, 8, 999, "bf16", 1e-3, "simt")
+    assert binding.workspace_size(bad, False) == 0
+    assert lib.gma_workspace_size(None, 0) == 0
+    assert binding.workspace_size(binding.make_desc(2, 3, 0, 16, 8, 12, "f32", 1e-3), True) == 0
