@@ -185,34 +185,29 @@ def roofline_for(w, per_kernel):
 
 
 def cpu_baseline(w, inp, budget_s=12.0):
-    """The fp64 oracle, as it stands, on a bounded sample of (b, h) slices of the same
-    workload, timed on this host's cores."""
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload (whole batch
+    elements, all heads of each), timed on this host's cores.  The oracle spreads its
+    (b, h) slices over OpenMP threads, so the threads used are min(threads, slices)."""
     import oracle
     threads = oracle.num_threads()
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
 
-    def run(hs):
+    def run(nb, nh=None):
+        nh = w.H if nh is None else nh
         t = time.perf_counter()
-        for b in sorted(set(b for b, _ in hs)):
-            hh = [h for bb, h in hs if bb == b]
-            lo, hi = min(hh), max(hh) + 1
-            oracle.forward(inp["qr"][b:b + 1, lo:hi], inp["kr"][b:b + 1, lo:hi], inp["v"][b:b + 1, lo:hi],
-                           inp["mu"][lo:hi], inp["var_raw"][lo:hi], inp["prior_logits"][lo:hi],
-                           w.causal, w.eps, w.var_floor)
+        oracle.forward(inp["qr"][:nb, :nh], inp["kr"][:nb, :nh], inp["v"][:nb, :nh],
+                       inp["mu"][:nh], inp["var_raw"][:nh], inp["prior_logits"][:nh],
+                       w.causal, w.eps, w.var_floor)
         return time.perf_counter() - t
 
-    # probe with one slice, then size the sample to the time budget (whole rows of heads)
-    t1 = run(heads[:1])
-    per = max(t1, 1e-6)
-    n = int(min(len(heads), max(1, budget_s * threads / per)))
-    n = min(len(heads), max(1, (n // w.H) * w.H if n >= w.H else n))
-    sample = heads[:n]
-    t = run(sample)
-    used = min(threads, n if n < w.H else w.H)
-    return {"value": round(n * w.N / t, 1), "unit": "token-heads/s", "cores": used,
+    per_slice = max(run(1, 1), 1e-6)          # one (b, h) slice on one thread
+    waves = max(1, int(budget_s / per_slice))  # slices each thread can do in the budget
+    nb = int(min(w.B, max(1, (waves * threads) // w.H)))
+    t = run(nb)
+    n = nb * w.H
+    return {"value": round(n * w.N / t, 1), "unit": "token-heads/s", "cores": min(threads, n),
             "kind": "oracle",
-            "sample": f"{n} of {len(heads)} (b,h) slices x N={w.N} (fp64 C oracle, OpenMP over "
-                      f"slices, {t:.2f} s)"}
+            "sample": f"{nb} of {w.B} batch elements x {w.H} heads x N={w.N} "
+                      f"(fp64 C oracle, OpenMP over (b,h) slices, {t:.2f} s)"}
 
 
 def main():

@@ -59,10 +59,10 @@ inline size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAli
 size_t simt_workspace(const gma_desc& d, int causal);
 hipError_t simt_forward(const Args& a);
 // Responsibilities only, written as float32 [2,B,H,N,K]; used for gamma_out by every family.
-hipError_t simt_gamma(const Args& a, float* gamma, const float* lam, const float* cst);
+hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst);
 // Parameter prep of the SIMT family: lam = 1/var [H,K,d_r], cst [H,K] (log prior minus half
-// the log-determinant), both float32.
-hipError_t simt_params(const Args& a, float* lam, float* cst);
+// the log-determinant), both double.
+hipError_t simt_params(const Args& a, double* lam, double* cst);
 size_t simt_param_bytes(const gma_desc& d);
 
 // MFMA family (bf16 inputs): fused matrix-core kernels.

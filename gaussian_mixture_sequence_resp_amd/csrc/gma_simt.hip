@@ -8,7 +8,10 @@
 // This family serves float32 inputs and any supported shape.  The log-density is taken in
 // its direct form, l_k(x) = c_k - 1/2 sum_d (x_d - mu_kd)^2 / var_kd with
 // c_k = log pi_k - 1/2 sum_d log var_kd; the constant (d/2) log 2 pi is the same for every
-// component of a row and cancels in the softmax, so it is not computed.  Responsibilities
+// component of a row and cancels in the softmax, so it is not computed.  Logits reach
+// magnitudes of hundreds while the softmax needs them to ~1e-6 absolute for fp32 parity, so
+// they are accumulated in double (parameters lam, c also kept in double); everything after
+// the max-shift (exp, sums, write, read, scan) is float32.  Responsibilities
 // are materialised in the workspace (float32 [2,B,H,N,K]), then the write and read phases
 // (or the causal scan) consume them.  Every sum runs in ascending index order, so results
 // are deterministic.
@@ -23,13 +26,13 @@ namespace {
 constexpr int kBlock = 256;
 
 // One block per head: lam[h,k,d] = 1/var, cst[h,k] = log pi_k - 1/2 sum_d log var_kd.
-// Computed in double, stored as float.
+// Computed and stored in double.
 __global__ void __launch_bounds__(kBlock) params_kernel(const float* __restrict__ mu,
                                                         const float* __restrict__ var_raw,
                                                         const float* __restrict__ prior, int K,
                                                         int dr, float var_floor,
-                                                        float* __restrict__ lam,
-                                                        float* __restrict__ cst) {
+                                                        double* __restrict__ lam,
+                                                        double* __restrict__ cst) {
     (void)mu;
     const int h = blockIdx.x;
     __shared__ double red[kBlock];
@@ -59,10 +62,10 @@ __global__ void __launch_bounds__(kBlock) params_kernel(const float* __restrict_
             const size_t i = ((size_t)h * K + k) * dr + d;
             const double r = var_raw[i];
             const double var = fmax(r, 0.0) + log1p(exp(-fabs(r))) + (double)var_floor;
-            lam[i] = (float)(1.0 / var);
+            lam[i] = 1.0 / var;
             half_logdet += 0.5 * log(var);
         }
-        cst[(size_t)h * K + k] = (float)((double)prior[(size_t)h * K + k] - lse - half_logdet);
+        cst[(size_t)h * K + k] = (double)prior[(size_t)h * K + k] - lse - half_logdet;
     }
 }
 
@@ -71,8 +74,8 @@ template <typename T>
 __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
                                                       const T* __restrict__ kr,
                                                       const float* __restrict__ mu,
-                                                      const float* __restrict__ lam,
-                                                      const float* __restrict__ cst,
+                                                      const double* __restrict__ lam,
+                                                      const double* __restrict__ cst,
                                                       float* __restrict__ gamma, int BH, int H,
                                                       int N, int dr, int K, int nblk) {
     const int side = blockIdx.y;
@@ -83,21 +86,29 @@ __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
     const T* x = (side == 0 ? qr : kr) + ((size_t)bh * N + n) * dr;
     float* g = gamma + (((size_t)side * BH + bh) * N + n) * K;
     const float* mu_h = mu + (size_t)h * K * dr;
-    const float* lam_h = lam + (size_t)h * K * dr;
-    float m = -INFINITY;
+    const double* lam_h = lam + (size_t)h * K * dr;
+    // pass 1: row max of the logits (double), pass 2: shifted logits -> exp (float)
+    double m = -INFINITY;
     for (int k = 0; k < K; ++k) {
-        float q = 0.0f;
+        double q = 0.0;
         for (int d = 0; d < dr; ++d) {
-            const float diff = Elem<T>::load(x, d) - mu_h[(size_t)k * dr + d];
-            q = fmaf(lam_h[(size_t)k * dr + d] * diff, diff, q);
+            const double diff = (double)Elem<T>::load(x, d) - (double)mu_h[(size_t)k * dr + d];
+            q = fma(lam_h[(size_t)k * dr + d] * diff, diff, q);
         }
-        const float l = cst[(size_t)h * K + k] - 0.5f * q;
-        g[k] = l;
-        m = fmaxf(m, l);
+        const double l = cst[(size_t)h * K + k] - 0.5 * q;
+        m = fmax(m, l);
+    }
+    for (int k = 0; k < K; ++k) {
+        double q = 0.0;
+        for (int d = 0; d < dr; ++d) {
+            const double diff = (double)Elem<T>::load(x, d) - (double)mu_h[(size_t)k * dr + d];
+            q = fma(lam_h[(size_t)k * dr + d] * diff, diff, q);
+        }
+        g[k] = (float)(cst[(size_t)h * K + k] - 0.5 * q - m);
     }
     float s = 0.0f;
     for (int k = 0; k < K; ++k) {
-        const float e = expf(g[k] - m);
+        const float e = expf(g[k]);
         g[k] = e;
         s += e;
     }
@@ -196,9 +207,9 @@ SimtLayout simt_layout(const gma_desc& d) {
     const size_t BH = (size_t)d.B * d.H;
     size_t off = 0;
     L.lam = off;
-    off += align_up((size_t)d.H * d.K * d.d_r * sizeof(float));
+    off += align_up((size_t)d.H * d.K * d.d_r * sizeof(double));
     L.cst = off;
-    off += align_up((size_t)d.H * d.K * sizeof(float));
+    off += align_up((size_t)d.H * d.K * sizeof(double));
     L.gamma = off;
     off += align_up(2 * BH * d.N * d.K * sizeof(float));
     L.mem = off;
@@ -211,8 +222,8 @@ template <typename T>
 hipError_t simt_forward_t(const Args& a) {
     const gma_desc& d = a.d;
     const SimtLayout L = simt_layout(d);
-    float* lam = reinterpret_cast<float*>(a.ws + L.lam);
-    float* cst = reinterpret_cast<float*>(a.ws + L.cst);
+    double* lam = reinterpret_cast<double*>(a.ws + L.lam);
+    double* cst = reinterpret_cast<double*>(a.ws + L.cst);
     float* gamma = a.gamma_out ? a.gamma_out : reinterpret_cast<float*>(a.ws + L.gamma);
     float* mem = reinterpret_cast<float*>(a.ws + L.mem);
     const int BH = d.B * d.H;
@@ -249,12 +260,12 @@ hipError_t simt_forward_t(const Args& a) {
 }  // namespace
 
 size_t simt_param_bytes(const gma_desc& d) {
-    return align_up((size_t)d.H * d.K * d.d_r * sizeof(float)) + align_up((size_t)d.H * d.K * sizeof(float));
+    return align_up((size_t)d.H * d.K * d.d_r * sizeof(double)) + align_up((size_t)d.H * d.K * sizeof(double));
 }
 
 size_t simt_workspace(const gma_desc& d, int /*causal*/) { return simt_layout(d).total; }
 
-hipError_t simt_params(const Args& a, float* lam, float* cst) {
+hipError_t simt_params(const Args& a, double* lam, double* cst) {
     rec_begin(a, "simt_params");
     params_kernel<<<dim3(a.d.H), dim3(kBlock), 0, a.stream>>>(a.mu, a.var_raw, a.prior, a.d.K, a.d.d_r,
                                                               a.d.var_floor, lam, cst);
@@ -262,7 +273,7 @@ hipError_t simt_params(const Args& a, float* lam, float* cst) {
     return hipGetLastError();
 }
 
-hipError_t simt_gamma(const Args& a, float* gamma, const float* lam, const float* cst) {
+hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst) {
     const gma_desc& d = a.d;
     const int BH = d.B * d.H;
     const int nblk = (d.N + kBlock - 1) / kBlock;
