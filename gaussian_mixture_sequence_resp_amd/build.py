@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgma.so")
-SOURCES = ["gma_api.cpp", "gma_simt.hip", "gma_mfma.hip"]
+SOURCES = ["gma_api.cpp", "gma_simt.hip", "gma_mfma.hip", "gma_mfma_causal.hip"]
 ARCH = "gfx950"
 
 
@@ -23,17 +23,33 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every source to an object in parallel, then link libgma.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+             "-Wno-pass-failed", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", os.path.join(HERE, "..", "include")]
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(msgs))
+        if msgs and verbose:
+            print("\n".join(msgs), file=sys.stderr)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(HERE, "..", "include")]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    cmd += ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    subprocess.run(cmd, check=True)
+    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], check=True)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,23 +1,548 @@
-// MFMA family of the GMA forward (bf16 inputs, fused matrix-core kernels).
+// MFMA family of the GMA forward for bf16 inputs (gfx950): parameter prep, the
+// bidirectional write/read kernels and host-side dispatch.
+//
+// Method: Gaussian Mixture Attention (arXiv 2606.18283), "Core mechanism":
+//   item 1 -- Gamma = GMM posterior responsibilities (diagonal Gaussians, softplus
+//             variances, softmax priors; item 3);
+//   item 2 -- write Vt = Gamma_K^T V, Z = Gamma_K^T 1; read O = Gamma_Q Vt / (Gamma_Q Z + eps).
+// Kernels:
+//   gma_prep          coefficients [ah|al|bh|bl] (bf16) and c_k of every head; zeroes the
+//                     split tickets.
+//   gma_bidir_write   Gamma_K tile by tile (logit MFMAs + in-lane softmax), staged in LDS,
+//                     then Gamma_K^T [V | 1] on MFMAs; each workgroup owns one contiguous
+//                     split of the sequence and writes a fp32 partial; the last workgroup of a
+//                     head to finish adds the partials in split order (deterministic) and
+//                     publishes Vt^T (bf16, component order permuted for the read MFMA) and Z.
+//   gma_bidir_read    Gamma_Q tile by tile, unnormalised (2^(l - max)); one MFMA chain gives
+//                     Gamma_Q Vt, Gamma_Q Z and the row sum s together; O = num / (den + eps s).
+// Gamma never leaves the chip in these kernels.
+#include <math.h>
+
 #include "gma_internal.h"
+#include "gma_mfma_common.h"
+#include "gma_mfma_geo.h"
+#include "gma_numeric.h"
 
 namespace gma {
 
-bool mfma_supported(const gma_desc& d, int causal) {
-    (void)d;
-    (void)causal;
+using namespace mf;
+
+namespace {
+
+constexpr int kMaxSplits = 64;
+
+// LDS row strides (bytes) of the token-major staging buffers, padded by 32 B.
+inline int gstride(const Geo& g) { return 2 * g.Kp + 32; }
+inline int vstride(const Geo& g) { return 2 * g.Dvp + 32; }
+inline int vtstride(const Geo& g) { return 2 * g.Kp + 16; }
+
+size_t write_lds_bytes(const Geo& g) {
+    return (size_t)g.Kp * g.wstride + (size_t)g.Kp * 4 + (size_t)kIterT * gstride(g) + (size_t)kIterT * vstride(g);
+}
+size_t read_lds_bytes(const Geo& g) {
+    return (size_t)g.Kp * g.wstride + (size_t)g.Kp * 4 + (size_t)(g.Dvp + 32) * vtstride(g);
+}
+
+int num_splits(const gma_desc& d) {
+    const int bh = d.B * d.H;
+    const int iters = (d.N + kIterT - 1) / kIterT;
+    int s = (256 + bh - 1) / bh;
+    if (s > iters) s = iters;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : s;
+}
+
+struct MfmaLayout {
+    size_t W, C, ticket, part_v, part_z, vt, z, total;
+};
+
+MfmaLayout mfma_layout(const gma_desc& d) {
+    const Geo g = geometry(d);
+    const size_t BH = (size_t)d.B * d.H;
+    const int S = num_splits(d);
+    MfmaLayout L;
+    size_t off = 0;
+    L.W = off;
+    off += align_up((size_t)d.H * g.Kp * 4 * g.Dp * sizeof(bf16_t));
+    L.C = off;
+    off += align_up((size_t)d.H * g.Kp * sizeof(float));
+    L.ticket = off;
+    off += align_up(BH * sizeof(int));
+    L.part_v = off;
+    off += align_up(BH * S * g.Kp * g.Dvp * sizeof(float));
+    L.part_z = off;
+    off += align_up(BH * S * g.Kp * sizeof(float));
+    L.vt = off;
+    off += align_up(BH * g.Dvp * g.Kp * sizeof(bf16_t));
+    L.z = off;
+    off += align_up(BH * g.Kp * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+// ---------------------------------------------------------------------------------- prep
+// One wave per (h, k), lanes over the routing dims: the bf16 hi/lo coefficients and c_k,
+// computed in double.  Threads below n_tickets also clear the split tickets.
+__global__ void __launch_bounds__(256) gma_prep(const float* __restrict__ mu, const float* __restrict__ var_raw,
+                                                const float* __restrict__ prior, int H, int K, int dr, int Kp,
+                                                int Dp, float var_floor, bf16_t* __restrict__ W,
+                                                float* __restrict__ cvec, int* __restrict__ tickets,
+                                                int n_tickets) {
+    const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
+    if (gtid < n_tickets) tickets[gtid] = 0;
+    const int gw = gtid >> 6, lane = threadIdx.x & 63;
+    if (gw >= H * Kp) return;
+    const int h = gw / Kp, k = gw % Kp;
+    bf16_t* row = W + (size_t)gw * 4 * Dp;
+    const double L2E = 1.4426950408889634;
+    double acc = 0.0;
+    for (int dd = lane; dd < Dp; dd += 64) {
+        double a = 0.0, b = 0.0;
+        if (k < K && dd < dr) {
+            const size_t i = ((size_t)h * K + k) * dr + dd;
+            const double r = var_raw[i];
+            const double var = fmax(r, 0.0) + log1p(exp(-fabs(r))) + (double)var_floor;
+            const double lam = 1.0 / var;
+            const double m = mu[i];
+            a = -0.5 * lam * L2E;
+            b = lam * m * L2E;
+            acc += log(var) + m * m * lam;
+        }
+        const bf16_t ah = f32_to_bf16((float)a);
+        const bf16_t al = f32_to_bf16((float)(a - (double)bf16_to_f32(ah)));
+        const bf16_t bh = f32_to_bf16((float)b);
+        const bf16_t bl = f32_to_bf16((float)(b - (double)bf16_to_f32(bh)));
+        row[dd] = ah;
+        row[Dp + dd] = al;
+        row[2 * Dp + dd] = bh;
+        row[3 * Dp + dd] = bl;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0)
+        cvec[gw] = (k < K) ? (float)(L2E * ((double)prior[(size_t)h * K + k] - 0.5 * acc))
+                           : -INFINITY;  // padded component: 2^-inf = 0 responsibility
+}
+
+// ---------------------------------------------------------------------------------- write
+// Raw V values of one token row for this lane: dims 8 half + 16 j, j < NT * 2 (zero-padded).
+template <int NT>
+__device__ __forceinline__ void load_vrow(bf16x8 (&vr)[2 * NT], const bf16_t* row, int dv) {
+    const int half = lane_id() >> 5;
+#pragma unroll
+    for (int j = 0; j < 2 * NT; ++j) {
+        const int d0 = 16 * j + 8 * half;
+        bf16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (row) {
+            if ((dv & 7) == 0) {
+                if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(row + d0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (d0 + e < dv) x[e] = (short)row[d0 + e];
+            }
+        }
+        vr[j] = x;
+    }
+}
+
+template <int MT, int NT, int NC>
+__global__ void __launch_bounds__(kThreads, 1)
+    gma_bidir_write(const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v, const bf16_t* __restrict__ W,
+                    const float* __restrict__ cvec, float* __restrict__ part_v, float* __restrict__ part_z,
+                    int* __restrict__ tickets, bf16_t* __restrict__ vt, float* __restrict__ zout, int BH, int H,
+                    int N, int dr, int dv, int S, int split_len) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int Kp = 32 * MT, Dvp = 32 * NT, Dp = 16 * NC;
+    constexpr int wstride = 8 * Dp + 16;
+    constexpr int gs = 2 * Kp + 32, vs = 2 * Dvp + 32;
+    unsigned char* sW = smem;
+    float* sC = reinterpret_cast<float*>(sW + (size_t)Kp * wstride);
+    unsigned char* sG = reinterpret_cast<unsigned char*>(sC + Kp);
+    unsigned char* sV = sG + (size_t)kIterT * gs;
+
+    int bh, split;
+    head_part(blockIdx.x, BH, S, bh, split);
+    const int h = bh % H;
+    const int l = lane_id(), w = wave_id(), half = l >> 5;
+    const int n_begin = split * split_len;
+    const int n_end = min(N, n_begin + split_len);
+
+    stage_coefficients(sW, sC, W, cvec, h, Kp, Dp, wstride);
+
+    // Output tiles of Gamma_K^T [V | 1]: (m, n) for n < NT, and the ones tile n = NT whose
+    // every column is Z_k.  Dealt to waves in contiguous runs (m-major).
+    constexpr int kTiles = MT * (NT + 1);
+    constexpr int kPerWave = (kTiles + kWaves - 1) / kWaves;
+    f32x16 wacc[kPerWave];
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wacc[j][i] = 0.0f;
+
+    const bf16_t* kr_h = kr + (size_t)bh * N * dr;
+    const bf16_t* v_h = v + (size_t)bh * N * dv;
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (short)0x3f80;
+
+    // registers for the next tile's raw k and v rows (prefetched one iteration ahead)
+    bf16x8 xr[NC], vr[2 * NT];
+    {
+        const int t = n_begin + kTileT * w + (l & 31);
+        load_xrow<NC>(xr, t < n_end ? kr_h + (size_t)t * dr : nullptr, dr);
+        load_vrow<NT>(vr, t < n_end ? v_h + (size_t)t * dv : nullptr, dv);
+    }
+    __syncthreads();
+
+    for (int base = n_begin; base < n_end; base += kIterT) {
+        // ---- this wave's 32 tokens: Gamma_K (normalised) into sG rows 32w .. 32w+31
+        {
+            const int t = base + kTileT * w + (l & 31);
+            const bool valid = t < n_end;
+            bf16x8 xc[NC], vc[2 * NT];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) xc[c] = xr[c];
+#pragma unroll
+            for (int j = 0; j < 2 * NT; ++j) vc[j] = vr[j];
+            const int tn = t + kIterT;
+            load_xrow<NC>(xr, tn < n_end ? kr_h + (size_t)tn * dr : nullptr, dr);
+            load_vrow<NT>(vr, tn < n_end ? v_h + (size_t)tn * dv : nullptr, dv);
+
+            f32x16 acc[MT];
+            tile_logits<MT, NC>(acc, xc, sW, wstride, sC);
+            const float s = tile_exp<MT>(acc);
+            const float inv = valid ? 1.0f / s : 0.0f;
+            unsigned char* grow = sG + (size_t)(kTileT * w + (l & 31)) * gs;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint2 p;
+                    p.x = pack_bf16(acc[m][4 * q] * inv, acc[m][4 * q + 1] * inv);
+                    p.y = pack_bf16(acc[m][4 * q + 2] * inv, acc[m][4 * q + 3] * inv);
+                    *reinterpret_cast<uint2*>(grow + 2 * (32 * m + 8 * q + 4 * half)) = p;
+                }
+            // ---- V rows of the same tokens into sV (zero-padded to Dvp, zero past n_end)
+            unsigned char* vrow = sV + (size_t)(kTileT * w + (l & 31)) * vs;
+#pragma unroll
+            for (int j = 0; j < 2 * NT; ++j)
+                *reinterpret_cast<bf16x8*>(vrow + 2 * (16 * j + 8 * half)) = vc[j];
+        }
+        lds_barrier();
+        // ---- Gamma_K^T [V | 1] over the 128 staged tokens, this wave's output tiles
+#pragma unroll
+        for (int ks = 0; ks < kIterT / 16; ++ks) {
+            int last_m = -1;
+            bf16x8 a;
+#pragma unroll
+            for (int j = 0; j < kPerWave; ++j) {
+                const int tile = w * kPerWave + j;
+                if (tile < kTiles) {
+                    const int m = tile / (NT + 1), n = tile % (NT + 1);
+                    if (m != last_m) {
+                        a = lds_frag_tr(sG, gs, 16 * ks, 32 * m);
+                        last_m = m;
+                    }
+                    const bf16x8 b = (n < NT) ? lds_frag_tr(sV, vs, 16 * ks, 32 * n) : ones;
+                    wacc[j] = mfma(a, b, wacc[j]);
+                }
+            }
+        }
+        lds_barrier();
+    }
+
+    // ---- partial of this split -> workspace (fp32)
+    float* pv = part_v + ((size_t)bh * S + split) * Kp * Dvp;
+    float* pz = part_z + ((size_t)bh * S + split) * Kp;
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+        const int tile = w * kPerWave + j;
+        if (tile >= kTiles) break;
+        const int m = tile / (NT + 1), n = tile % (NT + 1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int k = 32 * m + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (n < NT)
+                pv[(size_t)k * Dvp + 32 * n + (l & 31)] = wacc[j][i];
+            else if ((l & 31) == 0)
+                pz[k] = wacc[j][i];
+        }
+    }
+    // ---- last workgroup of this head adds the splits in order and publishes the memory
+    __shared__ int s_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = (atomicAdd(&tickets[bh], 1) == S - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const float* pv0 = part_v + (size_t)bh * S * Kp * Dvp;
+    const float* pz0 = part_z + (size_t)bh * S * Kp;
+    bf16_t* vt_h = vt + (size_t)bh * Dvp * Kp;
+    for (int idx = threadIdx.x; idx < Kp * Dvp; idx += blockDim.x) {
+        const int dd = idx / Kp, p = idx % Kp;  // output-major: coalesced stores
+        const int k = (p & ~15) + kperm(p & 15);
+        float acc = 0.0f;
+        for (int s = 0; s < S; ++s) acc += pv0[(size_t)s * Kp * Dvp + (size_t)k * Dvp + dd];
+        vt_h[idx] = f32_to_bf16(acc);
+    }
+    for (int k = threadIdx.x; k < Kp; k += blockDim.x) {
+        float acc = 0.0f;
+        for (int s = 0; s < S; ++s) acc += pz0[(size_t)s * Kp + k];
+        zout[(size_t)bh * Kp + k] = acc;
+    }
+    if (threadIdx.x == 0) tickets[bh] = 0;
+}
+
+// ---------------------------------------------------------------------------------- read
+constexpr int kReadWaves = 8;  // two waves per SIMD: one computes exponentials while the other
+                               // runs its MFMAs
+
+template <int MT, int NT, int NC>
+__global__ void __launch_bounds__(64 * kReadWaves, 2)
+    gma_bidir_read(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ W, const float* __restrict__ cvec,
+                   const bf16_t* __restrict__ vt, const float* __restrict__ zin, bf16_t* __restrict__ out,
+                   float eps, int BH, int H, int N, int dr, int dv, int parts, int part_len) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int Kp = 32 * MT, Dvp = 32 * NT, Dp = 16 * NC;
+    constexpr int wstride = 8 * Dp + 16;
+    constexpr int ts = 2 * Kp + 16;
+    unsigned char* sW = smem;
+    float* sC = reinterpret_cast<float*>(sW + (size_t)Kp * wstride);
+    unsigned char* sT = reinterpret_cast<unsigned char*>(sC + Kp);  // (Dvp + 32) rows x Kp
+
+    int bh, part;
+    head_part(blockIdx.x, BH, parts, bh, part);
+    const int h = bh % H;
+    const int l = lane_id(), w = wave_id(), half = l >> 5;
+    const bf16_t* q_h = qr + (size_t)bh * N * dr;
+    bf16_t* o_h = out + (size_t)bh * N * dv;
+    const int n_begin = part * part_len;
+    const int n_end = min(N, n_begin + part_len);
+    constexpr int kStep = kTileT * kReadWaves;
+
+    bf16x8 xr[NC];
+    {
+        const int t = n_begin + kTileT * w + (l & 31);
+        load_xrow<NC>(xr, t < n_end ? q_h + (size_t)t * dr : nullptr, dr);
+    }
+
+    stage_coefficients(sW, sC, W, cvec, h, Kp, Dp, wstride);
+    // memory rows: Vt^T (Dvp rows), then Z hi (8 rows), Z lo (8 rows), ones (16 rows);
+    // columns in the permuted component order of the logits tiles
+    const bf16_t* vt_h = vt + (size_t)bh * Dvp * Kp;
+    for (int i = threadIdx.x; i < Dvp * Kp / 8; i += blockDim.x) {
+        const int r = i / (Kp / 8), c = i % (Kp / 8);
+        *reinterpret_cast<bf16x8*>(sT + (size_t)r * ts + 16 * c) =
+            *reinterpret_cast<const bf16x8*>(vt_h + (size_t)r * Kp + 8 * c);
+    }
+    for (int i = threadIdx.x; i < 32 * Kp; i += blockDim.x) {
+        const int r = i / Kp, p = i % Kp;
+        const int k = (p & ~15) + kperm(p & 15);
+        const float z = zin[(size_t)bh * Kp + k];
+        const bf16_t zh = f32_to_bf16(z);
+        bf16_t val;
+        if (r < 8) val = zh;
+        else if (r < 16) val = f32_to_bf16(z - bf16_to_f32(zh));
+        else val = (bf16_t)0x3f80;
+        *reinterpret_cast<bf16_t*>(sT + (size_t)(Dvp + r) * ts + 2 * p) = val;
+    }
+    __syncthreads();
+
+    for (int base = n_begin + kTileT * w; base < n_end; base += kStep) {
+        const int t = base + (l & 31);
+        const bool valid = t < n_end;
+        f32x16 acc[MT];
+        tile_logits<MT, NC>(acc, xr, sW, wstride, sC);
+        // next tile's routing rows: in flight during the softmax and the read MFMAs
+        const int tn = t + kStep;
+        load_xrow<NC>(xr, tn < n_end ? q_h + (size_t)tn * dr : nullptr, dr);
+        (void)tile_exp<MT>(acc);  // unnormalised; the row sum comes out of the MFMAs below
+        f32x16 o[NT + 1];
+#pragma unroll
+        for (int n = 0; n <= NT; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[n][i] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) {
+                u32x4 bp;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bp[j] = pack_bf16(acc[m][8 * sh + 2 * j], acc[m][8 * sh + 2 * j + 1]);
+                const bf16x8 b = __builtin_bit_cast(bf16x8, bp);
+                const int kcol = 32 * m + 16 * sh + 8 * half;
+#pragma unroll
+                for (int n = 0; n <= NT; ++n) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sT + (size_t)(32 * n + (l & 31)) * ts + 2 * kcol);
+                    o[n] = mfma(a, b, o[n]);
+                }
+            }
+        // o[NT]: rows 0-7 Gamma_Q Z_hi, 8-15 Gamma_Q Z_lo, 16-31 row sum s
+        const float den = o[NT][0] + o[NT][4];
+        const float s = o[NT][8];
+        const float inv = 1.0f / (den + eps * s);
+        if (valid) {
+            bf16_t* orow = o_h + (size_t)t * dv;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int d0 = 32 * n + 8 * q + 4 * half;
+                    if ((dv & 3) == 0) {
+                        if (d0 < dv) {
+                            uint2 p;
+                            p.x = pack_bf16(o[n][4 * q] * inv, o[n][4 * q + 1] * inv);
+                            p.y = pack_bf16(o[n][4 * q + 2] * inv, o[n][4 * q + 3] * inv);
+                            *reinterpret_cast<uint2*>(orow + d0) = p;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (d0 + r < dv) orow[d0 + r] = (bf16_t)bf16_bits_rne(o[n][4 * q + r] * inv);
+                    }
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------- host
+typedef void (*WriteFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, float*, float*, int*, bf16_t*,
+                        float*, int, int, int, int, int, int, int);
+typedef void (*ReadFn)(const bf16_t*, const bf16_t*, const float*, const bf16_t*, const float*, bf16_t*, float, int,
+                       int, int, int, int, int, int);
+
+template <int MT, int NT, int NC>
+bool pick(WriteFn& wf, ReadFn& rf) {
+    wf = gma_bidir_write<MT, NT, NC>;
+    rf = gma_bidir_read<MT, NT, NC>;
+    return true;
+}
+
+template <int MT, int NT>
+bool select_nc(int NC, WriteFn& wf, ReadFn& rf) {
+    switch (NC) {
+        case 1: return pick<MT, NT, 1>(wf, rf);
+        case 2: return pick<MT, NT, 2>(wf, rf);
+        case 4: return pick<MT, NT, 4>(wf, rf);
+        case 8: return pick<MT, NT, 8>(wf, rf);
+    }
     return false;
 }
 
+template <int MT>
+bool select_nt(int NT, int NC, WriteFn& wf, ReadFn& rf) {
+    switch (NT) {
+        case 1: return select_nc<MT, 1>(NC, wf, rf);
+        case 2: return select_nc<MT, 2>(NC, wf, rf);
+        case 4: return select_nc<MT, 4>(NC, wf, rf);
+    }
+    return false;
+}
+
+bool select(const Geo& g, WriteFn& wf, ReadFn& rf) {
+    switch (g.MT) {
+        case 1: return select_nt<1>(g.NT, g.NC, wf, rf);
+        case 2: return select_nt<2>(g.NT, g.NC, wf, rf);
+        case 4: return select_nt<4>(g.NT, g.NC, wf, rf);
+        case 8: return select_nt<8>(g.NT, g.NC, wf, rf);
+    }
+    return false;
+}
+
+}  // namespace
+
+hipError_t mf::launch_prep(const Args& a, const Geo& g, bf16_t* W, float* cvec, int* tickets, int n_tickets) {
+    const gma_desc& d = a.d;
+    const long waves = (long)d.H * g.Kp;
+    const long threads = waves * 64 > n_tickets ? waves * 64 : n_tickets;
+    rec_begin(a, "gma_prep");
+    gma_prep<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, a.stream>>>(
+        a.mu, a.var_raw, a.prior, d.H, d.K, d.d_r, g.Kp, g.Dp, d.var_floor, W, cvec, tickets, n_tickets);
+    rec_end(a);
+    return hipGetLastError();
+}
+
+bool mfma_supported(const gma_desc& d, int causal) {
+    if (d.dtype != GMA_BF16) return false;
+    if (causal) return causal_supported(d);
+    const Geo g = geometry(d);
+    return write_lds_bytes(g) <= kLdsMax && read_lds_bytes(g) <= kLdsMax;
+}
+
 size_t mfma_workspace(const gma_desc& d, int causal) {
-    (void)d;
-    (void)causal;
-    return 0;
+    // + room for the float64 parameters of the optional gamma_out diagnostic
+    if (causal) return causal_workspace(d) + simt_param_bytes(d);
+    return mfma_layout(d).total + simt_param_bytes(d);
+}
+
+static hipError_t bidir_forward(const Args& a) {
+    const gma_desc& d = a.d;
+    const Geo g = geometry(d);
+    const MfmaLayout L = mfma_layout(d);
+    bf16_t* W = reinterpret_cast<bf16_t*>(a.ws + L.W);
+    float* cvec = reinterpret_cast<float*>(a.ws + L.C);
+    int* tickets = reinterpret_cast<int*>(a.ws + L.ticket);
+    float* part_v = reinterpret_cast<float*>(a.ws + L.part_v);
+    float* part_z = reinterpret_cast<float*>(a.ws + L.part_z);
+    bf16_t* vt = reinterpret_cast<bf16_t*>(a.ws + L.vt);
+    float* z = reinterpret_cast<float*>(a.ws + L.z);
+    const int BH = d.B * d.H;
+    hipError_t e;
+
+    WriteFn wf;
+    ReadFn rf;
+    if (!select(g, wf, rf)) return hipErrorNotSupported;
+
+    if ((e = launch_prep(a, g, W, cvec, tickets, BH)) != hipSuccess) return e;
+
+    const int S = num_splits(d);
+    const int split_len = ((d.N + S - 1) / S + kIterT - 1) / kIterT * kIterT;
+    const size_t wl = write_lds_bytes(g);
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(wf), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)wl)) != hipSuccess)
+        return e;
+    rec_begin(a, "gma_bidir_write");
+    hipLaunchKernelGGL(wf, dim3(BH * S), dim3(kThreads), wl, a.stream, static_cast<const bf16_t*>(a.kr),
+                       static_cast<const bf16_t*>(a.v), W, cvec, part_v, part_z, tickets, vt, z, BH, d.H, d.N,
+                       d.d_r, d.d_v, S, split_len);
+    rec_end(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    // read: about one workgroup per CU, each a contiguous run of the sequence of one head
+    const int step = kTileT * kReadWaves;
+    int parts = (256 + BH - 1) / BH;
+    const int max_parts = (d.N + step - 1) / step;
+    if (parts > max_parts) parts = max_parts;
+    if (parts < 1) parts = 1;
+    const int part_len = ((d.N + parts - 1) / parts + step - 1) / step * step;
+    parts = (d.N + part_len - 1) / part_len;
+    const size_t rl = read_lds_bytes(g);
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(rf), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)rl)) != hipSuccess)
+        return e;
+    rec_begin(a, "gma_bidir_read");
+    hipLaunchKernelGGL(rf, dim3(BH * parts), dim3(64 * kReadWaves), rl, a.stream, static_cast<const bf16_t*>(a.qr),
+                       W, cvec, vt, z, static_cast<bf16_t*>(a.out), a.eps, BH, d.H, d.N, d.d_r, d.d_v, parts,
+                       part_len);
+    rec_end(a);
+    return hipGetLastError();
 }
 
 hipError_t mfma_forward(const Args& a) {
-    (void)a;
-    return hipErrorNotSupported;
+    const gma_desc& d = a.d;
+    hipError_t e = a.causal ? causal_forward(a) : bidir_forward(a);
+    if (e != hipSuccess) return e;
+    if (a.gamma_out) {
+        // diagnostic responsibilities (float32), outside the fused path
+        const size_t off = a.causal ? causal_workspace(d) : mfma_layout(d).total;
+        double* lam = reinterpret_cast<double*>(a.ws + off);
+        double* cst = reinterpret_cast<double*>(a.ws + off + align_up((size_t)d.H * d.K * d.d_r * sizeof(double)));
+        if ((e = simt_params(a, lam, cst)) != hipSuccess) return e;
+        if ((e = simt_gamma(a, a.gamma_out, lam, cst)) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gma
