@@ -6,9 +6,10 @@
 A step is one full forward (parameter prep, responsibilities, write and read -- or the
 causal scan) over one batch of seeded synthetic inputs already resident in HBM.  W
 untimed warm-up steps, then exactly K timed steps bracketed by torch.cuda.synchronize()
-on both sides.  Each timed step runs through gma_forward_timed, which records a HIP
-event pair on the launch stream around every kernel, so per-kernel durations come from
-the same timed region.  Prints one JSON line.
+on both sides.  The same K steps are then run once more through gma_forward_timed, which
+records a HIP event pair on the launch stream around every kernel; those events give each
+kernel's average duration (the roofline's denominator), without their recording overhead
+entering the headline time.  Prints one JSON line.
 
 value = whole-job throughput in token-heads/s (B*H*N / seconds per step).  The
 default workload is the bidirectional bf16 K=128 workload (B=8, H=8, N=4096,
@@ -134,29 +135,31 @@ def run_workload(w, steps, warmup):
 
     for _ in range(warmup):
         step()
+    # timed region: exactly `steps` plain forwards (no instrumentation)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    # the same `steps` forwards again through gma_forward_timed: a HIP event pair on the
+    # launch stream around every kernel gives each kernel's duration
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
     for i in range(steps):
         step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    t3 = time.perf_counter()
     nk = gma.forward.last_kernel_count
     per_kernel = {}
     for j in range(min(nk, max_k)):
         name = names[j].decode()
         ts = [elapsed_ms(hip, evs[2 * max_k * i + 2 * j], evs[2 * max_k * i + 2 * j + 1]) for i in range(steps)]
         per_kernel[name] = sum(ts) / len(ts)
-    # the same K steps without event recording, for reference
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
     for e in evs:
         hip.hipEventDestroy(e)
     return {"ms_per_step": (t1 - t0) * 1e3 / steps,
-            "ms_per_step_no_events": (t3 - t2) * 1e3 / steps,
+            "ms_per_step_with_events": (t3 - t2) * 1e3 / steps,
             "per_kernel_ms": per_kernel,
             "workspace_bytes": need,
             "inputs": inp}
@@ -218,6 +221,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-causal", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the measurement, copy one 256 MiB device buffer, so that a profiler's "
+                         "memory counters can be scaled by a copy of known size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GMA forward here has no multi-GPU path "
@@ -245,7 +251,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d_r": w.d_r, "d_v": w.d_v,
                    "K": w.K, "causal": w.causal, "global_batch": w.B, "seq_len": w.N,
                    "parallelism": "none (1 GPU)"},
-        "ms_per_step_no_events": round(r["ms_per_step_no_events"], 5),
+        "ms_per_step_with_events": round(r["ms_per_step_with_events"], 5),
         "per_kernel_ms": {k: round(v, 5) for k, v in r["per_kernel_ms"].items()},
         "workspace_bytes": r["workspace_bytes"],
         "roofline": roofline_for(w, r["per_kernel_ms"]),
@@ -260,6 +266,14 @@ def main():
                           "value": round(wc.token_heads / (rc["ms_per_step"] * 1e-3), 1),
                           "per_kernel_ms": {k: round(v, 5) for k, v in rc["per_kernel_ms"].items()},
                           "roofline": roofline_for(wc, rc["per_kernel_ms"])}
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = src.numel()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inputs"])
     print(json.dumps(line), flush=True)

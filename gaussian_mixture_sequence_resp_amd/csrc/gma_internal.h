@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/gma.h"
+#include "gma.h"
 
 namespace gma {
 

@@ -6,14 +6,13 @@
 //             variances, softmax priors; item 3);
 //   item 2 -- write Vt = Gamma_K^T V, Z = Gamma_K^T 1; read O = Gamma_Q Vt / (Gamma_Q Z + eps).
 // Kernels:
-//   gma_prep          coefficients [ah|al|bh|bl] (bf16) and c_k of every head; zeroes the
-//                     split tickets.
+//   gma_prep          coefficients [ah|al|bh|bl] (bf16) and c_k of every head.
 //   gma_bidir_write   Gamma_K tile by tile (logit MFMAs + in-lane softmax), staged in LDS,
 //                     then Gamma_K^T [V | 1] on MFMAs; each workgroup owns one contiguous
-//                     split of the sequence and writes a fp32 partial; the last workgroup of a
-//                     head to finish adds the partials in split order (deterministic) and
-//                     publishes Vt^T (bf16, component order permuted for the read MFMA) and Z.
-//   gma_bidir_read    Gamma_Q tile by tile, unnormalised (2^(l - max)); one MFMA chain gives
+//                     split of the sequence and writes a fp32 partial of [Vt | Z].
+//   gma_bidir_read    adds the split partials of its head in split order (deterministic; no
+//                     cross-workgroup synchronisation), stages Vt^T and Z in LDS, then
+//                     Gamma_Q tile by tile, unnormalised (2^(l - max)); one MFMA chain gives
 //                     Gamma_Q Vt, Gamma_Q Z and the row sum s together; O = num / (den + eps s).
 // Gamma never leaves the chip in these kernels.
 #include <math.h>
@@ -53,7 +52,7 @@ int num_splits(const gma_desc& d) {
 }
 
 struct MfmaLayout {
-    size_t W, C, ticket, part_v, part_z, vt, z, total;
+    size_t W, C, part_v, part_z, total;
 };
 
 MfmaLayout mfma_layout(const gma_desc& d) {
@@ -66,30 +65,22 @@ MfmaLayout mfma_layout(const gma_desc& d) {
     off += align_up((size_t)d.H * g.Kp * 4 * g.Dp * sizeof(bf16_t));
     L.C = off;
     off += align_up((size_t)d.H * g.Kp * sizeof(float));
-    L.ticket = off;
-    off += align_up(BH * sizeof(int));
     L.part_v = off;
     off += align_up(BH * S * g.Kp * g.Dvp * sizeof(float));
     L.part_z = off;
     off += align_up(BH * S * g.Kp * sizeof(float));
-    L.vt = off;
-    off += align_up(BH * g.Dvp * g.Kp * sizeof(bf16_t));
-    L.z = off;
-    off += align_up(BH * g.Kp * sizeof(float));
     L.total = off;
     return L;
 }
 
 // ---------------------------------------------------------------------------------- prep
 // One wave per (h, k), lanes over the routing dims: the bf16 hi/lo coefficients and c_k,
-// computed in double.  Threads below n_tickets also clear the split tickets.
+// computed in double.
 __global__ void __launch_bounds__(256) gma_prep(const float* __restrict__ mu, const float* __restrict__ var_raw,
                                                 const float* __restrict__ prior, int H, int K, int dr, int Kp,
                                                 int Dp, float var_floor, bf16_t* __restrict__ W,
-                                                float* __restrict__ cvec, int* __restrict__ tickets,
-                                                int n_tickets) {
+                                                float* __restrict__ cvec) {
     const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
-    if (gtid < n_tickets) tickets[gtid] = 0;
     const int gw = gtid >> 6, lane = threadIdx.x & 63;
     if (gw >= H * Kp) return;
     const int h = gw / Kp, k = gw % Kp;
@@ -149,9 +140,8 @@ __device__ __forceinline__ void load_vrow(bf16x8 (&vr)[2 * NT], const bf16_t* ro
 template <int MT, int NT, int NC>
 __global__ void __launch_bounds__(kThreads, 1)
     gma_bidir_write(const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v, const bf16_t* __restrict__ W,
-                    const float* __restrict__ cvec, float* __restrict__ part_v, float* __restrict__ part_z,
-                    int* __restrict__ tickets, bf16_t* __restrict__ vt, float* __restrict__ zout, int BH, int H,
-                    int N, int dr, int dv, int S, int split_len) {
+                    const float* __restrict__ cvec, float* __restrict__ part_v, float* __restrict__ part_z, int BH,
+                    int H, int N, int dr, int dv, int S, int split_len) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int Kp = 32 * MT, Dvp = 32 * NT, Dp = 16 * NC;
     constexpr int wstride = 8 * Dp + 16;
@@ -269,30 +259,6 @@ __global__ void __launch_bounds__(kThreads, 1)
                 pz[k] = wacc[j][i];
         }
     }
-    // ---- last workgroup of this head adds the splits in order and publishes the memory
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(&tickets[bh], 1) == S - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const float* pv0 = part_v + (size_t)bh * S * Kp * Dvp;
-    const float* pz0 = part_z + (size_t)bh * S * Kp;
-    bf16_t* vt_h = vt + (size_t)bh * Dvp * Kp;
-    for (int idx = threadIdx.x; idx < Kp * Dvp; idx += blockDim.x) {
-        const int dd = idx / Kp, p = idx % Kp;  // output-major: coalesced stores
-        const int k = (p & ~15) + kperm(p & 15);
-        float acc = 0.0f;
-        for (int s = 0; s < S; ++s) acc += pv0[(size_t)s * Kp * Dvp + (size_t)k * Dvp + dd];
-        vt_h[idx] = f32_to_bf16(acc);
-    }
-    for (int k = threadIdx.x; k < Kp; k += blockDim.x) {
-        float acc = 0.0f;
-        for (int s = 0; s < S; ++s) acc += pz0[(size_t)s * Kp + k];
-        zout[(size_t)bh * Kp + k] = acc;
-    }
-    if (threadIdx.x == 0) tickets[bh] = 0;
 }
 
 // ---------------------------------------------------------------------------------- read
@@ -302,8 +268,8 @@ constexpr int kReadWaves = 8;  // two waves per SIMD: one computes exponentials 
 template <int MT, int NT, int NC>
 __global__ void __launch_bounds__(64 * kReadWaves, 2)
     gma_bidir_read(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ W, const float* __restrict__ cvec,
-                   const bf16_t* __restrict__ vt, const float* __restrict__ zin, bf16_t* __restrict__ out,
-                   float eps, int BH, int H, int N, int dr, int dv, int parts, int part_len) {
+                   const float* __restrict__ part_v, const float* __restrict__ part_z, bf16_t* __restrict__ out,
+                   float eps, int BH, int H, int N, int dr, int dv, int S, int parts, int part_len) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int Kp = 32 * MT, Dvp = 32 * NT, Dp = 16 * NC;
     constexpr int wstride = 8 * Dp + 16;
@@ -331,22 +297,60 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
     stage_coefficients(sW, sC, W, cvec, h, Kp, Dp, wstride);
     // memory rows: Vt^T (Dvp rows), then Z hi (8 rows), Z lo (8 rows), ones (16 rows);
     // columns in the permuted component order of the logits tiles
-    const bf16_t* vt_h = vt + (size_t)bh * Dvp * Kp;
-    for (int i = threadIdx.x; i < Dvp * Kp / 8; i += blockDim.x) {
-        const int r = i / (Kp / 8), c = i % (Kp / 8);
-        *reinterpret_cast<bf16x8*>(sT + (size_t)r * ts + 16 * c) =
-            *reinterpret_cast<const bf16x8*>(vt_h + (size_t)r * Kp + 8 * c);
-    }
-    for (int i = threadIdx.x; i < 32 * Kp; i += blockDim.x) {
-        const int r = i / Kp, p = i % Kp;
-        const int k = (p & ~15) + kperm(p & 15);
-        const float z = zin[(size_t)bh * Kp + k];
-        const bf16_t zh = f32_to_bf16(z);
-        bf16_t val;
-        if (r < 8) val = zh;
-        else if (r < 16) val = f32_to_bf16(z - bf16_to_f32(zh));
-        else val = (bf16_t)0x3f80;
-        *reinterpret_cast<bf16_t*>(sT + (size_t)(Dvp + r) * ts + 2 * p) = val;
+    // the head's memory [Vt | Z] = sum of the S split partials of the write kernel, added in
+    // split order (every workgroup of the head forms the identical sum); loads of one split are
+    // issued together.  Vt^T goes to LDS rows 0..Dvp-1 in the permuted component order.
+    {
+        constexpr int kThr = 64 * kReadWaves;
+        constexpr int kVec = Kp * Dvp / 4;
+        constexpr int P = (kVec + kThr - 1) / kThr;
+        const float* pv0 = part_v + (size_t)bh * S * Kp * Dvp;
+        const float* pz0 = part_z + (size_t)bh * S * Kp;
+        float4 sum[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) sum[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        float zsum = 0.0f;
+        for (int s = 0; s < S; ++s) {
+            const float4* src = reinterpret_cast<const float4*>(pv0 + (size_t)s * Kp * Dvp);
+            float4 x[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int i = threadIdx.x + p * kThr;
+                if (i < kVec) x[p] = src[i];
+            }
+            const float zx = ((int)threadIdx.x < Kp) ? pz0[(size_t)s * Kp + threadIdx.x] : 0.0f;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                sum[p].x += x[p].x;
+                sum[p].y += x[p].y;
+                sum[p].z += x[p].z;
+                sum[p].w += x[p].w;
+            }
+            zsum += zx;
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int i = threadIdx.x + p * kThr;
+            if (i < kVec) {
+                const int k = i / (Dvp / 4), d0 = 4 * (i % (Dvp / 4));
+                const int pos = (k & ~15) + kperm(k & 15);
+                *reinterpret_cast<bf16_t*>(sT + (size_t)(d0 + 0) * ts + 2 * pos) = f32_to_bf16(sum[p].x);
+                *reinterpret_cast<bf16_t*>(sT + (size_t)(d0 + 1) * ts + 2 * pos) = f32_to_bf16(sum[p].y);
+                *reinterpret_cast<bf16_t*>(sT + (size_t)(d0 + 2) * ts + 2 * pos) = f32_to_bf16(sum[p].z);
+                *reinterpret_cast<bf16_t*>(sT + (size_t)(d0 + 3) * ts + 2 * pos) = f32_to_bf16(sum[p].w);
+            }
+        }
+        // Z hi (8 rows), Z lo (8 rows), ones (16 rows) below Vt^T
+        if ((int)threadIdx.x < Kp) {
+            const int k = threadIdx.x;
+            const bf16_t zh = f32_to_bf16(zsum);
+            const bf16_t zl = f32_to_bf16(zsum - bf16_to_f32(zh));
+            const int pos = (k & ~15) + kperm(k & 15);
+#pragma unroll
+            for (int r = 0; r < 32; ++r)
+                *reinterpret_cast<bf16_t*>(sT + (size_t)(Dvp + r) * ts + 2 * pos) =
+                    r < 8 ? zh : (r < 16 ? zl : (bf16_t)0x3f80);
+        }
     }
     __syncthreads();
 
@@ -408,10 +412,10 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
 }
 
 // ---------------------------------------------------------------------------------- host
-typedef void (*WriteFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, float*, float*, int*, bf16_t*,
-                        float*, int, int, int, int, int, int, int);
-typedef void (*ReadFn)(const bf16_t*, const bf16_t*, const float*, const bf16_t*, const float*, bf16_t*, float, int,
-                       int, int, int, int, int, int);
+typedef void (*WriteFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, float*, float*, int, int, int,
+                        int, int, int, int);
+typedef void (*ReadFn)(const bf16_t*, const bf16_t*, const float*, const float*, const float*, bf16_t*, float, int,
+                       int, int, int, int, int, int, int);
 
 template <int MT, int NT, int NC>
 bool pick(WriteFn& wf, ReadFn& rf) {
@@ -453,13 +457,12 @@ bool select(const Geo& g, WriteFn& wf, ReadFn& rf) {
 
 }  // namespace
 
-hipError_t mf::launch_prep(const Args& a, const Geo& g, bf16_t* W, float* cvec, int* tickets, int n_tickets) {
+hipError_t mf::launch_prep(const Args& a, const Geo& g, bf16_t* W, float* cvec) {
     const gma_desc& d = a.d;
-    const long waves = (long)d.H * g.Kp;
-    const long threads = waves * 64 > n_tickets ? waves * 64 : n_tickets;
+    const long threads = (long)d.H * g.Kp * 64;
     rec_begin(a, "gma_prep");
     gma_prep<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, a.stream>>>(
-        a.mu, a.var_raw, a.prior, d.H, d.K, d.d_r, g.Kp, g.Dp, d.var_floor, W, cvec, tickets, n_tickets);
+        a.mu, a.var_raw, a.prior, d.H, d.K, d.d_r, g.Kp, g.Dp, d.var_floor, W, cvec);
     rec_end(a);
     return hipGetLastError();
 }
@@ -483,11 +486,8 @@ static hipError_t bidir_forward(const Args& a) {
     const MfmaLayout L = mfma_layout(d);
     bf16_t* W = reinterpret_cast<bf16_t*>(a.ws + L.W);
     float* cvec = reinterpret_cast<float*>(a.ws + L.C);
-    int* tickets = reinterpret_cast<int*>(a.ws + L.ticket);
     float* part_v = reinterpret_cast<float*>(a.ws + L.part_v);
     float* part_z = reinterpret_cast<float*>(a.ws + L.part_z);
-    bf16_t* vt = reinterpret_cast<bf16_t*>(a.ws + L.vt);
-    float* z = reinterpret_cast<float*>(a.ws + L.z);
     const int BH = d.B * d.H;
     hipError_t e;
 
@@ -495,7 +495,7 @@ static hipError_t bidir_forward(const Args& a) {
     ReadFn rf;
     if (!select(g, wf, rf)) return hipErrorNotSupported;
 
-    if ((e = launch_prep(a, g, W, cvec, tickets, BH)) != hipSuccess) return e;
+    if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
 
     const int S = num_splits(d);
     const int split_len = ((d.N + S - 1) / S + kIterT - 1) / kIterT * kIterT;
@@ -505,8 +505,8 @@ static hipError_t bidir_forward(const Args& a) {
         return e;
     rec_begin(a, "gma_bidir_write");
     hipLaunchKernelGGL(wf, dim3(BH * S), dim3(kThreads), wl, a.stream, static_cast<const bf16_t*>(a.kr),
-                       static_cast<const bf16_t*>(a.v), W, cvec, part_v, part_z, tickets, vt, z, BH, d.H, d.N,
-                       d.d_r, d.d_v, S, split_len);
+                       static_cast<const bf16_t*>(a.v), W, cvec, part_v, part_z, BH, d.H, d.N, d.d_r, d.d_v, S,
+                       split_len);
     rec_end(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -524,8 +524,8 @@ static hipError_t bidir_forward(const Args& a) {
         return e;
     rec_begin(a, "gma_bidir_read");
     hipLaunchKernelGGL(rf, dim3(BH * parts), dim3(64 * kReadWaves), rl, a.stream, static_cast<const bf16_t*>(a.qr),
-                       W, cvec, vt, z, static_cast<bf16_t*>(a.out), a.eps, BH, d.H, d.N, d.d_r, d.d_v, parts,
-                       part_len);
+                       W, cvec, part_v, part_z, static_cast<bf16_t*>(a.out), a.eps, BH, d.H, d.N, d.d_r, d.d_v, S,
+                       parts, part_len);
     rec_end(a);
     return hipGetLastError();
 }

@@ -93,11 +93,26 @@ __device__ __forceinline__ void stage_coefficient_chunks(unsigned char* sW, floa
     const bf16_t* src = W + (size_t)h * Kp * 4 * Dp;
     const int vec_per_piece = 2 * ncp;  // 16-byte vectors per piece of a row
     const int per_row = 4 * vec_per_piece;
-    for (int i = threadIdx.x; i < Kp * per_row; i += blockDim.x) {
-        const int r = i / per_row, rem = i % per_row;
-        const int piece = rem / vec_per_piece, v = rem % vec_per_piece;
-        *reinterpret_cast<bf16x8*>(sW + (size_t)r * wstride + 16 * (piece * vec_per_piece + v)) =
-            *reinterpret_cast<const bf16x8*>(src + (size_t)r * 4 * Dp + piece * Dp + 16 * c0 + 8 * v);
+    const int total = Kp * per_row;
+    for (int i0 = threadIdx.x; i0 < total; i0 += 8 * blockDim.x) {
+        bf16x8 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * blockDim.x;
+            if (i < total) {
+                const int r = i / per_row, rem = i % per_row;
+                const int piece = rem / vec_per_piece, vv = rem % vec_per_piece;
+                v[u] = *reinterpret_cast<const bf16x8*>(src + (size_t)r * 4 * Dp + piece * Dp + 16 * c0 + 8 * vv);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * blockDim.x;
+            if (i < total) {
+                const int r = i / per_row, rem = i % per_row;
+                *reinterpret_cast<bf16x8*>(sW + (size_t)r * wstride + 16 * rem) = v[u];
+            }
+        }
     }
     for (int i = threadIdx.x; i < Kp; i += blockDim.x) sC[i] = cvec[(size_t)h * Kp + i];
 }
@@ -291,10 +306,15 @@ __global__ void __launch_bounds__(256) gma_causal_carry(float* __restrict__ carr
     const size_t bh = idx / per, e = idx % per;
     float* c = carry + bh * S * per + e;
     float run = 0.0f;
-    for (int s = 0; s < S; ++s) {
-        const float t = (s < S - 1) ? c[(size_t)s * per] : 0.0f;
-        c[(size_t)s * per] = run;
-        run += t;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+        float t[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t[u] = (s0 + u < S - 1) ? c[(size_t)(s0 + u) * per] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (s0 + u < S) c[(size_t)(s0 + u) * per] = run;
+            run += t[u];
+        }
     }
 }
 
@@ -557,7 +577,7 @@ hipError_t causal_forward(const Args& a) {
     ScanFn sf;
     if (!rf || !select_scan(g, tf, sf)) return hipErrorNotSupported;
 
-    if ((e = launch_prep(a, g, W, cvec, nullptr, 0)) != hipSuccess) return e;
+    if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
 
     // responsibilities of both sides, ~2 workgroups per CU
     int parts = (512 + BH - 1) / BH;

@@ -35,15 +35,26 @@ inline Geo geometry(const gma_desc& d) {
 
 constexpr size_t kLdsMax = 160 * 1024 - 256;  // leave room for static LDS
 
-// Copy the coefficient block and c of head h into LDS (rows padded to g.wstride).
+// Copy the coefficient block and c of head h into LDS (rows padded to g.wstride).  Loads
+// are issued in batches of 8 per thread before their LDS stores, so their latencies overlap.
 __device__ __forceinline__ void stage_coefficients(unsigned char* sW, float* sC, const bf16_t* W, const float* cvec,
                                                    int h, int Kp, int Dp, int wstride) {
     const int vec_per_row = (8 * Dp) / 16;  // 16-byte vectors per row
-    const bf16_t* src = W + (size_t)h * Kp * 4 * Dp;
-    for (int i = threadIdx.x; i < Kp * vec_per_row; i += blockDim.x) {
-        const int r = i / vec_per_row, c = i % vec_per_row;
-        *reinterpret_cast<bf16x8*>(sW + (size_t)r * wstride + 16 * c) =
-            *reinterpret_cast<const bf16x8*>(reinterpret_cast<const unsigned char*>(src + (size_t)r * 4 * Dp) + 16 * c);
+    const int total = Kp * vec_per_row;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(W + (size_t)h * Kp * 4 * Dp);
+    for (int i0 = threadIdx.x; i0 < total; i0 += 8 * blockDim.x) {
+        bf16x8 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * blockDim.x;
+            if (i < total) v[u] = *reinterpret_cast<const bf16x8*>(src + 16 * (size_t)i);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * blockDim.x;
+            if (i < total)
+                *reinterpret_cast<bf16x8*>(sW + (size_t)(i / vec_per_row) * wstride + 16 * (i % vec_per_row)) = v[u];
+        }
     }
     for (int i = threadIdx.x; i < Kp; i += blockDim.x) sC[i] = cvec[(size_t)h * Kp + i];
 }
@@ -63,9 +74,9 @@ __device__ __forceinline__ void head_part(int b, int heads, int parts, int& head
     }
 }
 
-// Parameter prep (coefficients [ah|al|bh|bl] per head in bf16, c_k in float) and ticket
-// clearing; defined with the bidirectional kernels.
-hipError_t launch_prep(const Args& a, const Geo& g, bf16_t* W, float* cvec, int* tickets, int n_tickets);
+// Parameter prep (coefficients [ah|al|bh|bl] per head in bf16, c_k in float); defined with
+// the bidirectional kernels.
+hipError_t launch_prep(const Args& a, const Geo& g, bf16_t* W, float* cvec);
 
 // Causal family (defined in gma_mfma_causal.hip).
 bool causal_supported(const gma_desc& d);
