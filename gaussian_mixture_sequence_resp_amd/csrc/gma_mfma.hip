@@ -137,6 +137,9 @@ __device__ __forceinline__ void load_vrow(bf16x8 (&vr)[2 * NT], const bf16_t* ro
     }
 }
 
+// Stage assignment of the four softmax stages over the U units of a pipelined logits tile.
+__host__ __device__ constexpr int stage_unit(int st, int U) { return (st * U) / 4; }
+
 template <int MT, int NT, int NC>
 __global__ void __launch_bounds__(kThreads, 1)
     gma_bidir_write(const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v, const bf16_t* __restrict__ W,
@@ -146,6 +149,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     constexpr int Kp = 32 * MT, Dvp = 32 * NT, Dp = 16 * NC;
     constexpr int wstride = 8 * Dp + 16;
     constexpr int gs = 2 * Kp + 32, vs = 2 * Dvp + 32;
+    using UT = UpdateTiles<MT, NT>;
     unsigned char* sW = smem;
     float* sC = reinterpret_cast<float*>(sW + (size_t)Kp * wstride);
     unsigned char* sG = reinterpret_cast<unsigned char*>(sC + Kp);
@@ -154,111 +158,94 @@ __global__ void __launch_bounds__(kThreads, 1)
     int bh, split;
     head_part(blockIdx.x, BH, S, bh, split);
     const int h = bh % H;
-    const int l = lane_id(), w = wave_id(), half = l >> 5;
+    const int l = lane_id(), w = wave_id(), half = l >> 5, col = l & 31;
     const int n_begin = split * split_len;
     const int n_end = min(N, n_begin + split_len);
-
-    stage_coefficients(sW, sC, W, cvec, h, Kp, Dp, wstride);
-
-    // Output tiles of Gamma_K^T [V | 1]: (m, n) for n < NT, and the ones tile n = NT whose
-    // every column is Z_k.  Dealt to waves in contiguous runs (m-major).
-    constexpr int kTiles = MT * (NT + 1);
-    constexpr int kPerWave = (kTiles + kWaves - 1) / kWaves;
-    f32x16 wacc[kPerWave];
-#pragma unroll
-    for (int j = 0; j < kPerWave; ++j)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) wacc[j][i] = 0.0f;
-
+    const int nit = n_end > n_begin ? (n_end - n_begin + kIterT - 1) / kIterT : 0;
     const bf16_t* kr_h = kr + (size_t)bh * N * dr;
     const bf16_t* v_h = v + (size_t)bh * N * dv;
+    auto krow = [&](int it) -> const bf16_t* {
+        const int t = n_begin + it * kIterT + kTileT * w + col;
+        return (it < nit && t < n_end) ? kr_h + (size_t)t * dr : nullptr;
+    };
+    auto vrow = [&](int it) -> const bf16_t* {
+        const int t = n_begin + it * kIterT + kTileT * w + col;
+        return (it < nit && t < n_end) ? v_h + (size_t)t * dv : nullptr;
+    };
+
+    f32x16 wacc[UT::MW][UT::NW];
+#pragma unroll
+    for (int i = 0; i < UT::MW; ++i)
+#pragma unroll
+        for (int j = 0; j < UT::NW; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) wacc[i][j][e] = 0.0f;
     bf16x8 ones;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ones[j] = (short)0x3f80;
 
-    // registers for the next tile's raw k and v rows (prefetched one iteration ahead)
-    bf16x8 xr[NC], vr[2 * NT];
-    {
-        const int t = n_begin + kTileT * w + (l & 31);
-        load_xrow<NC>(xr, t < n_end ? kr_h + (size_t)t * dr : nullptr, dr);
-        load_vrow<NT>(vr, t < n_end ? v_h + (size_t)t * dv : nullptr, dv);
-    }
+    // k rows for steps 0 and 1, v rows for step 0 (register prefetch)
+    bf16x8 xa[NC], xb[NC], vcur[2 * NT];
+    load_xrow<NC>(xa, krow(0), dr);
+    load_xrow<NC>(xb, krow(1), dr);
+    load_vrow<NT>(vcur, vrow(0), dv);
+    stage_coefficients(sW, sC, W, cvec, h, Kp, Dp, wstride);
     __syncthreads();
 
-    for (int base = n_begin; base < n_end; base += kIterT) {
-        // ---- this wave's 32 tokens: Gamma_K (normalised) into sG rows 32w .. 32w+31
-        {
-            const int t = base + kTileT * w + (l & 31);
-            const bool valid = t < n_end;
-            bf16x8 xc[NC], vc[2 * NT];
-#pragma unroll
-            for (int c = 0; c < NC; ++c) xc[c] = xr[c];
-#pragma unroll
-            for (int j = 0; j < 2 * NT; ++j) vc[j] = vr[j];
-            const int tn = t + kIterT;
-            load_xrow<NC>(xr, tn < n_end ? kr_h + (size_t)tn * dr : nullptr, dr);
-            load_vrow<NT>(vr, tn < n_end ? v_h + (size_t)tn * dv : nullptr, dv);
+    f32x16 accA[MT], accB[MT];
+    tile_logits_overlap<MT, NC>(accA, xa, sW, wstride, sC, [](int, int) {});
+    load_xrow<NC>(xa, krow(2), dr);
 
-            f32x16 acc[MT];
-            tile_logits<MT, NC>(acc, xc, sW, wstride, sC);
-            const float s = tile_exp<MT>(acc);
-            const float inv = valid ? 1.0f / s : 0.0f;
-            unsigned char* grow = sG + (size_t)(kTileT * w + (l & 31)) * gs;
+    // One pipeline step: finish tile `it` (softmax, stage Gamma_K and V rows in LDS) while the
+    // logits of tile it+1 run, then the LDS-fed update over the 128 staged positions.
+    auto step = [&](int it, f32x16 (&cur)[MT], f32x16 (&nxt)[MT], bf16x8 (&xnext)[NC], bf16x8 (&xfar)[NC]) {
+        const int t = n_begin + it * kIterT + kTileT * w + col;
+        const bool valid = t < n_end;
+        bf16x8 vnext[2 * NT];
+        load_vrow<NT>(vnext, vrow(it + 1), dv);
+        SoftmaxStages<MT> sm;
+        unsigned char* grow = sG + (size_t)(kTileT * w + col) * gs;
+        unsigned char* vdst = sV + (size_t)(kTileT * w + col) * vs;
+        tile_logits_overlap<MT, NC>(nxt, xnext, sW, wstride, sC, [&](int u, int U) {
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+            for (int st = 0; st < 4; ++st)
+                if (stage_unit(st, U) == u) sm.stage(st, cur, valid, grow);
+            if (u == U - 1) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint2 p;
-                    p.x = pack_bf16(acc[m][4 * q] * inv, acc[m][4 * q + 1] * inv);
-                    p.y = pack_bf16(acc[m][4 * q + 2] * inv, acc[m][4 * q + 3] * inv);
-                    *reinterpret_cast<uint2*>(grow + 2 * (32 * m + 8 * q + 4 * half)) = p;
-                }
-            // ---- V rows of the same tokens into sV (zero-padded to Dvp, zero past n_end)
-            unsigned char* vrow = sV + (size_t)(kTileT * w + (l & 31)) * vs;
-#pragma unroll
-            for (int j = 0; j < 2 * NT; ++j)
-                *reinterpret_cast<bf16x8*>(vrow + 2 * (16 * j + 8 * half)) = vc[j];
-        }
-        lds_barrier();
-        // ---- Gamma_K^T [V | 1] over the 128 staged tokens, this wave's output tiles
-#pragma unroll
-        for (int ks = 0; ks < kIterT / 16; ++ks) {
-            int last_m = -1;
-            bf16x8 a;
-#pragma unroll
-            for (int j = 0; j < kPerWave; ++j) {
-                const int tile = w * kPerWave + j;
-                if (tile < kTiles) {
-                    const int m = tile / (NT + 1), n = tile % (NT + 1);
-                    if (m != last_m) {
-                        a = lds_frag_tr(sG, gs, 16 * ks, 32 * m);
-                        last_m = m;
-                    }
-                    const bf16x8 b = (n < NT) ? lds_frag_tr(sV, vs, 16 * ks, 32 * n) : ones;
-                    wacc[j] = mfma(a, b, wacc[j]);
-                }
+                for (int j = 0; j < 2 * NT; ++j) *reinterpret_cast<bf16x8*>(vdst + 2 * (16 * j + 8 * half)) = vcur[j];
             }
-        }
+        });
+        load_xrow<NC>(xfar, krow(it + 3), dr);
         lds_barrier();
+        update_from_lds<MT, NT, UT::MW, UT::NW>(wacc, sG, gs, sV, vs, ones);
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < 2 * NT; ++j) vcur[j] = vnext[j];
+    };
+    // xa holds step it+2's rows when step `it` starts with nxt rows in xb (and vice versa)
+    for (int it = 0; it < nit; it += 2) {
+        step(it, accA, accB, xb, xb);
+        if (it + 1 < nit) step(it + 1, accB, accA, xa, xa);
     }
 
     // ---- partial of this split -> workspace (fp32)
     float* pv = part_v + ((size_t)bh * S + split) * Kp * Dvp;
     float* pz = part_z + ((size_t)bh * S + split) * Kp;
 #pragma unroll
-    for (int j = 0; j < kPerWave; ++j) {
-        const int tile = w * kPerWave + j;
-        if (tile >= kTiles) break;
-        const int m = tile / (NT + 1), n = tile % (NT + 1);
+    for (int i = 0; i < UT::MW; ++i)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int k = 32 * m + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (n < NT)
-                pv[(size_t)k * Dvp + 32 * n + (l & 31)] = wacc[j][i];
-            else if ((l & 31) == 0)
-                pz[k] = wacc[j][i];
+        for (int j = 0; j < UT::NW; ++j) {
+            const int m = UT::m_of(w, i), n = UT::n_of(w, j);
+            if (n > NT) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int k = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
+                if (n < NT)
+                    pv[(size_t)k * Dvp + 32 * n + col] = wacc[i][j][e];
+                else if (col == 0)
+                    pz[k] = wacc[i][j][e];
+            }
         }
-    }
 }
 
 // ---------------------------------------------------------------------------------- read

@@ -117,20 +117,24 @@ __device__ __forceinline__ void stage_coefficient_chunks(unsigned char* sW, floa
     for (int i = threadIdx.x; i < Kp; i += blockDim.x) sC[i] = cvec[(size_t)h * Kp + i];
 }
 
-// Each wave handles one 32-position tile per 128-position step (one side per block row,
+// Eight waves (two per SIMD, so one wave's exponentials overlap the other's MFMAs); each
+// wave handles one 32-position tile per 256-position step (one side per block row,
 // blockIdx.y: 0 queries, 1 keys): logits (MFMA), softmax over the components, normalised
 // responsibilities stored token-major as bf16; positions in [N, Np) get zeros.  When the
 // coefficient block of a head exceeds LDS it is staged in NPH phases of the routing dims,
 // the logits accumulating across phases.  The key side also stores Gamma_K component-major:
 // a 32x32 MFMA against a permutation matrix moves the components from registers to lanes.
+constexpr int kRespWaves = 8;
+
 template <int MT, int NC, int NPH>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(64 * kRespWaves, 2)
     gma_causal_resp(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ W,
                     const float* __restrict__ cvec, bf16_t* __restrict__ GQ, bf16_t* __restrict__ GK,
                     bf16_t* __restrict__ GKT, int BH, int H, int N, int Np, int dr, int parts, int part_len) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int Kp = 32 * MT, Dp = 16 * NC, NCP = NC / NPH;
     constexpr int wstride = 8 * (16 * NCP) + 16;
+    constexpr int kStep = kTileT * kRespWaves;
     unsigned char* sW = smem;
     float* sC = reinterpret_cast<float*>(smem + (size_t)Kp * wstride);
     int bh, part;
@@ -148,51 +152,64 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
         for (int e = 0; e < 8; ++e) perm[s2][e] = (short)(col == 16 * s2 + kperm(8 * half + e) ? 0x3f80 : 0);
 
+    const int n_begin = part * part_len;
+    const int n_end = min(Np, n_begin + part_len);
+    auto row = [&](int b0) -> const bf16_t* {
+        const int t = b0 + kTileT * w + col;
+        return (t < n_end && t < N) ? x + (size_t)t * dr : nullptr;
+    };
+    bf16x8 xr[NC];
+    load_xrow<NC>(xr, row(n_begin), dr);
     if (NPH == 1) {
         stage_coefficient_chunks(sW, sC, W, cvec, h, Kp, Dp, 0, NC, wstride);
         __syncthreads();
     }
-    const int n_begin = part * part_len;
-    const int n_end = min(Np, n_begin + part_len);
-    for (int b0 = n_begin; b0 < n_end; b0 += kIterT) {
-        const int t = b0 + kTileT * w + col;
+    for (int b0 = n_begin; b0 < n_end; b0 += kStep) {
+        const int t0 = b0 + kTileT * w;  // this wave's tile
+        const int t = t0 + col;
         const bool valid = t < N;
-        bf16x8 xr[NC];
-        load_xrow<NC>(xr, valid ? x + (size_t)t * dr : nullptr, dr);
         f32x16 acc[MT];
+        if (NPH == 1) {
+            tile_logits_overlap<MT, NCP, true>(acc, xr, sW, wstride, sC, [](int, int) {});
+        } else {
 #pragma unroll
-        for (int ph = 0; ph < NPH; ++ph) {
-            if (NPH > 1) {
-                __syncthreads();
+            for (int ph = 0; ph < NPH; ++ph) {
+                lds_barrier();
                 stage_coefficient_chunks(sW, sC, W, cvec, h, Kp, Dp, ph * NCP, NCP, wstride);
                 __syncthreads();
+                if (ph == 0)
+                    tile_logits_overlap<MT, NCP, true>(acc, xr, sW, wstride, sC, [](int, int) {});
+                else
+                    tile_logits_overlap<MT, NCP, false>(acc, xr + ph * NCP, sW, wstride, sC, [](int, int) {});
             }
-            tile_logits<MT, NCP>(acc, xr + ph * NCP, sW, wstride, sC, ph == 0);
         }
+        load_xrow<NC>(xr, row(b0 + kStep), dr);  // next step's rows, in flight during the softmax
         const float s = tile_exp<MT>(acc);
         const float inv = valid ? 1.0f / s : 0.0f;
-        bf16_t* grow = G + (size_t)t * Kp;
+        if (t0 < n_end) {
+            bf16_t* grow = G + (size_t)t * Kp;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const bf16x8 g0 = pack8(acc[m], 0, inv), g1 = pack8(acc[m], 8, inv);
-            const u32x4 p0 = __builtin_bit_cast(u32x4, g0), p1 = __builtin_bit_cast(u32x4, g1);
-            // registers 4q..4q+3 hold components 32m + 8q + 4 half + (0..3)
-            *reinterpret_cast<uint2*>(grow + 32 * m + 0 + 4 * half) = make_uint2(p0[0], p0[1]);
-            *reinterpret_cast<uint2*>(grow + 32 * m + 8 + 4 * half) = make_uint2(p0[2], p0[3]);
-            *reinterpret_cast<uint2*>(grow + 32 * m + 16 + 4 * half) = make_uint2(p1[0], p1[1]);
-            *reinterpret_cast<uint2*>(grow + 32 * m + 24 + 4 * half) = make_uint2(p1[2], p1[3]);
-            if (side == 1) {
-                // D[t][k'] = sum_c G[t][c] B[c][k']: rows = positions, lanes = components
-                f32x16 tr;
+            for (int m = 0; m < MT; ++m) {
+                const bf16x8 g0 = pack8(acc[m], 0, inv), g1 = pack8(acc[m], 8, inv);
+                const u32x4 p0 = __builtin_bit_cast(u32x4, g0), p1 = __builtin_bit_cast(u32x4, g1);
+                // registers 4q..4q+3 hold components 32m + 8q + 4 half + (0..3)
+                *reinterpret_cast<uint2*>(grow + 32 * m + 0 + 4 * half) = make_uint2(p0[0], p0[1]);
+                *reinterpret_cast<uint2*>(grow + 32 * m + 8 + 4 * half) = make_uint2(p0[2], p0[3]);
+                *reinterpret_cast<uint2*>(grow + 32 * m + 16 + 4 * half) = make_uint2(p1[0], p1[1]);
+                *reinterpret_cast<uint2*>(grow + 32 * m + 24 + 4 * half) = make_uint2(p1[2], p1[3]);
+                if (side == 1) {
+                    // D[t][k'] = sum_c G[t][c] B[c][k']: rows = positions, lanes = components
+                    f32x16 tr;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) tr[i] = 0.0f;
-                tr = mfma(g0, perm[0], tr);
-                tr = mfma(g1, perm[1], tr);
-                bf16_t* trow = gt + (size_t)(32 * m + col) * Np + (b0 + kTileT * w);
+                    for (int i = 0; i < 16; ++i) tr[i] = 0.0f;
+                    tr = mfma(g0, perm[0], tr);
+                    tr = mfma(g1, perm[1], tr);
+                    bf16_t* trow = gt + (size_t)(32 * m + col) * Np + t0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<uint2*>(trow + 8 * q + 4 * half) =
-                        make_uint2(pack_bf16(tr[4 * q], tr[4 * q + 1]), pack_bf16(tr[4 * q + 2], tr[4 * q + 3]));
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint2*>(trow + 8 * q + 4 * half) = make_uint2(
+                            pack_bf16(tr[4 * q], tr[4 * q + 1]), pack_bf16(tr[4 * q + 2], tr[4 * q + 3]));
+                }
             }
         }
     }
@@ -579,17 +596,18 @@ hipError_t causal_forward(const Args& a) {
 
     if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
 
-    // responsibilities of both sides, ~2 workgroups per CU
-    int parts = (512 + BH - 1) / BH;
-    const int max_parts = L.Np / kIterT;
+    // responsibilities of both sides, ~one workgroup per CU per side
+    const int rstep = kTileT * kRespWaves;
+    int parts = (256 + BH - 1) / BH;
+    const int max_parts = (L.Np + rstep - 1) / rstep;
     if (parts > max_parts) parts = max_parts;
     if (parts < 1) parts = 1;
-    const int part_len = ((L.Np + parts - 1) / parts + kIterT - 1) / kIterT * kIterT;
+    const int part_len = ((L.Np + parts - 1) / parts + rstep - 1) / rstep * rstep;
     parts = (L.Np + part_len - 1) / part_len;
     const size_t rl = resp_lds(g, nph);
     if ((e = set_lds(reinterpret_cast<const void*>(rf), rl)) != hipSuccess) return e;
     rec_begin(a, "gma_causal_resp");
-    hipLaunchKernelGGL(rf, dim3(BH * parts, 2), dim3(kThreads), rl, a.stream, static_cast<const bf16_t*>(a.qr),
+    hipLaunchKernelGGL(rf, dim3(BH * parts, 2), dim3(64 * kRespWaves), rl, a.stream, static_cast<const bf16_t*>(a.qr),
                        static_cast<const bf16_t*>(a.kr), W, cvec, GQ, GK, GKT, BH, d.H, d.N, L.Np, d.d_r, parts,
                        part_len);
     rec_end(a);

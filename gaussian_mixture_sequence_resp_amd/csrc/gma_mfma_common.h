@@ -186,6 +186,121 @@ __device__ __forceinline__ void tile_logits(f32x16 (&acc)[MT], const bf16x8* xr,
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Software-pipelined logits.  The contraction of one tile is cut into units (a 16-wide chunk
+// of routing dims x a group of up to 4 component tiles: 16 coefficient fragments, 20 MFMAs).
+// The fragments of unit u+1 are loaded while unit u's MFMAs run, and `work(u, U)` -- VALU
+// work of another tile (its softmax, packing, stores) -- sits in the same scheduling region
+// as unit u's MFMAs, so the two interleave on one SIMD.  Regions are closed by
+// sched_barrier so nothing drifts across units (register pressure stays bounded).
+template <int MG>
+struct WFrag {
+    bf16x8 ah[MG], al[MG], bh[MG], bl[MG];
+};
+
+template <int MG, int Dp>
+__device__ __forceinline__ void load_wfrag(WFrag<MG>& f, const unsigned char* sW, int wstride, int c, int g0) {
+    const int l = lane_id(), h = l >> 5;
+    const unsigned char* wr = sW + (size_t)(l & 31) * wstride + (16 * c + 8 * h) * 2;
+#pragma unroll
+    for (int m = 0; m < MG; ++m) {
+        const unsigned char* wm = wr + (size_t)32 * (g0 + m) * wstride;
+        f.ah[m] = *reinterpret_cast<const bf16x8*>(wm);
+        f.al[m] = *reinterpret_cast<const bf16x8*>(wm + 2 * Dp);
+        f.bh[m] = *reinterpret_cast<const bf16x8*>(wm + 4 * Dp);
+        f.bl[m] = *reinterpret_cast<const bf16x8*>(wm + 6 * Dp);
+    }
+}
+
+template <int MT, int NC, bool INIT = true, typename Work>
+__device__ __forceinline__ void tile_logits_overlap(f32x16 (&acc)[MT], const bf16x8* xr, const unsigned char* sW,
+                                                    int wstride, const float* sC, Work&& work) {
+    constexpr int MG = MT < 2 ? MT : 2;  // 2 accumulators alternate; 2 x 8 fragments in flight
+    constexpr int GPC = MT / MG;  // groups per chunk
+    constexpr int U = NC * GPC;
+    constexpr int Dp = 16 * NC;
+    const int h = lane_id() >> 5;
+#pragma unroll
+    for (int m = 0; m < (INIT ? MT : 0); ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 cq = *reinterpret_cast<const float4*>(sC + 32 * m + 8 * q + 4 * h);
+            acc[m][4 * q] = cq.x;
+            acc[m][4 * q + 1] = cq.y;
+            acc[m][4 * q + 2] = cq.z;
+            acc[m][4 * q + 3] = cq.w;
+        }
+    WFrag<MG> cur;
+    load_wfrag<MG, Dp>(cur, sW, wstride, 0, 0);
+    XFrag f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = u / GPC, g0 = (u % GPC) * MG;
+        WFrag<MG> nxt;
+        if (u + 1 < U) load_wfrag<MG, Dp>(nxt, sW, wstride, (u + 1) / GPC, ((u + 1) % GPC) * MG);
+        if (g0 == 0) {
+            f.x1 = xr[c];
+            split_square(f);
+        }
+#pragma unroll
+        for (int m = 0; m < MG; ++m) acc[g0 + m] = mfma(cur.ah[m], f.x2h, acc[g0 + m]);
+#pragma unroll
+        for (int m = 0; m < MG; ++m) acc[g0 + m] = mfma(cur.bh[m], f.x1, acc[g0 + m]);
+#pragma unroll
+        for (int m = 0; m < MG; ++m) acc[g0 + m] = mfma(cur.al[m], f.x2h, acc[g0 + m]);
+#pragma unroll
+        for (int m = 0; m < MG; ++m) acc[g0 + m] = mfma(cur.bl[m], f.x1, acc[g0 + m]);
+#pragma unroll
+        for (int m = 0; m < MG; ++m) acc[g0 + m] = mfma(cur.ah[m], f.x2l, acc[g0 + m]);
+        work(u, U);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < U) cur = nxt;
+    }
+}
+
+// The softmax of a finished logits tile, cut into four stages so a pipelined loop can spread
+// it over the units of the next tile's logits: 0 row max, 1 exponentials of the first half
+// of the component tiles, 2 the second half, row sum and its reciprocal, 3 scale, pack to
+// bf16 and store the token's row (components 32m + 8q + 4 half + 0..3 as 8 bytes) at `grow`.
+template <int MT>
+struct SoftmaxStages {
+    float mx, s, inv;
+    __device__ __forceinline__ void stage(int st, f32x16 (&a)[MT], bool valid, unsigned char* grow) {
+        const int half = lane_id() >> 5;
+        if (st == 0) {
+            float m0 = -INFINITY;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, a[m][i]);
+            mx = max_halves(m0);
+            s = 0.0f;
+        } else if (st == 1 || st == 2) {
+            constexpr int H1 = (MT + 1) / 2;
+            const int lo = st == 1 ? 0 : H1, hi = st == 1 ? H1 : MT;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (m < lo || m >= hi) continue;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float e = fast_exp2(a[m][i] - mx);
+                    a[m][i] = e;
+                    s += e;
+                }
+            }
+            if (st == 2) inv = valid ? 1.0f / sum_halves(s) : 0.0f;
+        } else {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint2*>(grow + 2 * (32 * m + 8 * q + 4 * half)) =
+                        make_uint2(pack_bf16(a[m][4 * q] * inv, a[m][4 * q + 1] * inv),
+                                   pack_bf16(a[m][4 * q + 2] * inv, a[m][4 * q + 3] * inv));
+        }
+    }
+};
+
 // In-place softmax numerator: acc <- 2^(acc - max_k acc) for this lane's token; returns the
 // row sum over all components (both lane halves).
 template <int MT>
@@ -265,6 +380,43 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int first, float scale)
 #pragma unroll
     for (int j = 0; j < 4; ++j) p[j] = pack_bf16(c[first + 2 * j] * scale, c[first + 2 * j + 1] * scale);
     return __builtin_bit_cast(bf16x8, p);
+}
+
+// Output tiles of Gamma_K^T [V | 1] owned by one wave: tile (m, n), n < NT a value tile,
+// n == NT the ones tile whose every column accumulates z_k.  With MT >= 4 a wave owns MT/4
+// component tiles and every n; with MT < 4 the 4/MT waves sharing a component tile split the
+// n range (an index past NT is computed but never stored).  Compile-time counts, wave-uniform
+// indices: the loops are branch-free, so the transposed LDS reads of a whole group batch up.
+template <int MT, int NT>
+struct UpdateTiles {
+    static constexpr int MW = MT >= 4 ? MT / 4 : 1;
+    static constexpr int WPM = MT >= 4 ? 1 : 4 / MT;
+    static constexpr int NW = (NT + 1 + WPM - 1) / WPM;
+    __device__ static int m_of(int w, int j) { return MT >= 4 ? w * MW + j : w / WPM; }
+    __device__ static int n_of(int w, int j) { return MT >= 4 ? j : (w % WPM) * NW + j; }
+};
+
+template <int MT, int NT, int MW, int NW>
+__device__ __forceinline__ void update_from_lds(f32x16 (&acc)[MW][NW], const unsigned char* sG, int gs,
+                                                const unsigned char* sV, int vs, const bf16x8& ones) {
+    using UT = UpdateTiles<MT, NT>;
+    const int w = wave_id();
+#pragma unroll
+    for (int ks = 0; ks < kIterT / 16; ++ks) {
+        bf16x8 a[UT::MW], b[UT::NW];
+#pragma unroll
+        for (int j = 0; j < UT::MW; ++j) a[j] = lds_frag_tr(sG, gs, 16 * ks, 32 * UT::m_of(w, j));
+#pragma unroll
+        for (int j = 0; j < UT::NW; ++j) {
+            const int n = UT::n_of(w, j);
+            const bf16x8 t = lds_frag_tr(sV, vs, 16 * ks, n < NT ? 32 * n : 0);
+            b[j] = n < NT ? t : ones;
+        }
+#pragma unroll
+        for (int i = 0; i < UT::MW; ++i)
+#pragma unroll
+            for (int j = 0; j < UT::NW; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]);
+    }
 }
 
 // Position of component k inside its 16-wide block so that the C registers 8s..8s+7 of a
