@@ -10,20 +10,32 @@
 //     O_group = Gamma_Q [S | z]  +  tril(Gamma_Q Gamma_K^T) [V | 1]     (within the group)
 //     [S | z] += Gamma_K^T [V | 1]                                      (after the group)
 // The sequence of each head is cut into S contiguous segments that run in parallel; the
-// state entering segment s is the sum of the totals Gamma_K^T [V | 1] of segments 0..s-1,
-// added in segment order (deterministic).
+// state entering segment s is the sum of the totals Gamma_K^T [V | 1] of the positions
+// before it, added in a fixed order (deterministic).  Value dims are processed in slices of
+// at most 64 (one workgroup per slice; each slice carries its own copy of z).
+//
+// Responsibilities in memory.  Gamma_Q and Gamma_K (normalised, bf16) are stored in MFMA
+// operand order: for every 32-position tile and every 16-wide block ks of components, the
+// 64 lanes' 16-byte fragments lie contiguously (lane l = position l % 32 of the tile, holding
+// slots 8 (l / 32) .. + 7 of the block).  Every store of the producer and every load of the
+// consumers is then one contiguous 1 KB access per wave.  The slot order inside a block is
+// the C-register order of the logits tile, i.e. slot s holds component 16 ks + kperm(s); all
+// consumers index components by slot, so the state [S | z] is kept in the same order.
 //
 // Kernels (all on the caller's stream, in this order):
 //   gma_prep            (shared with the bidirectional path) coefficients and c_k
-//   gma_causal_resp     Gamma_Q and Gamma_K (normalised, bf16) of every position, token-major,
-//                       plus Gamma_K transposed (component-major) for the state update
-//   gma_causal_totals   per-segment totals Gamma_K^T [V | 1] (segments 0..S-2)
-//   gma_causal_carry    exclusive prefix of the totals over segments (in place)
-//   gma_causal_scan     one workgroup per (head, segment): sequential groups of 128
-//                       positions; fp32 state in MFMA accumulators split over the 4 waves by
-//                       output tile, bf16 shadow of the full state in LDS for Gamma_Q [S | z];
-//                       intra-group term from masked Gamma_Q Gamma_K^T MFMA tiles (zero-filled
-//                       above the diagonal, so positions after i never reach O_i).
+//   gma_causal_resp     Gamma_Q and Gamma_K of every position (logit MFMAs + softmax)
+//   gma_causal_totals   Gamma_K^T [V | 1] of fixed-length sub-segments before the last
+//                       segment (only when S > 1)
+//   gma_causal_carry    state entering every segment: ordered sum of the sub-segment totals
+//   gma_causal_scan     one workgroup per (head, segment, value slice): sequential groups of
+//                       128 positions; fp32 state in MFMA accumulators split over the 4 waves
+//                       by output tile, bf16 shadow of the full state in LDS for
+//                       Gamma_Q [S | z]; Gamma_K rows of the group staged in LDS for the
+//                       masked intra-group tiles (zero-filled above the diagonal, so
+//                       positions after i never reach O_i) and the state update.  The next
+//                       group's Gamma_K, Gamma_Q and V are loaded into registers while the
+//                       current group computes.
 #include <math.h>
 
 #include "gma_internal.h"
@@ -36,52 +48,68 @@ namespace mf {
 namespace {
 
 constexpr int kGroup = kIterT;  // 128 positions per scan step (one 32-position chunk per wave)
+constexpr int kSliceV = 64;     // value dims per scan workgroup
+constexpr int kFrag = 64 * 8;   // bf16 elements of one operand fragment block (64 lanes x 8)
 
 struct CausalLayout {
-    size_t W, C, gq, gk, gkt, carry, total;
-    int S, seg_len, Np;
+    size_t W, C, gq, gk, tpart, carry, total;
+    int S, seg_len, Np;     // segments, their length (multiple of kGroup), padded sequence
+    int NS, Dvs;            // value slices and their width (padded)
+    int TS, nsub, sub_len;  // totals: sub-segments per segment, their count and length
 };
-
-int causal_segments(const gma_desc& d) {
-    const int bh = d.B * d.H;
-    const int groups = (d.N + kGroup - 1) / kGroup;
-    int s = (256 + bh - 1) / bh;
-    if (s > groups) s = groups;
-    if (s > 64) s = 64;
-    return s < 1 ? 1 : s;
-}
 
 CausalLayout causal_layout(const gma_desc& d) {
     const Geo g = geometry(d);
-    const size_t BH = (size_t)d.B * d.H;
+    const int BH = d.B * d.H;
     CausalLayout L;
-    L.S = causal_segments(d);
-    L.seg_len = ((d.N + L.S - 1) / L.S + kGroup - 1) / kGroup * kGroup;
+    L.Dvs = g.Dvp < kSliceV ? g.Dvp : kSliceV;
+    L.NS = g.Dvp / L.Dvs;
+    const int groups = (d.N + kGroup - 1) / kGroup;
+    int s = (256 + BH * L.NS - 1) / (BH * L.NS);
+    if (s > groups) s = groups;
+    if (s > 64) s = 64;
+    if (s < 1) s = 1;
+    L.seg_len = ((d.N + s - 1) / s + kGroup - 1) / kGroup * kGroup;
     L.S = (d.N + L.seg_len - 1) / L.seg_len;
     if (L.S < 1) L.S = 1;
-    L.Np = (d.N + kGroup - 1) / kGroup * kGroup;
+    L.Np = groups * kGroup;
+    // totals: split every segment before the last into TS equal sub-segments so that about
+    // 256 workgroups run; TS divides the segment's group count
+    const int seg_groups = L.seg_len / kGroup;
+    L.TS = 1;
+    if (L.S > 1) {
+        const int want = (256 + BH * (L.S - 1) * L.NS - 1) / (BH * (L.S - 1) * L.NS);
+        for (int t = 1; t <= seg_groups && t <= want; ++t)
+            if (seg_groups % t == 0) L.TS = t;
+    }
+    L.sub_len = L.seg_len / L.TS;
+    L.nsub = (L.S - 1) * L.TS;
+    const size_t per = (size_t)g.Kp * (L.Dvs + 1);
     size_t off = 0;
     L.W = off;
     off += align_up((size_t)d.H * g.Kp * 4 * g.Dp * sizeof(bf16_t));
     L.C = off;
     off += align_up((size_t)d.H * g.Kp * sizeof(float));
     L.gq = off;
-    off += align_up(BH * L.Np * g.Kp * sizeof(bf16_t));
+    off += align_up((size_t)BH * L.Np * g.Kp * sizeof(bf16_t));
     L.gk = off;
-    off += align_up(BH * L.Np * g.Kp * sizeof(bf16_t));
-    L.gkt = off;
-    off += align_up(BH * L.Np * g.Kp * sizeof(bf16_t));
+    off += align_up((size_t)BH * L.Np * g.Kp * sizeof(bf16_t));
+    L.tpart = off;
+    off += align_up((size_t)BH * L.nsub * L.NS * per * sizeof(float));
     L.carry = off;
-    off += align_up(BH * L.S * g.Kp * (g.Dvp + 1) * sizeof(float));
+    off += align_up((size_t)BH * L.S * L.NS * per * sizeof(float));
     L.total = off;
     return L;
 }
 
-inline int cvstride(const Geo& g) { return 2 * g.Dvp + 32; }
-inline int shstride(const Geo& g) { return 2 * g.Kp + 16; }
-inline size_t totals_lds_bytes(const Geo& g) { return (size_t)kGroup * cvstride(g); }
-inline size_t scan_lds_bytes(const Geo& g) {
-    return (size_t)kGroup * cvstride(g) + (size_t)(g.Dvp + 32) * shstride(g);
+inline int gstride(int Kp) { return 2 * Kp + 32; }
+inline int vstride(int Dvs) { return 2 * Dvs + 32; }
+inline int shstride(int Kp) { return 2 * Kp + 16; }
+inline size_t totals_lds_bytes(const Geo& g, int Dvs) {
+    return (size_t)kGroup * gstride(g.Kp) + (size_t)kGroup * vstride(Dvs);
+}
+inline size_t scan_lds_bytes(const Geo& g, int Dvs) {
+    return totals_lds_bytes(g, Dvs) + (size_t)(Dvs + 32) * shstride(g.Kp);
 }
 
 // ----------------------------------------------------------------------------- responsibilities
@@ -120,19 +148,18 @@ __device__ __forceinline__ void stage_coefficient_chunks(unsigned char* sW, floa
 // Eight waves (two per SIMD, so one wave's exponentials overlap the other's MFMAs); each
 // wave handles one 32-position tile per 256-position step (one side per block row,
 // blockIdx.y: 0 queries, 1 keys): logits (MFMA), softmax over the components, normalised
-// responsibilities stored token-major as bf16; positions in [N, Np) get zeros.  When the
-// coefficient block of a head exceeds LDS it is staged in NPH phases of the routing dims,
-// the logits accumulating across phases.  The key side also stores Gamma_K component-major:
-// a 32x32 MFMA against a permutation matrix moves the components from registers to lanes.
+// responsibilities stored as bf16 operand fragments; positions in [N, Np) get zeros.  When
+// the coefficient block of a head exceeds LDS it is staged in NPH phases of the routing
+// dims, the logits accumulating across phases.
 constexpr int kRespWaves = 8;
 
 template <int MT, int NC, int NPH>
 __global__ void __launch_bounds__(64 * kRespWaves, 2)
     gma_causal_resp(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ W,
-                    const float* __restrict__ cvec, bf16_t* __restrict__ GQ, bf16_t* __restrict__ GK,
-                    bf16_t* __restrict__ GKT, int BH, int H, int N, int Np, int dr, int parts, int part_len) {
+                    const float* __restrict__ cvec, bf16_t* __restrict__ GQ, bf16_t* __restrict__ GK, int BH, int H,
+                    int N, int Np, int dr, int parts, int part_len) {
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int Kp = 32 * MT, Dp = 16 * NC, NCP = NC / NPH;
+    constexpr int Kp = 32 * MT, Dp = 16 * NC, NCP = NC / NPH, KS = Kp / 16;
     constexpr int wstride = 8 * (16 * NCP) + 16;
     constexpr int kStep = kTileT * kRespWaves;
     unsigned char* sW = smem;
@@ -140,17 +167,10 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
     int bh, part;
     head_part(blockIdx.x, BH, parts, bh, part);
     const int h = bh % H;
-    const int l = lane_id(), w = wave_id(), half = l >> 5, col = l & 31;
+    const int l = lane_id(), w = wave_id(), col = l & 31;
     const int side = blockIdx.y;
     const bf16_t* x = (side == 0 ? qr : kr) + (size_t)bh * N * dr;
-    bf16_t* G = (side == 0 ? GQ : GK) + (size_t)bh * Np * Kp;
-    bf16_t* gt = GKT + (size_t)bh * Kp * Np;
-    // permutation operands: B_s[c][k'] = 1 iff k' == 16 s + kperm(c) (c = 8 half + e)
-    bf16x8 perm[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) perm[s2][e] = (short)(col == 16 * s2 + kperm(8 * half + e) ? 0x3f80 : 0);
+    bf16_t* G = (side == 0 ? GQ : GK) + (size_t)bh * Np * Kp + 8 * l;
 
     const int n_begin = part * part_len;
     const int n_end = min(Np, n_begin + part_len);
@@ -166,8 +186,7 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
     }
     for (int b0 = n_begin; b0 < n_end; b0 += kStep) {
         const int t0 = b0 + kTileT * w;  // this wave's tile
-        const int t = t0 + col;
-        const bool valid = t < N;
+        const bool valid = t0 + col < N;
         f32x16 acc[MT];
         if (NPH == 1) {
             tile_logits_overlap<MT, NCP, true>(acc, xr, sW, wstride, sC, [](int, int) {});
@@ -187,260 +206,284 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
         const float s = tile_exp<MT>(acc);
         const float inv = valid ? 1.0f / s : 0.0f;
         if (t0 < n_end) {
-            bf16_t* grow = G + (size_t)t * Kp;
+            // registers 8 sh .. 8 sh + 7 of tile m are slots 8 half + 0..7 of block 2m + sh
+            bf16_t* gt = G + (size_t)(t0 / kTileT) * KS * kFrag;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const bf16x8 g0 = pack8(acc[m], 0, inv), g1 = pack8(acc[m], 8, inv);
-                const u32x4 p0 = __builtin_bit_cast(u32x4, g0), p1 = __builtin_bit_cast(u32x4, g1);
-                // registers 4q..4q+3 hold components 32m + 8q + 4 half + (0..3)
-                *reinterpret_cast<uint2*>(grow + 32 * m + 0 + 4 * half) = make_uint2(p0[0], p0[1]);
-                *reinterpret_cast<uint2*>(grow + 32 * m + 8 + 4 * half) = make_uint2(p0[2], p0[3]);
-                *reinterpret_cast<uint2*>(grow + 32 * m + 16 + 4 * half) = make_uint2(p1[0], p1[1]);
-                *reinterpret_cast<uint2*>(grow + 32 * m + 24 + 4 * half) = make_uint2(p1[2], p1[3]);
-                if (side == 1) {
-                    // D[t][k'] = sum_c G[t][c] B[c][k']: rows = positions, lanes = components
-                    f32x16 tr;
+                *reinterpret_cast<bf16x8*>(gt + (size_t)(2 * m) * kFrag) = pack8(acc[m], 0, inv);
+                *reinterpret_cast<bf16x8*>(gt + (size_t)(2 * m + 1) * kFrag) = pack8(acc[m], 8, inv);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------- group staging
+// Register prefetch of one group: this thread's share of the Gamma_K fragments (the group's
+// four tiles are one contiguous block of 16 Kp 16-byte chunks; thread i takes chunks
+// i + 256 u) and of the value slice rows (chunk c = row c / PPR, 8 dims at 8 (c % PPR)).
+template <int MT, int NTS>
+struct GroupRegs {
+    static constexpr int KS = 2 * MT;    // 16-wide component blocks
+    static constexpr int Dvs = 32 * NTS;
+    static constexpr int PPR = Dvs / 8;  // 16-byte pieces per value row
+    static constexpr int VU = kGroup * PPR / kThreads;
+    bf16x8 g[KS];
+    bf16x8 v[VU];
+
+    __device__ __forceinline__ void load(const bf16_t* gk_group, const bf16_t* v_h, int base, int n_end, int dv,
+                                         int dv0) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) tr[i] = 0.0f;
-                    tr = mfma(g0, perm[0], tr);
-                    tr = mfma(g1, perm[1], tr);
-                    bf16_t* trow = gt + (size_t)(32 * m + col) * Np + t0;
+        for (int u = 0; u < KS; ++u)
+            g[u] = *reinterpret_cast<const bf16x8*>(gk_group + 8 * ((size_t)threadIdx.x + kThreads * u));
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<uint2*>(trow + 8 * q + 4 * half) = make_uint2(
-                            pack_bf16(tr[4 * q], tr[4 * q + 1]), pack_bf16(tr[4 * q + 2], tr[4 * q + 3]));
+        for (int u = 0; u < VU; ++u) {
+            const int c = threadIdx.x + kThreads * u;
+            const int t = base + c / PPR, d0 = dv0 + 8 * (c % PPR);
+            bf16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (t < n_end) {
+                const bf16_t* src = v_h + (size_t)t * dv + d0;
+                if ((dv & 7) == 0) {
+                    if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(src);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (d0 + e < dv) x[e] = (short)src[e];
                 }
             }
+            v[u] = x;
         }
     }
-}
-
-// ----------------------------------------------------------------------------- state update
-// V rows [base, base + 128) into sV (zero past n_end), each wave its 32 rows.
-template <int NT>
-__device__ __forceinline__ void stage_v(unsigned char* sV, int vs, const bf16_t* v_h, int base, int n_end, int dv) {
-    const int l = lane_id(), w = wave_id(), half = l >> 5;
-    const int t = base + kTileT * w + (l & 31);
-    const bf16_t* row = t < n_end ? v_h + (size_t)t * dv : nullptr;
-    unsigned char* dst = sV + (size_t)(kTileT * w + (l & 31)) * vs;
+    // sG: row j = position j of the group, column = slot (Kp bf16, stride gs bytes);
+    // sV: row j = position, columns = the slice's value dims (stride vs bytes).
+    __device__ __forceinline__ void store(unsigned char* sG, int gs, unsigned char* sV, int vs) const {
+        const int l = lane_id(), w = wave_id();
 #pragma unroll
-    for (int j = 0; j < 2 * NT; ++j) {
-        const int d0 = 16 * j + 8 * half;
-        bf16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (row) {
-            if ((dv & 7) == 0) {
-                if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(row + d0);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (d0 + e < dv) x[e] = (short)row[d0 + e];
-            }
+        for (int u = 0; u < KS; ++u) {
+            const int blk = kWaves * u + w;  // = chunk / 64
+            const int tile = blk / KS, ks = blk % KS;
+            *reinterpret_cast<bf16x8*>(sG + (size_t)(kTileT * tile + (l & 31)) * gs + 2 * (16 * ks + 8 * (l >> 5))) =
+                g[u];
         }
-        *reinterpret_cast<bf16x8*>(dst + 2 * d0) = x;
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+            const int c = threadIdx.x + kThreads * u;
+            *reinterpret_cast<bf16x8*>(sV + (size_t)(c / PPR) * vs + 16 * (c % PPR)) = v[u];
+        }
     }
-}
+};
 
-// acc(tile m, n) += Gamma_K^T [k-tile m, 128 staged positions] x [V | 1][positions, d-tile n]
-// for this wave's output tiles (tiles dealt in contiguous m-major runs; n == NT is the ones
-// tile whose every column accumulates z_k).
-template <int MT, int NT, int PW>
-__device__ __forceinline__ void update_group(f32x16 (&acc)[PW], const bf16_t* gkt_h, int Np, int base,
-                                             const unsigned char* sV, int vs) {
-    constexpr int Tiles = MT * (NT + 1);
-    const int l = lane_id(), w = wave_id(), half = l >> 5;
+// ----------------------------------------------------------------------------- totals
+// [S | z] contribution Gamma_K^T [V | 1] of one sub-segment and one value slice, written as
+// fp32 rows k (slot order) of Dvs + 1 columns (the value dims, then z).
+template <int MT, int NTS>
+__global__ void __launch_bounds__(kThreads, 1)
+    gma_causal_totals(const bf16_t* __restrict__ GK, const bf16_t* __restrict__ v, float* __restrict__ tpart, int BH,
+                      int N, int Np, int dv, int NS, int nsub, int sub_len) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int Kp = 32 * MT, Dvs = 32 * NTS;
+    constexpr int gs = 2 * Kp + 32, vs = 2 * Dvs + 32;
+    using UT = UpdateTiles<MT, NTS>;
+    using GR = GroupRegs<MT, NTS>;
+    unsigned char* sG = smem;
+    unsigned char* sV = smem + (size_t)kGroup * gs;
+    int bh, sub;
+    head_part(blockIdx.x, BH, nsub, bh, sub);
+    const int y = blockIdx.y, dv0 = Dvs * y;
+    const int l = lane_id(), w = wave_id(), half = l >> 5, col = l & 31;
+    const int n_begin = sub * sub_len, n_end = min(N, n_begin + sub_len);
+    const bf16_t* gk_h = GK + (size_t)bh * Np * Kp;
+    const bf16_t* v_h = v + (size_t)bh * N * dv;
+
+    f32x16 acc[UT::MW][UT::NW];
+#pragma unroll
+    for (int i = 0; i < UT::MW; ++i)
+#pragma unroll
+        for (int j = 0; j < UT::NW; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     bf16x8 ones;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ones[j] = (short)0x3f80;
-#pragma unroll
-    for (int ks = 0; ks < kGroup / 16; ++ks) {
-        int last_m = -1;
-        bf16x8 a;
-#pragma unroll
-        for (int j = 0; j < PW; ++j) {
-            const int tile = w * PW + j;
-            if (tile < Tiles) {
-                const int m = tile / (NT + 1), n = tile % (NT + 1);
-                if (m != last_m) {
-                    a = *reinterpret_cast<const bf16x8*>(gkt_h + (size_t)(32 * m + (l & 31)) * Np + base + 16 * ks +
-                                                         8 * half);
-                    last_m = m;
-                }
-                const bf16x8 b = (n < NT) ? lds_frag_tr(sV, vs, 16 * ks, 32 * n) : ones;
-                acc[j] = mfma(a, b, acc[j]);
-            }
-        }
-    }
-}
 
-template <int MT, int NT>
-__global__ void __launch_bounds__(kThreads, 1)
-    gma_causal_totals(const bf16_t* __restrict__ GKT, const bf16_t* __restrict__ v, float* __restrict__ carry,
-                      int BH, int N, int Np, int dv, int S, int seg_len) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int Kp = 32 * MT, Dvp = 32 * NT;
-    constexpr int vs = 2 * Dvp + 32;
-    constexpr int Tiles = MT * (NT + 1);
-    constexpr int PW = (Tiles + kWaves - 1) / kWaves;
-    int bh, seg;
-    head_part(blockIdx.x, BH, S - 1, bh, seg);
-    const int l = lane_id(), w = wave_id(), half = l >> 5;
-    const int n_begin = seg * seg_len, n_end = min(N, n_begin + seg_len);
-    f32x16 acc[PW];
-#pragma unroll
-    for (int j = 0; j < PW; ++j)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
-    const bf16_t* gkt_h = GKT + (size_t)bh * Kp * Np;
-    const bf16_t* v_h = v + (size_t)bh * N * dv;
+    GR r;
+    r.load(gk_h + (size_t)n_begin * Kp, v_h, n_begin, n_end, dv, dv0);
     for (int base = n_begin; base < n_end; base += kGroup) {
-        stage_v<NT>(smem, vs, v_h, base, n_end, dv);
+        r.store(sG, gs, sV, vs);
+        if (base + kGroup < n_end) r.load(gk_h + (size_t)(base + kGroup) * Kp, v_h, base + kGroup, n_end, dv, dv0);
         lds_barrier();
-        update_group<MT, NT, PW>(acc, gkt_h, Np, base, smem, vs);
+        update_from_lds<MT, NTS, UT::MW, UT::NW>(acc, sG, gs, sV, vs, ones);
         lds_barrier();
     }
-    float* T = carry + ((size_t)bh * S + seg) * Kp * (Dvp + 1);
+
+    float* T = tpart + ((size_t)(bh * nsub + sub) * NS + y) * Kp * (Dvs + 1);
 #pragma unroll
-    for (int j = 0; j < PW; ++j) {
-        const int tile = w * PW + j;
-        if (tile < Tiles) {
-            const int m = tile / (NT + 1), n = tile % (NT + 1);
+    for (int i = 0; i < UT::MW; ++i)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int k = 32 * m + 8 * (i >> 2) + 4 * half + (i & 3);
-                if (n < NT)
-                    T[(size_t)k * (Dvp + 1) + 32 * n + (l & 31)] = acc[j][i];
-                else if ((l & 31) == 0)
-                    T[(size_t)k * (Dvp + 1) + Dvp] = acc[j][i];
+        for (int j = 0; j < UT::NW; ++j) {
+            const int m = UT::m_of(w, i), n = UT::n_of(w, j);
+            if (n > NTS) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int k = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
+                if (n < NTS)
+                    T[(size_t)k * (Dvs + 1) + 32 * n + col] = acc[i][j][e];
+                else if (col == 0)
+                    T[(size_t)k * (Dvs + 1) + Dvs] = acc[i][j][e];
             }
         }
-    }
 }
 
-// In place: slot s <- sum of the totals of segments 0..s-1 (slot 0 <- 0), in segment order.
-__global__ void __launch_bounds__(256) gma_causal_carry(float* __restrict__ carry, int BH, int S, int per) {
+// State entering segment s (s >= 1) of every head and slice: the totals of sub-segments
+// 0 .. s TS - 1 added in order.  Segment 0 starts from zero and is not stored.
+__global__ void __launch_bounds__(256)
+    gma_causal_carry(const float* __restrict__ tpart, float* __restrict__ carry, int BH, int S, int TS, int per_h) {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (size_t)BH * per) return;
-    const size_t bh = idx / per, e = idx % per;
-    float* c = carry + bh * S * per + e;
+    if (idx >= (size_t)BH * per_h) return;
+    const size_t bh = idx / per_h, e = idx % per_h;
+    const int nsub = (S - 1) * TS;
+    const float* src = tpart + bh * nsub * per_h + e;
+    float* dst = carry + bh * S * per_h + e;
     float run = 0.0f;
-    for (int s0 = 0; s0 < S; s0 += 16) {
+    for (int s0 = 0; s0 < nsub; s0 += 16) {
         float t[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) t[u] = (s0 + u < S - 1) ? c[(size_t)(s0 + u) * per] : 0.0f;
+        for (int u = 0; u < 16; ++u) t[u] = (s0 + u < nsub) ? src[(size_t)(s0 + u) * per_h] : 0.0f;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            if (s0 + u < S) c[(size_t)(s0 + u) * per] = run;
-            run += t[u];
+            if (s0 + u < nsub) {
+                run += t[u];
+                if ((s0 + u + 1) % TS == 0) dst[(size_t)((s0 + u + 1) / TS) * per_h] = run;
+            }
         }
     }
 }
 
 // ----------------------------------------------------------------------------- scan
-// Shadow (bf16, LDS) of the state, rows: S^T (Dvp rows, d), then z hi (8 rows), z lo (8 rows)
-// and 16 rows of ones; columns = components in natural order.  Written from this wave's
+// Shadow (bf16, LDS) of the state, rows: S^T (Dvs rows, value dims of the slice), then z hi
+// (8 rows), z lo (8 rows) and 16 rows of ones; columns = slots.  Written from this wave's
 // accumulator tiles.
-template <int MT, int NT, int PW>
-__device__ __forceinline__ void write_shadow(unsigned char* sS, int ss, const f32x16 (&acc)[PW]) {
-    constexpr int Tiles = MT * (NT + 1);
-    constexpr int Dvp = 32 * NT;
+template <int MT, int NTS, int MW, int NW>
+__device__ __forceinline__ void write_shadow(unsigned char* sS, int ss, const f32x16 (&acc)[MW][NW]) {
+    using UT = UpdateTiles<MT, NTS>;
+    constexpr int Dvs = 32 * NTS;
     const int l = lane_id(), w = wave_id(), half = l >> 5, col = l & 31;
 #pragma unroll
-    for (int j = 0; j < PW; ++j) {
-        const int tile = w * PW + j;
-        if (tile < Tiles) {
-            const int m = tile / (NT + 1), n = tile % (NT + 1);
+    for (int i = 0; i < MW; ++i)
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            const int m = UT::m_of(w, i), n = UT::n_of(w, j);
+            if (n > NTS) continue;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int k0 = 32 * m + 8 * q + 4 * half;
-                const float v0 = acc[j][4 * q], v1 = acc[j][4 * q + 1], v2 = acc[j][4 * q + 2],
-                            v3 = acc[j][4 * q + 3];
-                if (n < NT) {
+                const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
+                            v3 = acc[i][j][4 * q + 3];
+                if (n < NTS) {
                     uint2 p;
                     p.x = pack_bf16(v0, v1);
                     p.y = pack_bf16(v2, v3);
                     *reinterpret_cast<uint2*>(sS + (size_t)(32 * n + col) * ss + 2 * k0) = p;
                 } else if (col < 16) {
-                    // z: rows Dvp..Dvp+7 hi part, Dvp+8..Dvp+15 lo part
+                    // z: rows Dvs..Dvs+7 hi part, Dvs+8..Dvs+15 lo part
                     uint2 hi, lo;
                     hi.x = pack_bf16(v0, v1);
                     hi.y = pack_bf16(v2, v3);
                     lo.x = pack_bf16(v0 - bf16lo_to_f32(hi.x), v1 - bf16hi_to_f32(hi.x));
                     lo.y = pack_bf16(v2 - bf16lo_to_f32(hi.y), v3 - bf16hi_to_f32(hi.y));
-                    *reinterpret_cast<uint2*>(sS + (size_t)(Dvp + col) * ss + 2 * k0) = col < 8 ? hi : lo;
+                    *reinterpret_cast<uint2*>(sS + (size_t)(Dvs + col) * ss + 2 * k0) = col < 8 ? hi : lo;
                 }
             }
         }
-    }
 }
 
-template <int MT, int NT>
+template <int MT, int NTS>
 __global__ void __launch_bounds__(kThreads, 1)
-    gma_causal_scan(const bf16_t* __restrict__ GQ, const bf16_t* __restrict__ GK, const bf16_t* __restrict__ GKT,
-                    const bf16_t* __restrict__ v, const float* __restrict__ carry, bf16_t* __restrict__ out,
-                    float eps, int BH, int N, int Np, int dv, int S, int seg_len) {
+    gma_causal_scan(const bf16_t* __restrict__ GQ, const bf16_t* __restrict__ GK, const bf16_t* __restrict__ v,
+                    const float* __restrict__ carry, bf16_t* __restrict__ out, float eps, int BH, int N, int Np,
+                    int dv, int S, int NS, int seg_len) {
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int Kp = 32 * MT, Dvp = 32 * NT;
-    constexpr int vs = 2 * Dvp + 32, ss = 2 * Kp + 16;
-    constexpr int Tiles = MT * (NT + 1);
-    constexpr int PW = (Tiles + kWaves - 1) / kWaves;
+    constexpr int Kp = 32 * MT, Dvs = 32 * NTS;
+    constexpr int gs = 2 * Kp + 32, vs = 2 * Dvs + 32, ss = 2 * Kp + 16;
     constexpr int KS = Kp / 16;  // 16-wide contraction steps over the components
-    unsigned char* sV = smem;
-    unsigned char* sS = smem + (size_t)kGroup * vs;
+    using UT = UpdateTiles<MT, NTS>;
+    using GR = GroupRegs<MT, NTS>;
+    unsigned char* sG = smem;
+    unsigned char* sV = sG + (size_t)kGroup * gs;
+    unsigned char* sS = sV + (size_t)kGroup * vs;
 
     int bh, seg;
     head_part(blockIdx.x, BH, S, bh, seg);
+    const int y = blockIdx.y, dv0 = Dvs * y;
     const int l = lane_id(), w = wave_id(), half = l >> 5, col = l & 31;
     const int n_begin = seg * seg_len, n_end = min(N, n_begin + seg_len);
 
     // state entering this segment (fp32, this wave's output tiles)
-    f32x16 st[PW];
-    const float* cin = carry + ((size_t)bh * S + seg) * Kp * (Dvp + 1);
+    f32x16 st[UT::MW][UT::NW];
+    const float* cin = carry + ((size_t)(bh * S + seg) * NS + y) * Kp * (Dvs + 1);
 #pragma unroll
-    for (int j = 0; j < PW; ++j) {
-        const int tile = w * PW + j;
-        const int m = tile / (NT + 1), n = tile % (NT + 1);
+    for (int i = 0; i < UT::MW; ++i)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int k = 32 * m + 8 * (i >> 2) + 4 * half + (i & 3);
-            st[j][i] = (tile < Tiles) ? cin[(size_t)k * (Dvp + 1) + (n < NT ? 32 * n + col : Dvp)] : 0.0f;
+        for (int j = 0; j < UT::NW; ++j) {
+            const int m = UT::m_of(w, i), n = UT::n_of(w, j);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int k = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
+                st[i][j][e] = (seg > 0 && n <= NTS) ? cin[(size_t)k * (Dvs + 1) + (n < NTS ? 32 * n + col : Dvs)]
+                                                    : 0.0f;
+            }
         }
-    }
     // constant rows of the shadow: ones (den tile rows 16..31)
     for (int i = threadIdx.x; i < 16 * Kp; i += blockDim.x)
-        *reinterpret_cast<bf16_t*>(sS + (size_t)(Dvp + 16 + i / Kp) * ss + 2 * (i % Kp)) = (bf16_t)0x3f80;
-    write_shadow<MT, NT, PW>(sS, ss, st);
+        *reinterpret_cast<bf16_t*>(sS + (size_t)(Dvs + 16 + i / Kp) * ss + 2 * (i % Kp)) = (bf16_t)0x3f80;
+    write_shadow<MT, NTS, UT::MW, UT::NW>(sS, ss, st);
 
-    const bf16_t* gq_h = GQ + (size_t)bh * Np * Kp;
+    const bf16_t* gq_h = GQ + (size_t)bh * Np * Kp + 8 * l;
     const bf16_t* gk_h = GK + (size_t)bh * Np * Kp;
-    const bf16_t* gkt_h = GKT + (size_t)bh * Kp * Np;
     const bf16_t* v_h = v + (size_t)bh * N * dv;
     bf16_t* o_h = out + (size_t)bh * N * dv;
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (short)0x3f80;
     // den-tile operand for the intra term: ones in rows 0..7 (they add to the z-hi rows)
     bf16x8 den_ones;
 #pragma unroll
     for (int j = 0; j < 8; ++j) den_ones[j] = (short)(col < 8 ? 0x3f80 : 0);
 
+    // Gamma_Q fragments of this wave's chunk of the group at `base`
+    auto load_q = [&](bf16x8 (&qf)[KS], int base) {
+        const bf16_t* src = gq_h + (size_t)(base / kTileT + w) * KS * kFrag;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + (size_t)ks * kFrag);
+    };
+
+    GR r;
+    bf16x8 qn[KS];
+    r.load(gk_h + (size_t)n_begin * Kp, v_h, n_begin, n_end, dv, dv0);
+    load_q(qn, n_begin);
+
     for (int base = n_begin; base < n_end; base += kGroup) {
-        stage_v<NT>(sV, vs, v_h, base, n_end, dv);
+        r.store(sG, gs, sV, vs);
+        bf16x8 qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
+        if (base + kGroup < n_end) {
+            r.load(gk_h + (size_t)(base + kGroup) * Kp, v_h, base + kGroup, n_end, dv, dv0);
+            load_q(qn, base + kGroup);
+        }
         lds_barrier();
         // ---- outputs of chunk w: positions base + 32w + col
         {
-            const int i0 = base + kTileT * w;
-            const int t = i0 + col;
-            bf16x8 qf[KS];
+            const int t = base + kTileT * w + col;
+            f32x16 o[NTS + 1];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qf[ks] = *reinterpret_cast<const bf16x8*>(gq_h + (size_t)t * Kp + 16 * ks + 8 * half);
-            f32x16 o[NT + 1];
-#pragma unroll
-            for (int n = 0; n <= NT; ++n)
+            for (int n = 0; n <= NTS; ++n)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[n][i] = 0.0f;
             // inter-group: Gamma_Q [S | z] from the shadow
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int n = 0; n <= NT; ++n) {
+                for (int n = 0; n <= NTS; ++n) {
                     const bf16x8 a =
                         *reinterpret_cast<const bf16x8*>(sS + (size_t)(32 * n + col) * ss + 2 * (16 * ks + 8 * half));
                     o[n] = mfma(a, qf[ks], o[n]);
@@ -450,10 +493,10 @@ __global__ void __launch_bounds__(kThreads, 1)
                 f32x16 aff;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) aff[i] = 0.0f;
-                const bf16_t* krow = gk_h + (size_t)(base + kTileT * c + col) * Kp;
+                const unsigned char* grow = sG + (size_t)(kTileT * c + col) * gs + 16 * half;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    aff = mfma(*reinterpret_cast<const bf16x8*>(krow + 16 * ks + 8 * half), qf[ks], aff);
+                    aff = mfma(*reinterpret_cast<const bf16x8*>(grow + 32 * ks), qf[ks], aff);
                 if (c == w) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
@@ -465,20 +508,20 @@ __global__ void __launch_bounds__(kThreads, 1)
                 for (int sh = 0; sh < 2; ++sh) {
                     const bf16x8 b = pack8(aff, 8 * sh, 1.0f);
 #pragma unroll
-                    for (int n = 0; n < NT; ++n)
+                    for (int n = 0; n < NTS; ++n)
                         o[n] = mfma(lds_frag_tr_crows(sV, vs, kTileT * c + 16 * sh, 32 * n), b, o[n]);
-                    o[NT] = mfma(den_ones, b, o[NT]);
+                    o[NTS] = mfma(den_ones, b, o[NTS]);
                 }
             }
-            const float den = o[NT][0] + o[NT][4];
+            const float den = o[NTS][0] + o[NTS][4];
             const float inv = 1.0f / (den + eps);
             if (t < n_end) {
                 bf16_t* orow = o_h + (size_t)t * dv;
 #pragma unroll
-                for (int n = 0; n < NT; ++n)
+                for (int n = 0; n < NTS; ++n)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int d0 = 32 * n + 8 * q + 4 * half;
+                        const int d0 = dv0 + 32 * n + 8 * q + 4 * half;
                         if ((dv & 3) == 0) {
                             if (d0 < dv) {
                                 uint2 p;
@@ -488,25 +531,25 @@ __global__ void __launch_bounds__(kThreads, 1)
                             }
                         } else {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (d0 + r < dv) orow[d0 + r] = (bf16_t)bf16_bits_rne(o[n][4 * q + r] * inv);
+                            for (int rr = 0; rr < 4; ++rr)
+                                if (d0 + rr < dv) orow[d0 + rr] = (bf16_t)bf16_bits_rne(o[n][4 * q + rr] * inv);
                         }
                     }
             }
         }
         // ---- state += Gamma_K^T [V | 1] over the group (this wave's tiles)
-        update_group<MT, NT, PW>(st, gkt_h, Np, base, sV, vs);
-        lds_barrier();  // every wave is done reading sV and the old shadow
-        write_shadow<MT, NT, PW>(sS, ss, st);
+        update_from_lds<MT, NTS, UT::MW, UT::NW>(st, sG, gs, sV, vs, ones);
+        lds_barrier();  // every wave is done reading sG, sV and the old shadow
+        write_shadow<MT, NTS, UT::MW, UT::NW>(sS, ss, st);
     }
 }
 
 // ----------------------------------------------------------------------------- dispatch
-typedef void (*RespFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, bf16_t*, bf16_t*, int, int,
-                       int, int, int, int, int);
-typedef void (*TotFn)(const bf16_t*, const bf16_t*, float*, int, int, int, int, int, int);
-typedef void (*ScanFn)(const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, float, int,
-                       int, int, int, int, int);
+typedef void (*RespFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, bf16_t*, int, int, int,
+                       int, int, int, int);
+typedef void (*TotFn)(const bf16_t*, const bf16_t*, float*, int, int, int, int, int, int, int);
+typedef void (*ScanFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, float, int, int, int, int,
+                       int, int, int);
 
 template <int MT, int NC>
 RespFn resp_fn(int nph) {
@@ -544,20 +587,19 @@ int resp_phases(const Geo& g) {
     return 0;
 }
 template <int MT>
-bool select_scan_nt(int NT, TotFn& tf, ScanFn& sf) {
-    switch (NT) {
+bool select_scan_nt(int NTS, TotFn& tf, ScanFn& sf) {
+    switch (NTS) {
         case 1: tf = gma_causal_totals<MT, 1>; sf = gma_causal_scan<MT, 1>; return true;
         case 2: tf = gma_causal_totals<MT, 2>; sf = gma_causal_scan<MT, 2>; return true;
-        case 4: tf = gma_causal_totals<MT, 4>; sf = gma_causal_scan<MT, 4>; return true;
     }
     return false;
 }
-bool select_scan(const Geo& g, TotFn& tf, ScanFn& sf) {
+bool select_scan(const Geo& g, int NTS, TotFn& tf, ScanFn& sf) {
     switch (g.MT) {
-        case 1: return select_scan_nt<1>(g.NT, tf, sf);
-        case 2: return select_scan_nt<2>(g.NT, tf, sf);
-        case 4: return select_scan_nt<4>(g.NT, tf, sf);
-        case 8: return select_scan_nt<8>(g.NT, tf, sf);
+        case 1: return select_scan_nt<1>(NTS, tf, sf);
+        case 2: return select_scan_nt<2>(NTS, tf, sf);
+        case 4: return select_scan_nt<4>(NTS, tf, sf);
+        case 8: return select_scan_nt<8>(NTS, tf, sf);
     }
     return false;
 }
@@ -570,7 +612,8 @@ hipError_t set_lds(const void* f, size_t bytes) {
 
 bool causal_supported(const gma_desc& d) {
     const Geo g = geometry(d);
-    return scan_lds_bytes(g) <= kLdsMax && totals_lds_bytes(g) <= kLdsMax && resp_phases(g) > 0;
+    const int Dvs = g.Dvp < kSliceV ? g.Dvp : kSliceV;
+    return scan_lds_bytes(g, Dvs) <= kLdsMax && resp_phases(g) > 0;
 }
 
 size_t causal_workspace(const gma_desc& d) { return causal_layout(d).total; }
@@ -583,16 +626,17 @@ hipError_t causal_forward(const Args& a) {
     float* cvec = reinterpret_cast<float*>(a.ws + L.C);
     bf16_t* GQ = reinterpret_cast<bf16_t*>(a.ws + L.gq);
     bf16_t* GK = reinterpret_cast<bf16_t*>(a.ws + L.gk);
-    bf16_t* GKT = reinterpret_cast<bf16_t*>(a.ws + L.gkt);
+    float* tpart = reinterpret_cast<float*>(a.ws + L.tpart);
     float* carry = reinterpret_cast<float*>(a.ws + L.carry);
     const int BH = d.B * d.H;
+    const int NTS = L.Dvs / 32;
     hipError_t e;
 
     const int nph = resp_phases(g);
     RespFn rf = nph ? select_resp(g, nph) : nullptr;
     TotFn tf;
     ScanFn sf;
-    if (!rf || !select_scan(g, tf, sf)) return hipErrorNotSupported;
+    if (!rf || !select_scan(g, NTS, tf, sf)) return hipErrorNotSupported;
 
     if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
 
@@ -608,32 +652,32 @@ hipError_t causal_forward(const Args& a) {
     if ((e = set_lds(reinterpret_cast<const void*>(rf), rl)) != hipSuccess) return e;
     rec_begin(a, "gma_causal_resp");
     hipLaunchKernelGGL(rf, dim3(BH * parts, 2), dim3(64 * kRespWaves), rl, a.stream, static_cast<const bf16_t*>(a.qr),
-                       static_cast<const bf16_t*>(a.kr), W, cvec, GQ, GK, GKT, BH, d.H, d.N, L.Np, d.d_r, parts,
+                       static_cast<const bf16_t*>(a.kr), W, cvec, GQ, GK, BH, d.H, d.N, L.Np, d.d_r, parts,
                        part_len);
     rec_end(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    const int per = g.Kp * (g.Dvp + 1);
     if (L.S > 1) {
-        const size_t tl = totals_lds_bytes(g);
+        const size_t tl = totals_lds_bytes(g, L.Dvs);
         if ((e = set_lds(reinterpret_cast<const void*>(tf), tl)) != hipSuccess) return e;
         rec_begin(a, "gma_causal_totals");
-        hipLaunchKernelGGL(tf, dim3(BH * (L.S - 1)), dim3(kThreads), tl, a.stream, GKT,
-                           static_cast<const bf16_t*>(a.v), carry, BH, d.N, L.Np, d.d_v, L.S, L.seg_len);
+        hipLaunchKernelGGL(tf, dim3(BH * L.nsub, L.NS), dim3(kThreads), tl, a.stream, GK,
+                           static_cast<const bf16_t*>(a.v), tpart, BH, d.N, L.Np, d.d_v, L.NS, L.nsub, L.sub_len);
+        rec_end(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int per_h = L.NS * g.Kp * (L.Dvs + 1);
+        rec_begin(a, "gma_causal_carry");
+        gma_causal_carry<<<dim3((unsigned)(((size_t)BH * per_h + 255) / 256)), dim3(256), 0, a.stream>>>(
+            tpart, carry, BH, L.S, L.TS, per_h);
         rec_end(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    rec_begin(a, "gma_causal_carry");
-    gma_causal_carry<<<dim3((unsigned)(((size_t)BH * per + 255) / 256)), dim3(256), 0, a.stream>>>(carry, BH, L.S,
-                                                                                                   per);
-    rec_end(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    const size_t sl = scan_lds_bytes(g);
+    const size_t sl = scan_lds_bytes(g, L.Dvs);
     if ((e = set_lds(reinterpret_cast<const void*>(sf), sl)) != hipSuccess) return e;
     rec_begin(a, "gma_causal_scan");
-    hipLaunchKernelGGL(sf, dim3(BH * L.S), dim3(kThreads), sl, a.stream, GQ, GK, GKT, static_cast<const bf16_t*>(a.v),
-                       carry, static_cast<bf16_t*>(a.out), a.eps, BH, d.N, L.Np, d.d_v, L.S, L.seg_len);
+    hipLaunchKernelGGL(sf, dim3(BH * L.S, L.NS), dim3(kThreads), sl, a.stream, GQ, GK, static_cast<const bf16_t*>(a.v),
+                       carry, static_cast<bf16_t*>(a.out), a.eps, BH, d.N, L.Np, d.d_v, L.S, L.NS, L.seg_len);
     rec_end(a);
     return hipGetLastError();
 }
