@@ -184,12 +184,16 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
     for (int j = 0; j < 8; ++j) ones[j] = (short)0x3f80;
 
-    // k rows for steps 0 and 1, v rows for step 0 (register prefetch)
+    // coefficients, k rows for steps 0 and 1 and v rows for step 0: all loads in flight together
     bf16x8 xa[NC], xb[NC], vcur[2 * NT];
-    load_xrow<NC>(xa, krow(0), dr);
-    load_xrow<NC>(xb, krow(1), dr);
-    load_vrow<NT>(vcur, vrow(0), dv);
-    stage_coefficients(sW, sC, W, cvec, h, Kp, Dp, wstride);
+    {
+        CoefRegs<MT, NC, kThreads> cr;
+        cr.load(W, cvec, h);
+        load_xrow<NC>(xa, krow(0), dr);
+        load_xrow<NC>(xb, krow(1), dr);
+        load_vrow<NT>(vcur, vrow(0), dv);
+        cr.store(sW, sC, wstride);
+    }
     __syncthreads();
 
     f32x16 accA[MT], accB[MT];
@@ -281,39 +285,50 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
         load_xrow<NC>(xr, t < n_end ? q_h + (size_t)t * dr : nullptr, dr);
     }
 
-    stage_coefficients(sW, sC, W, cvec, h, Kp, Dp, wstride);
-    // memory rows: Vt^T (Dvp rows), then Z hi (8 rows), Z lo (8 rows), ones (16 rows);
-    // columns in the permuted component order of the logits tiles
     // the head's memory [Vt | Z] = sum of the S split partials of the write kernel, added in
-    // split order (every workgroup of the head forms the identical sum); loads of one split are
-    // issued together.  Vt^T goes to LDS rows 0..Dvp-1 in the permuted component order.
+    // split order (every workgroup of the head forms the identical sum).  The coefficient
+    // loads and the partial loads of up to SB splits are in flight together.  Vt^T goes to
+    // LDS rows 0..Dvp-1 in the permuted component order of the logits tiles, then Z hi
+    // (8 rows), Z lo (8 rows) and ones (16 rows).
     {
         constexpr int kThr = 64 * kReadWaves;
         constexpr int kVec = Kp * Dvp / 4;
         constexpr int P = (kVec + kThr - 1) / kThr;
+        constexpr int SB = P <= 4 ? 4 : (P <= 8 ? 2 : 1);  // splits per batch of loads
         const float* pv0 = part_v + (size_t)bh * S * Kp * Dvp;
         const float* pz0 = part_z + (size_t)bh * S * Kp;
         float4 sum[P];
 #pragma unroll
         for (int p = 0; p < P; ++p) sum[p] = make_float4(0.f, 0.f, 0.f, 0.f);
         float zsum = 0.0f;
-        for (int s = 0; s < S; ++s) {
-            const float4* src = reinterpret_cast<const float4*>(pv0 + (size_t)s * Kp * Dvp);
-            float4 x[P];
+        CoefRegs<MT, NC, kThr> cr;
+        cr.load(W, cvec, h);
+        for (int s0 = 0; s0 < S; s0 += SB) {
+            float4 x[SB][P];
+            float zx[SB];
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int i = threadIdx.x + p * kThr;
-                if (i < kVec) x[p] = src[i];
-            }
-            const float zx = ((int)threadIdx.x < Kp) ? pz0[(size_t)s * Kp + threadIdx.x] : 0.0f;
+            for (int u = 0; u < SB; ++u) {
+                const bool ok = s0 + u < S;
+                const float4* src = reinterpret_cast<const float4*>(pv0 + (size_t)(ok ? s0 + u : 0) * Kp * Dvp);
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                sum[p].x += x[p].x;
-                sum[p].y += x[p].y;
-                sum[p].z += x[p].z;
-                sum[p].w += x[p].w;
+                for (int p = 0; p < P; ++p) {
+                    const int i = threadIdx.x + p * kThr;
+                    x[u][p] = (ok && i < kVec) ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                zx[u] = (ok && (int)threadIdx.x < Kp) ? pz0[(size_t)(s0 + u) * Kp + threadIdx.x] : 0.0f;
             }
-            zsum += zx;
+            if (s0 == 0) cr.store(sW, sC, wstride);
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    sum[p].x += x[u][p].x;
+                    sum[p].y += x[u][p].y;
+                    sum[p].z += x[u][p].z;
+                    sum[p].w += x[u][p].w;
+                }
+                zsum += zx[u];
+            }
         }
 #pragma unroll
         for (int p = 0; p < P; ++p) {

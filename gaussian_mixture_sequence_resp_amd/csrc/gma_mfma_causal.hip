@@ -230,28 +230,39 @@ struct GroupRegs {
     bf16x8 g[KS];
     bf16x8 v[VU];
 
+    __device__ __forceinline__ void load_g(int u, const bf16_t* gk_group) {
+        g[u] = *reinterpret_cast<const bf16x8*>(gk_group + 8 * ((size_t)threadIdx.x + kThreads * u));
+    }
+    __device__ __forceinline__ void load_v(int u, const bf16_t* v_h, int base, int n_end, int dv, int dv0) {
+        const int c = threadIdx.x + kThreads * u;
+        const int t = base + c / PPR, d0 = dv0 + 8 * (c % PPR);
+        bf16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (t < n_end) {
+            const bf16_t* src = v_h + (size_t)t * dv + d0;
+            if ((dv & 7) == 0) {
+                if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(src);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (d0 + e < dv) x[e] = (short)src[e];
+            }
+        }
+        v[u] = x;
+    }
     __device__ __forceinline__ void load(const bf16_t* gk_group, const bf16_t* v_h, int base, int n_end, int dv,
                                          int dv0) {
 #pragma unroll
-        for (int u = 0; u < KS; ++u)
-            g[u] = *reinterpret_cast<const bf16x8*>(gk_group + 8 * ((size_t)threadIdx.x + kThreads * u));
+        for (int u = 0; u < KS; ++u) load_g(u, gk_group);
 #pragma unroll
-        for (int u = 0; u < VU; ++u) {
-            const int c = threadIdx.x + kThreads * u;
-            const int t = base + c / PPR, d0 = dv0 + 8 * (c % PPR);
-            bf16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (t < n_end) {
-                const bf16_t* src = v_h + (size_t)t * dv + d0;
-                if ((dv & 7) == 0) {
-                    if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(src);
-                } else {
+        for (int u = 0; u < VU; ++u) load_v(u, v_h, base, n_end, dv, dv0);
+    }
+    // The share of step s (of 8) of the loads above: indices u with u % 8 == s.
+    __device__ __forceinline__ void load_step(int s, const bf16_t* gk_group, const bf16_t* v_h, int base, int n_end,
+                                              int dv, int dv0) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (d0 + e < dv) x[e] = (short)src[e];
-                }
-            }
-            v[u] = x;
-        }
+        for (int u = s; u < KS; u += 8) load_g(u, gk_group);
+#pragma unroll
+        for (int u = s; u < VU; u += 8) load_v(u, v_h, base, n_end, dv, dv0);
     }
     // sG: row j = position j of the group, column = slot (Kp bf16, stride gs bytes);
     // sV: row j = position, columns = the slice's value dims (stride vs bytes).
@@ -305,13 +316,18 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
     for (int j = 0; j < 8; ++j) ones[j] = (short)0x3f80;
 
+    // the next group's loads are issued between the MFMAs of the current group's update
     GR r;
     r.load(gk_h + (size_t)n_begin * Kp, v_h, n_begin, n_end, dv, dv0);
     for (int base = n_begin; base < n_end; base += kGroup) {
         r.store(sG, gs, sV, vs);
-        if (base + kGroup < n_end) r.load(gk_h + (size_t)(base + kGroup) * Kp, v_h, base + kGroup, n_end, dv, dv0);
         lds_barrier();
-        update_from_lds<MT, NTS, UT::MW, UT::NW>(acc, sG, gs, sV, vs, ones);
+        const int nb = base + kGroup;
+        const bool more = nb < n_end;
+        const bf16_t* gnext = gk_h + (size_t)nb * Kp;
+        update_from_lds<MT, NTS, UT::MW, UT::NW>(acc, sG, gs, sV, vs, ones, [&](int s8) {
+            if (more) r.load_step(s8, gnext, v_h, nb, n_end, dv, dv0);
+        });
         lds_barrier();
     }
 
@@ -334,26 +350,21 @@ __global__ void __launch_bounds__(kThreads, 1)
 }
 
 // State entering segment s (s >= 1) of every head and slice: the totals of sub-segments
-// 0 .. s TS - 1 added in order.  Segment 0 starts from zero and is not stored.
+// 0 .. s TS - 1 added in order.  Segment 0 starts from zero and is not stored.  Grid:
+// (per_h / 256 rounded up, min(BH, 65535)), heads strided by gridDim.y; per_h = NS Kp (Dvs + 1)
+// floats per head.
 __global__ void __launch_bounds__(256)
     gma_causal_carry(const float* __restrict__ tpart, float* __restrict__ carry, int BH, int S, int TS, int per_h) {
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (size_t)BH * per_h) return;
-    const size_t bh = idx / per_h, e = idx % per_h;
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= per_h) return;
     const int nsub = (S - 1) * TS;
-    const float* src = tpart + bh * nsub * per_h + e;
-    float* dst = carry + bh * S * per_h + e;
-    float run = 0.0f;
-    for (int s0 = 0; s0 < nsub; s0 += 16) {
-        float t[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) t[u] = (s0 + u < nsub) ? src[(size_t)(s0 + u) * per_h] : 0.0f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            if (s0 + u < nsub) {
-                run += t[u];
-                if ((s0 + u + 1) % TS == 0) dst[(size_t)((s0 + u + 1) / TS) * per_h] = run;
-            }
+    for (size_t bh = blockIdx.y; bh < (size_t)BH; bh += gridDim.y) {
+        const float* src = tpart + bh * nsub * per_h + e;
+        float* dst = carry + bh * S * per_h + e;
+        float run = 0.0f;
+        for (int s = 1; s < S; ++s) {
+            for (int ts = 0; ts < TS; ++ts) run += src[(size_t)((s - 1) * TS + ts) * per_h];
+            dst[(size_t)s * per_h] = run;
         }
     }
 }
@@ -417,7 +428,8 @@ __global__ void __launch_bounds__(kThreads, 1)
     const int l = lane_id(), w = wave_id(), half = l >> 5, col = l & 31;
     const int n_begin = seg * seg_len, n_end = min(N, n_begin + seg_len);
 
-    // state entering this segment (fp32, this wave's output tiles)
+    // state entering this segment (fp32, this wave's output tiles).  Segment 0 starts from
+    // zero: its carry slot is never written and is read only to keep the loads unconditional.
     f32x16 st[UT::MW][UT::NW];
     const float* cin = carry + ((size_t)(bh * S + seg) * NS + y) * Kp * (Dvs + 1);
 #pragma unroll
@@ -425,16 +437,22 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
         for (int j = 0; j < UT::NW; ++j) {
             const int m = UT::m_of(w, i), n = UT::n_of(w, j);
+            const int cc = n < NTS ? 32 * n + col : Dvs;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int k = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
-                st[i][j][e] = (seg > 0 && n <= NTS) ? cin[(size_t)k * (Dvs + 1) + (n < NTS ? 32 * n + col : Dvs)]
-                                                    : 0.0f;
+                st[i][j][e] = cin[(size_t)k * (Dvs + 1) + cc];
             }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st[i][j][e] = (seg > 0 && n <= NTS) ? st[i][j][e] : 0.0f;
         }
     // constant rows of the shadow: ones (den tile rows 16..31)
-    for (int i = threadIdx.x; i < 16 * Kp; i += blockDim.x)
-        *reinterpret_cast<bf16_t*>(sS + (size_t)(Dvs + 16 + i / Kp) * ss + 2 * (i % Kp)) = (bf16_t)0x3f80;
+    for (int i = threadIdx.x; i < 2 * Kp; i += blockDim.x) {
+        bf16x8 o8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = (short)0x3f80;
+        *reinterpret_cast<bf16x8*>(sS + (size_t)(Dvs + 16 + i / (Kp / 8)) * ss + 16 * (i % (Kp / 8))) = o8;
+    }
     write_shadow<MT, NTS, UT::MW, UT::NW>(sS, ss, st);
 
     const bf16_t* gq_h = GQ + (size_t)bh * Np * Kp + 8 * l;
@@ -449,27 +467,20 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
     for (int j = 0; j < 8; ++j) den_ones[j] = (short)(col < 8 ? 0x3f80 : 0);
 
-    // Gamma_Q fragments of this wave's chunk of the group at `base`
-    auto load_q = [&](bf16x8 (&qf)[KS], int base) {
-        const bf16_t* src = gq_h + (size_t)(base / kTileT + w) * KS * kFrag;
+    // Group prefetch into registers: Gamma_K and V rows (stored to LDS at the top of the
+    // group) and this wave's Gamma_Q fragments, all loaded during the previous group's state
+    // update (qf is dead from the end of the intra term on).
+    GR r;
+    bf16x8 qf[KS];
+    r.load(gk_h + (size_t)n_begin * Kp, v_h, n_begin, n_end, dv, dv0);
+    {
+        const bf16_t* src = gq_h + (size_t)(n_begin / kTileT + w) * KS * kFrag;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + (size_t)ks * kFrag);
-    };
-
-    GR r;
-    bf16x8 qn[KS];
-    r.load(gk_h + (size_t)n_begin * Kp, v_h, n_begin, n_end, dv, dv0);
-    load_q(qn, n_begin);
+    }
 
     for (int base = n_begin; base < n_end; base += kGroup) {
         r.store(sG, gs, sV, vs);
-        bf16x8 qf[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
-        if (base + kGroup < n_end) {
-            r.load(gk_h + (size_t)(base + kGroup) * Kp, v_h, base + kGroup, n_end, dv, dv0);
-            load_q(qn, base + kGroup);
-        }
         lds_barrier();
         // ---- outputs of chunk w: positions base + 32w + col
         {
@@ -479,15 +490,22 @@ __global__ void __launch_bounds__(kThreads, 1)
             for (int n = 0; n <= NTS; ++n)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[n][i] = 0.0f;
-            // inter-group: Gamma_Q [S | z] from the shadow
+            // inter-group: Gamma_Q [S | z] from the shadow (A fragments read one step ahead)
+            {
+                constexpr int NI = KS * (NTS + 1);
+                const unsigned char* srow = sS + (size_t)col * ss + 16 * half;
+                bf16x8 an = *reinterpret_cast<const bf16x8*>(srow);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int n = 0; n <= NTS; ++n) {
-                    const bf16x8 a =
-                        *reinterpret_cast<const bf16x8*>(sS + (size_t)(32 * n + col) * ss + 2 * (16 * ks + 8 * half));
+                for (int idx = 0; idx < NI; ++idx) {
+                    const int ks = idx / (NTS + 1), n = idx % (NTS + 1);
+                    const bf16x8 a = an;
+                    if (idx + 1 < NI) {
+                        const int ks2 = (idx + 1) / (NTS + 1), n2 = (idx + 1) % (NTS + 1);
+                        an = *reinterpret_cast<const bf16x8*>(srow + (size_t)32 * n2 * ss + 32 * ks2);
+                    }
                     o[n] = mfma(a, qf[ks], o[n]);
                 }
+            }
             // intra-group: chunks c <= w; A[j', i] = gamma_K,j' . gamma_Q,i, zero for j' > i
             for (int c = 0; c <= w; ++c) {
                 f32x16 aff;
@@ -537,8 +555,19 @@ __global__ void __launch_bounds__(kThreads, 1)
                     }
             }
         }
-        // ---- state += Gamma_K^T [V | 1] over the group (this wave's tiles)
-        update_from_lds<MT, NTS, UT::MW, UT::NW>(st, sG, gs, sV, vs, ones);
+        // ---- state += Gamma_K^T [V | 1] over the group (this wave's tiles); the next group's
+        // loads go out between its MFMAs
+        const int nb = base + kGroup;
+        const bool more = nb < n_end;
+        const bf16_t* gnext = gk_h + (size_t)nb * Kp;
+        const bf16_t* qnext = gq_h + (size_t)(nb / kTileT + w) * KS * kFrag;
+        update_from_lds<MT, NTS, UT::MW, UT::NW>(st, sG, gs, sV, vs, ones, [&](int s8) {
+            if (more) {
+                r.load_step(s8, gnext, v_h, nb, n_end, dv, dv0);
+#pragma unroll
+                for (int ks = s8; ks < KS; ks += 8) qf[ks] = *reinterpret_cast<const bf16x8*>(qnext + (size_t)ks * kFrag);
+            }
+        });
         lds_barrier();  // every wave is done reading sG, sV and the old shadow
         write_shadow<MT, NTS, UT::MW, UT::NW>(sS, ss, st);
     }
@@ -667,8 +696,8 @@ hipError_t causal_forward(const Args& a) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int per_h = L.NS * g.Kp * (L.Dvs + 1);
         rec_begin(a, "gma_causal_carry");
-        gma_causal_carry<<<dim3((unsigned)(((size_t)BH * per_h + 255) / 256)), dim3(256), 0, a.stream>>>(
-            tpart, carry, BH, L.S, L.TS, per_h);
+        gma_causal_carry<<<dim3((unsigned)((per_h + 255) / 256), (unsigned)(BH < 65535 ? BH : 65535)), dim3(256), 0,
+                           a.stream>>>(tpart, carry, BH, L.S, L.TS, per_h);
         rec_end(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

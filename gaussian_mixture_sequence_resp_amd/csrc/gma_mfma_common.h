@@ -396,9 +396,11 @@ struct UpdateTiles {
     __device__ static int n_of(int w, int j) { return MT >= 4 ? j : (w % WPM) * NW + j; }
 };
 
-template <int MT, int NT, int MW, int NW>
+// `work(ks)` runs once per 16-position step, between the step's LDS reads and its MFMAs
+// (a hook for issuing other loads in the shadow of the matrix cores).
+template <int MT, int NT, int MW, int NW, typename Work>
 __device__ __forceinline__ void update_from_lds(f32x16 (&acc)[MW][NW], const unsigned char* sG, int gs,
-                                                const unsigned char* sV, int vs, const bf16x8& ones) {
+                                                const unsigned char* sV, int vs, const bf16x8& ones, Work&& work) {
     using UT = UpdateTiles<MT, NT>;
     const int w = wave_id();
 #pragma unroll
@@ -412,11 +414,18 @@ __device__ __forceinline__ void update_from_lds(f32x16 (&acc)[MW][NW], const uns
             const bf16x8 t = lds_frag_tr(sV, vs, 16 * ks, n < NT ? 32 * n : 0);
             b[j] = n < NT ? t : ones;
         }
+        work(ks);
 #pragma unroll
         for (int i = 0; i < UT::MW; ++i)
 #pragma unroll
             for (int j = 0; j < UT::NW; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]);
     }
+}
+
+template <int MT, int NT, int MW, int NW>
+__device__ __forceinline__ void update_from_lds(f32x16 (&acc)[MW][NW], const unsigned char* sG, int gs,
+                                                const unsigned char* sV, int vs, const bf16x8& ones) {
+    update_from_lds<MT, NT, MW, NW>(acc, sG, gs, sV, vs, ones, [](int) {});
 }
 
 // Position of component k inside its 16-wide block so that the C registers 8s..8s+7 of a

@@ -35,29 +35,59 @@ inline Geo geometry(const gma_desc& d) {
 
 constexpr size_t kLdsMax = 160 * 1024 - 256;  // leave room for static LDS
 
-// Copy the coefficient block and c of head h into LDS (rows padded to g.wstride).  Loads
-// are issued in batches of 8 per thread before their LDS stores, so their latencies overlap.
-__device__ __forceinline__ void stage_coefficients(unsigned char* sW, float* sC, const bf16_t* W, const float* cvec,
-                                                   int h, int Kp, int Dp, int wstride) {
-    const int vec_per_row = (8 * Dp) / 16;  // 16-byte vectors per row
-    const int total = Kp * vec_per_row;
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(W + (size_t)h * Kp * 4 * Dp);
-    for (int i0 = threadIdx.x; i0 < total; i0 += 8 * blockDim.x) {
-        bf16x8 v[8];
+// Coefficient block [ah | al | bh | bl] (Kp rows of 8 Dp bytes) and c of head h, staged into
+// LDS (rows padded to wstride) by a workgroup of THREADS threads: load() issues this thread's
+// first batch of global loads (up to 16 vectors), store() writes it to LDS and stages any
+// remaining batches, so a caller can put its other prologue loads in flight in between.
+template <int MT, int NC, int THREADS>
+struct CoefRegs {
+    static constexpr int Kp = 32 * MT, Dp = 16 * NC;
+    static constexpr int VPR = (8 * Dp) / 16;  // 16-byte vectors per row
+    static constexpr int TOTAL = Kp * VPR;
+    static constexpr int PER = (TOTAL + THREADS - 1) / THREADS;
+    static constexpr int BATCH = PER < 16 ? PER : 16;
+    static constexpr int CPER = (Kp + THREADS - 1) / THREADS;
+    bf16x8 v[BATCH];
+    float c[CPER];
+    const unsigned char* src;
+
+    __device__ __forceinline__ void load_batch(int u0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * blockDim.x;
-            if (i < total) v[u] = *reinterpret_cast<const bf16x8*>(src + 16 * (size_t)i);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * blockDim.x;
-            if (i < total)
-                *reinterpret_cast<bf16x8*>(sW + (size_t)(i / vec_per_row) * wstride + 16 * (i % vec_per_row)) = v[u];
+        for (int u = 0; u < BATCH; ++u) {
+            const int i = threadIdx.x + (u0 + u) * THREADS;
+            if (u0 + u < PER && i < TOTAL) v[u] = *reinterpret_cast<const bf16x8*>(src + 16 * (size_t)i);
         }
     }
-    for (int i = threadIdx.x; i < Kp; i += blockDim.x) sC[i] = cvec[(size_t)h * Kp + i];
-}
+    __device__ __forceinline__ void store_batch(unsigned char* sW, int wstride, int u0) const {
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int i = threadIdx.x + (u0 + u) * THREADS;
+            if (u0 + u < PER && i < TOTAL)
+                *reinterpret_cast<bf16x8*>(sW + (size_t)(i / VPR) * wstride + 16 * (i % VPR)) = v[u];
+        }
+    }
+    __device__ __forceinline__ void load(const bf16_t* W, const float* cvec, int h) {
+        src = reinterpret_cast<const unsigned char*>(W + (size_t)h * Kp * 4 * Dp);
+        load_batch(0);
+#pragma unroll
+        for (int u = 0; u < CPER; ++u) {
+            const int i = threadIdx.x + u * THREADS;
+            if (i < Kp) c[u] = cvec[(size_t)h * Kp + i];
+        }
+    }
+    __device__ __forceinline__ void store(unsigned char* sW, float* sC, int wstride) {
+        store_batch(sW, wstride, 0);
+#pragma unroll
+        for (int u = 0; u < CPER; ++u) {
+            const int i = threadIdx.x + u * THREADS;
+            if (i < Kp) sC[i] = c[u];
+        }
+        for (int u0 = BATCH; u0 < PER; u0 += BATCH) {
+            load_batch(u0);
+            store_batch(sW, wstride, u0);
+        }
+    }
+};
 
 // Map a linear block index to (head, part) so that the parts of one head run on one XCD
 // (blocks are dealt round-robin to the 8 XCDs): they then share the head's coefficients
