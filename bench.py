@@ -42,25 +42,32 @@ def metric_name() -> str:
 
 
 def algorithmic(w, kernel: str):
-    """Algorithmic bytes and flops of one launch of `kernel` on workload `w`.
+    """Algorithmic bytes and flops of one launch of `kernel` on workload `w`, or None for
+    a kernel that carries no algorithmic share (parameter prep, the causal segment totals
+    and carries: workspace traffic and recompute, not work the method itself must do).
 
     Per token-head the whole forward must read q, k, v once and write out once:
-    s_in*(2 d_r + d_v) + s_out*d_v bytes; it must do 4K(2d_r+1) flops for the Q and K
-    log-density contractions and 4K(d_v+1) for the write and read of [Vt | Z].  A kernel
-    that does one side of that work is charged that side only.
+    s*(2 d_r + 2 d_v) bytes; it must do 4K(2d_r+1) flops for the Q and K log-density
+    contractions and 4K(d_v+1) for the write and read of [Vt | Z].  A kernel that does one
+    part of that work is charged that part only.
     """
     s = 4 if w.dtype == "f32" else 2
     th = w.B * w.H * w.N
     K, dr, dv = w.K, w.d_r, w.d_v
-    side_flops = 2 * K * (2 * dr + 1) + 2 * K * (dv + 1)
-    if "write" in kernel:      # reads k and v, forms Gamma_K and Gamma_K^T [V, 1]
-        return th * s * (dr + dv), th * side_flops
-    if "read" in kernel:       # reads q, forms Gamma_Q, Gamma_Q [Vt, Z], writes out
-        return th * s * (dr + dv), th * side_flops
-    if "resp" in kernel:       # responsibilities of both sides
-        return th * s * 2 * dr, th * 4 * K * (2 * dr + 1)
-    # whole forward (a fused or scan kernel)
-    return th * s * (2 * dr + 2 * dv), th * 2 * side_flops
+    logits_side = 2 * K * (2 * dr + 1)   # one side's log-density contraction
+    memory_side = 2 * K * (dv + 1)       # Gamma^T [V | 1] or Gamma [Vt | Z]
+    if "prep" in kernel or "totals" in kernel or "carry" in kernel:
+        return None
+    if "bidir_write" in kernel:   # reads k and v, forms Gamma_K and Gamma_K^T [V, 1]
+        return th * s * (dr + dv), th * (logits_side + memory_side)
+    if "bidir_read" in kernel:    # reads q, forms Gamma_Q, Gamma_Q [Vt, Z], writes out
+        return th * s * (dr + dv), th * (logits_side + memory_side)
+    if "causal_resp" in kernel:   # reads q and k, forms both responsibility maps
+        return th * s * 2 * dr, th * 2 * logits_side
+    if "causal_scan" in kernel:   # reads v, writes out: the prefix [S | z] write and read
+        return th * s * 2 * dv, th * 2 * memory_side
+    # the whole forward
+    return th * s * (2 * dr + 2 * dv), th * 2 * (logits_side + memory_side)
 
 
 def hip_events(n):
@@ -166,7 +173,8 @@ def run_workload(w, steps, warmup):
 
 
 def roofline_for(w, per_kernel):
-    name = max(per_kernel, key=per_kernel.get)
+    """Roofline of the dominant kernel: the longest one that carries an algorithmic share."""
+    name = max((k for k in per_kernel if algorithmic(w, k) is not None), key=per_kernel.get)
     ms = per_kernel[name]
     nbytes, nflops = algorithmic(w, name)
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)

@@ -116,7 +116,8 @@ __global__ void __launch_bounds__(256) gma_prep(const float* __restrict__ mu, co
 }
 
 // ---------------------------------------------------------------------------------- write
-// Raw V values of one token row for this lane: dims 8 half + 16 j, j < NT * 2 (zero-padded).
+// Raw V values of one token row for this lane: dims 8 half + 16 j, j < NT * 2 (zero-padded;
+// d_v is a multiple of 8 on this path).
 template <int NT>
 __device__ __forceinline__ void load_vrow(bf16x8 (&vr)[2 * NT], const bf16_t* row, int dv) {
     const int half = lane_id() >> 5;
@@ -124,15 +125,7 @@ __device__ __forceinline__ void load_vrow(bf16x8 (&vr)[2 * NT], const bf16_t* ro
     for (int j = 0; j < 2 * NT; ++j) {
         const int d0 = 16 * j + 8 * half;
         bf16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (row) {
-            if ((dv & 7) == 0) {
-                if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(row + d0);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (d0 + e < dv) x[e] = (short)row[d0 + e];
-            }
-        }
+        if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(row + d0);
         vr[j] = x;
     }
 }
@@ -164,13 +157,14 @@ __global__ void __launch_bounds__(kThreads, 1)
     const int nit = n_end > n_begin ? (n_end - n_begin + kIterT - 1) / kIterT : 0;
     const bf16_t* kr_h = kr + (size_t)bh * N * dr;
     const bf16_t* v_h = v + (size_t)bh * N * dv;
+    // rows past the split read a valid row of the head (their responsibilities are zeroed)
     auto krow = [&](int it) -> const bf16_t* {
-        const int t = n_begin + it * kIterT + kTileT * w + col;
-        return (it < nit && t < n_end) ? kr_h + (size_t)t * dr : nullptr;
+        const int t = min(n_begin + it * kIterT + kTileT * w + col, N - 1);
+        return kr_h + (size_t)t * dr;
     };
     auto vrow = [&](int it) -> const bf16_t* {
-        const int t = n_begin + it * kIterT + kTileT * w + col;
-        return (it < nit && t < n_end) ? v_h + (size_t)t * dv : nullptr;
+        const int t = min(n_begin + it * kIterT + kTileT * w + col, N - 1);
+        return v_h + (size_t)t * dv;
     };
 
     f32x16 wacc[UT::MW][UT::NW];
@@ -282,7 +276,7 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
     bf16x8 xr[NC];
     {
         const int t = n_begin + kTileT * w + (l & 31);
-        load_xrow<NC>(xr, t < n_end ? q_h + (size_t)t * dr : nullptr, dr);
+        load_xrow<NC>(xr, q_h + (size_t)min(t, N - 1) * dr, dr);
     }
 
     // the head's memory [Vt | Z] = sum of the S split partials of the write kernel, added in
@@ -363,7 +357,7 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
         tile_logits<MT, NC>(acc, xr, sW, wstride, sC);
         // next tile's routing rows: in flight during the softmax and the read MFMAs
         const int tn = t + kStep;
-        load_xrow<NC>(xr, tn < n_end ? q_h + (size_t)tn * dr : nullptr, dr);
+        load_xrow<NC>(xr, q_h + (size_t)min(tn, N - 1) * dr, dr);
         (void)tile_exp<MT>(acc);  // unnormalised; the row sum comes out of the MFMAs below
         f32x16 o[NT + 1];
 #pragma unroll
@@ -396,17 +390,11 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int d0 = 32 * n + 8 * q + 4 * half;
-                    if ((dv & 3) == 0) {
-                        if (d0 < dv) {
-                            uint2 p;
-                            p.x = pack_bf16(o[n][4 * q] * inv, o[n][4 * q + 1] * inv);
-                            p.y = pack_bf16(o[n][4 * q + 2] * inv, o[n][4 * q + 3] * inv);
-                            *reinterpret_cast<uint2*>(orow + d0) = p;
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (d0 + r < dv) orow[d0 + r] = (bf16_t)bf16_bits_rne(o[n][4 * q + r] * inv);
+                    if (d0 < dv) {
+                        uint2 p;
+                        p.x = pack_bf16(o[n][4 * q] * inv, o[n][4 * q + 1] * inv);
+                        p.y = pack_bf16(o[n][4 * q + 2] * inv, o[n][4 * q + 3] * inv);
+                        *reinterpret_cast<uint2*>(orow + d0) = p;
                     }
                 }
         }
@@ -470,7 +458,8 @@ hipError_t mf::launch_prep(const Args& a, const Geo& g, bf16_t* W, float* cvec) 
 }
 
 bool mfma_supported(const gma_desc& d, int causal) {
-    if (d.dtype != GMA_BF16) return false;
+    // bf16 rows loaded as 16-byte vectors: d_r and d_v multiples of 8
+    if (d.dtype != GMA_BF16 || d.d_r % 8 != 0 || d.d_v % 8 != 0) return false;
     if (causal) return causal_supported(d);
     const Geo g = geometry(d);
     return write_lds_bytes(g) <= kLdsMax && read_lds_bytes(g) <= kLdsMax;

@@ -174,10 +174,8 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
 
     const int n_begin = part * part_len;
     const int n_end = min(Np, n_begin + part_len);
-    auto row = [&](int b0) -> const bf16_t* {
-        const int t = b0 + kTileT * w + col;
-        return (t < n_end && t < N) ? x + (size_t)t * dr : nullptr;
-    };
+    // positions past the sequence read its last row (their responsibilities are zeroed)
+    auto row = [&](int b0) -> const bf16_t* { return x + (size_t)min(b0 + kTileT * w + col, N - 1) * dr; };
     bf16x8 xr[NC];
     load_xrow<NC>(xr, row(n_begin), dr);
     if (NPH == 1) {
@@ -233,20 +231,13 @@ struct GroupRegs {
     __device__ __forceinline__ void load_g(int u, const bf16_t* gk_group) {
         g[u] = *reinterpret_cast<const bf16x8*>(gk_group + 8 * ((size_t)threadIdx.x + kThreads * u));
     }
+    // rows past n_end read a valid row: positions there have zero Gamma_K (past the sequence)
+    // or are masked out of every output that could see them
     __device__ __forceinline__ void load_v(int u, const bf16_t* v_h, int base, int n_end, int dv, int dv0) {
         const int c = threadIdx.x + kThreads * u;
-        const int t = base + c / PPR, d0 = dv0 + 8 * (c % PPR);
+        const int t = min(base + c / PPR, n_end - 1), d0 = dv0 + 8 * (c % PPR);
         bf16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (t < n_end) {
-            const bf16_t* src = v_h + (size_t)t * dv + d0;
-            if ((dv & 7) == 0) {
-                if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(src);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (d0 + e < dv) x[e] = (short)src[e];
-            }
-        }
+        if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(v_h + (size_t)t * dv + d0);
         v[u] = x;
     }
     __device__ __forceinline__ void load(const bf16_t* gk_group, const bf16_t* v_h, int base, int n_end, int dv,
@@ -540,17 +531,11 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int d0 = dv0 + 32 * n + 8 * q + 4 * half;
-                        if ((dv & 3) == 0) {
-                            if (d0 < dv) {
-                                uint2 p;
-                                p.x = pack_bf16(o[n][4 * q] * inv, o[n][4 * q + 1] * inv);
-                                p.y = pack_bf16(o[n][4 * q + 2] * inv, o[n][4 * q + 3] * inv);
-                                *reinterpret_cast<uint2*>(orow + d0) = p;
-                            }
-                        } else {
-#pragma unroll
-                            for (int rr = 0; rr < 4; ++rr)
-                                if (d0 + rr < dv) orow[d0 + rr] = (bf16_t)bf16_bits_rne(o[n][4 * q + rr] * inv);
+                        if (d0 < dv) {
+                            uint2 p;
+                            p.x = pack_bf16(o[n][4 * q] * inv, o[n][4 * q + 1] * inv);
+                            p.y = pack_bf16(o[n][4 * q + 2] * inv, o[n][4 * q + 3] * inv);
+                            *reinterpret_cast<uint2*>(orow + d0) = p;
                         }
                     }
             }

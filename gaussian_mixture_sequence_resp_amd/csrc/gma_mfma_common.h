@@ -102,19 +102,12 @@ __device__ __forceinline__ void split_square(XFrag& f) {
     f.x2l = __builtin_bit_cast(bf16x8, lp);
 }
 
-// Load this lane's 8 routing values of chunk `c` for token row `row` (nullptr = padding):
-// dims 16c + 8h .. 16c + 8h + 7, zero beyond d_r.
+// Load this lane's 8 routing values of chunk `c` of a token row: dims 16c + 8h .. 16c + 8h + 7,
+// zero beyond d_r (d_r is a multiple of 8 on this path, so a chunk half is all in or all out).
 __device__ __forceinline__ bf16x8 load_x8(const bf16_t* row, int c, int h, int dr) {
     bf16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (!row) return v;
     const int d0 = 16 * c + 8 * h;
-    if ((dr & 7) == 0) {
-        if (d0 < dr) v = *reinterpret_cast<const bf16x8*>(row + d0);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (d0 + j < dr) v[j] = static_cast<short>(row[d0 + j]);
-    }
+    if (d0 < dr) v = *reinterpret_cast<const bf16x8*>(row + d0);
     return v;
 }
 
@@ -212,10 +205,11 @@ __device__ __forceinline__ void load_wfrag(WFrag<MG>& f, const unsigned char* sW
     }
 }
 
-template <int MT, int NC, bool INIT = true, typename Work>
+template <int MT, int NC, bool INIT = true, int MGMAX = 2, typename Work>
 __device__ __forceinline__ void tile_logits_overlap(f32x16 (&acc)[MT], const bf16x8* xr, const unsigned char* sW,
                                                     int wstride, const float* sC, Work&& work) {
-    constexpr int MG = MT < 2 ? MT : 2;  // 2 accumulators alternate; 2 x 8 fragments in flight
+    // MG accumulators alternate (up to MGMAX); the fragments of two units are in flight
+    constexpr int MG = MT < MGMAX ? MT : MGMAX;
     constexpr int GPC = MT / MG;  // groups per chunk
     constexpr int U = NC * GPC;
     constexpr int Dp = 16 * NC;

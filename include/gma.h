@@ -78,9 +78,11 @@ typedef enum {
 
 typedef enum { GMA_F32 = 0, GMA_BF16 = 1 } gma_dtype;
 
-/* Kernel family.  AUTO picks MFMA for bf16 and SIMT for fp32.  SIMT is the plain
+/* Kernel family.  AUTO picks MFMA where it applies and SIMT otherwise.  SIMT is the plain
  * one-thread-per-element fp32 path (any supported shape, both dtypes); MFMA is the fused
- * matrix-core path (bf16 only). */
+ * matrix-core path: bf16 only, d_r and d_v multiples of 8 (rows are read as 16-byte
+ * vectors), and shapes whose staging fits in LDS.  An explicit GMA_ALGO_MFMA outside that
+ * range gives GMA_ERR_UNSUPPORTED (and gma_workspace_size returns 0). */
 typedef enum { GMA_ALGO_AUTO = 0, GMA_ALGO_SIMT = 1, GMA_ALGO_MFMA = 2 } gma_algo;
 
 typedef struct {

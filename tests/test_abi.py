@@ -124,3 +124,17 @@ def test_workspace_size(lib):
     assert binding.workspace_size(bad, False) == 0
     assert lib.gma_workspace_size(None, 0) == 0
     assert binding.workspace_size(binding.make_desc(2, 3, 0, 16, 8, 12, "f32", 1e-3), True) == 0
+
+
+def test_matrix_core_path_coverage(lib):
+    # the matrix-core path takes bf16 with d_r, d_v multiples of 8; an explicit request
+    # outside that range is unsupported (workspace 0), AUTO falls back to the SIMT path
+    ok = binding.make_desc(2, 3, 64, 64, 64, 128, "bf16", 1e-3, "mfma")
+    assert binding.workspace_size(ok, False) > 0 and binding.workspace_size(ok, True) > 0
+    for dr, dv in ((100, 64), (64, 100), (5, 7)):
+        bad = binding.make_desc(2, 3, 64, dr, dv, 128, "bf16", 1e-3, "mfma")
+        assert binding.workspace_size(bad, False) == 0 and binding.workspace_size(bad, True) == 0
+        auto = binding.make_desc(2, 3, 64, dr, dv, 128, "bf16", 1e-3, "auto")
+        simt = binding.make_desc(2, 3, 64, dr, dv, 128, "bf16", 1e-3, "simt")
+        assert binding.workspace_size(auto, False) == binding.workspace_size(simt, False) > 0
+    assert binding.workspace_size(binding.make_desc(2, 3, 64, 64, 64, 128, "f32", 1e-3, "mfma"), False) == 0

@@ -66,6 +66,8 @@ SMALL = [
     (100, 64, 64, 64, False), (100, 64, 64, 64, True), (257, 128, 64, 64, False),
     (257, 256, 64, 64, True), (300, 17, 40, 24, False), (129, 256, 128, 128, True),
     (512, 128, 64, 64, True), (1000, 33, 100, 128, False),
+    # ragged within the padded tiles on the matrix-core path (dims multiples of 8)
+    (1000, 33, 104, 72, False), (777, 200, 24, 40, True),
 ]
 
 
