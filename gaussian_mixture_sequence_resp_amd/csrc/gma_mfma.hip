@@ -74,8 +74,10 @@ MfmaLayout mfma_layout(const gma_desc& d) {
 }
 
 // ---------------------------------------------------------------------------------- prep
-// One wave per (h, k), lanes over the routing dims: the bf16 hi/lo coefficients and c_k,
-// computed in double.
+// One wave per (h, k), lanes over the routing dims: the bf16 hi/lo coefficients and c_k.
+// var = softplus(var_raw) + floor and log(var) in fp32 (relative error ~1e-7, far below the
+// ~2^-17 of the hi/lo coefficient pairs); 1/var, the coefficients and the sum over d for
+// c_k in double.
 __global__ void __launch_bounds__(256) gma_prep(const float* __restrict__ mu, const float* __restrict__ var_raw,
                                                 const float* __restrict__ prior, int H, int K, int dr, int Kp,
                                                 int Dp, float var_floor, bf16_t* __restrict__ W,
@@ -91,13 +93,13 @@ __global__ void __launch_bounds__(256) gma_prep(const float* __restrict__ mu, co
         double a = 0.0, b = 0.0;
         if (k < K && dd < dr) {
             const size_t i = ((size_t)h * K + k) * dr + dd;
-            const double r = var_raw[i];
-            const double var = fmax(r, 0.0) + log1p(exp(-fabs(r))) + (double)var_floor;
-            const double lam = 1.0 / var;
+            const float r = var_raw[i];
+            const float var = fmaxf(r, 0.0f) + log1pf(expf(-fabsf(r))) + var_floor;
+            const double lam = 1.0 / (double)var;
             const double m = mu[i];
             a = -0.5 * lam * L2E;
             b = lam * m * L2E;
-            acc += log(var) + m * m * lam;
+            acc += (double)logf(var) + m * m * lam;
         }
         const bf16_t ah = f32_to_bf16((float)a);
         const bf16_t al = f32_to_bf16((float)(a - (double)bf16_to_f32(ah)));

@@ -27,8 +27,9 @@
 //   gma_causal_resp     Gamma_Q and Gamma_K of every position (logit MFMAs + softmax)
 //   gma_causal_totals   Gamma_K^T [V | 1] of fixed-length sub-segments before the last
 //                       segment (only when S > 1)
-//   gma_causal_carry    state entering every segment: ordered sum of the sub-segment totals
-//   gma_causal_scan     one workgroup per (head, segment, value slice): sequential groups of
+//   gma_causal_scan     one workgroup per (head, segment, value slice); its prologue forms
+//                       the state entering the segment as the ordered sum of the sub-segment
+//                       totals before it; then sequential groups of
 //                       128 positions; fp32 state in MFMA accumulators split over the 4 waves
 //                       by output tile, bf16 shadow of the full state in LDS for
 //                       Gamma_Q [S | z]; Gamma_K rows of the group staged in LDS for the
@@ -52,7 +53,7 @@ constexpr int kSliceV = 64;     // value dims per scan workgroup
 constexpr int kFrag = 64 * 8;   // bf16 elements of one operand fragment block (64 lanes x 8)
 
 struct CausalLayout {
-    size_t W, C, gq, gk, tpart, carry, total;
+    size_t W, C, gq, gk, tpart, total;
     int S, seg_len, Np;     // segments, their length (multiple of kGroup), padded sequence
     int NS, Dvs;            // value slices and their width (padded)
     int TS, nsub, sub_len;  // totals: sub-segments per segment, their count and length
@@ -96,8 +97,6 @@ CausalLayout causal_layout(const gma_desc& d) {
     off += align_up((size_t)BH * L.Np * g.Kp * sizeof(bf16_t));
     L.tpart = off;
     off += align_up((size_t)BH * L.nsub * L.NS * per * sizeof(float));
-    L.carry = off;
-    off += align_up((size_t)BH * L.S * L.NS * per * sizeof(float));
     L.total = off;
     return L;
 }
@@ -340,26 +339,6 @@ __global__ void __launch_bounds__(kThreads, 1)
         }
 }
 
-// State entering segment s (s >= 1) of every head and slice: the totals of sub-segments
-// 0 .. s TS - 1 added in order.  Segment 0 starts from zero and is not stored.  Grid:
-// (per_h / 256 rounded up, min(BH, 65535)), heads strided by gridDim.y; per_h = NS Kp (Dvs + 1)
-// floats per head.
-__global__ void __launch_bounds__(256)
-    gma_causal_carry(const float* __restrict__ tpart, float* __restrict__ carry, int BH, int S, int TS, int per_h) {
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= per_h) return;
-    const int nsub = (S - 1) * TS;
-    for (size_t bh = blockIdx.y; bh < (size_t)BH; bh += gridDim.y) {
-        const float* src = tpart + bh * nsub * per_h + e;
-        float* dst = carry + bh * S * per_h + e;
-        float run = 0.0f;
-        for (int s = 1; s < S; ++s) {
-            for (int ts = 0; ts < TS; ++ts) run += src[(size_t)((s - 1) * TS + ts) * per_h];
-            dst[(size_t)s * per_h] = run;
-        }
-    }
-}
-
 // ----------------------------------------------------------------------------- scan
 // Shadow (bf16, LDS) of the state, rows: S^T (Dvs rows, value dims of the slice), then z hi
 // (8 rows), z lo (8 rows) and 16 rows of ones; columns = slots.  Written from this wave's
@@ -401,8 +380,8 @@ __device__ __forceinline__ void write_shadow(unsigned char* sS, int ss, const f3
 template <int MT, int NTS>
 __global__ void __launch_bounds__(kThreads, 1)
     gma_causal_scan(const bf16_t* __restrict__ GQ, const bf16_t* __restrict__ GK, const bf16_t* __restrict__ v,
-                    const float* __restrict__ carry, bf16_t* __restrict__ out, float eps, int BH, int N, int Np,
-                    int dv, int S, int NS, int seg_len) {
+                    const float* __restrict__ tpart, bf16_t* __restrict__ out, float eps, int BH, int N, int Np,
+                    int dv, int S, int NS, int seg_len, int TS) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int Kp = 32 * MT, Dvs = 32 * NTS;
     constexpr int gs = 2 * Kp + 32, vs = 2 * Dvs + 32, ss = 2 * Kp + 16;
@@ -419,24 +398,56 @@ __global__ void __launch_bounds__(kThreads, 1)
     const int l = lane_id(), w = wave_id(), half = l >> 5, col = l & 31;
     const int n_begin = seg * seg_len, n_end = min(N, n_begin + seg_len);
 
-    // state entering this segment (fp32, this wave's output tiles).  Segment 0 starts from
-    // zero: its carry slot is never written and is read only to keep the loads unconditional.
+    // state entering this segment (fp32, this wave's output tiles): the totals of the
+    // sub-segments before it, added in sub-segment order (a fixed order: every run gives the
+    // same bits); segment 0 starts from zero
     f32x16 st[UT::MW][UT::NW];
-    const float* cin = carry + ((size_t)(bh * S + seg) * NS + y) * Kp * (Dvs + 1);
 #pragma unroll
     for (int i = 0; i < UT::MW; ++i)
 #pragma unroll
-        for (int j = 0; j < UT::NW; ++j) {
-            const int m = UT::m_of(w, i), n = UT::n_of(w, j);
-            const int cc = n < NTS ? 32 * n + col : Dvs;
+        for (int j = 0; j < UT::NW; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int k = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
-                st[i][j][e] = cin[(size_t)k * (Dvs + 1) + cc];
-            }
+            for (int e = 0; e < 16; ++e) st[i][j][e] = 0.0f;
+    {
+        const int nsub = (S - 1) * TS, nprev = seg * TS;
+        const size_t per = (size_t)Kp * (Dvs + 1);
+        const float* src = tpart + ((size_t)bh * nsub * NS + y) * per;
+        for (int u0 = 0; u0 < nprev; u0 += 2) {
+            float x0[UT::MW][UT::NW][16], x1[UT::MW][UT::NW][16];
+            const bool ok1 = u0 + 1 < nprev;
+            const float* p0 = src + (size_t)u0 * NS * per;
+            const float* p1 = src + (size_t)(ok1 ? u0 + 1 : u0) * NS * per;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) st[i][j][e] = (seg > 0 && n <= NTS) ? st[i][j][e] : 0.0f;
+            for (int i = 0; i < UT::MW; ++i)
+#pragma unroll
+                for (int j = 0; j < UT::NW; ++j) {
+                    const int m = UT::m_of(w, i), n = UT::n_of(w, j);
+                    const int cc = n < NTS ? 32 * n + col : Dvs;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const size_t off = (size_t)(32 * m + 8 * (e >> 2) + 4 * half + (e & 3)) * (Dvs + 1) + cc;
+                        x0[i][j][e] = p0[off];
+                        x1[i][j][e] = p1[off];
+                    }
+                }
+#pragma unroll
+            for (int i = 0; i < UT::MW; ++i)
+#pragma unroll
+                for (int j = 0; j < UT::NW; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        st[i][j][e] += x0[i][j][e];
+                        if (ok1) st[i][j][e] += x1[i][j][e];
+                    }
         }
+#pragma unroll
+        for (int i = 0; i < UT::MW; ++i)
+#pragma unroll
+            for (int j = 0; j < UT::NW; ++j)
+                if (UT::n_of(w, j) > NTS)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) st[i][j][e] = 0.0f;
+    }
     // constant rows of the shadow: ones (den tile rows 16..31)
     for (int i = threadIdx.x; i < 2 * Kp; i += blockDim.x) {
         bf16x8 o8;
@@ -563,7 +574,7 @@ typedef void (*RespFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*
                        int, int, int, int);
 typedef void (*TotFn)(const bf16_t*, const bf16_t*, float*, int, int, int, int, int, int, int);
 typedef void (*ScanFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, float, int, int, int, int,
-                       int, int, int);
+                       int, int, int, int);
 
 template <int MT, int NC>
 RespFn resp_fn(int nph) {
@@ -641,7 +652,6 @@ hipError_t causal_forward(const Args& a) {
     bf16_t* GQ = reinterpret_cast<bf16_t*>(a.ws + L.gq);
     bf16_t* GK = reinterpret_cast<bf16_t*>(a.ws + L.gk);
     float* tpart = reinterpret_cast<float*>(a.ws + L.tpart);
-    float* carry = reinterpret_cast<float*>(a.ws + L.carry);
     const int BH = d.B * d.H;
     const int NTS = L.Dvs / 32;
     hipError_t e;
@@ -679,19 +689,13 @@ hipError_t causal_forward(const Args& a) {
                            static_cast<const bf16_t*>(a.v), tpart, BH, d.N, L.Np, d.d_v, L.NS, L.nsub, L.sub_len);
         rec_end(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int per_h = L.NS * g.Kp * (L.Dvs + 1);
-        rec_begin(a, "gma_causal_carry");
-        gma_causal_carry<<<dim3((unsigned)((per_h + 255) / 256), (unsigned)(BH < 65535 ? BH : 65535)), dim3(256), 0,
-                           a.stream>>>(tpart, carry, BH, L.S, L.TS, per_h);
-        rec_end(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 
     const size_t sl = scan_lds_bytes(g, L.Dvs);
     if ((e = set_lds(reinterpret_cast<const void*>(sf), sl)) != hipSuccess) return e;
     rec_begin(a, "gma_causal_scan");
     hipLaunchKernelGGL(sf, dim3(BH * L.S, L.NS), dim3(kThreads), sl, a.stream, GQ, GK, static_cast<const bf16_t*>(a.v),
-                       carry, static_cast<bf16_t*>(a.out), a.eps, BH, d.N, L.Np, d.d_v, L.S, L.NS, L.seg_len);
+                       tpart, static_cast<bf16_t*>(a.out), a.eps, BH, d.N, L.Np, d.d_v, L.S, L.NS, L.seg_len, L.TS);
     rec_end(a);
     return hipGetLastError();
 }
