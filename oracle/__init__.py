@@ -10,5 +10,6 @@ from .oracle import (  # noqa: F401
     log_joint,
     responsibilities,
     forward,
+    forward_cross,
     num_threads,
 )

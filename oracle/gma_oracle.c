@@ -20,6 +20,9 @@
  *     Vt = Gamma_K^T V,  Z = Gamma_K^T 1,  O = Gamma_Q Vt / (Gamma_Q Z + eps)
  *   Causal (Core mechanism 3): prefix sums of the memory and the normaliser, so that
  *     O_i uses only positions j <= i (inclusive of i).
+ *   Cross (the German page's closing paragraph names cross-attention as future work):
+ *     the bidirectional equations with Gamma_K, V over Nk key rows and Gamma_Q, O over
+ *     Nq query rows; Nk = Nq is self-mixing.
  *
  * Readings of points the pages leave open: the log-density keeps every constant
  * (log 2 pi and the prior's log-sum-exp); eps is added once per output row after
@@ -125,19 +128,21 @@ int gma_oracle_responsibilities(const double* x, int N, int d, const double* mu,
     return ORACLE_OK;
 }
 
-/* Bidirectional write then read for one head: gq, gk [N, K], v [N, dv] -> o [N, dv]. */
-static int mix_bidirectional(const double* gq, const double* gk, const double* v, int N, int K,
+/* Bidirectional write then read for one head: the memory Vt = Gamma_K^T V, Z = Gamma_K^T 1
+ * over the Nk key rows, read by the Nq query rows.  gq [Nq, K], gk [Nk, K], v [Nk, dv]
+ * -> o [Nq, dv].  Self-mixing is Nq = Nk with queries and keys of the same positions. */
+static int mix_bidirectional(const double* gq, int Nq, const double* gk, const double* v, int Nk, int K,
                              int dv, double eps, double* o) {
     double* vt = (double*)calloc((size_t)K * dv, sizeof(double)); /* Gamma_K^T V */
     double* z = (double*)calloc((size_t)K, sizeof(double));       /* Gamma_K^T 1 */
     if (!vt || !z) { free(vt); free(z); return ORACLE_NO_MEM; }
-    for (int j = 0; j < N; ++j)
+    for (int j = 0; j < Nk; ++j)
         for (int k = 0; k < K; ++k) {
             double g = gk[(size_t)j * K + k];
             z[k] += g;
             for (int c = 0; c < dv; ++c) vt[(size_t)k * dv + c] += g * v[(size_t)j * dv + c];
         }
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < Nq; ++i) {
         double den = 0.0;
         for (int k = 0; k < K; ++k) den += gq[(size_t)i * K + k] * z[k];
         for (int c = 0; c < dv; ++c) {
@@ -177,41 +182,36 @@ static int mix_causal(const double* gq, const double* gk, const double* v, int N
     return ORACLE_OK;
 }
 
-/*
- * Full forward.  All arrays are contiguous double:
- *   qr, kr [B,H,N,d_r]; v, out [B,H,N,d_v]; mu, var_raw [H,K,d_r]; prior_logits [H,K];
- *   gamma_q, gamma_k (each nullable) [B,H,N,K].
- * Slices (b, h) are independent and run in parallel; inside a slice everything is
- * sequential in index order.
- */
-int gma_oracle_forward(const double* qr, const double* kr, const double* v, const double* mu,
-                       const double* var_raw, const double* prior_logits, int B, int H, int N,
-                       int d_r, int d_v, int K, int causal, double eps, double var_floor,
-                       double* out, double* gamma_q, double* gamma_k) {
-    if (!qr || !kr || !v || !mu || !var_raw || !prior_logits || !out) return ORACLE_BAD_ARG;
-    if (B < 1 || H < 1 || N < 0 || d_r < 1 || d_v < 1 || K < 1) return ORACLE_BAD_ARG;
-    if (causal != 0 && causal != 1) return ORACLE_BAD_ARG;
-    const size_t nk = (size_t)N * K;
+/* One forward over all (b, h) slices with Nq query rows and Nk key rows (causal needs
+ * Nq == Nk).  Slices are independent and run in parallel; inside a slice everything is
+ * sequential in index order. */
+static int forward_slices(const double* qr, const double* kr, const double* v, const double* mu,
+                          const double* var_raw, const double* prior_logits, int B, int H, int Nq, int Nk,
+                          int d_r, int d_v, int K, int causal, double eps, double var_floor, double* out,
+                          double* gamma_q, double* gamma_k) {
+    const size_t nqk = (size_t)Nq * K, nkk = (size_t)Nk * K;
     int status = ORACLE_OK;
 
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < B * H; ++bh) {
         const int h = bh % H;
-        const size_t xoff = (size_t)bh * N * d_r;
-        const size_t voff = (size_t)bh * N * d_v;
-        double* gq = gamma_q ? gamma_q + (size_t)bh * nk : (double*)malloc(sizeof(double) * (nk ? nk : 1));
-        double* gk = gamma_k ? gamma_k + (size_t)bh * nk : (double*)malloc(sizeof(double) * (nk ? nk : 1));
+        double* gq = gamma_q ? gamma_q + (size_t)bh * nqk : (double*)malloc(sizeof(double) * (nqk ? nqk : 1));
+        double* gk = gamma_k ? gamma_k + (size_t)bh * nkk : (double*)malloc(sizeof(double) * (nkk ? nkk : 1));
         int st = (gq && gk) ? ORACLE_OK : ORACLE_NO_MEM;
         const double* mu_h = mu + (size_t)h * K * d_r;
         const double* vr_h = var_raw + (size_t)h * K * d_r;
         const double* p_h = prior_logits + (size_t)h * K;
+        const double* q_bh = qr + (size_t)bh * Nq * d_r;
+        const double* k_bh = kr + (size_t)bh * Nk * d_r;
+        const double* v_bh = v + (size_t)bh * Nk * d_v;
+        double* o_bh = out + (size_t)bh * Nq * d_v;
         if (st == ORACLE_OK)
-            st = gma_oracle_responsibilities(qr + xoff, N, d_r, mu_h, vr_h, p_h, K, var_floor, gq);
+            st = gma_oracle_responsibilities(q_bh, Nq, d_r, mu_h, vr_h, p_h, K, var_floor, gq);
         if (st == ORACLE_OK)
-            st = gma_oracle_responsibilities(kr + xoff, N, d_r, mu_h, vr_h, p_h, K, var_floor, gk);
+            st = gma_oracle_responsibilities(k_bh, Nk, d_r, mu_h, vr_h, p_h, K, var_floor, gk);
         if (st == ORACLE_OK)
-            st = causal ? mix_causal(gq, gk, v + voff, N, K, d_v, eps, out + voff)
-                        : mix_bidirectional(gq, gk, v + voff, N, K, d_v, eps, out + voff);
+            st = causal ? mix_causal(gq, gk, v_bh, Nq, K, d_v, eps, o_bh)
+                        : mix_bidirectional(gq, Nq, gk, v_bh, Nk, K, d_v, eps, o_bh);
         if (!gamma_q) free(gq);
         if (!gamma_k) free(gk);
         if (st != ORACLE_OK) {
@@ -220,4 +220,36 @@ int gma_oracle_forward(const double* qr, const double* kr, const double* v, cons
         }
     }
     return status;
+}
+
+/*
+ * Full forward.  All arrays are contiguous double:
+ *   qr, kr [B,H,N,d_r]; v, out [B,H,N,d_v]; mu, var_raw [H,K,d_r]; prior_logits [H,K];
+ *   gamma_q, gamma_k (each nullable) [B,H,N,K].
+ */
+int gma_oracle_forward(const double* qr, const double* kr, const double* v, const double* mu,
+                       const double* var_raw, const double* prior_logits, int B, int H, int N,
+                       int d_r, int d_v, int K, int causal, double eps, double var_floor,
+                       double* out, double* gamma_q, double* gamma_k) {
+    if (!qr || !kr || !v || !mu || !var_raw || !prior_logits || !out) return ORACLE_BAD_ARG;
+    if (B < 1 || H < 1 || N < 0 || d_r < 1 || d_v < 1 || K < 1) return ORACLE_BAD_ARG;
+    if (causal != 0 && causal != 1) return ORACLE_BAD_ARG;
+    return forward_slices(qr, kr, v, mu, var_raw, prior_logits, B, H, N, N, d_r, d_v, K, causal, eps,
+                          var_floor, out, gamma_q, gamma_k);
+}
+
+/*
+ * Cross variant (bidirectional): queries and keys of different lengths, the memory formed
+ * over the Nk key rows of each (b, h) and read by its Nq query rows.
+ *   qr [B,H,Nq,d_r]; kr [B,H,Nk,d_r]; v [B,H,Nk,d_v]; out [B,H,Nq,d_v];
+ *   gamma_q [B,H,Nq,K], gamma_k [B,H,Nk,K] (each nullable).
+ */
+int gma_oracle_forward_cross(const double* qr, const double* kr, const double* v, const double* mu,
+                             const double* var_raw, const double* prior_logits, int B, int H, int Nq, int Nk,
+                             int d_r, int d_v, int K, double eps, double var_floor, double* out,
+                             double* gamma_q, double* gamma_k) {
+    if (!qr || !kr || !v || !mu || !var_raw || !prior_logits || !out) return ORACLE_BAD_ARG;
+    if (B < 1 || H < 1 || Nq < 0 || Nk < 0 || d_r < 1 || d_v < 1 || K < 1) return ORACLE_BAD_ARG;
+    return forward_slices(qr, kr, v, mu, var_raw, prior_logits, B, H, Nq, Nk, d_r, d_v, K, 0, eps, var_floor,
+                          out, gamma_q, gamma_k);
 }

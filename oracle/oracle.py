@@ -53,6 +53,9 @@ def _load():
         lib.gma_oracle_forward.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, i, d, d,
                                            dp, dp, dp]
         lib.gma_oracle_forward.restype = i
+        lib.gma_oracle_forward_cross.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, i, d, d,
+                                                 dp, dp, dp]
+        lib.gma_oracle_forward_cross.restype = i
         lib.gma_oracle_num_threads.argtypes = []
         lib.gma_oracle_num_threads.restype = i
         _lib = lib
@@ -125,6 +128,34 @@ def forward(qr, kr, v, mu, var_raw, prior_logits, causal: bool, eps: float,
                                     float(var_floor), _ptr(out), _ptr(gq), _ptr(gk))
     if st != 0:
         raise RuntimeError(f"gma_oracle_forward failed: {st}")
+    if return_gamma:
+        return out, gq, gk
+    return out
+
+
+def forward_cross(qr, kr, v, mu, var_raw, prior_logits, eps: float, var_floor: float,
+                  return_gamma: bool = False):
+    """fp64 cross variant (bidirectional).  qr [B,H,Nq,d_r]; kr [B,H,Nk,d_r]; v [B,H,Nk,d_v];
+    mu, var_raw [H,K,d_r]; prior_logits [H,K].  Returns out [B,H,Nq,d_v] (and Gamma_Q
+    [B,H,Nq,K], Gamma_K [B,H,Nk,K])."""
+    qr, kr, v = _f64(qr), _f64(kr), _f64(v)
+    mu, vr, p = _f64(mu), _f64(var_raw), _f64(prior_logits)
+    B, H, Nq, d_r = qr.shape
+    Nk = kr.shape[2]
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    if kr.shape != (B, H, Nk, d_r) or v.shape[:3] != (B, H, Nk):
+        raise ValueError("shape mismatch")
+    if mu.shape != (H, K, d_r) or vr.shape != (H, K, d_r) or p.shape != (H, K):
+        raise ValueError("parameter shape mismatch")
+    out = np.empty((B, H, Nq, d_v), dtype=np.float64)
+    gq = np.empty((B, H, Nq, K), dtype=np.float64) if return_gamma else None
+    gk = np.empty((B, H, Nk, K), dtype=np.float64) if return_gamma else None
+    st = _load().gma_oracle_forward_cross(_ptr(qr), _ptr(kr), _ptr(v), _ptr(mu), _ptr(vr), _ptr(p),
+                                          B, H, Nq, Nk, d_r, d_v, K, float(eps), float(var_floor),
+                                          _ptr(out), _ptr(gq), _ptr(gk))
+    if st != 0:
+        raise RuntimeError(f"gma_oracle_forward_cross failed: {st}")
     if return_gamma:
         return out, gq, gk
     return out

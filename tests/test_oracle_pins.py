@@ -294,6 +294,83 @@ def test_empty_sequence():
         assert out.shape == (1, 1, 0, 3)
 
 
+# ---------------------------------------------------------------- cross variant
+# German page, closing paragraph: cross-attention named as future work.  Reading: the
+# bidirectional write/read with the memory over Nk key rows and the read over Nq query rows.
+
+def _cross_problem(rng, B, H, Nq, Nk, dr, dv, K):
+    qr = rng.normal(size=(B, H, Nq, dr))
+    kr = rng.normal(size=(B, H, Nk, dr))
+    v = rng.normal(size=(B, H, Nk, dv))
+    mu = rng.normal(size=(H, K, dr))
+    vr = rng.normal(0, 0.5, size=(H, K, dr))
+    p = rng.normal(size=(H, K))
+    return qr, kr, v, mu, vr, p
+
+
+@settings(max_examples=20, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(Nq=st.integers(1, 64), Nk=st.integers(1, 96), K=st.integers(1, 16), dr=st.integers(1, 8),
+       dv=st.integers(1, 8), seed=st.integers(0, 2 ** 31 - 1), eps=st.sampled_from([1e-6, 0.5]))
+def test_cross_matches_bruteforce(Nq, Nk, K, dr, dv, seed, eps):
+    # Nq x Nk affinity A = Gamma_Q Gamma_K^T, row-normalised A [V, 1]; Gamma from sklearn's
+    # posterior, not from the oracle
+    from sklearn.mixture import GaussianMixture
+
+    rng = np.random.default_rng(seed)
+    qr, kr, v, mu, vr, p = _cross_problem(rng, 1, 2, Nq, Nk, dr, dv, K)
+    out = oracle.forward_cross(qr, kr, v, mu, vr, p, eps, 1e-3)
+    assert out.shape == (1, 2, Nq, dv)
+    for h in range(2):
+        var = _var(vr[h], 1e-3)
+        gm = GaussianMixture(n_components=K, covariance_type="diag")
+        gm.weights_, gm.means_, gm.covariances_ = scipy.special.softmax(p[h]), mu[h], var
+        gm.precisions_cholesky_ = 1.0 / np.sqrt(var)
+        ref = _brute(gm.predict_proba(qr[0, h]), gm.predict_proba(kr[0, h]), v[0, h], eps, False)
+        assert metrics.rowrel(out[0, h][None, None], ref[None, None]) < 1e-10
+
+
+def test_cross_closed_forms():
+    rng = np.random.default_rng(21)
+    Nq, Nk, eps = 13, 41, 1e-3
+    # K = 1: every query reads the mean of the Nk values
+    qr, kr, v, mu, vr, p = _cross_problem(rng, 1, 1, Nq, Nk, 4, 5, 1)
+    out = oracle.forward_cross(qr, kr, v, mu, vr, p, eps, 1e-3)[0, 0]
+    np.testing.assert_allclose(out, np.tile(v[0, 0].sum(0) / (Nk + eps), (Nq, 1)), rtol=1e-13)
+    # identical components: gamma = pi, A_ij = |pi|^2
+    qr, kr, v, mu, vr, p = _cross_problem(rng, 1, 1, Nq, Nk, 3, 4, 6)
+    mu[0] = mu[0, :1]
+    vr[0] = vr[0, :1]
+    out = oracle.forward_cross(qr, kr, v, mu, vr, p, 0.01, 1e-3)[0, 0]
+    pi2 = float((scipy.special.softmax(p[0]) ** 2).sum())
+    np.testing.assert_allclose(out, np.tile(v[0, 0].sum(0) / (Nk + 0.01 / pi2), (Nq, 1)), rtol=1e-13)
+    # empty memory: 0 / (0 + eps); no queries: empty output
+    qr, kr, v, mu, vr, p = _cross_problem(rng, 1, 1, Nq, 0, 3, 4, 6)
+    assert np.array_equal(oracle.forward_cross(qr, kr, v, mu, vr, p, 0.5, 1e-3), np.zeros((1, 1, Nq, 4)))
+    qr, kr, v, mu, vr, p = _cross_problem(rng, 1, 1, 0, 9, 3, 4, 6)
+    assert oracle.forward_cross(qr, kr, v, mu, vr, p, 0.5, 1e-3).shape == (1, 1, 0, 4)
+
+
+def test_cross_invariants():
+    rng = np.random.default_rng(22)
+    Nq, Nk = 19, 57
+    qr, kr, v, mu, vr, p = _cross_problem(rng, 2, 2, Nq, Nk, 6, 5, 9)
+    o1 = oracle.forward_cross(qr, kr, v, mu, vr, p, 1e-6, 1e-3)
+    # permuting keys with their values changes nothing; permuting queries permutes rows
+    pk, pq = rng.permutation(Nk), rng.permutation(Nq)
+    o2 = oracle.forward_cross(qr[:, :, pq], kr[:, :, pk], v[:, :, pk], mu, vr, p, 1e-6, 1e-3)
+    np.testing.assert_allclose(o2, o1[:, :, pq], atol=1e-13)
+    # each query row depends on its own routing vector only: a query reads the same row
+    # whatever the other queries are
+    o3 = oracle.forward_cross(qr[:, :, :5], kr, v, mu, vr, p, 1e-6, 1e-3)
+    np.testing.assert_allclose(o3, o1[:, :, :5], atol=1e-15)
+    # convex combination of the values, scaled by A1/(A1+eps) < 1
+    assert np.all(np.abs(o1) <= np.abs(v).max(axis=2, keepdims=True) + 1e-12)
+    # with the same rows for queries and keys it is the bidirectional self-mixing
+    qr, kr, v, mu, vr, p = _cross_problem(rng, 1, 2, 30, 30, 4, 3, 5)
+    np.testing.assert_allclose(oracle.forward_cross(qr, kr, v, mu, vr, p, 1e-3, 1e-3),
+                               oracle.forward(qr, kr, v, mu, vr, p, False, 1e-3, 1e-3), rtol=0, atol=0)
+
+
 def test_golden_fixture_regression():
     import json
     import os
