@@ -7,9 +7,11 @@ The compute runs in ``libgma.so`` (hand-written HIP kernels behind the C ABI of
 from .binding import (  # noqa: F401
     GMAError,
     forward,
+    forward_cross,
     load_library,
     make_desc,
     strerror,
     version,
     workspace_size,
+    workspace_size_cross,
 )

@@ -57,6 +57,15 @@ def load_library(path: Optional[str] = None):
         ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
         ctypes.POINTER(ctypes.c_int)]
     lib.gma_forward_timed.restype = ctypes.c_int
+    lib.gma_workspace_size_cross.argtypes = [ctypes.POINTER(GmaDesc), ctypes.c_int32]
+    lib.gma_workspace_size_cross.restype = sz
+    lib.gma_forward_cross.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_float, vp, vp,
+                                      ctypes.POINTER(GmaDesc), vp, sz, vp]
+    lib.gma_forward_cross.restype = ctypes.c_int
+    lib.gma_forward_cross_timed.argtypes = lib.gma_forward_cross.argtypes + [
+        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+        ctypes.POINTER(ctypes.c_int)]
+    lib.gma_forward_cross_timed.restype = ctypes.c_int
     lib.gma_strerror.argtypes = [ctypes.c_int]
     lib.gma_strerror.restype = ctypes.c_char_p
     lib.gma_version.argtypes = []
@@ -82,6 +91,10 @@ def make_desc(B, H, N, d_r, d_v, K, dtype: str, var_floor: float, algo: str = "a
 
 def workspace_size(desc: GmaDesc, causal: bool) -> int:
     return int(load_library().gma_workspace_size(ctypes.byref(desc), 1 if causal else 0))
+
+
+def workspace_size_cross(desc: GmaDesc, n_k: int) -> int:
+    return int(load_library().gma_workspace_size_cross(ctypes.byref(desc), int(n_k)))
 
 
 def _dtype_name(t) -> str:
@@ -133,6 +146,45 @@ def forward(qr, kr, v, mu, var_raw, prior_logits, causal: bool = False, eps: flo
         nk = ctypes.c_int(0)
         st = lib.gma_forward_timed(*args, events, len(events), names, ctypes.byref(nk))
         forward.last_kernel_count = nk.value
+    if st != GMA_OK:
+        raise GMAError(st, strerror(st))
+    return out
+
+
+def forward_cross(qr, kr, v, mu, var_raw, prior_logits, eps: float = 1e-6, var_floor: float = 1e-3,
+                  out=None, gamma_out=None, workspace=None, algo: str = "auto", stream=None,
+                  events=None, names=None):
+    """Cross variant (bidirectional): qr [B,H,Nq,d_r]; kr [B,H,Nk,d_r]; v [B,H,Nk,d_v].
+    Returns ``out`` [B,H,Nq,d_v].  ``gamma_out`` (optional, float32, B*H*(Nq+Nk)*K
+    elements) receives Gamma_Q [B,H,Nq,K] followed by Gamma_K [B,H,Nk,K]."""
+    import torch
+    lib = load_library()
+    B, H, Nq, d_r = qr.shape
+    Nk = kr.shape[2]
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    desc = make_desc(B, H, Nq, d_r, d_v, K, _dtype_name(qr), var_floor, algo)
+    if out is None:
+        out = torch.empty((B, H, Nq, d_v), dtype=qr.dtype, device=qr.device)
+    need = int(lib.gma_workspace_size_cross(ctypes.byref(desc), Nk))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qr.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(qr.device).cuda_stream
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    args = (ptr(qr), ptr(kr), ptr(v), ptr(mu), ptr(var_raw), ptr(prior_logits), int(Nk), float(eps),
+            ptr(out), ptr(gamma_out), ctypes.byref(desc), ws_ptr, ws_bytes, stream)
+    if events is None:
+        st = lib.gma_forward_cross(*args)
+    else:
+        nk = ctypes.c_int(0)
+        st = lib.gma_forward_cross_timed(*args, events, len(events), names, ctypes.byref(nk))
+        forward_cross.last_kernel_count = nk.value
     if st != GMA_OK:
         raise GMAError(st, strerror(st))
     return out

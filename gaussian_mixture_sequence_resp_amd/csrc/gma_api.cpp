@@ -31,10 +31,10 @@ int resolve_algo(const gma_desc& d, int causal) {
     return (d.dtype == GMA_BF16 && gma::mfma_supported(d, causal)) ? GMA_ALGO_MFMA : GMA_ALGO_SIMT;
 }
 
-size_t workspace_for(const gma_desc& d, int causal) {
+size_t workspace_for(const gma_desc& d, int causal, int Nk) {
     const int algo = resolve_algo(d, causal);
-    if (algo == GMA_ALGO_MFMA) return gma::mfma_workspace(d, causal);
-    if (algo == GMA_ALGO_SIMT) return gma::simt_workspace(d, causal);
+    if (algo == GMA_ALGO_MFMA) return gma::mfma_workspace(d, causal, Nk);
+    if (algo == GMA_ALGO_SIMT) return gma::simt_workspace(d, causal, Nk);
     return 0;
 }
 
@@ -46,32 +46,51 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// The key length of a call: N for self-mixing, n_k for the cross variant (-1 = invalid).
+int key_rows(const gma_desc& d, int64_t n_k) {
+    if (n_k < 0 || (int64_t)d.B * d.H * n_k > INT32_MAX) return -1;
+    return (int)n_k;
+}
+
+size_t workspace_common(const gma_desc* desc, int causal, int64_t n_k) {
+    if (check_desc(desc) != GMA_OK || (causal != 0 && causal != 1)) return 0;
+    if ((int64_t)desc->B * desc->H * desc->N == 0) return 0;
+    const int Nk = key_rows(*desc, n_k);
+    if (Nk < 0) return 0;
+    return workspace_for(*desc, causal, Nk);
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t gma_workspace_size(const gma_desc* desc, int causal) {
-    if (check_desc(desc) != GMA_OK || (causal != 0 && causal != 1)) return 0;
-    if ((int64_t)desc->B * desc->H * desc->N == 0) return 0;
-    return workspace_for(*desc, causal);
+    return workspace_common(desc, causal, desc ? desc->N : 0);
 }
 
+size_t gma_workspace_size_cross(const gma_desc* desc, int32_t n_k) { return workspace_common(desc, 0, n_k); }
+
 static int forward_impl(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
-                        const float* prior_logits, int causal, float eps, void* out, float* gamma_out,
-                        const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream,
-                        gma::Recorder* rec) {
+                        const float* prior_logits, int causal, int64_t n_k, float eps, void* out,
+                        float* gamma_out, const gma_desc* desc, void* workspace, size_t workspace_bytes,
+                        void* stream, gma::Recorder* rec) {
     int st = check_desc(desc);
     if (st != GMA_OK) return st;
     const gma_desc d = *desc;
     if (causal != 0 && causal != 1) return GMA_ERR_BAD_SCALAR;
     if (!(eps >= 0.0f) || !isfinite(eps)) return GMA_ERR_BAD_SCALAR;
-    const size_t rows = (size_t)d.B * d.H * d.N;
+    const int Nk = key_rows(d, n_k);
+    if (Nk < 0) return GMA_ERR_BAD_SHAPE;
+    const size_t rows = (size_t)d.B * d.H * d.N;      // query and output rows
+    const size_t krows = (size_t)d.B * d.H * Nk;      // key and value rows
     if (rows == 0) return GMA_OK;  // empty sequence or batch: nothing to compute
-    if (!qr || !kr || !v || !mu || !var_raw || !prior_logits || !out) return GMA_ERR_NULL_ARG;
+    if (!qr || !mu || !var_raw || !prior_logits || !out) return GMA_ERR_NULL_ARG;
+    if (Nk > 0 && (!kr || !v)) return GMA_ERR_NULL_ARG;  // no key rows: kr and v are not read
     const size_t esz = d.dtype == GMA_F32 ? 4 : 2;
-    const size_t nx = rows * d.d_r * esz, nv = rows * d.d_v * esz;
+    const size_t nq = rows * d.d_r * esz, nk = krows * d.d_r * esz, nv = krows * d.d_v * esz;
+    const size_t no = rows * d.d_v * esz;
     const size_t np = (size_t)d.H * d.K * d.d_r * 4, npr = (size_t)d.H * d.K * 4;
-    const size_t ng = 2 * rows * d.K * 4;
+    const size_t ng = (rows + krows) * d.K * 4;
     if (misaligned(qr, 16) || misaligned(kr, 16) || misaligned(v, 16) || misaligned(out, 16))
         return GMA_ERR_ALIGN;
     if (misaligned(mu, 4) || misaligned(var_raw, 4) || misaligned(prior_logits, 4) ||
@@ -79,17 +98,17 @@ static int forward_impl(const void* qr, const void* kr, const void* v, const flo
         return GMA_ERR_ALIGN;
     if (workspace && misaligned(workspace, gma::kWsAlign)) return GMA_ERR_ALIGN;
     const void* ins[6] = {qr, kr, v, mu, var_raw, prior_logits};
-    const size_t ins_n[6] = {nx, nx, nv, np, np, npr};
+    const size_t ins_n[6] = {nq, nk, nv, np, np, npr};
     for (int i = 0; i < 6; ++i) {
-        if (overlaps(out, nv, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
+        if (overlaps(out, no, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
         if (gamma_out && overlaps(gamma_out, ng, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
     }
-    if (gamma_out && overlaps(out, nv, gamma_out, ng)) return GMA_ERR_ALIAS;
+    if (gamma_out && overlaps(out, no, gamma_out, ng)) return GMA_ERR_ALIAS;
     const int algo = resolve_algo(d, causal);
     if (algo < 0) return GMA_ERR_UNSUPPORTED;
-    const size_t need = workspace_for(d, causal);
+    const size_t need = workspace_for(d, causal, Nk);
     if (need > 0 && (!workspace || workspace_bytes < need)) return GMA_ERR_WORKSPACE;
-    if (workspace && (overlaps(workspace, need, out, nv) || (gamma_out && overlaps(workspace, need, gamma_out, ng))))
+    if (workspace && (overlaps(workspace, need, out, no) || (gamma_out && overlaps(workspace, need, gamma_out, ng))))
         return GMA_ERR_ALIAS;
     for (int i = 0; i < 6; ++i)
         if (workspace && overlaps(workspace, need, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
@@ -106,6 +125,7 @@ static int forward_impl(const void* qr, const void* kr, const void* v, const flo
     a.out = out;
     a.gamma_out = gamma_out;
     a.d = d;
+    a.Nk = Nk;
     a.ws = static_cast<unsigned char*>(workspace);
     a.ws_bytes = workspace_bytes;
     a.stream = static_cast<hipStream_t>(stream);
@@ -117,21 +137,44 @@ static int forward_impl(const void* qr, const void* kr, const void* v, const flo
 int gma_forward(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
                 const float* prior_logits, int causal, float eps, void* out, float* gamma_out,
                 const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
-    return forward_impl(qr, kr, v, mu, var_raw, prior_logits, causal, eps, out, gamma_out, desc, workspace,
+    return forward_impl(qr, kr, v, mu, var_raw, prior_logits, causal, desc ? desc->N : 0, eps, out, gamma_out,
+                        desc, workspace, workspace_bytes, stream, nullptr);
+}
+
+int gma_forward_cross(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                      const float* prior_logits, int32_t n_k, float eps, void* out, float* gamma_out,
+                      const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_impl(qr, kr, v, mu, var_raw, prior_logits, 0, n_k, eps, out, gamma_out, desc, workspace,
                         workspace_bytes, stream, nullptr);
+}
+
+static int timed(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                 const float* prior_logits, int causal, int64_t n_k, float eps, void* out, float* gamma_out,
+                 const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                 int n_events, const char** names, int* n_kernels) {
+    if (n_kernels) *n_kernels = 0;
+    if (n_events < 0 || (n_events > 0 && !events)) return GMA_ERR_NULL_ARG;
+    gma::Recorder rec{events, n_events, names, 0};
+    const int st = forward_impl(qr, kr, v, mu, var_raw, prior_logits, causal, n_k, eps, out, gamma_out, desc,
+                                workspace, workspace_bytes, stream, &rec);
+    if (n_kernels) *n_kernels = rec.count;
+    return st;
 }
 
 int gma_forward_timed(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
                       const float* prior_logits, int causal, float eps, void* out, float* gamma_out,
                       const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream,
                       void* const* events, int n_events, const char** names, int* n_kernels) {
-    if (n_kernels) *n_kernels = 0;
-    if (n_events < 0 || (n_events > 0 && !events)) return GMA_ERR_NULL_ARG;
-    gma::Recorder rec{events, n_events, names, 0};
-    const int st = forward_impl(qr, kr, v, mu, var_raw, prior_logits, causal, eps, out, gamma_out, desc,
-                                workspace, workspace_bytes, stream, &rec);
-    if (n_kernels) *n_kernels = rec.count;
-    return st;
+    return timed(qr, kr, v, mu, var_raw, prior_logits, causal, desc ? desc->N : 0, eps, out, gamma_out, desc,
+                 workspace, workspace_bytes, stream, events, n_events, names, n_kernels);
+}
+
+int gma_forward_cross_timed(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                            const float* prior_logits, int32_t n_k, float eps, void* out, float* gamma_out,
+                            const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events, int n_events, const char** names, int* n_kernels) {
+    return timed(qr, kr, v, mu, var_raw, prior_logits, 0, n_k, eps, out, gamma_out, desc, workspace,
+                 workspace_bytes, stream, events, n_events, names, n_kernels);
 }
 
 const char* gma_strerror(int status) {

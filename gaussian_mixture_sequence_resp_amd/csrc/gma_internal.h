@@ -28,7 +28,8 @@ struct Args {
     float eps;
     void* out;
     float* gamma_out;
-    gma_desc d;
+    gma_desc d;    // d.N is the query (and output) length
+    int Nk;        // key / value length (= d.N except in the cross variant)
     unsigned char* ws;
     size_t ws_bytes;
     hipStream_t stream;
@@ -56,9 +57,10 @@ constexpr size_t kWsAlign = 256;
 inline size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // SIMT family: plain fp32 arithmetic, one thread per output element.
-size_t simt_workspace(const gma_desc& d, int causal);
+size_t simt_workspace(const gma_desc& d, int causal, int Nk);
 hipError_t simt_forward(const Args& a);
-// Responsibilities only, written as float32 [2,B,H,N,K]; used for gamma_out by every family.
+// Responsibilities only, written as float32 Gamma_Q [B,H,N,K] then Gamma_K [B,H,Nk,K]; used for
+// gamma_out by every family.
 hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst);
 // Parameter prep of the SIMT family: lam = 1/var [H,K,d_r], cst [H,K] (log prior minus half
 // the log-determinant), both double.
@@ -66,7 +68,7 @@ hipError_t simt_params(const Args& a, double* lam, double* cst);
 size_t simt_param_bytes(const gma_desc& d);
 
 // MFMA family (bf16 inputs): fused matrix-core kernels.
-size_t mfma_workspace(const gma_desc& d, int causal);
+size_t mfma_workspace(const gma_desc& d, int causal, int Nk);
 bool mfma_supported(const gma_desc& d, int causal);
 hipError_t mfma_forward(const Args& a);
 

@@ -42,9 +42,10 @@ size_t read_lds_bytes(const Geo& g) {
     return (size_t)g.Kp * g.wstride + (size_t)g.Kp * 4 + (size_t)(g.Dvp + 32) * vtstride(g);
 }
 
-int num_splits(const gma_desc& d) {
+// Splits of the key sequence (length Nk) for the write kernel.
+int num_splits(const gma_desc& d, int Nk) {
     const int bh = d.B * d.H;
-    const int iters = (d.N + kIterT - 1) / kIterT;
+    const int iters = (Nk + kIterT - 1) / kIterT;
     int s = (256 + bh - 1) / bh;
     if (s > iters) s = iters;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -55,10 +56,10 @@ struct MfmaLayout {
     size_t W, C, part_v, part_z, total;
 };
 
-MfmaLayout mfma_layout(const gma_desc& d) {
+MfmaLayout mfma_layout(const gma_desc& d, int Nk) {
     const Geo g = geometry(d);
     const size_t BH = (size_t)d.B * d.H;
-    const int S = num_splits(d);
+    const int S = num_splits(d, Nk);
     MfmaLayout L;
     size_t off = 0;
     L.W = off;
@@ -157,6 +158,13 @@ __global__ void __launch_bounds__(kThreads, 1)
     const int n_begin = split * split_len;
     const int n_end = min(N, n_begin + split_len);
     const int nit = n_end > n_begin ? (n_end - n_begin + kIterT - 1) / kIterT : 0;
+    float* pv = part_v + ((size_t)bh * S + split) * Kp * Dvp;
+    float* pz = part_z + ((size_t)bh * S + split) * Kp;
+    if (N == 0) {  // empty key sequence (cross variant): a zero memory, no rows to read
+        for (int i = threadIdx.x; i < Kp * Dvp; i += kThreads) pv[i] = 0.0f;
+        for (int i = threadIdx.x; i < Kp; i += kThreads) pz[i] = 0.0f;
+        return;
+    }
     const bf16_t* kr_h = kr + (size_t)bh * N * dr;
     const bf16_t* v_h = v + (size_t)bh * N * dv;
     // rows past the split read a valid row of the head (their responsibilities are zeroed)
@@ -229,8 +237,6 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
 
     // ---- partial of this split -> workspace (fp32)
-    float* pv = part_v + ((size_t)bh * S + split) * Kp * Dvp;
-    float* pz = part_z + ((size_t)bh * S + split) * Kp;
 #pragma unroll
     for (int i = 0; i < UT::MW; ++i)
 #pragma unroll
@@ -467,16 +473,18 @@ bool mfma_supported(const gma_desc& d, int causal) {
     return write_lds_bytes(g) <= kLdsMax && read_lds_bytes(g) <= kLdsMax;
 }
 
-size_t mfma_workspace(const gma_desc& d, int causal) {
+size_t mfma_workspace(const gma_desc& d, int causal, int Nk) {
     // + room for the float64 parameters of the optional gamma_out diagnostic
     if (causal) return causal_workspace(d) + simt_param_bytes(d);
-    return mfma_layout(d).total + simt_param_bytes(d);
+    return mfma_layout(d, Nk).total + simt_param_bytes(d);
 }
 
+// Write over the Nk key rows (kr, v), read over the N query rows (qr, out).
 static hipError_t bidir_forward(const Args& a) {
     const gma_desc& d = a.d;
     const Geo g = geometry(d);
-    const MfmaLayout L = mfma_layout(d);
+    const int Nk = a.Nk;
+    const MfmaLayout L = mfma_layout(d, Nk);
     bf16_t* W = reinterpret_cast<bf16_t*>(a.ws + L.W);
     float* cvec = reinterpret_cast<float*>(a.ws + L.C);
     float* part_v = reinterpret_cast<float*>(a.ws + L.part_v);
@@ -490,15 +498,15 @@ static hipError_t bidir_forward(const Args& a) {
 
     if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
 
-    const int S = num_splits(d);
-    const int split_len = ((d.N + S - 1) / S + kIterT - 1) / kIterT * kIterT;
+    const int S = num_splits(d, Nk);
+    const int split_len = ((Nk + S - 1) / S + kIterT - 1) / kIterT * kIterT;
     const size_t wl = write_lds_bytes(g);
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(wf), hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)wl)) != hipSuccess)
         return e;
     rec_begin(a, "gma_bidir_write");
     hipLaunchKernelGGL(wf, dim3(BH * S), dim3(kThreads), wl, a.stream, static_cast<const bf16_t*>(a.kr),
-                       static_cast<const bf16_t*>(a.v), W, cvec, part_v, part_z, BH, d.H, d.N, d.d_r, d.d_v, S,
+                       static_cast<const bf16_t*>(a.v), W, cvec, part_v, part_z, BH, d.H, Nk, d.d_r, d.d_v, S,
                        split_len);
     rec_end(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -529,7 +537,7 @@ hipError_t mfma_forward(const Args& a) {
     if (e != hipSuccess) return e;
     if (a.gamma_out) {
         // diagnostic responsibilities (float32), outside the fused path
-        const size_t off = a.causal ? causal_workspace(d) : mfma_layout(d).total;
+        const size_t off = a.causal ? causal_workspace(d) : mfma_layout(d, a.Nk).total;
         double* lam = reinterpret_cast<double*>(a.ws + off);
         double* cst = reinterpret_cast<double*>(a.ws + off + align_up((size_t)d.H * d.K * d.d_r * sizeof(double)));
         if ((e = simt_params(a, lam, cst)) != hipSuccess) return e;

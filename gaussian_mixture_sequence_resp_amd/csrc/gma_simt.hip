@@ -12,7 +12,8 @@
 // magnitudes of hundreds while the softmax needs them to ~1e-6 absolute for fp32 parity, so
 // they are accumulated in double (parameters lam, c also kept in double); everything after
 // the max-shift (exp, sums, write, read, scan) is float32.  Responsibilities
-// are materialised in the workspace (float32 [2,B,H,N,K]), then the write and read phases
+// are materialised in the workspace (float32 Gamma_Q [B,H,N,K] then Gamma_K [B,H,Nk,K]; Nk = N
+// except in the cross variant), then the write and read phases
 // (or the causal scan) consume them.  Every sum runs in ascending index order, so results
 // are deterministic.
 #include <math.h>
@@ -69,7 +70,8 @@ __global__ void __launch_bounds__(kBlock) params_kernel(const float* __restrict_
     }
 }
 
-// One thread per routing row (side, b, h, n): gamma[side,b,h,n,:] = softmax_k l_k(x).
+// One thread per routing row (side, b, h, n) of either side: Gamma_Q rows [b,h,n] (Nq per head)
+// then Gamma_K rows (Nk per head), each = softmax_k l_k(x).
 template <typename T>
 __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
                                                       const T* __restrict__ kr,
@@ -77,14 +79,15 @@ __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
                                                       const double* __restrict__ lam,
                                                       const double* __restrict__ cst,
                                                       float* __restrict__ gamma, int BH, int H,
-                                                      int N, int dr, int K, int nblk) {
+                                                      int Nq, int Nk, int dr, int K, int nblk) {
     const int side = blockIdx.y;
+    const int N = side == 0 ? Nq : Nk;
     const int bh = blockIdx.x / nblk;
     const int n = (blockIdx.x % nblk) * kBlock + threadIdx.x;
     if (n >= N) return;
     const int h = bh % H;
     const T* x = (side == 0 ? qr : kr) + ((size_t)bh * N + n) * dr;
-    float* g = gamma + (((size_t)side * BH + bh) * N + n) * K;
+    float* g = gamma + ((size_t)side * BH * Nq + (size_t)bh * N + n) * K;
     const float* mu_h = mu + (size_t)h * K * dr;
     const double* lam_h = lam + (size_t)h * K * dr;
     // pass 1: row max of the logits (double), pass 2: shifted logits -> exp (float)
@@ -202,7 +205,7 @@ struct SimtLayout {
     size_t lam, cst, gamma, mem, total;
 };
 
-SimtLayout simt_layout(const gma_desc& d) {
+SimtLayout simt_layout(const gma_desc& d, int Nk) {
     SimtLayout L;
     const size_t BH = (size_t)d.B * d.H;
     size_t off = 0;
@@ -211,7 +214,7 @@ SimtLayout simt_layout(const gma_desc& d) {
     L.cst = off;
     off += align_up((size_t)d.H * d.K * sizeof(double));
     L.gamma = off;
-    off += align_up(2 * BH * d.N * d.K * sizeof(float));
+    off += align_up(BH * ((size_t)d.N + Nk) * d.K * sizeof(float));
     L.mem = off;
     off += align_up(BH * d.K * (d.d_v + 1) * sizeof(float));
     L.total = off;
@@ -221,7 +224,7 @@ SimtLayout simt_layout(const gma_desc& d) {
 template <typename T>
 hipError_t simt_forward_t(const Args& a) {
     const gma_desc& d = a.d;
-    const SimtLayout L = simt_layout(d);
+    const SimtLayout L = simt_layout(d, a.Nk);
     double* lam = reinterpret_cast<double*>(a.ws + L.lam);
     double* cst = reinterpret_cast<double*>(a.ws + L.cst);
     float* gamma = a.gamma_out ? a.gamma_out : reinterpret_cast<float*>(a.ws + L.gamma);
@@ -238,7 +241,7 @@ hipError_t simt_forward_t(const Args& a) {
     if (!a.causal) {
         const int wblk = (d.K * (d.d_v + 1) + kBlock - 1) / kBlock;
         rec_begin(a, "simt_write");
-        write_kernel<T><<<dim3(BH * wblk), dim3(kBlock), 0, a.stream>>>(gk, v, mem, d.N, d.K, d.d_v, wblk);
+        write_kernel<T><<<dim3(BH * wblk), dim3(kBlock), 0, a.stream>>>(gk, v, mem, a.Nk, d.K, d.d_v, wblk);
         rec_end(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int rblk = (int)(((size_t)d.N * d.d_v + kBlock - 1) / kBlock);
@@ -263,7 +266,7 @@ size_t simt_param_bytes(const gma_desc& d) {
     return align_up((size_t)d.H * d.K * d.d_r * sizeof(double)) + align_up((size_t)d.H * d.K * sizeof(double));
 }
 
-size_t simt_workspace(const gma_desc& d, int /*causal*/) { return simt_layout(d).total; }
+size_t simt_workspace(const gma_desc& d, int /*causal*/, int Nk) { return simt_layout(d, Nk).total; }
 
 hipError_t simt_params(const Args& a, double* lam, double* cst) {
     rec_begin(a, "simt_params");
@@ -276,17 +279,18 @@ hipError_t simt_params(const Args& a, double* lam, double* cst) {
 hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst) {
     const gma_desc& d = a.d;
     const int BH = d.B * d.H;
-    const int nblk = (d.N + kBlock - 1) / kBlock;
+    const int nmax = d.N > a.Nk ? d.N : a.Nk;
+    const int nblk = (nmax + kBlock - 1) / kBlock;
     dim3 grid(BH * nblk, 2);
     rec_begin(a, "simt_responsibilities");
     if (d.dtype == GMA_F32)
         resp_kernel<float><<<grid, dim3(kBlock), 0, a.stream>>>(
             static_cast<const float*>(a.qr), static_cast<const float*>(a.kr), a.mu, lam, cst, gamma, BH,
-            d.H, d.N, d.d_r, d.K, nblk);
+            d.H, d.N, a.Nk, d.d_r, d.K, nblk);
     else
         resp_kernel<bf16_t><<<grid, dim3(kBlock), 0, a.stream>>>(
             static_cast<const bf16_t*>(a.qr), static_cast<const bf16_t*>(a.kr), a.mu, lam, cst, gamma, BH,
-            d.H, d.N, d.d_r, d.K, nblk);
+            d.H, d.N, a.Nk, d.d_r, d.K, nblk);
     rec_end(a);
     return hipGetLastError();
 }

@@ -25,7 +25,7 @@ the Gaussian parameters stay float32.
 from __future__ import annotations
 
 from dataclasses import dataclass, field, replace
-from typing import Dict
+from typing import Dict, Optional
 
 import torch
 
@@ -51,6 +51,11 @@ class Workload:
     prior_std: float = 1.0
     sharp_frac: float = 0.0   # fraction of q/k rows drawn near a random mean
     sharp_noise: float = 0.1
+    N_k: Optional[int] = None  # key/value rows of the cross variant (None: N, self-mixing)
+
+    @property
+    def Nk(self) -> int:
+        return self.N if self.N_k is None else self.N_k
 
     @property
     def token_heads(self) -> int:
@@ -78,25 +83,28 @@ def torch_dtype(name: str) -> torch.dtype:
 def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
     """Draw the seeded CPU tensors of workload ``w``.
 
-    Returns a dict with ``qr, kr`` [B,H,N,d_r], ``v`` [B,H,N,d_v] in the workload
-    dtype and ``mu, var_raw`` [H,K,d_r], ``prior_logits`` [H,K] in float32.
+    Returns a dict with ``qr`` [B,H,N,d_r], ``kr`` [B,H,Nk,d_r], ``v`` [B,H,Nk,d_v] in the
+    workload dtype (Nk = N unless the workload sets N_k) and ``mu, var_raw`` [H,K,d_r],
+    ``prior_logits`` [H,K] in float32.
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(int(w.seed))
     B, H, N, dr, dv, K = w.B, w.H, w.N, w.d_r, w.d_v, w.K
+    Nk = w.Nk
     f32 = torch.float32
     q = torch.randn((B, H, N, dr), generator=g, dtype=f32) * w.x_std
-    k = torch.randn((B, H, N, dr), generator=g, dtype=f32) * w.x_std
-    v = torch.randn((B, H, N, dv), generator=g, dtype=f32) * w.v_std
+    k = torch.randn((B, H, Nk, dr), generator=g, dtype=f32) * w.x_std
+    v = torch.randn((B, H, Nk, dv), generator=g, dtype=f32) * w.v_std
     mu = torch.randn((H, K, dr), generator=g, dtype=f32) * w.mu_std
     var_raw = torch.randn((H, K, dr), generator=g, dtype=f32) * w.var_raw_std
     prior = torch.randn((H, K), generator=g, dtype=f32) * w.prior_std
     if w.sharp_frac > 0.0:
-        hidx = torch.arange(H).view(1, H, 1).expand(B, H, N)
         for x in (q, k):
-            mask = torch.rand((B, H, N), generator=g) < w.sharp_frac
-            comp = torch.randint(0, K, (B, H, N), generator=g)
-            noise = torch.randn((B, H, N, dr), generator=g, dtype=f32)
+            n = x.shape[2]
+            hidx = torch.arange(H).view(1, H, 1).expand(B, H, n)
+            mask = torch.rand((B, H, n), generator=g) < w.sharp_frac
+            comp = torch.randint(0, K, (B, H, n), generator=g)
+            noise = torch.randn((B, H, n, dr), generator=g, dtype=f32)
             near = mu[hidx, comp] + w.sharp_noise * noise
             x.copy_(torch.where(mask.unsqueeze(-1), near, x))
     dt = torch_dtype(w.dtype)

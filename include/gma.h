@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GMA_VERSION 10000 /* 1.0.0 */
+#define GMA_VERSION 10100 /* 1.1.0: cross variant */
 
 /* Limits of this build. */
 #define GMA_MAX_K 256
@@ -137,6 +137,36 @@ int gma_forward_timed(const void* qr, const void* kr, const void* v, const float
                       void* out, float* gamma_out, const gma_desc* desc, void* workspace,
                       size_t workspace_bytes, void* stream, void* const* events, int n_events,
                       const char** names, int* n_kernels);
+
+/*
+ * Cross variant (bidirectional only): queries and keys/values of different lengths.  The
+ * pages name cross-attention applications as future work (German page, closing paragraph
+ * on limitations and future work); this is the plainest reading of that: the write phase
+ * of "Core mechanism" item 2 over the N_k key rows, Vt = Gamma_K^T V and Z = Gamma_K^T 1,
+ * and its read phase O = Gamma_Q Vt / (Gamma_Q Z + eps) for the N_q query rows, with the
+ * same K Gaussians of the head for both sides.
+ *   desc->N        N_q: qr [B,H,N_q,d_r], out [B,H,N_q,d_v]
+ *   n_k            N_k >= 0: kr [B,H,N_k,d_r], v [B,H,N_k,d_v]
+ *   gamma_out      NULL, or float32 Gamma_Q [B,H,N_q,K] followed by Gamma_K [B,H,N_k,K]
+ * Every other argument, the alignment, aliasing and workspace rules and the status codes
+ * are those of gma_forward (causal = 0).  N_q = 0 (or B = 0, H = 0) is a no-op.  N_k = 0 is
+ * an empty memory: every output row is 0 / (0 + eps), i.e. 0 for eps > 0; kr and v are not
+ * read then and may be NULL.  With n_k = N and
+ * kr, v of the same positions as qr this is gma_forward(causal = 0).
+ */
+size_t gma_workspace_size_cross(const gma_desc* desc, int32_t n_k);
+
+int gma_forward_cross(const void* qr, const void* kr, const void* v, const float* mu,
+                      const float* var_raw, const float* prior_logits, int32_t n_k, float eps,
+                      void* out, float* gamma_out, const gma_desc* desc, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Profiling variant of gma_forward_cross, with the event arguments of gma_forward_timed. */
+int gma_forward_cross_timed(const void* qr, const void* kr, const void* v, const float* mu,
+                            const float* var_raw, const float* prior_logits, int32_t n_k, float eps,
+                            void* out, float* gamma_out, const gma_desc* desc, void* workspace,
+                            size_t workspace_bytes, void* stream, void* const* events, int n_events,
+                            const char** names, int* n_kernels);
 
 /* Static, NUL-terminated description of a status code. */
 const char* gma_strerror(int status);

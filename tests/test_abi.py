@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol(lib):
     txt = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
     names = set(re.findall(r"\b(gma_[a-z_]+)\s*\(", txt))
     assert names == {"gma_workspace_size", "gma_forward", "gma_forward_timed", "gma_strerror",
-                     "gma_version"}
+                     "gma_version", "gma_workspace_size_cross", "gma_forward_cross",
+                     "gma_forward_cross_timed"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -76,6 +77,12 @@ class Call:
         return lib.gma_forward(p["qr"], p["kr"], p["v"], p["mu"], p["var_raw"], p["prior"],
                                self.causal, self.eps, p["out"], p["gamma"], d, p["ws"],
                                self.ws_bytes, None)
+
+    def run_cross(self, lib, n_k):
+        p = self.ptr
+        return lib.gma_forward_cross(p["qr"], p["kr"], p["v"], p["mu"], p["var_raw"], p["prior"],
+                                     n_k, self.eps, p["out"], p["gamma"], ctypes.byref(self.desc),
+                                     p["ws"], self.ws_bytes, None)
 
 
 C = _codes()
@@ -138,3 +145,34 @@ def test_matrix_core_path_coverage(lib):
         simt = binding.make_desc(2, 3, 64, dr, dv, 128, "bf16", 1e-3, "simt")
         assert binding.workspace_size(auto, False) == binding.workspace_size(simt, False) > 0
     assert binding.workspace_size(binding.make_desc(2, 3, 64, 64, 64, 128, "f32", 1e-3, "mfma"), False) == 0
+
+
+def test_cross_validation_codes(lib):
+    # same checks as gma_forward, sized by N_q for qr/out and n_k for kr/v; no HIP call
+    step = 1 << 24
+    assert Call().run_cross(lib, -1) == C["GMA_ERR_BAD_SHAPE"]
+    assert Call(kr=None).run_cross(lib, 64) == C["GMA_ERR_NULL_ARG"]
+    assert Call(eps=-1.0).run_cross(lib, 64) == C["GMA_ERR_BAD_SCALAR"]
+    assert Call(v=Call.BASE + 2 * step + 8).run_cross(lib, 64) == C["GMA_ERR_ALIGN"]
+    assert Call(ws_bytes=16).run_cross(lib, 64) == C["GMA_ERR_WORKSPACE"]
+    # a long key sequence: kr (2*3*n_k*16 bf16 = 192 n_k bytes) and v (96 n_k bytes) grow
+    # into `out`, 5 and 4 slots later
+    assert Call().run_cross(lib, (4 * step) // 96 + 1) == C["GMA_ERR_ALIAS"]
+    # empty query side: a no-op that touches nothing
+    assert Call(N=0, qr=None, ws=None).run_cross(lib, 99) == C["GMA_OK"]
+    # empty key side: kr and v may be NULL (validation then fails later, on the workspace)
+    assert Call(kr=None, v=None, ws_bytes=16).run_cross(lib, 0) == C["GMA_ERR_WORKSPACE"]
+    assert Call(kr=None, v=None, ws_bytes=16).run_cross(lib, 1) == C["GMA_ERR_NULL_ARG"]
+
+
+def test_cross_workspace_size(lib):
+    d = binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "simt")
+    # SIMT materialises Gamma_Q (B*H*Nq*K) and Gamma_K (B*H*Nk*K) as float32
+    small, big = binding.workspace_size_cross(d, 10), binding.workspace_size_cross(d, 1000)
+    assert 0 < small < big and big >= 2 * 3 * (64 + 1000) * 12 * 4
+    assert binding.workspace_size_cross(d, 64) == binding.workspace_size(d, False)
+    assert binding.workspace_size_cross(d, -1) == 0
+    assert binding.workspace_size_cross(d, 0) > 0
+    dm = binding.make_desc(2, 3, 64, 64, 64, 128, "bf16", 1e-3, "mfma")
+    assert binding.workspace_size_cross(dm, 5000) > 0
+    assert binding.workspace_size_cross(dm, 64) == binding.workspace_size(dm, False)
