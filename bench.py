@@ -14,7 +14,8 @@ entering the headline time.  Prints one JSON line.
 value = whole-job throughput in token-heads/s (B*H*N / seconds per step).  The
 default workload is the bidirectional bf16 K=128 workload (B=8, H=8, N=4096,
 d_r=d_v=64); the causal LM-shaped workload (B=16, H=8, N=2048, K=256) is measured the
-same way and reported under "causal".
+same way and reported under "causal", and the cross variant (1024 queries reading a
+memory of 16384 keys per head, K=128) under "cross".
 """
 from __future__ import annotations
 
@@ -52,14 +53,15 @@ def algorithmic(w, kernel: str):
     part of that work is charged that part only.
     """
     s = 4 if w.dtype == "f32" else 2
-    th = w.B * w.H * w.N
+    th = w.B * w.H * w.N          # query (and output) rows
+    thk = w.B * w.H * w.Nk        # key (and value) rows; = th except in the cross variant
     K, dr, dv = w.K, w.d_r, w.d_v
     logits_side = 2 * K * (2 * dr + 1)   # one side's log-density contraction
     memory_side = 2 * K * (dv + 1)       # Gamma^T [V | 1] or Gamma [Vt | Z]
     if "prep" in kernel or "totals" in kernel or "carry" in kernel:
         return None
     if "bidir_write" in kernel:   # reads k and v, forms Gamma_K and Gamma_K^T [V, 1]
-        return th * s * (dr + dv), th * (logits_side + memory_side)
+        return thk * s * (dr + dv), thk * (logits_side + memory_side)
     if "bidir_read" in kernel:    # reads q, forms Gamma_Q, Gamma_Q [Vt, Z], writes out
         return th * s * (dr + dv), th * (logits_side + memory_side)
     if "causal_resp" in kernel:   # reads q and k, forms both responsibility maps
@@ -67,7 +69,7 @@ def algorithmic(w, kernel: str):
     if "causal_scan" in kernel:   # reads v, writes out: the prefix [S | z] write and read
         return th * s * 2 * dv, th * 2 * memory_side
     # the whole forward
-    return th * s * (2 * dr + 2 * dv), th * 2 * (logits_side + memory_side)
+    return (th + thk) * s * (dr + dv), (th + thk) * (logits_side + memory_side)
 
 
 def hip_events(n):
@@ -122,23 +124,25 @@ def run_workload(w, steps, warmup):
     d = {k: v.to(dev) for k, v in inp.items()}
     out = torch.empty((w.B, w.H, w.N, w.d_v), dtype=d["qr"].dtype, device=dev)
     desc = gma.make_desc(w.B, w.H, w.N, w.d_r, w.d_v, w.K, w.dtype, w.var_floor)
-    need = gma.workspace_size(desc, w.causal)
+    cross = w.N_k is not None
+    need = gma.workspace_size_cross(desc, w.Nk) if cross else gma.workspace_size(desc, w.causal)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     max_k = 8
     hip, evs = hip_events(2 * max_k * steps)
     names = (ctypes.c_char_p * max_k)()
 
+    fwd = gma.forward_cross if cross else gma.forward
+    kw = {} if cross else {"causal": w.causal}
+
     def step(i=None):
         if i is None:
-            gma.forward(d["qr"], d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"],
-                        causal=w.causal, eps=w.eps, var_floor=w.var_floor, out=out, workspace=ws,
-                        stream=stream)
+            fwd(d["qr"], d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"], eps=w.eps,
+                var_floor=w.var_floor, out=out, workspace=ws, stream=stream, **kw)
             return
         sub = (ctypes.c_void_p * (2 * max_k)).from_buffer(evs, ctypes.sizeof(ctypes.c_void_p) * 2 * max_k * i)
-        gma.forward(d["qr"], d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"],
-                    causal=w.causal, eps=w.eps, var_floor=w.var_floor, out=out, workspace=ws,
-                    stream=stream, events=sub, names=names)
+        fwd(d["qr"], d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"], eps=w.eps,
+            var_floor=w.var_floor, out=out, workspace=ws, stream=stream, events=sub, names=names, **kw)
 
     for _ in range(warmup):
         step()
@@ -157,7 +161,7 @@ def run_workload(w, steps, warmup):
         step(i)
     torch.cuda.synchronize()
     t3 = time.perf_counter()
-    nk = gma.forward.last_kernel_count
+    nk = fwd.last_kernel_count
     per_kernel = {}
     for j in range(min(nk, max_k)):
         name = names[j].decode()
@@ -229,6 +233,7 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-causal", action="store_true")
+    ap.add_argument("--no-cross", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy one 256 MiB device buffer, so that a profiler's "
                          "memory counters can be scaled by a copy of known size")
@@ -274,6 +279,15 @@ def main():
                           "value": round(wc.token_heads / (rc["ms_per_step"] * 1e-3), 1),
                           "per_kernel_ms": {k: round(v, 5) for k, v in rc["per_kernel_ms"].items()},
                           "roofline": roofline_for(wc, rc["per_kernel_ms"])}
+    if not args.no_cross and args.workload == 2:
+        wx = WORKLOADS[6]
+        rx = run_workload(wx, max(5, args.steps // 2), max(2, args.warmup // 2))
+        sec = rx["ms_per_step"] * 1e-3
+        line["cross"] = {"workload": wx.name, "N_q": wx.N, "N_k": wx.Nk, "ms_per_step": round(rx["ms_per_step"], 5),
+                         "value": round(wx.B * wx.H * wx.N / sec, 1), "unit": "query token-heads/s",
+                         "key_token_heads_per_s": round(wx.B * wx.H * wx.Nk / sec, 1),
+                         "per_kernel_ms": {k: round(v, 5) for k, v in rx["per_kernel_ms"].items()},
+                         "roofline": roofline_for(wx, rx["per_kernel_ms"])}
     if args.copy_calibration:
         import torch
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")

@@ -73,6 +73,9 @@ WORKLOADS: Dict[int, Workload] = {
                 seed=1004, var_floor=1e-2, sharp_frac=0.2),
     5: Workload("long-causal-bf16-K256-d128", "bf16", True, 1, 16, 32768, 128, 128, 256,
                 seed=1005, mu_std=2.0, var_raw_std=1.0, prior_std=2.0),
+    # cross variant: 1024 queries per head read a memory built from 16384 keys
+    6: Workload("cross-bf16-K128-q1024-k16384", "bf16", False, 8, 8, 1024, 64, 64, 128, seed=1006,
+                N_k=16384),
 }
 
 
