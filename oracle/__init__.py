@@ -11,5 +11,7 @@ from .oracle import (  # noqa: F401
     responsibilities,
     forward,
     forward_cross,
+    memory,
+    decode_step,
     num_threads,
 )

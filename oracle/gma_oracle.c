@@ -23,6 +23,10 @@
  *   Cross (the German page's closing paragraph names cross-attention as future work):
  *     the bidirectional equations with Gamma_K, V over Nk key rows and Gamma_Q, O over
  *     Nq query rows; Nk = Nq is self-mixing.
+ *   Decode (Core mechanism 3 read as a recurrence): the causal memory after positions
+ *     0..t-1 is the state [S | z] (K x (d_v+1)); one step adds gamma_K,t (x) [v_t | 1] and
+ *     reads O_t = gamma_Q,t S / (gamma_Q,t . z + eps), which is row t of the causal forward.
+ *     The memory of a prefix is the write phase over its positions.
  *
  * Readings of points the pages leave open: the log-density keeps every constant
  * (log 2 pi and the prior's log-sum-exp); eps is added once per output row after
@@ -252,4 +256,96 @@ int gma_oracle_forward_cross(const double* qr, const double* kr, const double* v
     if (B < 1 || H < 1 || Nq < 0 || Nk < 0 || d_r < 1 || d_v < 1 || K < 1) return ORACLE_BAD_ARG;
     return forward_slices(qr, kr, v, mu, var_raw, prior_logits, B, H, Nq, Nk, d_r, d_v, K, 0, eps, var_floor,
                           out, gamma_q, gamma_k);
+}
+
+/*
+ * Memory [S | z] of the first N positions of every (b, h): S[k][c] = sum_j gamma_K[j][k] v[j][c],
+ * z[k] = sum_j gamma_K[j][k], summed in position order.
+ *   kr [B,H,N,d_r]; v [B,H,N,d_v]; state [B,H,K,d_v+1] (row k: S[k][0..d_v-1], z[k]).
+ */
+int gma_oracle_memory(const double* kr, const double* v, const double* mu, const double* var_raw,
+                      const double* prior_logits, int B, int H, int N, int d_r, int d_v, int K,
+                      double var_floor, double* state) {
+    if (!kr || !v || !mu || !var_raw || !prior_logits || !state) return ORACLE_BAD_ARG;
+    if (B < 1 || H < 1 || N < 0 || d_r < 1 || d_v < 1 || K < 1) return ORACLE_BAD_ARG;
+    const int W = d_v + 1;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int h = bh % H;
+        double* gk = (double*)malloc(sizeof(double) * ((size_t)N * K + 1));
+        double* st_bh = state + (size_t)bh * K * W;
+        int st = gk ? ORACLE_OK : ORACLE_NO_MEM;
+        if (st == ORACLE_OK)
+            st = gma_oracle_responsibilities(kr + (size_t)bh * N * d_r, N, d_r, mu + (size_t)h * K * d_r,
+                                             var_raw + (size_t)h * K * d_r, prior_logits + (size_t)h * K, K,
+                                             var_floor, gk);
+        if (st == ORACLE_OK) {
+            for (size_t i = 0; i < (size_t)K * W; ++i) st_bh[i] = 0.0;
+            const double* v_bh = v + (size_t)bh * N * d_v;
+            for (int j = 0; j < N; ++j)
+                for (int k = 0; k < K; ++k) {
+                    const double g = gk[(size_t)j * K + k];
+                    st_bh[(size_t)k * W + d_v] += g;
+                    for (int c = 0; c < d_v; ++c) st_bh[(size_t)k * W + c] += g * v_bh[(size_t)j * d_v + c];
+                }
+        }
+        free(gk);
+        if (st != ORACLE_OK) {
+#pragma omp critical
+            status = st;
+        }
+    }
+    return status;
+}
+
+/*
+ * One causal decode step for every (b, h): with the state [S | z] of the positions before
+ * this one, add this position's gamma_K (x) [v | 1] (the sum is inclusive) and read
+ * out = gamma_Q S / (gamma_Q . z + eps).
+ *   qr, kr [B,H,d_r]; v, out [B,H,d_v]; state [B,H,K,d_v+1] (updated in place).
+ */
+int gma_oracle_decode_step(const double* qr, const double* kr, const double* v, const double* mu,
+                           const double* var_raw, const double* prior_logits, int B, int H, int d_r,
+                           int d_v, int K, double eps, double var_floor, double* state, double* out) {
+    if (!qr || !kr || !v || !mu || !var_raw || !prior_logits || !state || !out) return ORACLE_BAD_ARG;
+    if (B < 1 || H < 1 || d_r < 1 || d_v < 1 || K < 1) return ORACLE_BAD_ARG;
+    const int W = d_v + 1;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int h = bh % H;
+        double* gq = (double*)malloc(sizeof(double) * (size_t)K);
+        double* gk = (double*)malloc(sizeof(double) * (size_t)K);
+        int st = (gq && gk) ? ORACLE_OK : ORACLE_NO_MEM;
+        const double* mu_h = mu + (size_t)h * K * d_r;
+        const double* vr_h = var_raw + (size_t)h * K * d_r;
+        const double* p_h = prior_logits + (size_t)h * K;
+        if (st == ORACLE_OK)
+            st = gma_oracle_responsibilities(qr + (size_t)bh * d_r, 1, d_r, mu_h, vr_h, p_h, K, var_floor, gq);
+        if (st == ORACLE_OK)
+            st = gma_oracle_responsibilities(kr + (size_t)bh * d_r, 1, d_r, mu_h, vr_h, p_h, K, var_floor, gk);
+        if (st == ORACLE_OK) {
+            double* s = state + (size_t)bh * K * W;
+            const double* vt = v + (size_t)bh * d_v;
+            for (int k = 0; k < K; ++k) {
+                s[(size_t)k * W + d_v] += gk[k];
+                for (int c = 0; c < d_v; ++c) s[(size_t)k * W + c] += gk[k] * vt[c];
+            }
+            double den = 0.0;
+            for (int k = 0; k < K; ++k) den += gq[k] * s[(size_t)k * W + d_v];
+            for (int c = 0; c < d_v; ++c) {
+                double num = 0.0;
+                for (int k = 0; k < K; ++k) num += gq[k] * s[(size_t)k * W + c];
+                out[(size_t)bh * d_v + c] = num / (den + eps);
+            }
+        }
+        free(gq);
+        free(gk);
+        if (st != ORACLE_OK) {
+#pragma omp critical
+            status = st;
+        }
+    }
+    return status;
 }

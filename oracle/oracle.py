@@ -56,6 +56,10 @@ def _load():
         lib.gma_oracle_forward_cross.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, i, d, d,
                                                  dp, dp, dp]
         lib.gma_oracle_forward_cross.restype = i
+        lib.gma_oracle_memory.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, d, dp]
+        lib.gma_oracle_memory.restype = i
+        lib.gma_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i, i, d, d, dp, dp]
+        lib.gma_oracle_decode_step.restype = i
         lib.gma_oracle_num_threads.argtypes = []
         lib.gma_oracle_num_threads.restype = i
         _lib = lib
@@ -158,4 +162,39 @@ def forward_cross(qr, kr, v, mu, var_raw, prior_logits, eps: float, var_floor: f
         raise RuntimeError(f"gma_oracle_forward_cross failed: {st}")
     if return_gamma:
         return out, gq, gk
+    return out
+
+
+def memory(kr, v, mu, var_raw, prior_logits, var_floor: float) -> np.ndarray:
+    """Causal memory [S | z] of the N positions of every (b, h): kr [B,H,N,d_r], v [B,H,N,d_v]
+    -> state [B,H,K,d_v+1] (row k: S[k, :d_v], z[k])."""
+    kr, v = _f64(kr), _f64(v)
+    mu, vr, p = _f64(mu), _f64(var_raw), _f64(prior_logits)
+    B, H, N, d_r = kr.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    state = np.empty((B, H, K, d_v + 1), dtype=np.float64)
+    st = _load().gma_oracle_memory(_ptr(kr), _ptr(v), _ptr(mu), _ptr(vr), _ptr(p), B, H, N, d_r, d_v, K,
+                                   float(var_floor), _ptr(state))
+    if st != 0:
+        raise RuntimeError(f"gma_oracle_memory failed: {st}")
+    return state
+
+
+def decode_step(qr, kr, v, mu, var_raw, prior_logits, state: np.ndarray, eps: float,
+                var_floor: float) -> np.ndarray:
+    """One causal decode step: qr, kr [B,H,d_r], v [B,H,d_v]; ``state`` [B,H,K,d_v+1] float64
+    (C-contiguous) is updated in place; returns out [B,H,d_v]."""
+    qr, kr, v = _f64(qr), _f64(kr), _f64(v)
+    mu, vr, p = _f64(mu), _f64(var_raw), _f64(prior_logits)
+    B, H, d_r = qr.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    if state.dtype != np.float64 or not state.flags.c_contiguous or state.shape != (B, H, K, d_v + 1):
+        raise ValueError("state must be a C-contiguous float64 array [B,H,K,d_v+1]")
+    out = np.empty((B, H, d_v), dtype=np.float64)
+    st = _load().gma_oracle_decode_step(_ptr(qr), _ptr(kr), _ptr(v), _ptr(mu), _ptr(vr), _ptr(p), B, H, d_r,
+                                        d_v, K, float(eps), float(var_floor), _ptr(state), _ptr(out))
+    if st != 0:
+        raise RuntimeError(f"gma_oracle_decode_step failed: {st}")
     return out

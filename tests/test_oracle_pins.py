@@ -371,6 +371,63 @@ def test_cross_invariants():
                                oracle.forward(qr, kr, v, mu, vr, p, False, 1e-3, 1e-3), rtol=0, atol=0)
 
 
+# ---------------------------------------------------------------- decode step
+# Core mechanism item 3 read as a recurrence: the causal memory after positions 0..t-1 is
+# [S | z]; a step adds gamma_K,t (x) [v_t | 1] and reads row t.
+
+def _sk_gamma(x, mu, vr, p, floor=1e-3):
+    from sklearn.mixture import GaussianMixture
+    var = _var(vr, floor)
+    gm = GaussianMixture(n_components=mu.shape[0], covariance_type="diag")
+    gm.weights_, gm.means_, gm.covariances_ = scipy.special.softmax(p), mu, var
+    gm.precisions_cholesky_ = 1.0 / np.sqrt(var)
+    return gm.predict_proba(x)
+
+
+@pytest.mark.parametrize("N,K,dr,dv,split", [(1, 1, 3, 2, 0), (25, 7, 5, 4, 0), (40, 16, 8, 6, 17),
+                                             (64, 33, 4, 9, 63)])
+def test_memory_then_decode_matches_causal_bruteforce(N, K, dr, dv, split):
+    rng = np.random.default_rng(31 + N + K)
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 2, N, dr, dv, K)
+    eps = 1e-3
+    # prefill: the memory of positions 0..split-1, against an sklearn-posterior reference
+    state = oracle.memory(kr[:, :, :split], v[:, :, :split], mu, vr, p, 1e-3)
+    for h in range(2):
+        gk = _sk_gamma(kr[0, h, :split], mu[h], vr[h], p[h]) if split else np.zeros((0, K))
+        ref = np.concatenate([gk.T @ v[0, h, :split], gk.sum(0)[:, None]], axis=1)
+        np.testing.assert_allclose(state[0, h], ref, rtol=1e-12, atol=1e-13)
+    # decode the remaining positions one at a time: row t of the causal brute force
+    outs = []
+    for t in range(split, N):
+        outs.append(oracle.decode_step(qr[:, :, t], kr[:, :, t], v[:, :, t], mu, vr, p, state, eps, 1e-3))
+    got = np.stack(outs, axis=2) if outs else np.zeros((1, 2, 0, dv))
+    for h in range(2):
+        gq = _sk_gamma(qr[0, h], mu[h], vr[h], p[h])
+        gk = _sk_gamma(kr[0, h], mu[h], vr[h], p[h])
+        ref = _brute(gq, gk, v[0, h], eps, True)[split:]
+        assert metrics.rowrel(got[0, h][None, None], ref[None, None]) < 1e-10
+    # the state after the last step is the memory of the whole sequence
+    np.testing.assert_allclose(state, oracle.memory(kr, v, mu, vr, p, 1e-3), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_closed_forms():
+    rng = np.random.default_rng(41)
+    # K = 1: gamma = 1, the step returns the running mean of v (prefix mean)
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 1, 12, 3, 4, 1)
+    state = np.zeros((1, 1, 1, 5))
+    for t in range(12):
+        o = oracle.decode_step(qr[:, :, t], kr[:, :, t], v[:, :, t], mu, vr, p, state, 1e-6, 1e-3)
+        np.testing.assert_allclose(o[0, 0], v[0, 0, :t + 1].sum(0) / (t + 1 + 1e-6), rtol=1e-13)
+    # a single token into an empty memory: O = (gq.gk) v / (gq.gk + eps)
+    qr, kr, v, mu, vr, p = _random_problem(rng, 1, 1, 1, 5, 3, 6)
+    state = np.zeros((1, 1, 6, 4))
+    o = oracle.decode_step(qr[:, :, 0], kr[:, :, 0], v[:, :, 0], mu, vr, p, state, 0.25, 1e-3)
+    a = float(_sk_gamma(qr[0, 0, :1], mu[0], vr[0], p[0])[0] @ _sk_gamma(kr[0, 0, :1], mu[0], vr[0], p[0])[0])
+    np.testing.assert_allclose(o[0, 0], a * v[0, 0, 0] / (a + 0.25), rtol=1e-12)
+    # the memory of an empty prefix is zero
+    assert not oracle.memory(kr[:, :, :0], v[:, :, :0], mu, vr, p, 1e-3).any()
+
+
 def test_golden_fixture_regression():
     import json
     import os
