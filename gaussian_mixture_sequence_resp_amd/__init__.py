@@ -6,10 +6,12 @@ The compute runs in ``libgma.so`` (hand-written HIP kernels behind the C ABI of
 """
 from .binding import (  # noqa: F401
     GMAError,
+    decode_step,
     forward,
     forward_cross,
     load_library,
     make_desc,
+    memory,
     strerror,
     version,
     workspace_size,

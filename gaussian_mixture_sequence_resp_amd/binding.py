@@ -66,6 +66,15 @@ def load_library(path: Optional[str] = None):
         ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
         ctypes.POINTER(ctypes.c_int)]
     lib.gma_forward_cross_timed.restype = ctypes.c_int
+    lib.gma_memory_workspace_size.argtypes = [ctypes.POINTER(GmaDesc)]
+    lib.gma_memory_workspace_size.restype = sz
+    lib.gma_memory.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(GmaDesc), vp, sz, vp]
+    lib.gma_memory.restype = ctypes.c_int
+    lib.gma_decode_workspace_size.argtypes = [ctypes.POINTER(GmaDesc)]
+    lib.gma_decode_workspace_size.restype = sz
+    lib.gma_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.POINTER(GmaDesc), vp,
+                                    sz, vp]
+    lib.gma_decode_step.restype = ctypes.c_int
     lib.gma_strerror.argtypes = [ctypes.c_int]
     lib.gma_strerror.restype = ctypes.c_char_p
     lib.gma_version.argtypes = []
@@ -97,6 +106,14 @@ def workspace_size_cross(desc: GmaDesc, n_k: int) -> int:
     return int(load_library().gma_workspace_size_cross(ctypes.byref(desc), int(n_k)))
 
 
+def _dense(*ts):
+    """The C ABI takes dense row-major tensors: refuse strided views (a silent misread
+    otherwise)."""
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise GMAError(-2, f"tensor of shape {tuple(t.shape)} is not contiguous (call .contiguous())")
+
+
 def _dtype_name(t) -> str:
     import torch
     if t.dtype == torch.float32:
@@ -118,6 +135,7 @@ def forward(qr, kr, v, mu, var_raw, prior_logits, causal: bool = False, eps: flo
     """
     import torch
     lib = load_library()
+    _dense(qr, kr, v, mu, var_raw, prior_logits, out, gamma_out)
     B, H, N, d_r = qr.shape
     d_v = v.shape[-1]
     K = mu.shape[1]
@@ -159,6 +177,7 @@ def forward_cross(qr, kr, v, mu, var_raw, prior_logits, eps: float = 1e-6, var_f
     elements) receives Gamma_Q [B,H,Nq,K] followed by Gamma_K [B,H,Nk,K]."""
     import torch
     lib = load_library()
+    _dense(qr, kr, v, mu, var_raw, prior_logits, out, gamma_out)
     B, H, Nq, d_r = qr.shape
     Nk = kr.shape[2]
     d_v = v.shape[-1]
@@ -185,6 +204,65 @@ def forward_cross(qr, kr, v, mu, var_raw, prior_logits, eps: float = 1e-6, var_f
         nk = ctypes.c_int(0)
         st = lib.gma_forward_cross_timed(*args, events, len(events), names, ctypes.byref(nk))
         forward_cross.last_kernel_count = nk.value
+    if st != GMA_OK:
+        raise GMAError(st, strerror(st))
+    return out
+
+
+def _ws(need, like):
+    import torch
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=like.device)
+
+
+def memory(kr, v, mu, var_raw, prior_logits, var_floor: float = 1e-3, state=None, workspace=None,
+           algo: str = "auto", stream=None):
+    """Causal memory [S | z] of the N positions of kr [B,H,N,d_r], v [B,H,N,d_v]:
+    returns ``state`` float32 [B,H,K,d_v+1] (row k: S[k, :d_v], z[k])."""
+    import torch
+    lib = load_library()
+    _dense(kr, v, mu, var_raw, prior_logits, state)
+    B, H, N, d_r = kr.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    desc = make_desc(B, H, N, d_r, d_v, K, _dtype_name(kr), var_floor, algo)
+    if state is None:
+        state = torch.empty((B, H, K, d_v + 1), dtype=torch.float32, device=kr.device)
+    need = int(lib.gma_memory_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = _ws(need, kr)
+    if stream is None:
+        stream = torch.cuda.current_stream(kr.device).cuda_stream
+    nz = N > 0
+    st = lib.gma_memory(kr.data_ptr() if nz else None, v.data_ptr() if nz else None, mu.data_ptr(),
+                        var_raw.data_ptr(), prior_logits.data_ptr(), state.data_ptr(), ctypes.byref(desc),
+                        workspace.data_ptr(), workspace.numel(), stream)
+    if st != GMA_OK:
+        raise GMAError(st, strerror(st))
+    return state
+
+
+def decode_step(qr, kr, v, mu, var_raw, prior_logits, state, eps: float = 1e-6, var_floor: float = 1e-3,
+                out=None, workspace=None, algo: str = "auto", stream=None):
+    """One causal decode step: qr, kr [B,H,1,d_r] (or [B,H,d_r]), v [B,H,1,d_v] (or [B,H,d_v]);
+    ``state`` float32 [B,H,K,d_v+1] is updated in place; returns out [B,H,1,d_v]."""
+    import torch
+    lib = load_library()
+    qr, kr, v = qr.contiguous(), kr.contiguous(), v.contiguous()  # one row per (b, h): cheap
+    _dense(mu, var_raw, prior_logits, state, out)
+    B, H = qr.shape[0], qr.shape[1]
+    d_r, d_v = qr.shape[-1], v.shape[-1]
+    K = mu.shape[1]
+    desc = make_desc(B, H, 1, d_r, d_v, K, _dtype_name(qr), var_floor, algo)
+    if out is None:
+        out = torch.empty((B, H, 1, d_v), dtype=qr.dtype, device=qr.device)
+    need = int(lib.gma_decode_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = _ws(need, qr)
+    if stream is None:
+        stream = torch.cuda.current_stream(qr.device).cuda_stream
+    st = lib.gma_decode_step(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), mu.data_ptr(), var_raw.data_ptr(),
+                             prior_logits.data_ptr(), state.data_ptr(), float(eps), out.data_ptr(),
+                             ctypes.byref(desc), workspace.data_ptr(), workspace.numel(), stream)
     if st != GMA_OK:
         raise GMAError(st, strerror(st))
     return out

@@ -124,6 +124,7 @@ static int forward_impl(const void* qr, const void* kr, const void* v, const flo
     a.eps = eps;
     a.out = out;
     a.gamma_out = gamma_out;
+    a.state = nullptr;
     a.d = d;
     a.Nk = Nk;
     a.ws = static_cast<unsigned char*>(workspace);
@@ -175,6 +176,116 @@ int gma_forward_cross_timed(const void* qr, const void* kr, const void* v, const
                             void* const* events, int n_events, const char** names, int* n_kernels) {
     return timed(qr, kr, v, mu, var_raw, prior_logits, 0, n_k, eps, out, gamma_out, desc, workspace,
                  workspace_bytes, stream, events, n_events, names, n_kernels);
+}
+
+// ---- causal memory (prefill) and single-token decode step
+
+static bool memory_algo_ok(const gma_desc& d) {
+    return d.algo != GMA_ALGO_MFMA || (d.dtype == GMA_BF16 && gma::mfma_supported(d, 0));
+}
+
+size_t gma_memory_workspace_size(const gma_desc* desc) {
+    if (check_desc(desc) != GMA_OK || (int64_t)desc->B * desc->H == 0 || !memory_algo_ok(*desc)) return 0;
+    return gma::memory_workspace(*desc);
+}
+
+int gma_memory(const void* kr, const void* v, const float* mu, const float* var_raw, const float* prior_logits,
+               float* state, const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_desc(desc);
+    if (st != GMA_OK) return st;
+    const gma_desc d = *desc;
+    const size_t bh = (size_t)d.B * d.H;
+    if (bh == 0) return GMA_OK;
+    if (!mu || !var_raw || !prior_logits || !state) return GMA_ERR_NULL_ARG;
+    if (d.N > 0 && (!kr || !v)) return GMA_ERR_NULL_ARG;  // no positions: kr and v are not read
+    const size_t esz = d.dtype == GMA_F32 ? 4 : 2;
+    const size_t nk = bh * d.N * d.d_r * esz, nv = bh * d.N * d.d_v * esz;
+    const size_t np = (size_t)d.H * d.K * d.d_r * 4, npr = (size_t)d.H * d.K * 4;
+    const size_t ns = bh * d.K * (d.d_v + 1) * 4;
+    if (misaligned(kr, 16) || misaligned(v, 16)) return GMA_ERR_ALIGN;
+    if (misaligned(mu, 4) || misaligned(var_raw, 4) || misaligned(prior_logits, 4) || misaligned(state, 4))
+        return GMA_ERR_ALIGN;
+    if (workspace && misaligned(workspace, gma::kWsAlign)) return GMA_ERR_ALIGN;
+    if (!memory_algo_ok(d)) return GMA_ERR_UNSUPPORTED;
+    const void* ins[5] = {kr, v, mu, var_raw, prior_logits};
+    const size_t ins_n[5] = {nk, nv, np, np, npr};
+    const size_t need = gma::memory_workspace(d);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GMA_ERR_WORKSPACE;
+    if (workspace && overlaps(workspace, need, state, ns)) return GMA_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(state, ns, ins[i], ins_n[i]) || (workspace && overlaps(workspace, need, ins[i], ins_n[i])))
+            return GMA_ERR_ALIAS;
+    Args a;
+    memset(&a, 0, sizeof(a));
+    a.kr = kr;
+    a.v = v;
+    a.mu = mu;
+    a.var_raw = var_raw;
+    a.prior = prior_logits;
+    a.state = state;
+    a.d = d;
+    a.Nk = d.N;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.ws_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gma::memory_forward(a) == hipSuccess ? GMA_OK : GMA_ERR_HIP;
+}
+
+size_t gma_decode_workspace_size(const gma_desc* desc) {
+    if (check_desc(desc) != GMA_OK || desc->N != 1 || desc->algo == GMA_ALGO_MFMA) return 0;
+    if ((int64_t)desc->B * desc->H == 0) return 0;
+    return gma::decode_workspace(*desc);
+}
+
+int gma_decode_step(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                    const float* prior_logits, float* state, float eps, void* out, const gma_desc* desc,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_desc(desc);
+    if (st != GMA_OK) return st;
+    const gma_desc d = *desc;
+    if (d.N != 1) return GMA_ERR_BAD_SHAPE;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return GMA_ERR_BAD_SCALAR;
+    const size_t bh = (size_t)d.B * d.H;
+    if (bh == 0) return GMA_OK;
+    if (!qr || !kr || !v || !mu || !var_raw || !prior_logits || !state || !out) return GMA_ERR_NULL_ARG;
+    // one kernel family (a small latency-bound kernel): an explicit matrix-core request is
+    // not honoured
+    if (d.algo == GMA_ALGO_MFMA) return GMA_ERR_UNSUPPORTED;
+    const size_t esz = d.dtype == GMA_F32 ? 4 : 2;
+    const size_t nx = bh * d.d_r * esz, nv = bh * d.d_v * esz;
+    const size_t np = (size_t)d.H * d.K * d.d_r * 4, npr = (size_t)d.H * d.K * 4;
+    const size_t ns = bh * d.K * (d.d_v + 1) * 4;
+    if (misaligned(qr, 16) || misaligned(kr, 16) || misaligned(v, 16) || misaligned(out, 16)) return GMA_ERR_ALIGN;
+    if (misaligned(mu, 4) || misaligned(var_raw, 4) || misaligned(prior_logits, 4) || misaligned(state, 4))
+        return GMA_ERR_ALIGN;
+    if (workspace && misaligned(workspace, gma::kWsAlign)) return GMA_ERR_ALIGN;
+    const void* ins[6] = {qr, kr, v, mu, var_raw, prior_logits};
+    const size_t ins_n[6] = {nx, nx, nv, np, np, npr};
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(out, nv, ins[i], ins_n[i]) || overlaps(state, ns, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
+    if (overlaps(out, nv, state, ns)) return GMA_ERR_ALIAS;
+    const size_t need = gma::decode_workspace(d);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GMA_ERR_WORKSPACE;
+    if (workspace && (overlaps(workspace, need, out, nv) || overlaps(workspace, need, state, ns))) return GMA_ERR_ALIAS;
+    for (int i = 0; i < 6; ++i)
+        if (workspace && overlaps(workspace, need, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
+    Args a;
+    memset(&a, 0, sizeof(a));
+    a.qr = qr;
+    a.kr = kr;
+    a.v = v;
+    a.mu = mu;
+    a.var_raw = var_raw;
+    a.prior = prior_logits;
+    a.eps = eps;
+    a.out = out;
+    a.state = state;
+    a.d = d;
+    a.Nk = 1;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.ws_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gma::decode_forward(a) == hipSuccess ? GMA_OK : GMA_ERR_HIP;
 }
 
 const char* gma_strerror(int status) {

@@ -28,6 +28,7 @@ struct Args {
     float eps;
     void* out;
     float* gamma_out;
+    float* state;  // causal memory [B,H,K,d_v+1] (memory and decode entry points only)
     gma_desc d;    // d.N is the query (and output) length
     int Nk;        // key / value length (= d.N except in the cross variant)
     unsigned char* ws;
@@ -66,10 +67,23 @@ hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const doub
 // the log-determinant), both double.
 hipError_t simt_params(const Args& a, double* lam, double* cst);
 size_t simt_param_bytes(const gma_desc& d);
+// Causal memory [B,H,K,d_v+1] of the d.N positions of a.kr, a.v into a.state (SIMT).
+size_t simt_memory_workspace(const gma_desc& d);
+hipError_t simt_memory(const Args& a);
+
+// Causal memory (prefill) and single-token decode step (gma_decode.hip).
+size_t memory_workspace(const gma_desc& d);
+hipError_t memory_forward(const Args& a);
+size_t decode_workspace(const gma_desc& d);
+hipError_t decode_forward(const Args& a);
 
 // MFMA family (bf16 inputs): fused matrix-core kernels.
 size_t mfma_workspace(const gma_desc& d, int causal, int Nk);
 bool mfma_supported(const gma_desc& d, int causal);
 hipError_t mfma_forward(const Args& a);
+// Split partials of the bidirectional write kernel for the N key rows of a.kr, a.v, summed
+// in split order into a.state (the causal memory layout); used by memory_forward.
+hipError_t mfma_memory(const Args& a);
+size_t mfma_memory_workspace(const gma_desc& d);
 
 }  // namespace gma

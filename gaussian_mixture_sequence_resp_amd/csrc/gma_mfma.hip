@@ -409,6 +409,25 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
     }
 }
 
+// ---------------------------------------------------------------------------------- memory
+// Causal memory from the split partials of the write kernel: for component k < K,
+// state[bh][k][c] = sum_s part_v[bh][s][k][c] (c < d_v), state[bh][k][d_v] = sum_s part_z[bh][s][k],
+// in split order.  Grid (ceil(K (d_v+1) / 256), min(B H, 65535)), heads strided by gridDim.y.
+__global__ void __launch_bounds__(256)
+    gma_memory_reduce(const float* __restrict__ part_v, const float* __restrict__ part_z, float* __restrict__ state,
+                      int BH, int S, int K, int Kp, int dv, int Dvp) {
+    const int W = dv + 1;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= K * W) return;
+    const int k = i / W, c = i % W;
+    for (size_t bh = blockIdx.y; bh < (size_t)BH; bh += gridDim.y) {
+        float acc = 0.0f;
+        for (int s = 0; s < S; ++s)
+            acc += c < dv ? part_v[((bh * S + s) * Kp + k) * Dvp + c] : part_z[(bh * S + s) * Kp + k];
+        state[bh * K * W + i] = acc;
+    }
+}
+
 // ---------------------------------------------------------------------------------- host
 typedef void (*WriteFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, float*, float*, int, int, int,
                         int, int, int, int);
@@ -527,6 +546,45 @@ static hipError_t bidir_forward(const Args& a) {
     hipLaunchKernelGGL(rf, dim3(BH * parts), dim3(64 * kReadWaves), rl, a.stream, static_cast<const bf16_t*>(a.qr),
                        W, cvec, part_v, part_z, static_cast<bf16_t*>(a.out), a.eps, BH, d.H, d.N, d.d_r, d.d_v, S,
                        parts, part_len);
+    rec_end(a);
+    return hipGetLastError();
+}
+
+size_t mfma_memory_workspace(const gma_desc& d) { return mfma_layout(d, d.N).total; }
+
+// The write phase over the d.N positions of a.kr, a.v, then the split partials summed into
+// a.state.
+hipError_t mfma_memory(const Args& a) {
+    const gma_desc& d = a.d;
+    const Geo g = geometry(d);
+    const int N = d.N;
+    const MfmaLayout L = mfma_layout(d, N);
+    bf16_t* W = reinterpret_cast<bf16_t*>(a.ws + L.W);
+    float* cvec = reinterpret_cast<float*>(a.ws + L.C);
+    float* part_v = reinterpret_cast<float*>(a.ws + L.part_v);
+    float* part_z = reinterpret_cast<float*>(a.ws + L.part_z);
+    const int BH = d.B * d.H;
+    hipError_t e;
+    WriteFn wf;
+    ReadFn rf;
+    if (!select(g, wf, rf)) return hipErrorNotSupported;
+    if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
+    const int S = num_splits(d, N);
+    const int split_len = ((N + S - 1) / S + kIterT - 1) / kIterT * kIterT;
+    const size_t wl = write_lds_bytes(g);
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(wf), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)wl)) != hipSuccess)
+        return e;
+    rec_begin(a, "gma_bidir_write");
+    hipLaunchKernelGGL(wf, dim3(BH * S), dim3(kThreads), wl, a.stream, static_cast<const bf16_t*>(a.kr),
+                       static_cast<const bf16_t*>(a.v), W, cvec, part_v, part_z, BH, d.H, N, d.d_r, d.d_v, S,
+                       split_len);
+    rec_end(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int per = d.K * (d.d_v + 1);
+    rec_begin(a, "gma_memory_reduce");
+    gma_memory_reduce<<<dim3((unsigned)((per + 255) / 256), (unsigned)(BH < 65535 ? BH : 65535)), dim3(256), 0,
+                        a.stream>>>(part_v, part_z, a.state, BH, S, d.K, g.Kp, d.d_v, g.Dvp);
     rec_end(a);
     return hipGetLastError();
 }

@@ -299,4 +299,37 @@ hipError_t simt_forward(const Args& a) {
     return a.d.dtype == GMA_F32 ? simt_forward_t<float>(a) : simt_forward_t<bf16_t>(a);
 }
 
+// Causal memory of the a.d.N positions of a.kr, a.v: Gamma_K (float32, workspace) and the
+// write kernel straight into a.state ([B,H,K,d_v+1] is the write kernel's own layout).
+size_t simt_memory_workspace(const gma_desc& d) {
+    return simt_param_bytes(d) + align_up((size_t)d.B * d.H * d.N * d.K * sizeof(float));
+}
+
+template <typename T>
+hipError_t simt_memory_t(const Args& a) {
+    const gma_desc& d = a.d;
+    double* lam = reinterpret_cast<double*>(a.ws);
+    double* cst = reinterpret_cast<double*>(a.ws + align_up((size_t)d.H * d.K * d.d_r * sizeof(double)));
+    float* gk = reinterpret_cast<float*>(a.ws + simt_param_bytes(d));
+    hipError_t e = simt_params(a, lam, cst);
+    if (e != hipSuccess) return e;
+    // key side only: no query rows (Nq = 0), the N positions as keys
+    Args ka = a;
+    ka.d.N = 0;
+    ka.Nk = d.N;
+    ka.qr = a.kr;
+    if (d.N > 0 && (e = simt_gamma(ka, gk, lam, cst)) != hipSuccess) return e;
+    const int BH = d.B * d.H;
+    const int wblk = (d.K * (d.d_v + 1) + kBlock - 1) / kBlock;
+    rec_begin(a, "simt_write");
+    write_kernel<T><<<dim3(BH * wblk), dim3(kBlock), 0, a.stream>>>(gk, static_cast<const T*>(a.v), a.state, d.N,
+                                                                      d.K, d.d_v, wblk);
+    rec_end(a);
+    return hipGetLastError();
+}
+
+hipError_t simt_memory(const Args& a) {
+    return a.d.dtype == GMA_F32 ? simt_memory_t<float>(a) : simt_memory_t<bf16_t>(a);
+}
+
 }  // namespace gma

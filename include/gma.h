@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GMA_VERSION 10100 /* 1.1.0: cross variant */
+#define GMA_VERSION 10200 /* 1.2.0: cross variant, causal memory and decode step */
 
 /* Limits of this build. */
 #define GMA_MAX_K 256
@@ -167,6 +167,37 @@ int gma_forward_cross_timed(const void* qr, const void* kr, const void* v, const
                             void* out, float* gamma_out, const gma_desc* desc, void* workspace,
                             size_t workspace_bytes, void* stream, void* const* events, int n_events,
                             const char** names, int* n_kernels);
+
+/*
+ * Causal memory and single-token decode step: the causal variant of "Core mechanism" item
+ * 3 written as a recurrence over positions (the pages give the prefix-sum form; the
+ * recurrence is the same sums taken one position at a time).  The state of one (b, h)
+ * after positions 0..t-1 is the float32 memory [S | z], layout [B,H,K,d_v+1]: row k holds
+ * S[k][0..d_v-1] = sum_j gamma_K,j[k] v_j and, last, z[k] = sum_j gamma_K,j[k].
+ *
+ * gma_memory: the state after the desc->N positions of kr [B,H,N,d_r] and v [B,H,N,d_v]
+ *   (a prefill; N = 0 gives zeros; B = 0 or H = 0 is a no-op).  `state` is written.
+ * gma_decode_step: one position per (b, h); desc->N must be 1.  qr, kr [B,H,1,d_r],
+ *   v [B,H,1,d_v]; `state` is updated in place to include this position (the causal sum
+ *   is inclusive) and out [B,H,1,d_v] = gamma_Q S / (gamma_Q . z + eps): row t of the
+ *   causal forward when `state` held positions 0..t-1.
+ * Sums over positions are in position order (memory) and per step (decode), so a prefill
+ * followed by decode steps matches the causal forward to rounding, not bitwise.  The
+ * other rules (alignment: tensors 16 B, parameters and state 4 B, workspace 256 B; no
+ * aliasing between outputs, state and inputs; status codes) are those of gma_forward.
+ */
+size_t gma_memory_workspace_size(const gma_desc* desc);
+
+int gma_memory(const void* kr, const void* v, const float* mu, const float* var_raw,
+               const float* prior_logits, float* state, const gma_desc* desc, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+size_t gma_decode_workspace_size(const gma_desc* desc);
+
+int gma_decode_step(const void* qr, const void* kr, const void* v, const float* mu,
+                    const float* var_raw, const float* prior_logits, float* state, float eps,
+                    void* out, const gma_desc* desc, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* gma_strerror(int status);

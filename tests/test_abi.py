@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(lib):
     names = set(re.findall(r"\b(gma_[a-z_]+)\s*\(", txt))
     assert names == {"gma_workspace_size", "gma_forward", "gma_forward_timed", "gma_strerror",
                      "gma_version", "gma_workspace_size_cross", "gma_forward_cross",
-                     "gma_forward_cross_timed"}
+                     "gma_forward_cross_timed", "gma_memory_workspace_size", "gma_memory",
+                     "gma_decode_workspace_size", "gma_decode_step"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -176,3 +177,45 @@ def test_cross_workspace_size(lib):
     dm = binding.make_desc(2, 3, 64, 64, 64, 128, "bf16", 1e-3, "mfma")
     assert binding.workspace_size_cross(dm, 5000) > 0
     assert binding.workspace_size_cross(dm, 64) == binding.workspace_size(dm, False)
+
+
+def test_memory_and_decode_validation(lib):
+    vp = ctypes.c_void_p
+    lib.gma_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                    ctypes.POINTER(binding.GmaDesc), vp, ctypes.c_size_t, vp]
+    lib.gma_memory.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(binding.GmaDesc), vp, ctypes.c_size_t, vp]
+    step = 1 << 24
+    P = [Call.BASE + i * step for i in range(10)]  # qr kr v mu var_raw prior state out ws, spare
+
+    def dec(desc, eps=1e-6, **kw):
+        p = dict(qr=P[0], kr=P[1], v=P[2], mu=P[3], vr=P[4], pr=P[5], st=P[6], out=P[7], ws=P[8], nb=1 << 40)
+        p.update(kw)
+        return lib.gma_decode_step(p["qr"], p["kr"], p["v"], p["mu"], p["vr"], p["pr"], p["st"], eps, p["out"],
+                                   ctypes.byref(desc), p["ws"], p["nb"], None)
+
+    def mem(desc, **kw):
+        p = dict(kr=P[1], v=P[2], mu=P[3], vr=P[4], pr=P[5], st=P[6], ws=P[8], nb=1 << 40)
+        p.update(kw)
+        return lib.gma_memory(p["kr"], p["v"], p["mu"], p["vr"], p["pr"], p["st"], ctypes.byref(desc), p["ws"],
+                              p["nb"], None)
+
+    d1 = binding.make_desc(2, 3, 1, 16, 8, 12, "bf16", 1e-3, "auto")
+    assert dec(binding.make_desc(2, 3, 2, 16, 8, 12, "bf16", 1e-3)) == C["GMA_ERR_BAD_SHAPE"]
+    assert dec(binding.make_desc(2, 3, 1, 16, 8, 12, "bf16", 1e-3, "mfma")) == C["GMA_ERR_UNSUPPORTED"]
+    assert dec(d1, eps=-1.0) == C["GMA_ERR_BAD_SCALAR"]
+    assert dec(d1, st=None) == C["GMA_ERR_NULL_ARG"]
+    assert dec(d1, st=P[6] + 2) == C["GMA_ERR_ALIGN"]
+    assert dec(d1, out=P[6]) == C["GMA_ERR_ALIAS"]
+    assert dec(d1, st=P[0]) == C["GMA_ERR_ALIAS"]
+    assert dec(d1, nb=8) == C["GMA_ERR_WORKSPACE"]
+    assert dec(binding.make_desc(0, 3, 1, 16, 8, 12, "bf16", 1e-3), qr=None) == C["GMA_OK"]
+    assert binding.load_library().gma_decode_workspace_size(ctypes.byref(d1)) > 0
+    dm = binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "auto")
+    assert mem(dm, st=None) == C["GMA_ERR_NULL_ARG"]
+    assert mem(dm, kr=None) == C["GMA_ERR_NULL_ARG"]
+    assert mem(dm, st=P[1]) == C["GMA_ERR_ALIAS"]
+    assert mem(dm, nb=8) == C["GMA_ERR_WORKSPACE"]
+    assert mem(binding.make_desc(2, 3, 64, 100, 8, 12, "bf16", 1e-3, "mfma")) == C["GMA_ERR_UNSUPPORTED"]
+    # an empty prefix needs no kr / v (the state is still written: fails here on the workspace)
+    assert mem(binding.make_desc(2, 3, 0, 16, 8, 12, "bf16", 1e-3), kr=None, v=None, nb=8) == C["GMA_ERR_WORKSPACE"]
+    assert binding.load_library().gma_memory_workspace_size(ctypes.byref(dm)) > 0
