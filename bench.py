@@ -14,8 +14,9 @@ entering the headline time.  Prints one JSON line.
 value = whole-job throughput in token-heads/s (B*H*N / seconds per step).  The
 default workload is the bidirectional bf16 K=128 workload (B=8, H=8, N=4096,
 d_r=d_v=64); the causal LM-shaped workload (B=16, H=8, N=2048, K=256) is measured the
-same way and reported under "causal", and the cross variant (1024 queries reading a
-memory of 16384 keys per head, K=128) under "cross".
+same way and reported under "causal", the cross variant (1024 queries reading a
+memory of 16384 keys per head, K=128) under "cross", and the single-token causal decode
+step at the causal workload's shape under "decode".
 """
 from __future__ import annotations
 
@@ -199,6 +200,62 @@ def roofline_for(w, per_kernel):
     return rl
 
 
+def run_decode(w, steps, warmup):
+    """Single-token causal decode at workload w's (B, H, K, d) shape: the memory of a
+    prefix of w.N positions (gma_memory, timed on its own as the prefill), then `steps`
+    decode steps, each one gma_decode_step call (one kernel) over every (b, h).  Returns ms
+    per step, the prefill's ms and the bytes a step must move."""
+    import torch
+    import gaussian_mixture_sequence_resp_amd as gma
+    from gaussian_mixture_sequence_resp_amd.inputs import make_inputs
+
+    inp = make_inputs(w.with_(N=w.N + steps + warmup))
+    dev = torch.device("cuda:0")
+    d = {k: v.to(dev) for k, v in inp.items()}
+    kp, vp = d["kr"][:, :, :w.N].contiguous(), d["v"][:, :, :w.N].contiguous()
+    state = torch.empty((w.B, w.H, w.K, w.d_v + 1), dtype=torch.float32, device=dev)
+    mdesc = gma.make_desc(w.B, w.H, w.N, w.d_r, w.d_v, w.K, w.dtype, w.var_floor)
+    mws = torch.empty(max(int(gma.load_library().gma_memory_workspace_size(ctypes.byref(mdesc))), 1),
+                      dtype=torch.uint8, device=dev)
+
+    def prefill():
+        gma.memory(kp, vp, d["mu"], d["var_raw"], d["prior_logits"], var_floor=w.var_floor, state=state,
+                   workspace=mws)
+
+    for _ in range(3):
+        prefill()
+    torch.cuda.synchronize()
+    reps = 5
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        prefill()
+    torch.cuda.synchronize()
+    prefill_ms = (time.perf_counter() - t0) * 1e3 / reps
+    prefill()
+    rows = [(d["qr"][:, :, t].contiguous(), d["kr"][:, :, t].contiguous(), d["v"][:, :, t].contiguous())
+            for t in range(w.N, w.N + steps + warmup)]
+    out = torch.empty((w.B, w.H, 1, w.d_v), dtype=d["qr"].dtype, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(i):
+        q, k, v = rows[i]
+        gma.decode_step(q, k, v, d["mu"], d["var_raw"], d["prior_logits"], state, eps=w.eps,
+                        var_floor=w.var_floor, out=out, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, warmup + steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # state read and written once per step, plus this position's q, k, v and out
+    s = 4 if w.dtype == "f32" else 2
+    nbytes = w.B * w.H * (2 * 4 * w.K * (w.d_v + 1) + s * (2 * w.d_r + 2 * w.d_v))
+    return {"ms_per_step": ms, "bytes_per_step": nbytes, "prefill_ms": prefill_ms}
+
+
 def cpu_baseline(w, inp, budget_s=12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload (whole batch
     elements, all heads of each), timed on this host's cores.  The oracle spreads its
@@ -234,6 +291,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-causal", action="store_true")
     ap.add_argument("--no-cross", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy one 256 MiB device buffer, so that a profiler's "
                          "memory counters can be scaled by a copy of known size")
@@ -288,6 +346,19 @@ def main():
                          "key_token_heads_per_s": round(wx.B * wx.H * wx.Nk / sec, 1),
                          "per_kernel_ms": {k: round(v, 5) for k, v in rx["per_kernel_ms"].items()},
                          "roofline": roofline_for(wx, rx["per_kernel_ms"])}
+    if not args.no_decode and args.workload == 2:
+        wd = WORKLOADS[3]
+        rd = run_decode(wd, max(20, args.steps), max(5, args.warmup))
+        sec = rd["ms_per_step"] * 1e-3
+        line["decode"] = {"workload": f"{wd.name} decode (prefix {wd.N}, one position per step)",
+                          "us_per_step": round(rd["ms_per_step"] * 1e3, 2),
+                          "prefill_ms": round(rd["prefill_ms"], 4),
+                          "prefill_token_heads_per_s": round(wd.B * wd.H * wd.N / (rd["prefill_ms"] * 1e-3), 1),
+                          "value": round(wd.B * wd.H / sec, 1), "unit": "token-heads/s",
+                          "roofline": {"bound": "hbm", "achieved": round(rd["bytes_per_step"] / sec / 1e9, 2),
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": round(rd["bytes_per_step"] / sec / 1e9 / HBM_PEAK_GBS, 4),
+                                       "note": "whole step (launches included); latency-bound"}}
     if args.copy_calibration:
         import torch
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")

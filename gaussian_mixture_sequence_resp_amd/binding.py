@@ -256,13 +256,14 @@ def decode_step(qr, kr, v, mu, var_raw, prior_logits, state, eps: float = 1e-6, 
     if out is None:
         out = torch.empty((B, H, 1, d_v), dtype=qr.dtype, device=qr.device)
     need = int(lib.gma_decode_workspace_size(ctypes.byref(desc)))
-    if workspace is None:
+    if workspace is None and need > 0:
         workspace = _ws(need, qr)
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
     if stream is None:
         stream = torch.cuda.current_stream(qr.device).cuda_stream
     st = lib.gma_decode_step(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), mu.data_ptr(), var_raw.data_ptr(),
                              prior_logits.data_ptr(), state.data_ptr(), float(eps), out.data_ptr(),
-                             ctypes.byref(desc), workspace.data_ptr(), workspace.numel(), stream)
+                             ctypes.byref(desc), ws_ptr, ws_bytes, stream)
     if st != GMA_OK:
         raise GMAError(st, strerror(st))
     return out

@@ -181,7 +181,7 @@ int gma_forward_cross_timed(const void* qr, const void* kr, const void* v, const
 // ---- causal memory (prefill) and single-token decode step
 
 static bool memory_algo_ok(const gma_desc& d) {
-    return d.algo != GMA_ALGO_MFMA || (d.dtype == GMA_BF16 && gma::mfma_supported(d, 0));
+    return d.algo != GMA_ALGO_MFMA || (d.dtype == GMA_BF16 && gma::mfma_memory_supported(d));
 }
 
 size_t gma_memory_workspace_size(const gma_desc* desc) {

@@ -81,8 +81,11 @@ hipError_t decode_forward(const Args& a);
 size_t mfma_workspace(const gma_desc& d, int causal, int Nk);
 bool mfma_supported(const gma_desc& d, int causal);
 hipError_t mfma_forward(const Args& a);
-// Split partials of the bidirectional write kernel for the N key rows of a.kr, a.v, summed
-// in split order into a.state (the causal memory layout); used by memory_forward.
+// Causal memory of the N key rows of a.kr, a.v into a.state (layout [B,H,K,d_v+1]): split
+// partials of the bidirectional write kernel summed in split order, or, where that kernel's
+// coefficient block does not fit in LDS, Gamma_K from the causal responsibilities kernel and
+// sub-segment totals summed in order; used by memory_forward.
+bool mfma_memory_supported(const gma_desc& d);
 hipError_t mfma_memory(const Args& a);
 size_t mfma_memory_workspace(const gma_desc& d);
 

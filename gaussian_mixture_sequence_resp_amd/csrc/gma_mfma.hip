@@ -550,12 +550,24 @@ static hipError_t bidir_forward(const Args& a) {
     return hipGetLastError();
 }
 
-size_t mfma_memory_workspace(const gma_desc& d) { return mfma_layout(d, d.N).total; }
+// The fused write kernel when its coefficient block fits in LDS, else the two-pass form on
+// the causal kernels (responsibilities to HBM, then sub-segment totals).
+static bool memory_fused(const gma_desc& d) { return mfma_supported(d, 0); }
+
+bool mfma_memory_supported(const gma_desc& d) {
+    if (d.dtype != GMA_BF16 || d.d_r % 8 != 0 || d.d_v % 8 != 0) return false;
+    return memory_fused(d) || causal_supported(d);
+}
+
+size_t mfma_memory_workspace(const gma_desc& d) {
+    return memory_fused(d) ? mfma_layout(d, d.N).total : causal_memory_workspace(d);
+}
 
 // The write phase over the d.N positions of a.kr, a.v, then the split partials summed into
 // a.state.
 hipError_t mfma_memory(const Args& a) {
     const gma_desc& d = a.d;
+    if (!memory_fused(d)) return causal_memory(a);
     const Geo g = geometry(d);
     const int N = d.N;
     const MfmaLayout L = mfma_layout(d, N);

@@ -633,6 +633,50 @@ hipError_t set_lds(const void* f, size_t bytes) {
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// Responsibilities of `sides` sides (2: Gamma_Q into GQ and Gamma_K into GK; 1: Gamma_K
+// only, into GK), about one workgroup per CU per side.
+hipError_t launch_resp(const Args& a, const Geo& g, RespFn rf, int nph, int Np, int sides, const bf16_t* W,
+                       const float* cvec, bf16_t* GQ, bf16_t* GK) {
+    const gma_desc& d = a.d;
+    const int BH = d.B * d.H;
+    const int rstep = kTileT * kRespWaves;
+    int parts = (256 + BH - 1) / BH;
+    const int max_parts = (Np + rstep - 1) / rstep;
+    if (parts > max_parts) parts = max_parts;
+    if (parts < 1) parts = 1;
+    const int part_len = ((Np + parts - 1) / parts + rstep - 1) / rstep * rstep;
+    parts = (Np + part_len - 1) / part_len;
+    const size_t rl = resp_lds(g, nph);
+    hipError_t e;
+    if ((e = set_lds(reinterpret_cast<const void*>(rf), rl)) != hipSuccess) return e;
+    const bf16_t* kr = static_cast<const bf16_t*>(a.kr);
+    const bf16_t* qr = sides == 2 ? static_cast<const bf16_t*>(a.qr) : kr;
+    rec_begin(a, "gma_causal_resp");
+    hipLaunchKernelGGL(rf, dim3(BH * parts, sides), dim3(64 * kRespWaves), rl, a.stream, qr, kr, W, cvec,
+                       sides == 2 ? GQ : GK, GK, BH, d.H, d.N, Np, d.d_r, parts, part_len);
+    rec_end(a);
+    return hipGetLastError();
+}
+
+// Ordered sum over the nsub sub-segment totals of each head into the causal memory
+// [B,H,K,d_v+1] (natural component order; totals rows are slots, slot kperm(k) holds k).
+__global__ void __launch_bounds__(256)
+    gma_causal_memory_reduce(const float* __restrict__ tpart, float* __restrict__ state, int BH, int nsub, int NS,
+                             int K, int Kp, int dv, int Dvs) {
+    const int W = dv + 1;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= K * W) return;
+    const int k = i / W, c = i % W;
+    const int y = c < dv ? c / Dvs : 0, col = c < dv ? c % Dvs : Dvs;
+    const size_t tile = (size_t)Kp * (Dvs + 1);
+    for (size_t bh = blockIdx.y; bh < (size_t)BH; bh += gridDim.y) {
+        const float* p = tpart + (bh * nsub * NS + y) * tile + (size_t)kperm(k) * (Dvs + 1) + col;
+        float acc = 0.0f;
+        for (int s = 0; s < nsub; ++s) acc += p[(size_t)s * NS * tile];
+        state[bh * K * W + i] = acc;
+    }
+}
+
 }  // namespace
 
 bool causal_supported(const gma_desc& d) {
@@ -664,22 +708,7 @@ hipError_t causal_forward(const Args& a) {
 
     if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
 
-    // responsibilities of both sides, ~one workgroup per CU per side
-    const int rstep = kTileT * kRespWaves;
-    int parts = (256 + BH - 1) / BH;
-    const int max_parts = (L.Np + rstep - 1) / rstep;
-    if (parts > max_parts) parts = max_parts;
-    if (parts < 1) parts = 1;
-    const int part_len = ((L.Np + parts - 1) / parts + rstep - 1) / rstep * rstep;
-    parts = (L.Np + part_len - 1) / part_len;
-    const size_t rl = resp_lds(g, nph);
-    if ((e = set_lds(reinterpret_cast<const void*>(rf), rl)) != hipSuccess) return e;
-    rec_begin(a, "gma_causal_resp");
-    hipLaunchKernelGGL(rf, dim3(BH * parts, 2), dim3(64 * kRespWaves), rl, a.stream, static_cast<const bf16_t*>(a.qr),
-                       static_cast<const bf16_t*>(a.kr), W, cvec, GQ, GK, BH, d.H, d.N, L.Np, d.d_r, parts,
-                       part_len);
-    rec_end(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_resp(a, g, rf, nph, L.Np, 2, W, cvec, GQ, GK)) != hipSuccess) return e;
 
     if (L.S > 1) {
         const size_t tl = totals_lds_bytes(g, L.Dvs);
@@ -696,6 +725,78 @@ hipError_t causal_forward(const Args& a) {
     rec_begin(a, "gma_causal_scan");
     hipLaunchKernelGGL(sf, dim3(BH * L.S, L.NS), dim3(kThreads), sl, a.stream, GQ, GK, static_cast<const bf16_t*>(a.v),
                        tpart, static_cast<bf16_t*>(a.out), a.eps, BH, d.N, L.Np, d.d_v, L.S, L.NS, L.seg_len, L.TS);
+    rec_end(a);
+    return hipGetLastError();
+}
+
+// Causal memory (prefill) on the causal kernels: Gamma_K of every position (the
+// responsibilities kernel on the key side only), Gamma_K^T [V | 1] of nsub sub-segments
+// (the totals kernel over the whole sequence), then their ordered sum into the state.
+// Used where the fused write kernel of the bidirectional path does not fit in LDS.
+struct MemoryLayout {
+    size_t W, C, gk, tpart, total;
+    int Np, NS, Dvs, nsub, sub_len;
+};
+
+static MemoryLayout memory_layout(const gma_desc& d) {
+    const Geo g = geometry(d);
+    const int BH = d.B * d.H;
+    MemoryLayout L;
+    L.Dvs = g.Dvp < kSliceV ? g.Dvp : kSliceV;
+    L.NS = g.Dvp / L.Dvs;
+    const int groups = (d.N + kGroup - 1) / kGroup;
+    L.Np = groups * kGroup;
+    int s = (256 + BH * L.NS - 1) / (BH * L.NS);
+    if (s > groups) s = groups;
+    if (s < 1) s = 1;
+    L.sub_len = ((d.N + s - 1) / s + kGroup - 1) / kGroup * kGroup;
+    L.nsub = d.N > 0 ? (d.N + L.sub_len - 1) / L.sub_len : 0;
+    size_t off = 0;
+    L.W = off;
+    off += align_up((size_t)d.H * g.Kp * 4 * g.Dp * sizeof(bf16_t));
+    L.C = off;
+    off += align_up((size_t)d.H * g.Kp * sizeof(float));
+    L.gk = off;
+    off += align_up((size_t)BH * L.Np * g.Kp * sizeof(bf16_t));
+    L.tpart = off;
+    off += align_up((size_t)BH * L.nsub * L.NS * g.Kp * (L.Dvs + 1) * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+size_t causal_memory_workspace(const gma_desc& d) { return memory_layout(d).total; }
+
+hipError_t causal_memory(const Args& a) {
+    const gma_desc& d = a.d;
+    const Geo g = geometry(d);
+    const MemoryLayout L = memory_layout(d);
+    bf16_t* W = reinterpret_cast<bf16_t*>(a.ws + L.W);
+    float* cvec = reinterpret_cast<float*>(a.ws + L.C);
+    bf16_t* GK = reinterpret_cast<bf16_t*>(a.ws + L.gk);
+    float* tpart = reinterpret_cast<float*>(a.ws + L.tpart);
+    const int BH = d.B * d.H;
+    const int NTS = L.Dvs / 32;
+    hipError_t e;
+    const int nph = resp_phases(g);
+    RespFn rf = nph ? select_resp(g, nph) : nullptr;
+    TotFn tf;
+    ScanFn sf;
+    if (!rf || !select_scan(g, NTS, tf, sf)) return hipErrorNotSupported;
+    if (L.nsub > 0) {
+        if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
+        if ((e = launch_resp(a, g, rf, nph, L.Np, 1, W, cvec, nullptr, GK)) != hipSuccess) return e;
+        const size_t tl = totals_lds_bytes(g, L.Dvs);
+        if ((e = set_lds(reinterpret_cast<const void*>(tf), tl)) != hipSuccess) return e;
+        rec_begin(a, "gma_causal_totals");
+        hipLaunchKernelGGL(tf, dim3(BH * L.nsub, L.NS), dim3(kThreads), tl, a.stream, GK,
+                           static_cast<const bf16_t*>(a.v), tpart, BH, d.N, L.Np, d.d_v, L.NS, L.nsub, L.sub_len);
+        rec_end(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int per = d.K * (d.d_v + 1);
+    rec_begin(a, "gma_causal_memory_reduce");
+    gma_causal_memory_reduce<<<dim3((unsigned)((per + 255) / 256), (unsigned)(BH < 65535 ? BH : 65535)), dim3(256),
+                               0, a.stream>>>(tpart, a.state, BH, L.nsub, L.NS, d.K, g.Kp, d.d_v, L.Dvs);
     rec_end(a);
     return hipGetLastError();
 }

@@ -112,6 +112,8 @@ hipError_t launch_prep(const Args& a, const Geo& g, bf16_t* W, float* cvec);
 bool causal_supported(const gma_desc& d);
 size_t causal_workspace(const gma_desc& d);
 hipError_t causal_forward(const Args& a);
+size_t causal_memory_workspace(const gma_desc& d);
+hipError_t causal_memory(const Args& a);
 
 }  // namespace mf
 }  // namespace gma

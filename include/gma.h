@@ -180,7 +180,8 @@ int gma_forward_cross_timed(const void* qr, const void* kr, const void* v, const
  * gma_decode_step: one position per (b, h); desc->N must be 1.  qr, kr [B,H,1,d_r],
  *   v [B,H,1,d_v]; `state` is updated in place to include this position (the causal sum
  *   is inclusive) and out [B,H,1,d_v] = gamma_Q S / (gamma_Q . z + eps): row t of the
- *   causal forward when `state` held positions 0..t-1.
+ *   causal forward when `state` held positions 0..t-1.  One kernel launch; the
+ *   workspace size is 0 (workspace may be NULL), the mixture parameters are read raw.
  * Sums over positions are in position order (memory) and per step (decode), so a prefill
  * followed by decode steps matches the causal forward to rounding, not bitwise.  The
  * other rules (alignment: tensors 16 B, parameters and state 4 B, workspace 256 B; no

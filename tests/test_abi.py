@@ -207,9 +207,9 @@ def test_memory_and_decode_validation(lib):
     assert dec(d1, st=P[6] + 2) == C["GMA_ERR_ALIGN"]
     assert dec(d1, out=P[6]) == C["GMA_ERR_ALIAS"]
     assert dec(d1, st=P[0]) == C["GMA_ERR_ALIAS"]
-    assert dec(d1, nb=8) == C["GMA_ERR_WORKSPACE"]
     assert dec(binding.make_desc(0, 3, 1, 16, 8, 12, "bf16", 1e-3), qr=None) == C["GMA_OK"]
-    assert binding.load_library().gma_decode_workspace_size(ctypes.byref(d1)) > 0
+    # the decode step needs no workspace: one kernel, its reductions in LDS
+    assert binding.load_library().gma_decode_workspace_size(ctypes.byref(d1)) == 0
     dm = binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "auto")
     assert mem(dm, st=None) == C["GMA_ERR_NULL_ARG"]
     assert mem(dm, kr=None) == C["GMA_ERR_NULL_ARG"]

@@ -45,6 +45,9 @@ def _run(inp, w, split, algo="auto"):
 DECODE = [
     # (N, K, d_r, d_v, split)
     (40, 256, 64, 64, 0), (17, 5, 3, 7, 9), (33, 128, 128, 128, 20), (64, 33, 24, 40, 63), (1, 1, 8, 8, 0),
+    # bf16 prefills of these run on the causal responsibilities + totals kernels (coefficient
+    # blocks too large for the fused write kernel), ragged in positions and components
+    (300, 256, 64, 64, 250), (200, 200, 40, 24, 130),
 ]
 
 
@@ -66,10 +69,12 @@ def test_memory_then_decode_matches_causal_forward(N, K, dr, dv, split, dtype):
     assert metrics.rowrel(state, ref_state) <= tol
 
 
-@pytest.mark.parametrize("algo", ["simt", "auto"])
-def test_memory_long_prefix(algo):
-    # the prefill on the matrix-core write kernel (bf16, auto) and on the SIMT path
-    w = WORKLOADS[3].with_(B=2, H=2, N=2048 + 77, seed=61)
+@pytest.mark.parametrize("K", [256, 128])
+@pytest.mark.parametrize("algo", ["simt", "auto", "mfma"])
+def test_memory_long_prefix(algo, K):
+    # the prefill on the matrix cores (bf16; K = 128 the fused write kernel, K = 256 the
+    # causal responsibilities + totals kernels) and on the SIMT path
+    w = WORKLOADS[3].with_(B=2, H=2, N=2048 + 77, K=K, seed=61)
     inp = make_inputs(w)
     _say("memory long prefix", algo, w)
     d = {k: x.to(DEV) for k, x in inp.items()}
@@ -88,7 +93,7 @@ def test_memory_of_empty_prefix_is_zero():
     w = WORKLOADS[3].with_(B=2, H=2, N=0, seed=62)
     inp = make_inputs(w)
     d = {k: x.to(DEV) for k, x in inp.items()}
-    for algo in ("simt", "auto"):
+    for algo in ("simt", "auto", "mfma"):
         state = torch.full((2, 2, w.K, w.d_v + 1), 7.0, device=DEV)
         gma.memory(d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"], var_floor=w.var_floor, state=state,
                    algo=algo)
