@@ -99,3 +99,32 @@ def test_memory_of_empty_prefix_is_zero():
                    algo=algo)
         torch.cuda.synchronize()
         assert torch.count_nonzero(state) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_with_parameters_not_16_byte_aligned(dtype):
+    # mu and var_raw views starting one float into their buffers (4-byte aligned, as the ABI
+    # allows): the decode kernel takes its scalar-load path; same results as aligned copies
+    w = WORKLOADS[3].with_(B=2, H=3, N=6, K=40, d_r=32, d_v=16, dtype=dtype, seed=63)
+    inp = make_inputs(w)
+    d = {k: x.to(DEV) for k, x in inp.items()}
+    _say("decode unaligned parameters", dtype)
+
+    def shifted(x):
+        buf = torch.zeros(x.numel() + 1, dtype=x.dtype, device=DEV)
+        buf[1:] = x.reshape(-1)
+        return buf[1:].view(x.shape)
+
+    mu_s, vr_s = shifted(d["mu"]), shifted(d["var_raw"])
+    assert mu_s.data_ptr() % 16 != 0 and vr_s.data_ptr() % 16 != 0
+    outs = []
+    for mu, vr in ((d["mu"], d["var_raw"]), (mu_s, vr_s)):
+        state = gma.memory(d["kr"][:, :, :3].contiguous(), d["v"][:, :, :3].contiguous(), mu, vr, d["prior_logits"],
+                           var_floor=w.var_floor)
+        o = [gma.decode_step(d["qr"][:, :, t:t + 1], d["kr"][:, :, t:t + 1], d["v"][:, :, t:t + 1], mu, vr,
+                             d["prior_logits"], state, eps=w.eps, var_floor=w.var_floor) for t in range(3, 6)]
+        outs.append(torch.cat(o, dim=2).cpu())
+    ref = oracle.forward(inp["qr"], inp["kr"], inp["v"], inp["mu"], inp["var_raw"], inp["prior_logits"], True,
+                         w.eps, w.var_floor)
+    for o in outs:
+        assert metrics.rowrel(o, ref[:, :, 3:]) <= metrics.tol_for(dtype)
