@@ -13,5 +13,6 @@ from .oracle import (  # noqa: F401
     forward_cross,
     memory,
     decode_step,
+    resp_stats,
     num_threads,
 )

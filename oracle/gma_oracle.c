@@ -27,6 +27,10 @@
  *     0..t-1 is the state [S | z] (K x (d_v+1)); one step adds gamma_K,t (x) [v_t | 1] and
  *     reads O_t = gamma_Q,t S / (gamma_Q,t . z + eps), which is row t of the causal forward.
  *     The memory of a prefix is the write phase over its positions.
+ *   Responsibility statistics (the pages' interpretability analysis of learned
+ *     responsibilities: components used, usage entropy, hard assignments): per head, over
+ *     the rows of the batch, hard assignments (argmax), their histogram, the soft usage
+ *     sum of gamma, the number of components used and the normalised usage entropy.
  *
  * Readings of points the pages leave open: the log-density keeps every constant
  * (log 2 pi and the prior's log-sum-exp); eps is added once per output row after
@@ -342,6 +346,77 @@ int gma_oracle_decode_step(const double* qr, const double* kr, const double* v, 
         }
         free(gq);
         free(gk);
+        if (st != ORACLE_OK) {
+#pragma omp critical
+            status = st;
+        }
+    }
+    return status;
+}
+
+/*
+ * Responsibility statistics of the routing rows x [B,H,N,d_r] (queries or keys), per head,
+ * pooled over the batch and the positions: the quantities of the pages' interpretability
+ * analysis of learned responsibilities (components used, usage entropy, hard assignments).
+ * Readings (the pages name the quantities but do not define them):
+ *   hard    [B,H,N]  hard assignment: argmax_k of the log joint (= of gamma), the lowest k
+ *                    among equal maxima
+ *   counts  [H,K]    number of rows (b, n) whose hard assignment is k
+ *   usage   [H,K]    soft usage: sum over the rows (b, n) of gamma_k
+ *   used    [H]      number of components with counts > 0
+ *   entropy [H]      usage entropy: -sum_k p_k ln p_k / ln K with p_k = counts_k / (B N) and
+ *                    0 ln 0 = 0, i.e. the Shannon entropy of the hard-usage frequencies
+ *                    normalised to [0, 1]; 0 when K = 1 or B N = 0
+ * Rows are visited in the order b, then n; sums follow that order.
+ */
+int gma_oracle_resp_stats(const double* x, const double* mu, const double* var_raw, const double* prior_logits,
+                          int B, int H, int N, int d_r, int K, double var_floor, int* hard, long long* counts,
+                          double* usage, int* used, double* entropy) {
+    if (!x || !mu || !var_raw || !prior_logits || !hard || !counts || !usage || !used || !entropy)
+        return ORACLE_BAD_ARG;
+    if (B < 0 || H < 1 || N < 0 || d_r < 1 || K < 1) return ORACLE_BAD_ARG;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < H; ++h) {
+        long long* ch = counts + (size_t)h * K;
+        double* uh = usage + (size_t)h * K;
+        for (int k = 0; k < K; ++k) { ch[k] = 0; uh[k] = 0.0; }
+        const size_t n_alloc = (size_t)(N > 0 ? N : 1) * K;
+        double* lj = (double*)malloc(sizeof(double) * n_alloc);
+        double* g = (double*)malloc(sizeof(double) * n_alloc);
+        int st = (lj && g) ? ORACLE_OK : ORACLE_NO_MEM;
+        const double* mu_h = mu + (size_t)h * K * d_r;
+        const double* vr_h = var_raw + (size_t)h * K * d_r;
+        const double* p_h = prior_logits + (size_t)h * K;
+        for (int b = 0; b < B && st == ORACLE_OK && N > 0; ++b) {
+            const double* xb = x + ((size_t)b * H + h) * N * d_r;
+            st = gma_oracle_log_joint(xb, N, d_r, mu_h, vr_h, p_h, K, var_floor, lj);
+            if (st == ORACLE_OK) st = gma_oracle_responsibilities(xb, N, d_r, mu_h, vr_h, p_h, K, var_floor, g);
+            if (st != ORACLE_OK) break;
+            for (int i = 0; i < N; ++i) {
+                const double* li = lj + (size_t)i * K;
+                int best = 0;
+                for (int k = 1; k < K; ++k)
+                    if (li[k] > li[best]) best = k;
+                hard[((size_t)b * H + h) * N + i] = best;
+                ch[best] += 1;
+                for (int k = 0; k < K; ++k) uh[k] += g[(size_t)i * K + k];
+            }
+        }
+        int nu = 0;
+        double ent = 0.0;
+        const double rows = (double)B * (double)N;
+        for (int k = 0; k < K; ++k) {
+            if (ch[k] > 0) {
+                ++nu;
+                const double p = (double)ch[k] / rows;
+                ent -= p * log(p);
+            }
+        }
+        used[h] = nu;
+        entropy[h] = (K > 1 && rows > 0) ? ent / log((double)K) : 0.0;
+        free(lj);
+        free(g);
         if (st != ORACLE_OK) {
 #pragma omp critical
             status = st;

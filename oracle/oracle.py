@@ -60,6 +60,10 @@ def _load():
         lib.gma_oracle_memory.restype = i
         lib.gma_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i, i, d, d, dp, dp]
         lib.gma_oracle_decode_step.restype = i
+        ip = ctypes.POINTER(ctypes.c_int)
+        lp = ctypes.POINTER(ctypes.c_longlong)
+        lib.gma_oracle_resp_stats.argtypes = [dp, dp, dp, dp, i, i, i, i, i, d, ip, lp, dp, ip, dp]
+        lib.gma_oracle_resp_stats.restype = ctypes.c_int
         lib.gma_oracle_num_threads.argtypes = []
         lib.gma_oracle_num_threads.restype = i
         _lib = lib
@@ -198,3 +202,26 @@ def decode_step(qr, kr, v, mu, var_raw, prior_logits, state: np.ndarray, eps: fl
     if st != 0:
         raise RuntimeError(f"gma_oracle_decode_step failed: {st}")
     return out
+
+
+def resp_stats(x, mu, var_raw, prior_logits, var_floor: float) -> dict:
+    """Responsibility statistics of the routing rows x [B,H,N,d_r] per head, pooled over the
+    batch and the positions: ``hard`` int32 [B,H,N] (argmax, lowest index on ties),
+    ``counts`` int64 [H,K], ``usage`` float64 [H,K] (sum of gamma), ``used`` int32 [H],
+    ``entropy`` float64 [H] (hard-usage entropy over ln K)."""
+    lib = _load()
+    x, mu, vr, p = (_f64(a) for a in (x, mu, var_raw, prior_logits))
+    B, H, N, d_r = x.shape
+    K = mu.shape[1]
+    hard = np.zeros((B, H, N), dtype=np.int32)
+    counts = np.zeros((H, K), dtype=np.int64)
+    usage = np.zeros((H, K), dtype=np.float64)
+    used = np.zeros(H, dtype=np.int32)
+    entropy = np.zeros(H, dtype=np.float64)
+    ip = ctypes.POINTER(ctypes.c_int)
+    st = lib.gma_oracle_resp_stats(_ptr(x), _ptr(mu), _ptr(vr), _ptr(p), B, H, N, d_r, K, float(var_floor),
+                                   hard.ctypes.data_as(ip), counts.ctypes.data_as(ctypes.POINTER(ctypes.c_longlong)),
+                                   _ptr(usage), used.ctypes.data_as(ip), _ptr(entropy))
+    if st != 0:
+        raise RuntimeError(f"oracle resp_stats failed: {st}")
+    return {"hard": hard, "counts": counts, "usage": usage, "used": used, "entropy": entropy}

@@ -428,6 +428,76 @@ def test_decode_closed_forms():
     assert not oracle.memory(kr[:, :, :0], v[:, :, :0], mu, vr, p, 1e-3).any()
 
 
+# ---------------------------------------------------------------- responsibility statistics
+# The pages' interpretability analysis (components used, usage entropy, hard assignments):
+# hard = argmax of the posterior (lowest index on ties), counts = its histogram per head
+# over (b, n), usage = sum of the posteriors, used = #{counts > 0}, entropy = Shannon
+# entropy of counts / (B N) over ln K.
+
+@pytest.mark.parametrize("B,H,N,dr,K", [(2, 3, 50, 5, 7), (1, 2, 1, 3, 4), (3, 1, 33, 8, 16)])
+def test_resp_stats_match_sklearn(B, H, N, dr, K):
+    rng = np.random.default_rng(71 + N + K)
+    x, _, _, mu, vr, p = _random_problem(rng, B, H, N, dr, 1, K, mu_std=1.5)
+    r = oracle.resp_stats(x, mu, vr, p, 1e-3)
+    for h in range(H):
+        gam = np.concatenate([_sk_gamma(x[b, h], mu[h], vr[h], p[h]) for b in range(B)])
+        from sklearn.mixture import GaussianMixture
+        gm = GaussianMixture(n_components=K, covariance_type="diag")
+        var = _var(vr[h], 1e-3)
+        gm.weights_, gm.means_, gm.covariances_ = scipy.special.softmax(p[h]), mu[h], var
+        gm.precisions_cholesky_ = 1.0 / np.sqrt(var)
+        pred = np.concatenate([gm.predict(x[b, h]) for b in range(B)])
+        np.testing.assert_array_equal(r["hard"][:, h].reshape(-1), pred)
+        cnt = np.bincount(pred, minlength=K)
+        np.testing.assert_array_equal(r["counts"][h], cnt)
+        np.testing.assert_allclose(r["usage"][h], gam.sum(0), rtol=1e-12, atol=1e-12)
+        assert r["used"][h] == np.count_nonzero(cnt)
+        ref_ent = scipy.stats.entropy(cnt) / np.log(K) if K > 1 else 0.0
+        np.testing.assert_allclose(r["entropy"][h], ref_ent, rtol=1e-12, atol=1e-15)
+    # soft usage sums to the number of rows; counts too
+    np.testing.assert_allclose(r["usage"].sum(1), B * N, rtol=1e-12)
+    np.testing.assert_array_equal(r["counts"].sum(1), B * N)
+
+
+def test_resp_stats_closed_forms():
+    rng = np.random.default_rng(72)
+    # K = 1: everything to component 0, entropy 0
+    x, _, _, mu, vr, p = _random_problem(rng, 2, 2, 9, 3, 1, 1)
+    r = oracle.resp_stats(x, mu, vr, p, 1e-3)
+    assert (r["hard"] == 0).all() and (r["counts"] == 18).all() and (r["used"] == 1).all()
+    np.testing.assert_allclose(r["usage"], 18.0, rtol=1e-14)
+    assert (r["entropy"] == 0.0).all()
+    # identical Gaussians, different priors: gamma = pi for every row, hard = argmax prior
+    K, dr = 5, 4
+    mu = np.tile(rng.normal(size=(1, 1, dr)), (1, K, 1))
+    vr = np.tile(rng.normal(size=(1, 1, dr)), (1, K, 1))
+    p = np.array([[0.1, 0.7, -0.3, 0.7, 0.2]])
+    x = rng.normal(size=(2, 1, 6, dr))
+    r = oracle.resp_stats(x, mu, vr, p, 1e-3)
+    assert (r["hard"] == 1).all()  # components 1 and 3 tie on the prior: the lower index
+    np.testing.assert_allclose(r["usage"][0], 12 * scipy.special.softmax(p[0]), rtol=1e-12)
+    assert r["used"][0] == 1 and r["entropy"][0] == 0.0
+    # each row at a distinct, well-separated mean, every component hit equally often:
+    # uniform usage, entropy exactly 1
+    K, dr = 8, 3
+    mu = 10.0 * rng.normal(size=(1, K, dr))
+    vr = np.full((1, K, dr), -4.0)
+    p = np.zeros((1, K))
+    x = np.stack([mu[0][np.arange(4 * K) % K]]).reshape(1, 1, 4 * K, dr)
+    r = oracle.resp_stats(x, mu, vr, p, 1e-3)
+    np.testing.assert_array_equal(r["hard"][0, 0], np.arange(4 * K) % K)
+    assert (r["counts"][0] == 4).all() and r["used"][0] == K
+    np.testing.assert_allclose(r["entropy"][0], 1.0, rtol=1e-14)
+    # two of the components take all rows equally: entropy ln 2 / ln K
+    x2 = np.stack([mu[0][np.arange(6) % 2]]).reshape(1, 1, 6, dr)
+    r = oracle.resp_stats(x2, mu, vr, p, 1e-3)
+    assert r["used"][0] == 2
+    np.testing.assert_allclose(r["entropy"][0], np.log(2) / np.log(K), rtol=1e-14)
+    # no rows: nothing counted
+    r = oracle.resp_stats(x[:, :, :0], mu, vr, p, 1e-3)
+    assert r["counts"].sum() == 0 and r["used"][0] == 0 and r["entropy"][0] == 0.0
+
+
 def test_golden_fixture_regression():
     import json
     import os
