@@ -15,8 +15,9 @@ value = whole-job throughput in token-heads/s (B*H*N / seconds per step).  The
 default workload is the bidirectional bf16 K=128 workload (B=8, H=8, N=4096,
 d_r=d_v=64); the causal LM-shaped workload (B=16, H=8, N=2048, K=256) is measured the
 same way and reported under "causal", the cross variant (1024 queries reading a
-memory of 16384 keys per head, K=128) under "cross", and the single-token causal decode
-step at the causal workload's shape under "decode".
+memory of 16384 keys per head, K=128) under "cross", the single-token causal decode
+step at the causal workload's shape under "decode", and the responsibility statistics of
+that workload's key rows under "stats".
 """
 from __future__ import annotations
 
@@ -256,6 +257,40 @@ def run_decode(w, steps, warmup):
     return {"ms_per_step": ms, "bytes_per_step": nbytes, "prefill_ms": prefill_ms}
 
 
+def run_stats(w, steps, warmup):
+    """Responsibility statistics (gma_resp_stats: hard assignments, counts, soft usage, used,
+    entropy) of the key rows of workload w, one call per step; returns ms per call and the
+    call's algorithmic bytes and flops (one side's log-density; x read, hard written)."""
+    import torch
+    import gaussian_mixture_sequence_resp_amd as gma
+    from gaussian_mixture_sequence_resp_amd.inputs import make_inputs
+
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    d = {k: inp[k].to(dev) for k in ("kr", "mu", "var_raw", "prior_logits")}
+    desc = gma.make_desc(w.B, w.H, w.N, w.d_r, 1, w.K, w.dtype, w.var_floor)
+    ws = torch.empty(max(int(gma.load_library().gma_stats_workspace_size(ctypes.byref(desc))), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        return gma.resp_stats(d["kr"], d["mu"], d["var_raw"], d["prior_logits"], var_floor=w.var_floor,
+                              workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    s = 4 if w.dtype == "f32" else 2
+    th = w.B * w.H * w.N
+    return {"ms_per_call": ms, "bytes": th * (s * w.d_r + 4), "flops": th * 2 * w.K * (2 * w.d_r + 1)}
+
+
 def cpu_baseline(w, inp, budget_s=12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload (whole batch
     elements, all heads of each), timed on this host's cores.  The oracle spreads its
@@ -292,6 +327,7 @@ def main():
     ap.add_argument("--no-causal", action="store_true")
     ap.add_argument("--no-cross", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-stats", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy one 256 MiB device buffer, so that a profiler's "
                          "memory counters can be scaled by a copy of known size")
@@ -359,6 +395,19 @@ def main():
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": round(rd["bytes_per_step"] / sec / 1e9 / HBM_PEAK_GBS, 4),
                                        "note": "whole step (launches included); latency-bound"}}
+    if not args.no_stats and args.workload == 2:
+        ws_ = WORKLOADS[3]
+        rs = run_stats(ws_, max(10, args.steps // 2), max(3, args.warmup // 2))
+        sec = rs["ms_per_call"] * 1e-3
+        tf = rs["flops"] / sec / 1e12
+        line["stats"] = {"workload": f"{ws_.name} key rows: responsibility statistics (hard assignments, counts, "
+                                     "soft usage, components used, usage entropy)",
+                         "ms_per_call": round(rs["ms_per_call"], 5),
+                         "value": round(ws_.B * ws_.H * ws_.N / sec, 1), "unit": "token-heads/s",
+                         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                      "note": "whole call (prep, responsibilities, usage, finish) against the "
+                                              "log-density flops of one side"}}
     if args.copy_calibration:
         import torch
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     load_library,
     make_desc,
     memory,
+    resp_stats,
     strerror,
     version,
     workspace_size,

@@ -75,6 +75,10 @@ def load_library(path: Optional[str] = None):
     lib.gma_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.POINTER(GmaDesc), vp,
                                     sz, vp]
     lib.gma_decode_step.restype = ctypes.c_int
+    lib.gma_stats_workspace_size.argtypes = [ctypes.POINTER(GmaDesc)]
+    lib.gma_stats_workspace_size.restype = sz
+    lib.gma_resp_stats.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(GmaDesc), vp, sz, vp]
+    lib.gma_resp_stats.restype = ctypes.c_int
     lib.gma_strerror.argtypes = [ctypes.c_int]
     lib.gma_strerror.restype = ctypes.c_char_p
     lib.gma_version.argtypes = []
@@ -267,3 +271,39 @@ def decode_step(qr, kr, v, mu, var_raw, prior_logits, state, eps: float = 1e-6, 
     if st != GMA_OK:
         raise GMAError(st, strerror(st))
     return out
+
+
+def resp_stats(x, mu, var_raw, prior_logits, var_floor: float = 1e-3, with_hard: bool = True,
+               workspace=None, algo: str = "auto", stream=None) -> dict:
+    """Responsibility statistics of the routing rows x [B,H,N,d_r] per head (pooled over
+    the batch and the positions): ``hard`` int32 [B,H,N] (argmax, lowest index on ties; only
+    with ``with_hard``), ``counts`` int32 [H,K], ``usage`` float32 [H,K], ``used`` int32 [H],
+    ``entropy`` float32 [H] (hard-usage entropy over ln K)."""
+    import torch
+    lib = load_library()
+    _dense(x, mu, var_raw, prior_logits)
+    B, H, N, d_r = x.shape
+    K = mu.shape[1]
+    dev = x.device
+    desc = make_desc(B, H, N, d_r, 1, K, _dtype_name(x), var_floor, algo)
+    res = {
+        "hard": torch.empty((B, H, N), dtype=torch.int32, device=dev) if with_hard else None,
+        "counts": torch.empty((H, K), dtype=torch.int32, device=dev),
+        "usage": torch.empty((H, K), dtype=torch.float32, device=dev),
+        "used": torch.empty((H,), dtype=torch.int32, device=dev),
+        "entropy": torch.empty((H,), dtype=torch.float32, device=dev),
+    }
+    need = int(lib.gma_stats_workspace_size(ctypes.byref(desc)))
+    if workspace is None and need > 0:
+        workspace = _ws(need, x)
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    hard = res["hard"].data_ptr() if with_hard else None
+    st = lib.gma_resp_stats(x.data_ptr() if N > 0 else None, mu.data_ptr(), var_raw.data_ptr(),
+                            prior_logits.data_ptr(), hard, res["counts"].data_ptr(), res["usage"].data_ptr(),
+                            res["used"].data_ptr(), res["entropy"].data_ptr(), ctypes.byref(desc), ws_ptr, ws_bytes,
+                            stream)
+    if st != GMA_OK:
+        raise GMAError(st, strerror(st))
+    return res

@@ -288,6 +288,66 @@ int gma_decode_step(const void* qr, const void* kr, const void* v, const float* 
     return gma::decode_forward(a) == hipSuccess ? GMA_OK : GMA_ERR_HIP;
 }
 
+// ---- responsibility statistics
+
+static bool stats_algo_ok(const gma_desc& d) { return d.algo != GMA_ALGO_MFMA || gma::stats_on_mfma(d); }
+
+size_t gma_stats_workspace_size(const gma_desc* desc) {
+    if (check_desc(desc) != GMA_OK || (int64_t)desc->B * desc->H == 0 || !stats_algo_ok(*desc)) return 0;
+    return gma::stats_workspace(*desc);
+}
+
+int gma_resp_stats(const void* x, const float* mu, const float* var_raw, const float* prior_logits, int32_t* hard,
+                   int32_t* counts, float* usage, int32_t* used, float* entropy, const gma_desc* desc,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_desc(desc);
+    if (st != GMA_OK) return st;
+    const gma_desc d = *desc;
+    const size_t bh = (size_t)d.B * d.H;
+    if (bh == 0) return GMA_OK;
+    if (!mu || !var_raw || !prior_logits || !counts || !usage || !used || !entropy) return GMA_ERR_NULL_ARG;
+    if (d.N > 0 && !x) return GMA_ERR_NULL_ARG;  // no rows: x is not read
+    const size_t esz = d.dtype == GMA_F32 ? 4 : 2;
+    const size_t nx = bh * d.N * d.d_r * esz;
+    const size_t np = (size_t)d.H * d.K * d.d_r * 4, npr = (size_t)d.H * d.K * 4;
+    const size_t nhard = bh * d.N * 4, nhk = (size_t)d.H * d.K * 4, nh = (size_t)d.H * 4;
+    if (misaligned(x, 16)) return GMA_ERR_ALIGN;
+    if (misaligned(mu, 4) || misaligned(var_raw, 4) || misaligned(prior_logits, 4) || misaligned(hard, 4) ||
+        misaligned(counts, 4) || misaligned(usage, 4) || misaligned(used, 4) || misaligned(entropy, 4))
+        return GMA_ERR_ALIGN;
+    if (workspace && misaligned(workspace, gma::kWsAlign)) return GMA_ERR_ALIGN;
+    if (!stats_algo_ok(d)) return GMA_ERR_UNSUPPORTED;
+    const size_t need = gma::stats_workspace(d);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GMA_ERR_WORKSPACE;
+    const void* ins[4] = {x, mu, var_raw, prior_logits};
+    const size_t ins_n[4] = {nx, np, np, npr};
+    const void* outs[6] = {hard, counts, usage, used, entropy, workspace};
+    const size_t outs_n[6] = {nhard, nhk, nhk, nh, nh, need};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(outs[i], outs_n[i], ins[j], ins_n[j])) return GMA_ERR_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlaps(outs[i], outs_n[i], outs[j], outs_n[j])) return GMA_ERR_ALIAS;
+    }
+    Args a;
+    memset(&a, 0, sizeof(a));
+    a.kr = x;
+    a.mu = mu;
+    a.var_raw = var_raw;
+    a.prior = prior_logits;
+    a.hard = hard;
+    a.counts = counts;
+    a.usage = usage;
+    a.used = used;
+    a.entropy = entropy;
+    a.d = d;
+    a.Nk = d.N;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.ws_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gma::stats_forward(a) == hipSuccess ? GMA_OK : GMA_ERR_HIP;
+}
+
 const char* gma_strerror(int status) {
     switch (status) {
         case GMA_OK: return "success";

@@ -29,6 +29,12 @@ struct Args {
     void* out;
     float* gamma_out;
     float* state;  // causal memory [B,H,K,d_v+1] (memory and decode entry points only)
+    // responsibility statistics (stats entry point only)
+    int* hard;       // [B,H,N] or null
+    int* counts;     // [H,K]
+    float* usage;    // [H,K]
+    int* used;       // [H]
+    float* entropy;  // [H]
     gma_desc d;    // d.N is the query (and output) length
     int Nk;        // key / value length (= d.N except in the cross variant)
     unsigned char* ws;
@@ -62,7 +68,7 @@ size_t simt_workspace(const gma_desc& d, int causal, int Nk);
 hipError_t simt_forward(const Args& a);
 // Responsibilities only, written as float32 Gamma_Q [B,H,N,K] then Gamma_K [B,H,Nk,K]; used for
 // gamma_out by every family.
-hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst);
+hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst, int* hard = nullptr);
 // Parameter prep of the SIMT family: lam = 1/var [H,K,d_r], cst [H,K] (log prior minus half
 // the log-determinant), both double.
 hipError_t simt_params(const Args& a, double* lam, double* cst);
@@ -76,6 +82,11 @@ size_t memory_workspace(const gma_desc& d);
 hipError_t memory_forward(const Args& a);
 size_t decode_workspace(const gma_desc& d);
 hipError_t decode_forward(const Args& a);
+
+// Responsibility statistics of the rows a.kr (gma_stats.hip).
+size_t stats_workspace(const gma_desc& d);
+hipError_t stats_forward(const Args& a);
+bool stats_on_mfma(const gma_desc& d);
 
 // MFMA family (bf16 inputs): fused matrix-core kernels.
 size_t mfma_workspace(const gma_desc& d, int causal, int Nk);

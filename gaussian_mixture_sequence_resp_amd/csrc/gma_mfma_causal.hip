@@ -149,14 +149,16 @@ __device__ __forceinline__ void stage_coefficient_chunks(unsigned char* sW, floa
 // blockIdx.y: 0 queries, 1 keys): logits (MFMA), softmax over the components, normalised
 // responsibilities stored as bf16 operand fragments; positions in [N, Np) get zeros.  When
 // the coefficient block of a head exceeds LDS it is staged in NPH phases of the routing
-// dims, the logits accumulating across phases.
+// dims, the logits accumulating across phases.  STATS: also the hard assignment of every
+// position of side 0, argmax of its fp32 logits (lowest component among equal maxima),
+// into hard [BH][N].
 constexpr int kRespWaves = 8;
 
-template <int MT, int NC, int NPH>
+template <int MT, int NC, int NPH, bool STATS>
 __global__ void __launch_bounds__(64 * kRespWaves, 2)
     gma_causal_resp(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ W,
-                    const float* __restrict__ cvec, bf16_t* __restrict__ GQ, bf16_t* __restrict__ GK, int BH, int H,
-                    int N, int Np, int dr, int parts, int part_len) {
+                    const float* __restrict__ cvec, bf16_t* __restrict__ GQ, bf16_t* __restrict__ GK,
+                    int* __restrict__ hard, int BH, int H, int N, int Np, int dr, int parts, int part_len) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int Kp = 32 * MT, Dp = 16 * NC, NCP = NC / NPH, KS = Kp / 16;
     constexpr int wstride = 8 * (16 * NCP) + 16;
@@ -200,6 +202,27 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
             }
         }
         load_xrow<NC>(xr, row(b0 + kStep), dr);  // next step's rows, in flight during the softmax
+        if constexpr (STATS) {
+            // register e of tile m holds component 32 m + 8 (e / 4) + 4 half + e % 4 of token col
+            const int half = l >> 5;
+            float bv = -INFINITY;
+            int bk = 0;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int kc = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
+                    const float xv = acc[m][e];
+                    if (xv > bv || (xv == bv && kc < bk)) {
+                        bv = xv;
+                        bk = kc;
+                    }
+                }
+            const float ov = __shfl_xor(bv, 32, 64);
+            const int ok = __shfl_xor(bk, 32, 64);
+            if (ov > bv || (ov == bv && ok < bk)) bk = ok;
+            if (half == 0 && valid && t0 < n_end) hard[(size_t)bh * N + t0 + col] = bk;
+        }
         const float s = tile_exp<MT>(acc);
         const float inv = valid ? 1.0f / s : 0.0f;
         if (t0 < n_end) {
@@ -570,37 +593,41 @@ __global__ void __launch_bounds__(kThreads, 1)
 }
 
 // ----------------------------------------------------------------------------- dispatch
-typedef void (*RespFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, bf16_t*, int, int, int,
+typedef void (*RespFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, bf16_t*, int*, int, int, int,
                        int, int, int, int);
 typedef void (*TotFn)(const bf16_t*, const bf16_t*, float*, int, int, int, int, int, int, int);
 typedef void (*ScanFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, float, int, int, int, int,
                        int, int, int, int);
 
-template <int MT, int NC>
+template <int MT, int NC, bool STATS>
 RespFn resp_fn(int nph) {
-    if (nph == 1) return gma_causal_resp<MT, NC, 1>;
-    if (nph == 2 && NC % 2 == 0) return gma_causal_resp<MT, NC, (NC % 2 == 0 ? 2 : 1)>;
-    if (nph == 4 && NC % 4 == 0) return gma_causal_resp<MT, NC, (NC % 4 == 0 ? 4 : 1)>;
+    if (nph == 1) return gma_causal_resp<MT, NC, 1, STATS>;
+    if (nph == 2 && NC % 2 == 0) return gma_causal_resp<MT, NC, (NC % 2 == 0 ? 2 : 1), STATS>;
+    if (nph == 4 && NC % 4 == 0) return gma_causal_resp<MT, NC, (NC % 4 == 0 ? 4 : 1), STATS>;
     return nullptr;
 }
-template <int MT>
+template <int MT, bool STATS>
 RespFn resp_fn_nc(int NC, int nph) {
     switch (NC) {
-        case 1: return resp_fn<MT, 1>(nph);
-        case 2: return resp_fn<MT, 2>(nph);
-        case 4: return resp_fn<MT, 4>(nph);
-        case 8: return resp_fn<MT, 8>(nph);
+        case 1: return resp_fn<MT, 1, STATS>(nph);
+        case 2: return resp_fn<MT, 2, STATS>(nph);
+        case 4: return resp_fn<MT, 4, STATS>(nph);
+        case 8: return resp_fn<MT, 8, STATS>(nph);
     }
     return nullptr;
 }
-RespFn select_resp(const Geo& g, int nph) {
+template <bool STATS>
+RespFn select_resp_t(const Geo& g, int nph) {
     switch (g.MT) {
-        case 1: return resp_fn_nc<1>(g.NC, nph);
-        case 2: return resp_fn_nc<2>(g.NC, nph);
-        case 4: return resp_fn_nc<4>(g.NC, nph);
-        case 8: return resp_fn_nc<8>(g.NC, nph);
+        case 1: return resp_fn_nc<1, STATS>(g.NC, nph);
+        case 2: return resp_fn_nc<2, STATS>(g.NC, nph);
+        case 4: return resp_fn_nc<4, STATS>(g.NC, nph);
+        case 8: return resp_fn_nc<8, STATS>(g.NC, nph);
     }
     return nullptr;
+}
+RespFn select_resp(const Geo& g, int nph, bool stats = false) {
+    return stats ? select_resp_t<true>(g, nph) : select_resp_t<false>(g, nph);
 }
 // LDS of the responsibilities kernel with the routing dims staged in nph phases.
 size_t resp_lds(const Geo& g, int nph) {
@@ -636,7 +663,7 @@ hipError_t set_lds(const void* f, size_t bytes) {
 // Responsibilities of `sides` sides (2: Gamma_Q into GQ and Gamma_K into GK; 1: Gamma_K
 // only, into GK), about one workgroup per CU per side.
 hipError_t launch_resp(const Args& a, const Geo& g, RespFn rf, int nph, int Np, int sides, const bf16_t* W,
-                       const float* cvec, bf16_t* GQ, bf16_t* GK) {
+                       const float* cvec, bf16_t* GQ, bf16_t* GK, int* hard = nullptr) {
     const gma_desc& d = a.d;
     const int BH = d.B * d.H;
     const int rstep = kTileT * kRespWaves;
@@ -653,7 +680,7 @@ hipError_t launch_resp(const Args& a, const Geo& g, RespFn rf, int nph, int Np, 
     const bf16_t* qr = sides == 2 ? static_cast<const bf16_t*>(a.qr) : kr;
     rec_begin(a, "gma_causal_resp");
     hipLaunchKernelGGL(rf, dim3(BH * parts, sides), dim3(64 * kRespWaves), rl, a.stream, qr, kr, W, cvec,
-                       sides == 2 ? GQ : GK, GK, BH, d.H, d.N, Np, d.d_r, parts, part_len);
+                       sides == 2 ? GQ : GK, GK, hard, BH, d.H, d.N, Np, d.d_r, parts, part_len);
     rec_end(a);
     return hipGetLastError();
 }
@@ -799,6 +826,26 @@ hipError_t causal_memory(const Args& a) {
                                0, a.stream>>>(tpart, a.state, BH, L.nsub, L.NS, d.K, g.Kp, d.d_v, L.Dvs);
     rec_end(a);
     return hipGetLastError();
+}
+
+// Responsibility statistics on the matrix cores: Gamma of the rows a.kr (written like the
+// key side, operand fragments [B H][Np/32][Kp/16][64][8] into G) and the hard assignment of
+// every row into hard [B H][N]; coefficients into W, cvec.  Np = N rounded up to 128.
+bool stats_supported(const gma_desc& d) {
+    if (d.dtype != GMA_BF16 || d.d_r % 8 != 0) return false;
+    return resp_phases(geometry(d)) > 0;
+}
+
+hipError_t stats_resp(const Args& a, bf16_t* W, float* cvec, bf16_t* G, int* hard) {
+    const gma_desc& d = a.d;
+    const Geo g = geometry(d);
+    const int nph = resp_phases(g);
+    RespFn rf = nph ? select_resp(g, nph, true) : nullptr;
+    if (!rf) return hipErrorNotSupported;
+    hipError_t e;
+    if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
+    const int Np = (d.N + kGroup - 1) / kGroup * kGroup;
+    return launch_resp(a, g, rf, nph, Np, 1, W, cvec, nullptr, G, hard);
 }
 
 }  // namespace mf

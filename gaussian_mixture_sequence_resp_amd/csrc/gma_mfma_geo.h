@@ -114,6 +114,9 @@ size_t causal_workspace(const gma_desc& d);
 hipError_t causal_forward(const Args& a);
 size_t causal_memory_workspace(const gma_desc& d);
 hipError_t causal_memory(const Args& a);
+// Responsibility statistics: Gamma (fragment order) and hard assignments of the rows a.kr.
+bool stats_supported(const gma_desc& d);
+hipError_t stats_resp(const Args& a, bf16_t* W, float* cvec, bf16_t* G, int* hard);
 
 }  // namespace mf
 }  // namespace gma

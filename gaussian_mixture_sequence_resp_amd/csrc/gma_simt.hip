@@ -78,8 +78,8 @@ __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
                                                       const float* __restrict__ mu,
                                                       const double* __restrict__ lam,
                                                       const double* __restrict__ cst,
-                                                      float* __restrict__ gamma, int BH, int H,
-                                                      int Nq, int Nk, int dr, int K, int nblk) {
+                                                      float* __restrict__ gamma, int* __restrict__ hard,
+                                                      int BH, int H, int Nq, int Nk, int dr, int K, int nblk) {
     const int side = blockIdx.y;
     const int N = side == 0 ? Nq : Nk;
     const int bh = blockIdx.x / nblk;
@@ -90,8 +90,11 @@ __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
     float* g = gamma + ((size_t)side * BH * Nq + (size_t)bh * N + n) * K;
     const float* mu_h = mu + (size_t)h * K * dr;
     const double* lam_h = lam + (size_t)h * K * dr;
-    // pass 1: row max of the logits (double), pass 2: shifted logits -> exp (float)
+    // pass 1: row max of the logits (double) and its component (the first one reaching it:
+    // the hard assignment, written for the key side when `hard` is given), pass 2: shifted
+    // logits -> exp (float)
     double m = -INFINITY;
+    int best = 0;
     for (int k = 0; k < K; ++k) {
         double q = 0.0;
         for (int d = 0; d < dr; ++d) {
@@ -99,8 +102,12 @@ __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
             q = fma(lam_h[(size_t)k * dr + d] * diff, diff, q);
         }
         const double l = cst[(size_t)h * K + k] - 0.5 * q;
-        m = fmax(m, l);
+        if (l > m) {
+            m = l;
+            best = k;
+        }
     }
+    if (hard && side == 1) hard[(size_t)bh * N + n] = best;
     for (int k = 0; k < K; ++k) {
         double q = 0.0;
         for (int d = 0; d < dr; ++d) {
@@ -276,7 +283,7 @@ hipError_t simt_params(const Args& a, double* lam, double* cst) {
     return hipGetLastError();
 }
 
-hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst) {
+hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst, int* hard) {
     const gma_desc& d = a.d;
     const int BH = d.B * d.H;
     const int nmax = d.N > a.Nk ? d.N : a.Nk;
@@ -285,11 +292,11 @@ hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const doub
     rec_begin(a, "simt_responsibilities");
     if (d.dtype == GMA_F32)
         resp_kernel<float><<<grid, dim3(kBlock), 0, a.stream>>>(
-            static_cast<const float*>(a.qr), static_cast<const float*>(a.kr), a.mu, lam, cst, gamma, BH,
+            static_cast<const float*>(a.qr), static_cast<const float*>(a.kr), a.mu, lam, cst, gamma, hard, BH,
             d.H, d.N, a.Nk, d.d_r, d.K, nblk);
     else
         resp_kernel<bf16_t><<<grid, dim3(kBlock), 0, a.stream>>>(
-            static_cast<const bf16_t*>(a.qr), static_cast<const bf16_t*>(a.kr), a.mu, lam, cst, gamma, BH,
+            static_cast<const bf16_t*>(a.qr), static_cast<const bf16_t*>(a.kr), a.mu, lam, cst, gamma, hard, BH,
             d.H, d.N, a.Nk, d.d_r, d.K, nblk);
     rec_end(a);
     return hipGetLastError();

@@ -1,0 +1,243 @@
+// Responsibility statistics of one set of routing rows, per head.
+//
+// Method: Gaussian Mixture Attention (arXiv 2606.18283).  The pages analyse the learned
+// responsibilities by component usage (how many of the K components receive rows, and the
+// entropy of that usage) and by hard assignments compared with token categories.  Computed
+// here for the rows x [B,H,N,d_r] (queries or keys), per head h pooled over (b, n):
+//   hard[b,h,n]  argmax_k gamma (the lowest k among equal maxima)
+//   counts[h,k]  number of rows whose hard assignment is k
+//   usage[h,k]   sum over the rows of gamma_k (soft usage)
+//   used[h]      number of k with counts > 0
+//   entropy[h]   -sum_k p_k ln p_k / ln K, p_k = counts / (B N)  (0 when K = 1 or no rows)
+//
+// Kernels (caller's stream, in this order):
+//   bf16, matrix cores: gma_prep and gma_causal_resp<..., STATS> (Gamma of the rows in MFMA
+//     operand-fragment order, hard assignments from the fp32 logits), then
+//     gma_stats_usage_frag (per chunk of fragment blocks, partial soft usage per slot);
+//   SIMT: params_kernel and resp_kernel (Gamma rows in float32, hard assignments from the
+//     double logits), then gma_stats_usage_rows (per chunk of rows, partial soft usage);
+//   both: gma_stats_finish (one workgroup per head: histogram of the hard assignments in
+//     LDS with integer atomics, so the counts do not depend on the order of arrival; the
+//     usage partials summed in chunk order; components used and the entropy).
+// Every floating-point sum has a fixed order: the results are deterministic.
+#include <math.h>
+
+#include "gma_internal.h"
+#include "gma_mfma_common.h"
+#include "gma_mfma_geo.h"
+#include "gma_numeric.h"
+
+namespace gma {
+namespace {
+
+constexpr int kUsageChunks = 4;  // usage partials per head (x Kp/16 x H workgroups)
+constexpr int kFinishThreads = 1024;
+
+// Partial soft usage of chunk c of head h over the fragment blocks of component block ks:
+// block u of the head's B * tpb blocks (b = u / tpb) is 64 lanes x 8 slots of bf16; lane l
+// holds slots 8 (l / 32) .. + 7 of the block for token l % 32.  Four groups of 64 threads
+// take every fourth block; each thread sums its lane's 8 slots in block order; then the
+// 4 groups x 32 lanes of each half are summed in a fixed order into part[h][c][16 ks + s].
+__global__ void __launch_bounds__(256)
+    gma_stats_usage_frag(const bf16_t* __restrict__ G, float* __restrict__ part, int H, int B, int tpb, int KS,
+                         int C, int per_chunk) {
+    __shared__ float sacc[4][64][9];
+    const int ks = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
+    const int t = threadIdx.x, grp = t >> 6, l = t & 63;
+    const int total = B * tpb;
+    const int u0 = c * per_chunk, u1 = min(total, u0 + per_chunk);
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    auto block = [&](int u) -> const bf16_t* {
+        const int b = u / tpb, tile = u % tpb;
+        return G + (((size_t)(b * H + h) * tpb + tile) * KS + ks) * (64 * 8) + 8 * l;
+    };
+    for (int u = u0 + grp; u < u1; u += 16) {
+        mf::bf16x8 x[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (u + 4 * q < u1) x[q] = *reinterpret_cast<const mf::bf16x8*>(block(u + 4 * q));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (u + 4 * q < u1) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j] += __uint_as_float((uint32_t)(unsigned short)x[q][j] << 16);
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sacc[grp][l][j] = acc[j];
+    __syncthreads();
+    if (t < 16) {
+        const int half = t >> 3, j = t & 7;
+        float s = 0.0f;
+        for (int g = 0; g < 4; ++g)
+            for (int i = 0; i < 32; ++i) s += sacc[g][32 * half + i][j];
+        part[((size_t)h * C + c) * (16 * KS) + 16 * ks + t] = s;
+    }
+}
+
+// Partial soft usage of chunk c of head h from float32 Gamma rows [B H][N][K]: thread k sums
+// gamma[row][k] over the chunk's rows in order (rows u = b N + n).
+__global__ void __launch_bounds__(256)
+    gma_stats_usage_rows(const float* __restrict__ gamma, float* __restrict__ part, int H, int B, int N, int K, int C,
+                         int per_chunk) {
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    const int h = blockIdx.y, c = blockIdx.z;
+    if (k >= K) return;
+    const int total = B * N;
+    const int u0 = c * per_chunk, u1 = min(total, u0 + per_chunk);
+    float s = 0.0f;
+    for (int u = u0; u < u1; ++u) {
+        const int b = u / N, n = u % N;
+        s += gamma[((size_t)(b * H + h) * N + n) * K + k];
+    }
+    part[((size_t)h * C + c) * K + k] = s;
+}
+
+// One workgroup per head: counts (histogram of hard over the head's B N rows), usage (the
+// C partials in chunk order; partial index of component k is kperm(k) in fragment slot order,
+// k otherwise), used, entropy.
+__global__ void __launch_bounds__(kFinishThreads)
+    gma_stats_finish(const int* __restrict__ hard, const float* __restrict__ part, int* __restrict__ counts,
+                     float* __restrict__ usage, int* __restrict__ used, float* __restrict__ entropy, int H, int B,
+                     int N, int K, int C, int pstride, int slot_order) {
+    __shared__ int hist[GMA_MAX_K];
+    const int h = blockIdx.x, t = threadIdx.x;
+    for (int k = t; k < K; k += kFinishThreads) hist[k] = 0;
+    __syncthreads();
+    const int total = B * N;
+    for (int u = t; u < total; u += kFinishThreads) {
+        const int b = u / N, n = u % N;
+        const int k = hard[(size_t)(b * H + h) * N + n];
+        if ((unsigned)k < (unsigned)K) atomicAdd(&hist[k], 1);
+    }
+    __syncthreads();
+    for (int k = t; k < K; k += kFinishThreads) {
+        counts[(size_t)h * K + k] = hist[k];
+        const int pi = slot_order ? mf::kperm(k) : k;
+        float s = 0.0f;
+        for (int c = 0; c < C; ++c) s += part[((size_t)h * C + c) * pstride + pi];
+        usage[(size_t)h * K + k] = s;
+    }
+    if (t < 64) {
+        // components used and -sum p ln p over lanes k = t + 64 i, then across the wave
+        const double rows = (double)total;
+        int nu = 0;
+        double ent = 0.0;
+        for (int k = t; k < K; k += 64) {
+            const int n = hist[k];
+            if (n > 0) {
+                ++nu;
+                const double p = (double)n / rows;
+                ent -= p * log(p);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            nu += __shfl_xor(nu, o, 64);
+            ent += __shfl_xor(ent, o, 64);
+        }
+        if (t == 0) {
+            used[h] = nu;
+            entropy[h] = (K > 1 && total > 0) ? (float)(ent / log((double)K)) : 0.0f;
+        }
+    }
+}
+
+struct StatsLayout {
+    size_t lam, cst, gamma, W, C, G, hard, part, total;
+    int Np, Kp, KS, chunks, per_chunk;
+};
+
+StatsLayout stats_layout(const gma_desc& d) {
+    StatsLayout L{};
+    const int BH = d.B * d.H;
+    size_t off = 0;
+    if (stats_on_mfma(d)) {
+        const mf::Geo g = mf::geometry(d);
+        L.Kp = g.Kp;
+        L.KS = g.Kp / 16;
+        L.Np = (d.N + mf::kIterT - 1) / mf::kIterT * mf::kIterT;
+        const int tpb = L.Np / 32;
+        L.chunks = d.N > 0 ? kUsageChunks : 0;
+        L.per_chunk = L.chunks ? (d.B * tpb + L.chunks - 1) / L.chunks : 0;
+        L.W = off;
+        off += align_up((size_t)d.H * g.Kp * 4 * g.Dp * sizeof(bf16_t));
+        L.C = off;
+        off += align_up((size_t)d.H * g.Kp * sizeof(float));
+        L.G = off;
+        off += align_up((size_t)BH * L.Np * g.Kp * sizeof(bf16_t));
+        L.part = off;
+        off += align_up((size_t)d.H * (L.chunks ? L.chunks : 1) * g.Kp * sizeof(float));
+    } else {
+        L.Kp = d.K;
+        // row chunks: about 256 workgroups over the heads
+        const int rows = d.B * d.N;
+        int c = (256 + d.H - 1) / d.H;
+        if (c > rows) c = rows;
+        L.chunks = rows > 0 ? c : 0;
+        L.per_chunk = L.chunks ? (rows + L.chunks - 1) / L.chunks : 0;
+        L.lam = off;
+        off += simt_param_bytes(d);
+        L.gamma = off;
+        off += align_up((size_t)BH * d.N * d.K * sizeof(float));
+        L.part = off;
+        off += align_up((size_t)d.H * (L.chunks ? L.chunks : 1) * d.K * sizeof(float));
+    }
+    L.hard = off;
+    off += align_up((size_t)BH * d.N * sizeof(int));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+bool stats_on_mfma(const gma_desc& d) { return d.algo != GMA_ALGO_SIMT && mf::stats_supported(d); }
+
+size_t stats_workspace(const gma_desc& d) { return stats_layout(d).total; }
+
+hipError_t stats_forward(const Args& a) {
+    const gma_desc& d = a.d;
+    const StatsLayout L = stats_layout(d);
+    int* hard = a.hard ? a.hard : reinterpret_cast<int*>(a.ws + L.hard);
+    float* part = reinterpret_cast<float*>(a.ws + L.part);
+    const bool mfma = stats_on_mfma(d);
+    hipError_t e;
+    if (d.N > 0) {
+        if (mfma) {
+            bf16_t* W = reinterpret_cast<bf16_t*>(a.ws + L.W);
+            float* cvec = reinterpret_cast<float*>(a.ws + L.C);
+            bf16_t* G = reinterpret_cast<bf16_t*>(a.ws + L.G);
+            if ((e = mf::stats_resp(a, W, cvec, G, hard)) != hipSuccess) return e;
+            rec_begin(a, "gma_stats_usage_frag");
+            gma_stats_usage_frag<<<dim3(L.KS, d.H, L.chunks), dim3(256), 0, a.stream>>>(
+                G, part, d.H, d.B, L.Np / 32, L.KS, L.chunks, L.per_chunk);
+            rec_end(a);
+        } else {
+            double* lam = reinterpret_cast<double*>(a.ws + L.lam);
+            double* cst = reinterpret_cast<double*>(a.ws + L.lam + align_up((size_t)d.H * d.K * d.d_r * sizeof(double)));
+            float* gamma = reinterpret_cast<float*>(a.ws + L.gamma);
+            if ((e = simt_params(a, lam, cst)) != hipSuccess) return e;
+            // the rows as the key side (no query rows)
+            Args ka = a;
+            ka.d.N = 0;
+            ka.Nk = d.N;
+            ka.qr = a.kr;
+            if ((e = simt_gamma(ka, gamma, lam, cst, hard)) != hipSuccess) return e;
+            rec_begin(a, "gma_stats_usage_rows");
+            gma_stats_usage_rows<<<dim3((d.K + 255) / 256, d.H, L.chunks), dim3(256), 0, a.stream>>>(
+                gamma, part, d.H, d.B, d.N, d.K, L.chunks, L.per_chunk);
+            rec_end(a);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    rec_begin(a, "gma_stats_finish");
+    gma_stats_finish<<<dim3(d.H), dim3(kFinishThreads), 0, a.stream>>>(
+        hard, part, a.counts, a.usage, a.used, a.entropy, d.H, d.B, d.N, d.K, L.chunks, mfma ? L.Kp : d.K,
+        mfma ? 1 : 0);
+    rec_end(a);
+    return hipGetLastError();
+}
+
+}  // namespace gma

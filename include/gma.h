@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GMA_VERSION 10200 /* 1.2.0: cross variant, causal memory and decode step */
+#define GMA_VERSION 10300 /* 1.3.0: responsibility statistics */
 
 /* Limits of this build. */
 #define GMA_MAX_K 256
@@ -199,6 +199,32 @@ int gma_decode_step(const void* qr, const void* kr, const void* v, const float* 
                     const float* var_raw, const float* prior_logits, float* state, float eps,
                     void* out, const gma_desc* desc, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * Responsibility statistics of one set of routing rows: the quantities of the pages'
+ * analysis of learned responsibilities (Results, interpretability: components used out of K,
+ * usage entropy, hard assignments compared with token categories).  The pages name them
+ * without defining them; the readings, per head h pooled over the batch and the positions:
+ *   hard    int32 [B,H,N]  argmax_k gamma of row (b, h, n), the lowest k among equal maxima;
+ *                          may be NULL (then kept in the workspace)
+ *   counts  int32 [H,K]    number of rows whose hard assignment is k
+ *   usage   float [H,K]    soft usage: sum over the rows of gamma_k
+ *   used    int32 [H]      number of components with counts > 0
+ *   entropy float [H]      -sum_k p_k ln p_k / ln K with p_k = counts / (B N): the usage
+ *                          entropy normalised to [0, 1] (0 when K = 1 or there are no rows)
+ * x [B,H,N,d_r] in desc->dtype (queries or keys; desc->d_v is not used but must be valid).
+ * The argmax is taken in the precision of the path's logits (fp32 on the matrix cores for
+ * bf16 inputs, double on the SIMT path), so rows whose two best components are closer than
+ * that precision may differ from a higher-precision evaluation.  Deterministic: the same
+ * call gives bitwise the same results.  Alignment: x 16 B, parameters and outputs 4 B,
+ * workspace 256 B; outputs and the workspace may not overlap each other or the inputs.
+ * N = 0 gives zero counts, usage, used and entropy; B = 0 or H = 0 is a no-op.
+ */
+size_t gma_stats_workspace_size(const gma_desc* desc);
+
+int gma_resp_stats(const void* x, const float* mu, const float* var_raw, const float* prior_logits,
+                   int32_t* hard, int32_t* counts, float* usage, int32_t* used, float* entropy,
+                   const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* gma_strerror(int status);

@@ -37,7 +37,8 @@ def test_exports_every_declared_symbol(lib):
     assert names == {"gma_workspace_size", "gma_forward", "gma_forward_timed", "gma_strerror",
                      "gma_version", "gma_workspace_size_cross", "gma_forward_cross",
                      "gma_forward_cross_timed", "gma_memory_workspace_size", "gma_memory",
-                     "gma_decode_workspace_size", "gma_decode_step"}
+                     "gma_decode_workspace_size", "gma_decode_step", "gma_stats_workspace_size",
+                     "gma_resp_stats"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -219,3 +220,43 @@ def test_memory_and_decode_validation(lib):
     # an empty prefix needs no kr / v (the state is still written: fails here on the workspace)
     assert mem(binding.make_desc(2, 3, 0, 16, 8, 12, "bf16", 1e-3), kr=None, v=None, nb=8) == C["GMA_ERR_WORKSPACE"]
     assert binding.load_library().gma_memory_workspace_size(ctypes.byref(dm)) > 0
+
+
+def test_stats_validation(lib):
+    # every call below fails validation (or is an empty no-op) before any HIP call
+    vp = ctypes.c_void_p
+    lib.gma_resp_stats.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(binding.GmaDesc), vp,
+                                   ctypes.c_size_t, vp]
+    step = 1 << 24
+    P = [Call.BASE + i * step for i in range(12)]  # x mu var_raw prior hard counts usage used entropy ws
+
+    def call(desc, **kw):
+        p = dict(x=P[0], mu=P[1], vr=P[2], pr=P[3], hard=P[4], counts=P[5], usage=P[6], used=P[7], ent=P[8],
+                 ws=P[9], nb=1 << 40)
+        p.update(kw)
+        return lib.gma_resp_stats(p["x"], p["mu"], p["vr"], p["pr"], p["hard"], p["counts"], p["usage"],
+                                  p["used"], p["ent"], ctypes.byref(desc), p["ws"], p["nb"], None)
+
+    d = binding.make_desc(2, 3, 64, 16, 1, 12, "bf16", 1e-3, "auto")
+    assert call(binding.make_desc(0, 3, 64, 16, 1, 12, "bf16", 1e-3), x=None, counts=None) == C["GMA_OK"]
+    assert call(d, counts=None) == C["GMA_ERR_NULL_ARG"]
+    assert call(d, ent=None) == C["GMA_ERR_NULL_ARG"]
+    assert call(d, x=None) == C["GMA_ERR_NULL_ARG"]
+    assert call(d, x=P[0] + 2) == C["GMA_ERR_ALIGN"]
+    assert call(d, counts=P[5] + 2) == C["GMA_ERR_ALIGN"]
+    assert call(d, ws=P[9] + 16) == C["GMA_ERR_ALIGN"]
+    assert call(binding.make_desc(2, 3, 64, 16, 1, 12, "f32", 1e-3, "mfma")) == C["GMA_ERR_UNSUPPORTED"]
+    assert call(binding.make_desc(2, 3, 64, 12, 1, 12, "bf16", 1e-3, "mfma")) == C["GMA_ERR_UNSUPPORTED"]
+    assert call(binding.make_desc(2, 3, 64, 16, 1, 300, "bf16", 1e-3)) == C["GMA_ERR_UNSUPPORTED"]
+    assert call(d, nb=8) == C["GMA_ERR_WORKSPACE"]
+    assert call(d, ws=None) == C["GMA_ERR_WORKSPACE"]
+    assert call(d, usage=P[5]) == C["GMA_ERR_ALIAS"]
+    assert call(d, hard=P[0]) == C["GMA_ERR_ALIAS"]
+    assert call(d, ws=P[1]) == C["GMA_ERR_ALIAS"]
+    sz = binding.load_library().gma_stats_workspace_size
+    sz.argtypes = [ctypes.POINTER(binding.GmaDesc)]
+    sz.restype = ctypes.c_size_t
+    assert sz(ctypes.byref(d)) > 0
+    assert sz(ctypes.byref(binding.make_desc(2, 3, 64, 16, 1, 12, "f32", 1e-3))) > 0
+    assert sz(ctypes.byref(binding.make_desc(0, 3, 64, 16, 1, 12, "bf16", 1e-3))) == 0
+    assert sz(ctypes.byref(binding.make_desc(2, 3, 64, 12, 1, 12, "bf16", 1e-3, "mfma"))) == 0
