@@ -203,7 +203,8 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
         }
         load_xrow<NC>(xr, row(b0 + kStep), dr);  // next step's rows, in flight during the softmax
         if constexpr (STATS) {
-            // register e of tile m holds component 32 m + 8 (e / 4) + 4 half + e % 4 of token col
+            // register e of tile m holds component 32 m + 8 (e / 4) + 4 half + e % 4 of token
+            // col: increasing in (m, e), so a strict > keeps the lowest of equal maxima
             const int half = l >> 5;
             float bv = -INFINITY;
             int bk = 0;
@@ -211,11 +212,10 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
             for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int kc = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
                     const float xv = acc[m][e];
-                    if (xv > bv || (xv == bv && kc < bk)) {
+                    if (xv > bv) {
                         bv = xv;
-                        bk = kc;
+                        bk = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
                     }
                 }
             const float ov = __shfl_xor(bv, 32, 64);

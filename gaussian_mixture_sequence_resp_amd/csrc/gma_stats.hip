@@ -16,9 +16,10 @@
 //     gma_stats_usage_frag (per chunk of fragment blocks, partial soft usage per slot);
 //   SIMT: params_kernel and resp_kernel (Gamma rows in float32, hard assignments from the
 //     double logits), then gma_stats_usage_rows (per chunk of rows, partial soft usage);
-//   both: gma_stats_finish (one workgroup per head: histogram of the hard assignments in
-//     LDS with integer atomics, so the counts do not depend on the order of arrival; the
-//     usage partials summed in chunk order; components used and the entropy).
+//   both: gma_stats_hist (per chunk of rows: histogram of the hard assignments in LDS with
+//     integer atomics, so the counts do not depend on the order of arrival), then
+//     gma_stats_finish (one workgroup per head: the chunk histograms and the usage partials
+//     summed in chunk order; components used and the entropy).
 // Every floating-point sum has a fixed order: the results are deterministic.
 #include <math.h>
 
@@ -31,7 +32,28 @@ namespace gma {
 namespace {
 
 constexpr int kUsageChunks = 4;  // usage partials per head (x Kp/16 x H workgroups)
+constexpr int kHistChunks = 16;  // count partials per head
 constexpr int kFinishThreads = 1024;
+
+// Partial histogram of the hard assignments of chunk c of head h's rows u = b N + n (integer
+// atomics in LDS: the counts do not depend on the order of arrival).
+__global__ void __launch_bounds__(1024)
+    gma_stats_hist(const int* __restrict__ hard, int* __restrict__ cpart, int H, int B, int N, int K,
+                   int per_chunk) {
+    __shared__ int hist[GMA_MAX_K];
+    const int h = blockIdx.x, c = blockIdx.y, t = threadIdx.x;
+    for (int k = t; k < K; k += blockDim.x) hist[k] = 0;
+    __syncthreads();
+    const int total = B * N;
+    const int u0 = c * per_chunk, u1 = min(total, u0 + per_chunk);
+    for (int u = u0 + t; u < u1; u += blockDim.x) {
+        const int b = u / N, n = u % N;
+        const int k = hard[(size_t)(b * H + h) * N + n];
+        if ((unsigned)k < (unsigned)K) atomicAdd(&hist[k], 1);
+    }
+    __syncthreads();
+    for (int k = t; k < K; k += blockDim.x) cpart[((size_t)h * kHistChunks + c) * K + k] = hist[k];
+}
 
 // Partial soft usage of chunk c of head h over the fragment blocks of component block ks:
 // block u of the head's B * tpb blocks (b = u / tpb) is 64 lanes x 8 slots of bf16; lane l
@@ -95,29 +117,39 @@ __global__ void __launch_bounds__(256)
     part[((size_t)h * C + c) * K + k] = s;
 }
 
-// One workgroup per head: counts (histogram of hard over the head's B N rows), usage (the
-// C partials in chunk order; partial index of component k is kperm(k) in fragment slot order,
-// k otherwise), used, entropy.
+// One workgroup per head: counts (the chunk histograms summed), usage (the C partials in
+// chunk order; partial index of component k is kperm(k) in fragment slot order, k
+// otherwise), used, entropy.
 __global__ void __launch_bounds__(kFinishThreads)
-    gma_stats_finish(const int* __restrict__ hard, const float* __restrict__ part, int* __restrict__ counts,
+    gma_stats_finish(const int* __restrict__ cpart, const float* __restrict__ part, int* __restrict__ counts,
                      float* __restrict__ usage, int* __restrict__ used, float* __restrict__ entropy, int H, int B,
-                     int N, int K, int C, int pstride, int slot_order) {
+                     int N, int K, int CH, int C, int pstride, int slot_order) {
     __shared__ int hist[GMA_MAX_K];
     const int h = blockIdx.x, t = threadIdx.x;
-    for (int k = t; k < K; k += kFinishThreads) hist[k] = 0;
-    __syncthreads();
     const int total = B * N;
-    for (int u = t; u < total; u += kFinishThreads) {
-        const int b = u / N, n = u % N;
-        const int k = hard[(size_t)(b * H + h) * N + n];
-        if ((unsigned)k < (unsigned)K) atomicAdd(&hist[k], 1);
+    // (partials loaded 16 at a time, then added in chunk order)
+    for (int k = t; k < K; k += kFinishThreads) {
+        int v[kHistChunks];
+#pragma unroll
+        for (int c = 0; c < kHistChunks; ++c) v[c] = c < CH ? cpart[((size_t)h * kHistChunks + c) * K + k] : 0;
+        int n = 0;
+#pragma unroll
+        for (int c = 0; c < kHistChunks; ++c) n += v[c];
+        hist[k] = n;
     }
     __syncthreads();
     for (int k = t; k < K; k += kFinishThreads) {
         counts[(size_t)h * K + k] = hist[k];
         const int pi = slot_order ? mf::kperm(k) : k;
         float s = 0.0f;
-        for (int c = 0; c < C; ++c) s += part[((size_t)h * C + c) * pstride + pi];
+        for (int c0 = 0; c0 < C; c0 += 16) {
+            float v[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) v[c] = c0 + c < C ? part[((size_t)h * C + c0 + c) * pstride + pi] : 0.0f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                if (c0 + c < C) s += v[c];
+        }
         usage[(size_t)h * K + k] = s;
     }
     if (t < 64) {
@@ -146,8 +178,8 @@ __global__ void __launch_bounds__(kFinishThreads)
 }
 
 struct StatsLayout {
-    size_t lam, cst, gamma, W, C, G, hard, part, total;
-    int Np, Kp, KS, chunks, per_chunk;
+    size_t lam, cst, gamma, W, C, G, hard, part, cpart, total;
+    int Np, Kp, KS, chunks, per_chunk, hchunks, hper;
 };
 
 StatsLayout stats_layout(const gma_desc& d) {
@@ -187,6 +219,11 @@ StatsLayout stats_layout(const gma_desc& d) {
     }
     L.hard = off;
     off += align_up((size_t)BH * d.N * sizeof(int));
+    const int rows = d.B * d.N;
+    L.hchunks = rows > 0 ? (rows < kHistChunks ? rows : kHistChunks) : 0;
+    L.hper = L.hchunks ? (rows + L.hchunks - 1) / L.hchunks : 0;
+    L.cpart = off;
+    off += align_up((size_t)d.H * kHistChunks * d.K * sizeof(int));
     L.total = off;
     return L;
 }
@@ -202,6 +239,7 @@ hipError_t stats_forward(const Args& a) {
     const StatsLayout L = stats_layout(d);
     int* hard = a.hard ? a.hard : reinterpret_cast<int*>(a.ws + L.hard);
     float* part = reinterpret_cast<float*>(a.ws + L.part);
+    int* cpart = reinterpret_cast<int*>(a.ws + L.cpart);
     const bool mfma = stats_on_mfma(d);
     hipError_t e;
     if (d.N > 0) {
@@ -231,11 +269,15 @@ hipError_t stats_forward(const Args& a) {
             rec_end(a);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        rec_begin(a, "gma_stats_hist");
+        gma_stats_hist<<<dim3(d.H, L.hchunks), dim3(1024), 0, a.stream>>>(hard, cpart, d.H, d.B, d.N, d.K, L.hper);
+        rec_end(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     rec_begin(a, "gma_stats_finish");
     gma_stats_finish<<<dim3(d.H), dim3(kFinishThreads), 0, a.stream>>>(
-        hard, part, a.counts, a.usage, a.used, a.entropy, d.H, d.B, d.N, d.K, L.chunks, mfma ? L.Kp : d.K,
-        mfma ? 1 : 0);
+        cpart, part, a.counts, a.usage, a.used, a.entropy, d.H, d.B, d.N, d.K, L.hchunks, L.chunks,
+        mfma ? L.Kp : d.K, mfma ? 1 : 0);
     rec_end(a);
     return hipGetLastError();
 }
