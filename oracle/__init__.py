@@ -14,5 +14,6 @@ from .oracle import (  # noqa: F401
     memory,
     decode_step,
     resp_stats,
+    backward,
     num_threads,
 )

@@ -27,6 +27,8 @@
  *     0..t-1 is the state [S | z] (K x (d_v+1)); one step adds gamma_K,t (x) [v_t | 1] and
  *     reads O_t = gamma_Q,t S / (gamma_Q,t . z + eps), which is row t of the causal forward.
  *     The memory of a prefix is the write phase over its positions.
+ *   Backward: the gradients of a loss with respect to every input (the pages train the
+ *     mixture end to end by backpropagation), the chain rule of the above written out.
  *   Responsibility statistics (the pages' interpretability analysis of learned
  *     responsibilities: components used, usage entropy, hard assignments): per head, over
  *     the rows of the batch, hard assignments (argmax), their histogram, the soft usage
@@ -422,5 +424,218 @@ int gma_oracle_resp_stats(const double* x, const double* mu, const double* var_r
             status = st;
         }
     }
+    return status;
+}
+
+/*
+ * Backward of the forward mixer (bidirectional or causal): the gradients of a scalar loss L
+ * with respect to every input, given dout = dL/dO [B,H,N,d_v].  The pages train the mixture
+ * parameters end to end by backpropagation (Core mechanism 3) and analyse the gradients'
+ * structure; the gradients here are the chain rule of the forward above, written out:
+ *   num_i = gamma_Q,i Vt_i, den_i = gamma_Q,i . Z_i + eps, O_i = num_i / den_i, where
+ *   (Vt_i, Z_i) are the totals (bidirectional) or the inclusive prefix sums up to i (causal)
+ *   g_num_i = dO_i / den_i,  g_den_i = -(dO_i . O_i) / den_i
+ *   dgamma_Q,i[k] = g_num_i . Vt_i[k,:] + g_den_i Z_i[k]
+ *   R_j[k,:] = sum_i gamma_Q,i[k] g_num_i,  r_j[k] = sum_i gamma_Q,i[k] g_den_i, over all i
+ *              (bidirectional) or over i >= j (causal: the positions that read j)
+ *   dv_j = sum_k gamma_K,j[k] R_j[k,:],  dgamma_K,j[k] = v_j . R_j[k,:] + r_j[k]
+ *   softmax:  dl_k = gamma_k (dgamma_k - sum_m gamma_m dgamma_m)
+ *   log joint l_k(x) = log pi_k - 1/2 sum_d (log 2 pi + log var_kd + (x_d - mu_kd)^2 / var_kd):
+ *     dx_d      = -sum_k dl_k (x_d - mu_kd) / var_kd
+ *     dmu_kd   += dl_k (x_d - mu_kd) / var_kd
+ *     dvar_kd  += dl_k (-1/2) (1 / var_kd - (x_d - mu_kd)^2 / var_kd^2)
+ *     dlogpi_k += dl_k
+ *   var = softplus(var_raw) + floor:  dvar_raw = dvar * sigmoid(var_raw)
+ *   log pi = p - logsumexp(p):        dp_j = dlogpi_j - pi_j sum_k dlogpi_k
+ * Parameter gradients sum over both sides, all rows and the batch (b ascending).
+ *   dqr, dkr [B,H,N,d_r]; dv [B,H,N,d_v]; dmu, dvar_raw [H,K,d_r]; dprior [H,K].
+ */
+int gma_oracle_backward(const double* qr, const double* kr, const double* v, const double* mu,
+                        const double* var_raw, const double* prior_logits, const double* dout, int B, int H,
+                        int N, int d_r, int d_v, int K, int causal, double eps, double var_floor, double* dqr,
+                        double* dkr, double* dv, double* dmu, double* dvar_raw, double* dprior) {
+    if (!qr || !kr || !v || !mu || !var_raw || !prior_logits || !dout || !dqr || !dkr || !dv || !dmu ||
+        !dvar_raw || !dprior)
+        return ORACLE_BAD_ARG;
+    if (B < 1 || H < 1 || N < 0 || d_r < 1 || d_v < 1 || K < 1 || (causal != 0 && causal != 1))
+        return ORACLE_BAD_ARG;
+    const size_t BH = (size_t)B * H;
+    const size_t nkd = (size_t)K * d_r;
+    /* per-(b,h) contributions to the parameter gradients, summed over b afterwards */
+    double* cmu = (double*)calloc(BH * nkd, sizeof(double));
+    double* cvar = (double*)calloc(BH * nkd, sizeof(double));
+    double* cpi = (double*)calloc(BH * (size_t)K, sizeof(double));
+    if (!cmu || !cvar || !cpi) {
+        free(cmu);
+        free(cvar);
+        free(cpi);
+        return ORACLE_NO_MEM;
+    }
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < (int)BH; ++bh) {
+        const int h = bh % H;
+        const size_t nN = (size_t)(N > 0 ? N : 1);
+        double* gq = (double*)malloc(sizeof(double) * nN * K);
+        double* gk = (double*)malloc(sizeof(double) * nN * K);
+        double* dgq = (double*)calloc(nN * K, sizeof(double));
+        double* dgk = (double*)calloc(nN * K, sizeof(double));
+        double* gnum = (double*)malloc(sizeof(double) * nN * d_v);
+        double* gden = (double*)malloc(sizeof(double) * nN);
+        double* S = (double*)calloc((size_t)K * d_v, sizeof(double));
+        double* z = (double*)calloc((size_t)K, sizeof(double));
+        double* var = (double*)malloc(sizeof(double) * nkd);
+        double* o = (double*)malloc(sizeof(double) * d_v);
+        int st = (gq && gk && dgq && dgk && gnum && gden && S && z && var && o) ? ORACLE_OK : ORACLE_NO_MEM;
+        const double* mu_h = mu + (size_t)h * nkd;
+        const double* vr_h = var_raw + (size_t)h * nkd;
+        const double* p_h = prior_logits + (size_t)h * K;
+        const double* q_bh = qr + (size_t)bh * N * d_r;
+        const double* k_bh = kr + (size_t)bh * N * d_r;
+        const double* v_bh = v + (size_t)bh * N * d_v;
+        const double* do_bh = dout + (size_t)bh * N * d_v;
+        double* dq_bh = dqr + (size_t)bh * N * d_r;
+        double* dk_bh = dkr + (size_t)bh * N * d_r;
+        double* dv_bh = dv + (size_t)bh * N * d_v;
+        if (st == ORACLE_OK && N > 0)
+            st = gma_oracle_responsibilities(q_bh, N, d_r, mu_h, vr_h, p_h, K, var_floor, gq);
+        if (st == ORACLE_OK && N > 0)
+            st = gma_oracle_responsibilities(k_bh, N, d_r, mu_h, vr_h, p_h, K, var_floor, gk);
+        if (st == ORACLE_OK) {
+            for (size_t i = 0; i < nkd; ++i) var[i] = softplus(vr_h[i]) + var_floor;
+            /* bidirectional: the totals of the memory first */
+            if (!causal)
+                for (int j = 0; j < N; ++j)
+                    for (int k = 0; k < K; ++k) {
+                        const double g = gk[(size_t)j * K + k];
+                        z[k] += g;
+                        for (int c = 0; c < d_v; ++c) S[(size_t)k * d_v + c] += g * v_bh[(size_t)j * d_v + c];
+                    }
+            /* rows in order: (causal) add row i to the prefix, then the read and its gradient */
+            for (int i = 0; i < N; ++i) {
+                if (causal)
+                    for (int k = 0; k < K; ++k) {
+                        const double g = gk[(size_t)i * K + k];
+                        z[k] += g;
+                        for (int c = 0; c < d_v; ++c) S[(size_t)k * d_v + c] += g * v_bh[(size_t)i * d_v + c];
+                    }
+                const double* gqi = gq + (size_t)i * K;
+                double den = eps;
+                for (int k = 0; k < K; ++k) den += gqi[k] * z[k];
+                double dot = 0.0;
+                for (int c = 0; c < d_v; ++c) {
+                    double num = 0.0;
+                    for (int k = 0; k < K; ++k) num += gqi[k] * S[(size_t)k * d_v + c];
+                    o[c] = num / den;
+                    dot += do_bh[(size_t)i * d_v + c] * o[c];
+                }
+                gden[i] = -dot / den;
+                for (int c = 0; c < d_v; ++c) gnum[(size_t)i * d_v + c] = do_bh[(size_t)i * d_v + c] / den;
+                for (int k = 0; k < K; ++k) {
+                    double a = gden[i] * z[k];
+                    for (int c = 0; c < d_v; ++c) a += gnum[(size_t)i * d_v + c] * S[(size_t)k * d_v + c];
+                    dgq[(size_t)i * K + k] = a;
+                }
+            }
+            /* R, r: sums of gamma_Q (x) [g_num | g_den] over the rows that read row j */
+            for (size_t t = 0; t < (size_t)K * d_v; ++t) S[t] = 0.0; /* S reused as R */
+            for (int k = 0; k < K; ++k) z[k] = 0.0;                 /* z reused as r */
+            if (!causal)
+                for (int i = 0; i < N; ++i)
+                    for (int k = 0; k < K; ++k) {
+                        const double g = gq[(size_t)i * K + k];
+                        z[k] += g * gden[i];
+                        for (int c = 0; c < d_v; ++c) S[(size_t)k * d_v + c] += g * gnum[(size_t)i * d_v + c];
+                    }
+            for (int j = N - 1; j >= 0; --j) {
+                if (causal)
+                    for (int k = 0; k < K; ++k) {
+                        const double g = gq[(size_t)j * K + k];
+                        z[k] += g * gden[j];
+                        for (int c = 0; c < d_v; ++c) S[(size_t)k * d_v + c] += g * gnum[(size_t)j * d_v + c];
+                    }
+                const double* gkj = gk + (size_t)j * K;
+                for (int c = 0; c < d_v; ++c) {
+                    double a = 0.0;
+                    for (int k = 0; k < K; ++k) a += gkj[k] * S[(size_t)k * d_v + c];
+                    dv_bh[(size_t)j * d_v + c] = a;
+                }
+                for (int k = 0; k < K; ++k) {
+                    double a = z[k];
+                    for (int c = 0; c < d_v; ++c) a += v_bh[(size_t)j * d_v + c] * S[(size_t)k * d_v + c];
+                    dgk[(size_t)j * K + k] = a;
+                }
+            }
+            /* softmax backward, then the log joint's, for both sides */
+            for (int side = 0; side < 2; ++side) {
+                const double* g = side == 0 ? gq : gk;
+                double* dg = side == 0 ? dgq : dgk;
+                const double* x = side == 0 ? q_bh : k_bh;
+                double* dx = side == 0 ? dq_bh : dk_bh;
+                for (int i = 0; i < N; ++i) {
+                    double s = 0.0;
+                    for (int k = 0; k < K; ++k) s += g[(size_t)i * K + k] * dg[(size_t)i * K + k];
+                    for (int k = 0; k < K; ++k) dg[(size_t)i * K + k] = g[(size_t)i * K + k] * (dg[(size_t)i * K + k] - s);
+                    const double* xi = x + (size_t)i * d_r;
+                    for (int d = 0; d < d_r; ++d) dx[(size_t)i * d_r + d] = 0.0;
+                    for (int k = 0; k < K; ++k) {
+                        const double dl = dg[(size_t)i * K + k];
+                        cpi[(size_t)bh * K + k] += dl;
+                        for (int d = 0; d < d_r; ++d) {
+                            const size_t kd = (size_t)k * d_r + d;
+                            const double diff = xi[d] - mu_h[kd];
+                            dx[(size_t)i * d_r + d] -= dl * diff / var[kd];
+                            cmu[(size_t)bh * nkd + kd] += dl * diff / var[kd];
+                            cvar[(size_t)bh * nkd + kd] += dl * -0.5 * (1.0 / var[kd] - diff * diff / (var[kd] * var[kd]));
+                        }
+                    }
+                }
+            }
+        }
+        free(gq);
+        free(gk);
+        free(dgq);
+        free(dgk);
+        free(gnum);
+        free(gden);
+        free(S);
+        free(z);
+        free(var);
+        free(o);
+        if (st != ORACLE_OK) {
+#pragma omp critical
+            status = st;
+        }
+    }
+    if (status == ORACLE_OK) {
+        for (int h = 0; h < H; ++h) {
+            const double* p_h = prior_logits + (size_t)h * K;
+            double m = p_h[0];
+            for (int k = 1; k < K; ++k) m = fmax(m, p_h[k]);
+            double se = 0.0;
+            for (int k = 0; k < K; ++k) se += exp(p_h[k] - m);
+            double tot = 0.0;
+            for (int k = 0; k < K; ++k) {
+                double a = 0.0;
+                for (int b = 0; b < B; ++b) a += cpi[((size_t)b * H + h) * K + k];
+                dprior[(size_t)h * K + k] = a;
+                tot += a;
+            }
+            for (int k = 0; k < K; ++k) dprior[(size_t)h * K + k] -= exp(p_h[k] - m) / se * tot;
+            for (size_t kd = 0; kd < nkd; ++kd) {
+                double am = 0.0, av = 0.0;
+                for (int b = 0; b < B; ++b) {
+                    am += cmu[((size_t)b * H + h) * nkd + kd];
+                    av += cvar[((size_t)b * H + h) * nkd + kd];
+                }
+                const double r = var_raw[(size_t)h * nkd + kd];
+                dmu[(size_t)h * nkd + kd] = am;
+                dvar_raw[(size_t)h * nkd + kd] = av / (1.0 + exp(-r));
+            }
+        }
+    }
+    free(cmu);
+    free(cvar);
+    free(cpi);
     return status;
 }

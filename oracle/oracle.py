@@ -64,6 +64,9 @@ def _load():
         lp = ctypes.POINTER(ctypes.c_longlong)
         lib.gma_oracle_resp_stats.argtypes = [dp, dp, dp, dp, i, i, i, i, i, d, ip, lp, dp, ip, dp]
         lib.gma_oracle_resp_stats.restype = ctypes.c_int
+        lib.gma_oracle_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, i, d, d,
+                                            dp, dp, dp, dp, dp, dp]
+        lib.gma_oracle_backward.restype = ctypes.c_int
         lib.gma_oracle_num_threads.argtypes = []
         lib.gma_oracle_num_threads.restype = i
         _lib = lib
@@ -225,3 +228,22 @@ def resp_stats(x, mu, var_raw, prior_logits, var_floor: float) -> dict:
     if st != 0:
         raise RuntimeError(f"oracle resp_stats failed: {st}")
     return {"hard": hard, "counts": counts, "usage": usage, "used": used, "entropy": entropy}
+
+
+def backward(qr, kr, v, mu, var_raw, prior_logits, dout, causal: bool, eps: float, var_floor: float) -> dict:
+    """Gradients of L = sum(dout * O) for the forward mixer: ``dqr``, ``dkr`` [B,H,N,d_r],
+    ``dv`` [B,H,N,d_v], ``dmu``, ``dvar_raw`` [H,K,d_r], ``dprior`` [H,K] (float64)."""
+    lib = _load()
+    qr, kr, v, mu, vr, p, do = (_f64(a) for a in (qr, kr, v, mu, var_raw, prior_logits, dout))
+    B, H, N, d_r = qr.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    out = {"dqr": np.zeros_like(qr), "dkr": np.zeros_like(kr), "dv": np.zeros_like(v), "dmu": np.zeros_like(mu),
+           "dvar_raw": np.zeros_like(vr), "dprior": np.zeros_like(p)}
+    st = lib.gma_oracle_backward(_ptr(qr), _ptr(kr), _ptr(v), _ptr(mu), _ptr(vr), _ptr(p), _ptr(do), B, H, N, d_r,
+                                 d_v, K, 1 if causal else 0, float(eps), float(var_floor), _ptr(out["dqr"]),
+                                 _ptr(out["dkr"]), _ptr(out["dv"]), _ptr(out["dmu"]), _ptr(out["dvar_raw"]),
+                                 _ptr(out["dprior"]))
+    if st != 0:
+        raise RuntimeError(f"oracle backward failed: {st}")
+    return out

@@ -498,6 +498,107 @@ def test_resp_stats_closed_forms():
     assert r["counts"].sum() == 0 and r["used"][0] == 0 and r["entropy"][0] == 0.0
 
 
+# ---------------------------------------------------------------- backward
+# The pages train the mixture end to end by backpropagation.  The oracle's hand-written chain
+# rule is pinned by central differences of the oracle forward, by autograd through an fp64
+# torch formulation of the forward written here from the definitions, and by invariants.
+
+def _loss(qr, kr, v, mu, vr, p, dout, causal, eps):
+    return float((oracle.forward(qr, kr, v, mu, vr, p, causal, eps, 1e-3) * dout).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_central_differences(causal):
+    rng = np.random.default_rng(101 + causal)
+    B, H, N, dr, dv, K = 2, 2, 5, 3, 2, 4
+    qr, kr, v, mu, vr, p = _random_problem(rng, B, H, N, dr, dv, K)
+    dout = rng.normal(size=(B, H, N, dv))
+    eps = 0.05
+    g = oracle.backward(qr, kr, v, mu, vr, p, dout, causal, eps, 1e-3)
+    args = {"qr": qr, "kr": kr, "v": v, "mu": mu, "vr": vr, "p": p}
+    names = {"qr": "dqr", "kr": "dkr", "v": "dv", "mu": "dmu", "vr": "dvar_raw", "p": "dprior"}
+    step = 1e-5
+    for a, arr in args.items():
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + step
+            lp = _loss(args["qr"], args["kr"], args["v"], args["mu"], args["vr"], args["p"], dout, causal, eps)
+            arr[idx] = old - step
+            lm = _loss(args["qr"], args["kr"], args["v"], args["mu"], args["vr"], args["p"], dout, causal, eps)
+            arr[idx] = old
+            fd[idx] = (lp - lm) / (2 * step)
+        np.testing.assert_allclose(g[names[a]], fd, rtol=1e-6, atol=1e-8, err_msg=a)
+
+
+def _torch_forward(qr, kr, v, mu, vr, p, causal, eps, floor):
+    import torch
+    var = torch.nn.functional.softplus(vr) + floor                      # [H,K,d]
+    logpi = p - torch.logsumexp(p, dim=-1, keepdim=True)                 # [H,K]
+
+    def post(x):                                                         # x [B,H,N,d]
+        diff = x[:, :, :, None, :] - mu[None, :, None, :, :]             # [B,H,N,K,d]
+        logn = -0.5 * (np.log(2 * np.pi) + torch.log(var)[None, :, None] + diff ** 2 / var[None, :, None]).sum(-1)
+        return torch.softmax(logpi[None, :, None, :] + logn, dim=-1)     # [B,H,N,K]
+
+    gq, gk = post(qr), post(kr)
+    aff = gq @ gk.transpose(-1, -2)                                      # [B,H,N,N]
+    if causal:
+        aff = torch.tril(aff)
+    num = aff @ v
+    den = aff.sum(-1, keepdim=True) + eps
+    return num / den
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,dr,dv,K", [(2, 3, 17, 5, 4, 6), (1, 2, 33, 8, 3, 16), (1, 1, 1, 2, 2, 1)])
+def test_backward_matches_autograd(B, H, N, dr, dv, K, causal):
+    import torch
+    rng = np.random.default_rng(111 + N + K + causal)
+    qr, kr, v, mu, vr, p = _random_problem(rng, B, H, N, dr, dv, K)
+    dout = rng.normal(size=(B, H, N, dv))
+    eps = 1e-3
+    ts = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (qr, kr, v, mu, vr, p)]
+    out = _torch_forward(*ts, causal, eps, 1e-3)
+    (out * torch.tensor(dout)).sum().backward()
+    g = oracle.backward(qr, kr, v, mu, vr, p, dout, causal, eps, 1e-3)
+    for t, name in zip(ts, ("dqr", "dkr", "dv", "dmu", "dvar_raw", "dprior")):
+        ref = t.grad.numpy()
+        np.testing.assert_allclose(g[name], ref, rtol=1e-9, atol=1e-11 * max(1.0, np.abs(ref).max()), err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    rng = np.random.default_rng(121 + causal)
+    B, H, N, dr, dv, K = 2, 2, 40, 4, 3, 7
+    qr, kr, v, mu, vr, p = _random_problem(rng, B, H, N, dr, dv, K)
+    dout = rng.normal(size=(B, H, N, dv))
+    eps = 1e-3
+    g = oracle.backward(qr, kr, v, mu, vr, p, dout, causal, eps, 1e-3)
+    L = _loss(qr, kr, v, mu, vr, p, dout, causal, eps)
+    # prior logits: the forward is invariant to a common shift, so the gradient sums to zero
+    np.testing.assert_allclose(g["dprior"].sum(-1), 0.0, atol=1e-12)
+    # the output is linear in V: sum dV * V = L
+    np.testing.assert_allclose((g["dv"] * v).sum(), L, rtol=1e-12)
+    # shifting every routing row and every mean of a head by one vector changes nothing
+    tot = g["dqr"].sum(axis=(0, 2)) + g["dkr"].sum(axis=(0, 2)) + g["dmu"].sum(axis=1)
+    np.testing.assert_allclose(tot, 0.0, atol=1e-10)
+    if causal:
+        # rows at or after t receive gradient only from outputs at or after them: with dO = 0
+        # from t on, dv and dk vanish there, and dq too
+        t = 25
+        d2 = dout.copy()
+        d2[:, :, t:] = 0.0
+        g2 = oracle.backward(qr, kr, v, mu, vr, p, d2, causal, eps, 1e-3)
+        assert not g2["dv"][:, :, t:].any() and not g2["dkr"][:, :, t:].any() and not g2["dqr"][:, :, t:].any()
+        # and the gradients before t equal those of the prefix problem alone
+        gp = oracle.backward(qr[:, :, :t], kr[:, :, :t], v[:, :, :t], mu, vr, p, dout[:, :, :t], causal, eps, 1e-3)
+        for name in ("dqr", "dkr", "dv"):
+            np.testing.assert_allclose(g2[name][:, :, :t], gp[name], rtol=1e-12, atol=1e-14)
+        for name in ("dmu", "dvar_raw", "dprior"):
+            np.testing.assert_allclose(g2[name], gp[name], rtol=1e-10, atol=1e-13)
+
+
 def test_golden_fixture_regression():
     import json
     import os
