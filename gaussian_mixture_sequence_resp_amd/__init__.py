@@ -6,6 +6,7 @@ The compute runs in ``libgma.so`` (hand-written HIP kernels behind the C ABI of
 """
 from .binding import (  # noqa: F401
     GMAError,
+    backward,
     decode_step,
     forward,
     forward_cross,

@@ -75,6 +75,11 @@ def load_library(path: Optional[str] = None):
     lib.gma_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.POINTER(GmaDesc), vp,
                                     sz, vp]
     lib.gma_decode_step.restype = ctypes.c_int
+    lib.gma_backward_workspace_size.argtypes = [ctypes.POINTER(GmaDesc), ctypes.c_int]
+    lib.gma_backward_workspace_size.restype = sz
+    lib.gma_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp,
+                                 ctypes.POINTER(GmaDesc), vp, sz, vp]
+    lib.gma_backward.restype = ctypes.c_int
     lib.gma_stats_workspace_size.argtypes = [ctypes.POINTER(GmaDesc)]
     lib.gma_stats_workspace_size.restype = sz
     lib.gma_resp_stats.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(GmaDesc), vp, sz, vp]
@@ -307,3 +312,32 @@ def resp_stats(x, mu, var_raw, prior_logits, var_floor: float = 1e-3, with_hard:
     if st != GMA_OK:
         raise GMAError(st, strerror(st))
     return res
+
+
+def backward(qr, kr, v, mu, var_raw, prior_logits, dout, causal: bool, eps: float = 1e-6, var_floor: float = 1e-3,
+             workspace=None, algo: str = "auto", stream=None) -> dict:
+    """Gradients of L = sum(dout * O) for gma_forward: ``dqr``, ``dkr``, ``dv`` (input dtype,
+    shapes of qr, kr, v) and ``dmu``, ``dvar_raw`` [H,K,d_r], ``dprior`` [H,K] (float32)."""
+    import torch
+    lib = load_library()
+    _dense(qr, kr, v, mu, var_raw, prior_logits, dout)
+    B, H, N, d_r = qr.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    desc = make_desc(B, H, N, d_r, d_v, K, _dtype_name(qr), var_floor, algo)
+    g = {"dqr": torch.empty_like(qr), "dkr": torch.empty_like(kr), "dv": torch.empty_like(v),
+         "dmu": torch.empty_like(mu), "dvar_raw": torch.empty_like(var_raw), "dprior": torch.empty_like(prior_logits)}
+    need = int(lib.gma_backward_workspace_size(ctypes.byref(desc), 1 if causal else 0))
+    if workspace is None and need > 0:
+        workspace = _ws(need, qr)
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(qr.device).cuda_stream
+    ptr = (lambda t: t.data_ptr() if t.numel() else None)
+    st = lib.gma_backward(ptr(qr), ptr(kr), ptr(v), mu.data_ptr(), var_raw.data_ptr(), prior_logits.data_ptr(),
+                          ptr(dout), 1 if causal else 0, float(eps), ptr(g["dqr"]), ptr(g["dkr"]), ptr(g["dv"]),
+                          g["dmu"].data_ptr(), g["dvar_raw"].data_ptr(), g["dprior"].data_ptr(), ctypes.byref(desc),
+                          ws_ptr, ws_bytes, stream)
+    if st != GMA_OK:
+        raise GMAError(st, strerror(st))
+    return g

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgma.so")
-SOURCES = ["gma_api.cpp", "gma_simt.hip", "gma_mfma.hip", "gma_mfma_causal.hip", "gma_decode.hip", "gma_stats.hip"]
+SOURCES = ["gma_api.cpp", "gma_simt.hip", "gma_mfma.hip", "gma_mfma_causal.hip", "gma_decode.hip", "gma_stats.hip", "gma_backward.hip"]
 ARCH = "gfx950"
 
 

@@ -288,6 +288,79 @@ int gma_decode_step(const void* qr, const void* kr, const void* v, const float* 
     return gma::decode_forward(a) == hipSuccess ? GMA_OK : GMA_ERR_HIP;
 }
 
+// ---- backward
+
+static bool backward_algo_ok(const gma_desc& d) { return d.algo != GMA_ALGO_MFMA && gma::backward_supported(d); }
+
+size_t gma_backward_workspace_size(const gma_desc* desc, int causal) {
+    if (check_desc(desc) != GMA_OK || (causal != 0 && causal != 1)) return 0;
+    if ((int64_t)desc->B * desc->H == 0 || !backward_algo_ok(*desc)) return 0;
+    return gma::backward_workspace(*desc);
+}
+
+int gma_backward(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                 const float* prior_logits, const void* dout, int causal, float eps, void* dqr, void* dkr, void* dv,
+                 float* dmu, float* dvar_raw, float* dprior, const gma_desc* desc, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    int st = check_desc(desc);
+    if (st != GMA_OK) return st;
+    const gma_desc d = *desc;
+    if (causal != 0 && causal != 1) return GMA_ERR_BAD_SCALAR;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return GMA_ERR_BAD_SCALAR;
+    const size_t bh = (size_t)d.B * d.H;
+    if (bh == 0) return GMA_OK;
+    if (!mu || !var_raw || !prior_logits || !dmu || !dvar_raw || !dprior) return GMA_ERR_NULL_ARG;
+    if (d.N > 0 && (!qr || !kr || !v || !dout || !dqr || !dkr || !dv)) return GMA_ERR_NULL_ARG;
+    if (d.algo == GMA_ALGO_MFMA) return GMA_ERR_UNSUPPORTED;  // one kernel family so far
+    if (!gma::backward_supported(d)) return GMA_ERR_UNSUPPORTED;
+    const size_t esz = d.dtype == GMA_F32 ? 4 : 2;
+    const size_t nx = bh * d.N * d.d_r * esz, nv = bh * d.N * d.d_v * esz;
+    const size_t np = (size_t)d.H * d.K * d.d_r * 4, npr = (size_t)d.H * d.K * 4;
+    if (misaligned(qr, 16) || misaligned(kr, 16) || misaligned(v, 16) || misaligned(dout, 16) ||
+        misaligned(dqr, 16) || misaligned(dkr, 16) || misaligned(dv, 16))
+        return GMA_ERR_ALIGN;
+    if (misaligned(mu, 4) || misaligned(var_raw, 4) || misaligned(prior_logits, 4) || misaligned(dmu, 4) ||
+        misaligned(dvar_raw, 4) || misaligned(dprior, 4))
+        return GMA_ERR_ALIGN;
+    if (workspace && misaligned(workspace, gma::kWsAlign)) return GMA_ERR_ALIGN;
+    const size_t need = gma::backward_workspace(d);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GMA_ERR_WORKSPACE;
+    const void* ins[7] = {qr, kr, v, mu, var_raw, prior_logits, dout};
+    const size_t ins_n[7] = {nx, nx, nv, np, np, npr, nv};
+    const void* outs[7] = {dqr, dkr, dv, dmu, dvar_raw, dprior, workspace};
+    const size_t outs_n[7] = {nx, nx, nv, np, np, npr, need};
+    for (int i = 0; i < 7; ++i) {
+        for (int j = 0; j < 7; ++j)
+            if (overlaps(outs[i], outs_n[i], ins[j], ins_n[j])) return GMA_ERR_ALIAS;
+        for (int j = i + 1; j < 7; ++j)
+            if (overlaps(outs[i], outs_n[i], outs[j], outs_n[j])) return GMA_ERR_ALIAS;
+    }
+    Args a;
+    memset(&a, 0, sizeof(a));
+    a.qr = qr;
+    a.kr = kr;
+    a.v = v;
+    a.mu = mu;
+    a.var_raw = var_raw;
+    a.prior = prior_logits;
+    a.causal = causal;
+    a.eps = eps;
+    a.d = d;
+    a.Nk = d.N;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.ws_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    gma::BwdArgs g;
+    g.dout = dout;
+    g.dqr = dqr;
+    g.dkr = dkr;
+    g.dv = dv;
+    g.dmu = dmu;
+    g.dvar_raw = dvar_raw;
+    g.dprior = dprior;
+    return gma::backward_run(a, g) == hipSuccess ? GMA_OK : GMA_ERR_HIP;
+}
+
 // ---- responsibility statistics
 
 static bool stats_algo_ok(const gma_desc& d) { return d.algo != GMA_ALGO_MFMA || gma::stats_on_mfma(d); }

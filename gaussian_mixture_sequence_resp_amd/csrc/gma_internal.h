@@ -69,6 +69,8 @@ hipError_t simt_forward(const Args& a);
 // Responsibilities only, written as float32 Gamma_Q [B,H,N,K] then Gamma_K [B,H,Nk,K]; used for
 // gamma_out by every family.
 hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst, int* hard = nullptr);
+// The same responsibilities in double (the backward of float32 inputs).
+hipError_t simt_gamma(const Args& a, double* gamma, const double* lam, const double* cst);
 // Parameter prep of the SIMT family: lam = 1/var [H,K,d_r], cst [H,K] (log prior minus half
 // the log-determinant), both double.
 hipError_t simt_params(const Args& a, double* lam, double* cst);
@@ -82,6 +84,21 @@ size_t memory_workspace(const gma_desc& d);
 hipError_t memory_forward(const Args& a);
 size_t decode_workspace(const gma_desc& d);
 hipError_t decode_forward(const Args& a);
+
+// Backward (gma_backward.hip): dout and the gradients; the inputs are those of the forward
+// in Args (qr, kr, v, mu, var_raw, prior, causal, eps).
+struct BwdArgs {
+    const void* dout;  // [B,H,N,d_v], input dtype
+    void* dqr;         // [B,H,N,d_r], input dtype
+    void* dkr;
+    void* dv;          // [B,H,N,d_v], input dtype
+    float* dmu;        // [H,K,d_r]
+    float* dvar_raw;   // [H,K,d_r]
+    float* dprior;     // [H,K]
+};
+size_t backward_workspace(const gma_desc& d);
+bool backward_supported(const gma_desc& d);
+hipError_t backward_run(const Args& a, const BwdArgs& g);
 
 // Responsibility statistics of the rows a.kr (gma_stats.hip).
 size_t stats_workspace(const gma_desc& d);

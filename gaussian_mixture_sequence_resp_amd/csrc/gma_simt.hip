@@ -72,13 +72,13 @@ __global__ void __launch_bounds__(kBlock) params_kernel(const float* __restrict_
 
 // One thread per routing row (side, b, h, n) of either side: Gamma_Q rows [b,h,n] (Nq per head)
 // then Gamma_K rows (Nk per head), each = softmax_k l_k(x).
-template <typename T>
+template <typename T, typename G>
 __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
                                                       const T* __restrict__ kr,
                                                       const float* __restrict__ mu,
                                                       const double* __restrict__ lam,
                                                       const double* __restrict__ cst,
-                                                      float* __restrict__ gamma, int* __restrict__ hard,
+                                                      G* __restrict__ gamma, int* __restrict__ hard,
                                                       int BH, int H, int Nq, int Nk, int dr, int K, int nblk) {
     const int side = blockIdx.y;
     const int N = side == 0 ? Nq : Nk;
@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
     if (n >= N) return;
     const int h = bh % H;
     const T* x = (side == 0 ? qr : kr) + ((size_t)bh * N + n) * dr;
-    float* g = gamma + ((size_t)side * BH * Nq + (size_t)bh * N + n) * K;
+    G* g = gamma + ((size_t)side * BH * Nq + (size_t)bh * N + n) * K;
     const float* mu_h = mu + (size_t)h * K * dr;
     const double* lam_h = lam + (size_t)h * K * dr;
     // pass 1: row max of the logits (double) and its component (the first one reaching it:
@@ -114,15 +114,19 @@ __global__ void __launch_bounds__(kBlock) resp_kernel(const T* __restrict__ qr,
             const double diff = (double)Elem<T>::load(x, d) - (double)mu_h[(size_t)k * dr + d];
             q = fma(lam_h[(size_t)k * dr + d] * diff, diff, q);
         }
-        g[k] = (float)(cst[(size_t)h * K + k] - 0.5 * q - m);
+        g[k] = (G)(cst[(size_t)h * K + k] - 0.5 * q - m);
     }
-    float s = 0.0f;
+    G s = 0;
     for (int k = 0; k < K; ++k) {
-        const float e = expf(g[k]);
+        G e;
+        if constexpr (sizeof(G) == 4)
+            e = expf(g[k]);
+        else
+            e = exp(g[k]);
         g[k] = e;
         s += e;
     }
-    const float inv = 1.0f / s;
+    const G inv = (G)1 / s;
     for (int k = 0; k < K; ++k) g[k] *= inv;
 }
 
@@ -283,7 +287,8 @@ hipError_t simt_params(const Args& a, double* lam, double* cst) {
     return hipGetLastError();
 }
 
-hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst, int* hard) {
+template <typename G>
+static hipError_t simt_gamma_t(const Args& a, G* gamma, const double* lam, const double* cst, int* hard) {
     const gma_desc& d = a.d;
     const int BH = d.B * d.H;
     const int nmax = d.N > a.Nk ? d.N : a.Nk;
@@ -291,15 +296,23 @@ hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const doub
     dim3 grid(BH * nblk, 2);
     rec_begin(a, "simt_responsibilities");
     if (d.dtype == GMA_F32)
-        resp_kernel<float><<<grid, dim3(kBlock), 0, a.stream>>>(
+        resp_kernel<float, G><<<grid, dim3(kBlock), 0, a.stream>>>(
             static_cast<const float*>(a.qr), static_cast<const float*>(a.kr), a.mu, lam, cst, gamma, hard, BH,
             d.H, d.N, a.Nk, d.d_r, d.K, nblk);
     else
-        resp_kernel<bf16_t><<<grid, dim3(kBlock), 0, a.stream>>>(
+        resp_kernel<bf16_t, G><<<grid, dim3(kBlock), 0, a.stream>>>(
             static_cast<const bf16_t*>(a.qr), static_cast<const bf16_t*>(a.kr), a.mu, lam, cst, gamma, hard, BH,
             d.H, d.N, a.Nk, d.d_r, d.K, nblk);
     rec_end(a);
     return hipGetLastError();
+}
+
+hipError_t simt_gamma(const Args& a, float* gamma, const double* lam, const double* cst, int* hard) {
+    return simt_gamma_t<float>(a, gamma, lam, cst, hard);
+}
+
+hipError_t simt_gamma(const Args& a, double* gamma, const double* lam, const double* cst) {
+    return simt_gamma_t<double>(a, gamma, lam, cst, nullptr);
 }
 
 hipError_t simt_forward(const Args& a) {

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GMA_VERSION 10300 /* 1.3.0: responsibility statistics */
+#define GMA_VERSION 10400 /* 1.4.0: backward */
 
 /* Limits of this build. */
 #define GMA_MAX_K 256
@@ -199,6 +199,27 @@ int gma_decode_step(const void* qr, const void* kr, const void* v, const float* 
                     const float* var_raw, const float* prior_logits, float* state, float eps,
                     void* out, const gma_desc* desc, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * Backward of gma_forward: the pages train the mixture parameters end to end by
+ * backpropagation ("Core mechanism" item 3).  Given dout = dL/dO [B,H,N,d_v] (desc->dtype),
+ * writes dL/dqr, dL/dkr [B,H,N,d_r] and dL/dv [B,H,N,d_v] (desc->dtype) and, summed over the
+ * batch and both sides, dL/dmu, dL/dvar_raw [H,K,d_r] and dL/dprior_logits [H,K] (float32;
+ * all outputs are overwritten, not accumulated).  Same inputs, causal flag, eps and layout
+ * as gma_forward; the forward is recomputed inside.  The gradients are the chain rule of the
+ * forward: see the kernels' source for the formulas.  SIMT kernels (algo AUTO or SIMT; an
+ * explicit MFMA request returns GMA_ERR_UNSUPPORTED); the per-head scans accumulate in
+ * double for float32 inputs and in float for bf16, the parameter and input-row gradients
+ * in double; deterministic.  Every shape within the limits is supported.
+ * Alignment, aliasing and status codes as gma_forward (no output may overlap an input, the
+ * workspace or another output).  N = 0 gives zero parameter gradients.
+ */
+size_t gma_backward_workspace_size(const gma_desc* desc, int causal);
+
+int gma_backward(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                 const float* prior_logits, const void* dout, int causal, float eps, void* dqr,
+                 void* dkr, void* dv, float* dmu, float* dvar_raw, float* dprior,
+                 const gma_desc* desc, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Responsibility statistics of one set of routing rows: the quantities of the pages'

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
                      "gma_version", "gma_workspace_size_cross", "gma_forward_cross",
                      "gma_forward_cross_timed", "gma_memory_workspace_size", "gma_memory",
                      "gma_decode_workspace_size", "gma_decode_step", "gma_stats_workspace_size",
-                     "gma_resp_stats"}
+                     "gma_resp_stats", "gma_backward_workspace_size", "gma_backward"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -260,3 +260,40 @@ def test_stats_validation(lib):
     assert sz(ctypes.byref(binding.make_desc(2, 3, 64, 16, 1, 12, "f32", 1e-3))) > 0
     assert sz(ctypes.byref(binding.make_desc(0, 3, 64, 16, 1, 12, "bf16", 1e-3))) == 0
     assert sz(ctypes.byref(binding.make_desc(2, 3, 64, 12, 1, 12, "bf16", 1e-3, "mfma"))) == 0
+
+
+def test_backward_validation(lib):
+    # every call below fails validation (or is an empty no-op) before any HIP call
+    vp = ctypes.c_void_p
+    lib.gma_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp,
+                                 ctypes.POINTER(binding.GmaDesc), vp, ctypes.c_size_t, vp]
+    step = 1 << 24
+    P = [Call.BASE + i * step for i in range(16)]
+    names = ("qr", "kr", "v", "mu", "vr", "pr", "do", "dq", "dk", "dv", "dmu", "dvr", "dpr", "ws")
+
+    def call(desc, causal=0, eps=1e-6, **kw):
+        p = dict(zip(names, P))
+        p["nb"] = 1 << 40
+        p.update(kw)
+        return lib.gma_backward(p["qr"], p["kr"], p["v"], p["mu"], p["vr"], p["pr"], p["do"], causal, eps, p["dq"],
+                                p["dk"], p["dv"], p["dmu"], p["dvr"], p["dpr"], ctypes.byref(desc), p["ws"], p["nb"],
+                                None)
+
+    d = binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "auto")
+    assert call(binding.make_desc(0, 3, 64, 16, 8, 12, "bf16", 1e-3), qr=None, dmu=None) == C["GMA_OK"]
+    assert call(d, causal=2) == C["GMA_ERR_BAD_SCALAR"]
+    assert call(d, eps=-1.0) == C["GMA_ERR_BAD_SCALAR"]
+    assert call(d, dmu=None) == C["GMA_ERR_NULL_ARG"]
+    assert call(d, do=None) == C["GMA_ERR_NULL_ARG"]
+    assert call(d, dq=P[7] + 8) == C["GMA_ERR_ALIGN"]
+    assert call(d, dpr=P[12] + 2) == C["GMA_ERR_ALIGN"]
+    assert call(binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "mfma")) == C["GMA_ERR_UNSUPPORTED"]
+    assert call(d, nb=8) == C["GMA_ERR_WORKSPACE"]
+    assert call(d, dq=P[0]) == C["GMA_ERR_ALIAS"]
+    assert call(d, dk=P[7]) == C["GMA_ERR_ALIAS"]
+    assert call(d, dv=P[6]) == C["GMA_ERR_ALIAS"]
+    assert call(d, ws=P[3]) == C["GMA_ERR_ALIAS"]
+    sz = binding.load_library().gma_backward_workspace_size
+    assert sz(ctypes.byref(d), 0) > 0 and sz(ctypes.byref(d), 1) > 0
+    assert sz(ctypes.byref(d), 2) == 0
+    assert sz(ctypes.byref(binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "mfma")), 0) == 0
