@@ -16,8 +16,9 @@ default workload is the bidirectional bf16 K=128 workload (B=8, H=8, N=4096,
 d_r=d_v=64); the causal LM-shaped workload (B=16, H=8, N=2048, K=256) is measured the
 same way and reported under "causal", the cross variant (1024 queries reading a
 memory of 16384 keys per head, K=128) under "cross", the single-token causal decode
-step at the causal workload's shape under "decode", and the responsibility statistics of
-that workload's key rows under "stats".
+step at the causal workload's shape under "decode", the responsibility statistics of
+that workload's key rows under "stats", and the backward of the headline and causal
+workloads under "backward".
 """
 from __future__ import annotations
 
@@ -291,6 +292,45 @@ def run_stats(w, steps, warmup):
     return {"ms_per_call": ms, "bytes": th * (s * w.d_r + 4), "flops": th * 2 * w.K * (2 * w.d_r + 1)}
 
 
+def run_backward(w, steps, warmup):
+    """Backward (gma_backward: gradients of qr, kr, v, mu, var_raw, prior logits) of workload
+    w with a seeded dO, one call per step; ms per call and the call's algorithmic bytes
+    (read q, k, v, dO; write dq, dk, dv) and flops (twice the forward's: the recomputed
+    forward, then the same contractions transposed)."""
+    import torch
+    import gaussian_mixture_sequence_resp_amd as gma
+    from gaussian_mixture_sequence_resp_amd.inputs import make_inputs
+
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    d = {k: v.to(dev) for k, v in inp.items()}
+    g = torch.Generator().manual_seed(w.seed + 7)
+    dout = torch.randn(w.B, w.H, w.N, w.d_v, generator=g).to(d["v"].dtype).to(dev)
+    desc = gma.make_desc(w.B, w.H, w.N, w.d_r, w.d_v, w.K, w.dtype, w.var_floor)
+    ws = torch.empty(max(int(gma.load_library().gma_backward_workspace_size(ctypes.byref(desc), int(w.causal))), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        return gma.backward(d["qr"], d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"], dout, w.causal,
+                            eps=w.eps, var_floor=w.var_floor, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    s = 4 if w.dtype == "f32" else 2
+    th = w.B * w.H * w.N
+    nbytes = th * s * 2 * (2 * w.d_r + 2 * w.d_v)
+    _, fwd_flops = algorithmic(w, "step")
+    return {"ms_per_call": ms, "bytes": nbytes, "flops": 2 * fwd_flops}
+
+
 def cpu_baseline(w, inp, budget_s=12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload (whole batch
     elements, all heads of each), timed on this host's cores.  The oracle spreads its
@@ -328,6 +368,7 @@ def main():
     ap.add_argument("--no-cross", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stats", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy one 256 MiB device buffer, so that a profiler's "
                          "memory counters can be scaled by a copy of known size")
@@ -408,6 +449,18 @@ def main():
                                       "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                                       "note": "whole call (prep, responsibilities, usage, finish) against the "
                                               "log-density flops of one side"}}
+    if not args.no_backward and args.workload == 2:
+        bl = {}
+        for wb in (w, WORKLOADS[3]):
+            rb = run_backward(wb, 2, 1)
+            sec = rb["ms_per_call"] * 1e-3
+            tf = rb["flops"] / sec / 1e12
+            bl[wb.name] = {"ms_per_call": round(rb["ms_per_call"], 4),
+                           "value": round(wb.B * wb.H * wb.N / sec, 1), "unit": "token-heads/s",
+                           "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 6),
+                                        "note": "whole call against twice the forward's algorithmic flops"}}
+        line["backward"] = bl
     if args.copy_calibration:
         import torch
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")

@@ -17,7 +17,9 @@
 //
 // Kernels (caller's stream, in this order):
 //   params_kernel, resp_kernel   (the SIMT forward's) 1/var and constants; gamma_Q, gamma_K
-//                                (in double for float32 inputs)
+//                                (in double for float32 inputs); for bf16 inputs the
+//                                matrix-core responsibilities kernel (gma_prep, then
+//                                gma_causal_resp writing float rows) gives gamma instead
 //   bwd_scan       one workgroup per (b, h), the state K x (d_v + 1) in LDS (in the workspace
 //                  when it does not fit; double for float32 inputs): pass 1 over the
 //                  rows in order (forming the prefix, or the totals first) gives g_num, g_den
@@ -31,6 +33,7 @@
 #include <math.h>
 
 #include "gma_internal.h"
+#include "gma_mfma_geo.h"
 #include "gma_numeric.h"
 
 namespace gma {
@@ -295,8 +298,14 @@ size_t scan_scratch(const gma_desc& d) { return (3 * (size_t)d.K + (d.d_v + 1) +
 size_t scan_state(const gma_desc& d) { return (size_t)d.K * (d.d_v + 1) * acc_size(d); }
 bool state_in_lds(const gma_desc& d) { return scan_state(d) + scan_scratch(d) <= kScanLdsMax; }
 
+// bf16 inputs whose routing rows the matrix-core responsibilities kernel covers take gamma
+// from it (fp32 logits, float rows); float32 inputs and other shapes from the SIMT kernel.
+bool resp_on_mfma(const gma_desc& d) {
+    return d.dtype == GMA_BF16 && d.algo != GMA_ALGO_SIMT && mf::stats_supported(d);
+}
+
 struct BwdLayout {
-    size_t lam, gamma, dl, gnum, gden, state, pmu, pvar, ppi, total;
+    size_t lam, W, C, gamma, dl, gnum, gden, state, pmu, pvar, ppi, total;
     int chunks, per_chunk;
 };
 
@@ -307,6 +316,13 @@ BwdLayout bwd_layout(const gma_desc& d) {
     size_t off = 0;
     L.lam = off;
     off += simt_param_bytes(d);
+    if (resp_on_mfma(d)) {
+        const mf::Geo g = mf::geometry(d);
+        L.W = off;
+        off += align_up((size_t)d.H * g.Kp * 4 * g.Dp * sizeof(bf16_t));
+        L.C = off;
+        off += align_up((size_t)d.H * g.Kp * sizeof(float));
+    }
     L.gamma = off;
     off += align_up(2 * BH * d.N * d.K * as);
     L.dl = off;
@@ -349,7 +365,17 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
     hipError_t e;
     if ((e = simt_params(a, lam, cst)) != hipSuccess) return e;
     if (d.N > 0) {
-        if ((e = simt_gamma(a, gamma, lam, cst)) != hipSuccess) return e;
+        if constexpr (sizeof(A) == sizeof(float)) {
+            if (resp_on_mfma(d)) {
+                if ((e = mf::resp_rows(a, reinterpret_cast<bf16_t*>(a.ws + L.W), reinterpret_cast<float*>(a.ws + L.C),
+                                       gamma)) != hipSuccess)
+                    return e;
+            } else if ((e = simt_gamma(a, gamma, lam, cst)) != hipSuccess) {
+                return e;
+            }
+        } else if ((e = simt_gamma(a, gamma, lam, cst)) != hipSuccess) {
+            return e;
+        }
         const size_t lds = scan_scratch(d) + (st_global ? 0 : scan_state(d));
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_scan<T, A>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)

@@ -149,16 +149,19 @@ __device__ __forceinline__ void stage_coefficient_chunks(unsigned char* sW, floa
 // blockIdx.y: 0 queries, 1 keys): logits (MFMA), softmax over the components, normalised
 // responsibilities stored as bf16 operand fragments; positions in [N, Np) get zeros.  When
 // the coefficient block of a head exceeds LDS it is staged in NPH phases of the routing
-// dims, the logits accumulating across phases.  STATS: also the hard assignment of every
-// position of side 0, argmax of its fp32 logits (lowest component among equal maxima),
-// into hard [BH][N].
+// dims, the logits accumulating across phases.  MODE kRespStats: also the hard assignment
+// of every position of side 0, argmax of its fp32 logits (lowest component among equal
+// maxima), into hard [BH][N].  MODE kRespRows: instead of fragments, the normalised
+// responsibilities as float32 rows [BH][N][K] (components < K) into GQ / GK reinterpreted
+// as float (the backward's layout).
 constexpr int kRespWaves = 8;
+constexpr int kRespFrag = 0, kRespStats = 1, kRespRows = 2;
 
-template <int MT, int NC, int NPH, bool STATS>
+template <int MT, int NC, int NPH, int MODE>
 __global__ void __launch_bounds__(64 * kRespWaves, 2)
     gma_causal_resp(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ W,
                     const float* __restrict__ cvec, bf16_t* __restrict__ GQ, bf16_t* __restrict__ GK,
-                    int* __restrict__ hard, int BH, int H, int N, int Np, int dr, int parts, int part_len) {
+                    int* __restrict__ hard, int BH, int H, int N, int Np, int dr, int parts, int part_len, int K) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int Kp = 32 * MT, Dp = 16 * NC, NCP = NC / NPH, KS = Kp / 16;
     constexpr int wstride = 8 * (16 * NCP) + 16;
@@ -202,7 +205,7 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
             }
         }
         load_xrow<NC>(xr, row(b0 + kStep), dr);  // next step's rows, in flight during the softmax
-        if constexpr (STATS) {
+        if constexpr (MODE == kRespStats) {
             // register e of tile m holds component 32 m + 8 (e / 4) + 4 half + e % 4 of token
             // col: increasing in (m, e), so a strict > keeps the lowest of equal maxima
             const int half = l >> 5;
@@ -225,7 +228,20 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
         }
         const float s = tile_exp<MT>(acc);
         const float inv = valid ? 1.0f / s : 0.0f;
-        if (t0 < n_end) {
+        if constexpr (MODE == kRespRows) {
+            // register e of tile m: component 32 m + 8 (e / 4) + 4 half + e % 4 of row t0 + col
+            float* gr = reinterpret_cast<float*>(side == 0 ? GQ : GK) + ((size_t)bh * N + t0 + col) * K;
+            const int half = l >> 5;
+            if (valid) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int kc = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
+                        if (kc < K) gr[kc] = acc[m][e] * inv;
+                    }
+            }
+        } else if (t0 < n_end) {
             // registers 8 sh .. 8 sh + 7 of tile m are slots 8 half + 0..7 of block 2m + sh
             bf16_t* gt = G + (size_t)(t0 / kTileT) * KS * kFrag;
 #pragma unroll
@@ -594,40 +610,42 @@ __global__ void __launch_bounds__(kThreads, 1)
 
 // ----------------------------------------------------------------------------- dispatch
 typedef void (*RespFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, bf16_t*, int*, int, int, int,
-                       int, int, int, int);
+                       int, int, int, int, int);
 typedef void (*TotFn)(const bf16_t*, const bf16_t*, float*, int, int, int, int, int, int, int);
 typedef void (*ScanFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, bf16_t*, float, int, int, int, int,
                        int, int, int, int);
 
-template <int MT, int NC, bool STATS>
+template <int MT, int NC, int MODE>
 RespFn resp_fn(int nph) {
-    if (nph == 1) return gma_causal_resp<MT, NC, 1, STATS>;
-    if (nph == 2 && NC % 2 == 0) return gma_causal_resp<MT, NC, (NC % 2 == 0 ? 2 : 1), STATS>;
-    if (nph == 4 && NC % 4 == 0) return gma_causal_resp<MT, NC, (NC % 4 == 0 ? 4 : 1), STATS>;
+    if (nph == 1) return gma_causal_resp<MT, NC, 1, MODE>;
+    if (nph == 2 && NC % 2 == 0) return gma_causal_resp<MT, NC, (NC % 2 == 0 ? 2 : 1), MODE>;
+    if (nph == 4 && NC % 4 == 0) return gma_causal_resp<MT, NC, (NC % 4 == 0 ? 4 : 1), MODE>;
     return nullptr;
 }
-template <int MT, bool STATS>
+template <int MT, int MODE>
 RespFn resp_fn_nc(int NC, int nph) {
     switch (NC) {
-        case 1: return resp_fn<MT, 1, STATS>(nph);
-        case 2: return resp_fn<MT, 2, STATS>(nph);
-        case 4: return resp_fn<MT, 4, STATS>(nph);
-        case 8: return resp_fn<MT, 8, STATS>(nph);
+        case 1: return resp_fn<MT, 1, MODE>(nph);
+        case 2: return resp_fn<MT, 2, MODE>(nph);
+        case 4: return resp_fn<MT, 4, MODE>(nph);
+        case 8: return resp_fn<MT, 8, MODE>(nph);
     }
     return nullptr;
 }
-template <bool STATS>
+template <int MODE>
 RespFn select_resp_t(const Geo& g, int nph) {
     switch (g.MT) {
-        case 1: return resp_fn_nc<1, STATS>(g.NC, nph);
-        case 2: return resp_fn_nc<2, STATS>(g.NC, nph);
-        case 4: return resp_fn_nc<4, STATS>(g.NC, nph);
-        case 8: return resp_fn_nc<8, STATS>(g.NC, nph);
+        case 1: return resp_fn_nc<1, MODE>(g.NC, nph);
+        case 2: return resp_fn_nc<2, MODE>(g.NC, nph);
+        case 4: return resp_fn_nc<4, MODE>(g.NC, nph);
+        case 8: return resp_fn_nc<8, MODE>(g.NC, nph);
     }
     return nullptr;
 }
-RespFn select_resp(const Geo& g, int nph, bool stats = false) {
-    return stats ? select_resp_t<true>(g, nph) : select_resp_t<false>(g, nph);
+RespFn select_resp(const Geo& g, int nph, int mode = kRespFrag) {
+    if (mode == kRespStats) return select_resp_t<kRespStats>(g, nph);
+    if (mode == kRespRows) return select_resp_t<kRespRows>(g, nph);
+    return select_resp_t<kRespFrag>(g, nph);
 }
 // LDS of the responsibilities kernel with the routing dims staged in nph phases.
 size_t resp_lds(const Geo& g, int nph) {
@@ -680,7 +698,7 @@ hipError_t launch_resp(const Args& a, const Geo& g, RespFn rf, int nph, int Np, 
     const bf16_t* qr = sides == 2 ? static_cast<const bf16_t*>(a.qr) : kr;
     rec_begin(a, "gma_causal_resp");
     hipLaunchKernelGGL(rf, dim3(BH * parts, sides), dim3(64 * kRespWaves), rl, a.stream, qr, kr, W, cvec,
-                       sides == 2 ? GQ : GK, GK, hard, BH, d.H, d.N, Np, d.d_r, parts, part_len);
+                       sides == 2 ? GQ : GK, GK, hard, BH, d.H, d.N, Np, d.d_r, parts, part_len, d.K);
     rec_end(a);
     return hipGetLastError();
 }
@@ -840,12 +858,28 @@ hipError_t stats_resp(const Args& a, bf16_t* W, float* cvec, bf16_t* G, int* har
     const gma_desc& d = a.d;
     const Geo g = geometry(d);
     const int nph = resp_phases(g);
-    RespFn rf = nph ? select_resp(g, nph, true) : nullptr;
+    RespFn rf = nph ? select_resp(g, nph, kRespStats) : nullptr;
     if (!rf) return hipErrorNotSupported;
     hipError_t e;
     if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
     const int Np = (d.N + kGroup - 1) / kGroup * kGroup;
     return launch_resp(a, g, rf, nph, Np, 1, W, cvec, nullptr, G, hard);
+}
+
+// Responsibilities of both sides as float32 rows [2][B H][N][K] (queries, then keys) for
+// the backward of bf16 inputs: logits on the matrix cores (coefficients into W, cvec).
+hipError_t resp_rows(const Args& a, bf16_t* W, float* cvec, float* gamma) {
+    const gma_desc& d = a.d;
+    const Geo g = geometry(d);
+    const int nph = resp_phases(g);
+    RespFn rf = nph ? select_resp(g, nph, kRespRows) : nullptr;
+    if (!rf) return hipErrorNotSupported;
+    hipError_t e;
+    if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
+    const int Np = (d.N + kGroup - 1) / kGroup * kGroup;
+    bf16_t* gq = reinterpret_cast<bf16_t*>(gamma);
+    bf16_t* gk = reinterpret_cast<bf16_t*>(gamma + (size_t)d.B * d.H * d.N * d.K);
+    return launch_resp(a, g, rf, nph, Np, 2, W, cvec, gq, gk);
 }
 
 }  // namespace mf

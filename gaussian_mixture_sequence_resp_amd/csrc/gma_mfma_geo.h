@@ -117,6 +117,8 @@ hipError_t causal_memory(const Args& a);
 // Responsibility statistics: Gamma (fragment order) and hard assignments of the rows a.kr.
 bool stats_supported(const gma_desc& d);
 hipError_t stats_resp(const Args& a, bf16_t* W, float* cvec, bf16_t* G, int* hard);
+// Responsibilities of both sides as float32 rows [2][B H][N][K] (the backward's layout).
+hipError_t resp_rows(const Args& a, bf16_t* W, float* cvec, float* gamma);
 
 }  // namespace mf
 }  // namespace gma
