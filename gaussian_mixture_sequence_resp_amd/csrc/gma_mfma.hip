@@ -38,6 +38,10 @@ inline int vtstride(const Geo& g) { return 2 * g.Kp + 16; }
 size_t write_lds_bytes(const Geo& g) {
     return (size_t)g.Kp * g.wstride + (size_t)g.Kp * 4 + (size_t)kIterT * gstride(g) + (size_t)kIterT * vstride(g);
 }
+// The read kernel keeps the memory operand of its output MFMAs (MT * 2 * (NT + 1) fragments of
+// 4 registers) in registers when that leaves it within 256 registers (no spills).
+__host__ __device__ constexpr bool read_regmem(int MT, int NT) { return MT * (NT + 1) <= 12; }
+
 size_t read_lds_bytes(const Geo& g) {
     return (size_t)g.Kp * g.wstride + (size_t)g.Kp * 4 + (size_t)(g.Dvp + 32) * vtstride(g);
 }
@@ -358,6 +362,22 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
     }
     __syncthreads();
 
+    // The memory operand of the output MFMAs (Vt^T, Z hi/lo, ones) stays in registers for the
+    // whole kernel where it fits (read_regmem); larger memories are read from LDS per tile.
+    constexpr bool kRegMem = read_regmem(MT, NT);
+    bf16x8 aV[kRegMem ? MT : 1][2][NT + 1];
+    auto mem_frag = [&](int m, int sh, int n) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(sT + (size_t)(32 * n + (l & 31)) * ts + 2 * (32 * m + 16 * sh + 8 * half));
+    };
+    if constexpr (kRegMem) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+                for (int n = 0; n <= NT; ++n) aV[m][sh][n] = mem_frag(m, sh, n);
+    }
+
     for (int base = n_begin + kTileT * w; base < n_end; base += kStep) {
         const int t = base + (l & 31);
         const bool valid = t < n_end;
@@ -380,11 +400,12 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) bp[j] = pack_bf16(acc[m][8 * sh + 2 * j], acc[m][8 * sh + 2 * j + 1]);
                 const bf16x8 b = __builtin_bit_cast(bf16x8, bp);
-                const int kcol = 32 * m + 16 * sh + 8 * half;
 #pragma unroll
                 for (int n = 0; n <= NT; ++n) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sT + (size_t)(32 * n + (l & 31)) * ts + 2 * kcol);
-                    o[n] = mfma(a, b, o[n]);
+                    if constexpr (kRegMem)
+                        o[n] = mfma(aV[m][sh][n], b, o[n]);
+                    else
+                        o[n] = mfma(mem_frag(m, sh, n), b, o[n]);
                 }
             }
         // o[NT]: rows 0-7 Gamma_Q Z_hi, 8-15 Gamma_Q Z_lo, 16-31 row sum s
