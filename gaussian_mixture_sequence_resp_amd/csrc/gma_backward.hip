@@ -20,11 +20,14 @@
 //                                (in double for float32 inputs); for bf16 inputs the
 //                                matrix-core responsibilities kernel (gma_prep, then
 //                                gma_causal_resp writing float rows) gives gamma instead
-//   bwd_scan       one workgroup per (b, h), the state K x (d_v + 1) in LDS (in the workspace
-//                  when it does not fit; double for float32 inputs): pass 1 over the
-//                  rows in order (forming the prefix, or the totals first) gives g_num, g_den
-//                  and dl_Q; pass 2 over the rows in reverse (the suffix, or the totals) gives
-//                  dv and dl_K
+//   per pass (pass 1 gives g_num, g_den and dl_Q; pass 2 gives dv and dl_K), the rows of each
+//   head cut into SEG contiguous segments:
+//   bwd_seg_partial  the segment's weighted rows summed in order (K x (d_v + 1) per segment)
+//   bwd_seg_start    each segment's starting state from those partials in segment order: the
+//                  prefix before it (causal pass 1), the suffix after it (causal pass 2) or
+//                  the head's total (bidirectional)
+//   bwd_seg_rows     one workgroup per (b, h, segment) walks its rows (pass 2 in reverse) with the
+//                  state in LDS (in the workspace when it does not fit)
 //   bwd_x          dqr, dkr: one thread per (side, row, dim), double accumulation over k
 //   bwd_param_part per chunk of rows (both sides, all b), one thread per (h, k, d): partial
 //                  dmu, dvar and dlog pi in double
@@ -42,149 +45,227 @@ namespace {
 constexpr int kBwdThreads = 256;
 constexpr int kParamChunks = 64;
 
-// Per-head scan, in A: double for float32 inputs (gamma included: the chain rule cancels,
-// e.g. R v_j + r against gamma . dgamma, and a sharp posterior's dl = gamma (dgamma - s) is
-// far smaller than float's rounding of gamma times dgamma; the 1e-5 gate needs double);
-// float for bf16.  st [K][W] (W = d_v + 1: the state, then reused for [R | r]) lives in LDS when it
-// fits (st_global == null) and otherwise in the workspace at st_global + bh K W; row scratch
-// in LDS: sgq [K], sgk [K], sdg [K], srow [W] (v_j or [g_num | g_den]), sred [2].
-template <typename T, typename A>
+// Sums over rows are split into SEG contiguous segments of L rows per head.  The state of a
+// pass is [K][W] (W = d_v + 1), kept in A: double for float32 inputs (gamma included: the
+// chain rule cancels, e.g. R v_j + r against gamma . dgamma, and a sharp posterior's
+// dl = gamma (dgamma - s) is far smaller than float's rounding of gamma times dgamma; the
+// 1e-5 gate needs double); float for bf16.
+//   pass 1: rows u_j = [v_j | 1] weighted by gamma_K,j  (the forward's memory / prefix);
+//   pass 2: rows u_i = [g_num_i | g_den_i] weighted by gamma_Q,i  ([R | r]; suffix for causal).
+
+// Row j of a pass's weighted rows: weight gamma_j[k], row entry c (c < d_v: v or g_num; c = d_v:
+// 1 or g_den).
+template <typename T, typename A, int PASS>
+__device__ __forceinline__ A pass_row(const T* v_bh, const A* gnum_bh, const A* gden_bh, int dv, int j, int c) {
+    if constexpr (PASS == 1)
+        return c < dv ? (A)Elem<T>::load(v_bh, (size_t)j * dv + c) : (A)1;
+    else
+        return c < dv ? gnum_bh[(size_t)j * dv + c] : gden_bh[j];
+}
+
+// Partial state of every segment: part[bh][seg][k][c] = sum over the segment's rows j, in
+// order, of gamma[side][bh][j][k] * u_j[c].  Grid (ceil(K W / 256), BH * SEG).
+template <typename T, typename A, int PASS>
 __global__ void __launch_bounds__(kBwdThreads)
-    bwd_scan(const A* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
-             A* __restrict__ gnum, A* __restrict__ gden, A* __restrict__ dl, T* __restrict__ dv_out,
-             A* st_global, int BH, int N, int K, int dv, float eps, int causal) {
+    bwd_seg_partial(const A* __restrict__ gamma, const T* __restrict__ v, const A* __restrict__ gnum,
+                    const A* __restrict__ gden, A* __restrict__ part, int BH, int N, int K, int dv, int SEG, int L) {
+    const int W = dv + 1;
+    const int e = blockIdx.x * kBwdThreads + threadIdx.x;
+    const int bs = blockIdx.y, bh = bs / SEG, seg = bs % SEG;
+    if (e >= K * W) return;
+    const int k = e / W, c = e % W;
+    const int side = PASS == 1 ? 1 : 0;  // pass 1 weights by gamma_K, pass 2 by gamma_Q
+    const A* g = gamma + ((size_t)side * BH + bh) * N * K;
+    const T* v_bh = v + (size_t)bh * N * dv;
+    const A* gnum_bh = gnum + (size_t)bh * N * dv;
+    const A* gden_bh = gden + (size_t)bh * N;
+    const int j0 = seg * L, j1 = min(N, j0 + L);
+    A acc = 0;
+    int j = j0;
+    for (; j + 4 <= j1; j += 4) {  // the loads of 4 rows in flight together, summed in row order
+        A gg[4], uu[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            gg[q] = g[(size_t)(j + q) * K + k];
+            uu[q] = pass_row<T, A, PASS>(v_bh, gnum_bh, gden_bh, dv, j + q, c);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc += gg[q] * uu[q];
+    }
+    for (; j < j1; ++j) acc += g[(size_t)j * K + k] * pass_row<T, A, PASS>(v_bh, gnum_bh, gden_bh, dv, j, c);
+    part[(size_t)bs * K * W + e] = acc;
+}
+
+// Starting state of every segment from the partials, summed in segment order: causal pass 1
+// the exclusive prefix (segments before), causal pass 2 the exclusive suffix (segments after);
+// bidirectional the total of all segments (slot 0 only).  Grid (ceil(K W / 256), BH).
+template <typename A, int PASS>
+__global__ void __launch_bounds__(kBwdThreads)
+    bwd_seg_start(const A* __restrict__ part, A* __restrict__ start, int K, int dv, int SEG, int causal) {
+    const int W = dv + 1;
+    const int e = blockIdx.x * kBwdThreads + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (e >= K * W) return;
+    const size_t base = (size_t)bh * SEG * K * W + e;
+    A acc = 0;
+    if (!causal) {
+        for (int s = 0; s < SEG; ++s) acc += part[base + (size_t)s * K * W];
+        start[base] = acc;
+    } else if (PASS == 1) {
+        for (int s = 0; s < SEG; ++s) {
+            start[base + (size_t)s * K * W] = acc;
+            acc += part[base + (size_t)s * K * W];
+        }
+    } else {
+        for (int s = SEG - 1; s >= 0; --s) {
+            start[base + (size_t)s * K * W] = acc;
+            acc += part[base + (size_t)s * K * W];
+        }
+    }
+}
+
+// Wave-wide sum (64 lanes).
+template <typename A>
+__device__ __forceinline__ A wave_sum(A x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+constexpr int kRowThreads = 256;
+constexpr int kRowWaves = kRowThreads / 64;
+
+// sum_{k in [k0, k1)} g[k] st[k W + c], four independent partial sums (added in a fixed order).
+template <typename A>
+__device__ __forceinline__ A dot_k(const A* g, const A* st, int W, int c, int k0, int k1) {
+    A p0 = 0, p1 = 0, p2 = 0, p3 = 0;
+    int k = k0;
+    for (; k + 4 <= k1; k += 4) {
+        p0 += g[k] * st[(size_t)k * W + c];
+        p1 += g[k + 1] * st[(size_t)(k + 1) * W + c];
+        p2 += g[k + 2] * st[(size_t)(k + 2) * W + c];
+        p3 += g[k + 3] * st[(size_t)(k + 3) * W + c];
+    }
+    for (; k < k1; ++k) p0 += g[k] * st[(size_t)k * W + c];
+    return (p0 + p1) + (p2 + p3);
+}
+
+// sum_c st[k W + c] u[c] over all W columns, four independent partial sums.
+template <typename A>
+__device__ __forceinline__ A dot_c(const A* st, const A* u, int W, int k) {
+    const A* r = st + (size_t)k * W;
+    A p0 = 0, p1 = 0, p2 = 0, p3 = 0;
+    int c = 0;
+    for (; c + 4 <= W; c += 4) {
+        p0 += r[c] * u[c];
+        p1 += r[c + 1] * u[c + 1];
+        p2 += r[c + 2] * u[c + 2];
+        p3 += r[c + 3] * u[c + 3];
+    }
+    for (; c < W; ++c) p0 += r[c] * u[c];
+    return (p0 + p1) + (p2 + p3);
+}
+
+// One workgroup (4 waves) per (bh, segment): the segment's rows in order (pass 1: ascending;
+// pass 2: descending), the state st [K][W] in LDS (or in the workspace at st_global when it
+// does not fit), starting from the segment's start state.  Causal: the row's own weighted row
+// is added first (the sums are inclusive).  Pass 1 row i: num | den = gamma_Q,i . st, g_num,
+// g_den, dgamma_Q = st g, dl_Q.  Pass 2 row j: dv_j = gamma_K,j . st (value part),
+// dgamma_K = st [v_j | 1], dl_K.  Contractions over k are split into one contiguous range of
+// components per wave, and the four wave partials are added in wave order.  LDS scratch after
+// the state: sga [K] (the row's gamma), sgb [K] (the other side's, then dgamma), su [W],
+// sw [W], spart [4][W], sred [4].
+template <typename T, typename A, int PASS>
+__global__ void __launch_bounds__(kRowThreads)
+    bwd_seg_rows(const A* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
+                 A* __restrict__ gnum, A* __restrict__ gden, A* __restrict__ dl, T* __restrict__ dv_out,
+                 const A* __restrict__ start, A* st_global, int BH, int N, int K, int dv, float eps, int causal,
+                 int SEG, int L) {
     extern __shared__ double smem_d[];
     A* smem = reinterpret_cast<A*>(smem_d);
     const int W = dv + 1;
-    const int bh = blockIdx.x, t = threadIdx.x;
-    A* st = st_global ? st_global + (size_t)bh * K * W : smem;
-    A* sgq = st_global ? smem : smem + (size_t)K * W;
-    A* sgk = sgq + K;
-    A* sdg = sgk + K;
-    A* srow = sdg + K;
-    A* sred = srow + W;
+    const int KW = K * W;
+    const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    A* st = st_global ? st_global + (size_t)bs * KW : smem;
+    A* sga = st_global ? smem : smem + (size_t)KW;
+    A* sgb = sga + K;
+    A* su = sgb + K;
+    A* sw = su + W;
+    A* spart = sw + W;
+    A* sred = spart + kRowWaves * W;
     const A* gq = gamma + (size_t)bh * N * K;
     const A* gk = gamma + ((size_t)BH + bh) * N * K;
     const T* v_bh = v + (size_t)bh * N * dv;
     const T* do_bh = dout + (size_t)bh * N * dv;
     A* gnum_bh = gnum + (size_t)bh * N * dv;
     A* gden_bh = gden + (size_t)bh * N;
-    A* dlq = dl + (size_t)bh * N * K;
-    A* dlk = dl + ((size_t)BH + bh) * N * K;
-    T* dv_bh = dv_out + (size_t)bh * N * dv;
-
-    for (int e = t; e < K * W; e += kBwdThreads) st[e] = 0.0f;
-    __syncthreads();
-    // st += g (x) [u | w] for row j (u = v_j or g_num_j; w = 1 or g_den_j), staged in srow
-    auto add_row = [&](const A* g) {
-        for (int e = t; e < K * W; e += kBwdThreads) st[e] += g[e / W] * srow[e % W];
-    };
-    auto stage_v = [&](int j) {
-        for (int c = t; c < W; c += kBwdThreads) srow[c] = c < dv ? (A)Elem<T>::load(v_bh, (size_t)j * dv + c) : (A)1;
-    };
-    auto stage_g = [&](int j) {
-        for (int c = t; c < W; c += kBwdThreads) srow[c] = c < dv ? gnum_bh[(size_t)j * dv + c] : gden_bh[j];
-    };
-
-    // ---- pass 1: rows in order
-    if (!causal)
-        for (int j = 0; j < N; ++j) {
-            __syncthreads();
-            stage_v(j);
-            __syncthreads();
-            add_row(gk + (size_t)j * K);
-        }
-    for (int i = 0; i < N; ++i) {
+    const A* st0 = start + ((size_t)bh * SEG + (causal ? seg : 0)) * KW;
+    for (int e = t; e < KW; e += kRowThreads) st[e] = st0[e];
+    // this wave's component range of the k-contractions
+    const int kq = (K + kRowWaves - 1) / kRowWaves;
+    const int k0 = min(K, wv * kq), k1 = min(K, k0 + kq);
+    const int i0 = seg * L, i1 = min(N, i0 + L);
+    for (int step = 0; step < i1 - i0; ++step) {
+        const int i = PASS == 1 ? i0 + step : i1 - 1 - step;
         __syncthreads();
-        if (causal) stage_v(i);
-        for (int k = t; k < K; k += kBwdThreads) sgq[k] = gq[(size_t)i * K + k];
-        __syncthreads();
+        // sga: this row's gamma on the reading side; sgb, su: the weighted row added to the state
+        const A* grow = (PASS == 1 ? gq : gk) + (size_t)i * K;
+        for (int k = t; k < K; k += kRowThreads) sga[k] = grow[k];
         if (causal) {
-            add_row(gk + (size_t)i * K);
+            const A* wrow = (PASS == 1 ? gk : gq) + (size_t)i * K;
+            for (int k = t; k < K; k += kRowThreads) sgb[k] = wrow[k];
+            for (int c = t; c < W; c += kRowThreads) su[c] = pass_row<T, A, PASS>(v_bh, gnum_bh, gden_bh, dv, i, c);
             __syncthreads();
-        }
-        // num (c < d_v) and den (c = d_v) of row i
-        for (int c = t; c < W; c += kBwdThreads) {
-            A a = 0;
-            for (int k = 0; k < K; ++k) a += sgq[k] * st[(size_t)k * W + c];
-            srow[c] = a;
+            for (int k = wv; k < K; k += kRowWaves) {
+                const A gkk = sgb[k];
+                for (int c = lane; c < W; c += 64) st[(size_t)k * W + c] += gkk * su[c];
+            }
         }
         __syncthreads();
-        if (t == 0) {
-            const A den = srow[dv] + (A)eps;
-            A dot = 0;
-            for (int c = 0; c < dv; ++c) dot += (A)Elem<T>::load(do_bh, (size_t)i * dv + c) * (srow[c] / den);
-            sred[0] = den;
-            sred[1] = -dot / den;
-            gden_bh[i] = sred[1];
-        }
+        // gamma . st over this wave's components, for the value columns (and den in pass 1)
+        const int ncol = PASS == 1 ? W : dv;
+        for (int c = lane; c < ncol; c += 64) spart[wv * W + c] = dot_k(sga, st, W, c, k0, k1);
         __syncthreads();
-        const A den = sred[0], gd = sred[1];
-        __syncthreads();
-        for (int c = t; c < W; c += kBwdThreads) {
-            const A g = c < dv ? (A)Elem<T>::load(do_bh, (size_t)i * dv + c) / den : gd;
-            srow[c] = g;
-            if (c < dv) gnum_bh[(size_t)i * dv + c] = g;
-        }
-        __syncthreads();
-        // dgamma_Q = S g_num + z g_den, then the softmax backward
-        for (int k = t; k < K; k += kBwdThreads) {
-            A a = 0;
-            for (int c = 0; c < W; ++c) a += st[(size_t)k * W + c] * srow[c];
-            sdg[k] = a;
-        }
-        __syncthreads();
-        if (t == 0) {
-            A s = 0;
-            for (int k = 0; k < K; ++k) s += sgq[k] * sdg[k];
-            sred[0] = s;
-        }
-        __syncthreads();
-        for (int k = t; k < K; k += kBwdThreads) dlq[(size_t)i * K + k] = sgq[k] * (sdg[k] - sred[0]);
-    }
-
-    // ---- pass 2: rows in reverse, st now [R | r]
-    __syncthreads();
-    for (int e = t; e < K * W; e += kBwdThreads) st[e] = 0.0f;
-    if (!causal)
-        for (int j = 0; j < N; ++j) {
+        if constexpr (PASS == 1) {
+            for (int c = t; c < W; c += kRowThreads) sw[c] = ((spart[c] + spart[W + c]) + spart[2 * W + c]) + spart[3 * W + c];
             __syncthreads();
-            stage_g(j);
+            const A den = sw[dv] + (A)eps;
+            if (wv == 0) {
+                A dot = 0;
+                for (int c = lane; c < dv; c += 64) dot += (A)Elem<T>::load(do_bh, (size_t)i * dv + c) * (sw[c] / den);
+                dot = wave_sum(dot);
+                if (lane == 0) sred[0] = -dot / den;
+            }
             __syncthreads();
-            add_row(gq + (size_t)j * K);
-        }
-    for (int j = N - 1; j >= 0; --j) {
-        __syncthreads();
-        if (causal) stage_g(j);
-        for (int k = t; k < K; k += kBwdThreads) sgk[k] = gk[(size_t)j * K + k];
-        __syncthreads();
-        if (causal) {
-            add_row(gq + (size_t)j * K);
-            __syncthreads();
-        }
-        // dv_j = gamma_K,j R ; stage v_j for dgamma_K
-        for (int c = t; c < dv; c += kBwdThreads) {
-            A a = 0;
-            for (int k = 0; k < K; ++k) a += sgk[k] * st[(size_t)k * W + c];
-            Elem<T>::store(dv_bh, (size_t)j * dv + c, (float)a);
+            const A gd = sred[0];
+            for (int c = t; c < W; c += kRowThreads) {
+                const A g = c < dv ? (A)Elem<T>::load(do_bh, (size_t)i * dv + c) / den : gd;
+                sw[c] = g;
+                if (c < dv) gnum_bh[(size_t)i * dv + c] = g;
+            }
+            if (t == 0) gden_bh[i] = gd;
+        } else {
+            T* dv_bh = dv_out + (size_t)bh * N * dv;
+            for (int c = t; c < dv; c += kRowThreads)
+                Elem<T>::store(dv_bh, (size_t)i * dv + c,
+                               (float)(((spart[c] + spart[W + c]) + spart[2 * W + c]) + spart[3 * W + c]));
+            for (int c = t; c < W; c += kRowThreads) sw[c] = c < dv ? (A)Elem<T>::load(v_bh, (size_t)i * dv + c) : (A)1;
         }
         __syncthreads();
-        stage_v(j);
-        __syncthreads();
-        // dgamma_K = R v_j + r  (srow[d_v] = 1 multiplies r)
-        for (int k = t; k < K; k += kBwdThreads) {
-            A a = 0;
-            for (int c = 0; c < W; ++c) a += st[(size_t)k * W + c] * srow[c];
-            sdg[k] = a;
+        // dgamma = st sw, then the softmax backward dl = gamma (dgamma - gamma . dgamma)
+        A part = 0;
+        for (int k = t; k < K; k += kRowThreads) {
+            const A a = dot_c(st, sw, W, k);
+            sgb[k] = a;  // sgb is free once the state update above is done
+            part += sga[k] * a;
         }
+        part = wave_sum(part);
+        if (lane == 0) sred[1 + wv] = part;  // sred[1..4]
         __syncthreads();
-        if (t == 0) {
-            A s = 0;
-            for (int k = 0; k < K; ++k) s += sgk[k] * sdg[k];
-            sred[0] = s;
-        }
-        __syncthreads();
-        for (int k = t; k < K; k += kBwdThreads) dlk[(size_t)j * K + k] = sgk[k] * (sdg[k] - sred[0]);
+        const A s = ((sred[1] + sred[2]) + sred[3]) + sred[4];
+        A* dl_row = dl + ((size_t)(PASS == 1 ? 0 : BH) + bh) * N * K + (size_t)i * K;
+        for (int k = t; k < K; k += kRowThreads) dl_row[k] = sga[k] * (sgb[k] - s);
     }
 }
 
@@ -207,9 +288,18 @@ __global__ void __launch_bounds__(kBwdThreads)
     const A* dlr = dl + ((size_t)side * BH * N + row) * K;
     const float* mu_h = mu + (size_t)h * K * dr;
     const double* lam_h = lam + (size_t)h * K * dr;
-    double a = 0.0;
-    for (int k = 0; k < K; ++k) a -= (double)dlr[k] * (xd - (double)mu_h[(size_t)k * dr + d]) * lam_h[(size_t)k * dr + d];
-    Elem<T>::store(side == 0 ? dqr : dkr, r, (float)a);
+    // four independent partial sums over k (added in a fixed order): the loads of four
+    // components are in flight together
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    int k = 0;
+    for (; k + 4 <= K; k += 4) {
+        a0 += (double)dlr[k] * (xd - (double)mu_h[(size_t)k * dr + d]) * lam_h[(size_t)k * dr + d];
+        a1 += (double)dlr[k + 1] * (xd - (double)mu_h[(size_t)(k + 1) * dr + d]) * lam_h[(size_t)(k + 1) * dr + d];
+        a2 += (double)dlr[k + 2] * (xd - (double)mu_h[(size_t)(k + 2) * dr + d]) * lam_h[(size_t)(k + 2) * dr + d];
+        a3 += (double)dlr[k + 3] * (xd - (double)mu_h[(size_t)(k + 3) * dr + d]) * lam_h[(size_t)(k + 3) * dr + d];
+    }
+    for (; k < K; ++k) a0 += (double)dlr[k] * (xd - (double)mu_h[(size_t)k * dr + d]) * lam_h[(size_t)k * dr + d];
+    Elem<T>::store(side == 0 ? dqr : dkr, r, (float)-((a0 + a1) + (a2 + a3)));
 }
 
 // Partial parameter gradients of chunk c of head h's 2 B N rows (side, b, i in that order):
@@ -229,15 +319,43 @@ __global__ void __launch_bounds__(kBwdThreads)
     const int u0 = c * per_chunk, u1 = min(total, u0 + per_chunk);
     const double m = mu[(size_t)h * K * dr + e], l = lam[(size_t)h * K * dr + e];
     double am = 0.0, av = 0.0, ap = 0.0;
-    for (int u = u0; u < u1; ++u) {
-        const int side = u / (B * N), rem = u % (B * N);
-        const int b = rem / N, i = rem % N;
-        const size_t row = (size_t)(b * H + h) * N + i;
-        const double g = dl[((size_t)side * BH * N + row) * K + k];
-        const double diff = (double)Elem<T>::load(side == 0 ? qr : kr, row * dr + d) - m;
-        am += g * diff * l;
-        av += g * -0.5 * (l - diff * diff * l * l);
-        ap += g;
+    if (u0 < u1) {
+        // walk the rows (side, b, i) incrementally; the loads of 4 rows are in flight together
+        int side = u0 / (B * N), rem = u0 % (B * N);
+        int b = rem / N, i = rem % N;
+        auto next = [&]() {
+            if (++i == N) {
+                i = 0;
+                if (++b == B) {
+                    b = 0;
+                    ++side;
+                }
+            }
+        };
+        int u = u0;
+        while (u < u1) {
+            const int n = min(4, u1 - u);
+            double g[4], x[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q < n) {
+                    const size_t row = (size_t)(b * H + h) * N + i;
+                    g[q] = dl[((size_t)side * BH * N + row) * K + k];
+                    x[q] = (double)Elem<T>::load(side == 0 ? qr : kr, row * dr + d);
+                    next();
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q < n) {
+                    const double diff = x[q] - m;
+                    am += g[q] * diff * l;
+                    av += g[q] * -0.5 * (l - diff * diff * l * l);
+                    ap += g[q];
+                }
+            }
+            u += n;
+        }
     }
     const size_t o = ((size_t)c * H + h) * K * dr + e;
     pmu[o] = am;
@@ -292,11 +410,25 @@ __global__ void __launch_bounds__(kBwdThreads)
 
 constexpr size_t kScanLdsMax = 150 * 1024;
 
-// Scratch of the scan besides its state, and whether the state fits in LDS with it.
+// Scratch of the rows kernel besides its state, and whether the state fits in LDS with it.
 size_t acc_size(const gma_desc& d) { return d.dtype == GMA_F32 ? sizeof(double) : sizeof(float); }
-size_t scan_scratch(const gma_desc& d) { return (3 * (size_t)d.K + (d.d_v + 1) + 2) * acc_size(d); }
+size_t scan_scratch(const gma_desc& d) { return (2 * (size_t)d.K + 6 * ((size_t)d.d_v + 1) + 5) * acc_size(d); }
 size_t scan_state(const gma_desc& d) { return (size_t)d.K * (d.d_v + 1) * acc_size(d); }
 bool state_in_lds(const gma_desc& d) { return scan_state(d) + scan_scratch(d) <= kScanLdsMax; }
+
+// Segments per head: about 2048 (head, segment) waves in all, at least 16 rows per segment,
+// and the two per-segment state arrays bounded to ~256 MB.
+void segments(const gma_desc& d, int& SEG, int& L) {
+    const long BH = (long)d.B * d.H;
+    long seg = BH > 0 ? (2048 + BH - 1) / BH : 1;
+    const long by_rows = (d.N + 15) / 16;
+    if (seg > by_rows) seg = by_rows;
+    const long per = BH * (long)scan_state(d) * 2;
+    while (seg > 1 && per * seg > (256l << 20)) seg >>= 1;
+    if (seg < 1) seg = 1;
+    L = d.N > 0 ? (int)((d.N + seg - 1) / seg) : 1;
+    SEG = d.N > 0 ? (d.N + L - 1) / L : 1;
+}
 
 // bf16 inputs whose routing rows the matrix-core responsibilities kernel covers take gamma
 // from it (fp32 logits, float rows); float32 inputs and other shapes from the SIMT kernel.
@@ -305,14 +437,15 @@ bool resp_on_mfma(const gma_desc& d) {
 }
 
 struct BwdLayout {
-    size_t lam, W, C, gamma, dl, gnum, gden, state, pmu, pvar, ppi, total;
-    int chunks, per_chunk;
+    size_t lam, W, C, gamma, dl, gnum, gden, part, start, state, pmu, pvar, ppi, total;
+    int chunks, per_chunk, seg, seg_len;
 };
 
 BwdLayout bwd_layout(const gma_desc& d) {
     BwdLayout L{};
     const size_t BH = (size_t)d.B * d.H;
     const size_t as = acc_size(d);
+    segments(d, L.seg, L.seg_len);
     size_t off = 0;
     L.lam = off;
     off += simt_param_bytes(d);
@@ -331,8 +464,13 @@ BwdLayout bwd_layout(const gma_desc& d) {
     off += align_up(BH * d.N * d.d_v * as);
     L.gden = off;
     off += align_up(BH * d.N * as);
+    const size_t segs = BH * L.seg * scan_state(d);
+    L.part = off;
+    off += align_up(segs);
+    L.start = off;
+    off += align_up(segs);
     L.state = off;
-    if (!state_in_lds(d)) off += align_up(BH * scan_state(d));
+    if (!state_in_lds(d)) off += align_up(segs);
     const int rows = 2 * d.B * d.N;
     L.chunks = rows > 0 ? (rows < kParamChunks ? rows : kParamChunks) : 0;
     L.per_chunk = L.chunks ? (rows + L.chunks - 1) / L.chunks : 0;
@@ -347,6 +485,39 @@ BwdLayout bwd_layout(const gma_desc& d) {
     return L;
 }
 
+// One pass over the rows: segment partials, their ordered starts, then the segment walks.
+template <typename T, typename A, int PASS>
+hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamma, A* dl, A* gnum, A* gden) {
+    const gma_desc& d = a.d;
+    const int BH = d.B * d.H;
+    const int KW = d.K * (d.d_v + 1);
+    A* part = reinterpret_cast<A*>(a.ws + L.part);
+    A* start = reinterpret_cast<A*>(a.ws + L.start);
+    A* st_global = state_in_lds(d) ? nullptr : reinterpret_cast<A*>(a.ws + L.state);
+    const unsigned gx = (unsigned)((KW + kBwdThreads - 1) / kBwdThreads);
+    rec_begin(a, PASS == 1 ? "bwd_partial_1" : "bwd_partial_2");
+    bwd_seg_partial<T, A, PASS><<<dim3(gx, (unsigned)(BH * L.seg)), dim3(kBwdThreads), 0, a.stream>>>(
+        gamma, static_cast<const T*>(a.v), gnum, gden, part, BH, d.N, d.K, d.d_v, L.seg, L.seg_len);
+    rec_end(a);
+    hipError_t e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    rec_begin(a, PASS == 1 ? "bwd_start_1" : "bwd_start_2");
+    bwd_seg_start<A, PASS><<<dim3(gx, (unsigned)BH), dim3(kBwdThreads), 0, a.stream>>>(part, start, d.K, d.d_v,
+                                                                                       L.seg, a.causal);
+    rec_end(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t lds = scan_scratch(d) + (st_global ? 0 : scan_state(d));
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_seg_rows<T, A, PASS>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    rec_begin(a, PASS == 1 ? "bwd_rows_1" : "bwd_rows_2");
+    bwd_seg_rows<T, A, PASS><<<dim3((unsigned)(BH * L.seg)), dim3(kRowThreads), lds, a.stream>>>(
+        gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
+        start, st_global, BH, d.N, d.K, d.d_v, a.eps, a.causal, L.seg, L.seg_len);
+    rec_end(a);
+    return hipGetLastError();
+}
+
 template <typename T, typename A>
 hipError_t backward_t(const Args& a, const BwdArgs& g) {
     const gma_desc& d = a.d;
@@ -358,7 +529,6 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
     A* dl = reinterpret_cast<A*>(a.ws + L.dl);
     A* gnum = reinterpret_cast<A*>(a.ws + L.gnum);
     A* gden = reinterpret_cast<A*>(a.ws + L.gden);
-    A* st_global = state_in_lds(d) ? nullptr : reinterpret_cast<A*>(a.ws + L.state);
     double* pmu = reinterpret_cast<double*>(a.ws + L.pmu);
     double* pvar = reinterpret_cast<double*>(a.ws + L.pvar);
     double* ppi = reinterpret_cast<double*>(a.ws + L.ppi);
@@ -376,16 +546,8 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
         } else if ((e = simt_gamma(a, gamma, lam, cst)) != hipSuccess) {
             return e;
         }
-        const size_t lds = scan_scratch(d) + (st_global ? 0 : scan_state(d));
-        if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_scan<T, A>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-            return e;
-        rec_begin(a, "bwd_scan");
-        bwd_scan<T, A><<<dim3(BH), dim3(kBwdThreads), lds, a.stream>>>(
-            gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
-            st_global, BH, d.N, d.K, d.d_v, a.eps, a.causal);
-        rec_end(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = bwd_pass<T, A, 1>(a, g, L, gamma, dl, gnum, gden)) != hipSuccess) return e;
+        if ((e = bwd_pass<T, A, 2>(a, g, L, gamma, dl, gnum, gden)) != hipSuccess) return e;
         const size_t nx = 2 * (size_t)BH * d.N * d.d_r;
         rec_begin(a, "bwd_x");
         bwd_x<T, A><<<dim3((unsigned)((nx + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads), 0, a.stream>>>(
