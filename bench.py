@@ -96,10 +96,16 @@ def elapsed_ms(hip, a, b) -> float:
     return float(t.value)
 
 
+# Sources the forward kernels (whose HBM traffic profiles/traffic.json records) are built
+# and dispatched from; the backward, decode, statistics and SIMT files do not enter them.
+FORWARD_SOURCES = ("gma_api.cpp", "gma_internal.h", "gma_mfma.hip", "gma_mfma_causal.hip", "gma_mfma_common.h",
+                   "gma_mfma_geo.h", "gma_numeric.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gaussian_mixture_sequence_resp_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in FORWARD_SOURCES:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
