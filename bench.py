@@ -187,6 +187,47 @@ def run_workload(w, steps, warmup, per_rep=True):
             "inputs": inp}
 
 
+def device_peaks():
+    """Practical peaks of this device under load, next to the datasheet ones: the bf16 MFMA
+    rate of a register-only loop of the instruction the GMA kernels use (libgma_probe.so), and
+    the HBM bandwidth of a plain 1 GiB device-to-device copy (read + write bytes)."""
+    import torch
+    dev = torch.device("cuda:0")
+    probe = ctypes.CDLL(os.path.join(ROOT, "gaussian_mixture_sequence_resp_amd", "libgma_probe.so"))
+    probe.gma_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.gma_probe_mfma.restype = ctypes.c_int
+    blocks, iters = 2048, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def mfma():
+        rc = probe.gma_probe_mfma(blocks, iters, out.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"gma_probe_mfma failed: {rc}")
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    flops = blocks * 4 * iters * 4 * 32 * 32 * 16 * 2
+    tf = flops / timed(mfma) / 1e12
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    gbs = 2 * src.numel() / timed(lambda: dst.copy_(src)) / 1e9
+    del src, dst, out
+    return {"mfma_bf16_tflops": round(tf, 1), "hbm_copy_gbs": round(gbs, 1),
+            "datasheet": {"mfma_bf16_tflops": BF16_PEAK_TFLOPS, "hbm_gbs": HBM_PEAK_GBS},
+            "note": "register-only loop of v_mfma_f32_32x32x16_bf16 (4 accumulators per wave, 8192 waves); "
+                    "1 GiB device copy, read + write bytes"}
+
+
 def rep_timing(step, torch, dev, reps=100, warmup=10, flush_bytes=512 << 20):
     """Per-rep timing: `warmup` untimed reps, then `reps` reps each timed alone with an event
     pair on the launch stream, (a) cold: a 512 MiB scratch buffer written before each rep
@@ -425,6 +466,8 @@ def main():
     ap.add_argument("--no-per-rep", action="store_true",
                     help="skip the per-rep (cold / warm) timing, e.g. under a profiler whose kernel "
                          "averages should cover the timed steps only")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the device peak probes (MFMA loop, 1 GiB copy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy one 256 MiB device buffer, so that a profiler's "
                          "memory counters can be scaled by a copy of known size")
@@ -520,6 +563,13 @@ def main():
                                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 6),
                                         "note": "whole call against twice the forward's algorithmic flops"}}
         line["backward"] = bl
+    if not args.no_peaks:
+        pk = device_peaks()
+        line["device_peaks"] = pk
+        for rl in [line["roofline"]] + [line[k]["roofline"] for k in ("causal", "cross") if k in line]:
+            m = pk["hbm_copy_gbs"] if rl["bound"] == "hbm" else pk["mfma_bf16_tflops"]
+            if rl["bound"] in ("hbm", "mfma") and rl["peak"] in (HBM_PEAK_GBS, BF16_PEAK_TFLOPS):
+                rl["frac_of_measured_peak"] = round(rl["achieved"] / m, 4)
     if args.copy_calibration:
         import torch
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")

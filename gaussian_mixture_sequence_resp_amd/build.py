@@ -1,4 +1,5 @@
-"""Builds libgma.so (HIP C++ for gfx950) in-tree with hipcc.
+"""Builds libgma.so (HIP C++ for gfx950) in-tree with hipcc, and the benchmark's device peak
+probe libgma_probe.so.
 
 Flags: -O3 for gfx950 only; packed-fp32 VALU instructions are disabled for every
 HIP translation unit (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
@@ -14,6 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgma.so")
 SOURCES = ["gma_api.cpp", "gma_simt.hip", "gma_mfma.hip", "gma_mfma_causal.hip", "gma_decode.hip", "gma_stats.hip", "gma_backward.hip"]
 ARCH = "gfx950"
+PROBE = "gma_probe.hip"
+PROBE_LIB = os.path.join(HERE, "libgma_probe.so")
 
 
 def hipcc() -> str:
@@ -51,6 +54,11 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     tmp = LIB + ".tmp"
     subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], check=True)
     os.replace(tmp, LIB)
+    # the benchmark's device peak probe, a library of its own (not part of the GMA ABI)
+    pobj = compile_one(PROBE)
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", pobj, "-o", tmp], check=True)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
