@@ -22,16 +22,19 @@
 //                                gma_causal_resp writing float rows) gives gamma instead
 //   per pass (pass 1 gives g_num, g_den and dl_Q; pass 2 gives dv and dl_K), the rows of each
 //   head cut into SEG contiguous segments:
-//   bwd_seg_partial  the segment's weighted rows summed in order (K x (d_v + 1) per segment)
+//   bwd_seg_partial  the segment's weighted rows summed in order (K x (d_v + 1) per segment,
+//                  LDS-tiled)
 //   bwd_seg_start    each segment's starting state from those partials in segment order: the
 //                  prefix before it (causal pass 1), the suffix after it (causal pass 2) or
 //                  the head's total (bidirectional)
 //   bwd_seg_rows     one workgroup per (b, h, segment) walks its rows (pass 2 in reverse) with the
 //                  state in LDS (in the workspace when it does not fit)
-//   bwd_x          dqr, dkr: one thread per (side, row, dim), double accumulation over k
-//   bwd_param_part per chunk of rows (both sides, all b), one thread per (h, k, d): partial
-//                  dmu, dvar and dlog pi in double
-//   bwd_param_final the partials summed in chunk order; dvar_raw, dprior
+//   bwd_x          dqr, dkr = Q - x P with P = dl lam, Q = dl (mu lam): LDS-tiled contractions
+//                  over the components (in A)
+//   bwd_param_part per chunk of rows (both sides, all b), LDS-tiled sums S0 = sum dl,
+//                  S1 = sum dl x, S2 = sum dl x^2 per (h, k, d) (in A), stored in double
+//   bwd_param_final, bwd_prior_final the chunk sums added in chunk order; dmu, dvar_raw;
+//                  dprior
 // Every sum has a fixed order: results are deterministic.
 #include <math.h>
 
@@ -64,36 +67,58 @@ __device__ __forceinline__ A pass_row(const T* v_bh, const A* gnum_bh, const A* 
 }
 
 // Partial state of every segment: part[bh][seg][k][c] = sum over the segment's rows j, in
-// order, of gamma[side][bh][j][k] * u_j[c].  Grid (ceil(K W / 256), BH * SEG).
+// order, of gamma[side][bh][j][k] * u_j[c], for a tile of 32 components x 64 columns per
+// workgroup (rows staged 64 at a time in LDS; each thread one component and 8 columns).
+// Grid (ceil(K / 32) ceil(W / 64), BH * SEG).
+constexpr int kSK = 32, kSC = 64, kSR = 64;
 template <typename T, typename A, int PASS>
 __global__ void __launch_bounds__(kBwdThreads)
     bwd_seg_partial(const A* __restrict__ gamma, const T* __restrict__ v, const A* __restrict__ gnum,
                     const A* __restrict__ gden, A* __restrict__ part, int BH, int N, int K, int dv, int SEG, int L) {
+    __shared__ A sg[kSR][kSK + 1];
+    __shared__ A su[kSR][kSC + 1];
     const int W = dv + 1;
-    const int e = blockIdx.x * kBwdThreads + threadIdx.x;
+    const int t = threadIdx.x;
+    const int nkt = (K + kSK - 1) / kSK;
+    const int k0 = (blockIdx.x % nkt) * kSK, c0 = (blockIdx.x / nkt) * kSC;
     const int bs = blockIdx.y, bh = bs / SEG, seg = bs % SEG;
-    if (e >= K * W) return;
-    const int k = e / W, c = e % W;
     const int side = PASS == 1 ? 1 : 0;  // pass 1 weights by gamma_K, pass 2 by gamma_Q
     const A* g = gamma + ((size_t)side * BH + bh) * N * K;
     const T* v_bh = v + (size_t)bh * N * dv;
     const A* gnum_bh = gnum + (size_t)bh * N * dv;
     const A* gden_bh = gden + (size_t)bh * N;
     const int j0 = seg * L, j1 = min(N, j0 + L);
-    A acc = 0;
-    int j = j0;
-    for (; j + 4 <= j1; j += 4) {  // the loads of 4 rows in flight together, summed in row order
-        A gg[4], uu[4];
+    const int kl = t >> 3, cg = t & 7;
+    A acc[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            gg[q] = g[(size_t)(j + q) * K + k];
-            uu[q] = pass_row<T, A, PASS>(v_bh, gnum_bh, gden_bh, dv, j + q, c);
+    for (int q = 0; q < 8; ++q) acc[q] = 0;
+    for (int jb = j0; jb < j1; jb += kSR) {
+        for (int idx = t; idx < kSR * kSK; idx += kBwdThreads) {
+            const int rr = idx / kSK, kk = idx % kSK;
+            const int j = jb + rr, k = k0 + kk;
+            sg[rr][kk] = (j < j1 && k < K) ? g[(size_t)j * K + k] : (A)0;
         }
+        for (int idx = t; idx < kSR * kSC; idx += kBwdThreads) {
+            const int rr = idx / kSC, cc = idx % kSC;
+            const int j = jb + rr, c = c0 + cc;
+            su[rr][cc] = (j < j1 && c < W) ? pass_row<T, A, PASS>(v_bh, gnum_bh, gden_bh, dv, j, c) : (A)0;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int rr = 0; rr < kSR; ++rr) {
+            const A gv = sg[rr][kl];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc += gg[q] * uu[q];
+            for (int q = 0; q < 8; ++q) acc[q] += gv * su[rr][cg + 8 * q];
+        }
+        __syncthreads();
     }
-    for (; j < j1; ++j) acc += g[(size_t)j * K + k] * pass_row<T, A, PASS>(v_bh, gnum_bh, gden_bh, dv, j, c);
-    part[(size_t)bs * K * W + e] = acc;
+    const int k = k0 + kl;
+    if (k >= K) return;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int c = c0 + cg + 8 * q;
+        if (c < W) part[(size_t)bs * K * W + (size_t)k * W + c] = acc[q];
+    }
 }
 
 // Starting state of every segment from the partials, summed in segment order: causal pass 1
@@ -269,122 +294,189 @@ __global__ void __launch_bounds__(kRowThreads)
     }
 }
 
-// dx of both sides: dx[side][bh][i][d] = -sum_k dl (x_d - mu_kd) lam_kd.
+// dx of both sides: dx[side][bh][i][d] = -sum_k dl_k (x_d - mu_kd) lam_kd = Q_d - x_d P_d with
+// P_d = sum_k dl_k lam_kd and Q_d = sum_k dl_k mu_kd lam_kd: a tile of 64 rows of one (side, bh)
+// and 64 dims per workgroup, the components in blocks of 32 staged in LDS (in A), each
+// thread 16 dims of one row; the sums over k in component order.
+// Grid (ceil(N / 64), 2 BH, ceil(d_r / 64)).
+constexpr int kXR = 64, kXD = 64, kXK = 32;
 template <typename T, typename A>
 __global__ void __launch_bounds__(kBwdThreads)
     bwd_x(const T* __restrict__ qr, const T* __restrict__ kr, const float* __restrict__ mu,
           const double* __restrict__ lam, const A* __restrict__ dl, T* __restrict__ dqr, T* __restrict__ dkr,
           int BH, int H, int N, int K, int dr) {
-    const size_t per_side = (size_t)BH * N * dr;
-    const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= 2 * per_side) return;
-    const int side = (int)(e / per_side);
-    const size_t r = e % per_side;
-    const size_t row = r / dr;  // bh * N + i
-    const int d = (int)(r % dr);
-    const int h = (int)((row / N) % H);
-    const T* x = side == 0 ? qr : kr;
-    const double xd = (double)Elem<T>::load(x, r);
-    const A* dlr = dl + ((size_t)side * BH * N + row) * K;
+    __shared__ A sdl[kXR][kXK + 1];
+    __shared__ A sl[kXK][kXD + 1], sml[kXK][kXD + 1];
+    const int t = threadIdx.x;
+    const int i0 = blockIdx.x * kXR, sb = blockIdx.y, d0 = blockIdx.z * kXD;
+    const int side = sb / BH, bh = sb % BH, h = bh % H;
+    const A* dl_r = dl + ((size_t)side * BH + bh) * N * K;
     const float* mu_h = mu + (size_t)h * K * dr;
     const double* lam_h = lam + (size_t)h * K * dr;
-    // four independent partial sums over k (added in a fixed order): the loads of four
-    // components are in flight together
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    int k = 0;
-    for (; k + 4 <= K; k += 4) {
-        a0 += (double)dlr[k] * (xd - (double)mu_h[(size_t)k * dr + d]) * lam_h[(size_t)k * dr + d];
-        a1 += (double)dlr[k + 1] * (xd - (double)mu_h[(size_t)(k + 1) * dr + d]) * lam_h[(size_t)(k + 1) * dr + d];
-        a2 += (double)dlr[k + 2] * (xd - (double)mu_h[(size_t)(k + 2) * dr + d]) * lam_h[(size_t)(k + 2) * dr + d];
-        a3 += (double)dlr[k + 3] * (xd - (double)mu_h[(size_t)(k + 3) * dr + d]) * lam_h[(size_t)(k + 3) * dr + d];
+    const int rl = t >> 2, dg = t & 3;
+    A P[16], Q[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) P[j] = Q[j] = 0;
+    for (int kb = 0; kb < K; kb += kXK) {
+        for (int idx = t; idx < kXR * kXK; idx += kBwdThreads) {
+            const int rr = idx / kXK, kk = idx % kXK;
+            const int i = i0 + rr, k = kb + kk;
+            sdl[rr][kk] = (i < N && k < K) ? dl_r[(size_t)i * K + k] : (A)0;
+        }
+        for (int idx = t; idx < kXK * kXD; idx += kBwdThreads) {
+            const int kk = idx / kXD, dd = idx % kXD;
+            const int k = kb + kk, d = d0 + dd;
+            A lv = 0, mv = 0;
+            if (k < K && d < dr) {
+                const double l = lam_h[(size_t)k * dr + d];
+                lv = (A)l;
+                mv = (A)((double)mu_h[(size_t)k * dr + d] * l);
+            }
+            sl[kk][dd] = lv;
+            sml[kk][dd] = mv;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < kXK; ++kk) {
+            const A g = sdl[rl][kk];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                P[j] += g * sl[kk][dg + 4 * j];
+                Q[j] += g * sml[kk][dg + 4 * j];
+            }
+        }
+        __syncthreads();
     }
-    for (; k < K; ++k) a0 += (double)dlr[k] * (xd - (double)mu_h[(size_t)k * dr + d]) * lam_h[(size_t)k * dr + d];
-    Elem<T>::store(side == 0 ? dqr : dkr, r, (float)-((a0 + a1) + (a2 + a3)));
+    const int i = i0 + rl;
+    if (i >= N) return;
+    const T* x = (side == 0 ? qr : kr) + ((size_t)bh * N + i) * dr;
+    T* dx = (side == 0 ? dqr : dkr) + ((size_t)bh * N + i) * dr;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int d = d0 + dg + 4 * j;
+        if (d < dr) Elem<T>::store(dx, d, (float)(Q[j] - (A)Elem<T>::load(x, d) * P[j]));
+    }
 }
 
-// Partial parameter gradients of chunk c of head h's 2 B N rows (side, b, i in that order):
-// thread (k, d); the d = 0 thread of each k also sums dlog pi_k.
+// Parameter-gradient sums of chunk c of head h's 2 B N rows (side, b, i in that order), for a
+// tile of 32 components x 64 dims: S0_k = sum dl_k, S1_kd = sum dl_k x_d, S2_kd = sum dl_k x_d^2
+// (in A, over the chunk's rows in order; rows staged 64 at a time in LDS).  Each thread owns one
+// component and 8 dims.  Grid (ceil(K / 32) ceil(d_r / 64), H, chunks).
+constexpr int kPK = 32, kPD = 64, kPR = 64;
 template <typename T, typename A>
 __global__ void __launch_bounds__(kBwdThreads)
-    bwd_param_part(const T* __restrict__ qr, const T* __restrict__ kr, const float* __restrict__ mu,
-                   const double* __restrict__ lam, const A* __restrict__ dl, double* __restrict__ pmu,
-                   double* __restrict__ pvar, double* __restrict__ ppi, int B, int H, int N, int K, int dr,
-                   int per_chunk) {
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    bwd_param_part(const T* __restrict__ qr, const T* __restrict__ kr, const A* __restrict__ dl,
+                   double* __restrict__ p1, double* __restrict__ p2, double* __restrict__ p0, int B, int H, int N,
+                   int K, int dr, int per_chunk) {
+    __shared__ A sdl[kPR][kPK + 1];
+    __shared__ A sx[kPR][kPD + 1];
+    const int t = threadIdx.x;
+    const int nkt = (K + kPK - 1) / kPK;
+    const int k0 = (blockIdx.x % nkt) * kPK, d0 = (blockIdx.x / nkt) * kPD;
     const int h = blockIdx.y, c = blockIdx.z;
-    if (e >= K * dr) return;
-    const int k = e / dr, d = e % dr;
-    const int BH = B * H;
-    const int total = 2 * B * N;
+    const int BH = B * H, BN = B * N;
+    const int total = 2 * BN;
     const int u0 = c * per_chunk, u1 = min(total, u0 + per_chunk);
-    const double m = mu[(size_t)h * K * dr + e], l = lam[(size_t)h * K * dr + e];
-    double am = 0.0, av = 0.0, ap = 0.0;
-    if (u0 < u1) {
-        // walk the rows (side, b, i) incrementally; the loads of 4 rows are in flight together
-        int side = u0 / (B * N), rem = u0 % (B * N);
-        int b = rem / N, i = rem % N;
-        auto next = [&]() {
-            if (++i == N) {
-                i = 0;
-                if (++b == B) {
-                    b = 0;
-                    ++side;
-                }
-            }
-        };
-        int u = u0;
-        while (u < u1) {
-            const int n = min(4, u1 - u);
-            double g[4], x[4];
+    const int kl = t >> 3, dg = t & 7;
+    A s0 = 0, s1[8], s2[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (q < n) {
-                    const size_t row = (size_t)(b * H + h) * N + i;
-                    g[q] = dl[((size_t)side * BH * N + row) * K + k];
-                    x[q] = (double)Elem<T>::load(side == 0 ? qr : kr, row * dr + d);
-                    next();
-                }
+    for (int j = 0; j < 8; ++j) s1[j] = s2[j] = 0;
+    // row u of the head -> (side, flat row of dl [side][BH][N], row of x [BH][N])
+    auto rows_of = [&](int u, size_t& dl_row, size_t& x_row, int& side) {
+        side = u / BN;
+        const int rem = u - side * BN;
+        const int b = rem / N, i = rem - b * N;
+        x_row = (size_t)(b * H + h) * N + i;
+        dl_row = (size_t)side * BH * N + x_row;
+    };
+    for (int ub = u0; ub < u1; ub += kPR) {
+        for (int idx = t; idx < kPR * kPK; idx += kBwdThreads) {
+            const int rr = idx / kPK, kk = idx % kPK;
+            const int u = ub + rr, k = k0 + kk;
+            A g = 0;
+            if (u < u1 && k < K) {
+                size_t dr_, xr_;
+                int sd;
+                rows_of(u, dr_, xr_, sd);
+                g = dl[dr_ * K + k];
             }
+            sdl[rr][kk] = g;
+        }
+        for (int idx = t; idx < kPR * kPD; idx += kBwdThreads) {
+            const int rr = idx / kPD, dd = idx % kPD;
+            const int u = ub + rr, d = d0 + dd;
+            A xv = 0;
+            if (u < u1 && d < dr) {
+                size_t dr_, xr_;
+                int sd;
+                rows_of(u, dr_, xr_, sd);
+                xv = (A)Elem<T>::load(sd == 0 ? qr : kr, xr_ * dr + d);
+            }
+            sx[rr][dd] = xv;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int rr = 0; rr < kPR; ++rr) {
+            const A g = sdl[rr][kl];
+            s0 += g;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (q < n) {
-                    const double diff = x[q] - m;
-                    am += g[q] * diff * l;
-                    av += g[q] * -0.5 * (l - diff * diff * l * l);
-                    ap += g[q];
-                }
+            for (int j = 0; j < 8; ++j) {
+                const A xv = sx[rr][dg + 8 * j];
+                const A gx = g * xv;
+                s1[j] += gx;
+                s2[j] += gx * xv;
             }
-            u += n;
+        }
+        __syncthreads();
+    }
+    const int k = k0 + kl;
+    if (k >= K) return;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int d = d0 + dg + 8 * j;
+        if (d < dr) {
+            const size_t o = ((size_t)c * H + h) * K * dr + (size_t)k * dr + d;
+            p1[o] = (double)s1[j];
+            p2[o] = (double)s2[j];
         }
     }
-    const size_t o = ((size_t)c * H + h) * K * dr + e;
-    pmu[o] = am;
-    pvar[o] = av;
-    if (d == 0) ppi[((size_t)c * H + h) * K + k] = ap;
+    if (d0 == 0 && dg == 0) p0[((size_t)c * H + h) * K + k] = (double)s0;
 }
 
-// One workgroup per head: the C partials in chunk order; dvar_raw = dvar sigmoid(var_raw);
+// The C chunk sums added in chunk order (double), one thread per (h, k, d):
+// dmu = lam (S1 - mu S0), dvar = -lam S0 / 2 + lam^2 (S2 - 2 mu S1 + mu^2 S0) / 2,
+// dvar_raw = dvar sigmoid(var_raw).  Grid (ceil(K d_r / 256), H).
+__global__ void __launch_bounds__(kBwdThreads)
+    bwd_param_final(const double* __restrict__ p1, const double* __restrict__ p2, const double* __restrict__ p0,
+                    const float* __restrict__ mu, const double* __restrict__ lam, const float* __restrict__ var_raw,
+                    float* __restrict__ dmu, float* __restrict__ dvar_raw, int H, int K, int dr, int C) {
+    const int e = blockIdx.x * kBwdThreads + threadIdx.x, h = blockIdx.y;
+    if (e >= K * dr) return;
+    const int k = e / dr;
+    double S0 = 0.0, S1 = 0.0, S2 = 0.0;
+    for (int c = 0; c < C; ++c) {
+        S0 += p0[((size_t)c * H + h) * K + k];
+        S1 += p1[((size_t)c * H + h) * K * dr + e];
+        S2 += p2[((size_t)c * H + h) * K * dr + e];
+    }
+    const size_t o = (size_t)h * K * dr + e;
+    const double m = mu[o], l = lam[o], r = var_raw[o];
+    dmu[o] = (float)(l * (S1 - m * S0));
+    const double dvar = -0.5 * l * S0 + 0.5 * l * l * (S2 - 2.0 * m * S1 + m * m * S0);
+    dvar_raw[o] = (float)(dvar / (1.0 + exp(-r)));
+}
+
+// One workgroup per head: dlog pi_k = S0_k (chunk sums in chunk order);
 // dprior = dlog pi - pi sum dlog pi.
 __global__ void __launch_bounds__(kBwdThreads)
-    bwd_param_final(const double* __restrict__ pmu, const double* __restrict__ pvar, const double* __restrict__ ppi,
-                    const float* __restrict__ var_raw, const float* __restrict__ prior, float* __restrict__ dmu,
-                    float* __restrict__ dvar_raw, float* __restrict__ dprior, int H, int K, int dr, int C) {
+    bwd_prior_final(const double* __restrict__ p0, const float* __restrict__ prior, float* __restrict__ dprior, int H,
+                    int K, int C) {
     __shared__ double sdp[GMA_MAX_K];
     __shared__ double sred[3];
     const int h = blockIdx.x, t = threadIdx.x;
-    for (int e = t; e < K * dr; e += kBwdThreads) {
-        double am = 0.0, av = 0.0;
-        for (int c = 0; c < C; ++c) {
-            am += pmu[((size_t)c * H + h) * K * dr + e];
-            av += pvar[((size_t)c * H + h) * K * dr + e];
-        }
-        const double r = var_raw[(size_t)h * K * dr + e];
-        dmu[(size_t)h * K * dr + e] = (float)am;
-        dvar_raw[(size_t)h * K * dr + e] = (float)(av / (1.0 + exp(-r)));
-    }
     for (int k = t; k < K; k += kBwdThreads) {
         double a = 0.0;
-        for (int c = 0; c < C; ++c) a += ppi[((size_t)c * H + h) * K + k];
+        for (int c = 0; c < C; ++c) a += p0[((size_t)c * H + h) * K + k];
         sdp[k] = a;
     }
     __syncthreads();
@@ -495,8 +587,9 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
     A* start = reinterpret_cast<A*>(a.ws + L.start);
     A* st_global = state_in_lds(d) ? nullptr : reinterpret_cast<A*>(a.ws + L.state);
     const unsigned gx = (unsigned)((KW + kBwdThreads - 1) / kBwdThreads);
+    const unsigned ptiles = (unsigned)(((d.K + kSK - 1) / kSK) * ((d.d_v + 1 + kSC - 1) / kSC));
     rec_begin(a, PASS == 1 ? "bwd_partial_1" : "bwd_partial_2");
-    bwd_seg_partial<T, A, PASS><<<dim3(gx, (unsigned)(BH * L.seg)), dim3(kBwdThreads), 0, a.stream>>>(
+    bwd_seg_partial<T, A, PASS><<<dim3(ptiles, (unsigned)(BH * L.seg)), dim3(kBwdThreads), 0, a.stream>>>(
         gamma, static_cast<const T*>(a.v), gnum, gden, part, BH, d.N, d.K, d.d_v, L.seg, L.seg_len);
     rec_end(a);
     hipError_t e;
@@ -548,24 +641,28 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
         }
         if ((e = bwd_pass<T, A, 1>(a, g, L, gamma, dl, gnum, gden)) != hipSuccess) return e;
         if ((e = bwd_pass<T, A, 2>(a, g, L, gamma, dl, gnum, gden)) != hipSuccess) return e;
-        const size_t nx = 2 * (size_t)BH * d.N * d.d_r;
         rec_begin(a, "bwd_x");
-        bwd_x<T, A><<<dim3((unsigned)((nx + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads), 0, a.stream>>>(
-            static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), a.mu, lam, dl, static_cast<T*>(g.dqr),
-            static_cast<T*>(g.dkr), BH, d.H, d.N, d.K, d.d_r);
+        bwd_x<T, A><<<dim3((unsigned)((d.N + kXR - 1) / kXR), (unsigned)(2 * BH), (unsigned)((d.d_r + kXD - 1) / kXD)),
+                      dim3(kBwdThreads), 0, a.stream>>>(static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), a.mu,
+                                                        lam, dl, static_cast<T*>(g.dqr), static_cast<T*>(g.dkr), BH,
+                                                        d.H, d.N, d.K, d.d_r);
         rec_end(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         rec_begin(a, "bwd_param_part");
-        bwd_param_part<T, A><<<dim3((d.K * d.d_r + kBwdThreads - 1) / kBwdThreads, d.H, L.chunks),
-                               dim3(kBwdThreads), 0, a.stream>>>(static_cast<const T*>(a.qr),
-                                                                  static_cast<const T*>(a.kr), a.mu, lam, dl, pmu,
-                                                                  pvar, ppi, d.B, d.H, d.N, d.K, d.d_r, L.per_chunk);
+        const int ptiles = ((d.K + kPK - 1) / kPK) * ((d.d_r + kPD - 1) / kPD);
+        bwd_param_part<T, A><<<dim3((unsigned)ptiles, d.H, L.chunks), dim3(kBwdThreads), 0, a.stream>>>(
+            static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), dl, pmu, pvar, ppi, d.B, d.H, d.N, d.K, d.d_r,
+            L.per_chunk);
         rec_end(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     rec_begin(a, "bwd_param_final");
-    bwd_param_final<<<dim3(d.H), dim3(kBwdThreads), 0, a.stream>>>(pmu, pvar, ppi, a.var_raw, a.prior, g.dmu,
-                                                                   g.dvar_raw, g.dprior, d.H, d.K, d.d_r, L.chunks);
+    bwd_param_final<<<dim3((unsigned)((d.K * d.d_r + kBwdThreads - 1) / kBwdThreads), d.H), dim3(kBwdThreads), 0,
+                      a.stream>>>(pmu, pvar, ppi, a.mu, lam, a.var_raw, g.dmu, g.dvar_raw, d.H, d.K, d.d_r, L.chunks);
+    rec_end(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    rec_begin(a, "bwd_prior_final");
+    bwd_prior_final<<<dim3(d.H), dim3(kBwdThreads), 0, a.stream>>>(ppi, a.prior, g.dprior, d.H, d.K, L.chunks);
     rec_end(a);
     return hipGetLastError();
 }
