@@ -27,8 +27,10 @@
 //   bwd_seg_start    each segment's starting state from those partials in segment order: the
 //                  prefix before it (causal pass 1), the suffix after it (causal pass 2) or
 //                  the head's total (bidirectional)
-//   bwd_seg_rows     one workgroup per (b, h, segment) walks its rows (pass 2 in reverse) with the
-//                  state in LDS (in the workspace when it does not fit)
+//   bwd_seg_rows     causal: one workgroup per (b, h, segment) walks its rows (pass 2 in
+//                  reverse) with the state in LDS (in the workspace when it does not fit)
+//   bwd_bidir_rows   bidirectional: the same per-row arithmetic against the head's total, each
+//                  wave of a workgroup walking its own rows
 //   bwd_x          dqr, dkr = Q - x P with P = dl lam, Q = dl (mu lam): LDS-tiled contractions
 //                  over the components (in A)
 //   bwd_param_part per chunk of rows (both sides, all b), LDS-tiled sums S0 = sum dl,
@@ -291,6 +293,84 @@ __global__ void __launch_bounds__(kRowThreads)
         const A s = ((sred[1] + sred[2]) + sred[3]) + sred[4];
         A* dl_row = dl + ((size_t)(PASS == 1 ? 0 : BH) + bh) * N * K + (size_t)i * K;
         for (int k = t; k < K; k += kRowThreads) dl_row[k] = sga[k] * (sgb[k] - s);
+    }
+}
+
+// Bidirectional rows: the state (the head's total) is the same for every row, so each wave
+// walks its own rows of the segment (rows i0 + wave, i0 + wave + 4, ...) with wave-private
+// LDS scratch and no workgroup barrier in the loop; the per-row arithmetic is that of
+// bwd_seg_rows with every contraction over components taken by one wave.  LDS: the state
+// [K][W], then per wave sga [K], sgb [K], sw [W].
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+template <typename T, typename A, int PASS>
+__global__ void __launch_bounds__(kRowThreads)
+    bwd_bidir_rows(const A* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
+                   A* __restrict__ gnum, A* __restrict__ gden, A* __restrict__ dl, T* __restrict__ dv_out,
+                   const A* __restrict__ start, const A* st_global, int BH, int N, int K, int dv, float eps, int SEG,
+                   int L) {
+    extern __shared__ double smem_d[];
+    A* smem = reinterpret_cast<A*>(smem_d);
+    const int W = dv + 1;
+    const int KW = K * W;
+    const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const A* st0 = start + (size_t)bh * SEG * KW;  // slot 0: the head's total
+    A* st_lds = smem;
+    const A* st = st_global ? st0 : st_lds;
+    A* scratch = st_global ? smem : smem + (size_t)KW;
+    A* sga = scratch + (size_t)wv * (2 * K + W);
+    A* sgb = sga + K;
+    A* sw = sgb + K;
+    if (!st_global) {
+        for (int e = t; e < KW; e += kRowThreads) st_lds[e] = st0[e];
+        __syncthreads();
+    }
+    const A* gq = gamma + (size_t)bh * N * K;
+    const A* gk = gamma + ((size_t)BH + bh) * N * K;
+    const T* v_bh = v + (size_t)bh * N * dv;
+    const T* do_bh = dout + (size_t)bh * N * dv;
+    A* gnum_bh = gnum + (size_t)bh * N * dv;
+    A* gden_bh = gden + (size_t)bh * N;
+    const int i0 = seg * L, i1 = min(N, i0 + L);
+    for (int i = i0 + wv; i < i1; i += kRowWaves) {
+        const A* grow = (PASS == 1 ? gq : gk) + (size_t)i * K;
+        for (int k = lane; k < K; k += 64) sga[k] = grow[k];
+        wave_lds_sync();
+        if constexpr (PASS == 1) {
+            for (int c = lane; c < W; c += 64) sw[c] = dot_k(sga, st, W, c, 0, K);
+            wave_lds_sync();
+            const A den = sw[dv] + (A)eps;
+            A dot = 0;
+            for (int c = lane; c < dv; c += 64) dot += (A)Elem<T>::load(do_bh, (size_t)i * dv + c) * (sw[c] / den);
+            const A gd = -wave_sum(dot) / den;
+            wave_lds_sync();
+            for (int c = lane; c < W; c += 64) {
+                const A g = c < dv ? (A)Elem<T>::load(do_bh, (size_t)i * dv + c) / den : gd;
+                sw[c] = g;
+                if (c < dv) gnum_bh[(size_t)i * dv + c] = g;
+            }
+            if (lane == 0) gden_bh[i] = gd;
+        } else {
+            T* dv_bh = dv_out + (size_t)bh * N * dv;
+            for (int c = lane; c < dv; c += 64) Elem<T>::store(dv_bh, (size_t)i * dv + c, (float)dot_k(sga, st, W, c, 0, K));
+            for (int c = lane; c < W; c += 64) sw[c] = c < dv ? (A)Elem<T>::load(v_bh, (size_t)i * dv + c) : (A)1;
+        }
+        wave_lds_sync();
+        A part = 0;
+        for (int k = lane; k < K; k += 64) {
+            const A a = dot_c(st, sw, W, k);
+            sgb[k] = a;
+            part += sga[k] * a;
+        }
+        const A s = wave_sum(part);
+        A* dl_row = dl + ((size_t)(PASS == 1 ? 0 : BH) + bh) * N * K + (size_t)i * K;
+        for (int k = lane; k < K; k += 64) dl_row[k] = sga[k] * (sgb[k] - s);
+        wave_lds_sync();
     }
 }
 
@@ -599,6 +679,19 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
                                                                                        L.seg, a.causal);
     rec_end(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!a.causal) {
+        // rows independent given the head's total: each wave walks its own rows
+        const size_t lds = (size_t)kRowWaves * (2 * d.K + d.d_v + 1) * acc_size(d) + (st_global ? 0 : scan_state(d));
+        if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_bidir_rows<T, A, PASS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+            return e;
+        rec_begin(a, PASS == 1 ? "bwd_rows_1" : "bwd_rows_2");
+        bwd_bidir_rows<T, A, PASS><<<dim3((unsigned)(BH * L.seg)), dim3(kRowThreads), lds, a.stream>>>(
+            gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
+            start, st_global ? start : nullptr, BH, d.N, d.K, d.d_v, a.eps, L.seg, L.seg_len);
+        rec_end(a);
+        return hipGetLastError();
+    }
     const size_t lds = scan_scratch(d) + (st_global ? 0 : scan_state(d));
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_seg_rows<T, A, PASS>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
