@@ -207,10 +207,12 @@ int gma_decode_step(const void* qr, const void* kr, const void* v, const float* 
  * batch and both sides, dL/dmu, dL/dvar_raw [H,K,d_r] and dL/dprior_logits [H,K] (float32;
  * all outputs are overwritten, not accumulated).  Same inputs, causal flag, eps and layout
  * as gma_forward; the forward is recomputed inside.  The gradients are the chain rule of the
- * forward: see the kernels' source for the formulas.  SIMT kernels (algo AUTO or SIMT; an
- * explicit MFMA request returns GMA_ERR_UNSUPPORTED); the per-head scans accumulate in
- * double for float32 inputs and in float for bf16, the parameter and input-row gradients
- * in double; deterministic.  Every shape within the limits is supported.
+ * forward: see the kernels' source for the formulas.  The responsibilities come from the
+ * matrix-core responsibilities kernel for bf16 inputs it covers (else the SIMT one); the
+ * passes over the rows are SIMT kernels (algo AUTO or SIMT; an explicit MFMA request returns
+ * GMA_ERR_UNSUPPORTED).  Sums accumulate in double for float32 inputs and in float for bf16
+ * (chunk sums of the parameter gradients combined in double); every sum has a fixed order,
+ * so results are deterministic.  Every shape within the limits is supported.
  * Alignment, aliasing and status codes as gma_forward (no output may overlap an input, the
  * workspace or another output).  N = 0 gives zero parameter gradients.
  */
