@@ -38,11 +38,11 @@ BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VALU_PEAK_TFLOPS = 157.3
 
 
+METRIC = "GMA forward tokens/s per head-layer; % of HBM/MFMA roofline (bidir+causal)"
+
+
 def metric_name() -> str:
-    try:
-        return json.load(open(os.path.join(ROOT, "BASELINE.json")))["metric"]
-    except Exception:
-        return "GMA forward tokens/s per head-layer"
+    return METRIC
 
 
 def algorithmic(w, kernel: str):
@@ -474,7 +474,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GMA forward here has no multi-GPU path "
-              "(the (b, h) slices shard with no communication; see DESIGN.md). Run --gpus 1.",
+              "(its (b, h) slices would shard across GPUs with no communication). Run --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     from gaussian_mixture_sequence_resp_amd.inputs import WORKLOADS
