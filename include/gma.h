@@ -56,7 +56,7 @@ extern "C" {
 
 #define GMA_VERSION 10400 /* 1.4.0: backward */
 
-/* Limits of this build. */
+/* Limits of the library (kernel tile and LDS sizes). */
 #define GMA_MAX_K 256
 #define GMA_MAX_DR 128
 #define GMA_MAX_DV 128
