@@ -374,6 +374,184 @@ __global__ void __launch_bounds__(kRowThreads)
     }
 }
 
+// Causal rows in chunks of kCh positions (the chunked form of the walk, as the forward's
+// scan): with St the state before the chunk (pass 1: the prefix before it; pass 2: the
+// suffix after it), rows r of the chunk and the chunk's own rows j on the inclusive side
+// (pass 1: j <= r; pass 2: j >= r),
+//   read_r   = ga_r St + sum_j (ga_r . gb_j) w_j        (pass 1: num; pass 2: dv)
+//   dgamma_r = St x_r + sum_j (w_j . x_r) gb_j          (x: g_r in pass 1, [v_r | 1] in pass 2)
+// with ga the row's own gamma (pass 1 gamma_Q, pass 2 gamma_K), gb the weighted side's
+// gamma and w its rows ([v | 1], or [g_num | g_den]); then St += sum_j gb_j (x) w_j.  The
+// same sums as the row-at-a-time walk, regrouped, with one workgroup barrier per step of a
+// chunk instead of per row.  LDS: St [K][W], sga, sgb [kCh][K + 1], sw, sx [kCh][W + 1],
+// sP, sQ [kCh][kCh].
+constexpr int kCh = 16;
+
+template <typename A>
+__device__ __forceinline__ A sum16(A x) {  // over the 16 lanes of a row group
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
+template <typename T, typename A, int PASS>
+__global__ void __launch_bounds__(kBwdThreads)
+    bwd_seg_chunks(const A* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
+                   A* __restrict__ gnum, A* __restrict__ gden, A* __restrict__ dl, T* __restrict__ dv_out,
+                   const A* __restrict__ start, int BH, int N, int K, int dv, float eps, int SEG, int L) {
+    extern __shared__ double smem_d[];
+    A* st = reinterpret_cast<A*>(smem_d);
+    const int W = dv + 1, KW = K * W, K1 = K + 1, W1 = W + 1;
+    A* sga = st + KW;
+    A* sgb = sga + kCh * K1;
+    A* sw = sgb + kCh * K1;
+    A* sx = sw + kCh * W1;
+    A* sP = sx + kCh * W1;
+    A* sQ = sP + kCh * kCh;
+    const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
+    const int t = threadIdx.x;
+    const A* st0 = start + ((size_t)bh * SEG + seg) * KW;
+    for (int e = t; e < KW; e += kBwdThreads) st[e] = st0[e];
+    const A* gq = gamma + (size_t)bh * N * K;
+    const A* gk = gamma + ((size_t)BH + bh) * N * K;
+    const A* ga_g = PASS == 1 ? gq : gk;  // the row's own side
+    const A* gb_g = PASS == 1 ? gk : gq;  // the weighted side
+    const T* v_bh = v + (size_t)bh * N * dv;
+    const T* do_bh = dout + (size_t)bh * N * dv;
+    A* gnum_bh = gnum + (size_t)bh * N * dv;
+    A* gden_bh = gden + (size_t)bh * N;
+    A* dl_bh = dl + ((size_t)(PASS == 1 ? 0 : BH) + bh) * N * K;
+    const int i0 = seg * L, i1 = min(N, i0 + L);
+    const int nch = (i1 - i0 + kCh - 1) / kCh;
+    const int rg = t >> 4, l16 = t & 15;  // row group of 16 lanes
+    for (int q = 0; q < nch; ++q) {
+        const int c0 = PASS == 1 ? i0 + kCh * q : max(i0, i1 - kCh * (q + 1));
+        const int c1 = PASS == 1 ? min(i1, c0 + kCh) : i1 - kCh * q;
+        const int nr = c1 - c0;
+        __syncthreads();
+        for (int idx = t; idx < kCh * K; idx += kBwdThreads) {
+            const int r = idx / K, k = idx % K;
+            sga[r * K1 + k] = r < nr ? ga_g[(size_t)(c0 + r) * K + k] : (A)0;
+            sgb[r * K1 + k] = r < nr ? gb_g[(size_t)(c0 + r) * K + k] : (A)0;
+        }
+        for (int idx = t; idx < kCh * W; idx += kBwdThreads) {
+            const int r = idx / W, c = idx % W;
+            A wv = 0, xv = 0;
+            if (r < nr) {
+                const A u = c < dv ? (A)Elem<T>::load(v_bh, (size_t)(c0 + r) * dv + c) : (A)1;
+                if constexpr (PASS == 1) {
+                    wv = u;
+                } else {
+                    wv = c < dv ? gnum_bh[(size_t)(c0 + r) * dv + c] : gden_bh[c0 + r];
+                    xv = u;
+                }
+            }
+            sw[r * W1 + c] = wv;
+            sx[r * W1 + c] = xv;
+        }
+        __syncthreads();
+        // P[r][j] = ga_r . gb_j on the inclusive side
+        {
+            const int r = t >> 4, j = t & 15;
+            A a = 0;
+            if (PASS == 1 ? j <= r : j >= r)
+                for (int k = 0; k < K; ++k) a += sga[r * K1 + k] * sgb[j * K1 + k];
+            sP[r * kCh + j] = a;
+        }
+        __syncthreads();
+        // read_r[c] = ga_r St[:, c] + sum_j P[r][j] w_j[c]
+        const int ncol = PASS == 1 ? W : dv;
+        for (int idx = t; idx < kCh * ncol; idx += kBwdThreads) {
+            const int r = idx / ncol, c = idx % ncol;
+            A a0 = 0, a1 = 0;
+            int k = 0;
+            for (; k + 2 <= K; k += 2) {
+                a0 += sga[r * K1 + k] * st[(size_t)k * W + c];
+                a1 += sga[r * K1 + k + 1] * st[(size_t)(k + 1) * W + c];
+            }
+            for (; k < K; ++k) a0 += sga[r * K1 + k] * st[(size_t)k * W + c];
+            A a = a0 + a1;
+            for (int j = 0; j < kCh; ++j) a += sP[r * kCh + j] * sw[j * W1 + c];
+            if constexpr (PASS == 1) {
+                sx[r * W1 + c] = a;  // num, turned into g below
+            } else if (r < nr) {
+                Elem<T>::store(dv_out + (size_t)bh * N * dv, (size_t)(c0 + r) * dv + c, (float)a);
+            }
+        }
+        __syncthreads();
+        if constexpr (PASS == 1) {
+            // g_r = [dout_r / den_r | -(dout_r . num_r / den_r) / den_r], 16 lanes per row
+            const int r = rg;
+            const bool ok = r < nr;
+            const A den = sx[r * W1 + dv] + (A)eps;
+            A dot = 0;
+            for (int c = l16; c < dv; c += 16)
+                if (ok) dot += (A)Elem<T>::load(do_bh, (size_t)(c0 + r) * dv + c) * (sx[r * W1 + c] / den);
+            const A gd = -sum16(dot) / den;
+            for (int c = l16; c < W; c += 16) {
+                const A gv = c < dv ? (ok ? (A)Elem<T>::load(do_bh, (size_t)(c0 + r) * dv + c) / den : (A)0) : (ok ? gd : (A)0);
+                sx[r * W1 + c] = gv;
+                if (ok && c < dv) gnum_bh[(size_t)(c0 + r) * dv + c] = gv;
+            }
+            if (ok && l16 == 0) gden_bh[c0 + r] = gd;
+            __syncthreads();
+        }
+        // Q[r][j] = w_j . x_r on the inclusive side
+        {
+            const int r = t >> 4, j = t & 15;
+            A a = 0;
+            if (PASS == 1 ? j <= r : j >= r)
+                for (int c = 0; c < W; ++c) a += sw[j * W1 + c] * sx[r * W1 + c];
+            sQ[r * kCh + j] = a;
+        }
+        __syncthreads();
+        // dgamma_r[k] = St[k] . x_r + sum_j Q[r][j] gb_j[k]; s_r; dl_r = ga_r (dgamma_r - s_r)
+        {
+            const int r = rg;
+            constexpr int kMaxPer = GMA_MAX_K / 16;
+            A dg[kMaxPer];
+            A part = 0;
+#pragma unroll
+            for (int m = 0; m < kMaxPer; ++m) {
+                const int k = l16 + 16 * m;
+                A a = 0;
+                if (k < K) {
+                    const A* srow = st + (size_t)k * W;
+                    A b0 = 0, b1 = 0;
+                    int c = 0;
+                    for (; c + 2 <= W; c += 2) {
+                        b0 += srow[c] * sx[r * W1 + c];
+                        b1 += srow[c + 1] * sx[r * W1 + c + 1];
+                    }
+                    for (; c < W; ++c) b0 += srow[c] * sx[r * W1 + c];
+                    a = b0 + b1;
+                    for (int j = 0; j < kCh; ++j) a += sQ[r * kCh + j] * sgb[j * K1 + k];
+                    part += sga[r * K1 + k] * a;
+                }
+                dg[m] = a;
+            }
+            const A sdot = sum16(part);
+            if (r < nr) {
+#pragma unroll
+                for (int m = 0; m < kMaxPer; ++m) {
+                    const int k = l16 + 16 * m;
+                    if (k < K) dl_bh[(size_t)(c0 + r) * K + k] = sga[r * K1 + k] * (dg[m] - sdot);
+                }
+            }
+        }
+        __syncthreads();
+        // St += sum_j gb_j (x) w_j over the chunk (rows past its end are zero)
+        for (int e = t; e < KW; e += kBwdThreads) {
+            const int k = e / W, c = e - k * W;
+            A a = st[e];
+            for (int j = 0; j < kCh; ++j) a += sgb[j * K1 + k] * sw[j * W1 + c];
+            st[e] = a;
+        }
+    }
+}
+
 // dx of both sides: dx[side][bh][i][d] = -sum_k dl_k (x_d - mu_kd) lam_kd = Q_d - x_d P_d with
 // P_d = sum_k dl_k lam_kd and Q_d = sum_k dl_k mu_kd lam_kd: a tile of 64 rows of one (side, bh)
 // and 64 dims per workgroup, the components in blocks of 32 staged in LDS (in A), each
@@ -689,6 +867,20 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
         bwd_bidir_rows<T, A, PASS><<<dim3((unsigned)(BH * L.seg)), dim3(kRowThreads), lds, a.stream>>>(
             gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
             start, st_global ? start : nullptr, BH, d.N, d.K, d.d_v, a.eps, L.seg, L.seg_len);
+        rec_end(a);
+        return hipGetLastError();
+    }
+    const size_t chunk_lds = scan_state(d) + (size_t)(2 * kCh * (d.K + 1) + 2 * kCh * (d.d_v + 2) + 2 * kCh * kCh) *
+                                                 acc_size(d);
+    if (chunk_lds <= kScanLdsMax) {
+        // causal: the segment walked in chunks of kCh positions
+        if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_seg_chunks<T, A, PASS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_lds)) != hipSuccess)
+            return e;
+        rec_begin(a, PASS == 1 ? "bwd_rows_1" : "bwd_rows_2");
+        bwd_seg_chunks<T, A, PASS><<<dim3((unsigned)(BH * L.seg)), dim3(kBwdThreads), chunk_lds, a.stream>>>(
+            gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
+            start, BH, d.N, d.K, d.d_v, a.eps, L.seg, L.seg_len);
         rec_end(a);
         return hipGetLastError();
     }
