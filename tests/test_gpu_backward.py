@@ -53,6 +53,9 @@ SHAPES = [
     # (B, H, N, d_r, d_v, K)
     (2, 3, 37, 16, 8, 12), (1, 2, 130, 64, 64, 128), (2, 2, 65, 24, 40, 33), (1, 1, 1, 8, 8, 1),
     (1, 2, 50, 5, 7, 7), (1, 1, 300, 64, 64, 256), (1, 1, 40, 128, 128, 256),
+    # enough (b, h) x positions that each head's rows are cut into segments of several
+    # 16-position chunks (32 and 64 rows per segment, the last one ragged)
+    (4, 4, 4096, 16, 16, 32), (4, 8, 4000, 16, 24, 20),
 ]
 
 
