@@ -98,3 +98,27 @@ def test_backward_deterministic_and_empty():
     torch.cuda.synchronize()
     for n in ("dmu", "dvar_raw", "dprior"):
         assert int(torch.count_nonzero(g0[n])) == 0, n
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_backward_full_size_sampled_heads(cfg):
+    """The backward at the benchmark's full sizes (the bidirectional K=128 and causal LM
+    workloads, the launch configuration the benchmark times), every gradient of two heads
+    (0 and H-1, all batch elements) against the oracle run on those heads alone: heads are
+    independent, so each is an H = 1 problem with that head's parameters."""
+    w = WORKLOADS[cfg]
+    inp = make_inputs(w)
+    dout = _dout(w, w.seed + 7)
+    _say("backward full size", w.name, dict(B=w.B, H=w.H, N=w.N, K=w.K))
+    d = {k: x.to(DEV) for k, x in inp.items()}
+    got = gma.backward(d["qr"], d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"], dout.to(DEV), w.causal,
+                       eps=w.eps, var_floor=w.var_floor)
+    torch.cuda.synchronize()
+    for h in (0, w.H - 1):
+        sub = {k: (x[:, h:h + 1].contiguous() if k in ("qr", "kr", "v") else x[h:h + 1].contiguous())
+               for k, x in inp.items()}
+        ref = oracle.backward(sub["qr"], sub["kr"], sub["v"], sub["mu"], sub["var_raw"], sub["prior_logits"],
+                              dout[:, h:h + 1].contiguous(), w.causal, w.eps, w.var_floor)
+        mine = {n: (got[n][:, h:h + 1] if n in ("dqr", "dkr", "dv") else got[n][h:h + 1]) for n in NAMES}
+        errs = _compare(mine, ref, metrics.tol_for(w.dtype))
+        _say("backward full size head", h, {n: f"{e:.2e}" for n, e in errs.items()})
