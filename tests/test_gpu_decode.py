@@ -128,3 +128,27 @@ def test_decode_with_parameters_not_16_byte_aligned(dtype):
                          w.eps, w.var_floor)
     for o in outs:
         assert metrics.rowrel(o, ref[:, :, 3:]) <= metrics.tol_for(dtype)
+
+
+def test_decode_full_size_sampled_heads():
+    """Prefill and decode at the benchmark's shape (the causal LM workload: B=16, H=8, K=256,
+    d=64, a prefix of 2048 positions, then 8 decode steps, all (b, h) in each launch): the
+    memory and the step outputs of heads 0 and H-1 (all batch elements) against the oracle
+    run on those heads alone."""
+    base = WORKLOADS[3]
+    steps = 8
+    w = base.with_(N=base.N + steps)
+    inp = make_inputs(w)
+    _say("decode full size", w.name, dict(B=w.B, H=w.H, prefix=base.N, steps=steps, K=w.K))
+    out, state = _run(inp, w, base.N)
+    tol = metrics.tol_for(w.dtype)
+    for h in (0, w.H - 1):
+        sub = {k: (x[:, h:h + 1].contiguous() if k in ("qr", "kr", "v") else x[h:h + 1].contiguous())
+               for k, x in inp.items()}
+        ref = oracle.forward(sub["qr"], sub["kr"], sub["v"], sub["mu"], sub["var_raw"], sub["prior_logits"], True,
+                             w.eps, w.var_floor)
+        err = metrics.rowrel(out[:, h:h + 1], ref[:, :, base.N:])
+        ref_state = oracle.memory(sub["kr"], sub["v"], sub["mu"], sub["var_raw"], sub["prior_logits"], w.var_floor)
+        serr = metrics.rowrel(state[:, h:h + 1], ref_state)
+        _say("decode full size head", h, f"out {err:.2e}", f"state after the steps {serr:.2e}")
+        assert err <= tol and serr <= tol, (h, err, serr)
