@@ -227,15 +227,26 @@ def device_peaks():
             raise RuntimeError(f"gma_probe_mfma_lds failed: {rc}")
 
     tf_lds = flops / timed(mfma_lds) / 1e12
+    probe.gma_probe_mfma_lds2.argtypes = probe.gma_probe_mfma.argtypes
+    probe.gma_probe_mfma_lds2.restype = ctypes.c_int
+
+    def mfma_lds2():
+        rc = probe.gma_probe_mfma_lds2(blocks, iters, out.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"gma_probe_mfma_lds2 failed: {rc}")
+
+    tf_lds2 = flops / timed(mfma_lds2) / 1e12
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     gbs = 2 * src.numel() / timed(lambda: dst.copy_(src)) / 1e9
     del src, dst, out
     return {"mfma_bf16_tflops": round(tf, 1), "mfma_bf16_lds_operand_tflops": round(tf_lds, 1),
+            "mfma_bf16_lds_both_operands_tflops": round(tf_lds2, 1),
             "hbm_copy_gbs": round(gbs, 1),
             "datasheet": {"mfma_bf16_tflops": BF16_PEAK_TFLOPS, "hbm_gbs": HBM_PEAK_GBS},
             "note": "register-only loop of v_mfma_f32_32x32x16_bf16 (4 accumulators per wave, 8192 waves); "
-                    "the same loop with each MFMA's A operand read from LDS (1 KB per wave per MFMA); "
+                    "the same loop with each MFMA's A operand read from LDS (1 KB per wave per MFMA), and with both "
+                    "operands read from LDS (2 KB); "
                     "1 GiB device copy, read + write bytes"}
 
 
