@@ -412,21 +412,27 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
         const float den = o[NT][0] + o[NT][4];
         const float s = o[NT][8];
         const float inv = 1.0f / (den + eps * s);
-        if (valid) {
-            bf16_t* orow = o_h + (size_t)t * dv;
+        // C register group q of o[n] holds value dims 32 n + 8 q + 4 half + 0..3 of this lane's
+        // position; the wave halves trade groups so that each lane stores 8 contiguous dims (16
+        // bytes): half the store instructions of 8-byte stores
+        bf16_t* orow = o_h + (size_t)t * dv;
 #pragma unroll
-            for (int n = 0; n < NT; ++n)
+        for (int n = 0; n < NT; ++n)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int d0 = 32 * n + 8 * q + 4 * half;
-                    if (d0 < dv) {
-                        uint2 p;
-                        p.x = pack_bf16(o[n][4 * q] * inv, o[n][4 * q + 1] * inv);
-                        p.y = pack_bf16(o[n][4 * q + 2] * inv, o[n][4 * q + 3] * inv);
-                        *reinterpret_cast<uint2*>(orow + d0) = p;
-                    }
-                }
-        }
+            for (int qp = 0; qp < 2; ++qp) {
+                uint2 p0, p1;  // groups q = 2 qp and 2 qp + 1 of this lane
+                p0.x = pack_bf16(o[n][8 * qp] * inv, o[n][8 * qp + 1] * inv);
+                p0.y = pack_bf16(o[n][8 * qp + 2] * inv, o[n][8 * qp + 3] * inv);
+                p1.x = pack_bf16(o[n][8 * qp + 4] * inv, o[n][8 * qp + 5] * inv);
+                p1.y = pack_bf16(o[n][8 * qp + 6] * inv, o[n][8 * qp + 7] * inv);
+                // one swap of the upper lanes of p0 with the lower lanes of p1: the lower half then
+                // holds group 2 qp of both halves (dims 16 qp + 0..7), the upper half group 2 qp + 1
+                auto sx = __builtin_amdgcn_permlane32_swap(p0.x, p1.x, false, false);
+                auto sy = __builtin_amdgcn_permlane32_swap(p0.y, p1.y, false, false);
+                const uint4 v16 = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+                const int d0 = 32 * n + 16 * qp + 8 * half;
+                if (valid && d0 < dv) *reinterpret_cast<uint4*>(orow + d0) = v16;
+            }
     }
 }
 

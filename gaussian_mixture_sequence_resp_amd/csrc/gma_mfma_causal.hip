@@ -574,21 +574,25 @@ __global__ void __launch_bounds__(kThreads, 1)
             }
             const float den = o[NTS][0] + o[NTS][4];
             const float inv = 1.0f / (den + eps);
-            if (t < n_end) {
-                bf16_t* orow = o_h + (size_t)t * dv;
+            // register group q of o[n] holds dims 32 n + 8 q + 4 half + 0..3 of this lane's
+            // position; one swap per group pair gives each lane 8 contiguous dims (one 16-byte
+            // store): the lower half takes group 2 qp of both halves, the upper half 2 qp + 1
+            bf16_t* orow = o_h + (size_t)t * dv;
 #pragma unroll
-                for (int n = 0; n < NTS; ++n)
+            for (int n = 0; n < NTS; ++n)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int d0 = dv0 + 32 * n + 8 * q + 4 * half;
-                        if (d0 < dv) {
-                            uint2 p;
-                            p.x = pack_bf16(o[n][4 * q] * inv, o[n][4 * q + 1] * inv);
-                            p.y = pack_bf16(o[n][4 * q + 2] * inv, o[n][4 * q + 3] * inv);
-                            *reinterpret_cast<uint2*>(orow + d0) = p;
-                        }
-                    }
-            }
+                for (int qp = 0; qp < 2; ++qp) {
+                    uint2 p0, p1;
+                    p0.x = pack_bf16(o[n][8 * qp] * inv, o[n][8 * qp + 1] * inv);
+                    p0.y = pack_bf16(o[n][8 * qp + 2] * inv, o[n][8 * qp + 3] * inv);
+                    p1.x = pack_bf16(o[n][8 * qp + 4] * inv, o[n][8 * qp + 5] * inv);
+                    p1.y = pack_bf16(o[n][8 * qp + 6] * inv, o[n][8 * qp + 7] * inv);
+                    auto sx = __builtin_amdgcn_permlane32_swap(p0.x, p1.x, false, false);
+                    auto sy = __builtin_amdgcn_permlane32_swap(p0.y, p1.y, false, false);
+                    const int d0 = dv0 + 32 * n + 16 * qp + 8 * half;
+                    if (t < n_end && d0 < dv)
+                        *reinterpret_cast<uint4*>(orow + d0) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+                }
         }
         // ---- state += Gamma_K^T [V | 1] over the group (this wave's tiles); the next group's
         // loads go out between its MFMAs
