@@ -284,13 +284,23 @@ struct SoftmaxStages {
             }
             if (st == 2) inv = valid ? 1.0f / sum_halves(s) : 0.0f;
         } else {
+            // register group q of tile m holds components 32 m + 8 q + 4 half + 0..3; one swap
+            // of the upper lanes of group 2 qp with the lower lanes of group 2 qp + 1 gives each
+            // lane 8 contiguous components (one 16-byte LDS store)
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<uint2*>(grow + 2 * (32 * m + 8 * q + 4 * half)) =
-                        make_uint2(pack_bf16(a[m][4 * q] * inv, a[m][4 * q + 1] * inv),
-                                   pack_bf16(a[m][4 * q + 2] * inv, a[m][4 * q + 3] * inv));
+                for (int qp = 0; qp < 2; ++qp) {
+                    const int i0 = 8 * qp;
+                    auto sx = __builtin_amdgcn_permlane32_swap(pack_bf16(a[m][i0] * inv, a[m][i0 + 1] * inv),
+                                                               pack_bf16(a[m][i0 + 4] * inv, a[m][i0 + 5] * inv),
+                                                               false, false);
+                    auto sy = __builtin_amdgcn_permlane32_swap(pack_bf16(a[m][i0 + 2] * inv, a[m][i0 + 3] * inv),
+                                                               pack_bf16(a[m][i0 + 6] * inv, a[m][i0 + 7] * inv),
+                                                               false, false);
+                    *reinterpret_cast<uint4*>(grow + 2 * (32 * m + 16 * qp + 8 * half)) =
+                        make_uint4(sx[0], sy[0], sx[1], sy[1]);
+                }
         }
     }
 };
