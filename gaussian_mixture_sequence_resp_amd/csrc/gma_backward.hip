@@ -374,6 +374,172 @@ __global__ void __launch_bounds__(kRowThreads)
     }
 }
 
+// Bidirectional rows on the matrix cores (bf16 inputs: float state and gamma).  Each wave
+// takes 32 rows at a time.  With G the rows' own gamma (32 x K) and St the head's total
+// (K x W, W = d_v + 1):
+//   C1 = St^T G^T (W x 32): pass 1 [num | den - eps] of every row, pass 2 [dv | .];
+//   the per-row epilogue turns C1 into w (pass 1 [g_num | g_den], pass 2 [v | 1]);
+//   C2 = St w^T (K x 32): dgamma of every row; then dl = gamma (dgamma - gamma . dgamma).
+// v_mfma_f32_32x32x2_f32 (fp32 products and sums).  Every contraction step pairs one index
+// of each lane half, chosen so that the B operand of the step is a register the lane already
+// holds in the C layout (lane l, register i of tile m: index 32 m + 8 (i / 4) + 4 (l / 32) +
+// i % 4 of row l % 32): gamma feeds C1 and the dl epilogue from the same registers, and C1
+// after the epilogue is the B operand of C2.  St sits in LDS as [32 MT][32 NTW + 1], zero
+// padded; the odd row length puts 32 consecutive rows of one column in distinct banks.
+constexpr int kMfRowThreads = 256;
+using mf::f32x16;
+using mf::sum_halves;
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T, int PASS, int MT, int NTW>
+__global__ void __launch_bounds__(kMfRowThreads)
+    bwd_bidir_mfma(const float* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
+                   float* __restrict__ gnum, float* __restrict__ gden, float* __restrict__ dl, T* __restrict__ dv_out,
+                   const float* __restrict__ start, int BH, int N, int K, int dv, float eps, int SEG, int L) {
+    extern __shared__ double smem_d[];
+    float* sS = reinterpret_cast<float*>(smem_d);
+    constexpr int Kp = 32 * MT, Wp = 32 * NTW, Ws = Wp + 1;
+    const int W = dv + 1;
+    const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
+    const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
+    const float* st0 = start + (size_t)bh * SEG * K * W;  // slot 0: the head's total
+    for (int e = t; e < Kp * Wp; e += kMfRowThreads) {
+        const int k = e / Wp, c = e % Wp;
+        sS[k * Ws + c] = (k < K && c < W) ? st0[(size_t)k * W + c] : 0.0f;
+    }
+    __syncthreads();
+    const size_t side = PASS == 1 ? 0 : (size_t)BH;
+    const float* g_bh = gamma + (side + bh) * N * K;
+    float* dl_bh = dl + (side + bh) * N * K;
+    const int i0 = seg * L, i1 = min(N, i0 + L);
+    const bool vec_k = (K & 3) == 0;
+    for (int tb = i0 + 32 * wv; tb < i1; tb += 32 * (kMfRowThreads / 64)) {
+        const int row = tb + col;
+        const bool ok = row < i1;
+        const size_t rr = (size_t)(ok ? row : i0);  // rows past the segment read a valid row
+        // gamma of this lane's row at its C-layout indices (zero past K)
+        f32x16 g[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k0 = 32 * m + 8 * q + 4 * half;
+                if (vec_k && k0 < K) {
+                    const float4 x = *reinterpret_cast<const float4*>(g_bh + rr * K + k0);
+                    g[m][4 * q] = x.x;
+                    g[m][4 * q + 1] = x.y;
+                    g[m][4 * q + 2] = x.z;
+                    g[m][4 * q + 3] = x.w;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) g[m][4 * q + j] = k0 + j < K ? g_bh[rr * K + k0 + j] : 0.0f;
+                }
+            }
+        // C1 = St^T G^T: step (m, i) contracts index 32 m + 8 (i / 4) + 4 h + i % 4 of half h
+        f32x16 c1[NTW];
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c1[n][i] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float* srow = sS + (32 * m + 8 * (i >> 2) + 4 * half + (i & 3)) * Ws + col;
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) c1[n] = mfma_f32(srow[32 * n], g[m][i], c1[n]);
+            }
+        // epilogue: C1 register i of tile n is column c = 32 n + 8 (i / 4) + 4 h + i % 4
+        if constexpr (PASS == 1) {
+            const T* do_r = dout + ((size_t)bh * N + rr) * dv;
+            float dp = 0.0f;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * n + 8 * (i >> 2) + 4 * half + (i & 3) == dv) dp = c1[n][i];
+            const float den = sum_halves(dp) + eps;
+            float dot = 0.0f;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
+                    if (c < dv) dot += Elem<T>::load(do_r, c) * (c1[n][i] / den);
+                }
+            const float gd = -sum_halves(dot) / den;
+            float* gn = gnum + ((size_t)bh * N + rr) * dv;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
+                    const float wv_c = c < dv ? Elem<T>::load(do_r, c) / den : (c == dv ? gd : 0.0f);
+                    c1[n][i] = wv_c;
+                    if (ok && c < dv) gn[c] = wv_c;
+                }
+            if (ok && half == 0) gden[(size_t)bh * N + rr] = gd;
+        } else {
+            const T* v_r = v + ((size_t)bh * N + rr) * dv;
+            T* dvo = dv_out + ((size_t)bh * N + rr) * dv;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
+                    if (ok && c < dv) Elem<T>::store(dvo, c, c1[n][i]);
+                    c1[n][i] = c < dv ? Elem<T>::load(v_r, c) : (c == dv ? 1.0f : 0.0f);
+                }
+        }
+        // C2 = St w^T: step (n, i) contracts column 32 n + 8 (i / 4) + 4 h + i % 4 of half h
+        f32x16 c2[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c2[m][i] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float* scol = sS + col * Ws + 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) c2[m] = mfma_f32(scol[32 * m * Ws], c1[n][i], c2[m]);
+            }
+        // dl = gamma (dgamma - gamma . dgamma)
+        float sp = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sp += g[m][i] * c2[m][i];
+        const float s = sum_halves(sp);
+        if (ok) {
+            float* dl_r = dl_bh + rr * K;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k0 = 32 * m + 8 * q + 4 * half;
+                    float4 x;
+                    x.x = g[m][4 * q] * (c2[m][4 * q] - s);
+                    x.y = g[m][4 * q + 1] * (c2[m][4 * q + 1] - s);
+                    x.z = g[m][4 * q + 2] * (c2[m][4 * q + 2] - s);
+                    x.w = g[m][4 * q + 3] * (c2[m][4 * q + 3] - s);
+                    if (vec_k && k0 < K) {
+                        *reinterpret_cast<float4*>(dl_r + k0) = x;
+                    } else {
+                        if (k0 < K) dl_r[k0] = x.x;
+                        if (k0 + 1 < K) dl_r[k0 + 1] = x.y;
+                        if (k0 + 2 < K) dl_r[k0 + 2] = x.z;
+                        if (k0 + 3 < K) dl_r[k0 + 3] = x.w;
+                    }
+                }
+        }
+    }
+}
+
 // Causal rows in chunks of kCh positions (the chunked form of the walk, as the forward's
 // scan): with St the state before the chunk (pass 1: the prefix before it; pass 2: the
 // suffix after it), rows r of the chunk and the chunk's own rows j on the inclusive side
@@ -836,6 +1002,35 @@ BwdLayout bwd_layout(const gma_desc& d) {
 }
 
 // One pass over the rows: segment partials, their ordered starts, then the segment walks.
+template <typename T, int PASS, int MT, int NTW>
+hipError_t launch_bidir_mfma_t(const Args& a, const BwdArgs& g, const float* gamma, float* gnum, float* gden,
+                               float* dl, const float* start, const BwdLayout& L) {
+    const gma_desc& d = a.d;
+    const int BH = d.B * d.H;
+    const size_t lds = (size_t)(32 * MT) * (32 * NTW + 1) * sizeof(float);
+    hipError_t e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_bidir_mfma<T, PASS, MT, NTW>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    bwd_bidir_mfma<T, PASS, MT, NTW><<<dim3((unsigned)(BH * L.seg)), dim3(kMfRowThreads), lds, a.stream>>>(
+        gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
+        start, BH, d.N, d.K, d.d_v, a.eps, L.seg, L.seg_len);
+    return hipGetLastError();
+}
+
+// MT = 32-component tiles (1, 2 or 4), NTW = 32-column tiles of the state (1, 2 or 3).
+template <typename T, int PASS>
+hipError_t launch_bidir_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, const float* gamma, float* gnum,
+                             float* gden, float* dl, const float* start, const BwdLayout& L) {
+#define GMA_BWD_MF(mt, ntw) \
+    if (MT == mt && NTW == ntw) return launch_bidir_mfma_t<T, PASS, mt, ntw>(a, g, gamma, gnum, gden, dl, start, L);
+    GMA_BWD_MF(1, 1) GMA_BWD_MF(1, 2) GMA_BWD_MF(1, 3)
+    GMA_BWD_MF(2, 1) GMA_BWD_MF(2, 2) GMA_BWD_MF(2, 3)
+    GMA_BWD_MF(4, 1) GMA_BWD_MF(4, 2) GMA_BWD_MF(4, 3)
+#undef GMA_BWD_MF
+    return hipErrorInvalidValue;
+}
+
 template <typename T, typename A, int PASS>
 hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamma, A* dl, A* gnum, A* gden) {
     const gma_desc& d = a.d;
@@ -858,6 +1053,17 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
     rec_end(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!a.causal) {
+        if constexpr (sizeof(A) == sizeof(float)) {
+            // bf16 inputs: 32-row tiles on the matrix cores when the state fits the tile shapes
+            const int MT = d.K <= 32 ? 1 : (d.K <= 64 ? 2 : (d.K <= 128 ? 4 : 0));
+            const int NTW = (d.d_v + 1 + 31) / 32;
+            if (MT > 0 && NTW <= 3) {
+                rec_begin(a, PASS == 1 ? "bwd_rows_1" : "bwd_rows_2");
+                e = launch_bidir_mfma<T, PASS>(a, g, MT, NTW, gamma, gnum, gden, dl, start, L);
+                rec_end(a);
+                return e;
+            }
+        }
         // rows independent given the head's total: each wave walks its own rows
         const size_t lds = (size_t)kRowWaves * (2 * d.K + d.d_v + 1) * acc_size(d) + (st_global ? 0 : scan_state(d));
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_bidir_rows<T, A, PASS>),

@@ -56,6 +56,8 @@ SHAPES = [
     # enough (b, h) x positions that each head's rows are cut into segments of several
     # 16-position chunks (32 and 64 rows per segment, the last one ragged)
     (4, 4, 4096, 16, 16, 32), (4, 8, 4000, 16, 24, 20),
+    # state widths at the 32-column tile edges (d_v + 1 = 96 and 32), K padded within a tile
+    (1, 2, 100, 32, 95, 96), (2, 1, 70, 8, 31, 64),
 ]
 
 
