@@ -48,6 +48,7 @@ namespace gma {
 namespace {
 
 constexpr int kBwdThreads = 256;
+constexpr size_t kScanLdsMax = 150 * 1024;  // dynamic LDS cap of the row, chunk and dx kernels
 constexpr int kParamChunks = 64;
 
 // Sums over rows are split into SEG contiguous segments of L rows per head.  The state of a
@@ -782,6 +783,109 @@ __global__ void __launch_bounds__(kBwdThreads)
     }
 }
 
+// dx of both sides on the matrix cores (bf16 inputs, float dl): per 32-row tile of one
+// (side, bh), P^T = lam^T dl^T and Q^T = (mu lam)^T dl^T (d_r x 32 each) with
+// v_mfma_f32_32x32x2_f32 over the components in blocks of 32; step i of a block contracts
+// component kb + 8 (i / 4) + 4 h + i % 4 of lane half h, so the B operand is the lane's own
+// dl register.  lam and mu lam of the head (float) sit in LDS as [32 ceil(K / 32)][32 NTD + 1].
+// Grid (ceil(N / 128), 2 BH); each wave takes 32 rows of the workgroup's 128.
+template <typename T, int NTD>
+__global__ void __launch_bounds__(kMfRowThreads)
+    bwd_x_mfma(const T* __restrict__ qr, const T* __restrict__ kr, const float* __restrict__ mu,
+               const double* __restrict__ lam, const float* __restrict__ dl, T* __restrict__ dqr, T* __restrict__ dkr,
+               int BH, int H, int N, int K, int dr) {
+    extern __shared__ double smem_d[];
+    constexpr int Ds = 32 * NTD + 1;
+    const int Kp = (K + 31) & ~31;
+    float* sL = reinterpret_cast<float*>(smem_d);
+    float* sM = sL + (size_t)Kp * Ds;
+    const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
+    const int sb = blockIdx.y, side = sb / BH, bh = sb % BH, h = bh % H;
+    const float* mu_h = mu + (size_t)h * K * dr;
+    const double* lam_h = lam + (size_t)h * K * dr;
+    for (int e = t; e < Kp * 32 * NTD; e += kMfRowThreads) {
+        const int k = e / (32 * NTD), d = e % (32 * NTD);
+        float lv = 0.0f, mv = 0.0f;
+        if (k < K && d < dr) {
+            const double lm = lam_h[(size_t)k * dr + d];
+            lv = (float)lm;
+            mv = (float)((double)mu_h[(size_t)k * dr + d] * lm);
+        }
+        sL[k * Ds + d] = lv;
+        sM[k * Ds + d] = mv;
+    }
+    __syncthreads();
+    const int row = blockIdx.x * 128 + 32 * wv + col;
+    const bool ok = row < N;
+    const size_t rr = (size_t)(ok ? row : N - 1);
+    const float* dl_r = dl + (((size_t)side * BH + bh) * N + rr) * K;
+    const bool vec_k = (K & 3) == 0;
+    f32x16 P[NTD], Q[NTD];
+#pragma unroll
+    for (int n = 0; n < NTD; ++n)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) P[n][i] = Q[n][i] = 0.0f;
+    for (int kb = 0; kb < Kp; kb += 32) {
+        float g[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k0 = kb + 8 * q + 4 * half;
+            if (vec_k && k0 < K) {
+                const float4 x = *reinterpret_cast<const float4*>(dl_r + k0);
+                g[4 * q] = x.x;
+                g[4 * q + 1] = x.y;
+                g[4 * q + 2] = x.z;
+                g[4 * q + 3] = x.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) g[4 * q + j] = k0 + j < K ? dl_r[k0 + j] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int k = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+#pragma unroll
+            for (int n = 0; n < NTD; ++n) {
+                P[n] = mfma_f32(sL[k * Ds + 32 * n + col], g[i], P[n]);
+                Q[n] = mfma_f32(sM[k * Ds + 32 * n + col], g[i], Q[n]);
+            }
+        }
+    }
+    if (!ok) return;
+    const T* x = (side == 0 ? qr : kr) + ((size_t)bh * N + rr) * dr;
+    T* dx = (side == 0 ? dqr : dkr) + ((size_t)bh * N + rr) * dr;
+#pragma unroll
+    for (int n = 0; n < NTD; ++n)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int d = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (d < dr) Elem<T>::store(dx, d, Q[n][i] - Elem<T>::load(x, d) * P[n][i]);
+        }
+}
+
+template <typename T, int NTD>
+hipError_t launch_x_mfma_t(const Args& a, const BwdArgs& g, const double* lam, const float* dl) {
+    const gma_desc& d = a.d;
+    const int BH = d.B * d.H;
+    const size_t lds = 2 * (size_t)((d.K + 31) & ~31) * (32 * NTD + 1) * sizeof(float);
+    hipError_t e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_x_mfma<T, NTD>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    bwd_x_mfma<T, NTD><<<dim3((unsigned)((d.N + 127) / 128), (unsigned)(2 * BH)), dim3(kMfRowThreads), lds, a.stream>>>(
+        static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), a.mu, lam, dl, static_cast<T*>(g.dqr),
+        static_cast<T*>(g.dkr), BH, d.H, d.N, d.K, d.d_r);
+    return hipGetLastError();
+}
+
+// LDS bytes of bwd_x_mfma (0: the shape is not taken).
+size_t x_mfma_lds(const gma_desc& d) {
+    const int ntd = (d.d_r + 31) / 32;
+    if (ntd > 4) return 0;
+    const size_t lds = 2 * (size_t)((d.K + 31) & ~31) * (32 * ntd + 1) * sizeof(float);
+    return lds <= kScanLdsMax ? lds : 0;
+}
+
 // Parameter-gradient sums of chunk c of head h's 2 B N rows (side, b, i in that order), for a
 // tile of 32 components x 64 dims: S0_k = sum dl_k, S1_kd = sum dl_k x_d, S2_kd = sum dl_k x_d^2
 // (in A, over the chunk's rows in order; rows staged 64 at a time in LDS).  Each thread owns one
@@ -923,8 +1027,6 @@ __global__ void __launch_bounds__(kBwdThreads)
         dprior[(size_t)h * K + k] = (float)(sdp[k] - pi * sred[2]);
     }
 }
-
-constexpr size_t kScanLdsMax = 150 * 1024;
 
 // Scratch of the rows kernel besides its state, and whether the state fits in LDS with it.
 size_t acc_size(const gma_desc& d) { return d.dtype == GMA_F32 ? sizeof(double) : sizeof(float); }
@@ -1133,12 +1235,26 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
         if ((e = bwd_pass<T, A, 1>(a, g, L, gamma, dl, gnum, gden)) != hipSuccess) return e;
         if ((e = bwd_pass<T, A, 2>(a, g, L, gamma, dl, gnum, gden)) != hipSuccess) return e;
         rec_begin(a, "bwd_x");
-        bwd_x<T, A><<<dim3((unsigned)((d.N + kXR - 1) / kXR), (unsigned)(2 * BH), (unsigned)((d.d_r + kXD - 1) / kXD)),
-                      dim3(kBwdThreads), 0, a.stream>>>(static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), a.mu,
-                                                        lam, dl, static_cast<T*>(g.dqr), static_cast<T*>(g.dkr), BH,
-                                                        d.H, d.N, d.K, d.d_r);
+        bool x_done = false;
+        if constexpr (sizeof(A) == sizeof(float)) {
+            if (x_mfma_lds(d) > 0) {
+                const int ntd = (d.d_r + 31) / 32;
+                e = ntd == 1   ? launch_x_mfma_t<T, 1>(a, g, lam, dl)
+                    : ntd == 2 ? launch_x_mfma_t<T, 2>(a, g, lam, dl)
+                    : ntd == 3 ? launch_x_mfma_t<T, 3>(a, g, lam, dl)
+                               : launch_x_mfma_t<T, 4>(a, g, lam, dl);
+                x_done = true;
+            }
+        }
+        if (!x_done) {
+            bwd_x<T, A><<<dim3((unsigned)((d.N + kXR - 1) / kXR), (unsigned)(2 * BH), (unsigned)((d.d_r + kXD - 1) / kXD)),
+                          dim3(kBwdThreads), 0, a.stream>>>(static_cast<const T*>(a.qr), static_cast<const T*>(a.kr),
+                                                            a.mu, lam, dl, static_cast<T*>(g.dqr),
+                                                            static_cast<T*>(g.dkr), BH, d.H, d.N, d.K, d.d_r);
+            e = hipGetLastError();
+        }
         rec_end(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (e != hipSuccess) return e;
         rec_begin(a, "bwd_param_part");
         const int ptiles = ((d.K + kPK - 1) / kPK) * ((d.d_r + kPD - 1) / kPD);
         bwd_param_part<T, A><<<dim3((unsigned)ptiles, d.H, L.chunks), dim3(kBwdThreads), 0, a.stream>>>(
