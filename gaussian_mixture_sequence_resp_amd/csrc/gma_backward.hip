@@ -29,10 +29,13 @@
 //                  the head's total (bidirectional)
 //   bwd_seg_rows     causal: one workgroup per (b, h, segment) walks its rows (pass 2 in
 //                  reverse) with the state in LDS (in the workspace when it does not fit)
-//   bwd_bidir_rows   bidirectional: the same per-row arithmetic against the head's total, each
-//                  wave of a workgroup walking its own rows
-//   bwd_x          dqr, dkr = Q - x P with P = dl lam, Q = dl (mu lam): LDS-tiled contractions
-//                  over the components (in A)
+//   bwd_bidir_mfma bidirectional, bf16 inputs: the per-row arithmetic against the head's
+//                  total as fp32 matrix-core products over 32-row tiles
+//   bwd_bidir_rows   bidirectional otherwise: the same per-row arithmetic, each wave of a
+//                  workgroup walking its own rows
+//   bwd_x_mfma     bf16 inputs: dqr, dkr = Q - x P with P = dl lam, Q = dl (mu lam) as fp32
+//                  matrix-core products over 32-row tiles
+//   bwd_x          otherwise: the same with LDS-tiled contractions over the components (in A)
 //   bwd_param_part per chunk of rows (both sides, all b), LDS-tiled sums S0 = sum dl,
 //                  S1 = sum dl x, S2 = sum dl x^2 per (h, k, d) (in A), stored in double
 //   bwd_param_final, bwd_prior_final the chunk sums added in chunk order; dmu, dvar_raw;
