@@ -23,7 +23,8 @@
 //   per pass (pass 1 gives g_num, g_den and dl_Q; pass 2 gives dv and dl_K), the rows of each
 //   head cut into SEG contiguous segments:
 //   bwd_seg_partial  the segment's weighted rows summed in order (K x (d_v + 1) per segment,
-//                  LDS-tiled)
+//                  LDS-tiled; bwd_seg_partial_mfma for bf16 inputs: fp32 matrix-core
+//                  products over 32-row blocks staged in LDS)
 //   bwd_seg_start    each segment's starting state from those partials in segment order: the
 //                  prefix before it (causal pass 1), the suffix after it (causal pass 2) or
 //                  the head's total (bidirectional)
@@ -1136,6 +1137,110 @@ hipError_t launch_bidir_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, c
     return hipErrorInvalidValue;
 }
 
+// Segment partials on the matrix cores (bf16 inputs: float gamma and rows): part[bs] =
+// G^T U over the segment's rows (K x W), G the weighting side's gamma rows and U the pass's
+// rows, in blocks of 32 rows staged in LDS (float, row strides padded to an odd multiple of
+// 32 words so the two lane halves, which read two different rows, use disjoint banks).  The
+// MT x NTW output tiles of 32 x 32 are dealt over the 4 waves (tile w, w + 4, ...); each
+// v_mfma_f32_32x32x2_f32 step contracts two rows, one per lane half.  Grid (BH * SEG).
+template <typename T, int PASS, int MT, int NTW>
+__global__ void __launch_bounds__(kMfRowThreads)
+    bwd_seg_partial_mfma(const float* __restrict__ gamma, const T* __restrict__ v, const float* __restrict__ gnum,
+                         const float* __restrict__ gden, float* __restrict__ part, int BH, int N, int K, int dv,
+                         int SEG, int L) {
+    extern __shared__ double smem_d[];
+    constexpr int GS = 32 * (MT + (MT % 2 == 0 ? 1 : 0)), US = 32 * (NTW + (NTW % 2 == 0 ? 1 : 0));
+    constexpr int kTiles = MT * NTW, kWaves = kMfRowThreads / 64, TPW = (kTiles + kWaves - 1) / kWaves;
+    float* sG = reinterpret_cast<float*>(smem_d);  // [32][GS]
+    float* sU = sG + 32 * GS;                      // [32][US]
+    const int W = dv + 1;
+    const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
+    const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
+    const int side = PASS == 1 ? 1 : 0;  // pass 1 weights by gamma_K, pass 2 by gamma_Q
+    const float* g = gamma + ((size_t)side * BH + bh) * N * K;
+    const T* v_bh = v + (size_t)bh * N * dv;
+    const float* gnum_bh = gnum + (size_t)bh * N * dv;
+    const float* gden_bh = gden + (size_t)bh * N;
+    const int j0 = seg * L, j1 = min(N, j0 + L);
+    f32x16 acc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[u][e] = 0.0f;
+    for (int jb = j0; jb < j1; jb += 32) {
+        for (int e = t; e < 32 * 32 * MT; e += kMfRowThreads) {
+            const int r = e / (32 * MT), k = e % (32 * MT), j = jb + r;
+            sG[r * GS + k] = (j < j1 && k < K) ? g[(size_t)j * K + k] : 0.0f;
+        }
+        for (int e = t; e < 32 * 32 * NTW; e += kMfRowThreads) {
+            const int r = e / (32 * NTW), c = e % (32 * NTW), j = jb + r;
+            float u = 0.0f;
+            if (j < j1 && c < W) {
+                if constexpr (PASS == 1)
+                    u = c < dv ? Elem<T>::load(v_bh, (size_t)j * dv + c) : 1.0f;
+                else
+                    u = c < dv ? gnum_bh[(size_t)j * dv + c] : gden_bh[j];
+            }
+            sU[r * US + c] = u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tau = wv + kWaves * u;
+            if (tau < kTiles) {
+                const int m = tau / NTW, n = tau % NTW;
+                const float* ga = sG + half * GS + 32 * m + col;
+                const float* ub = sU + half * US + 32 * n + col;
+#pragma unroll
+                for (int st = 0; st < 16; ++st)
+                    acc[u] = mfma_f32(ga[2 * st * GS], ub[2 * st * US], acc[u]);
+            }
+        }
+        __syncthreads();
+    }
+    float* out = part + (size_t)bs * K * W;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tau = wv + kWaves * u;
+        if (tau < kTiles) {
+            const int m = tau / NTW, n = tau % NTW, c = 32 * n + col;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int k = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
+                if (k < K && c < W) out[(size_t)k * W + c] = acc[u][e];
+            }
+        }
+    }
+}
+
+template <typename T, int PASS, int MT, int NTW>
+hipError_t launch_partial_mfma_t(const Args& a, const float* gamma, const float* gnum, const float* gden, float* part,
+                                 const BwdLayout& L) {
+    const gma_desc& d = a.d;
+    constexpr int GS = 32 * (MT + (MT % 2 == 0 ? 1 : 0)), US = 32 * (NTW + (NTW % 2 == 0 ? 1 : 0));
+    const size_t lds = (size_t)32 * (GS + US) * sizeof(float);
+    hipError_t e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_seg_partial_mfma<T, PASS, MT, NTW>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    bwd_seg_partial_mfma<T, PASS, MT, NTW><<<dim3((unsigned)(d.B * d.H * L.seg)), dim3(kMfRowThreads), lds, a.stream>>>(
+        gamma, static_cast<const T*>(a.v), gnum, gden, part, d.B * d.H, d.N, d.K, d.d_v, L.seg, L.seg_len);
+    return hipGetLastError();
+}
+
+template <typename T, int PASS>
+hipError_t launch_partial_mfma(const Args& a, int MT, int NTW, const float* gamma, const float* gnum,
+                               const float* gden, float* part, const BwdLayout& L) {
+#define GMA_BWD_PM(mt, ntw) \
+    if (MT == mt && NTW == ntw) return launch_partial_mfma_t<T, PASS, mt, ntw>(a, gamma, gnum, gden, part, L);
+    GMA_BWD_PM(1, 1) GMA_BWD_PM(1, 2) GMA_BWD_PM(1, 3)
+    GMA_BWD_PM(2, 1) GMA_BWD_PM(2, 2) GMA_BWD_PM(2, 3)
+    GMA_BWD_PM(4, 1) GMA_BWD_PM(4, 2) GMA_BWD_PM(4, 3)
+    GMA_BWD_PM(8, 1) GMA_BWD_PM(8, 2) GMA_BWD_PM(8, 3)
+#undef GMA_BWD_PM
+    return hipErrorInvalidValue;
+}
+
 template <typename T, typename A, int PASS>
 hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamma, A* dl, A* gnum, A* gden) {
     const gma_desc& d = a.d;
@@ -1147,11 +1252,24 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
     const unsigned gx = (unsigned)((KW + kBwdThreads - 1) / kBwdThreads);
     const unsigned ptiles = (unsigned)(((d.K + kSK - 1) / kSK) * ((d.d_v + 1 + kSC - 1) / kSC));
     rec_begin(a, PASS == 1 ? "bwd_partial_1" : "bwd_partial_2");
-    bwd_seg_partial<T, A, PASS><<<dim3(ptiles, (unsigned)(BH * L.seg)), dim3(kBwdThreads), 0, a.stream>>>(
-        gamma, static_cast<const T*>(a.v), gnum, gden, part, BH, d.N, d.K, d.d_v, L.seg, L.seg_len);
+    hipError_t e = hipSuccess;
+    bool p_done = false;
+    if constexpr (sizeof(A) == sizeof(float)) {
+        // bf16 inputs: matrix-core partials when the tile shapes cover K and d_v + 1
+        const int MT = d.K <= 32 ? 1 : (d.K <= 64 ? 2 : (d.K <= 128 ? 4 : (d.K <= 256 ? 8 : 0)));
+        const int NTW = (d.d_v + 1 + 31) / 32;
+        if (MT > 0 && NTW <= 3) {
+            e = launch_partial_mfma<T, PASS>(a, MT, NTW, gamma, gnum, gden, part, L);
+            p_done = true;
+        }
+    }
+    if (!p_done) {
+        bwd_seg_partial<T, A, PASS><<<dim3(ptiles, (unsigned)(BH * L.seg)), dim3(kBwdThreads), 0, a.stream>>>(
+            gamma, static_cast<const T*>(a.v), gnum, gden, part, BH, d.N, d.K, d.d_v, L.seg, L.seg_len);
+        e = hipGetLastError();
+    }
     rec_end(a);
-    hipError_t e;
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
     rec_begin(a, PASS == 1 ? "bwd_start_1" : "bwd_start_2");
     bwd_seg_start<A, PASS><<<dim3(gx, (unsigned)BH), dim3(kBwdThreads), 0, a.stream>>>(part, start, d.K, d.d_v,
                                                                                        L.seg, a.causal);
