@@ -38,7 +38,8 @@
 //                  matrix-core products over 32-row tiles
 //   bwd_x          otherwise: the same with LDS-tiled contractions over the components (in A)
 //   bwd_param_part per chunk of rows (both sides, all b), LDS-tiled sums S0 = sum dl,
-//                  S1 = sum dl x, S2 = sum dl x^2 per (h, k, d) (in A), stored in double
+//                  S1 = sum dl x, S2 = sum dl x^2 per (h, k, d) (in A), stored in double;
+//                  bwd_param_mfma the same for bf16 inputs as fp32 matrix-core products
 //   bwd_param_final, bwd_prior_final the chunk sums added in chunk order; dmu, dvar_raw;
 //                  dprior
 // Every sum has a fixed order: results are deterministic.
@@ -1325,6 +1326,119 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
     return hipGetLastError();
 }
 
+// Parameter-gradient sums on the matrix cores (bf16 inputs, float dl): for chunk c of head h,
+// S1 = dl^T x and S2 = dl^T x^2 (K x d_r) from blocks of 32 of the chunk's rows staged in LDS
+// (dl and x as float; strides padded as in bwd_seg_partial_mfma), the MT x NTD output tiles
+// dealt over the 4 waves, each v_mfma_f32_32x32x2_f32 step contracting one row per lane half
+// (x^2 formed from the staged x); S0 = sum dl by one thread per component, rows in order.
+// Grid (H, chunks).
+template <typename T, int MT, int NTD>
+__global__ void __launch_bounds__(kMfRowThreads)
+    bwd_param_mfma(const T* __restrict__ qr, const T* __restrict__ kr, const float* __restrict__ dl,
+                   double* __restrict__ p1, double* __restrict__ p2, double* __restrict__ p0, int B, int H, int N,
+                   int K, int dr, int per_chunk) {
+    extern __shared__ double smem_d[];
+    constexpr int GS = 32 * (MT + (MT % 2 == 0 ? 1 : 0)), XS = 32 * (NTD + (NTD % 2 == 0 ? 1 : 0));
+    constexpr int kTiles = MT * NTD, kWaves = kMfRowThreads / 64, TPW = (kTiles + kWaves - 1) / kWaves;
+    size_t* sRow = reinterpret_cast<size_t*>(smem_d);   // [32] x row of each staged row
+    int* sSide = reinterpret_cast<int*>(sRow + 32);     // [32]
+    float* sD = reinterpret_cast<float*>(sSide + 32);   // [32][GS]
+    float* sX = sD + 32 * GS;                           // [32][XS]
+    const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
+    const int h = blockIdx.x, c = blockIdx.y;
+    const int BH = B * H, BN = B * N;
+    const int u0 = c * per_chunk, u1 = min(2 * BN, u0 + per_chunk);
+    f32x16 a1[TPW], a2[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) a1[u][e] = a2[u][e] = 0.0f;
+    float s0 = 0.0f;
+    for (int ub = u0; ub < u1; ub += 32) {
+        if (t < 32) {
+            const int u = min(ub + t, u1 - 1);  // rows past the chunk: a valid row, zeroed below
+            const int side = u / BN, rem = u - side * BN, b = rem / N, i = rem - b * N;
+            sRow[t] = ((size_t)b * H + h) * N + i;
+            sSide[t] = side;
+        }
+        __syncthreads();
+        for (int e = t; e < 32 * 32 * MT; e += kMfRowThreads) {
+            const int r = e / (32 * MT), k = e % (32 * MT);
+            const size_t drow = (size_t)sSide[r] * BH * N + sRow[r];
+            sD[r * GS + k] = (ub + r < u1 && k < K) ? dl[drow * K + k] : 0.0f;
+        }
+        for (int e = t; e < 32 * 32 * NTD; e += kMfRowThreads) {
+            const int r = e / (32 * NTD), d = e % (32 * NTD);
+            sX[r * XS + d] = (ub + r < u1 && d < dr) ? Elem<T>::load(sSide[r] == 0 ? qr : kr, sRow[r] * dr + d) : 0.0f;
+        }
+        __syncthreads();
+        if (t < 32 * MT) {
+            for (int r = 0; r < 32; ++r) s0 += sD[r * GS + t];
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tau = wv + kWaves * u;
+            if (tau < kTiles) {
+                const int m = tau / NTD, n = tau % NTD;
+                const float* da = sD + half * GS + 32 * m + col;
+                const float* xb = sX + half * XS + 32 * n + col;
+#pragma unroll
+                for (int st = 0; st < 16; ++st) {
+                    const float av = da[2 * st * GS], xv = xb[2 * st * XS];
+                    a1[u] = mfma_f32(av, xv, a1[u]);
+                    a2[u] = mfma_f32(av, xv * xv, a2[u]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    const size_t base = ((size_t)c * H + h) * K;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tau = wv + kWaves * u;
+        if (tau < kTiles) {
+            const int m = tau / NTD, n = tau % NTD, d = 32 * n + col;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int k = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
+                if (k < K && d < dr) {
+                    p1[(base + k) * dr + d] = (double)a1[u][e];
+                    p2[(base + k) * dr + d] = (double)a2[u][e];
+                }
+            }
+        }
+    }
+    if (t < K) p0[base + t] = (double)s0;
+}
+
+template <typename T, int MT, int NTD>
+hipError_t launch_param_mfma_t(const Args& a, const BwdLayout& L, const float* dl, double* pmu, double* pvar,
+                               double* ppi) {
+    const gma_desc& d = a.d;
+    constexpr int GS = 32 * (MT + (MT % 2 == 0 ? 1 : 0)), XS = 32 * (NTD + (NTD % 2 == 0 ? 1 : 0));
+    const size_t lds = 32 * (sizeof(size_t) + sizeof(int)) + (size_t)32 * (GS + XS) * sizeof(float);
+    hipError_t e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_param_mfma<T, MT, NTD>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    bwd_param_mfma<T, MT, NTD><<<dim3((unsigned)d.H, (unsigned)L.chunks), dim3(kMfRowThreads), lds, a.stream>>>(
+        static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), dl, pmu, pvar, ppi, d.B, d.H, d.N, d.K, d.d_r,
+        L.per_chunk);
+    return hipGetLastError();
+}
+
+// MT = 32-component tiles (1, 2, 4, 8), NTD = 32-dim tiles (1, 2), at most 8 tiles.
+template <typename T>
+hipError_t launch_param_mfma(const Args& a, int MT, int NTD, const BwdLayout& L, const float* dl, double* pmu,
+                             double* pvar, double* ppi) {
+#define GMA_BWD_PP(mt, ntd) \
+    if (MT == mt && NTD == ntd) return launch_param_mfma_t<T, mt, ntd>(a, L, dl, pmu, pvar, ppi);
+    GMA_BWD_PP(1, 1) GMA_BWD_PP(1, 2) GMA_BWD_PP(2, 1) GMA_BWD_PP(2, 2)
+    GMA_BWD_PP(4, 1) GMA_BWD_PP(4, 2) GMA_BWD_PP(8, 1)
+#undef GMA_BWD_PP
+    return hipErrorInvalidValue;
+}
+
 template <typename T, typename A>
 hipError_t backward_t(const Args& a, const BwdArgs& g) {
     const gma_desc& d = a.d;
@@ -1377,12 +1491,27 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
         rec_end(a);
         if (e != hipSuccess) return e;
         rec_begin(a, "bwd_param_part");
-        const int ptiles = ((d.K + kPK - 1) / kPK) * ((d.d_r + kPD - 1) / kPD);
-        bwd_param_part<T, A><<<dim3((unsigned)ptiles, d.H, L.chunks), dim3(kBwdThreads), 0, a.stream>>>(
-            static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), dl, pmu, pvar, ppi, d.B, d.H, d.N, d.K, d.d_r,
-            L.per_chunk);
+        bool p_done = false;
+        if constexpr (sizeof(A) == sizeof(float)) {
+            // bf16 inputs: matrix-core sums for up to 8 output tiles (K <= 128 with d_r <= 64, or
+            // K <= 256 with d_r <= 32); 16 tiles leave one wave per SIMD and measured slower
+            // than the LDS-tiled kernel
+            const int MT = d.K <= 32 ? 1 : (d.K <= 64 ? 2 : (d.K <= 128 ? 4 : (d.K <= 256 ? 8 : 0)));
+            const int NTD = (d.d_r + 31) / 32;
+            if (MT > 0 && NTD <= 2 && MT * NTD <= 8) {
+                e = launch_param_mfma<T>(a, MT, NTD, L, dl, pmu, pvar, ppi);
+                p_done = true;
+            }
+        }
+        if (!p_done) {
+            const int ptiles = ((d.K + kPK - 1) / kPK) * ((d.d_r + kPD - 1) / kPD);
+            bwd_param_part<T, A><<<dim3((unsigned)ptiles, d.H, L.chunks), dim3(kBwdThreads), 0, a.stream>>>(
+                static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), dl, pmu, pvar, ppi, d.B, d.H, d.N, d.K,
+                d.d_r, L.per_chunk);
+            e = hipGetLastError();
+        }
         rec_end(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (e != hipSuccess) return e;
     }
     rec_begin(a, "bwd_param_final");
     bwd_param_final<<<dim3((unsigned)((d.K * d.d_r + kBwdThreads - 1) / kBwdThreads), d.H), dim3(kBwdThreads), 0,
