@@ -1331,7 +1331,7 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
 // (dl and x as float; strides padded as in bwd_seg_partial_mfma), the MT x NTD output tiles
 // dealt over the 4 waves, each v_mfma_f32_32x32x2_f32 step contracting one row per lane half
 // (x^2 formed from the staged x); S0 = sum dl by one thread per component, rows in order.
-// Grid (H, chunks).
+// Workgroup z takes components [32 MT z, 32 MT (z + 1)).  Grid (H, chunks, ceil(K / (32 MT))).
 template <typename T, int MT, int NTD>
 __global__ void __launch_bounds__(kMfRowThreads)
     bwd_param_mfma(const T* __restrict__ qr, const T* __restrict__ kr, const float* __restrict__ dl,
@@ -1345,7 +1345,7 @@ __global__ void __launch_bounds__(kMfRowThreads)
     float* sD = reinterpret_cast<float*>(sSide + 32);   // [32][GS]
     float* sX = sD + 32 * GS;                           // [32][XS]
     const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
-    const int h = blockIdx.x, c = blockIdx.y;
+    const int h = blockIdx.x, c = blockIdx.y, kz = 32 * MT * blockIdx.z;
     const int BH = B * H, BN = B * N;
     const int u0 = c * per_chunk, u1 = min(2 * BN, u0 + per_chunk);
     f32x16 a1[TPW], a2[TPW];
@@ -1365,7 +1365,7 @@ __global__ void __launch_bounds__(kMfRowThreads)
         for (int e = t; e < 32 * 32 * MT; e += kMfRowThreads) {
             const int r = e / (32 * MT), k = e % (32 * MT);
             const size_t drow = (size_t)sSide[r] * BH * N + sRow[r];
-            sD[r * GS + k] = (ub + r < u1 && k < K) ? dl[drow * K + k] : 0.0f;
+            sD[r * GS + k] = (ub + r < u1 && kz + k < K) ? dl[drow * K + kz + k] : 0.0f;
         }
         for (int e = t; e < 32 * 32 * NTD; e += kMfRowThreads) {
             const int r = e / (32 * NTD), d = e % (32 * NTD);
@@ -1400,7 +1400,7 @@ __global__ void __launch_bounds__(kMfRowThreads)
             const int m = tau / NTD, n = tau % NTD, d = 32 * n + col;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int k = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
+                const int k = kz + 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
                 if (k < K && d < dr) {
                     p1[(base + k) * dr + d] = (double)a1[u][e];
                     p2[(base + k) * dr + d] = (double)a2[u][e];
@@ -1408,7 +1408,7 @@ __global__ void __launch_bounds__(kMfRowThreads)
             }
         }
     }
-    if (t < K) p0[base + t] = (double)s0;
+    if (t < 32 * MT && kz + t < K) p0[base + kz + t] = (double)s0;
 }
 
 template <typename T, int MT, int NTD>
@@ -1421,20 +1421,21 @@ hipError_t launch_param_mfma_t(const Args& a, const BwdLayout& L, const float* d
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_param_mfma<T, MT, NTD>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
         return e;
-    bwd_param_mfma<T, MT, NTD><<<dim3((unsigned)d.H, (unsigned)L.chunks), dim3(kMfRowThreads), lds, a.stream>>>(
+    const unsigned kzs = (unsigned)((d.K + 32 * MT - 1) / (32 * MT));
+    bwd_param_mfma<T, MT, NTD><<<dim3((unsigned)d.H, (unsigned)L.chunks, kzs), dim3(kMfRowThreads), lds, a.stream>>>(
         static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), dl, pmu, pvar, ppi, d.B, d.H, d.N, d.K, d.d_r,
         L.per_chunk);
     return hipGetLastError();
 }
 
-// MT = 32-component tiles (1, 2, 4, 8), NTD = 32-dim tiles (1, 2), at most 8 tiles.
+// MT = 32-component tiles per workgroup (1, 2, 4), NTD = 32-dim tiles (1, 2).
 template <typename T>
 hipError_t launch_param_mfma(const Args& a, int MT, int NTD, const BwdLayout& L, const float* dl, double* pmu,
                              double* pvar, double* ppi) {
 #define GMA_BWD_PP(mt, ntd) \
     if (MT == mt && NTD == ntd) return launch_param_mfma_t<T, mt, ntd>(a, L, dl, pmu, pvar, ppi);
     GMA_BWD_PP(1, 1) GMA_BWD_PP(1, 2) GMA_BWD_PP(2, 1) GMA_BWD_PP(2, 2)
-    GMA_BWD_PP(4, 1) GMA_BWD_PP(4, 2) GMA_BWD_PP(8, 1)
+    GMA_BWD_PP(4, 1) GMA_BWD_PP(4, 2)
 #undef GMA_BWD_PP
     return hipErrorInvalidValue;
 }
@@ -1493,12 +1494,12 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
         rec_begin(a, "bwd_param_part");
         bool p_done = false;
         if constexpr (sizeof(A) == sizeof(float)) {
-            // bf16 inputs: matrix-core sums for up to 8 output tiles (K <= 128 with d_r <= 64, or
-            // K <= 256 with d_r <= 32); 16 tiles leave one wave per SIMD and measured slower
-            // than the LDS-tiled kernel
-            const int MT = d.K <= 32 ? 1 : (d.K <= 64 ? 2 : (d.K <= 128 ? 4 : (d.K <= 256 ? 8 : 0)));
+            // bf16 inputs: matrix-core sums, at most 4 component tiles per workgroup (more
+            // components are split over grid z: 16 tiles in one workgroup leave one wave per
+            // SIMD and measured slower than the LDS-tiled kernel), d_r <= 64
+            const int MT = d.K <= 32 ? 1 : (d.K <= 64 ? 2 : 4);
             const int NTD = (d.d_r + 31) / 32;
-            if (MT > 0 && NTD <= 2 && MT * NTD <= 8) {
+            if (NTD <= 2) {
                 e = launch_param_mfma<T>(a, MT, NTD, L, dl, pmu, pvar, ppi);
                 p_done = true;
             }
