@@ -233,12 +233,23 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
             float* gr = reinterpret_cast<float*>(side == 0 ? GQ : GK) + ((size_t)bh * N + t0 + col) * K;
             const int half = l >> 5;
             if (valid) {
+                // registers 4 q .. 4 q + 3 are 4 consecutive components: one 16-byte store when
+                // K is a multiple of 4 (rows then start on 16-byte boundaries)
+                const bool vec = (K & 3) == 0;
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int kc = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
-                        if (kc < K) gr[kc] = acc[m][e] * inv;
+                    for (int q = 0; q < 4; ++q) {
+                        const int kc = 32 * m + 8 * q + 4 * half;
+                        if (vec && kc < K) {
+                            *reinterpret_cast<float4*>(gr + kc) = make_float4(
+                                acc[m][4 * q] * inv, acc[m][4 * q + 1] * inv, acc[m][4 * q + 2] * inv,
+                                acc[m][4 * q + 3] * inv);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                if (kc + j < K) gr[kc + j] = acc[m][4 * q + j] * inv;
+                        }
                     }
             }
         } else if (t0 < n_end) {
