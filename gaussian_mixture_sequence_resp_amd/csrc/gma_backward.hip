@@ -1333,7 +1333,7 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
 // (x^2 formed from the staged x); S0 = sum dl by one thread per component, rows in order.
 // Workgroup z takes components [32 MT z, 32 MT (z + 1)).  Grid (H, chunks, ceil(K / (32 MT))).
 template <typename T, int MT, int NTD>
-__global__ void __launch_bounds__(kMfRowThreads)
+__global__ void __launch_bounds__(kMfRowThreads, 4)
     bwd_param_mfma(const T* __restrict__ qr, const T* __restrict__ kr, const float* __restrict__ dl,
                    double* __restrict__ p1, double* __restrict__ p2, double* __restrict__ p0, int B, int H, int N,
                    int K, int dr, int per_chunk) {
