@@ -400,8 +400,10 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Two waves per SIMD requested at MT = 4 (measured faster); smaller tiles keep the default
+// (there the bound made one instantiation spill).
 template <typename T, int PASS, int MT, int NTW>
-__global__ void __launch_bounds__(kMfRowThreads, 2)
+__global__ void __launch_bounds__(kMfRowThreads, MT == 4 ? 2 : 1)
     bwd_bidir_mfma(const float* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
                    float* __restrict__ gnum, float* __restrict__ gden, float* __restrict__ dl, T* __restrict__ dv_out,
                    const float* __restrict__ start, int BH, int N, int K, int dv, float eps, int SEG, int L) {
