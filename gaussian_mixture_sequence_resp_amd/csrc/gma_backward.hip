@@ -795,7 +795,9 @@ __global__ void __launch_bounds__(kBwdThreads)
 // v_mfma_f32_32x32x2_f32 over the components in blocks of 32; step i of a block contracts
 // component kb + 8 (i / 4) + 4 h + i % 4 of lane half h, so the B operand is the lane's own
 // dl register.  lam and mu lam of the head (float) sit in LDS as [32 ceil(K / 32)][32 NTD + 1].
-// Grid (ceil(N / 128), 2 BH); each wave takes 32 rows of the workgroup's 128.
+// Grid (ceil(N / (128 kXTiles)), 2 BH); each wave takes kXTiles tiles of 32 rows, one after
+// the other, against the one staged copy of lam and mu lam.
+constexpr int kXTiles = 4;
 template <typename T, int NTD>
 __global__ void __launch_bounds__(kMfRowThreads)
     bwd_x_mfma(const T* __restrict__ qr, const T* __restrict__ kr, const float* __restrict__ mu,
@@ -822,52 +824,54 @@ __global__ void __launch_bounds__(kMfRowThreads)
         sM[k * Ds + d] = mv;
     }
     __syncthreads();
-    const int row = blockIdx.x * 128 + 32 * wv + col;
-    const bool ok = row < N;
-    const size_t rr = (size_t)(ok ? row : N - 1);
-    const float* dl_r = dl + (((size_t)side * BH + bh) * N + rr) * K;
-    const bool vec_k = (K & 3) == 0;
-    f32x16 P[NTD], Q[NTD];
+    for (int rt = 0; rt < kXTiles; ++rt) {
+        const int row = blockIdx.x * (128 * kXTiles) + 128 * rt + 32 * wv + col;
+        const bool ok = row < N;
+        const size_t rr = (size_t)(ok ? row : N - 1);
+        const float* dl_r = dl + (((size_t)side * BH + bh) * N + rr) * K;
+        const bool vec_k = (K & 3) == 0;
+        f32x16 P[NTD], Q[NTD];
 #pragma unroll
-    for (int n = 0; n < NTD; ++n)
+        for (int n = 0; n < NTD; ++n)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) P[n][i] = Q[n][i] = 0.0f;
-    for (int kb = 0; kb < Kp; kb += 32) {
-        float g[16];
+            for (int i = 0; i < 16; ++i) P[n][i] = Q[n][i] = 0.0f;
+        for (int kb = 0; kb < Kp; kb += 32) {
+            float g[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int k0 = kb + 8 * q + 4 * half;
-            if (vec_k && k0 < K) {
-                const float4 x = *reinterpret_cast<const float4*>(dl_r + k0);
-                g[4 * q] = x.x;
-                g[4 * q + 1] = x.y;
-                g[4 * q + 2] = x.z;
-                g[4 * q + 3] = x.w;
-            } else {
+            for (int q = 0; q < 4; ++q) {
+                const int k0 = kb + 8 * q + 4 * half;
+                if (vec_k && k0 < K) {
+                    const float4 x = *reinterpret_cast<const float4*>(dl_r + k0);
+                    g[4 * q] = x.x;
+                    g[4 * q + 1] = x.y;
+                    g[4 * q + 2] = x.z;
+                    g[4 * q + 3] = x.w;
+                } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) g[4 * q + j] = k0 + j < K ? dl_r[k0 + j] : 0.0f;
+                    for (int j = 0; j < 4; ++j) g[4 * q + j] = k0 + j < K ? dl_r[k0 + j] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int k = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+#pragma unroll
+                for (int n = 0; n < NTD; ++n) {
+                    P[n] = mfma_f32(sL[k * Ds + 32 * n + col], g[i], P[n]);
+                    Q[n] = mfma_f32(sM[k * Ds + 32 * n + col], g[i], Q[n]);
+                }
             }
         }
+        if (!ok) continue;
+        const T* x = (side == 0 ? qr : kr) + ((size_t)bh * N + rr) * dr;
+        T* dx = (side == 0 ? dqr : dkr) + ((size_t)bh * N + rr) * dr;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int k = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+        for (int n = 0; n < NTD; ++n)
 #pragma unroll
-            for (int n = 0; n < NTD; ++n) {
-                P[n] = mfma_f32(sL[k * Ds + 32 * n + col], g[i], P[n]);
-                Q[n] = mfma_f32(sM[k * Ds + 32 * n + col], g[i], Q[n]);
+            for (int i = 0; i < 16; ++i) {
+                const int d = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
+                if (d < dr) Elem<T>::store(dx, d, Q[n][i] - Elem<T>::load(x, d) * P[n][i]);
             }
-        }
     }
-    if (!ok) return;
-    const T* x = (side == 0 ? qr : kr) + ((size_t)bh * N + rr) * dr;
-    T* dx = (side == 0 ? dqr : dkr) + ((size_t)bh * N + rr) * dr;
-#pragma unroll
-    for (int n = 0; n < NTD; ++n)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int d = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (d < dr) Elem<T>::store(dx, d, Q[n][i] - Elem<T>::load(x, d) * P[n][i]);
-        }
 }
 
 template <typename T, int NTD>
@@ -879,7 +883,8 @@ hipError_t launch_x_mfma_t(const Args& a, const BwdArgs& g, const double* lam, c
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_x_mfma<T, NTD>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
         return e;
-    bwd_x_mfma<T, NTD><<<dim3((unsigned)((d.N + 127) / 128), (unsigned)(2 * BH)), dim3(kMfRowThreads), lds, a.stream>>>(
+    const unsigned gx = (unsigned)((d.N + 128 * kXTiles - 1) / (128 * kXTiles));
+    bwd_x_mfma<T, NTD><<<dim3(gx, (unsigned)(2 * BH)), dim3(kMfRowThreads), lds, a.stream>>>(
         static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), a.mu, lam, dl, static_cast<T*>(g.dqr),
         static_cast<T*>(g.dkr), BH, d.H, d.N, d.K, d.d_r);
     return hipGetLastError();
