@@ -392,7 +392,10 @@ __global__ void __launch_bounds__(kRowThreads)
 // i % 4 of row l % 32): gamma feeds C1 and the dl epilogue from the same registers, and C1
 // after the epilogue is the B operand of C2.  St sits in LDS as [32 MT][32 NTW + 1], zero
 // padded; the odd row length puts 32 consecutive rows of one column in distinct banks.
+// Grid (BH ceil(N / RB)): a workgroup takes RB rows of one head, its waves 32-row tiles in
+// turn, all against the one staged copy of the head's total (slot 0 of its SEG segments).
 constexpr int kMfRowThreads = 256;
+constexpr int kMfRowBlock = 512;  // rows per workgroup of bwd_bidir_mfma: 4 tiles per wave
 using mf::f32x16;
 using mf::sum_halves;
 
@@ -406,12 +409,13 @@ template <typename T, int PASS, int MT, int NTW>
 __global__ void __launch_bounds__(kMfRowThreads, MT == 4 ? 2 : 1)
     bwd_bidir_mfma(const float* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
                    float* __restrict__ gnum, float* __restrict__ gden, float* __restrict__ dl, T* __restrict__ dv_out,
-                   const float* __restrict__ start, int BH, int N, int K, int dv, float eps, int SEG, int L) {
+                   const float* __restrict__ start, int BH, int N, int K, int dv, float eps, int SEG, int RB) {
     extern __shared__ double smem_d[];
     float* sS = reinterpret_cast<float*>(smem_d);
     constexpr int Kp = 32 * MT, Wp = 32 * NTW, Ws = Wp + 1;
     const int W = dv + 1;
-    const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
+    const int NB = (N + RB - 1) / RB;
+    const int bs = blockIdx.x, bh = bs / NB, blk = bs % NB;
     const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
     const float* st0 = start + (size_t)bh * SEG * K * W;  // slot 0: the head's total
     for (int e = t; e < Kp * Wp; e += kMfRowThreads) {
@@ -422,7 +426,7 @@ __global__ void __launch_bounds__(kMfRowThreads, MT == 4 ? 2 : 1)
     const size_t side = PASS == 1 ? 0 : (size_t)BH;
     const float* g_bh = gamma + (side + bh) * N * K;
     float* dl_bh = dl + (side + bh) * N * K;
-    const int i0 = seg * L, i1 = min(N, i0 + L);
+    const int i0 = blk * RB, i1 = min(N, i0 + RB);
     const bool vec_k = (K & 3) == 0;
     for (int tb = i0 + 32 * wv; tb < i1; tb += 32 * (kMfRowThreads / 64)) {
         const int row = tb + col;
@@ -1126,9 +1130,10 @@ hipError_t launch_bidir_mfma_t(const Args& a, const BwdArgs& g, const float* gam
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_bidir_mfma<T, PASS, MT, NTW>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
         return e;
-    bwd_bidir_mfma<T, PASS, MT, NTW><<<dim3((unsigned)(BH * L.seg)), dim3(kMfRowThreads), lds, a.stream>>>(
+    const int nb = (d.N + kMfRowBlock - 1) / kMfRowBlock;
+    bwd_bidir_mfma<T, PASS, MT, NTW><<<dim3((unsigned)(BH * nb)), dim3(kMfRowThreads), lds, a.stream>>>(
         gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
-        start, BH, d.N, d.K, d.d_v, a.eps, L.seg, L.seg_len);
+        start, BH, d.N, d.K, d.d_v, a.eps, L.seg, kMfRowBlock);
     return hipGetLastError();
 }
 
