@@ -132,6 +132,49 @@ def _dtype_name(t) -> str:
     raise GMAError(-3, f"unsupported dtype {t.dtype}")
 
 
+GMA_ERR_DEVICE = -101  # binding only: a tensor is not on the GPU that holds qr (or x)
+
+
+def _check(specs, device_of):
+    """Validate every tensor argument before any library call: ``specs`` lists
+    (name, tensor, expected shape or None for any, expected torch dtype or None, required).
+    Shapes and dtypes are checked first (status -2 / -3, as the library would report for
+    its own descriptor), then that every tensor lives on the CUDA device of ``device_of``
+    (-101): a host pointer or another device's memory would be read by the kernels."""
+    for name, t, shape, dtype, required in specs:
+        if t is None:
+            if required:
+                raise GMAError(-1, f"{name} is required")
+            continue
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise GMAError(-2, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if dtype is not None and t.dtype != dtype:
+            raise GMAError(-3, f"{name} has dtype {t.dtype}, expected {dtype}")
+    dev = device_of.device
+    if dev.type != "cuda":
+        raise GMAError(GMA_ERR_DEVICE, f"tensors must be on a GPU (got {dev})")
+    for name, t, _, _, _ in specs:
+        if t is not None and t.device != dev:
+            raise GMAError(GMA_ERR_DEVICE, f"{name} is on {t.device}, expected {dev}")
+
+
+def _need4(name, t):
+    if t.dim() != 4:
+        raise GMAError(-2, f"{name} must be 4-D, got shape {tuple(t.shape)}")
+
+
+def _params_specs(H, K, d_r, mu, var_raw, prior_logits):
+    import torch
+    return [("mu", mu, (H, K, d_r), torch.float32, True),
+            ("var_raw", var_raw, (H, K, d_r), torch.float32, True),
+            ("prior_logits", prior_logits, (H, K), torch.float32, True)]
+
+
+def _ws_spec(workspace):
+    import torch
+    return [("workspace", workspace, None, torch.uint8, False)]
+
+
 def forward(qr, kr, v, mu, var_raw, prior_logits, causal: bool = False, eps: float = 1e-6,
             var_floor: float = 1e-3, out=None, gamma_out=None, workspace=None,
             algo: str = "auto", stream=None, events=None, names=None):
@@ -143,12 +186,21 @@ def forward(qr, kr, v, mu, var_raw, prior_logits, causal: bool = False, eps: flo
     Gamma_K.  ``workspace`` (optional, uint8 device tensor) is allocated if not given.
     """
     import torch
-    lib = load_library()
-    _dense(qr, kr, v, mu, var_raw, prior_logits, out, gamma_out)
+    _need4("qr", qr)
+    _need4("v", v)
     B, H, N, d_r = qr.shape
     d_v = v.shape[-1]
+    if mu.dim() != 3:
+        raise GMAError(-2, f"mu must be [H, K, d_r], got shape {tuple(mu.shape)}")
     K = mu.shape[1]
     dt = _dtype_name(qr)
+    _check([("qr", qr, None, None, True), ("kr", kr, (B, H, N, d_r), qr.dtype, True),
+            ("v", v, (B, H, N, d_v), qr.dtype, True)]
+           + _params_specs(H, K, d_r, mu, var_raw, prior_logits)
+           + [("out", out, (B, H, N, d_v), qr.dtype, False),
+              ("gamma_out", gamma_out, (2, B, H, N, K), torch.float32, False)] + _ws_spec(workspace), qr)
+    _dense(qr, kr, v, mu, var_raw, prior_logits, out, gamma_out)
+    lib = load_library()
     desc = make_desc(B, H, N, d_r, d_v, K, dt, var_floor, algo)
     if out is None:
         out = torch.empty((B, H, N, d_v), dtype=qr.dtype, device=qr.device)
@@ -185,13 +237,28 @@ def forward_cross(qr, kr, v, mu, var_raw, prior_logits, eps: float = 1e-6, var_f
     Returns ``out`` [B,H,Nq,d_v].  ``gamma_out`` (optional, float32, B*H*(Nq+Nk)*K
     elements) receives Gamma_Q [B,H,Nq,K] followed by Gamma_K [B,H,Nk,K]."""
     import torch
-    lib = load_library()
-    _dense(qr, kr, v, mu, var_raw, prior_logits, out, gamma_out)
+    _need4("qr", qr)
+    _need4("kr", kr)
+    _need4("v", v)
     B, H, Nq, d_r = qr.shape
     Nk = kr.shape[2]
     d_v = v.shape[-1]
+    if mu.dim() != 3:
+        raise GMAError(-2, f"mu must be [H, K, d_r], got shape {tuple(mu.shape)}")
     K = mu.shape[1]
-    desc = make_desc(B, H, Nq, d_r, d_v, K, _dtype_name(qr), var_floor, algo)
+    dt = _dtype_name(qr)
+    gamma_shape = None if gamma_out is None else (gamma_out.numel(),)
+    if gamma_out is not None and gamma_out.numel() != B * H * (Nq + Nk) * K:
+        raise GMAError(-2, f"gamma_out has {gamma_out.numel()} elements, expected {B * H * (Nq + Nk) * K}")
+    _check([("qr", qr, None, None, True), ("kr", kr, (B, H, Nk, d_r), qr.dtype, True),
+            ("v", v, (B, H, Nk, d_v), qr.dtype, True)]
+           + _params_specs(H, K, d_r, mu, var_raw, prior_logits)
+           + [("out", out, (B, H, Nq, d_v), qr.dtype, False),
+              ("gamma_out", None if gamma_out is None else gamma_out.reshape(-1), gamma_shape, torch.float32,
+               False)] + _ws_spec(workspace), qr)
+    _dense(qr, kr, v, mu, var_raw, prior_logits, out, gamma_out)
+    lib = load_library()
+    desc = make_desc(B, H, Nq, d_r, d_v, K, dt, var_floor, algo)
     if out is None:
         out = torch.empty((B, H, Nq, d_v), dtype=qr.dtype, device=qr.device)
     need = int(lib.gma_workspace_size_cross(ctypes.byref(desc), Nk))
@@ -228,12 +295,20 @@ def memory(kr, v, mu, var_raw, prior_logits, var_floor: float = 1e-3, state=None
     """Causal memory [S | z] of the N positions of kr [B,H,N,d_r], v [B,H,N,d_v]:
     returns ``state`` float32 [B,H,K,d_v+1] (row k: S[k, :d_v], z[k])."""
     import torch
-    lib = load_library()
-    _dense(kr, v, mu, var_raw, prior_logits, state)
+    _need4("kr", kr)
+    _need4("v", v)
     B, H, N, d_r = kr.shape
     d_v = v.shape[-1]
+    if mu.dim() != 3:
+        raise GMAError(-2, f"mu must be [H, K, d_r], got shape {tuple(mu.shape)}")
     K = mu.shape[1]
-    desc = make_desc(B, H, N, d_r, d_v, K, _dtype_name(kr), var_floor, algo)
+    dt = _dtype_name(kr)
+    _check([("kr", kr, None, None, True), ("v", v, (B, H, N, d_v), kr.dtype, True)]
+           + _params_specs(H, K, d_r, mu, var_raw, prior_logits)
+           + [("state", state, (B, H, K, d_v + 1), torch.float32, False)] + _ws_spec(workspace), kr)
+    _dense(kr, v, mu, var_raw, prior_logits, state)
+    lib = load_library()
+    desc = make_desc(B, H, N, d_r, d_v, K, dt, var_floor, algo)
     if state is None:
         state = torch.empty((B, H, K, d_v + 1), dtype=torch.float32, device=kr.device)
     need = int(lib.gma_memory_workspace_size(ctypes.byref(desc)))
@@ -255,13 +330,26 @@ def decode_step(qr, kr, v, mu, var_raw, prior_logits, state, eps: float = 1e-6, 
     """One causal decode step: qr, kr [B,H,1,d_r] (or [B,H,d_r]), v [B,H,1,d_v] (or [B,H,d_v]);
     ``state`` float32 [B,H,K,d_v+1] is updated in place; returns out [B,H,1,d_v]."""
     import torch
-    lib = load_library()
-    qr, kr, v = qr.contiguous(), kr.contiguous(), v.contiguous()  # one row per (b, h): cheap
-    _dense(mu, var_raw, prior_logits, state, out)
+    if qr.dim() not in (3, 4) or (qr.dim() == 4 and qr.shape[2] != 1):
+        raise GMAError(-2, f"qr must be [B, H, 1, d_r] or [B, H, d_r], got shape {tuple(qr.shape)}")
     B, H = qr.shape[0], qr.shape[1]
     d_r, d_v = qr.shape[-1], v.shape[-1]
+    if mu.dim() != 3:
+        raise GMAError(-2, f"mu must be [H, K, d_r], got shape {tuple(mu.shape)}")
     K = mu.shape[1]
-    desc = make_desc(B, H, 1, d_r, d_v, K, _dtype_name(qr), var_floor, algo)
+    dt = _dtype_name(qr)
+    row = (lambda t: None if t is None else t.reshape(t.shape[0], t.shape[1], -1) if t.dim() in (3, 4) else t)
+    if kr.dim() not in (3, 4) or v.dim() not in (3, 4):
+        raise GMAError(-2, "kr and v must be [B, H, 1, d] or [B, H, d]")
+    _check([("qr", row(qr), None, None, True), ("kr", row(kr), (B, H, d_r), qr.dtype, True),
+            ("v", row(v), (B, H, d_v), qr.dtype, True)]
+           + _params_specs(H, K, d_r, mu, var_raw, prior_logits)
+           + [("state", state, (B, H, K, d_v + 1), torch.float32, True),
+              ("out", out, (B, H, 1, d_v), qr.dtype, False)] + _ws_spec(workspace), qr)
+    qr, kr, v = qr.contiguous(), kr.contiguous(), v.contiguous()  # one row per (b, h): cheap
+    _dense(mu, var_raw, prior_logits, state, out)
+    lib = load_library()
+    desc = make_desc(B, H, 1, d_r, d_v, K, dt, var_floor, algo)
     if out is None:
         out = torch.empty((B, H, 1, d_v), dtype=qr.dtype, device=qr.device)
     need = int(lib.gma_decode_workspace_size(ctypes.byref(desc)))
@@ -285,12 +373,18 @@ def resp_stats(x, mu, var_raw, prior_logits, var_floor: float = 1e-3, with_hard:
     with ``with_hard``), ``counts`` int32 [H,K], ``usage`` float32 [H,K], ``used`` int32 [H],
     ``entropy`` float32 [H] (hard-usage entropy over ln K)."""
     import torch
-    lib = load_library()
-    _dense(x, mu, var_raw, prior_logits)
+    _need4("x", x)
     B, H, N, d_r = x.shape
+    if mu.dim() != 3:
+        raise GMAError(-2, f"mu must be [H, K, d_r], got shape {tuple(mu.shape)}")
     K = mu.shape[1]
+    dt = _dtype_name(x)
+    _check([("x", x, None, None, True)] + _params_specs(H, K, d_r, mu, var_raw, prior_logits) + _ws_spec(workspace),
+           x)
+    _dense(x, mu, var_raw, prior_logits)
+    lib = load_library()
     dev = x.device
-    desc = make_desc(B, H, N, d_r, 1, K, _dtype_name(x), var_floor, algo)
+    desc = make_desc(B, H, N, d_r, 1, K, dt, var_floor, algo)
     res = {
         "hard": torch.empty((B, H, N), dtype=torch.int32, device=dev) if with_hard else None,
         "counts": torch.empty((H, K), dtype=torch.int32, device=dev),
@@ -319,12 +413,21 @@ def backward(qr, kr, v, mu, var_raw, prior_logits, dout, causal: bool, eps: floa
     """Gradients of L = sum(dout * O) for gma_forward: ``dqr``, ``dkr``, ``dv`` (input dtype,
     shapes of qr, kr, v) and ``dmu``, ``dvar_raw`` [H,K,d_r], ``dprior`` [H,K] (float32)."""
     import torch
-    lib = load_library()
-    _dense(qr, kr, v, mu, var_raw, prior_logits, dout)
+    _need4("qr", qr)
+    _need4("v", v)
     B, H, N, d_r = qr.shape
     d_v = v.shape[-1]
+    if mu.dim() != 3:
+        raise GMAError(-2, f"mu must be [H, K, d_r], got shape {tuple(mu.shape)}")
     K = mu.shape[1]
-    desc = make_desc(B, H, N, d_r, d_v, K, _dtype_name(qr), var_floor, algo)
+    dt = _dtype_name(qr)
+    _check([("qr", qr, None, None, True), ("kr", kr, (B, H, N, d_r), qr.dtype, True),
+            ("v", v, (B, H, N, d_v), qr.dtype, True)]
+           + _params_specs(H, K, d_r, mu, var_raw, prior_logits)
+           + [("dout", dout, (B, H, N, d_v), qr.dtype, True)] + _ws_spec(workspace), qr)
+    _dense(qr, kr, v, mu, var_raw, prior_logits, dout)
+    lib = load_library()
+    desc = make_desc(B, H, N, d_r, d_v, K, dt, var_floor, algo)
     g = {"dqr": torch.empty_like(qr), "dkr": torch.empty_like(kr), "dv": torch.empty_like(v),
          "dmu": torch.empty_like(mu), "dvar_raw": torch.empty_like(var_raw), "dprior": torch.empty_like(prior_logits)}
     need = int(lib.gma_backward_workspace_size(ctypes.byref(desc), 1 if causal else 0))

@@ -1,4 +1,5 @@
-// Backward of the GMA forward mixer (bidirectional and causal), SIMT kernels.
+// Backward of the GMA forward mixer (bidirectional and causal): SIMT kernels, with fp32
+// matrix-core forms of the row passes, dx and the parameter sums for bf16 inputs.
 //
 // Method: Gaussian Mixture Attention (arXiv 2606.18283).  The mixture parameters are trained
 // end to end by backpropagation ("Core mechanism" item 3); the pages analyse the gradients'
@@ -1541,7 +1542,11 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
 
 size_t backward_workspace(const gma_desc& d) { return bwd_layout(d).total; }
 
-bool backward_supported(const gma_desc& d) { return scan_scratch(d) <= kScanLdsMax; }
+// The row passes index both sides of the batch's rows of a head, 2 B N, in int.
+bool backward_supported(const gma_desc& d) {
+    if (2 * (int64_t)d.B * d.N > INT32_MAX) return false;
+    return scan_scratch(d) <= kScanLdsMax;
+}
 
 hipError_t backward_run(const Args& a, const BwdArgs& g) {
     return a.d.dtype == GMA_F32 ? backward_t<float, double>(a, g) : backward_t<bf16_t, float>(a, g);

@@ -633,7 +633,17 @@ hipError_t mfma_forward(const Args& a) {
     hipError_t e = a.causal ? causal_forward(a) : bidir_forward(a);
     if (e != hipSuccess) return e;
     if (a.gamma_out) {
-        // diagnostic responsibilities (float32), outside the fused path
+        // diagnostic responsibilities (float32), outside the fused path: for self-mixing
+        // shapes the responsibilities kernel gives them from the same matrix-core logits (the
+        // five-pass split contraction) as the fused kernels, so they show what the fused path
+        // routes; the cross variant (two lengths) takes the SIMT kernel's double logits
+        if (a.Nk == d.N && stats_supported(d)) {
+            // both workspace layouts open with the coefficient block W, then c
+            const Geo g = geometry(d);
+            bf16_t* W = reinterpret_cast<bf16_t*>(a.ws);
+            float* cvec = reinterpret_cast<float*>(a.ws + align_up((size_t)d.H * g.Kp * 4 * g.Dp * sizeof(bf16_t)));
+            return resp_rows(a, W, cvec, a.gamma_out);
+        }
         const size_t off = a.causal ? causal_workspace(d) : mfma_layout(d, a.Nk).total;
         double* lam = reinterpret_cast<double*>(a.ws + off);
         double* cst = reinterpret_cast<double*>(a.ws + off + align_up((size_t)d.H * d.K * d.d_r * sizeof(double)));

@@ -207,12 +207,17 @@ int gma_decode_step(const void* qr, const void* kr, const void* v, const float* 
  * batch and both sides, dL/dmu, dL/dvar_raw [H,K,d_r] and dL/dprior_logits [H,K] (float32;
  * all outputs are overwritten, not accumulated).  Same inputs, causal flag, eps and layout
  * as gma_forward; the forward is recomputed inside.  The gradients are the chain rule of the
- * forward: see the kernels' source for the formulas.  The responsibilities come from the
- * matrix-core responsibilities kernel for bf16 inputs it covers (else the SIMT one); the
- * passes over the rows are SIMT kernels (algo AUTO or SIMT; an explicit MFMA request returns
- * GMA_ERR_UNSUPPORTED).  Sums accumulate in double for float32 inputs and in float for bf16
- * (chunk sums of the parameter gradients combined in double); every sum has a fixed order,
- * so results are deterministic.  Every shape within the limits is supported.
+ * forward: see the kernels' source for the formulas.  For bf16 inputs the responsibilities
+ * come from the matrix-core responsibilities kernel where it covers the shape (else the SIMT
+ * one), and the passes over the rows, dqr/dkr and the parameter sums run as fp32 matrix-core
+ * products (the causal segment walk stays a SIMT kernel); float32 inputs run SIMT kernels
+ * throughout.  algo SIMT only makes bf16 inputs take their responsibilities from the SIMT
+ * kernel (double logits); the other kernels are those of AUTO.  An explicit MFMA request
+ * returns GMA_ERR_UNSUPPORTED.  Sums accumulate in
+ * double for float32 inputs and in float for bf16 (chunk sums of the parameter gradients
+ * combined in double); every sum has a fixed order, so results are deterministic.  Every
+ * shape within the limits is supported, except 2 B N > INT32_MAX (the row passes index both
+ * sides of a head's rows in 32 bits): GMA_ERR_UNSUPPORTED and a workspace size of 0.
  * Alignment, aliasing and status codes as gma_forward (no output may overlap an input, the
  * workspace or another output).  N = 0 gives zero parameter gradients.
  */

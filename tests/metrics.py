@@ -43,3 +43,29 @@ def globalrel(out, ref) -> float:
 
 def tol_for(dtype: str) -> float:
     return FP32_TOL if dtype == "f32" else BF16_TOL
+
+
+# Responsibilities of the matrix-core path (bf16 inputs): the logits come from the five-pass
+# split contraction in fp32, so each gamma carries the logit error as a relative error:
+# log2(g_k / r_k) = dl_k - log2(sum_j r_j 2^dl_j), at most 2 max_k |dl_k| (log2 units).
+# The check takes entries whose reference is at least GAMMA_FLOOR (below it the fp32
+# rounding of tiny values, not the logits, dominates; those entries are held to an
+# absolute bound instead).  The bound on |log2(g/r)| is measured against what the split
+# must deliver: a dropped hi/lo pass or a single bf16 operand gives logit errors of
+# 0.1 to several units, far above it.
+GAMMA_FLOOR = 1e-3
+GAMMA_LOG2_TOL_BF16 = 2e-2
+GAMMA_ABS_TOL_BF16 = 2e-5
+
+
+def gamma_errors(g, ref):
+    """(max |log2(g / ref)| over ref >= GAMMA_FLOOR, max |g - ref| over ref < GAMMA_FLOOR)."""
+    gg, r = _np(g), _np(ref)
+    assert gg.shape == r.shape, (gg.shape, r.shape)
+    big = r >= GAMMA_FLOOR
+    lr = 0.0
+    if big.any():
+        with np.errstate(divide="ignore"):
+            lr = float(np.abs(np.log2(np.maximum(gg[big], 1e-300) / r[big])).max())
+    ab = float(np.abs(gg[~big] - r[~big]).max()) if (~big).any() else 0.0
+    return lr, ab

@@ -297,3 +297,101 @@ def test_backward_validation(lib):
     assert sz(ctypes.byref(d), 0) > 0 and sz(ctypes.byref(d), 1) > 0
     assert sz(ctypes.byref(d), 2) == 0
     assert sz(ctypes.byref(binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "mfma")), 0) == 0
+    # 2 B N above INT32_MAX (B H N itself within it): the row passes would overflow their
+    # 32-bit row index, so the shape is refused with a workspace size of 0
+    big = binding.make_desc(1 << 15, 1, (1 << 15) + 1, 16, 8, 12, "bf16", 1e-3, "auto")
+    assert sz(ctypes.byref(big), 0) == 0 and sz(ctypes.byref(big), 1) == 0
+    assert call(big) == C["GMA_ERR_UNSUPPORTED"]
+    ok = binding.make_desc(1 << 14, 1, (1 << 16) - 1, 16, 8, 12, "bf16", 1e-3, "auto")  # 2 B N < 2^31
+    assert sz(ctypes.byref(ok), 0) > 0
+
+
+# ---- Python binding: every tensor argument is validated before any library call, so a
+# mismatched shape, dtype or device raises GMAError instead of letting a kernel read or write
+# out of bounds (or dereference a host pointer).  All tensors here are CPU tensors: the shape
+# and dtype checks fire first, and a call that passes them fails on the device check.
+
+torch = pytest.importorskip("torch")
+
+
+def _fwd_inputs(B=2, H=3, N=16, dr=8, dv=8, K=4, dt=None):
+    dt = dt or torch.bfloat16
+    return dict(qr=torch.zeros(B, H, N, dr, dtype=dt), kr=torch.zeros(B, H, N, dr, dtype=dt),
+                v=torch.zeros(B, H, N, dv, dtype=dt), mu=torch.zeros(H, K, dr),
+                var_raw=torch.zeros(H, K, dr), prior_logits=torch.zeros(H, K))
+
+
+def _code(fn, *a, **kw):
+    with pytest.raises(binding.GMAError) as ei:
+        fn(*a, **kw)
+    return ei.value.code
+
+
+@pytest.mark.parametrize("field,bad", [
+    ("kr", lambda t: t[:, :, :-1].contiguous()),          # shorter key sequence
+    ("kr", lambda t: t[..., :-1].contiguous()),           # other routing dim
+    ("v", lambda t: t[:, :, :-2].contiguous()),           # fewer value rows
+    ("mu", lambda t: t[:, :-1].contiguous()),             # other K than var_raw
+    ("var_raw", lambda t: t[:, :, :-1].contiguous()),     # other d_r
+    ("prior_logits", lambda t: t[:, :-1].contiguous()),   # other K
+    ("mu", lambda t: t[:-1].contiguous()),                # fewer heads
+])
+def test_binding_rejects_shape_mismatch(field, bad):
+    inp = _fwd_inputs()
+    inp[field] = bad(inp[field])
+    assert _code(binding.forward, **inp) == -2
+    if field not in ("kr",):
+        assert _code(binding.backward, **inp, dout=torch.zeros(2, 3, 16, 8, dtype=torch.bfloat16),
+                     causal=False) == -2
+
+
+@pytest.mark.parametrize("field,dt", [("v", torch.float32), ("kr", torch.float32), ("mu", torch.bfloat16),
+                                      ("var_raw", torch.float64), ("prior_logits", torch.bfloat16)])
+def test_binding_rejects_dtype_mismatch(field, dt):
+    inp = _fwd_inputs()
+    inp[field] = inp[field].to(dt)
+    assert _code(binding.forward, **inp) == -3
+    assert _code(binding.backward, **inp, dout=torch.zeros(2, 3, 16, 8, dtype=torch.bfloat16), causal=True) == -3
+
+
+def test_binding_rejects_bad_outputs_and_buffers():
+    inp = _fwd_inputs()
+    assert _code(binding.forward, **inp, out=torch.zeros(2, 3, 16, 7, dtype=torch.bfloat16)) == -2
+    assert _code(binding.forward, **inp, out=torch.zeros(2, 3, 16, 8)) == -3
+    assert _code(binding.forward, **inp, gamma_out=torch.zeros(2, 2, 3, 16, 5)) == -2
+    assert _code(binding.forward, **inp, gamma_out=torch.zeros(2, 2, 3, 16, 4, dtype=torch.float64)) == -3
+    assert _code(binding.forward, **inp, workspace=torch.zeros(16, dtype=torch.float32)) == -3
+    assert _code(binding.backward, **inp, dout=torch.zeros(2, 3, 15, 8, dtype=torch.bfloat16), causal=False) == -2
+    # cross: keys of another length are fine, value rows must match the keys
+    x = _fwd_inputs()
+    x["kr"] = torch.zeros(2, 3, 40, 8, dtype=torch.bfloat16)
+    x["v"] = torch.zeros(2, 3, 39, 8, dtype=torch.bfloat16)
+    assert _code(binding.forward_cross, **x) == -2
+    x["v"] = torch.zeros(2, 3, 40, 8, dtype=torch.bfloat16)
+    assert _code(binding.forward_cross, **x, gamma_out=torch.zeros(2 * 3 * 16 * 4)) == -2
+    # memory, decode and statistics
+    m = _fwd_inputs()
+    assert _code(binding.memory, m["kr"], m["v"], m["mu"], m["var_raw"], m["prior_logits"],
+                 state=torch.zeros(2, 3, 4, 8)) == -2
+    assert _code(binding.decode_step, m["qr"][:, :, :1], m["kr"][:, :, :1], m["v"][:, :, :1], m["mu"],
+                 m["var_raw"], m["prior_logits"], torch.zeros(2, 3, 4, 8)) == -2
+    assert _code(binding.decode_step, m["qr"][:, :, :2], m["kr"][:, :, :1], m["v"][:, :, :1], m["mu"],
+                 m["var_raw"], m["prior_logits"], torch.zeros(2, 3, 4, 9)) == -2
+    assert _code(binding.resp_stats, m["kr"], m["mu"][:, :, :4].contiguous(), m["var_raw"],
+                 m["prior_logits"]) == -2
+
+
+def test_binding_rejects_host_tensors():
+    """Well-formed arguments that live in host memory: refused before the library sees a
+    host pointer (which a kernel would fault on)."""
+    inp = _fwd_inputs()
+    assert _code(binding.forward, **inp) == binding.GMA_ERR_DEVICE
+    assert _code(binding.forward_cross, **inp) == binding.GMA_ERR_DEVICE
+    assert _code(binding.backward, **inp, dout=torch.zeros(2, 3, 16, 8, dtype=torch.bfloat16),
+                 causal=False) == binding.GMA_ERR_DEVICE
+    assert _code(binding.memory, inp["kr"], inp["v"], inp["mu"], inp["var_raw"],
+                 inp["prior_logits"]) == binding.GMA_ERR_DEVICE
+    assert _code(binding.resp_stats, inp["kr"], inp["mu"], inp["var_raw"],
+                 inp["prior_logits"]) == binding.GMA_ERR_DEVICE
+    assert _code(binding.decode_step, inp["qr"][:, :, :1], inp["kr"][:, :, :1], inp["v"][:, :, :1], inp["mu"],
+                 inp["var_raw"], inp["prior_logits"], torch.zeros(2, 3, 4, 9)) == binding.GMA_ERR_DEVICE
