@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     decode_step,
     forward,
     forward_cross,
+    forward_noalloc,
     load_library,
     make_desc,
     memory,

@@ -84,6 +84,9 @@ def load_library(path: Optional[str] = None):
     lib.gma_stats_workspace_size.restype = sz
     lib.gma_resp_stats.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(GmaDesc), vp, sz, vp]
     lib.gma_resp_stats.restype = ctypes.c_int
+    lib.gma_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp,
+                                        ctypes.POINTER(GmaDesc), vp]
+    lib.gma_forward_noalloc.restype = ctypes.c_int
     lib.gma_strerror.argtypes = [ctypes.c_int]
     lib.gma_strerror.restype = ctypes.c_char_p
     lib.gma_version.argtypes = []
@@ -225,6 +228,37 @@ def forward(qr, kr, v, mu, var_raw, prior_logits, causal: bool = False, eps: flo
         nk = ctypes.c_int(0)
         st = lib.gma_forward_timed(*args, events, len(events), names, ctypes.byref(nk))
         forward.last_kernel_count = nk.value
+    if st != GMA_OK:
+        raise GMAError(st, strerror(st))
+    return out
+
+
+def forward_noalloc(qr, kr, v, mu, var_raw, prior_logits, out, causal: bool = False, eps: float = 1e-6,
+                    var_floor: float = 1e-3, gamma_out=None, algo: str = "auto", stream=None):
+    """gma_forward_noalloc: the forward with the library's static scratch (no workspace,
+    nothing allocated by the call).  ``out`` [B,H,N,d_v] must be given (preallocated)."""
+    import torch
+    _need4("qr", qr)
+    _need4("v", v)
+    B, H, N, d_r = qr.shape
+    d_v = v.shape[-1]
+    if mu.dim() != 3:
+        raise GMAError(-2, f"mu must be [H, K, d_r], got shape {tuple(mu.shape)}")
+    K = mu.shape[1]
+    dt = _dtype_name(qr)
+    _check([("qr", qr, None, None, True), ("kr", kr, (B, H, N, d_r), qr.dtype, True),
+            ("v", v, (B, H, N, d_v), qr.dtype, True)]
+           + _params_specs(H, K, d_r, mu, var_raw, prior_logits)
+           + [("out", out, (B, H, N, d_v), qr.dtype, True),
+              ("gamma_out", gamma_out, (2, B, H, N, K), torch.float32, False)], qr)
+    _dense(qr, kr, v, mu, var_raw, prior_logits, out, gamma_out)
+    lib = load_library()
+    desc = make_desc(B, H, N, d_r, d_v, K, dt, var_floor, algo)
+    if stream is None:
+        stream = torch.cuda.current_stream(qr.device).cuda_stream
+    st = lib.gma_forward_noalloc(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), mu.data_ptr(), var_raw.data_ptr(),
+                                 prior_logits.data_ptr(), 1 if causal else 0, float(eps), out.data_ptr(),
+                                 None if gamma_out is None else gamma_out.data_ptr(), ctypes.byref(desc), stream)
     if st != GMA_OK:
         raise GMAError(st, strerror(st))
     return out

@@ -73,7 +73,7 @@ size_t gma_workspace_size_cross(const gma_desc* desc, int32_t n_k) { return work
 static int forward_impl(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
                         const float* prior_logits, int causal, int64_t n_k, float eps, void* out,
                         float* gamma_out, const gma_desc* desc, void* workspace, size_t workspace_bytes,
-                        void* stream, gma::Recorder* rec) {
+                        void* stream, gma::Recorder* rec, const gma::ScratchSource* scratch = nullptr) {
     int st = check_desc(desc);
     if (st != GMA_OK) return st;
     const gma_desc d = *desc;
@@ -107,6 +107,18 @@ static int forward_impl(const void* qr, const void* kr, const void* v, const flo
     const int algo = resolve_algo(d, causal);
     if (algo < 0) return GMA_ERR_UNSUPPORTED;
     const size_t need = workspace_for(d, causal, Nk);
+    if (scratch) {
+        // the library's own scratch: every other check has passed, so this is the first HIP call
+        if (need > scratch->capacity) return GMA_ERR_TOO_LARGE;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            int sst = GMA_OK;
+            workspace = scratch->get(stream, &sst);
+            if (!workspace) return sst != GMA_OK ? sst : GMA_ERR_HIP;
+            workspace_bytes = scratch->capacity;
+        }
+    }
     if (need > 0 && (!workspace || workspace_bytes < need)) return GMA_ERR_WORKSPACE;
     if (workspace && (overlaps(workspace, need, out, no) || (gamma_out && overlaps(workspace, need, gamma_out, ng))))
         return GMA_ERR_ALIAS;
@@ -134,6 +146,17 @@ static int forward_impl(const void* qr, const void* kr, const void* v, const flo
     const hipError_t e = (algo == GMA_ALGO_MFMA) ? gma::mfma_forward(a) : gma::simt_forward(a);
     return e == hipSuccess ? GMA_OK : GMA_ERR_HIP;
 }
+
+}  // extern "C"
+
+int gma::forward_with_scratch(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                              const float* prior_logits, int causal, float eps, void* out, float* gamma_out,
+                              const gma_desc* desc, void* stream, const ScratchSource& scratch) {
+    return forward_impl(qr, kr, v, mu, var_raw, prior_logits, causal, desc ? desc->N : 0, eps, out, gamma_out,
+                        desc, nullptr, 0, stream, nullptr, &scratch);
+}
+
+extern "C" {
 
 int gma_forward(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
                 const float* prior_logits, int causal, float eps, void* out, float* gamma_out,
@@ -432,6 +455,9 @@ const char* gma_strerror(int status) {
         case GMA_ERR_WORKSPACE: return "workspace missing or smaller than gma_workspace_size()";
         case GMA_ERR_ALIAS: return "an output overlaps an input, the workspace or the other output";
         case GMA_ERR_HIP: return "a HIP kernel launch failed";
+        case GMA_ERR_TOO_LARGE:
+            return "the call needs more scratch than gma_forward_noalloc's static buffer holds "
+                   "(GMA_NOALLOC_SCRATCH_BYTES); use gma_forward with a workspace";
         default: return "unknown status";
     }
 }

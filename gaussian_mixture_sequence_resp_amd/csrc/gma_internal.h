@@ -105,6 +105,18 @@ size_t stats_workspace(const gma_desc& d);
 hipError_t stats_forward(const Args& a);
 bool stats_on_mfma(const gma_desc& d);
 
+// Scratch that the library supplies itself (gma_forward_noalloc): `get` returns the device
+// address of `capacity` bytes of scratch on the device that `stream` runs on, or nullptr
+// with *status set.
+struct ScratchSource {
+    size_t capacity;
+    void* (*get)(void* stream, int* status);
+};
+// gma_forward with the workspace taken from `scratch` once every argument has been checked.
+int forward_with_scratch(const void* qr, const void* kr, const void* v, const float* mu, const float* var_raw,
+                         const float* prior_logits, int causal, float eps, void* out, float* gamma_out,
+                         const gma_desc* desc, void* stream, const ScratchSource& scratch);
+
 // MFMA family (bf16 inputs): fused matrix-core kernels.
 size_t mfma_workspace(const gma_desc& d, int causal, int Nk);
 bool mfma_supported(const gma_desc& d, int causal);

@@ -73,7 +73,9 @@ typedef enum {
     GMA_ERR_BAD_SCALAR = -5,  /* eps or var_floor negative or not finite; causal not 0 or 1  */
     GMA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than gma_workspace_size()         */
     GMA_ERR_ALIAS = -7,       /* out or gamma_out overlaps an input or each other            */
-    GMA_ERR_HIP = -8          /* a kernel launch reported an error                           */
+    GMA_ERR_HIP = -8,         /* a kernel launch reported an error                           */
+    GMA_ERR_TOO_LARGE = -9    /* gma_forward_noalloc: the call needs more scratch than its
+                                 static buffer (GMA_NOALLOC_SCRATCH_BYTES) holds              */
 } gma_status;
 
 typedef enum { GMA_F32 = 0, GMA_BF16 = 1 } gma_dtype;
@@ -137,6 +139,23 @@ int gma_forward_timed(const void* qr, const void* kr, const void* v, const float
                       void* out, float* gamma_out, const gma_desc* desc, void* workspace,
                       size_t workspace_bytes, void* stream, void* const* events, int n_events,
                       const char** names, int* n_kernels);
+
+/*
+ * gma_forward without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, kernels, results and status codes as gma_forward; the scratch is a static device
+ * array of GMA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the process
+ * ends.  The call itself allocates nothing.  A call whose gma_workspace_size(desc, causal)
+ * exceeds GMA_NOALLOC_SCRATCH_BYTES returns GMA_ERR_TOO_LARGE before any HIP call.  Every call
+ * on one GPU shares that GPU's array: calls that can overlap on one GPU (other streams, other
+ * host threads without ordering) race on it and must not be issued; calls in order on one
+ * stream are safe.  The first call on a device looks up the array's device address there.
+ */
+#define GMA_NOALLOC_SCRATCH_BYTES (64u << 20) /* 64 MiB per GPU */
+
+int gma_forward_noalloc(const void* qr, const void* kr, const void* v, const float* mu,
+                        const float* var_raw, const float* prior_logits, int causal, float eps,
+                        void* out, float* gamma_out, const gma_desc* desc, void* stream);
 
 /*
  * Cross variant (bidirectional only): queries and keys/values of different lengths.  The

@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(lib):
                      "gma_version", "gma_workspace_size_cross", "gma_forward_cross",
                      "gma_forward_cross_timed", "gma_memory_workspace_size", "gma_memory",
                      "gma_decode_workspace_size", "gma_decode_step", "gma_stats_workspace_size",
-                     "gma_resp_stats", "gma_backward_workspace_size", "gma_backward"}
+                     "gma_resp_stats", "gma_backward_workspace_size", "gma_backward",
+                     "gma_forward_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -395,3 +396,32 @@ def test_binding_rejects_host_tensors():
                  inp["prior_logits"]) == binding.GMA_ERR_DEVICE
     assert _code(binding.decode_step, inp["qr"][:, :, :1], inp["kr"][:, :, :1], inp["v"][:, :, :1], inp["mu"],
                  inp["var_raw"], inp["prior_logits"], torch.zeros(2, 3, 4, 9)) == binding.GMA_ERR_DEVICE
+
+
+def test_noalloc_validation(lib):
+    """gma_forward_noalloc: same checks as gma_forward, then GMA_ERR_TOO_LARGE for a call whose
+    workspace exceeds the static scratch -- all before any HIP call (fake pointers here)."""
+    cap = int(re.search(r"#define GMA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", _header_text()).group(1)) << 20
+    vp = ctypes.c_void_p
+    step = 1 << 28
+    P = [Call.BASE + i * step for i in range(8)]
+
+    def call(desc, causal=0, eps=1e-6, **kw):
+        p = dict(zip(("qr", "kr", "v", "mu", "vr", "pr", "out"), P))
+        p.update(kw)
+        return lib.gma_forward_noalloc(p["qr"], p["kr"], p["v"], p["mu"], p["vr"], p["pr"], causal, eps, p["out"],
+                                       None, ctypes.byref(desc), None)
+
+    d = binding.make_desc(2, 3, 64, 16, 8, 12, "bf16", 1e-3, "auto")
+    assert call(d, causal=2) == C["GMA_ERR_BAD_SCALAR"]
+    assert call(d, out=None) == C["GMA_ERR_NULL_ARG"]
+    assert call(d, out=P[0]) == C["GMA_ERR_ALIAS"]
+    assert call(d, qr=P[0] + 8) == C["GMA_ERR_ALIGN"]
+    assert call(binding.make_desc(0, 3, 64, 16, 8, 12, "bf16", 1e-3)) == C["GMA_OK"]  # empty: no launch
+    # a shape whose workspace is beyond the static scratch
+    big = binding.make_desc(64, 8, 8192, 64, 64, 128, "bf16", 1e-3, "simt")
+    need = binding.workspace_size(big, False)
+    assert need > cap
+    big_ptrs = {n: Call.BASE + i * (1 << 34) for i, n in enumerate(("qr", "kr", "v", "mu", "vr", "pr", "out"))}
+    assert call(big, **big_ptrs) == C["GMA_ERR_TOO_LARGE"]
+    assert "GMA_NOALLOC_SCRATCH_BYTES" in binding.strerror(C["GMA_ERR_TOO_LARGE"])
