@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgma.so")
-SOURCES = ["gma_api.cpp", "gma_simt.hip", "gma_mfma.hip", "gma_mfma_causal.hip", "gma_decode.hip", "gma_stats.hip", "gma_backward.hip",
+SOURCES = ["gma_api.cpp", "gma_simt.hip", "gma_mfma.hip", "gma_mfma_causal.hip", "gma_causal_fused.hip", "gma_decode.hip", "gma_stats.hip", "gma_backward.hip",
            "gma_noalloc.hip"]
 ARCH = "gfx950"
 PROBE = "gma_probe.hip"

@@ -740,14 +740,20 @@ __global__ void __launch_bounds__(256)
 }  // namespace
 
 bool causal_supported(const gma_desc& d) {
+    if (fused_causal_supported(d)) return true;
     const Geo g = geometry(d);
     const int Dvs = g.Dvp < kSliceV ? g.Dvp : kSliceV;
     return scan_lds_bytes(g, Dvs) <= kLdsMax && resp_phases(g) > 0;
 }
 
-size_t causal_workspace(const gma_desc& d) { return causal_layout(d).total; }
+size_t causal_workspace(const gma_desc& d) {
+    return fused_causal_supported(d) ? fused_causal_workspace(d) : causal_layout(d).total;
+}
 
+// The fused kernels where they apply (responsibilities on chip); otherwise responsibilities
+// to the workspace, segment totals, then the scan.
 hipError_t causal_forward(const Args& a) {
+    if (fused_causal_supported(a.d)) return fused_causal_forward(a);
     const gma_desc& d = a.d;
     const Geo g = geometry(d);
     const CausalLayout L = causal_layout(d);

@@ -50,6 +50,14 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 MFMA (fp32 accumulate), layouts:
+//   A (16 x 32): lane l holds A[l % 16][8 (l / 16) + j];  B (32 x 16): lane l holds B[8 (l / 16) + j][l % 16];
+//   C (16 x 16): lane l, register i holds C[4 (l / 16) + i][l % 16].
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

@@ -108,6 +108,12 @@ __device__ __forceinline__ void head_part(int b, int heads, int parts, int& head
 // the bidirectional kernels.
 hipError_t launch_prep(const Args& a, const Geo& g, bf16_t* W, float* cvec);
 
+// Causal forward with the responsibilities kept on chip (gma_causal_fused.hip): eight
+// component tiles (128 < K <= 256), d_r <= 64, d_v <= 64.
+bool fused_causal_supported(const gma_desc& d);
+size_t fused_causal_workspace(const gma_desc& d);
+hipError_t fused_causal_forward(const Args& a);
+
 // Causal family (defined in gma_mfma_causal.hip).
 bool causal_supported(const gma_desc& d);
 size_t causal_workspace(const gma_desc& d);
