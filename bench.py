@@ -325,14 +325,18 @@ def step_roofline(w, ms):
 
 def run_decode(w, steps, warmup):
     """Single-token causal decode at workload w's (B, H, K, d) shape: the memory of a
-    prefix of w.N positions (gma_memory, timed on its own as the prefill), then `steps`
-    decode steps, each one gma_decode_step call (one kernel) over every (b, h).  Returns ms
-    per step, the prefill's ms and the bytes a step must move."""
+    prefix of w.N positions (gma_memory, timed on its own as the prefill), then decode steps
+    over every (b, h), each one kernel: gma_decode_step on the raw parameters and
+    gma_decode_step_prepared on parameters prepared once (gma_decode_prepare, timed on its
+    own).  The steps of each kind are captured in one HIP graph of `steps` launches and
+    replayed, as a serving loop would run them: the per-step time is the GPU's, not the
+    Python binding's.  Returns ms per step of each kind, the prefill's and the preparation's
+    ms, and the bytes a step must move."""
     import torch
     import gaussian_mixture_sequence_resp_amd as gma
     from gaussian_mixture_sequence_resp_amd.inputs import make_inputs
 
-    inp = make_inputs(w.with_(N=w.N + steps + warmup))
+    inp = make_inputs(w.with_(N=w.N + steps))
     dev = torch.device("cuda:0")
     d = {k: v.to(dev) for k, v in inp.items()}
     kp, vp = d["kr"][:, :, :w.N].contiguous(), d["v"][:, :, :w.N].contiguous()
@@ -345,38 +349,66 @@ def run_decode(w, steps, warmup):
         gma.memory(kp, vp, d["mu"], d["var_raw"], d["prior_logits"], var_floor=w.var_floor, state=state,
                    workspace=mws)
 
-    for _ in range(3):
-        prefill()
-    torch.cuda.synchronize()
-    reps = 5
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        prefill()
-    torch.cuda.synchronize()
-    prefill_ms = (time.perf_counter() - t0) * 1e3 / reps
-    prefill()
-    rows = [(d["qr"][:, :, t].contiguous(), d["kr"][:, :, t].contiguous(), d["v"][:, :, t].contiguous())
-            for t in range(w.N, w.N + steps + warmup)]
-    out = torch.empty((w.B, w.H, 1, w.d_v), dtype=d["qr"].dtype, device=dev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
+    def timed(f, reps):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
 
-    def step(i):
+    prefill_ms = timed(prefill, 5)
+    params = [None]
+
+    def prepare():
+        params[0] = gma.decode_prepare(d["mu"], d["var_raw"], d["prior_logits"], dtype=w.dtype,
+                                       var_floor=w.var_floor)
+
+    prepare_ms = timed(prepare, 5)
+    rows = [(d["qr"][:, :, t].contiguous(), d["kr"][:, :, t].contiguous(), d["v"][:, :, t].contiguous())
+            for t in range(w.N, w.N + steps)]
+    out = torch.empty((w.B, w.H, 1, w.d_v), dtype=d["qr"].dtype, device=dev)
+
+    def raw_step(i):
         q, k, v = rows[i]
         gma.decode_step(q, k, v, d["mu"], d["var_raw"], d["prior_logits"], state, eps=w.eps,
-                        var_floor=w.var_floor, out=out, stream=stream)
+                        var_floor=w.var_floor, out=out)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(warmup, warmup + steps):
-        step(i)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    def prepared_step(i):
+        q, k, v = rows[i]
+        gma.decode_step_prepared(q, k, v, params[0], state, eps=w.eps, out=out)
+
+    res = {}
+    for name, step in (("raw", raw_step), ("prepared", prepared_step)):
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for i in range(min(steps, max(warmup, 3))):
+                step(i)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        prefill()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                step(i)
+        graph.replay()  # warm
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / (reps * steps)
     # state read and written once per step, plus this position's q, k, v and out
     s = 4 if w.dtype == "f32" else 2
     nbytes = w.B * w.H * (2 * 4 * w.K * (w.d_v + 1) + s * (2 * w.d_r + 2 * w.d_v))
-    return {"ms_per_step": ms, "bytes_per_step": nbytes, "prefill_ms": prefill_ms}
+    return {"ms_per_step": res["prepared"], "raw_ms_per_step": res["raw"], "bytes_per_step": nbytes,
+            "prefill_ms": prefill_ms, "prepare_ms": prepare_ms}
 
 
 def run_stats(w, steps, warmup):
@@ -607,13 +639,16 @@ def main():
         sec = rd["ms_per_step"] * 1e-3
         line["decode"] = {"workload": f"{wd.name} decode (prefix {wd.N}, one position per step)",
                           "us_per_step": round(rd["ms_per_step"] * 1e3, 2),
+                          "step": "gma_decode_step_prepared, steps replayed from one HIP graph",
+                          "raw_parameters_us_per_step": round(rd["raw_ms_per_step"] * 1e3, 2),
+                          "prepare_ms": round(rd["prepare_ms"], 4),
                           "prefill_ms": round(rd["prefill_ms"], 4),
                           "prefill_token_heads_per_s": round(wd.B * wd.H * wd.N / (rd["prefill_ms"] * 1e-3), 1),
                           "value": round(wd.B * wd.H / sec, 1), "unit": "token-heads/s",
                           "roofline": {"bound": "hbm", "achieved": round(rd["bytes_per_step"] / sec / 1e9, 2),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": round(rd["bytes_per_step"] / sec / 1e9 / HBM_PEAK_GBS, 4),
-                                       "note": "whole step (launches included); latency-bound"}}
+                                       "note": "whole step (one kernel, graph replay); latency-bound"}}
     if not args.no_stats and args.workload == 2:
         ws_ = WORKLOADS[3]
         rs = run_stats(ws_, max(10, args.steps // 2), max(3, args.warmup // 2))

@@ -7,7 +7,10 @@ The compute runs in ``libgma.so`` (hand-written HIP kernels behind the C ABI of
 from .binding import (  # noqa: F401
     GMAError,
     backward,
+    DecodeParams,
+    decode_prepare,
     decode_step,
+    decode_step_prepared,
     forward,
     forward_cross,
     forward_noalloc,

@@ -75,6 +75,12 @@ def load_library(path: Optional[str] = None):
     lib.gma_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.POINTER(GmaDesc), vp,
                                     sz, vp]
     lib.gma_decode_step.restype = ctypes.c_int
+    lib.gma_decode_prepared_size.argtypes = [ctypes.POINTER(GmaDesc)]
+    lib.gma_decode_prepared_size.restype = sz
+    lib.gma_decode_prepare.argtypes = [vp, vp, vp, vp, sz, ctypes.POINTER(GmaDesc), vp]
+    lib.gma_decode_prepare.restype = ctypes.c_int
+    lib.gma_decode_step_prepared.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.POINTER(GmaDesc), vp]
+    lib.gma_decode_step_prepared.restype = ctypes.c_int
     lib.gma_backward_workspace_size.argtypes = [ctypes.POINTER(GmaDesc), ctypes.c_int]
     lib.gma_backward_workspace_size.restype = sz
     lib.gma_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp, vp, vp,
@@ -395,6 +401,77 @@ def decode_step(qr, kr, v, mu, var_raw, prior_logits, state, eps: float = 1e-6, 
     st = lib.gma_decode_step(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), mu.data_ptr(), var_raw.data_ptr(),
                              prior_logits.data_ptr(), state.data_ptr(), float(eps), out.data_ptr(),
                              ctypes.byref(desc), ws_ptr, ws_bytes, stream)
+    if st != GMA_OK:
+        raise GMAError(st, strerror(st))
+    return out
+
+
+class DecodeParams:
+    """Prepared mixture parameters of the decode step (gma_decode_prepare): ``block`` is the
+    opaque uint8 device tensor, valid for heads H, K components, d_r routing dims and the
+    input dtype it was prepared for."""
+
+    def __init__(self, block, H: int, K: int, d_r: int, dtype: str, var_floor: float):
+        self.block, self.H, self.K, self.d_r, self.dtype, self.var_floor = block, H, K, d_r, dtype, var_floor
+
+
+def decode_prepare(mu, var_raw, prior_logits, dtype: str = "bf16", var_floor: float = 1e-3,
+                   stream=None) -> DecodeParams:
+    """Prepare mu, var_raw [H,K,d_r] and prior_logits [H,K] (float32, on the GPU) for
+    ``decode_step_prepared`` on inputs of ``dtype`` ("f32" or "bf16")."""
+    import torch
+    if mu.dim() != 3:
+        raise GMAError(-2, f"mu must be [H, K, d_r], got shape {tuple(mu.shape)}")
+    if dtype not in ("f32", "bf16"):
+        raise GMAError(-3, f"unsupported dtype {dtype!r}")
+    H, K, d_r = mu.shape
+    _check(_params_specs(H, K, d_r, mu, var_raw, prior_logits), mu)
+    _dense(mu, var_raw, prior_logits)
+    lib = load_library()
+    desc = make_desc(1, H, 1, d_r, 1, K, dtype, var_floor)
+    need = int(lib.gma_decode_prepared_size(ctypes.byref(desc)))
+    if need == 0:
+        raise GMAError(-3, f"decode parameters not supported for H={H}, K={K}, d_r={d_r}")
+    block = torch.empty(need, dtype=torch.uint8, device=mu.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(mu.device).cuda_stream
+    st = lib.gma_decode_prepare(mu.data_ptr(), var_raw.data_ptr(), prior_logits.data_ptr(), block.data_ptr(),
+                                need, ctypes.byref(desc), stream)
+    if st != GMA_OK:
+        raise GMAError(st, strerror(st))
+    return DecodeParams(block, H, K, d_r, dtype, var_floor)
+
+
+def decode_step_prepared(qr, kr, v, params: DecodeParams, state, eps: float = 1e-6, out=None, stream=None):
+    """``decode_step`` on prepared parameters: qr, kr [B,H,1,d_r] (or [B,H,d_r]), v [B,H,1,d_v]
+    (or [B,H,d_v]); ``state`` float32 [B,H,K,d_v+1] is updated in place; returns out [B,H,1,d_v]."""
+    import torch
+    if qr.dim() not in (3, 4) or (qr.dim() == 4 and qr.shape[2] != 1):
+        raise GMAError(-2, f"qr must be [B, H, 1, d_r] or [B, H, d_r], got shape {tuple(qr.shape)}")
+    if kr.dim() not in (3, 4) or v.dim() not in (3, 4):
+        raise GMAError(-2, "kr and v must be [B, H, 1, d] or [B, H, d]")
+    B, H = qr.shape[0], qr.shape[1]
+    d_r, d_v = qr.shape[-1], v.shape[-1]
+    dt = _dtype_name(qr)
+    if (H, d_r, dt) != (params.H, params.d_r, params.dtype):
+        raise GMAError(-2, f"prepared parameters are for H={params.H}, d_r={params.d_r}, {params.dtype}; "
+                           f"got H={H}, d_r={d_r}, {dt}")
+    K = params.K
+    row = (lambda t: None if t is None else t.reshape(t.shape[0], t.shape[1], -1))
+    _check([("qr", row(qr), None, None, True), ("kr", row(kr), (B, H, d_r), qr.dtype, True),
+            ("v", row(v), (B, H, d_v), qr.dtype, True), ("prepared", params.block, None, torch.uint8, True),
+            ("state", state, (B, H, K, d_v + 1), torch.float32, True),
+            ("out", out, (B, H, 1, d_v), qr.dtype, False)], qr)
+    qr, kr, v = qr.contiguous(), kr.contiguous(), v.contiguous()
+    _dense(state, out)
+    lib = load_library()
+    desc = make_desc(B, H, 1, d_r, d_v, K, dt, params.var_floor)
+    if out is None:
+        out = torch.empty((B, H, 1, d_v), dtype=qr.dtype, device=qr.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(qr.device).cuda_stream
+    st = lib.gma_decode_step_prepared(qr.data_ptr(), kr.data_ptr(), v.data_ptr(), params.block.data_ptr(),
+                                      state.data_ptr(), float(eps), out.data_ptr(), ctypes.byref(desc), stream)
     if st != GMA_OK:
         raise GMAError(st, strerror(st))
     return out

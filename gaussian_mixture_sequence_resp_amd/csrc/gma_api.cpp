@@ -311,6 +311,76 @@ int gma_decode_step(const void* qr, const void* kr, const void* v, const float* 
     return gma::decode_forward(a) == hipSuccess ? GMA_OK : GMA_ERR_HIP;
 }
 
+size_t gma_decode_prepared_size(const gma_desc* desc) {
+    if (check_desc(desc) != GMA_OK || desc->algo == GMA_ALGO_MFMA || desc->H == 0) return 0;
+    return gma::decode_prepared_bytes(*desc);
+}
+
+int gma_decode_prepare(const float* mu, const float* var_raw, const float* prior_logits, void* prepared,
+                       size_t prepared_bytes, const gma_desc* desc, void* stream) {
+    int st = check_desc(desc);
+    if (st != GMA_OK) return st;
+    const gma_desc d = *desc;
+    if (d.algo == GMA_ALGO_MFMA) return GMA_ERR_UNSUPPORTED;
+    if (d.H == 0) return GMA_OK;
+    if (!mu || !var_raw || !prior_logits || !prepared) return GMA_ERR_NULL_ARG;
+    if (misaligned(mu, 4) || misaligned(var_raw, 4) || misaligned(prior_logits, 4)) return GMA_ERR_ALIGN;
+    if (misaligned(prepared, gma::kWsAlign)) return GMA_ERR_ALIGN;
+    const size_t need = gma::decode_prepared_bytes(d);
+    if (prepared_bytes < need) return GMA_ERR_WORKSPACE;
+    const size_t np = (size_t)d.H * d.K * d.d_r * 4, npr = (size_t)d.H * d.K * 4;
+    if (overlaps(prepared, need, mu, np) || overlaps(prepared, need, var_raw, np) ||
+        overlaps(prepared, need, prior_logits, npr))
+        return GMA_ERR_ALIAS;
+    Args a;
+    memset(&a, 0, sizeof(a));
+    a.mu = mu;
+    a.var_raw = var_raw;
+    a.prior = prior_logits;
+    a.d = d;
+    a.ws = static_cast<unsigned char*>(prepared);
+    a.ws_bytes = prepared_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gma::decode_prepare(a) == hipSuccess ? GMA_OK : GMA_ERR_HIP;
+}
+
+int gma_decode_step_prepared(const void* qr, const void* kr, const void* v, const void* prepared, float* state,
+                             float eps, void* out, const gma_desc* desc, void* stream) {
+    int st = check_desc(desc);
+    if (st != GMA_OK) return st;
+    const gma_desc d = *desc;
+    if (d.N != 1) return GMA_ERR_BAD_SHAPE;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return GMA_ERR_BAD_SCALAR;
+    const size_t bh = (size_t)d.B * d.H;
+    if (bh == 0) return GMA_OK;
+    if (!qr || !kr || !v || !prepared || !state || !out) return GMA_ERR_NULL_ARG;
+    if (d.algo == GMA_ALGO_MFMA) return GMA_ERR_UNSUPPORTED;
+    const size_t esz = d.dtype == GMA_F32 ? 4 : 2;
+    const size_t nx = bh * d.d_r * esz, nv = bh * d.d_v * esz;
+    const size_t ns = bh * d.K * (d.d_v + 1) * 4, np = gma::decode_prepared_bytes(d);
+    if (misaligned(qr, 16) || misaligned(kr, 16) || misaligned(v, 16) || misaligned(out, 16)) return GMA_ERR_ALIGN;
+    if (misaligned(state, 4) || misaligned(prepared, gma::kWsAlign)) return GMA_ERR_ALIGN;
+    const void* ins[4] = {qr, kr, v, prepared};
+    const size_t ins_n[4] = {nx, nx, nv, np};
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(out, nv, ins[i], ins_n[i]) || overlaps(state, ns, ins[i], ins_n[i])) return GMA_ERR_ALIAS;
+    if (overlaps(out, nv, state, ns)) return GMA_ERR_ALIAS;
+    Args a;
+    memset(&a, 0, sizeof(a));
+    a.qr = qr;
+    a.kr = kr;
+    a.v = v;
+    a.eps = eps;
+    a.out = out;
+    a.state = state;
+    a.d = d;
+    a.Nk = 1;
+    a.ws = static_cast<unsigned char*>(const_cast<void*>(prepared));
+    a.ws_bytes = np;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gma::decode_prepared_forward(a, 0) == hipSuccess ? GMA_OK : GMA_ERR_HIP;
+}
+
 // ---- backward
 
 static bool backward_algo_ok(const gma_desc& d) { return d.algo != GMA_ALGO_MFMA && gma::backward_supported(d); }

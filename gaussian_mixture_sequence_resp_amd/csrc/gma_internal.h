@@ -84,6 +84,11 @@ size_t memory_workspace(const gma_desc& d);
 hipError_t memory_forward(const Args& a);
 size_t decode_workspace(const gma_desc& d);
 hipError_t decode_forward(const Args& a);
+// Prepared parameters of the decode step (gma_decode.hip): byte size, the preparation
+// (a.ws = the prepared block) and the step on them (groups <= 0: the default column groups).
+size_t decode_prepared_bytes(const gma_desc& d);
+hipError_t decode_prepare(const Args& a);
+hipError_t decode_prepared_forward(const Args& a, int groups);
 
 // Backward (gma_backward.hip): dout and the gradients; the inputs are those of the forward
 // in Args (qr, kr, v, mu, var_raw, prior, causal, eps).

@@ -220,6 +220,35 @@ int gma_decode_step(const void* qr, const void* kr, const void* v, const float* 
                     void* stream);
 
 /*
+ * The decode step on prepared parameters, for callers that decode many positions with the
+ * same weights: the same step as gma_decode_step (same recurrence, state layout, update in
+ * place and output), with the per-component variance transcendentals of the mixture taken
+ * once instead of at every step.
+ *
+ * gma_decode_prepared_size: bytes of the prepared block for desc (H, K, d_r, dtype; B and N
+ *   are not read); 0 for an invalid desc.
+ * gma_decode_prepare: writes the prepared block from mu, var_raw [H,K,d_r] and prior_logits
+ *   [H,K] (float32) and desc->var_floor.  Its content is opaque (per head: the means and the
+ *   precisions 1 / (softplus(var_raw) + var_floor), float64 for float32 inputs, float32 for
+ *   bf16, and the constants prior_logit - (1/2) sum log var in float64).  `prepared` is
+ *   caller-owned device memory, 256-byte aligned, of at least gma_decode_prepared_size bytes,
+ *   not overlapping the parameters; it stays valid until the parameters change.
+ * gma_decode_step_prepared: one position per (b, h), desc->N must be 1 and desc must carry the
+ *   H, K, d_r and dtype given to gma_decode_prepare (a mismatch is not detectable and gives
+ *   wrong results).  qr, kr [B,H,1,d_r], v [B,H,1,d_v] (desc->dtype, 16-byte aligned); `state`
+ *   float32 [B,H,K,d_v+1], updated in place; out [B,H,1,d_v].  One kernel launch, no
+ *   workspace; `prepared` is only read.  Status codes as gma_decode_step.
+ */
+size_t gma_decode_prepared_size(const gma_desc* desc);
+
+int gma_decode_prepare(const float* mu, const float* var_raw, const float* prior_logits,
+                       void* prepared, size_t prepared_bytes, const gma_desc* desc, void* stream);
+
+int gma_decode_step_prepared(const void* qr, const void* kr, const void* v, const void* prepared,
+                             float* state, float eps, void* out, const gma_desc* desc,
+                             void* stream);
+
+/*
  * Backward of gma_forward: the pages train the mixture parameters end to end by
  * backpropagation ("Core mechanism" item 3).  Given dout = dL/dO [B,H,N,d_v] (desc->dtype),
  * writes dL/dqr, dL/dkr [B,H,N,d_r] and dL/dv [B,H,N,d_v] (desc->dtype) and, summed over the

@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(lib):
                      "gma_forward_cross_timed", "gma_memory_workspace_size", "gma_memory",
                      "gma_decode_workspace_size", "gma_decode_step", "gma_stats_workspace_size",
                      "gma_resp_stats", "gma_backward_workspace_size", "gma_backward",
-                     "gma_forward_noalloc"}
+                     "gma_forward_noalloc", "gma_decode_prepared_size", "gma_decode_prepare",
+                     "gma_decode_step_prepared"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -221,6 +222,49 @@ def test_memory_and_decode_validation(lib):
     # an empty prefix needs no kr / v (the state is still written: fails here on the workspace)
     assert mem(binding.make_desc(2, 3, 0, 16, 8, 12, "bf16", 1e-3), kr=None, v=None, nb=8) == C["GMA_ERR_WORKSPACE"]
     assert binding.load_library().gma_memory_workspace_size(ctypes.byref(dm)) > 0
+
+
+def test_prepared_decode_validation(lib):
+    # every call below fails validation (or is an empty no-op) before any HIP call
+    vp = ctypes.c_void_p
+    lib.gma_decode_prepare.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, ctypes.POINTER(binding.GmaDesc), vp]
+    lib.gma_decode_step_prepared.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                             ctypes.POINTER(binding.GmaDesc), vp]
+    step = 1 << 24
+    P = [Call.BASE + i * step for i in range(8)]  # mu var_raw prior prepared qr kr v state; out spare
+
+    def prep(desc, **kw):
+        p = dict(mu=P[0], vr=P[1], pr=P[2], pp=P[3], nb=1 << 30)
+        p.update(kw)
+        return lib.gma_decode_prepare(p["mu"], p["vr"], p["pr"], p["pp"], p["nb"], ctypes.byref(desc), None)
+
+    def step_(desc, eps=1e-6, **kw):
+        p = dict(qr=P[4], kr=P[5], v=P[6], pp=P[3], st=P[7], out=P[7] + step // 2)
+        p.update(kw)
+        return lib.gma_decode_step_prepared(p["qr"], p["kr"], p["v"], p["pp"], p["st"], eps, p["out"],
+                                            ctypes.byref(desc), None)
+
+    d1 = binding.make_desc(2, 3, 1, 16, 8, 12, "bf16", 1e-3)
+    need = int(lib.gma_decode_prepared_size(ctypes.byref(d1)))
+    # float32 (mu, lambda) pairs for bf16 inputs, float64 for float32, and one float64 constant per component
+    assert need == 3 * 12 * 16 * 8 + 3 * 12 * 8
+    assert int(lib.gma_decode_prepared_size(ctypes.byref(binding.make_desc(2, 3, 1, 16, 8, 12, "f32", 1e-3)))) \
+        == 3 * 12 * 16 * 16 + 3 * 12 * 8
+    assert lib.gma_decode_prepared_size(ctypes.byref(binding.make_desc(2, 3, 1, 16, 8, 300, "bf16", 1e-3))) == 0
+    assert prep(d1, nb=need - 1) == C["GMA_ERR_WORKSPACE"]
+    assert prep(d1, pp=None) == C["GMA_ERR_NULL_ARG"]
+    assert prep(d1, pp=P[3] + 64) == C["GMA_ERR_ALIGN"]
+    assert prep(d1, pp=P[0]) == C["GMA_ERR_ALIAS"]
+    assert prep(binding.make_desc(2, 3, 1, 16, 8, 12, "bf16", -1.0)) == C["GMA_ERR_BAD_SCALAR"]
+    assert prep(binding.make_desc(2, 0, 1, 16, 8, 12, "bf16", 1e-3), mu=None) == C["GMA_OK"]
+    assert step_(binding.make_desc(2, 3, 2, 16, 8, 12, "bf16", 1e-3)) == C["GMA_ERR_BAD_SHAPE"]
+    assert step_(binding.make_desc(2, 3, 1, 16, 8, 12, "bf16", 1e-3, "mfma")) == C["GMA_ERR_UNSUPPORTED"]
+    assert step_(d1, eps=float("nan")) == C["GMA_ERR_BAD_SCALAR"]
+    assert step_(d1, pp=None) == C["GMA_ERR_NULL_ARG"]
+    assert step_(d1, pp=P[3] + 16) == C["GMA_ERR_ALIGN"]
+    assert step_(d1, st=P[3]) == C["GMA_ERR_ALIAS"]
+    assert step_(d1, out=P[4]) == C["GMA_ERR_ALIAS"]
+    assert step_(binding.make_desc(0, 3, 1, 16, 8, 12, "bf16", 1e-3), qr=None) == C["GMA_OK"]
 
 
 def test_stats_validation(lib):

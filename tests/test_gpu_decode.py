@@ -1,5 +1,6 @@
 """GPU parity of the causal memory (prefill) and the single-token decode step against the
-fp64 oracle, through the C ABI (gma_memory, gma_decode_step).
+fp64 oracle, through the C ABI (gma_memory, gma_decode_step, and gma_decode_prepare +
+gma_decode_step_prepared).
 
 Core mechanism item 3 read as a recurrence: decoding positions t = s..N-1 one at a time
 from the memory of positions 0..s-1 reproduces rows s..N-1 of the causal forward.  Gate:
@@ -27,16 +28,23 @@ def _say(*a):
     print("[gpu-case]", *a, file=sys.stderr, flush=True)
 
 
-def _run(inp, w, split, algo="auto"):
-    """Memory of positions [0, split), then decode steps for the rest; returns (outs, state)."""
+def _run(inp, w, split, algo="auto", prepared=False):
+    """Memory of positions [0, split), then decode steps for the rest (on the raw parameters,
+    or on parameters prepared once); returns (outs, state)."""
     d = {k: x.to(DEV) for k, x in inp.items()}
     state = gma.memory(d["kr"][:, :, :split].contiguous(), d["v"][:, :, :split].contiguous(), d["mu"],
                        d["var_raw"], d["prior_logits"], var_floor=w.var_floor, algo=algo)
+    params = gma.decode_prepare(d["mu"], d["var_raw"], d["prior_logits"], dtype=w.dtype,
+                                var_floor=w.var_floor) if prepared else None
     outs = []
     for t in range(split, w.N):
         sl = slice(t, t + 1)
-        outs.append(gma.decode_step(d["qr"][:, :, sl], d["kr"][:, :, sl], d["v"][:, :, sl], d["mu"],
-                                    d["var_raw"], d["prior_logits"], state, eps=w.eps, var_floor=w.var_floor))
+        if prepared:
+            outs.append(gma.decode_step_prepared(d["qr"][:, :, sl], d["kr"][:, :, sl], d["v"][:, :, sl], params,
+                                                 state, eps=w.eps))
+        else:
+            outs.append(gma.decode_step(d["qr"][:, :, sl], d["kr"][:, :, sl], d["v"][:, :, sl], d["mu"],
+                                        d["var_raw"], d["prior_logits"], state, eps=w.eps, var_floor=w.var_floor))
     torch.cuda.synchronize()
     out = torch.cat(outs, dim=2).cpu() if outs else None
     return out, state.cpu()
@@ -51,13 +59,14 @@ DECODE = [
 ]
 
 
+@pytest.mark.parametrize("prepared", [False, True])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("N,K,dr,dv,split", DECODE)
-def test_memory_then_decode_matches_causal_forward(N, K, dr, dv, split, dtype):
+def test_memory_then_decode_matches_causal_forward(N, K, dr, dv, split, dtype, prepared):
     w = WORKLOADS[3].with_(B=2, H=3, N=N, K=K, d_r=dr, d_v=dv, dtype=dtype, seed=51 + N + K)
     inp = make_inputs(w)
-    _say("decode", dtype, dict(N=N, K=K, dr=dr, dv=dv, split=split, seed=w.seed))
-    out, state = _run(inp, w, split)
+    _say("decode", dtype, dict(N=N, K=K, dr=dr, dv=dv, split=split, seed=w.seed, prepared=prepared))
+    out, state = _run(inp, w, split, prepared=prepared)
     ref = oracle.forward(inp["qr"], inp["kr"], inp["v"], inp["mu"], inp["var_raw"], inp["prior_logits"], True,
                          w.eps, w.var_floor)
     tol = metrics.tol_for(dtype)
@@ -130,7 +139,8 @@ def test_decode_with_parameters_not_16_byte_aligned(dtype):
         assert metrics.rowrel(o, ref[:, :, 3:]) <= metrics.tol_for(dtype)
 
 
-def test_decode_full_size_sampled_heads():
+@pytest.mark.parametrize("prepared", [False, True])
+def test_decode_full_size_sampled_heads(prepared):
     """Prefill and decode at the benchmark's shape (the causal LM workload: B=16, H=8, K=256,
     d=64, a prefix of 2048 positions, then 8 decode steps, all (b, h) in each launch): the
     memory and the step outputs of heads 0 and H-1 (all batch elements) against the oracle
@@ -139,8 +149,8 @@ def test_decode_full_size_sampled_heads():
     steps = 8
     w = base.with_(N=base.N + steps)
     inp = make_inputs(w)
-    _say("decode full size", w.name, dict(B=w.B, H=w.H, prefix=base.N, steps=steps, K=w.K))
-    out, state = _run(inp, w, base.N)
+    _say("decode full size", w.name, dict(B=w.B, H=w.H, prefix=base.N, steps=steps, K=w.K, prepared=prepared))
+    out, state = _run(inp, w, base.N, prepared=prepared)
     tol = metrics.tol_for(w.dtype)
     for h in (0, w.H - 1):
         sub = {k: (x[:, h:h + 1].contiguous() if k in ("qr", "kr", "v") else x[h:h + 1].contiguous())
@@ -152,3 +162,79 @@ def test_decode_full_size_sampled_heads():
         serr = metrics.rowrel(state[:, h:h + 1], ref_state)
         _say("decode full size head", h, f"out {err:.2e}", f"state after the steps {serr:.2e}")
         assert err <= tol and serr <= tol, (h, err, serr)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prepared_step_matches_raw_step(dtype):
+    """The prepared and the raw decode step are two evaluations of the same step: after the
+    same prefill, their outputs and states agree to the dtype's gate, for every (b, h) of a
+    batch large enough that the prepared step splits each (b, h) over several column groups
+    (B*H = 24, d_v = 96)."""
+    w = WORKLOADS[3].with_(B=4, H=6, N=70, K=256, d_r=64, d_v=96, dtype=dtype, seed=64)
+    inp = make_inputs(w)
+    _say("prepared vs raw", dtype)
+    raw, sraw = _run(inp, w, 60)
+    prep, sprep = _run(inp, w, 60, prepared=True)
+    tol = metrics.tol_for(dtype)
+    assert metrics.rowrel(prep, raw) <= tol
+    assert metrics.rowrel(sprep, sraw) <= tol
+    ref = oracle.forward(inp["qr"], inp["kr"], inp["v"], inp["mu"], inp["var_raw"], inp["prior_logits"], True,
+                         w.eps, w.var_floor)
+    assert metrics.rowrel(prep, ref[:, :, 60:]) <= tol
+
+
+@pytest.mark.parametrize("prepared", [False, True])
+def test_decode_steps_replayed_from_a_graph(prepared):
+    """Decode steps captured in a HIP graph (the way a serving loop launches them; neither
+    step allocates or clears memory) and replayed three times, each replay from the same
+    prefill, eager work and synchronisation in between: every replay's outputs and state
+    equal the eager run's bitwise (the same kernels on the same inputs)."""
+    w = WORKLOADS[3].with_(B=4, H=4, N=40, seed=65)
+    inp = make_inputs(w)
+    d = {k: x.to(DEV) for k, x in inp.items()}
+    split, steps = 32, 8
+    _say("decode graph replay", dict(prepared=prepared, steps=steps))
+    state = torch.empty((w.B, w.H, w.K, w.d_v + 1), dtype=torch.float32, device=DEV)
+    params = gma.decode_prepare(d["mu"], d["var_raw"], d["prior_logits"], dtype=w.dtype,
+                                var_floor=w.var_floor) if prepared else None
+    rows = [(d["qr"][:, :, t:t + 1].contiguous(), d["kr"][:, :, t:t + 1].contiguous(),
+             d["v"][:, :, t:t + 1].contiguous()) for t in range(split, split + steps)]
+    outs = [torch.empty((w.B, w.H, 1, w.d_v), dtype=d["qr"].dtype, device=DEV) for _ in range(steps)]
+
+    def prefill():
+        gma.memory(d["kr"][:, :, :split].contiguous(), d["v"][:, :, :split].contiguous(), d["mu"], d["var_raw"],
+                   d["prior_logits"], var_floor=w.var_floor, state=state)
+
+    def run_steps():
+        for i, (q, k, v) in enumerate(rows):
+            if prepared:
+                gma.decode_step_prepared(q, k, v, params, state, eps=w.eps, out=outs[i])
+            else:
+                gma.decode_step(q, k, v, d["mu"], d["var_raw"], d["prior_logits"], state, eps=w.eps,
+                                var_floor=w.var_floor, out=outs[i])
+
+    prefill()
+    run_steps()
+    torch.cuda.synchronize()
+    eager_out = torch.cat([o.clone() for o in outs], dim=2).cpu()
+    eager_state = state.clone().cpu()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        prefill()
+        run_steps()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_steps()
+    for rep in range(3):
+        prefill()
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = torch.cat([o.clone() for o in outs], dim=2).cpu()
+        assert torch.equal(got, eager_out), rep
+        assert torch.equal(state.cpu(), eager_state), rep
