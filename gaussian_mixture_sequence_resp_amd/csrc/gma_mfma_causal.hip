@@ -144,14 +144,61 @@ __device__ __forceinline__ void stage_coefficient_chunks(unsigned char* sW, floa
     for (int i = threadIdx.x; i < Kp; i += blockDim.x) sC[i] = cvec[(size_t)h * Kp + i];
 }
 
+// ---- soft usage inside the responsibilities kernel (statistics mode)
+// Sum over the 32 tokens of a tile (lanes l % 32 of each half) of every component, as a
+// reduce-scatter: five exchange stages, each pairing lane l with a partner that differs in
+// one lane bit (l ^ 16: lane swap; l ^ 8: DPP row rotate by 8; 7 - l mod 8: DPP half-row
+// mirror; l ^ 2, l ^ 1: DPP quad permutes).  At each stage a lane keeps the lower or the
+// upper half of its values (by that bit) and adds the partner's copy of that half, so the
+// 16 MT values of a lane end as MT / 2 sums (tokens added in a fixed pairing order) of the
+// flattened indices (MT / 2) (l % 32) .. + MT / 2 - 1; for MT = 1 the last stage adds the
+// pair's single values instead (both lanes of the pair then hold the same sum).
+template <int STAGE>
+__device__ __forceinline__ float rs_partner(float x) {
+    if constexpr (STAGE == 0) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float((lane_id() >> 4) & 1 ? r[0] : r[1]);
+    } else {
+        constexpr int ctrl = STAGE == 1 ? 0x128 : STAGE == 2 ? 0x141 : STAGE == 3 ? 0x4E : 0xB1;
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, false));
+    }
+}
+template <int STAGE, int N>
+__device__ __forceinline__ void rs_stage(const float (&v)[N], float (&o)[N / 2]) {
+    const bool bit = (lane_id() >> (4 - STAGE)) & 1;
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+        const float keep = bit ? v[j + N / 2] : v[j];
+        const float send = bit ? v[j] : v[j + N / 2];
+        o[j] = keep + rs_partner<STAGE>(send);
+    }
+}
+// v: the tile's values (16 MT, flattened 16 m + e); out: this lane's F = max(1, MT / 2) sums.
+template <int MT>
+__device__ __forceinline__ void tile_token_sums(const float (&v)[16 * MT], float (&out)[MT >= 2 ? MT / 2 : 1]) {
+    float a[8 * MT], b[4 * MT], c[2 * MT], d[MT];
+    rs_stage<0>(v, a);
+    rs_stage<1>(a, b);
+    rs_stage<2>(b, c);
+    rs_stage<3>(c, d);
+    if constexpr (MT >= 2) {
+        rs_stage<4>(d, out);
+    } else {
+        out[0] = d[0] + rs_partner<4>(d[0]);
+    }
+}
+
 // Eight waves (two per SIMD, so one wave's exponentials overlap the other's MFMAs); each
 // wave handles one 32-position tile per 256-position step (one side per block row,
 // blockIdx.y: 0 queries, 1 keys): logits (MFMA), softmax over the components, normalised
 // responsibilities stored as bf16 operand fragments; positions in [N, Np) get zeros.  When
 // the coefficient block of a head exceeds LDS it is staged in NPH phases of the routing
-// dims, the logits accumulating across phases.  MODE kRespStats: also the hard assignment
-// of every position of side 0, argmax of its fp32 logits (lowest component among equal
-// maxima), into hard [BH][N].  MODE kRespRows: instead of fragments, the normalised
+// dims, the logits accumulating across phases.  MODE kRespStats: instead of fragments, the
+// hard assignment of every position of side 0, argmax of its fp32 logits (lowest component
+// among equal maxima), into hard [BH][N], and the workgroup's soft usage (its positions'
+// float32 responsibilities summed per component: per tile across the tokens, per lane
+// across tiles, then across the waves in wave order) as float32 [BH parts][Kp] into GK
+// reinterpreted as float (natural component order).  MODE kRespRows: instead of fragments, the normalised
 // responsibilities as float32 rows [BH][N][K] (components < K) into GQ / GK reinterpreted
 // as float (the backward's layout).
 constexpr int kRespWaves = 8;
@@ -186,6 +233,10 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
         stage_coefficient_chunks(sW, sC, W, cvec, h, Kp, Dp, 0, NC, wstride);
         __syncthreads();
     }
+    constexpr int UF = MT >= 2 ? MT / 2 : 1;  // usage sums per lane (statistics mode)
+    float us[UF];
+#pragma unroll
+    for (int i = 0; i < UF; ++i) us[i] = 0.0f;
     for (int b0 = n_begin; b0 < n_end; b0 += kStep) {
         const int t0 = b0 + kTileT * w;  // this wave's tile
         const bool valid = t0 + col < N;
@@ -252,6 +303,17 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
                         }
                     }
             }
+        } else if constexpr (MODE == kRespStats) {
+            const float sc = t0 < n_end ? inv : 0.0f;
+            float v[16 * MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) v[16 * m + e] = acc[m][e] * sc;
+            float r[UF];
+            tile_token_sums<MT>(v, r);
+#pragma unroll
+            for (int i = 0; i < UF; ++i) us[i] += r[i];
         } else if (t0 < n_end) {
             // registers 8 sh .. 8 sh + 7 of tile m are slots 8 half + 0..7 of block 2m + sh
             bf16_t* gt = G + (size_t)(t0 / kTileT) * KS * kFrag;
@@ -260,6 +322,29 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
                 *reinterpret_cast<bf16x8*>(gt + (size_t)(2 * m) * kFrag) = pack8(acc[m], 0, inv);
                 *reinterpret_cast<bf16x8*>(gt + (size_t)(2 * m + 1) * kFrag) = pack8(acc[m], 8, inv);
             }
+        }
+    }
+    if constexpr (MODE == kRespStats) {
+        // lane (half, c) holds flattened indices UF c + i (UF (c >> 1) for MT = 1, where the
+        // odd lanes repeat their even neighbour): index 16 m + e is component
+        // 32 m + 8 (e / 4) + 4 half + e % 4.  Per-wave sums to LDS, then over the waves.
+        float* su = reinterpret_cast<float*>(smem);
+        __syncthreads();  // the coefficient block is no longer read
+        const int half = l >> 5;
+#pragma unroll
+        for (int i = 0; i < UF; ++i) {
+            const int idx = MT >= 2 ? UF * col + i : (col >> 1);
+            const int m = idx >> 4, e = idx & 15;
+            const int k = 32 * m + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (MT >= 2 || (col & 1) == 0) su[w * Kp + k] = us[i];
+        }
+        __syncthreads();
+        float* up = reinterpret_cast<float*>(GK) + ((size_t)bh * parts + part) * Kp;
+        for (int k = threadIdx.x; k < Kp; k += blockDim.x) {
+            float t = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < kRespWaves; ++ww) t += su[ww * Kp + k];
+            up[k] = t;
         }
     }
 }
@@ -693,19 +778,31 @@ hipError_t set_lds(const void* f, size_t bytes) {
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+}  // namespace
+
+// Position parts per (b, h) of the responsibilities kernel: about one workgroup per CU over
+// all (b, h), each part a multiple of the workgroup's 256-position step.
+int resp_parts(int BH, int Np, int* part_len) {
+    const int rstep = kTileT * kRespWaves;
+    int parts = (256 + BH - 1) / BH;
+    const int max_parts = (Np + rstep - 1) / rstep;
+    if (parts > max_parts) parts = max_parts;
+    if (parts < 1) parts = 1;
+    const int len = ((Np + parts - 1) / parts + rstep - 1) / rstep * rstep;
+    if (part_len) *part_len = len;
+    return (Np + len - 1) / len;
+}
+
+namespace {
+
 // Responsibilities of `sides` sides (2: Gamma_Q into GQ and Gamma_K into GK; 1: Gamma_K
 // only, into GK), about one workgroup per CU per side.
 hipError_t launch_resp(const Args& a, const Geo& g, RespFn rf, int nph, int Np, int sides, const bf16_t* W,
                        const float* cvec, bf16_t* GQ, bf16_t* GK, int* hard = nullptr) {
     const gma_desc& d = a.d;
     const int BH = d.B * d.H;
-    const int rstep = kTileT * kRespWaves;
-    int parts = (256 + BH - 1) / BH;
-    const int max_parts = (Np + rstep - 1) / rstep;
-    if (parts > max_parts) parts = max_parts;
-    if (parts < 1) parts = 1;
-    const int part_len = ((Np + parts - 1) / parts + rstep - 1) / rstep * rstep;
-    parts = (Np + part_len - 1) / part_len;
+    int part_len = 0;
+    const int parts = resp_parts(BH, Np, &part_len);
     const size_t rl = resp_lds(g, nph);
     hipError_t e;
     if ((e = set_lds(reinterpret_cast<const void*>(rf), rl)) != hipSuccess) return e;
@@ -867,15 +964,18 @@ hipError_t causal_memory(const Args& a) {
     return hipGetLastError();
 }
 
-// Responsibility statistics on the matrix cores: Gamma of the rows a.kr (written like the
-// key side, operand fragments [B H][Np/32][Kp/16][64][8] into G) and the hard assignment of
-// every row into hard [B H][N]; coefficients into W, cvec.  Np = N rounded up to 128.
+// Responsibility statistics on the matrix cores: the hard assignment of every row of a.kr
+// into hard [B H][N] and the soft usage partials of every (b h, part) workgroup into
+// upart [B H parts][Kp] (parts = resp_parts(B H, Np)); coefficients into W, cvec.  Np = N
+// rounded up to 128.
 bool stats_supported(const gma_desc& d) {
     if (d.dtype != GMA_BF16 || d.d_r % 8 != 0) return false;
     return resp_phases(geometry(d)) > 0;
 }
 
-hipError_t stats_resp(const Args& a, bf16_t* W, float* cvec, bf16_t* G, int* hard) {
+int stats_np(const gma_desc& d) { return (d.N + kGroup - 1) / kGroup * kGroup; }
+
+hipError_t stats_resp(const Args& a, bf16_t* W, float* cvec, float* upart, int* hard) {
     const gma_desc& d = a.d;
     const Geo g = geometry(d);
     const int nph = resp_phases(g);
@@ -883,8 +983,7 @@ hipError_t stats_resp(const Args& a, bf16_t* W, float* cvec, bf16_t* G, int* har
     if (!rf) return hipErrorNotSupported;
     hipError_t e;
     if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
-    const int Np = (d.N + kGroup - 1) / kGroup * kGroup;
-    return launch_resp(a, g, rf, nph, Np, 1, W, cvec, nullptr, G, hard);
+    return launch_resp(a, g, rf, nph, stats_np(d), 1, W, cvec, nullptr, reinterpret_cast<bf16_t*>(upart), hard);
 }
 
 // Responsibilities of both sides as float32 rows [2][B H][N][K] (queries, then keys) for

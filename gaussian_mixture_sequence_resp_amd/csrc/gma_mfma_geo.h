@@ -120,9 +120,13 @@ size_t causal_workspace(const gma_desc& d);
 hipError_t causal_forward(const Args& a);
 size_t causal_memory_workspace(const gma_desc& d);
 hipError_t causal_memory(const Args& a);
-// Responsibility statistics: Gamma (fragment order) and hard assignments of the rows a.kr.
+// Position parts per (b, h) of the responsibilities kernel (and the part length).
+int resp_parts(int BH, int Np, int* part_len);
+// Responsibility statistics: hard assignments of the rows a.kr and the soft usage partials
+// [B H parts][Kp] of the responsibilities kernel's workgroups (Np = stats_np(d)).
 bool stats_supported(const gma_desc& d);
-hipError_t stats_resp(const Args& a, bf16_t* W, float* cvec, bf16_t* G, int* hard);
+int stats_np(const gma_desc& d);
+hipError_t stats_resp(const Args& a, bf16_t* W, float* cvec, float* upart, int* hard);
 // Responsibilities of both sides as float32 rows [2][B H][N][K] (the backward's layout).
 hipError_t resp_rows(const Args& a, bf16_t* W, float* cvec, float* gamma);
 

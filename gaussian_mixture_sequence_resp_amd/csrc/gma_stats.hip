@@ -11,15 +11,15 @@
 //   entropy[h]   -sum_k p_k ln p_k / ln K, p_k = counts / (B N)  (0 when K = 1 or no rows)
 //
 // Kernels (caller's stream, in this order):
-//   bf16, matrix cores: gma_prep and gma_causal_resp<..., STATS> (Gamma of the rows in MFMA
-//     operand-fragment order, hard assignments from the fp32 logits), then
-//     gma_stats_usage_frag (per chunk of fragment blocks, partial soft usage per slot);
+//   bf16, matrix cores: gma_prep and gma_causal_resp<..., STATS> (hard assignments from the
+//     fp32 logits; the soft usage summed inside the kernel, one partial per workgroup, so
+//     Gamma never leaves the chip);
 //   SIMT: params_kernel and resp_kernel (Gamma rows in float32, hard assignments from the
 //     double logits), then gma_stats_usage_rows (per chunk of rows, partial soft usage);
 //   both: gma_stats_hist (per chunk of rows: histogram of the hard assignments in LDS with
 //     integer atomics, so the counts do not depend on the order of arrival), then
 //     gma_stats_finish (one workgroup per head: the chunk histograms and the usage partials
-//     summed in chunk order; components used and the entropy).
+//     summed in a fixed order; components used and the entropy).
 // Every floating-point sum has a fixed order: the results are deterministic.
 #include <math.h>
 
@@ -31,7 +31,6 @@
 namespace gma {
 namespace {
 
-constexpr int kUsageChunks = 4;  // usage partials per head (x Kp/16 x H workgroups)
 constexpr int kHistChunks = 16;  // count partials per head
 constexpr int kFinishThreads = 1024;
 
@@ -55,50 +54,6 @@ __global__ void __launch_bounds__(1024)
     for (int k = t; k < K; k += blockDim.x) cpart[((size_t)h * kHistChunks + c) * K + k] = hist[k];
 }
 
-// Partial soft usage of chunk c of head h over the fragment blocks of component block ks:
-// block u of the head's B * tpb blocks (b = u / tpb) is 64 lanes x 8 slots of bf16; lane l
-// holds slots 8 (l / 32) .. + 7 of the block for token l % 32.  Four groups of 64 threads
-// take every fourth block; each thread sums its lane's 8 slots in block order; then the
-// 4 groups x 32 lanes of each half are summed in a fixed order into part[h][c][16 ks + s].
-__global__ void __launch_bounds__(256)
-    gma_stats_usage_frag(const bf16_t* __restrict__ G, float* __restrict__ part, int H, int B, int tpb, int KS,
-                         int C, int per_chunk) {
-    __shared__ float sacc[4][64][9];
-    const int ks = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
-    const int t = threadIdx.x, grp = t >> 6, l = t & 63;
-    const int total = B * tpb;
-    const int u0 = c * per_chunk, u1 = min(total, u0 + per_chunk);
-    float acc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-    auto block = [&](int u) -> const bf16_t* {
-        const int b = u / tpb, tile = u % tpb;
-        return G + (((size_t)(b * H + h) * tpb + tile) * KS + ks) * (64 * 8) + 8 * l;
-    };
-    for (int u = u0 + grp; u < u1; u += 16) {
-        mf::bf16x8 x[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (u + 4 * q < u1) x[q] = *reinterpret_cast<const mf::bf16x8*>(block(u + 4 * q));
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (u + 4 * q < u1) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] += __uint_as_float((uint32_t)(unsigned short)x[q][j] << 16);
-            }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sacc[grp][l][j] = acc[j];
-    __syncthreads();
-    if (t < 16) {
-        const int half = t >> 3, j = t & 7;
-        float s = 0.0f;
-        for (int g = 0; g < 4; ++g)
-            for (int i = 0; i < 32; ++i) s += sacc[g][32 * half + i][j];
-        part[((size_t)h * C + c) * (16 * KS) + 16 * ks + t] = s;
-    }
-}
-
 // Partial soft usage of chunk c of head h from float32 Gamma rows [B H][N][K]: thread k sums
 // gamma[row][k] over the chunk's rows in order (rows u = b N + n).
 __global__ void __launch_bounds__(256)
@@ -117,13 +72,14 @@ __global__ void __launch_bounds__(256)
     part[((size_t)h * C + c) * K + k] = s;
 }
 
-// One workgroup per head: counts (the chunk histograms summed), usage (the C partials in
-// chunk order; partial index of component k is kperm(k) in fragment slot order, k
-// otherwise), used, entropy.
+// One workgroup per head: counts (the chunk histograms summed), usage (the C partials of the
+// head in order: rows h C + c of part when P = 0 (the SIMT chunks), rows
+// (b H + h) P + p for c = b P + p otherwise (the matrix-core workgroups: batch element b,
+// part p)), used, entropy.
 __global__ void __launch_bounds__(kFinishThreads)
     gma_stats_finish(const int* __restrict__ cpart, const float* __restrict__ part, int* __restrict__ counts,
                      float* __restrict__ usage, int* __restrict__ used, float* __restrict__ entropy, int H, int B,
-                     int N, int K, int CH, int C, int pstride, int slot_order) {
+                     int N, int K, int CH, int C, int pstride, int P) {
     __shared__ int hist[GMA_MAX_K];
     const int h = blockIdx.x, t = threadIdx.x;
     const int total = B * N;
@@ -140,12 +96,14 @@ __global__ void __launch_bounds__(kFinishThreads)
     __syncthreads();
     for (int k = t; k < K; k += kFinishThreads) {
         counts[(size_t)h * K + k] = hist[k];
-        const int pi = slot_order ? mf::kperm(k) : k;
+        auto prow = [&](int c) -> size_t {
+            return P == 0 ? (size_t)h * C + c : ((size_t)(c / P) * H + h) * P + c % P;
+        };
         float s = 0.0f;
         for (int c0 = 0; c0 < C; c0 += 16) {
             float v[16];
 #pragma unroll
-            for (int c = 0; c < 16; ++c) v[c] = c0 + c < C ? part[((size_t)h * C + c0 + c) * pstride + pi] : 0.0f;
+            for (int c = 0; c < 16; ++c) v[c] = c0 + c < C ? part[prow(c0 + c) * pstride + k] : 0.0f;
 #pragma unroll
             for (int c = 0; c < 16; ++c)
                 if (c0 + c < C) s += v[c];
@@ -178,8 +136,8 @@ __global__ void __launch_bounds__(kFinishThreads)
 }
 
 struct StatsLayout {
-    size_t lam, cst, gamma, W, C, G, hard, part, cpart, total;
-    int Np, Kp, KS, chunks, per_chunk, hchunks, hper;
+    size_t lam, cst, gamma, W, C, hard, part, cpart, total;
+    int Kp, chunks, per_chunk, parts, hchunks, hper;
 };
 
 StatsLayout stats_layout(const gma_desc& d) {
@@ -189,19 +147,15 @@ StatsLayout stats_layout(const gma_desc& d) {
     if (stats_on_mfma(d)) {
         const mf::Geo g = mf::geometry(d);
         L.Kp = g.Kp;
-        L.KS = g.Kp / 16;
-        L.Np = (d.N + mf::kIterT - 1) / mf::kIterT * mf::kIterT;
-        const int tpb = L.Np / 32;
-        L.chunks = d.N > 0 ? kUsageChunks : 0;
-        L.per_chunk = L.chunks ? (d.B * tpb + L.chunks - 1) / L.chunks : 0;
+        // one usage partial per workgroup of the responsibilities kernel: (b, part) per head
+        L.parts = d.N > 0 ? mf::resp_parts(BH, mf::stats_np(d), nullptr) : 0;
+        L.chunks = d.B * L.parts;
         L.W = off;
         off += align_up((size_t)d.H * g.Kp * 4 * g.Dp * sizeof(bf16_t));
         L.C = off;
         off += align_up((size_t)d.H * g.Kp * sizeof(float));
-        L.G = off;
-        off += align_up((size_t)BH * L.Np * g.Kp * sizeof(bf16_t));
         L.part = off;
-        off += align_up((size_t)d.H * (L.chunks ? L.chunks : 1) * g.Kp * sizeof(float));
+        off += align_up((size_t)BH * (L.parts ? L.parts : 1) * g.Kp * sizeof(float));
     } else {
         L.Kp = d.K;
         // row chunks: about 256 workgroups over the heads
@@ -246,12 +200,7 @@ hipError_t stats_forward(const Args& a) {
         if (mfma) {
             bf16_t* W = reinterpret_cast<bf16_t*>(a.ws + L.W);
             float* cvec = reinterpret_cast<float*>(a.ws + L.C);
-            bf16_t* G = reinterpret_cast<bf16_t*>(a.ws + L.G);
-            if ((e = mf::stats_resp(a, W, cvec, G, hard)) != hipSuccess) return e;
-            rec_begin(a, "gma_stats_usage_frag");
-            gma_stats_usage_frag<<<dim3(L.KS, d.H, L.chunks), dim3(256), 0, a.stream>>>(
-                G, part, d.H, d.B, L.Np / 32, L.KS, L.chunks, L.per_chunk);
-            rec_end(a);
+            if ((e = mf::stats_resp(a, W, cvec, part, hard)) != hipSuccess) return e;
         } else {
             double* lam = reinterpret_cast<double*>(a.ws + L.lam);
             double* cst = reinterpret_cast<double*>(a.ws + L.lam + align_up((size_t)d.H * d.K * d.d_r * sizeof(double)));
@@ -277,7 +226,7 @@ hipError_t stats_forward(const Args& a) {
     rec_begin(a, "gma_stats_finish");
     gma_stats_finish<<<dim3(d.H), dim3(kFinishThreads), 0, a.stream>>>(
         cpart, part, a.counts, a.usage, a.used, a.entropy, d.H, d.B, d.N, d.K, L.hchunks, L.chunks,
-        mfma ? L.Kp : d.K, mfma ? 1 : 0);
+        mfma ? L.Kp : d.K, mfma ? L.parts : 0);
     rec_end(a);
     return hipGetLastError();
 }
