@@ -63,6 +63,8 @@ def algorithmic(w, kernel: str):
     memory_side = 2 * K * (dv + 1)       # Gamma^T [V | 1] or Gamma [Vt | Z]
     if "prep" in kernel or "totals" in kernel or "carry" in kernel:
         return None
+    if "causal_fused_scan" in kernel:  # the whole causal forward, responsibilities on chip
+        return (th + thk) * s * (dr + dv), (th + thk) * (logits_side + memory_side)
     if "bidir_write" in kernel:   # reads k and v, forms Gamma_K and Gamma_K^T [V, 1]
         return thk * s * (dr + dv), thk * (logits_side + memory_side)
     if "bidir_read" in kernel:    # reads q, forms Gamma_Q, Gamma_Q [Vt, Z], writes out
@@ -98,8 +100,8 @@ def elapsed_ms(hip, a, b) -> float:
 
 # Sources the forward kernels (whose HBM traffic profiles/traffic.json records) are built
 # and dispatched from; the backward, decode, statistics and SIMT files do not enter them.
-FORWARD_SOURCES = ("gma_api.cpp", "gma_internal.h", "gma_mfma.hip", "gma_mfma_causal.hip", "gma_mfma_common.h",
-                   "gma_mfma_geo.h", "gma_numeric.h")
+FORWARD_SOURCES = ("gma_api.cpp", "gma_internal.h", "gma_mfma.hip", "gma_mfma_causal.hip", "gma_causal_fused.hip",
+                   "gma_mfma_common.h", "gma_mfma_geo.h", "gma_numeric.h")
 
 
 def kernel_source_hash() -> str:
