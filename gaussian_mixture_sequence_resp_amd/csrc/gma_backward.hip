@@ -29,8 +29,13 @@
 //   bwd_seg_start    each segment's starting state from those partials in segment order: the
 //                  prefix before it (causal pass 1), the suffix after it (causal pass 2) or
 //                  the head's total (bidirectional)
-//   bwd_seg_rows     causal: one workgroup per (b, h, segment) walks its rows (pass 2 in
-//                  reverse) with the state in LDS (in the workspace when it does not fit)
+//   bwd_causal_mfma  causal, bf16 inputs (K <= 256, d_v = 32, 64 or 128): one wave per
+//                  (b, h, segment) walks its rows in chunks of 32 (pass 2 in reverse), the
+//                  chunk's products as fp32 matrix-core tiles against the state in LDS
+//   bwd_seg_chunks   causal otherwise, when the state and a chunk's rows fit LDS: the same
+//                  chunk walk, 16 rows at a time, on the vector ALUs
+//   bwd_seg_rows     causal otherwise: one workgroup per (b, h, segment) walks its rows (pass
+//                  2 in reverse) with the state in LDS (in the workspace when it does not fit)
 //   bwd_bidir_mfma bidirectional, bf16 inputs: the per-row arithmetic against the head's
 //                  total as fp32 matrix-core products over 32-row tiles
 //   bwd_bidir_rows   bidirectional otherwise: the same per-row arithmetic, each wave of a
@@ -731,6 +736,317 @@ __global__ void __launch_bounds__(kBwdThreads)
     }
 }
 
+// Causal rows on the matrix cores (bf16 inputs: float gamma and state): one wave per
+// (b, h, segment) walks the segment in chunks of 32 positions (pass 1 ascending, pass 2
+// descending), the state St (value columns [Kp][32 NTW + 1] and the normaliser column z
+// [Kp]) in LDS.  For chunk rows r and the chunk's rows j on the inclusive side (pass 1:
+// j <= r, pass 2: j >= r), with ga the rows' own gamma, gb the weighted side's, W the
+// weighted rows (pass 1 [v | 1], pass 2 [g_num | g_den]) and X the rows' multipliers
+// (pass 1 [g_num | g_den], formed here; pass 2 [v | 1]):
+//   P^T[j][r]   = gb_j . ga_r                   (masked to the inclusive side)
+//   READ^T      = St^T ga^T + W^T P^T           (pass 1: [num | den - eps]; pass 2: dv)
+//   Q^T[j][r]   = W_j . X_r                     (masked)
+//   DG^T        = St X^T + gb^T Q^T             (dgamma of every row)
+//   dl_r        = ga_r (dg_r - s_r),  s_r = ga_r . dg_r = X_r . READ0_r + Q_r . P_r
+//   St         += gb^T W
+// where READ0 = ga St is READ without the chunk's own rows: the regrouped row sum s_r
+// lets each 32-component tile of DG be finished and stored as soon as it is formed.
+// v_mfma_f32_32x32x2_f32 throughout (fp32 products and sums).  A step contracts one index
+// per lane half, paired so that the register operands are read in the C layout (lane l,
+// register i of a tile: row 8 (i / 4) + 4 (l / 32) + i % 4 of the tile, column l % 32):
+// ga, gb, P^T, X^T and Q^T in that layout; St from LDS (odd row stride: the 32 rows of one
+// column fall in distinct banks); gb^T (gb with rows and components swapped) and W rows
+// loaded from global memory in the operand order each step needs.  The z column (value
+// dv) is handled alongside on the vector ALUs.
+template <int MT, int NTW>
+struct CausalMf {
+    static constexpr int Kp = 32 * MT, Wv = 32 * NTW, Ws = Wv + 1;
+    static size_t lds_bytes() { return ((size_t)Kp * Ws + Kp) * sizeof(float); }
+};
+
+__device__ __forceinline__ int tile_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+template <typename T, int PASS, int MT, int NTW>
+__global__ void __launch_bounds__(64)
+    bwd_causal_mfma(const float* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
+                    float* __restrict__ gnum, float* __restrict__ gden, float* __restrict__ dl,
+                    T* __restrict__ dv_out, const float* __restrict__ start, int BH, int N, int K, int dv, float eps,
+                    int SEG, int L) {
+    extern __shared__ double smem_d[];
+    using C = CausalMf<MT, NTW>;
+    constexpr int Kp = C::Kp, Wv = C::Wv, Ws = C::Ws;
+    float* sS = reinterpret_cast<float*>(smem_d);  // [Kp][Ws]: value columns
+    float* sZ = sS + (size_t)Kp * Ws;               // [Kp]: the normaliser column
+    const int W = dv + 1;                           // dv == Wv
+    const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
+    const int l = threadIdx.x, col = l & 31, h = l >> 5;
+    const float* st0 = start + ((size_t)bh * SEG + seg) * K * W;
+    for (int e = l; e < Kp * Wv; e += 64) {
+        const int k = e / Wv, c = e % Wv;
+        sS[k * Ws + c] = k < K ? st0[(size_t)k * W + c] : 0.0f;
+    }
+    for (int k = l; k < Kp; k += 64) sZ[k] = k < K ? st0[(size_t)k * W + dv] : 0.0f;
+    const float* ga_g = gamma + ((size_t)(PASS == 1 ? 0 : BH) + bh) * N * K;  // the rows' own side
+    const float* gb_g = gamma + ((size_t)(PASS == 1 ? BH : 0) + bh) * N * K;  // the weighted side
+    const T* v_bh = v + (size_t)bh * N * dv;
+    const T* do_bh = dout + (size_t)bh * N * dv;
+    float* gnum_bh = gnum + (size_t)bh * N * dv;
+    float* gden_bh = gden + (size_t)bh * N;
+    float* dl_bh = dl + ((size_t)(PASS == 1 ? 0 : BH) + bh) * N * K;
+    T* dvo_bh = dv_out + (size_t)bh * N * dv;
+    const bool vec_k = (K & 3) == 0;
+    const int i0 = seg * L, i1 = min(N, i0 + L);
+    const int nch = (i1 - i0 + 31) / 32;
+    // W row j (value columns) and its last entry, in float
+    auto wval = [&](int p, int c) -> float {
+        if constexpr (PASS == 1) return Elem<T>::load(v_bh, (size_t)p * dv + c);
+        else return gnum_bh[(size_t)p * dv + c];
+    };
+    auto wz = [&](int p) -> float {
+        if constexpr (PASS == 1) return 1.0f;
+        else return gden_bh[p];
+    };
+    // this lane's row p at its C-layout components 32 m + 8 q + 4 h + (0..3) of tile m (zeros
+    // past K); rows outside the segment are loaded (clamped) and zeroed at the chunk's start,
+    // so that no wait for these loads falls where they are issued
+    auto gamma_tile = [&](const float* g, int p, int m, f32x16& out) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k0 = 32 * m + 8 * q + 4 * h;
+            if (vec_k && k0 < K) {
+                const float4 x = *reinterpret_cast<const float4*>(g + (size_t)p * K + k0);
+                out[4 * q] = x.x;
+                out[4 * q + 1] = x.y;
+                out[4 * q + 2] = x.z;
+                out[4 * q + 3] = x.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[4 * q + e] = k0 + e < K ? g[(size_t)p * K + k0 + e] : 0.0f;
+            }
+        }
+    };
+    auto gamma_c = [&](const float* g, int p, f32x16 (&out)[MT]) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) gamma_tile(g, p, m, out[m]);
+    };
+    // chunk qc's rows r are positions base(qc) + r; rows outside [i0, i1) take no part
+    auto base_of = [&](int qc) { return PASS == 1 ? i0 + 32 * qc : i1 - 32 * (qc + 1); };
+    // gamma of a chunk's rows in the C layout; loaded for chunk 0 here and for chunk qc + 1
+    // into each register array as soon as chunk qc is done with it (ga after the dl tiles,
+    // gb one component tile at a time during the state update), so the loads overlap that
+    // chunk's matrix work
+    f32x16 ga[MT], gb[MT];
+    {
+        const int b0 = base_of(0), p0 = min(max(b0 + col, i0), i1 - 1);
+        gamma_c(ga_g, p0, ga);
+        gamma_c(gb_g, p0, gb);
+    }
+    for (int qc = 0; qc < nch; ++qc) {
+        const int base = base_of(qc);
+        auto in_seg = [&](int r) { return base + r >= i0 && base + r < i1; };
+        auto clampp = [&](int r) { return min(max(base + r, i0), i1 - 1); };
+        const bool okr = in_seg(col);
+        const int pr = clampp(col);  // this lane's row (as r, and as j in the C layouts)
+        // the next chunk's row of this lane (for the refills at the end)
+        const int nbase = base_of(qc + 1);
+        const int pn = min(max(nbase + col, i0), i1 - 1);
+        if (!okr) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ga[m][i] = gb[m][i] = 0.0f;
+        }
+        // ---- P^T = gb ga^T, masked to the inclusive side
+        f32x16 pt;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pt[i] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) pt = mfma_f32(gb[m][i], ga[m][i], pt);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = tile_row(i, h);
+            if (!(PASS == 1 ? j <= col : j >= col)) pt[i] = 0.0f;
+        }
+        // ---- W rows in the operand orders used below: wa[n][i] = W[j = tile_row(i, h)][32 n + col]
+        float wa[NTW][16], wzj[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int pj = clampp(tile_row(i, h));
+            wzj[i] = wz(pj);
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) wa[n][i] = wval(pj, 32 * n + col);
+        }
+        // the epilogue's dO (pass 1) or v (pass 2) at this lane's columns and Q's W operand
+        // (row col at columns 32 n + tile_row(i, h)): loaded now, used after READ0
+        float xrow[NTW][16];
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int c = 32 * n + tile_row(i, h);
+                xrow[n][i] = PASS == 1 ? (float)Elem<T>::load(do_bh, (size_t)pr * dv + c)
+                                       : (float)Elem<T>::load(v_bh, (size_t)pr * dv + c);
+            }
+        // ---- READ0^T = St^T ga^T (value columns) and its z entry; PW^T = W^T P^T
+        f32x16 rd0[NTW], pw[NTW];
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) rd0[n][i] = pw[n][i] = 0.0f;
+        float r0z = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int k = 32 * m + tile_row(i, h);
+                const float* srow = sS + k * Ws + col;
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) rd0[n] = mfma_f32(srow[32 * n], ga[m][i], rd0[n]);
+                r0z = fmaf(ga[m][i], sZ[k], r0z);
+            }
+        r0z = sum_halves(r0z);
+        float pwz = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) pw[n] = mfma_f32(wa[n][i], pt[i], pw[n]);
+            pwz = fmaf(pt[i], wzj[i], pwz);
+        }
+        pwz = sum_halves(pwz);
+        // ---- the rows' multipliers X^T (C layout: register i of tile n is column 32 n + tile_row(i, h))
+        f32x16 x[NTW];
+        float xz;
+        if constexpr (PASS == 1) {
+            const float den = r0z + pwz + eps;
+            float dot = 0.0f;
+            const float(&dov)[NTW][16] = xrow;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dot = fmaf(dov[n][i], (rd0[n][i] + pw[n][i]) / den, dot);
+            const float gd = -sum_halves(dot) / den;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float g = okr ? dov[n][i] / den : 0.0f;
+                    x[n][i] = g;
+                    if (okr) gnum_bh[(size_t)pr * dv + 32 * n + tile_row(i, h)] = g;
+                }
+            xz = okr ? gd : 0.0f;
+            if (okr && h == 0) gden_bh[pr] = gd;
+        } else {
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c = 32 * n + tile_row(i, h);
+                    if (okr) Elem<T>::store(dvo_bh, (size_t)pr * dv + c, rd0[n][i] + pw[n][i]);
+                    x[n][i] = okr ? xrow[n][i] : 0.0f;
+                }
+            xz = okr ? 1.0f : 0.0f;
+        }
+        // ---- Q^T = W X^T, masked (A: W row col at column 32 n + tile_row(i, h))
+        f32x16 qt;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qt[i] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) qt = mfma_f32(wval(pr, 32 * n + tile_row(i, h)), x[n][i], qt);
+        // z: Q^T[j][r] += W[j][dv] X[r][dv]; X[r][dv] of this register's column r = col is this lane's
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = tile_row(i, h);
+            qt[i] = (PASS == 1 ? j <= col : j >= col) ? fmaf(wzj[i], xz, qt[i]) : 0.0f;
+        }
+        // ---- s_r = X_r . READ0_r + Q_r . P_r
+        float sp = xz * r0z * 0.5f;  // both halves add it: half each
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sp = fmaf(x[n][i], rd0[n][i], sp);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sp = fmaf(qt[i], pt[i], sp);
+        const float s = sum_halves(sp);
+        // ---- gb^T: gbt[m][i] = gb[j = tile_row(i, h)][32 m + col] (reusing gb's registers)
+        f32x16 (&gbt)[MT] = gb;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rj = tile_row(i, h);
+            const bool okj = in_seg(rj);
+            const int pj = clampp(rj);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int k = 32 * m + col;
+                gbt[m][i] = (okj && k < K) ? gb_g[(size_t)pj * K + k] : 0.0f;
+            }
+        }
+        // ---- DG^T tile m, then dl; register i of tile m is component 32 m + tile_row(i, h)
+        float* dl_r = dl_bh + (size_t)pr * K;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            f32x16 dg;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dg[i] = 0.0f;
+            const float* srow = sS + (32 * m + col) * Ws;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dg = mfma_f32(srow[32 * n + tile_row(i, h)], x[n][i], dg);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dg = mfma_f32(gbt[m][i], qt[i], dg);
+            if (okr) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k0 = 32 * m + 8 * q + 4 * h;
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float dgz = fmaf(sZ[k0 + e], xz, dg[4 * q + e]);
+                        o[e] = ga[m][4 * q + e] * (dgz - s);
+                    }
+                    if (vec_k && k0 < K) {
+                        *reinterpret_cast<float4*>(dl_r + k0) = make_float4(o[0], o[1], o[2], o[3]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (k0 + e < K) dl_r[k0 + e] = o[e];
+                    }
+                }
+            }
+        }
+        // ga is done with: the next chunk's rows go in now
+        if (qc + 1 < nch) gamma_c(ga_g, pn, ga);
+        // ---- St += gb^T W (rows k of tile m, columns 32 n + col), z += gb^T W[:, dv]; then
+        //      tile m of gb^T is done with and takes tile m of the next chunk's gb
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) {
+                f32x16 u;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) u[i] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) u = mfma_f32(gbt[m][i], wa[n][i], u);
+                float old_s[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) old_s[i] = sS[(32 * m + tile_row(i, h)) * Ws + 32 * n + col];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sS[(32 * m + tile_row(i, h)) * Ws + 32 * n + col] = old_s[i] + u[i];
+            }
+            float zp = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) zp = fmaf(gbt[m][i], wzj[i], zp);
+            zp = sum_halves(zp);
+            if (h == 0) sZ[32 * m + col] += zp;
+            if (qc + 1 < nch) gamma_tile(gb_g, pn, m, gb[m]);
+        }
+    }
+}
+
 // dx of both sides: dx[side][bh][i][d] = -sum_k dl_k (x_d - mu_kd) lam_kd = Q_d - x_d P_d with
 // P_d = sum_k dl_k lam_kd and Q_d = sum_k dl_k mu_kd lam_kd: a tile of 64 rows of one (side, bh)
 // and 64 dims per workgroup, the components in blocks of 32 staged in LDS (in A), each
@@ -1138,6 +1454,36 @@ hipError_t launch_bidir_mfma_t(const Args& a, const BwdArgs& g, const float* gam
     return hipGetLastError();
 }
 
+template <typename T, int PASS, int MT, int NTW>
+hipError_t launch_causal_mfma_t(const Args& a, const BwdArgs& g, const float* gamma, float* gnum, float* gden,
+                                float* dl, const float* start, const BwdLayout& L) {
+    const gma_desc& d = a.d;
+    const int BH = d.B * d.H;
+    const size_t lds = CausalMf<MT, NTW>::lds_bytes();
+    hipError_t e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_causal_mfma<T, PASS, MT, NTW>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    bwd_causal_mfma<T, PASS, MT, NTW><<<dim3((unsigned)(BH * L.seg)), dim3(64), lds, a.stream>>>(
+        gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
+        start, BH, d.N, d.K, d.d_v, a.eps, L.seg, L.seg_len);
+    return hipGetLastError();
+}
+
+// MT = 32-component tiles (1, 2, 4 or 8), NTW = 32-column value tiles (1, 2 or 4: d_v = 32 NTW).
+template <typename T, int PASS>
+hipError_t launch_causal_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, const float* gamma, float* gnum,
+                              float* gden, float* dl, const float* start, const BwdLayout& L) {
+#define GMA_BWD_CMF(mt, ntw) \
+    if (MT == mt && NTW == ntw) return launch_causal_mfma_t<T, PASS, mt, ntw>(a, g, gamma, gnum, gden, dl, start, L);
+    GMA_BWD_CMF(1, 1) GMA_BWD_CMF(1, 2) GMA_BWD_CMF(1, 4)
+    GMA_BWD_CMF(2, 1) GMA_BWD_CMF(2, 2) GMA_BWD_CMF(2, 4)
+    GMA_BWD_CMF(4, 1) GMA_BWD_CMF(4, 2) GMA_BWD_CMF(4, 4)
+    GMA_BWD_CMF(8, 1) GMA_BWD_CMF(8, 2) GMA_BWD_CMF(8, 4)
+#undef GMA_BWD_CMF
+    return hipErrorInvalidValue;
+}
+
 // MT = 32-component tiles (1, 2 or 4), NTW = 32-column tiles of the state (1, 2 or 3).
 template <typename T, int PASS>
 hipError_t launch_bidir_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, const float* gamma, float* gnum,
@@ -1312,6 +1658,17 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
             start, st_global ? start : nullptr, BH, d.N, d.K, d.d_v, a.eps, L.seg, L.seg_len);
         rec_end(a);
         return hipGetLastError();
+    }
+    if constexpr (sizeof(A) == sizeof(float)) {
+        // bf16 inputs: the chunk walk on the matrix cores, one wave per segment
+        const int MT = d.K <= 32 ? 1 : (d.K <= 64 ? 2 : (d.K <= 128 ? 4 : (d.K <= 256 ? 8 : 0)));
+        const int NTW = d.d_v == 32 ? 1 : (d.d_v == 64 ? 2 : (d.d_v == 128 ? 4 : 0));
+        if (MT > 0 && NTW > 0) {
+            rec_begin(a, PASS == 1 ? "bwd_rows_1" : "bwd_rows_2");
+            e = launch_causal_mfma<T, PASS>(a, g, MT, NTW, gamma, gnum, gden, dl, start, L);
+            rec_end(a);
+            return e;
+        }
     }
     const size_t chunk_lds = scan_state(d) + (size_t)(2 * kCh * (d.K + 1) + 2 * kCh * (d.d_v + 2) + 2 * kCh * kCh) *
                                                  acc_size(d);

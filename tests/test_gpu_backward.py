@@ -58,6 +58,9 @@ SHAPES = [
     (4, 4, 4096, 16, 16, 32), (4, 8, 4000, 16, 24, 20),
     # state widths at the 32-column tile edges (d_v + 1 = 96 and 32), K padded within a tile
     (1, 2, 100, 32, 95, 96), (2, 1, 70, 8, 31, 64),
+    # causal bf16 chunk walk on the matrix cores: d_v = 32 and 64, K within a tile (ragged,
+    # not a multiple of 4), segments and their last chunks ragged
+    (4, 4, 1000, 16, 32, 64), (2, 4, 777, 32, 64, 99),
 ]
 
 
