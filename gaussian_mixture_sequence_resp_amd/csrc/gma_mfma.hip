@@ -124,23 +124,42 @@ __global__ void __launch_bounds__(256) gma_prep(const float* __restrict__ mu, co
 
 // ---------------------------------------------------------------------------------- write
 // Raw V values of one token row for this lane: dims 8 half + 16 j, j < NT * 2 (zero-padded;
-// d_v is a multiple of 8 on this path).
-template <int NT>
+// d_v is a multiple of 8 on this path).  FULL (d_v = 32 NT): every load is whole, so the loads
+// are unconditional and no register is zeroed first (a conditional load costs a move per
+// register and splits the scheduling region).
+template <int NT, bool FULL>
 __device__ __forceinline__ void load_vrow(bf16x8 (&vr)[2 * NT], const bf16_t* row, int dv) {
     const int half = lane_id() >> 5;
 #pragma unroll
     for (int j = 0; j < 2 * NT; ++j) {
         const int d0 = 16 * j + 8 * half;
-        bf16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(row + d0);
-        vr[j] = x;
+        if (FULL) {
+            vr[j] = *reinterpret_cast<const bf16x8*>(row + d0);
+        } else {
+            bf16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (d0 < dv) x = *reinterpret_cast<const bf16x8*>(row + d0);
+            vr[j] = x;
+        }
+    }
+}
+
+// Routing values of one token row for this lane (as load_xrow); FULL: d_r = 16 NC, no tail,
+// unconditional loads.
+template <int NC, bool FULL>
+__device__ __forceinline__ void load_krow(bf16x8 (&xr)[NC], const bf16_t* row, int dr) {
+    if (FULL) {
+        const int h = lane_id() >> 5;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) xr[c] = *reinterpret_cast<const bf16x8*>(row + 16 * c + 8 * h);
+    } else {
+        load_xrow<NC>(xr, row, dr);
     }
 }
 
 // Stage assignment of the four softmax stages over the U units of a pipelined logits tile.
 __host__ __device__ constexpr int stage_unit(int st, int U) { return (st * U) / 4; }
 
-template <int MT, int NT, int NC>
+template <int MT, int NT, int NC, bool FULL>
 __global__ void __launch_bounds__(kThreads, 1)
     gma_bidir_write(const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v, const bf16_t* __restrict__ W,
                     const float* __restrict__ cvec, float* __restrict__ part_v, float* __restrict__ part_z, int BH,
@@ -197,16 +216,16 @@ __global__ void __launch_bounds__(kThreads, 1)
     {
         CoefRegs<MT, NC, kThreads> cr;
         cr.load(W, cvec, h);
-        load_xrow<NC>(xa, krow(0), dr);
-        load_xrow<NC>(xb, krow(1), dr);
-        load_vrow<NT>(vcur, vrow(0), dv);
+        load_krow<NC, FULL>(xa, krow(0), dr);
+        load_krow<NC, FULL>(xb, krow(1), dr);
+        load_vrow<NT, FULL>(vcur, vrow(0), dv);
         cr.store(sW, sC, wstride);
     }
     __syncthreads();
 
     f32x16 accA[MT], accB[MT];
     tile_logits_overlap<MT, NC>(accA, xa, sW, wstride, sC, [](int, int) {});
-    load_xrow<NC>(xa, krow(2), dr);
+    load_krow<NC, FULL>(xa, krow(2), dr);
 
     // One pipeline step: finish tile `it` (softmax, stage Gamma_K and V rows in LDS) while the
     // logits of tile it+1 run, then the LDS-fed update over the 128 staged positions.
@@ -214,7 +233,7 @@ __global__ void __launch_bounds__(kThreads, 1)
         const int t = n_begin + it * kIterT + kTileT * w + col;
         const bool valid = t < n_end;
         bf16x8 vnext[2 * NT];
-        load_vrow<NT>(vnext, vrow(it + 1), dv);
+        load_vrow<NT, FULL>(vnext, vrow(it + 1), dv);
         SoftmaxStages<MT> sm;
         unsigned char* grow = sG + (size_t)(kTileT * w + col) * gs;
         unsigned char* vdst = sV + (size_t)(kTileT * w + col) * vs;
@@ -227,17 +246,38 @@ __global__ void __launch_bounds__(kThreads, 1)
                 for (int j = 0; j < 2 * NT; ++j) *reinterpret_cast<bf16x8*>(vdst + 2 * (16 * j + 8 * half)) = vcur[j];
             }
         });
-        load_xrow<NC>(xfar, krow(it + 3), dr);
+        load_krow<NC, FULL>(xfar, krow(it + 3), dr);
         lds_barrier();
         update_from_lds<MT, NT, UT::MW, UT::NW>(wacc, sG, gs, sV, vs, ones);
         lds_barrier();
 #pragma unroll
         for (int j = 0; j < 2 * NT; ++j) vcur[j] = vnext[j];
     };
-    // xa holds step it+2's rows when step `it` starts with nxt rows in xb (and vice versa)
-    for (int it = 0; it < nit; it += 2) {
+    // The last step has no next tile: softmax and update only.
+    auto last = [&](int it, f32x16 (&cur)[MT]) {
+        const int t = n_begin + it * kIterT + kTileT * w + col;
+        const bool valid = t < n_end;
+        SoftmaxStages<MT> sm;
+        unsigned char* grow = sG + (size_t)(kTileT * w + col) * gs;
+        unsigned char* vdst = sV + (size_t)(kTileT * w + col) * vs;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) sm.stage(st, cur, valid, grow);
+#pragma unroll
+        for (int j = 0; j < 2 * NT; ++j) *reinterpret_cast<bf16x8*>(vdst + 2 * (16 * j + 8 * half)) = vcur[j];
+        lds_barrier();
+        update_from_lds<MT, NT, UT::MW, UT::NW>(wacc, sG, gs, sV, vs, ones);
+    };
+    // Steps run in pairs (an odd count gets one step past the split, all of whose rows are
+    // zeroed), so the loop body has no branch: xa holds step it+2's rows when step `it` starts
+    // with nxt rows in xb (and vice versa).
+    const int nit2 = (nit + 1) & ~1;
+    for (int it = 0; it + 2 < nit2; it += 2) {
         step(it, accA, accB, xb, xb);
-        if (it + 1 < nit) step(it + 1, accB, accA, xa, xa);
+        step(it + 1, accB, accA, xa, xa);
+    }
+    if (nit2 > 0) {
+        step(nit2 - 2, accA, accB, xb, xb);
+        last(nit2 - 1, accB);
     }
 
     // ---- partial of this split -> workspace (fp32)
@@ -461,40 +501,50 @@ typedef void (*WriteFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float
 typedef void (*ReadFn)(const bf16_t*, const bf16_t*, const float*, const float*, const float*, bf16_t*, float, int,
                        int, int, int, int, int, int, int);
 
+// The exact-fit write kernel is built where it does not spill registers (the largest tiles
+// keep the general form).
+constexpr bool write_full_ok(int MT, int NT, int NC) { return MT <= 4 && MT * NT * NC < 128; }
+
 template <int MT, int NT, int NC>
-bool pick(WriteFn& wf, ReadFn& rf) {
-    wf = gma_bidir_write<MT, NT, NC>;
+bool pick(bool full, WriteFn& wf, ReadFn& rf) {
+    if constexpr (write_full_ok(MT, NT, NC))
+        wf = full ? gma_bidir_write<MT, NT, NC, true> : gma_bidir_write<MT, NT, NC, false>;
+    else
+        wf = gma_bidir_write<MT, NT, NC, false>;
     rf = gma_bidir_read<MT, NT, NC>;
     return true;
 }
 
 template <int MT, int NT>
-bool select_nc(int NC, WriteFn& wf, ReadFn& rf) {
+bool select_nc(int NC, bool full, WriteFn& wf, ReadFn& rf) {
     switch (NC) {
-        case 1: return pick<MT, NT, 1>(wf, rf);
-        case 2: return pick<MT, NT, 2>(wf, rf);
-        case 4: return pick<MT, NT, 4>(wf, rf);
-        case 8: return pick<MT, NT, 8>(wf, rf);
+        case 1: return pick<MT, NT, 1>(full, wf, rf);
+        case 2: return pick<MT, NT, 2>(full, wf, rf);
+        case 4: return pick<MT, NT, 4>(full, wf, rf);
+        case 8: return pick<MT, NT, 8>(full, wf, rf);
     }
     return false;
 }
 
 template <int MT>
-bool select_nt(int NT, int NC, WriteFn& wf, ReadFn& rf) {
+bool select_nt(int NT, int NC, bool full, WriteFn& wf, ReadFn& rf) {
     switch (NT) {
-        case 1: return select_nc<MT, 1>(NC, wf, rf);
-        case 2: return select_nc<MT, 2>(NC, wf, rf);
-        case 4: return select_nc<MT, 4>(NC, wf, rf);
+        case 1: return select_nc<MT, 1>(NC, full, wf, rf);
+        case 2: return select_nc<MT, 2>(NC, full, wf, rf);
+        case 4: return select_nc<MT, 4>(NC, full, wf, rf);
     }
     return false;
 }
 
-bool select(const Geo& g, WriteFn& wf, ReadFn& rf) {
+bool select(const Geo& g, const gma_desc& d, WriteFn& wf, ReadFn& rf) {
+    // exact fit (d_r = Dp, d_v = Dvp): every row load of the write kernel is whole, no zero
+    // tail (the read kernel measured no faster in that form)
+    const bool full = d.d_r == g.Dp && d.d_v == g.Dvp;
     switch (g.MT) {
-        case 1: return select_nt<1>(g.NT, g.NC, wf, rf);
-        case 2: return select_nt<2>(g.NT, g.NC, wf, rf);
-        case 4: return select_nt<4>(g.NT, g.NC, wf, rf);
-        case 8: return select_nt<8>(g.NT, g.NC, wf, rf);
+        case 1: return select_nt<1>(g.NT, g.NC, full, wf, rf);
+        case 2: return select_nt<2>(g.NT, g.NC, full, wf, rf);
+        case 4: return select_nt<4>(g.NT, g.NC, full, wf, rf);
+        case 8: return select_nt<8>(g.NT, g.NC, full, wf, rf);
     }
     return false;
 }
@@ -540,7 +590,7 @@ static hipError_t bidir_forward(const Args& a) {
 
     WriteFn wf;
     ReadFn rf;
-    if (!select(g, wf, rf)) return hipErrorNotSupported;
+    if (!select(g, d, wf, rf)) return hipErrorNotSupported;
 
     if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
 
@@ -606,7 +656,7 @@ hipError_t mfma_memory(const Args& a) {
     hipError_t e;
     WriteFn wf;
     ReadFn rf;
-    if (!select(g, wf, rf)) return hipErrorNotSupported;
+    if (!select(g, d, wf, rf)) return hipErrorNotSupported;
     if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
     const int S = num_splits(d, N);
     const int split_len = ((N + S - 1) / S + kIterT - 1) / kIterT * kIterT;
