@@ -29,9 +29,12 @@
 //   bwd_seg_start    each segment's starting state from those partials in segment order: the
 //                  prefix before it (causal pass 1), the suffix after it (causal pass 2) or
 //                  the head's total (bidirectional)
-//   bwd_causal_mfma  causal, bf16 inputs (K <= 256, d_v = 32, 64 or 128): one wave per
+//   bwd_causal_mfma  causal, bf16 inputs (K <= 128, d_v = 32, 64 or 128): one wave per
 //                  (b, h, segment) walks its rows in chunks of 32 (pass 2 in reverse), the
 //                  chunk's products as fp32 matrix-core tiles against the state in LDS
+//   bwd_causal_mfma2 the same for 128 < K <= 256 with two waves per (b, h, segment), each
+//                  half the components (the contractions over the components added
+//                  through LDS)
 //   bwd_seg_chunks   causal otherwise, when the state and a chunk's rows fit LDS: the same
 //                  chunk walk, 16 rows at a time, on the vector ALUs
 //   bwd_seg_rows     causal otherwise: one workgroup per (b, h, segment) walks its rows (pass
@@ -1047,6 +1050,333 @@ __global__ void __launch_bounds__(64)
     }
 }
 
+// The same chunk walk with the components split over two waves (K up to 256: wave w takes
+// component tiles 4 w .. 4 w + 3), so that a workgroup's state is worked on by two SIMDs and
+// two workgroups fit in a CU's LDS: each wave forms its components' part of P^T and READ0^T
+// (contractions over the components), wave 1 hands its parts to wave 0 through LDS, wave 0
+// adds them (wave 0's part first) and hands the sums back, and both then form PW^T, X^T,
+// Q^T and s from the same sums (bitwise the same on both waves); DG^T, dl and the state
+// update are per component, each wave its own tiles.  Two barriers per chunk.
+template <int NTW>
+struct CausalMf2 {
+    static constexpr int MT = 8, MTH = 4, Kp = 32 * MT, Wv = 32 * NTW, Ws = Wv + 1;
+    // exchange block: P^T part (16 floats per lane), READ0^T part (NTW x 16), r0z part (1)
+    static constexpr int XF = 16 + 16 * NTW + 1;
+    static size_t lds_bytes() { return ((size_t)Kp * Ws + Kp + (size_t)64 * XF) * sizeof(float); }
+};
+
+template <typename T, int PASS, int NTW>
+__global__ void __launch_bounds__(128)
+    bwd_causal_mfma2(const float* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
+                     float* __restrict__ gnum, float* __restrict__ gden, float* __restrict__ dl,
+                     T* __restrict__ dv_out, const float* __restrict__ start, int BH, int N, int K, int dv, float eps,
+                     int SEG, int L) {
+    extern __shared__ double smem_d[];
+    using C = CausalMf2<NTW>;
+    constexpr int MTH = C::MTH, Kp = C::Kp, Wv = C::Wv, Ws = C::Ws, XF = C::XF;
+    float* sS = reinterpret_cast<float*>(smem_d);  // [Kp][Ws]: value columns
+    float* sZ = sS + (size_t)Kp * Ws;               // [Kp]: the normaliser column
+    float* sX = sZ + Kp;                            // [XF][64]: the exchange block
+    const int W = dv + 1;                           // dv == Wv
+    const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
+    const int l = threadIdx.x & 63, col = l & 31, h = l >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kb = 32 * MTH * wv;  // this wave's first component
+    const float* st0 = start + ((size_t)bh * SEG + seg) * K * W;
+    // each wave loads (and later updates) only its own components' state rows
+    for (int e = l; e < 32 * MTH * Wv; e += 64) {
+        const int k = kb + e / Wv, c = e % Wv;
+        sS[k * Ws + c] = k < K ? st0[(size_t)k * W + c] : 0.0f;
+    }
+    for (int k = kb + l; k < kb + 32 * MTH; k += 64) sZ[k] = k < K ? st0[(size_t)k * W + dv] : 0.0f;
+    const float* ga_g = gamma + ((size_t)(PASS == 1 ? 0 : BH) + bh) * N * K;  // the rows' own side
+    const float* gb_g = gamma + ((size_t)(PASS == 1 ? BH : 0) + bh) * N * K;  // the weighted side
+    const T* v_bh = v + (size_t)bh * N * dv;
+    const T* do_bh = dout + (size_t)bh * N * dv;
+    float* gnum_bh = gnum + (size_t)bh * N * dv;
+    float* gden_bh = gden + (size_t)bh * N;
+    float* dl_bh = dl + ((size_t)(PASS == 1 ? 0 : BH) + bh) * N * K;
+    T* dvo_bh = dv_out + (size_t)bh * N * dv;
+    const bool vec_k = (K & 3) == 0;
+    const int i0 = seg * L, i1 = min(N, i0 + L);
+    const int nch = (i1 - i0 + 31) / 32;
+    auto wval = [&](int p, int c) -> float {
+        if constexpr (PASS == 1) return Elem<T>::load(v_bh, (size_t)p * dv + c);
+        else return gnum_bh[(size_t)p * dv + c];
+    };
+    auto wz = [&](int p) -> float {
+        if constexpr (PASS == 1) return 1.0f;
+        else return gden_bh[p];
+    };
+    // this lane's row p at its C-layout components kb + 32 m + 8 q + 4 h + (0..3) (zeros past K)
+    auto gamma_tile = [&](const float* g, int p, int m, f32x16& out) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k0 = kb + 32 * m + 8 * q + 4 * h;
+            if (vec_k && k0 < K) {
+                const float4 x = *reinterpret_cast<const float4*>(g + (size_t)p * K + k0);
+                out[4 * q] = x.x;
+                out[4 * q + 1] = x.y;
+                out[4 * q + 2] = x.z;
+                out[4 * q + 3] = x.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[4 * q + e] = k0 + e < K ? g[(size_t)p * K + k0 + e] : 0.0f;
+            }
+        }
+    };
+    auto gamma_c = [&](const float* g, int p, f32x16 (&out)[MTH]) {
+#pragma unroll
+        for (int m = 0; m < MTH; ++m) gamma_tile(g, p, m, out[m]);
+    };
+    auto base_of = [&](int qc) { return PASS == 1 ? i0 + 32 * qc : i1 - 32 * (qc + 1); };
+    f32x16 ga[MTH], gb[MTH];
+    {
+        const int b0 = base_of(0), p0 = min(max(b0 + col, i0), i1 - 1);
+        gamma_c(ga_g, p0, ga);
+        gamma_c(gb_g, p0, gb);
+    }
+    for (int qc = 0; qc < nch; ++qc) {
+        const int base = base_of(qc);
+        auto in_seg = [&](int r) { return base + r >= i0 && base + r < i1; };
+        auto clampp = [&](int r) { return min(max(base + r, i0), i1 - 1); };
+        const bool okr = in_seg(col);
+        const int pr = clampp(col);
+        const int nbase = base_of(qc + 1);
+        const int pn = min(max(nbase + col, i0), i1 - 1);
+        if (!okr) {
+#pragma unroll
+            for (int m = 0; m < MTH; ++m)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ga[m][i] = gb[m][i] = 0.0f;
+        }
+        // ---- this wave's parts of P^T = gb ga^T and READ0^T = St^T ga^T (and its z entry)
+        f32x16 pt, rd0[NTW];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pt[i] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) rd0[n][i] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MTH; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) pt = mfma_f32(gb[m][i], ga[m][i], pt);
+        // ---- W rows in the operand orders used below (loads in flight during READ0)
+        float wa[NTW][16], wzj[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int pj = clampp(tile_row(i, h));
+            wzj[i] = wz(pj);
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) wa[n][i] = wval(pj, 32 * n + col);
+        }
+        float xrow[NTW][16];
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int c = 32 * n + tile_row(i, h);
+                xrow[n][i] = PASS == 1 ? (float)Elem<T>::load(do_bh, (size_t)pr * dv + c)
+                                       : (float)Elem<T>::load(v_bh, (size_t)pr * dv + c);
+            }
+        float r0z = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MTH; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int k = kb + 32 * m + tile_row(i, h);
+                const float* srow = sS + k * Ws + col;
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) rd0[n] = mfma_f32(srow[32 * n], ga[m][i], rd0[n]);
+                r0z = fmaf(ga[m][i], sZ[k], r0z);
+            }
+        // ---- exchange: wave 1's parts to wave 0, the sums (wave 0's part first) back
+        if (wv == 1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sX[i * 64 + l] = pt[i];
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sX[(16 + 16 * n + i) * 64 + l] = rd0[n][i];
+            sX[(XF - 1) * 64 + l] = r0z;
+        }
+        __syncthreads();
+        if (wv == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                pt[i] = pt[i] + sX[i * 64 + l];
+                sX[i * 64 + l] = pt[i];
+            }
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    rd0[n][i] = rd0[n][i] + sX[(16 + 16 * n + i) * 64 + l];
+                    sX[(16 + 16 * n + i) * 64 + l] = rd0[n][i];
+                }
+            r0z = r0z + sX[(XF - 1) * 64 + l];
+            sX[(XF - 1) * 64 + l] = r0z;
+        }
+        __syncthreads();
+        if (wv == 1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) pt[i] = sX[i * 64 + l];
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) rd0[n][i] = sX[(16 + 16 * n + i) * 64 + l];
+            r0z = sX[(XF - 1) * 64 + l];
+        }
+        r0z = sum_halves(r0z);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = tile_row(i, h);
+            if (!(PASS == 1 ? j <= col : j >= col)) pt[i] = 0.0f;
+        }
+        // ---- PW^T = W^T P^T (both waves, from the same sums)
+        f32x16 pw[NTW];
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) pw[n][i] = 0.0f;
+        float pwz = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) pw[n] = mfma_f32(wa[n][i], pt[i], pw[n]);
+            pwz = fmaf(pt[i], wzj[i], pwz);
+        }
+        pwz = sum_halves(pwz);
+        // ---- X^T (the rows' outputs are stored by wave 0)
+        f32x16 x[NTW];
+        float xz;
+        if constexpr (PASS == 1) {
+            const float den = r0z + pwz + eps;
+            float dot = 0.0f;
+            const float(&dov)[NTW][16] = xrow;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dot = fmaf(dov[n][i], (rd0[n][i] + pw[n][i]) / den, dot);
+            const float gd = -sum_halves(dot) / den;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float g = okr ? dov[n][i] / den : 0.0f;
+                    x[n][i] = g;
+                    if (okr && wv == 0) gnum_bh[(size_t)pr * dv + 32 * n + tile_row(i, h)] = g;
+                }
+            xz = okr ? gd : 0.0f;
+            if (okr && h == 0 && wv == 0) gden_bh[pr] = gd;
+        } else {
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c = 32 * n + tile_row(i, h);
+                    if (okr && wv == 0) Elem<T>::store(dvo_bh, (size_t)pr * dv + c, rd0[n][i] + pw[n][i]);
+                    x[n][i] = okr ? xrow[n][i] : 0.0f;
+                }
+            xz = okr ? 1.0f : 0.0f;
+        }
+        // ---- Q^T = W X^T, masked (both waves)
+        f32x16 qt;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qt[i] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) qt = mfma_f32(wval(pr, 32 * n + tile_row(i, h)), x[n][i], qt);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = tile_row(i, h);
+            qt[i] = (PASS == 1 ? j <= col : j >= col) ? fmaf(wzj[i], xz, qt[i]) : 0.0f;
+        }
+        // ---- s_r = X_r . READ0_r + Q_r . P_r (both waves, the same order)
+        float sp = xz * r0z * 0.5f;
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sp = fmaf(x[n][i], rd0[n][i], sp);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sp = fmaf(qt[i], pt[i], sp);
+        const float s = sum_halves(sp);
+        // ---- gb^T of this wave's tiles (reusing gb's registers)
+        f32x16 (&gbt)[MTH] = gb;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rj = tile_row(i, h);
+            const bool okj = in_seg(rj);
+            const int pj = clampp(rj);
+#pragma unroll
+            for (int m = 0; m < MTH; ++m) {
+                const int k = kb + 32 * m + col;
+                gbt[m][i] = (okj && k < K) ? gb_g[(size_t)pj * K + k] : 0.0f;
+            }
+        }
+        // ---- DG^T of this wave's tiles, then dl
+        float* dl_r = dl_bh + (size_t)pr * K;
+#pragma unroll
+        for (int m = 0; m < MTH; ++m) {
+            f32x16 dg;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dg[i] = 0.0f;
+            const float* srow = sS + (kb + 32 * m + col) * Ws;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dg = mfma_f32(srow[32 * n + tile_row(i, h)], x[n][i], dg);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dg = mfma_f32(gbt[m][i], qt[i], dg);
+            if (okr) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k0 = kb + 32 * m + 8 * q + 4 * h;
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float dgz = fmaf(sZ[k0 + e], xz, dg[4 * q + e]);
+                        o[e] = ga[m][4 * q + e] * (dgz - s);
+                    }
+                    if (vec_k && k0 < K) {
+                        *reinterpret_cast<float4*>(dl_r + k0) = make_float4(o[0], o[1], o[2], o[3]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (k0 + e < K) dl_r[k0 + e] = o[e];
+                    }
+                }
+            }
+        }
+        if (qc + 1 < nch) gamma_c(ga_g, pn, ga);
+        // ---- St += gb^T W, z += gb^T W[:, dv] over this wave's tiles
+#pragma unroll
+        for (int m = 0; m < MTH; ++m) {
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) {
+                f32x16 u;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) u[i] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) u = mfma_f32(gbt[m][i], wa[n][i], u);
+                float old_s[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) old_s[i] = sS[(kb + 32 * m + tile_row(i, h)) * Ws + 32 * n + col];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sS[(kb + 32 * m + tile_row(i, h)) * Ws + 32 * n + col] = old_s[i] + u[i];
+            }
+            float zp = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) zp = fmaf(gbt[m][i], wzj[i], zp);
+            zp = sum_halves(zp);
+            if (h == 0) sZ[kb + 32 * m + col] += zp;
+            if (qc + 1 < nch) gamma_tile(gb_g, pn, m, gb[m]);
+        }
+    }
+}
+
 // dx of both sides: dx[side][bh][i][d] = -sum_k dl_k (x_d - mu_kd) lam_kd = Q_d - x_d P_d with
 // P_d = sum_k dl_k lam_kd and Q_d = sum_k dl_k mu_kd lam_kd: a tile of 64 rows of one (side, bh)
 // and 64 dims per workgroup, the components in blocks of 32 staged in LDS (in A), each
@@ -1470,16 +1800,37 @@ hipError_t launch_causal_mfma_t(const Args& a, const BwdArgs& g, const float* ga
     return hipGetLastError();
 }
 
+template <typename T, int PASS, int NTW>
+hipError_t launch_causal_mfma2_t(const Args& a, const BwdArgs& g, const float* gamma, float* gnum, float* gden,
+                                 float* dl, const float* start, const BwdLayout& L) {
+    const gma_desc& d = a.d;
+    const int BH = d.B * d.H;
+    const size_t lds = CausalMf2<NTW>::lds_bytes();
+    hipError_t e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_causal_mfma2<T, PASS, NTW>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    bwd_causal_mfma2<T, PASS, NTW><<<dim3((unsigned)(BH * L.seg)), dim3(128), lds, a.stream>>>(
+        gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
+        start, BH, d.N, d.K, d.d_v, a.eps, L.seg, L.seg_len);
+    return hipGetLastError();
+}
+
 // MT = 32-component tiles (1, 2, 4 or 8), NTW = 32-column value tiles (1, 2 or 4: d_v = 32 NTW).
+// Eight component tiles (128 < K <= 256) take the two-wave form.
 template <typename T, int PASS>
 hipError_t launch_causal_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, const float* gamma, float* gnum,
                               float* gden, float* dl, const float* start, const BwdLayout& L) {
+    if (MT == 8) {
+        if (NTW == 1) return launch_causal_mfma2_t<T, PASS, 1>(a, g, gamma, gnum, gden, dl, start, L);
+        if (NTW == 2) return launch_causal_mfma2_t<T, PASS, 2>(a, g, gamma, gnum, gden, dl, start, L);
+        if (NTW == 4) return launch_causal_mfma2_t<T, PASS, 4>(a, g, gamma, gnum, gden, dl, start, L);
+    }
 #define GMA_BWD_CMF(mt, ntw) \
     if (MT == mt && NTW == ntw) return launch_causal_mfma_t<T, PASS, mt, ntw>(a, g, gamma, gnum, gden, dl, start, L);
     GMA_BWD_CMF(1, 1) GMA_BWD_CMF(1, 2) GMA_BWD_CMF(1, 4)
     GMA_BWD_CMF(2, 1) GMA_BWD_CMF(2, 2) GMA_BWD_CMF(2, 4)
     GMA_BWD_CMF(4, 1) GMA_BWD_CMF(4, 2) GMA_BWD_CMF(4, 4)
-    GMA_BWD_CMF(8, 1) GMA_BWD_CMF(8, 2) GMA_BWD_CMF(8, 4)
 #undef GMA_BWD_CMF
     return hipErrorInvalidValue;
 }

@@ -61,6 +61,9 @@ SHAPES = [
     # causal bf16 chunk walk on the matrix cores: d_v = 32 and 64, K within a tile (ragged,
     # not a multiple of 4), segments and their last chunks ragged
     (4, 4, 1000, 16, 32, 64), (2, 4, 777, 32, 64, 99),
+    # eight component tiles (two waves per segment, each half the components): K not a multiple
+    # of 4 with the second wave's components mostly padding, and d_v = 32
+    (2, 2, 333, 64, 64, 131), (1, 3, 250, 32, 32, 200),
 ]
 
 
