@@ -22,7 +22,9 @@
 //            intra-group affinity Gamma_K Gamma_Q^T, zero above the diagonal (positions after i
 //            cannot reach O_i); after a barrier the value waves add affinity x [V | 1];
 //   update   every wave: its state tiles (its components x [value dims | 1], fp32 in
-//            registers) += Gamma_K^T [V | 1] over the group, then its part of the bf16 shadow.
+//            registers) += Gamma_K^T [V | 1] over the group, then its part of the bf16 shadow;
+//            waves 4..7, which hold no output tile, also stage the next group's rows (the
+//            exact x^2 split into LDS) and load the rows of the group after it.
 // The sequence of a head is cut into segments that run in parallel; the state entering a
 // segment is the ordered sum of the totals Gamma_K^T [V | 1] of the sub-segments before it,
 // which the same kernel computes in its totals mode (key side only) beforehand.
@@ -115,6 +117,65 @@ struct VRows {
         constexpr int VSt = 2 * Dvs + 32;
         const int t = threadIdx.x;
         unsigned char* dst = t < 4 * Dvs ? sV + (size_t)(t / (Dvs / 8)) * VSt + 16 * (t % (Dvs / 8)) : dummy;
+        *reinterpret_cast<bf16x8*>(dst) = v;
+    }
+};
+
+// The same staging done by the waves 4..7 alone (256 threads, index ts): XV vectors of
+// routing rows and one of value rows per thread.  In the scan these waves have the least work
+// after the responsibilities are in LDS (the output tiles are on waves 0..NTS+1), so the next
+// group's rows are split, stored and the following group's loaded there.
+template <int NC>
+struct XRowsW {
+    static constexpr int XV = (128 * NC + 255) / 256;
+    bf16x8 x[XV];
+    __device__ __forceinline__ void load(const bf16_t* q_h, const bf16_t* k_h, int p0, int N, int dr, int ts) {
+#pragma unroll
+        for (int e = 0; e < XV; ++e) {
+            const int t = (ts + 256 * e) % (128 * NC);
+            const int side = t / (64 * NC), rem = t % (64 * NC), c = rem / 64, lane = rem % 64;
+            const int pos = min(p0 + (lane & 31), N - 1), d0 = 16 * c + 8 * (lane >> 5);
+            const bool in = d0 < dr;
+            const bf16_t* src = (side == 0 ? q_h : k_h) + (size_t)pos * dr + (in ? d0 : 0);
+            const bf16x8 val = *reinterpret_cast<const bf16x8*>(src);
+            const bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+            x[e] = in ? val : z;
+        }
+    }
+    __device__ __forceinline__ void store(unsigned char* xs, unsigned char* dummy, int ts) const {
+#pragma unroll
+        for (int e = 0; e < XV; ++e) {
+            const int tt = ts + 256 * e;
+            const int t = tt % (128 * NC);
+            const int side = t / (64 * NC), rem = t % (64 * NC), c = rem / 64, lane = rem % 64;
+            XFrag f;
+            f.x1 = x[e];
+            split_square(f);
+            const bool real = tt < 128 * NC;
+            unsigned char* dst = real ? xs + ((size_t)(side * NC + c) * 3) * 1024 + 16 * lane : dummy;
+            const int step = real ? 1024 : 0;
+            *reinterpret_cast<bf16x8*>(dst) = f.x1;
+            *reinterpret_cast<bf16x8*>(dst + step) = f.x2h;
+            *reinterpret_cast<bf16x8*>(dst + 2 * step) = f.x2l;
+        }
+    }
+};
+
+template <int NTS>
+struct VRowsW {
+    static constexpr int Dvs = 32 * NTS;
+    bf16x8 v;
+    __device__ __forceinline__ void load(const bf16_t* v_h, int p0, int N, int dv, int ts) {
+        const int t = ts % (4 * Dvs);
+        const int pos = min(p0 + t / (Dvs / 8), N - 1), d0 = 8 * (t % (Dvs / 8));
+        const bool in = d0 < dv;
+        const bf16x8 val = *reinterpret_cast<const bf16x8*>(v_h + (size_t)pos * dv + (in ? d0 : 0));
+        const bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+        v = in ? val : z;
+    }
+    __device__ __forceinline__ void store(unsigned char* sV, unsigned char* dummy, int ts) const {
+        constexpr int VSt = 2 * Dvs + 32;
+        unsigned char* dst = ts < 4 * Dvs ? sV + (size_t)(ts / (Dvs / 8)) * VSt + 16 * (ts % (Dvs / 8)) : dummy;
         *reinterpret_cast<bf16x8*>(dst) = v;
     }
 };
@@ -327,14 +388,29 @@ __global__ void __launch_bounds__(kFThreads, 2)
     const int ngroups = n_end > n_begin ? (n_end - n_begin + kGrp - 1) / kGrp : 0;
     XRows<NC> xr;
     VRows<NTS> vr;
-    // group 0's rows staged, group 1's in flight
+    XRowsW<NC> xw;
+    VRowsW<NTS> vw;
+    const bool stager = w >= kFWaves / 2;
+    const int ts = (int)threadIdx.x - kFThreads / 2;
+    // group 0's rows staged, group 1's in flight (scan: by the waves 4..7)
     if (ngroups > 0) {
-        xr.load(q_h, k_h, n_begin, N, dr, !kScan);
-        vr.load(v_h, n_begin, N, dv);
-        xr.store(smem + L::xs0, smem + L::dummy);
-        vr.store(smem + L::v0, smem + L::dummy);
-        xr.load(q_h, k_h, n_begin + kGrp, N, dr, !kScan);
-        vr.load(v_h, n_begin + kGrp, N, dv);
+        if constexpr (kScan) {
+            if (stager) {
+                xw.load(q_h, k_h, n_begin, N, dr, ts);
+                vw.load(v_h, n_begin, N, dv, ts);
+                xw.store(smem + L::xs0, smem + L::dummy, ts);
+                vw.store(smem + L::v0, smem + L::dummy, ts);
+                xw.load(q_h, k_h, n_begin + kGrp, N, dr, ts);
+                vw.load(v_h, n_begin + kGrp, N, dv, ts);
+            }
+        } else {
+            xr.load(q_h, k_h, n_begin, N, dr, !kScan);
+            vr.load(v_h, n_begin, N, dv);
+            xr.store(smem + L::xs0, smem + L::dummy);
+            vr.store(smem + L::v0, smem + L::dummy);
+            xr.load(q_h, k_h, n_begin + kGrp, N, dr, !kScan);
+            vr.load(v_h, n_begin + kGrp, N, dv);
+        }
     }
     __syncthreads();
     bf16x8 den_ones;  // normaliser tile of the intra term: ones in rows 0..7 (the z hi rows)
@@ -357,10 +433,12 @@ __global__ void __launch_bounds__(kFThreads, 2)
         // that loaded
 #pragma unroll
         for (int side = S0; side < 2; ++side) assemble(lg[side], side, side == 0 || p0 + col < n_end);
-        xr.store(smem + ((g & 1) ? L::xs0 : L::xs1), smem + L::dummy);
-        vr.store(smem + ((g & 1) ? L::v0 : L::v1), smem + L::dummy);
-        xr.load(q_h, k_h, p0 + 2 * kGrp, N, dr, !kScan);
-        vr.load(v_h, p0 + 2 * kGrp, N, dv);
+        if constexpr (!kScan) {
+            xr.store(smem + ((g & 1) ? L::xs0 : L::xs1), smem + L::dummy);
+            vr.store(smem + ((g & 1) ? L::v0 : L::v1), smem + L::dummy);
+            xr.load(q_h, k_h, p0 + 2 * kGrp, N, dr, !kScan);
+            vr.load(v_h, p0 + 2 * kGrp, N, dv);
+        }
         lds_barrier();  // ---- 2: responsibilities of the group in LDS
         const unsigned char* gq = sG;
         const unsigned char* gk = sG + (size_t)kGrp * L::GS;
@@ -410,6 +488,13 @@ __global__ void __launch_bounds__(kFThreads, 2)
         if (!kScan) {
             lds_barrier();  // ---- everyone done with this group's responsibilities
             continue;
+        }
+        if (stager) {
+            // the next group's rows (into the buffers group g - 1 used), the one after loaded
+            xw.store(smem + ((g & 1) ? L::xs0 : L::xs1), smem + L::dummy, ts);
+            vw.store(smem + ((g & 1) ? L::v0 : L::v1), smem + L::dummy, ts);
+            xw.load(q_h, k_h, p0 + 2 * kGrp, N, dr, ts);
+            vw.load(v_h, p0 + 2 * kGrp, N, dv, ts);
         }
         lds_barrier();  // ---- 3: affinity in LDS; the old shadow is no longer read
         if (w <= NTS) {
