@@ -43,8 +43,11 @@
 //                  total as fp32 matrix-core products over 32-row tiles
 //   bwd_bidir_rows   bidirectional otherwise: the same per-row arithmetic, each wave of a
 //                  workgroup walking its own rows
-//   bwd_x_mfma     bf16 inputs: dqr, dkr = Q - x P with P = dl lam, Q = dl (mu lam) as fp32
-//                  matrix-core products over 32-row tiles
+//   bwd_x_bf16     bf16 inputs, d_r <= 64: dqr, dkr = Q - x P with P = dl lam, Q = dl (mu lam)
+//                  on bf16 matrix cores, every fp32 operand split exactly into a bf16 pair
+//                  (hi.hi + lo.hi + hi.lo); the lam / mu lam pieces prepared by bwd_x_pieces
+//   bwd_x_mfma     bf16 inputs otherwise: the same as fp32 matrix-core products over 32-row
+//                  tiles
 //   bwd_x          otherwise: the same with LDS-tiled contractions over the components (in A)
 //   bwd_param_part per chunk of rows (both sides, all b), LDS-tiled sums S0 = sum dl,
 //                  S1 = sum dl x, S2 = sum dl x^2 per (h, k, d) (in A), stored in double;
@@ -1541,6 +1544,196 @@ hipError_t launch_x_mfma_t(const Args& a, const BwdArgs& g, const double* lam, c
     return hipGetLastError();
 }
 
+// dx on the bf16 matrix cores (bf16 inputs, d_r <= 64): the same P^T = lam^T dl^T and
+// Q^T = (mu lam)^T dl^T per 32-row tile, with every fp32 operand split exactly into a bf16
+// pair (hi = bf16(v), lo = bf16(v - hi)) and each product formed as hi.hi + lo.hi + hi.lo on
+// v_mfma_f32_32x32x16_bf16 (the dropped lo.lo is below 2^-16 of the product).  The A operand
+// (lam and mu lam, as four bf16 pieces [lam hi, lam lo, (mu lam) hi, (mu lam) lo], each
+// [32 NTD dims][KS components] per head) is prepared once per call by bwd_x_pieces and copied
+// to LDS by each workgroup; the B operand is the lane's own dl row: 8 consecutive components
+// per lane half and contraction step, split in registers.
+__host__ __device__ constexpr int x_pieces_stride(int K) { return ((K + 15) & ~15) + 8; }
+constexpr int kXSC = 4;  // contraction steps of 16 components per dl chunk
+
+template <int NTD>
+__global__ void __launch_bounds__(256)
+    bwd_x_pieces(const float* __restrict__ mu, const double* __restrict__ lam, bf16_t* __restrict__ xp, int K, int dr) {
+    const int h = blockIdx.y, KS = x_pieces_stride(K);
+    const int e = blockIdx.x * 256 + threadIdx.x;  // (dim, component) of the head's pieces
+    if (e >= 32 * NTD * KS) return;
+    const int d = e / KS, k = e % KS;
+    float lv = 0.0f, mv = 0.0f;
+    if (k < K && d < dr) {
+        const double lm = lam[((size_t)h * K + k) * dr + d];
+        lv = (float)lm;
+        mv = (float)((double)mu[((size_t)h * K + k) * dr + d] * lm);
+    }
+    const bf16_t lh = f32_to_bf16(lv), mh = f32_to_bf16(mv);
+    const size_t piece = (size_t)32 * NTD * KS;
+    bf16_t* dst = xp + (size_t)h * 4 * piece + e;
+    dst[0] = lh;
+    dst[piece] = f32_to_bf16(lv - bf16_to_f32(lh));
+    dst[2 * piece] = mh;
+    dst[3 * piece] = f32_to_bf16(mv - bf16_to_f32(mh));
+}
+
+template <typename T, int NTD, bool FAST>
+__global__ void __launch_bounds__(kMfRowThreads)
+    bwd_x_bf16(const T* __restrict__ qr, const T* __restrict__ kr, const bf16_t* __restrict__ xp,
+               const float* __restrict__ dl, T* __restrict__ dqr, T* __restrict__ dkr, int BH, int H, int N, int K,
+               int dr) {
+    extern __shared__ double smem_d[];
+    bf16_t* sP = reinterpret_cast<bf16_t*>(smem_d);  // [4][32 NTD][KS]
+    const int KS = x_pieces_stride(K), K16 = (K + 15) & ~15;
+    const size_t piece = (size_t)32 * NTD * KS;
+    const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
+    const int sb = blockIdx.y, side = sb / BH, bh = sb % BH, h = bh % H;
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(xp + (size_t)h * 4 * piece);
+        uint4* dst = reinterpret_cast<uint4*>(sP);
+        const int nvec = (int)(4 * piece / 8);
+        for (int i = t; i < nvec; i += kMfRowThreads) dst[i] = src[i];
+    }
+    __syncthreads();
+    const bool vec_k = (K & 3) == 0;
+    for (int rt = 0; rt < kXTiles; ++rt) {
+        const int row = blockIdx.x * (128 * kXTiles) + 128 * rt + 32 * wv + col;
+        const bool ok = row < N;
+        const size_t rr = (size_t)(ok ? row : N - 1);
+        const float* dl_r = dl + (((size_t)side * BH + bh) * N + rr) * K;
+        f32x16 P[NTD], Q[NTD];
+#pragma unroll
+        for (int n = 0; n < NTD; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) P[n][i] = Q[n][i] = 0.0f;
+        // the row's dl in chunks of kXSC contraction steps, the next chunk's loads in flight
+        // during this chunk's MFMAs (two register buffers, chunks taken in pairs)
+        auto load_chunk = [&](int kb0, float (&gb)[kXSC][8]) {
+#pragma unroll
+            for (int sc = 0; sc < kXSC; ++sc)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int kq = kb0 + 16 * sc + 8 * half + 4 * q;
+                    if (FAST || (vec_k && kq < K)) {
+                        const float4 x = *reinterpret_cast<const float4*>(dl_r + kq);
+                        gb[sc][4 * q] = x.x;
+                        gb[sc][4 * q + 1] = x.y;
+                        gb[sc][4 * q + 2] = x.z;
+                        gb[sc][4 * q + 3] = x.w;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) gb[sc][4 * q + j] = kq + j < K ? dl_r[kq + j] : 0.0f;
+                    }
+                }
+        };
+        auto run_chunk = [&](int kb0, const float (&gb)[kXSC][8]) {
+#pragma unroll
+            for (int sc = 0; sc < kXSC; ++sc) {
+                const int kb = kb0 + 16 * sc;
+                if (kb >= K16) break;
+                const int k0 = kb + 8 * half;
+                mf::u32x4 gh, gl;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    gh[j] = mf::pack_bf16(gb[sc][2 * j], gb[sc][2 * j + 1]);
+                    gl[j] = mf::pack_bf16(gb[sc][2 * j] - mf::bf16lo_to_f32(gh[j]),
+                                          gb[sc][2 * j + 1] - mf::bf16hi_to_f32(gh[j]));
+                }
+                const mf::bf16x8 bh8 = __builtin_bit_cast(mf::bf16x8, gh), bl8 = __builtin_bit_cast(mf::bf16x8, gl);
+#pragma unroll
+                for (int n = 0; n < NTD; ++n) {
+                    const bf16_t* arow = sP + (size_t)(32 * n + col) * KS + k0;
+                    const mf::bf16x8 lh = *reinterpret_cast<const mf::bf16x8*>(arow);
+                    const mf::bf16x8 ll = *reinterpret_cast<const mf::bf16x8*>(arow + piece);
+                    const mf::bf16x8 mh = *reinterpret_cast<const mf::bf16x8*>(arow + 2 * piece);
+                    const mf::bf16x8 ml = *reinterpret_cast<const mf::bf16x8*>(arow + 3 * piece);
+                    P[n] = mf::mfma(lh, bh8, P[n]);
+                    Q[n] = mf::mfma(mh, bh8, Q[n]);
+                    P[n] = mf::mfma(ll, bh8, P[n]);
+                    Q[n] = mf::mfma(ml, bh8, Q[n]);
+                    P[n] = mf::mfma(lh, bl8, P[n]);
+                    Q[n] = mf::mfma(mh, bl8, Q[n]);
+                }
+            }
+        };
+        float ga[kXSC][8], gb[kXSC][8];
+        load_chunk(0, ga);
+        for (int kb0 = 0; kb0 < K16; kb0 += 32 * kXSC) {
+            if (kb0 + 16 * kXSC < K16) load_chunk(kb0 + 16 * kXSC, gb);
+            run_chunk(kb0, ga);
+            if (kb0 + 16 * kXSC >= K16) break;
+            if (kb0 + 32 * kXSC < K16) load_chunk(kb0 + 32 * kXSC, ga);
+            run_chunk(kb0 + 16 * kXSC, gb);
+        }
+        if (!ok) continue;
+        const T* x = (side == 0 ? qr : kr) + ((size_t)bh * N + rr) * dr;
+        T* dx = (side == 0 ? dqr : dkr) + ((size_t)bh * N + rr) * dr;
+        if constexpr (FAST) {
+            // d_r = 32 NTD: every group of 4 dims is whole, 8-byte loads and stores
+            uint2 xv[NTD][4];
+#pragma unroll
+            for (int n = 0; n < NTD; ++n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xv[n][q] = *reinterpret_cast<const uint2*>(x + 32 * n + 8 * q + 4 * half);
+#pragma unroll
+            for (int n = 0; n < NTD; ++n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint2 u = xv[n][q];
+                    const float x0 = mf::bf16lo_to_f32(u.x), x1 = mf::bf16hi_to_f32(u.x);
+                    const float x2 = mf::bf16lo_to_f32(u.y), x3 = mf::bf16hi_to_f32(u.y);
+                    uint2 o;
+                    o.x = mf::pack_bf16(Q[n][4 * q] - x0 * P[n][4 * q], Q[n][4 * q + 1] - x1 * P[n][4 * q + 1]);
+                    o.y = mf::pack_bf16(Q[n][4 * q + 2] - x2 * P[n][4 * q + 2], Q[n][4 * q + 3] - x3 * P[n][4 * q + 3]);
+                    *reinterpret_cast<uint2*>(dx + 32 * n + 8 * q + 4 * half) = o;
+                }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NTD; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int d = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
+                    if (d < dr) Elem<T>::store(dx, d, Q[n][i] - Elem<T>::load(x, d) * P[n][i]);
+                }
+        }
+    }
+}
+
+// LDS bytes of bwd_x_bf16 (0: the shape is not taken: d_r > 64).
+size_t x_bf16_lds(const gma_desc& d) {
+    const int ntd = (d.d_r + 31) / 32;
+    if (ntd > 2) return 0;
+    const size_t lds = 4 * (size_t)(32 * ntd) * x_pieces_stride(d.K) * sizeof(bf16_t);
+    return lds <= kScanLdsMax ? lds : 0;
+}
+size_t x_bf16_pieces_bytes(const gma_desc& d) {
+    const int ntd = (d.d_r + 31) / 32;
+    return (size_t)d.H * 4 * (32 * ntd) * x_pieces_stride(d.K) * sizeof(bf16_t);
+}
+
+template <typename T, int NTD>
+hipError_t launch_x_bf16_t(const Args& a, const BwdArgs& g, const double* lam, const float* dl, bf16_t* xp) {
+    const gma_desc& d = a.d;
+    const int BH = d.B * d.H;
+    const int KS = x_pieces_stride(d.K);
+    bwd_x_pieces<NTD><<<dim3((unsigned)((32 * NTD * KS + 255) / 256), (unsigned)d.H), dim3(256), 0, a.stream>>>(
+        a.mu, lam, xp, d.K, d.d_r);
+    hipError_t e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t lds = 4 * (size_t)(32 * NTD) * KS * sizeof(bf16_t);
+    // whole 16-component steps and whole 4-dim groups: unconditional loads and stores
+    const bool fast = d.K % 16 == 0 && d.d_r == 32 * NTD;
+    auto kern = fast ? &bwd_x_bf16<T, NTD, true> : &bwd_x_bf16<T, NTD, false>;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)lds)) != hipSuccess)
+        return e;
+    const unsigned gx = (unsigned)((d.N + 128 * kXTiles - 1) / (128 * kXTiles));
+    kern<<<dim3(gx, (unsigned)(2 * BH)), dim3(kMfRowThreads), lds, a.stream>>>(
+        static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), xp, dl, static_cast<T*>(g.dqr),
+        static_cast<T*>(g.dkr), BH, d.H, d.N, d.K, d.d_r);
+    return hipGetLastError();
+}
+
 // LDS bytes of bwd_x_mfma (0: the shape is not taken).
 size_t x_mfma_lds(const gma_desc& d) {
     const int ntd = (d.d_r + 31) / 32;
@@ -1718,7 +1911,7 @@ bool resp_on_mfma(const gma_desc& d) {
 }
 
 struct BwdLayout {
-    size_t lam, W, C, gamma, dl, gnum, gden, part, start, state, pmu, pvar, ppi, total;
+    size_t lam, W, C, gamma, dl, gnum, gden, part, start, state, pmu, pvar, ppi, xp, total;
     int chunks, per_chunk, seg, seg_len;
 };
 
@@ -1762,6 +1955,8 @@ BwdLayout bwd_layout(const gma_desc& d) {
     off += align_up(nc * d.H * d.K * d.d_r * sizeof(double));
     L.ppi = off;
     off += align_up(nc * d.H * d.K * sizeof(double));
+    L.xp = off;
+    if (d.dtype == GMA_BF16 && x_bf16_lds(d) > 0) off += align_up(x_bf16_pieces_bytes(d));
     L.total = off;
     return L;
 }
@@ -2194,7 +2389,12 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
         rec_begin(a, "bwd_x");
         bool x_done = false;
         if constexpr (sizeof(A) == sizeof(float)) {
-            if (x_mfma_lds(d) > 0) {
+            if (x_bf16_lds(d) > 0) {
+                bf16_t* xp = reinterpret_cast<bf16_t*>(a.ws + L.xp);
+                e = (d.d_r + 31) / 32 == 1 ? launch_x_bf16_t<T, 1>(a, g, lam, dl, xp)
+                                           : launch_x_bf16_t<T, 2>(a, g, lam, dl, xp);
+                x_done = true;
+            } else if (x_mfma_lds(d) > 0) {
                 const int ntd = (d.d_r + 31) / 32;
                 e = ntd == 1   ? launch_x_mfma_t<T, 1>(a, g, lam, dl)
                     : ntd == 2 ? launch_x_mfma_t<T, 2>(a, g, lam, dl)
