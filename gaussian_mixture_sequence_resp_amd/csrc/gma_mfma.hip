@@ -9,9 +9,14 @@
 //   gma_prep          coefficients [ah|al|bh|bl] (bf16) and c_k of every head.
 //   gma_bidir_write   Gamma_K tile by tile (logit MFMAs + in-lane softmax), staged in LDS,
 //                     then Gamma_K^T [V | 1] on MFMAs; each workgroup owns one contiguous
-//                     split of the sequence and writes a fp32 partial of [Vt | Z].
-//   gma_bidir_read    adds the split partials of its head in split order (deterministic; no
-//                     cross-workgroup synchronisation), stages Vt^T and Z in LDS, then
+//                     split of the sequence and writes a fp32 partial of [Vt | Z].  Small
+//                     tiles (K <= 64, d_r, d_v <= 64) run two workgroups per CU over twice the
+//                     splits.
+//   gma_split_reduce  (after the two-per-CU write) the split partials of each head added in
+//                     split order into the first split's slot, once, instead of by every
+//                     read workgroup of the head.
+//   gma_bidir_read    adds the split partials of its head in split order (deterministic), or
+//                     takes the reduced one, stages Vt^T and Z in LDS, then
 //                     Gamma_Q tile by tile, unnormalised (2^(l - max)); one MFMA chain gives
 //                     Gamma_Q Vt, Gamma_Q Z and the row sum s together; O = num / (den + eps s).
 // Gamma never leaves the chip in these kernels.
@@ -35,9 +40,15 @@ inline int gstride(const Geo& g) { return 2 * g.Kp + 32; }
 inline int vstride(const Geo& g) { return 2 * g.Dvp + 32; }
 inline int vtstride(const Geo& g) { return 2 * g.Kp + 16; }
 
+// + one 64-byte row of bf16 ones (the ones operand of the update MFMAs)
 size_t write_lds_bytes(const Geo& g) {
-    return (size_t)g.Kp * g.wstride + (size_t)g.Kp * 4 + (size_t)kIterT * gstride(g) + (size_t)kIterT * vstride(g);
+    return (size_t)g.Kp * g.wstride + (size_t)g.Kp * 4 + (size_t)kIterT * gstride(g) + (size_t)kIterT * vstride(g) + 64;
 }
+
+// Write instances that run two workgroups per CU (at most 256 registers, LDS for two): small
+// component and dim tiles.  Their launches use twice the splits, combined in pairs.
+__host__ __device__ constexpr bool write_dual(int MT, int NT, int NC) { return MT <= 2 && NT <= 2 && NC <= 4; }
+inline bool write_dual(const Geo& g) { return write_dual(g.MT, g.NT, g.NC) && 2 * write_lds_bytes(g) <= kLdsMax; }
 // The read kernel keeps the memory operand of its output MFMAs (MT * 2 * (NT + 1) fragments of
 // 4 registers) in registers when that leaves it within 256 registers (no spills).
 __host__ __device__ constexpr bool read_regmem(int MT, int NT) { return MT * (NT + 1) <= 12; }
@@ -46,11 +57,13 @@ size_t read_lds_bytes(const Geo& g) {
     return (size_t)g.Kp * g.wstride + (size_t)g.Kp * 4 + (size_t)(g.Dvp + 32) * vtstride(g);
 }
 
-// Splits of the key sequence (length Nk) for the write kernel.
+// Splits of the key sequence (length Nk) for the write kernel: about one workgroup per CU,
+// two for the dual-occupancy instances.
 int num_splits(const gma_desc& d, int Nk) {
     const int bh = d.B * d.H;
     const int iters = (Nk + kIterT - 1) / kIterT;
-    int s = (256 + bh - 1) / bh;
+    const int target = write_dual(geometry(d)) ? 512 : 256;
+    int s = (target + bh - 1) / bh;
     if (s > iters) s = iters;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 1 ? 1 : s;
@@ -159,8 +172,44 @@ __device__ __forceinline__ void load_krow(bf16x8 (&xr)[NC], const bf16_t* row, i
 // Stage assignment of the four softmax stages over the U units of a pipelined logits tile.
 __host__ __device__ constexpr int stage_unit(int st, int U) { return (st * U) / 4; }
 
+// The update of the write kernel: wave-uniform tile indices, the ones operand read from a
+// 64-byte LDS row of ones with a zero row stride (so value and ones tiles take the same code,
+// no per-register select); a wave whose last tile index lies past the ones tile (component
+// tiles shared by several waves) skips that tile.
+template <int MT, int NT, int MW, int NW, int NJ>
+__device__ __forceinline__ void write_update_n(f32x16 (&acc)[MW][NW], const unsigned char* sG, int gs,
+                                               const unsigned char* sV, int vs, const unsigned char* sOnes, int w) {
+    using UT = UpdateTiles<MT, NT>;
+#pragma unroll
+    for (int ks = 0; ks < kIterT / 16; ++ks) {
+        bf16x8 a[MW], b[NJ];
+#pragma unroll
+        for (int j = 0; j < MW; ++j) a[j] = lds_frag_tr(sG, gs, 16 * ks, 32 * UT::m_of(w, j));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int n = UT::n_of(w, j);
+            const bool isv = n < NT;
+            b[j] = lds_frag_tr(isv ? sV : sOnes, isv ? vs : 0, isv ? 16 * ks : 0, isv ? 32 * n : 0);
+        }
+#pragma unroll
+        for (int i = 0; i < MW; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]);
+    }
+}
+template <int MT, int NT, int MW, int NW>
+__device__ __forceinline__ void write_update(f32x16 (&acc)[MW][NW], const unsigned char* sG, int gs,
+                                             const unsigned char* sV, int vs, const unsigned char* sOnes) {
+    using UT = UpdateTiles<MT, NT>;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (MT < 4 && NW > 1 && UT::n_of(w, NW - 1) > NT)
+        write_update_n<MT, NT, MW, NW, (NW > 1 ? NW - 1 : NW)>(acc, sG, gs, sV, vs, sOnes, w);
+    else
+        write_update_n<MT, NT, MW, NW, NW>(acc, sG, gs, sV, vs, sOnes, w);
+}
+
 template <int MT, int NT, int NC, bool FULL>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, write_dual(MT, NT, NC) ? 2 : 1)
     gma_bidir_write(const bf16_t* __restrict__ kr, const bf16_t* __restrict__ v, const bf16_t* __restrict__ W,
                     const float* __restrict__ cvec, float* __restrict__ part_v, float* __restrict__ part_z, int BH,
                     int H, int N, int dr, int dv, int S, int split_len) {
@@ -173,6 +222,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     float* sC = reinterpret_cast<float*>(sW + (size_t)Kp * wstride);
     unsigned char* sG = reinterpret_cast<unsigned char*>(sC + Kp);
     unsigned char* sV = sG + (size_t)kIterT * gs;
+    unsigned char* sOnes = sV + (size_t)kIterT * vs;
 
     int bh, split;
     head_part(blockIdx.x, BH, S, bh, split);
@@ -207,10 +257,6 @@ __global__ void __launch_bounds__(kThreads, 1)
         for (int j = 0; j < UT::NW; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) wacc[i][j][e] = 0.0f;
-    bf16x8 ones;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ones[j] = (short)0x3f80;
-
     // coefficients, k rows for steps 0 and 1 and v rows for step 0: all loads in flight together
     bf16x8 xa[NC], xb[NC], vcur[2 * NT];
     {
@@ -220,6 +266,7 @@ __global__ void __launch_bounds__(kThreads, 1)
         load_krow<NC, FULL>(xb, krow(1), dr);
         load_vrow<NT, FULL>(vcur, vrow(0), dv);
         cr.store(sW, sC, wstride);
+        if (threadIdx.x < 16) reinterpret_cast<uint32_t*>(sOnes)[threadIdx.x] = 0x3f803f80u;  // bf16 1.0
     }
     __syncthreads();
 
@@ -248,7 +295,7 @@ __global__ void __launch_bounds__(kThreads, 1)
         });
         load_krow<NC, FULL>(xfar, krow(it + 3), dr);
         lds_barrier();
-        update_from_lds<MT, NT, UT::MW, UT::NW>(wacc, sG, gs, sV, vs, ones);
+        write_update<MT, NT, UT::MW, UT::NW>(wacc, sG, gs, sV, vs, sOnes);
         lds_barrier();
 #pragma unroll
         for (int j = 0; j < 2 * NT; ++j) vcur[j] = vnext[j];
@@ -265,7 +312,7 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
         for (int j = 0; j < 2 * NT; ++j) *reinterpret_cast<bf16x8*>(vdst + 2 * (16 * j + 8 * half)) = vcur[j];
         lds_barrier();
-        update_from_lds<MT, NT, UT::MW, UT::NW>(wacc, sG, gs, sV, vs, ones);
+        write_update<MT, NT, UT::MW, UT::NW>(wacc, sG, gs, sV, vs, sOnes);
     };
     // Steps run in pairs (an odd count gets one step past the split, all of whose rows are
     // zeroed), so the loop body has no branch: xa holds step it+2's rows when step `it` starts
@@ -296,6 +343,7 @@ __global__ void __launch_bounds__(kThreads, 1)
                     pz[k] = wacc[i][j][e];
             }
         }
+
 }
 
 // ---------------------------------------------------------------------------------- read
@@ -306,7 +354,7 @@ template <int MT, int NT, int NC>
 __global__ void __launch_bounds__(64 * kReadWaves, 2)
     gma_bidir_read(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ W, const float* __restrict__ cvec,
                    const float* __restrict__ part_v, const float* __restrict__ part_z, bf16_t* __restrict__ out,
-                   float eps, int BH, int H, int N, int dr, int dv, int S, int parts, int part_len) {
+                   float eps, int BH, int H, int N, int dr, int dv, int S, int sstep, int parts, int part_len) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int Kp = 32 * MT, Dvp = 32 * NT, Dp = 16 * NC;
     constexpr int wstride = 8 * Dp + 16;
@@ -331,8 +379,9 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
         load_xrow<NC>(xr, q_h + (size_t)min(t, N - 1) * dr, dr);
     }
 
-    // the head's memory [Vt | Z] = sum of the S split partials of the write kernel, added in
-    // split order (every workgroup of the head forms the identical sum).  The coefficient
+    // the head's memory [Vt | Z] = sum of the split partials of the write kernel (slots
+    // 0, sstep, 2 sstep, ... of the S: sstep = S where gma_split_reduce has already added
+    // them into slot 0), in split order (every workgroup of the head forms the identical sum).  The coefficient
     // loads and the partial loads of up to SB splits are in flight together.  Vt^T goes to
     // LDS rows 0..Dvp-1 in the permuted component order of the logits tiles, then Z hi
     // (8 rows), Z lo (8 rows) and ones (16 rows).
@@ -349,19 +398,21 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
         float zsum = 0.0f;
         CoefRegs<MT, NC, kThr> cr;
         cr.load(W, cvec, h);
-        for (int s0 = 0; s0 < S; s0 += SB) {
+        const int nslot = (S + sstep - 1) / sstep;
+        for (int s0 = 0; s0 < nslot; s0 += SB) {
             float4 x[SB][P];
             float zx[SB];
 #pragma unroll
             for (int u = 0; u < SB; ++u) {
-                const bool ok = s0 + u < S;
-                const float4* src = reinterpret_cast<const float4*>(pv0 + (size_t)(ok ? s0 + u : 0) * Kp * Dvp);
+                const bool ok = s0 + u < nslot;
+                const int sp = ok ? (s0 + u) * sstep : 0;
+                const float4* src = reinterpret_cast<const float4*>(pv0 + (size_t)sp * Kp * Dvp);
 #pragma unroll
                 for (int p = 0; p < P; ++p) {
                     const int i = threadIdx.x + p * kThr;
                     x[u][p] = (ok && i < kVec) ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
-                zx[u] = (ok && (int)threadIdx.x < Kp) ? pz0[(size_t)(s0 + u) * Kp + threadIdx.x] : 0.0f;
+                zx[u] = (ok && (int)threadIdx.x < Kp) ? pz0[(size_t)sp * Kp + threadIdx.x] : 0.0f;
             }
             if (s0 == 0) cr.store(sW, sC, wstride);
 #pragma unroll
@@ -476,6 +527,32 @@ __global__ void __launch_bounds__(64 * kReadWaves, 2)
     }
 }
 
+// ---------------------------------------------------------------------------------- split reduce
+// The S split partials of every head added in split order into split 0's slot (in place:
+// each element is read and written by one thread; the loads of 8 splits are issued together,
+// then added in order).  Grid (ceil(Kp (Dvp + 1) / 256), min(B H, 65535)), heads strided by
+// gridDim.y.
+__global__ void __launch_bounds__(256)
+    gma_split_reduce(float* __restrict__ part_v, float* __restrict__ part_z, int BH, int S, int Kp, int Dvp) {
+    const int nv = Kp * Dvp;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nv + Kp) return;
+    for (size_t bh = blockIdx.y; bh < (size_t)BH; bh += gridDim.y) {
+        float* p = i < nv ? part_v + bh * S * nv + i : part_z + bh * S * Kp + (i - nv);
+        const size_t stride = i < nv ? (size_t)nv : (size_t)Kp;
+        float acc = p[0];
+        for (int s0 = 1; s0 < S; s0 += 8) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = s0 + u < S ? p[(size_t)(s0 + u) * stride] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < S) acc += x[u];
+        }
+        p[0] = acc;
+    }
+}
+
 // ---------------------------------------------------------------------------------- memory
 // Causal memory from the split partials of the write kernel: for component k < K,
 // state[bh][k][c] = sum_s part_v[bh][s][k][c] (c < d_v), state[bh][k][d_v] = sum_s part_z[bh][s][k],
@@ -499,11 +576,11 @@ __global__ void __launch_bounds__(256)
 typedef void (*WriteFn)(const bf16_t*, const bf16_t*, const bf16_t*, const float*, float*, float*, int, int, int,
                         int, int, int, int);
 typedef void (*ReadFn)(const bf16_t*, const bf16_t*, const float*, const float*, const float*, bf16_t*, float, int,
-                       int, int, int, int, int, int, int);
+                       int, int, int, int, int, int, int, int);
 
 // The exact-fit write kernel is built where it does not spill registers (the largest tiles
 // keep the general form).
-constexpr bool write_full_ok(int MT, int NT, int NC) { return MT <= 4 && MT * NT * NC < 128; }
+constexpr bool write_full_ok(int MT, int NT, int NC) { return MT <= 4 && MT * NT * NC < 128 && !(MT == 4 && NC == 8); }
 
 template <int MT, int NT, int NC>
 bool pick(bool full, WriteFn& wf, ReadFn& rf) {
@@ -595,6 +672,7 @@ static hipError_t bidir_forward(const Args& a) {
     if ((e = launch_prep(a, g, W, cvec)) != hipSuccess) return e;
 
     const int S = num_splits(d, Nk);
+
     const int split_len = ((Nk + S - 1) / S + kIterT - 1) / kIterT * kIterT;
     const size_t wl = write_lds_bytes(g);
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(wf), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -606,6 +684,17 @@ static hipError_t bidir_forward(const Args& a) {
                        split_len);
     rec_end(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the two-per-CU write runs twice the splits: add them once here rather than in every
+    // read workgroup's prologue
+    const bool reduced = write_dual(g) && S > 1;
+    if (reduced) {
+        const int nv = g.Kp * (g.Dvp + 1);
+        rec_begin(a, "gma_split_reduce");
+        gma_split_reduce<<<dim3((unsigned)((nv + 255) / 256), (unsigned)(BH < 65535 ? BH : 65535)), dim3(256), 0,
+                           a.stream>>>(part_v, part_z, BH, S, g.Kp, g.Dvp);
+        rec_end(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
 
     // read: about one workgroup per CU, each a contiguous run of the sequence of one head
     const int step = kTileT * kReadWaves;
@@ -622,7 +711,7 @@ static hipError_t bidir_forward(const Args& a) {
     rec_begin(a, "gma_bidir_read");
     hipLaunchKernelGGL(rf, dim3(BH * parts), dim3(64 * kReadWaves), rl, a.stream, static_cast<const bf16_t*>(a.qr),
                        W, cvec, part_v, part_z, static_cast<bf16_t*>(a.out), a.eps, BH, d.H, d.N, d.d_r, d.d_v, S,
-                       parts, part_len);
+                       reduced ? S : 1, parts, part_len);
     rec_end(a);
     return hipGetLastError();
 }

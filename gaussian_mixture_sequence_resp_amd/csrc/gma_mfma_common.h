@@ -290,7 +290,12 @@ struct SoftmaxStages {
                     s += e;
                 }
             }
-            if (st == 2) inv = valid ? 1.0f / sum_halves(s) : 0.0f;
+            if (st == 2) {
+                // s >= 1 (the maximum contributes 2^0): the hardware reciprocal (~1 ulp) is
+                // far below the bf16 rounding of the responsibilities it scales
+                const float r = __builtin_amdgcn_rcpf(sum_halves(s));
+                inv = valid ? r : 0.0f;
+            }
         } else {
             // register group q of tile m holds components 32 m + 8 q + 4 half + 0..3; one swap
             // of the upper lanes of group 2 qp with the lower lanes of group 2 qp + 1 gives each
