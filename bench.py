@@ -48,7 +48,8 @@ def metric_name() -> str:
 def algorithmic(w, kernel: str):
     """Algorithmic bytes and flops of one launch of `kernel` on workload `w`, or None for
     a kernel that carries no algorithmic share (parameter prep, the causal segment totals
-    and carries: workspace traffic and recompute, not work the method itself must do).
+    and carries, the sum of the write kernel's split partials: workspace traffic and
+    recompute, not work the method itself must do).
 
     Per token-head the whole forward must read q, k, v once and write out once:
     s*(2 d_r + 2 d_v) bytes; it must do 4K(2d_r+1) flops for the Q and K log-density
@@ -61,7 +62,7 @@ def algorithmic(w, kernel: str):
     K, dr, dv = w.K, w.d_r, w.d_v
     logits_side = 2 * K * (2 * dr + 1)   # one side's log-density contraction
     memory_side = 2 * K * (dv + 1)       # Gamma^T [V | 1] or Gamma [Vt | Z]
-    if "prep" in kernel or "totals" in kernel or "carry" in kernel:
+    if "prep" in kernel or "totals" in kernel or "carry" in kernel or "split_reduce" in kernel:
         return None
     if "causal_fused_scan" in kernel:  # the whole causal forward, responsibilities on chip
         return (th + thk) * s * (dr + dv), (th + thk) * (logits_side + memory_side)
