@@ -1,5 +1,7 @@
-// Backward of the GMA forward mixer (bidirectional and causal): SIMT kernels, with fp32
-// matrix-core forms of the row passes, dx and the parameter sums for bf16 inputs.
+// Backward of the GMA forward mixer (bidirectional and causal): SIMT kernels, with
+// matrix-core forms of the row passes, the segment partials, dx and the parameter sums for
+// bf16 inputs (fp32 matrix cores, or bf16 matrix cores on exact hi/lo splits of the fp32
+// operands).
 //
 // Method: Gaussian Mixture Attention (arXiv 2606.18283).  The mixture parameters are trained
 // end to end by backpropagation ("Core mechanism" item 3); the pages analyse the gradients'
@@ -24,7 +26,7 @@
 //   per pass (pass 1 gives g_num, g_den and dl_Q; pass 2 gives dv and dl_K), the rows of each
 //   head cut into SEG contiguous segments:
 //   bwd_seg_partial  the segment's weighted rows summed in order (K x (d_v + 1) per segment,
-//                  LDS-tiled; bwd_seg_partial_mfma for bf16 inputs: fp32 matrix-core
+//                  LDS-tiled; bwd_seg_partial_bf16 for bf16 inputs: split-bf16 matrix-core
 //                  products over 32-row blocks staged in LDS)
 //   bwd_seg_start    each segment's starting state from those partials in segment order: the
 //                  prefix before it (causal pass 1), the suffix after it (causal pass 2) or
@@ -51,7 +53,7 @@
 //   bwd_x          otherwise: the same with LDS-tiled contractions over the components (in A)
 //   bwd_param_part per chunk of rows (both sides, all b), LDS-tiled sums S0 = sum dl,
 //                  S1 = sum dl x, S2 = sum dl x^2 per (h, k, d) (in A), stored in double;
-//                  bwd_param_mfma the same for bf16 inputs as fp32 matrix-core products
+//                  bwd_param_bf16 the same for bf16 inputs as split-bf16 matrix-core products
 //   bwd_param_final, bwd_prior_final the chunk sums added in chunk order; dmu, dvar_raw;
 //                  dprior
 // Every sum has a fixed order: results are deterministic.
@@ -2043,22 +2045,43 @@ hipError_t launch_bidir_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, c
     return hipErrorInvalidValue;
 }
 
-// Segment partials on the matrix cores (bf16 inputs: float gamma and rows): part[bs] =
-// G^T U over the segment's rows (K x W), G the weighting side's gamma rows and U the pass's
-// rows, in blocks of 32 rows staged in LDS (float, row strides padded to an odd multiple of
-// 32 words so the two lane halves, which read two different rows, use disjoint banks).  The
-// MT x NTW output tiles of 32 x 32 are dealt over the 4 waves (tile w, w + 4, ...); each
-// v_mfma_f32_32x32x2_f32 step contracts two rows, one per lane half.  Grid (BH * SEG).
-template <typename T, int PASS, int MT, int NTW>
+// ---- split-bf16 row contractions (bf16 inputs).  A sum over rows of G[r][k] U[r][c] with
+// fp32 G and U runs on v_mfma_f32_32x32x16_bf16: every fp32 value is staged as the bf16 pair
+// hi = rne(v), lo = rne(v - hi) (v to ~2^-17 relative), and a product as
+// hi.hi + lo.hi + hi.lo (the dropped lo.lo is ~2^-16 of it); an operand that is bf16 already
+// (the value rows, the routing rows) has no lo part.  Blocks of 32 rows are staged in LDS
+// row-major as bf16 (row strides padded by 32 bytes) and read as MFMA fragments with the
+// transposed LDS reads; the next block's values are loaded into registers while the current
+// block's products run.
+
+// Two fp32 values as their bf16 hi and lo pairs (element 0 in the low half).
+__device__ __forceinline__ void split_pair(float v0, float v1, uint32_t& hi, uint32_t& lo) {
+    hi = mf::pack_bf16(v0, v1);
+    lo = mf::pack_bf16(v0 - mf::bf16lo_to_f32(hi), v1 - mf::bf16hi_to_f32(hi));
+}
+
+// Segment partials: part[bs] = G^T U over the segment's rows (K x W),
+// G the weighting side's gamma rows (K columns), U = [v | 1] (pass 1: bf16 values, exact) or
+// [g_num | g_den] (pass 2: fp32, split).  The MT x NTW output tiles are dealt over the 4 waves.
+// Staging in groups of 4 columns per thread; VEC (K and d_v multiples of 4): one 16-byte load
+// of gamma / g_num or one 8-byte load of v per group.  Grid (BH * SEG).
+template <typename T, int PASS, int MT, int NTW, bool VEC>
 __global__ void __launch_bounds__(kMfRowThreads)
-    bwd_seg_partial_mfma(const float* __restrict__ gamma, const T* __restrict__ v, const float* __restrict__ gnum,
+    bwd_seg_partial_bf16(const float* __restrict__ gamma, const T* __restrict__ v, const float* __restrict__ gnum,
                          const float* __restrict__ gden, float* __restrict__ part, int BH, int N, int K, int dv,
                          int SEG, int L) {
+    static_assert(sizeof(T) == 2, "bf16 values");
     extern __shared__ double smem_d[];
-    constexpr int GS = 32 * (MT + (MT % 2 == 0 ? 1 : 0)), US = 32 * (NTW + (NTW % 2 == 0 ? 1 : 0));
+    constexpr int GC = 32 * MT, UC = 32 * NTW;       // staged columns
+    constexpr int GB = 2 * GC + 32, UB = 2 * UC + 32;  // row strides, bytes
+    constexpr bool ULO = PASS == 2;                    // U needs a lo part
+    constexpr int NG = 32 * (GC / 4) / kMfRowThreads;  // column groups per thread and block
+    constexpr int NU = 32 * (UC / 4) / kMfRowThreads;
     constexpr int kTiles = MT * NTW, kWaves = kMfRowThreads / 64, TPW = (kTiles + kWaves - 1) / kWaves;
-    float* sG = reinterpret_cast<float*>(smem_d);  // [32][GS]
-    float* sU = sG + 32 * GS;                      // [32][US]
+    unsigned char* sGh = reinterpret_cast<unsigned char*>(smem_d);
+    unsigned char* sGl = sGh + 32 * GB;
+    unsigned char* sUh = sGl + 32 * GB;
+    unsigned char* sUl = sUh + 32 * UB;
     const int W = dv + 1;
     const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
     const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
@@ -2068,38 +2091,104 @@ __global__ void __launch_bounds__(kMfRowThreads)
     const float* gnum_bh = gnum + (size_t)bh * N * dv;
     const float* gden_bh = gden + (size_t)bh * N;
     const int j0 = seg * L, j1 = min(N, j0 + L);
+    float4 gv[NG];
+    float4 uf[PASS == 2 ? NU : 1];  // pass 2: fp32 values
+    uint2 ub[PASS == 1 ? NU : 1];   // pass 1: bf16 values (bits)
+    auto load_blk = [&](int jb) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int e = t + kMfRowThreads * i, r = e / (GC / 4), c = 4 * (e % (GC / 4)), j = jb + r;
+            const float* gr = g + (size_t)min(j, N - 1) * K + c;
+            const bool in = j < j1;
+            if (VEC) {
+                gv[i] = (in && c < K) ? *reinterpret_cast<const float4*>(gr) : make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+                gv[i].x = (in && c < K) ? gr[0] : 0.0f;
+                gv[i].y = (in && c + 1 < K) ? gr[1] : 0.0f;
+                gv[i].z = (in && c + 2 < K) ? gr[2] : 0.0f;
+                gv[i].w = (in && c + 3 < K) ? gr[3] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int e = t + kMfRowThreads * i, r = e / (UC / 4), c = 4 * (e % (UC / 4)), j = jb + r;
+            const size_t jj = (size_t)min(j, N - 1);
+            const bool in = j < j1;
+            if constexpr (PASS == 1) {
+                // [v | 1]: value columns c < dv, the ones column at dv
+                const T* vr = v_bh + jj * dv + c;
+                uint32_t w[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    w[q] = !in ? 0u : (c + q < dv ? (VEC ? 0u : (uint32_t)vr[q]) : (c + q == dv ? 0x3f80u : 0u));
+                if (VEC && in && c < dv) {
+                    const uint2 x = *reinterpret_cast<const uint2*>(vr);
+                    ub[i] = x;
+                } else {
+                    ub[i] = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+                }
+            } else {
+                // [g_num | g_den]
+                const float* gr = gnum_bh + jj * dv + c;
+                float x[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    x[q] = !in ? 0.0f : (c + q < dv ? (VEC ? 0.0f : gr[q]) : (c + q == dv ? gden_bh[jj] : 0.0f));
+                if (VEC && in && c < dv)
+                    uf[i] = *reinterpret_cast<const float4*>(gr);
+                else
+                    uf[i] = make_float4(x[0], x[1], x[2], x[3]);
+            }
+        }
+    };
+    auto store_blk = [&]() {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int e = t + kMfRowThreads * i, r = e / (GC / 4), c = 4 * (e % (GC / 4));
+            uint2 hi, lo;
+            split_pair(gv[i].x, gv[i].y, hi.x, lo.x);
+            split_pair(gv[i].z, gv[i].w, hi.y, lo.y);
+            *reinterpret_cast<uint2*>(sGh + r * GB + 2 * c) = hi;
+            *reinterpret_cast<uint2*>(sGl + r * GB + 2 * c) = lo;
+        }
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int e = t + kMfRowThreads * i, r = e / (UC / 4), c = 4 * (e % (UC / 4));
+            if constexpr (PASS == 1) {
+                *reinterpret_cast<uint2*>(sUh + r * UB + 2 * c) = ub[i];
+            } else {
+                uint2 hi, lo;
+                split_pair(uf[i].x, uf[i].y, hi.x, lo.x);
+                split_pair(uf[i].z, uf[i].w, hi.y, lo.y);
+                *reinterpret_cast<uint2*>(sUh + r * UB + 2 * c) = hi;
+                *reinterpret_cast<uint2*>(sUl + r * UB + 2 * c) = lo;
+            }
+        }
+    };
     f32x16 acc[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[u][e] = 0.0f;
+    if (j0 < j1) load_blk(j0);
     for (int jb = j0; jb < j1; jb += 32) {
-        for (int e = t; e < 32 * 32 * MT; e += kMfRowThreads) {
-            const int r = e / (32 * MT), k = e % (32 * MT), j = jb + r;
-            sG[r * GS + k] = (j < j1 && k < K) ? g[(size_t)j * K + k] : 0.0f;
-        }
-        for (int e = t; e < 32 * 32 * NTW; e += kMfRowThreads) {
-            const int r = e / (32 * NTW), c = e % (32 * NTW), j = jb + r;
-            float u = 0.0f;
-            if (j < j1 && c < W) {
-                if constexpr (PASS == 1)
-                    u = c < dv ? Elem<T>::load(v_bh, (size_t)j * dv + c) : 1.0f;
-                else
-                    u = c < dv ? gnum_bh[(size_t)j * dv + c] : gden_bh[j];
-            }
-            sU[r * US + c] = u;
-        }
+        store_blk();
         __syncthreads();
+        if (jb + 32 < j1) load_blk(jb + 32);  // in flight during the products
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int tau = wv + kWaves * u;
             if (tau < kTiles) {
                 const int m = tau / NTW, n = tau % NTW;
-                const float* ga = sG + half * GS + 32 * m + col;
-                const float* ub = sU + half * US + 32 * n + col;
 #pragma unroll
-                for (int st = 0; st < 16; ++st)
-                    acc[u] = mfma_f32(ga[2 * st * GS], ub[2 * st * US], acc[u]);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const mf::bf16x8 ah = mf::lds_frag_tr(sGh, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 al = mf::lds_frag_tr(sGl, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 bh = mf::lds_frag_tr(sUh, UB, 16 * ks, 32 * n);
+                    acc[u] = mf::mfma(ah, bh, acc[u]);
+                    acc[u] = mf::mfma(al, bh, acc[u]);
+                    if (ULO) acc[u] = mf::mfma(ah, mf::lds_frag_tr(sUl, UB, 16 * ks, 32 * n), acc[u]);
+                }
             }
         }
         __syncthreads();
@@ -2119,31 +2208,37 @@ __global__ void __launch_bounds__(kMfRowThreads)
     }
 }
 
+template <int MT, int NTW>
+constexpr size_t partial_bf16_lds() {
+    return (size_t)32 * (2 * (64 * MT + 32) + 2 * (64 * NTW + 32));
+}
+
 template <typename T, int PASS, int MT, int NTW>
-hipError_t launch_partial_mfma_t(const Args& a, const float* gamma, const float* gnum, const float* gden, float* part,
+hipError_t launch_partial_bf16_t(const Args& a, const float* gamma, const float* gnum, const float* gden, float* part,
                                  const BwdLayout& L) {
     const gma_desc& d = a.d;
-    constexpr int GS = 32 * (MT + (MT % 2 == 0 ? 1 : 0)), US = 32 * (NTW + (NTW % 2 == 0 ? 1 : 0));
-    const size_t lds = (size_t)32 * (GS + US) * sizeof(float);
+    constexpr size_t lds = partial_bf16_lds<MT, NTW>();
+    const bool vec = d.K % 4 == 0 && d.d_v % 4 == 0;
+    auto fn = vec ? &bwd_seg_partial_bf16<T, PASS, MT, NTW, true> : &bwd_seg_partial_bf16<T, PASS, MT, NTW, false>;
     hipError_t e;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_seg_partial_mfma<T, PASS, MT, NTW>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)lds)) != hipSuccess)
         return e;
-    bwd_seg_partial_mfma<T, PASS, MT, NTW><<<dim3((unsigned)(d.B * d.H * L.seg)), dim3(kMfRowThreads), lds, a.stream>>>(
+    fn<<<dim3((unsigned)(d.B * d.H * L.seg)), dim3(kMfRowThreads), lds, a.stream>>>(
         gamma, static_cast<const T*>(a.v), gnum, gden, part, d.B * d.H, d.N, d.K, d.d_v, L.seg, L.seg_len);
     return hipGetLastError();
 }
 
 template <typename T, int PASS>
-hipError_t launch_partial_mfma(const Args& a, int MT, int NTW, const float* gamma, const float* gnum,
+hipError_t launch_partial_bf16(const Args& a, int MT, int NTW, const float* gamma, const float* gnum,
                                const float* gden, float* part, const BwdLayout& L) {
-#define GMA_BWD_PM(mt, ntw) \
-    if (MT == mt && NTW == ntw) return launch_partial_mfma_t<T, PASS, mt, ntw>(a, gamma, gnum, gden, part, L);
-    GMA_BWD_PM(1, 1) GMA_BWD_PM(1, 2) GMA_BWD_PM(1, 3)
-    GMA_BWD_PM(2, 1) GMA_BWD_PM(2, 2) GMA_BWD_PM(2, 3)
-    GMA_BWD_PM(4, 1) GMA_BWD_PM(4, 2) GMA_BWD_PM(4, 3)
-    GMA_BWD_PM(8, 1) GMA_BWD_PM(8, 2) GMA_BWD_PM(8, 3)
-#undef GMA_BWD_PM
+#define GMA_BWD_PB(mt, ntw) \
+    if (MT == mt && NTW == ntw) return launch_partial_bf16_t<T, PASS, mt, ntw>(a, gamma, gnum, gden, part, L);
+    GMA_BWD_PB(1, 1) GMA_BWD_PB(1, 2) GMA_BWD_PB(1, 3)
+    GMA_BWD_PB(2, 1) GMA_BWD_PB(2, 2) GMA_BWD_PB(2, 3)
+    GMA_BWD_PB(4, 1) GMA_BWD_PB(4, 2) GMA_BWD_PB(4, 3)
+    GMA_BWD_PB(8, 1) GMA_BWD_PB(8, 2) GMA_BWD_PB(8, 3)
+#undef GMA_BWD_PB
     return hipErrorInvalidValue;
 }
 
@@ -2165,7 +2260,7 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
         const int MT = d.K <= 32 ? 1 : (d.K <= 64 ? 2 : (d.K <= 128 ? 4 : (d.K <= 256 ? 8 : 0)));
         const int NTW = (d.d_v + 1 + 31) / 32;
         if (MT > 0 && NTW <= 3) {
-            e = launch_partial_mfma<T, PASS>(a, MT, NTW, gamma, gnum, gden, part, L);
+            e = launch_partial_bf16<T, PASS>(a, MT, NTW, gamma, gnum, gden, part, L);
             p_done = true;
         }
     }
@@ -2242,67 +2337,139 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
     return hipGetLastError();
 }
 
-// Parameter-gradient sums on the matrix cores (bf16 inputs, float dl): for chunk c of head h,
-// S1 = dl^T x and S2 = dl^T x^2 (K x d_r) from blocks of 32 of the chunk's rows staged in LDS
-// (dl and x as float; strides padded as in bwd_seg_partial_mfma), the MT x NTD output tiles
-// dealt over the 4 waves, each v_mfma_f32_32x32x2_f32 step contracting one row per lane half
-// (x^2 formed from the staged x); S0 = sum dl by one thread per component, rows in order.
+// Parameter-gradient sums on bf16 matrix cores (bf16 inputs, float dl; the split-bf16 form
+// of the row contractions above): for chunk c of head h, S1 = dl^T x, S2 = dl^T x^2 and
+// S0 = dl^T 1 over the chunk's rows (both sides, all b), dl split into hi/lo, x exact in
+// bf16, x^2 split exactly into hi/lo (x^2 of a bf16 value has at most 16 significant bits).
+// The MT x NTD tiles of S1 and S2 are dealt over the 4 waves; the wave of tile (m, 0) also
+// forms S0 of component tile m against a ones operand.  Staging in groups of 4 columns; VEC
+// (K and d_r multiples of 4): one 16-byte load of dl and one 8-byte load of x per group.
 // Workgroup z takes components [32 MT z, 32 MT (z + 1)).  Grid (H, chunks, ceil(K / (32 MT))).
-template <typename T, int MT, int NTD>
-__global__ void __launch_bounds__(kMfRowThreads, 4)
-    bwd_param_mfma(const T* __restrict__ qr, const T* __restrict__ kr, const float* __restrict__ dl,
+template <typename T, int MT, int NTD, bool VEC>
+__global__ void __launch_bounds__(kMfRowThreads, 2)
+    bwd_param_bf16(const T* __restrict__ qr, const T* __restrict__ kr, const float* __restrict__ dl,
                    double* __restrict__ p1, double* __restrict__ p2, double* __restrict__ p0, int B, int H, int N,
                    int K, int dr, int per_chunk) {
+    static_assert(sizeof(T) == 2, "bf16 routing rows");
     extern __shared__ double smem_d[];
-    constexpr int GS = 32 * (MT + (MT % 2 == 0 ? 1 : 0)), XS = 32 * (NTD + (NTD % 2 == 0 ? 1 : 0));
+    constexpr int GC = 32 * MT, XC = 32 * NTD;
+    constexpr int GB = 2 * GC + 32, XB = 2 * XC + 32;
+    constexpr int NG = 32 * (GC / 4) / kMfRowThreads, NX = (32 * (XC / 4) + kMfRowThreads - 1) / kMfRowThreads;
     constexpr int kTiles = MT * NTD, kWaves = kMfRowThreads / 64, TPW = (kTiles + kWaves - 1) / kWaves;
-    size_t* sRow = reinterpret_cast<size_t*>(smem_d);   // [32] x row of each staged row
-    int* sSide = reinterpret_cast<int*>(sRow + 32);     // [32]
-    float* sD = reinterpret_cast<float*>(sSide + 32);   // [32][GS]
-    float* sX = sD + 32 * GS;                           // [32][XS]
+    unsigned char* sGh = reinterpret_cast<unsigned char*>(smem_d);
+    unsigned char* sGl = sGh + 32 * GB;
+    unsigned char* sX = sGl + 32 * GB;
+    unsigned char* sX2h = sX + 32 * XB;
+    unsigned char* sX2l = sX2h + 32 * XB;
     const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
     const int h = blockIdx.x, c = blockIdx.y, kz = 32 * MT * blockIdx.z;
     const int BH = B * H, BN = B * N;
     const int u0 = c * per_chunk, u1 = min(2 * BN, u0 + per_chunk);
-    f32x16 a1[TPW], a2[TPW];
+    // row u of the chunk: side u / BN (queries, keys), batch and position; the row of dl is
+    // side * BH * N + (b H + h) N + i, the routing row (b H + h) N + i of qr or kr
+    auto rows = [&](int u, size_t& drow, const T*& xrow) {
+        const int uu = min(u, u1 - 1);
+        const int side = uu / BN, rem = uu - side * BN, b = rem / N, i = rem - b * N;
+        const size_t r = ((size_t)b * H + h) * N + i;
+        drow = (size_t)side * BH * N + r;
+        xrow = (side == 0 ? qr : kr) + r * dr;
+    };
+    float4 gv[NG];
+    uint2 xv[NX];
+    auto load_blk = [&](int ub) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int e = t + kMfRowThreads * i, r = e / (GC / 4), k = 4 * (e % (GC / 4)), u = ub + r;
+            size_t drow;
+            const T* xrow;
+            rows(u, drow, xrow);
+            const float* g = dl + drow * K + kz + k;
+            const bool in = u < u1;
+            if (VEC) {
+                gv[i] = (in && kz + k < K) ? *reinterpret_cast<const float4*>(g) : make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+                gv[i].x = (in && kz + k < K) ? g[0] : 0.0f;
+                gv[i].y = (in && kz + k + 1 < K) ? g[1] : 0.0f;
+                gv[i].z = (in && kz + k + 2 < K) ? g[2] : 0.0f;
+                gv[i].w = (in && kz + k + 3 < K) ? g[3] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int e = t + kMfRowThreads * i, r = e / (XC / 4), d = 4 * (e % (XC / 4)), u = ub + r;
+            size_t drow;
+            const T* xrow;
+            rows(u, drow, xrow);
+            const bool in = u < u1 && r < 32;
+            if (VEC) {
+                xv[i] = (in && d < dr) ? *reinterpret_cast<const uint2*>(xrow + d) : make_uint2(0u, 0u);
+            } else {
+                uint32_t w[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = (in && d + q < dr) ? (uint32_t)xrow[d + q] : 0u;
+                xv[i] = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+            }
+        }
+    };
+    auto store_blk = [&]() {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            const int e = t + kMfRowThreads * i, r = e / (GC / 4), k = 4 * (e % (GC / 4));
+            uint2 hi, lo;
+            split_pair(gv[i].x, gv[i].y, hi.x, lo.x);
+            split_pair(gv[i].z, gv[i].w, hi.y, lo.y);
+            *reinterpret_cast<uint2*>(sGh + r * GB + 2 * k) = hi;
+            *reinterpret_cast<uint2*>(sGl + r * GB + 2 * k) = lo;
+        }
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int e = t + kMfRowThreads * i, r = e / (XC / 4), d = 4 * (e % (XC / 4));
+            if (r < 32) {
+                const float x0 = mf::bf16lo_to_f32(xv[i].x), x1 = mf::bf16hi_to_f32(xv[i].x);
+                const float x2 = mf::bf16lo_to_f32(xv[i].y), x3 = mf::bf16hi_to_f32(xv[i].y);
+                uint2 hi, lo;
+                split_pair(x0 * x0, x1 * x1, hi.x, lo.x);  // exact: x^2 has <= 16 significant bits
+                split_pair(x2 * x2, x3 * x3, hi.y, lo.y);
+                *reinterpret_cast<uint2*>(sX + r * XB + 2 * d) = xv[i];
+                *reinterpret_cast<uint2*>(sX2h + r * XB + 2 * d) = hi;
+                *reinterpret_cast<uint2*>(sX2l + r * XB + 2 * d) = lo;
+            }
+        }
+    };
+    f32x16 a1[TPW], a2[TPW], a0[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) a1[u][e] = a2[u][e] = 0.0f;
-    float s0 = 0.0f;
+        for (int e = 0; e < 16; ++e) a1[u][e] = a2[u][e] = a0[u][e] = 0.0f;
+    mf::bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (short)0x3f80;
+    if (u0 < u1) load_blk(u0);
     for (int ub = u0; ub < u1; ub += 32) {
-        if (t < 32) {
-            const int u = min(ub + t, u1 - 1);  // rows past the chunk: a valid row, zeroed below
-            const int side = u / BN, rem = u - side * BN, b = rem / N, i = rem - b * N;
-            sRow[t] = ((size_t)b * H + h) * N + i;
-            sSide[t] = side;
-        }
+        store_blk();
         __syncthreads();
-        for (int e = t; e < 32 * 32 * MT; e += kMfRowThreads) {
-            const int r = e / (32 * MT), k = e % (32 * MT);
-            const size_t drow = (size_t)sSide[r] * BH * N + sRow[r];
-            sD[r * GS + k] = (ub + r < u1 && kz + k < K) ? dl[drow * K + kz + k] : 0.0f;
-        }
-        for (int e = t; e < 32 * 32 * NTD; e += kMfRowThreads) {
-            const int r = e / (32 * NTD), d = e % (32 * NTD);
-            sX[r * XS + d] = (ub + r < u1 && d < dr) ? Elem<T>::load(sSide[r] == 0 ? qr : kr, sRow[r] * dr + d) : 0.0f;
-        }
-        __syncthreads();
-        if (t < 32 * MT) {
-            for (int r = 0; r < 32; ++r) s0 += sD[r * GS + t];
-        }
+        if (ub + 32 < u1) load_blk(ub + 32);  // in flight during the products
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int tau = wv + kWaves * u;
             if (tau < kTiles) {
                 const int m = tau / NTD, n = tau % NTD;
-                const float* da = sD + half * GS + 32 * m + col;
-                const float* xb = sX + half * XS + 32 * n + col;
 #pragma unroll
-                for (int st = 0; st < 16; ++st) {
-                    const float av = da[2 * st * GS], xv = xb[2 * st * XS];
-                    a1[u] = mfma_f32(av, xv, a1[u]);
-                    a2[u] = mfma_f32(av, xv * xv, a2[u]);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const mf::bf16x8 ah = mf::lds_frag_tr(sGh, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 al = mf::lds_frag_tr(sGl, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 bx = mf::lds_frag_tr(sX, XB, 16 * ks, 32 * n);
+                    const mf::bf16x8 b2h = mf::lds_frag_tr(sX2h, XB, 16 * ks, 32 * n);
+                    const mf::bf16x8 b2l = mf::lds_frag_tr(sX2l, XB, 16 * ks, 32 * n);
+                    a1[u] = mf::mfma(ah, bx, a1[u]);
+                    a1[u] = mf::mfma(al, bx, a1[u]);
+                    a2[u] = mf::mfma(ah, b2h, a2[u]);
+                    a2[u] = mf::mfma(al, b2h, a2[u]);
+                    a2[u] = mf::mfma(ah, b2l, a2[u]);
+                    if (n == 0) {
+                        a0[u] = mf::mfma(ah, ones, a0[u]);
+                        a0[u] = mf::mfma(al, ones, a0[u]);
+                    }
                 }
             }
         }
@@ -2321,24 +2488,25 @@ __global__ void __launch_bounds__(kMfRowThreads, 4)
                     p1[(base + k) * dr + d] = (double)a1[u][e];
                     p2[(base + k) * dr + d] = (double)a2[u][e];
                 }
+                if (n == 0 && col == 0 && k < K) p0[base + k] = (double)a0[u][e];
             }
         }
     }
-    if (t < 32 * MT && kz + t < K) p0[base + kz + t] = (double)s0;
 }
 
 template <typename T, int MT, int NTD>
-hipError_t launch_param_mfma_t(const Args& a, const BwdLayout& L, const float* dl, double* pmu, double* pvar,
+hipError_t launch_param_bf16_t(const Args& a, const BwdLayout& L, const float* dl, double* pmu, double* pvar,
                                double* ppi) {
     const gma_desc& d = a.d;
-    constexpr int GS = 32 * (MT + (MT % 2 == 0 ? 1 : 0)), XS = 32 * (NTD + (NTD % 2 == 0 ? 1 : 0));
-    const size_t lds = 32 * (sizeof(size_t) + sizeof(int)) + (size_t)32 * (GS + XS) * sizeof(float);
+    const size_t lds = (size_t)32 * (2 * (64 * MT + 32) + 3 * (64 * NTD + 32));
+    const bool vec = d.K % 4 == 0 && d.d_r % 4 == 0;
+    auto fn = vec ? &bwd_param_bf16<T, MT, NTD, true> : &bwd_param_bf16<T, MT, NTD, false>;
     hipError_t e;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_param_mfma<T, MT, NTD>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)lds)) != hipSuccess)
         return e;
     const unsigned kzs = (unsigned)((d.K + 32 * MT - 1) / (32 * MT));
-    bwd_param_mfma<T, MT, NTD><<<dim3((unsigned)d.H, (unsigned)L.chunks, kzs), dim3(kMfRowThreads), lds, a.stream>>>(
+    fn<<<dim3((unsigned)d.H, (unsigned)L.chunks, kzs), dim3(kMfRowThreads), lds, a.stream>>>(
         static_cast<const T*>(a.qr), static_cast<const T*>(a.kr), dl, pmu, pvar, ppi, d.B, d.H, d.N, d.K, d.d_r,
         L.per_chunk);
     return hipGetLastError();
@@ -2346,15 +2514,16 @@ hipError_t launch_param_mfma_t(const Args& a, const BwdLayout& L, const float* d
 
 // MT = 32-component tiles per workgroup (1, 2, 4), NTD = 32-dim tiles (1, 2).
 template <typename T>
-hipError_t launch_param_mfma(const Args& a, int MT, int NTD, const BwdLayout& L, const float* dl, double* pmu,
+hipError_t launch_param_bf16(const Args& a, int MT, int NTD, const BwdLayout& L, const float* dl, double* pmu,
                              double* pvar, double* ppi) {
-#define GMA_BWD_PP(mt, ntd) \
-    if (MT == mt && NTD == ntd) return launch_param_mfma_t<T, mt, ntd>(a, L, dl, pmu, pvar, ppi);
-    GMA_BWD_PP(1, 1) GMA_BWD_PP(1, 2) GMA_BWD_PP(2, 1) GMA_BWD_PP(2, 2)
-    GMA_BWD_PP(4, 1) GMA_BWD_PP(4, 2)
-#undef GMA_BWD_PP
+#define GMA_BWD_PPB(mt, ntd) \
+    if (MT == mt && NTD == ntd) return launch_param_bf16_t<T, mt, ntd>(a, L, dl, pmu, pvar, ppi);
+    GMA_BWD_PPB(1, 1) GMA_BWD_PPB(1, 2) GMA_BWD_PPB(2, 1) GMA_BWD_PPB(2, 2)
+    GMA_BWD_PPB(4, 1) GMA_BWD_PPB(4, 2)
+#undef GMA_BWD_PPB
     return hipErrorInvalidValue;
 }
+
 
 template <typename T, typename A>
 hipError_t backward_t(const Args& a, const BwdArgs& g) {
@@ -2421,7 +2590,7 @@ hipError_t backward_t(const Args& a, const BwdArgs& g) {
             const int MT = d.K <= 32 ? 1 : (d.K <= 64 ? 2 : 4);
             const int NTD = (d.d_r + 31) / 32;
             if (NTD <= 2) {
-                e = launch_param_mfma<T>(a, MT, NTD, L, dl, pmu, pvar, ppi);
+                e = launch_param_bf16<T>(a, MT, NTD, L, dl, pmu, pvar, ppi);
                 p_done = true;
             }
         }
