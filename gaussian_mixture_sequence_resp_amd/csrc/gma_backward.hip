@@ -41,8 +41,8 @@
 //                  chunk walk, 16 rows at a time, on the vector ALUs
 //   bwd_seg_rows     causal otherwise: one workgroup per (b, h, segment) walks its rows (pass
 //                  2 in reverse) with the state in LDS (in the workspace when it does not fit)
-//   bwd_bidir_mfma bidirectional, bf16 inputs: the per-row arithmetic against the head's
-//                  total as fp32 matrix-core products over 32-row tiles
+//   bwd_bidir_bf16 bidirectional, bf16 inputs: the per-row arithmetic against the head's
+//                  total as split-bf16 matrix-core products over 32-row tiles
 //   bwd_bidir_rows   bidirectional otherwise: the same per-row arithmetic, each wave of a
 //                  workgroup walking its own rows
 //   bwd_x_bf16     bf16 inputs, d_r <= 64: dqr, dkr = Q - x P with P = dl lam, Q = dl (mu lam)
@@ -394,22 +394,15 @@ __global__ void __launch_bounds__(kRowThreads)
     }
 }
 
-// Bidirectional rows on the matrix cores (bf16 inputs: float state and gamma).  Each wave
-// takes 32 rows at a time.  With G the rows' own gamma (32 x K) and St the head's total
-// (K x W, W = d_v + 1):
-//   C1 = St^T G^T (W x 32): pass 1 [num | den - eps] of every row, pass 2 [dv | .];
-//   the per-row epilogue turns C1 into w (pass 1 [g_num | g_den], pass 2 [v | 1]);
-//   C2 = St w^T (K x 32): dgamma of every row; then dl = gamma (dgamma - gamma . dgamma).
-// v_mfma_f32_32x32x2_f32 (fp32 products and sums).  Every contraction step pairs one index
-// of each lane half, chosen so that the B operand of the step is a register the lane already
-// holds in the C layout (lane l, register i of tile m: index 32 m + 8 (i / 4) + 4 (l / 32) +
-// i % 4 of row l % 32): gamma feeds C1 and the dl epilogue from the same registers, and C1
-// after the epilogue is the B operand of C2.  St sits in LDS as [32 MT][32 NTW + 1], zero
-// padded; the odd row length puts 32 consecutive rows of one column in distinct banks.
-// Grid (BH ceil(N / RB)): a workgroup takes RB rows of one head, its waves 32-row tiles in
-// turn, all against the one staged copy of the head's total (slot 0 of its SEG segments).
+// Matrix-core forms for bf16 inputs (float state, gamma and row gradients).  The fp32 form
+// (v_mfma_f32_32x32x2_f32, used by the causal chunk walks) pairs one contraction index of
+// each lane half per step, chosen so that the B operand of the step is a register the lane
+// already holds in the C layout (lane l, register i of tile m: index 32 m + 8 (i / 4) +
+// 4 (l / 32) + i % 4 of row l % 32).  The split-bf16 forms (v_mfma_f32_32x32x16_bf16 on
+// hi/lo pairs) stage or regroup their operands into 8 consecutive contraction indices per
+// lane.  Row kernels take blocks of RB rows of one head, their waves 32-row tiles in turn.
 constexpr int kMfRowThreads = 256;
-constexpr int kMfRowBlock = 512;  // rows per workgroup of bwd_bidir_mfma: 4 tiles per wave
+constexpr int kMfRowBlock = 512;  // rows per workgroup of bwd_bidir_bf16: 4 tiles per wave
 using mf::f32x16;
 using mf::sum_halves;
 
@@ -417,153 +410,11 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Two waves per SIMD requested at MT = 4 (measured faster); smaller tiles keep the default
-// (there the bound made one instantiation spill).
-template <typename T, int PASS, int MT, int NTW>
-__global__ void __launch_bounds__(kMfRowThreads, MT == 4 ? 2 : 1)
-    bwd_bidir_mfma(const float* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
-                   float* __restrict__ gnum, float* __restrict__ gden, float* __restrict__ dl, T* __restrict__ dv_out,
-                   const float* __restrict__ start, int BH, int N, int K, int dv, float eps, int SEG, int RB) {
-    extern __shared__ double smem_d[];
-    float* sS = reinterpret_cast<float*>(smem_d);
-    constexpr int Kp = 32 * MT, Wp = 32 * NTW, Ws = Wp + 1;
-    const int W = dv + 1;
-    const int NB = (N + RB - 1) / RB;
-    const int bs = blockIdx.x, bh = bs / NB, blk = bs % NB;
-    const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
-    const float* st0 = start + (size_t)bh * SEG * K * W;  // slot 0: the head's total
-    for (int e = t; e < Kp * Wp; e += kMfRowThreads) {
-        const int k = e / Wp, c = e % Wp;
-        sS[k * Ws + c] = (k < K && c < W) ? st0[(size_t)k * W + c] : 0.0f;
-    }
-    __syncthreads();
-    const size_t side = PASS == 1 ? 0 : (size_t)BH;
-    const float* g_bh = gamma + (side + bh) * N * K;
-    float* dl_bh = dl + (side + bh) * N * K;
-    const int i0 = blk * RB, i1 = min(N, i0 + RB);
-    const bool vec_k = (K & 3) == 0;
-    for (int tb = i0 + 32 * wv; tb < i1; tb += 32 * (kMfRowThreads / 64)) {
-        const int row = tb + col;
-        const bool ok = row < i1;
-        const size_t rr = (size_t)(ok ? row : i0);  // rows past the segment read a valid row
-        // gamma of this lane's row at its C-layout indices (zero past K)
-        f32x16 g[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int k0 = 32 * m + 8 * q + 4 * half;
-                if (vec_k && k0 < K) {
-                    const float4 x = *reinterpret_cast<const float4*>(g_bh + rr * K + k0);
-                    g[m][4 * q] = x.x;
-                    g[m][4 * q + 1] = x.y;
-                    g[m][4 * q + 2] = x.z;
-                    g[m][4 * q + 3] = x.w;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) g[m][4 * q + j] = k0 + j < K ? g_bh[rr * K + k0 + j] : 0.0f;
-                }
-            }
-        // C1 = St^T G^T: step (m, i) contracts index 32 m + 8 (i / 4) + 4 h + i % 4 of half h
-        f32x16 c1[NTW];
-#pragma unroll
-        for (int n = 0; n < NTW; ++n)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) c1[n][i] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float* srow = sS + (32 * m + 8 * (i >> 2) + 4 * half + (i & 3)) * Ws + col;
-#pragma unroll
-                for (int n = 0; n < NTW; ++n) c1[n] = mfma_f32(srow[32 * n], g[m][i], c1[n]);
-            }
-        // epilogue: C1 register i of tile n is column c = 32 n + 8 (i / 4) + 4 h + i % 4
-        if constexpr (PASS == 1) {
-            const T* do_r = dout + ((size_t)bh * N + rr) * dv;
-            float dp = 0.0f;
-#pragma unroll
-            for (int n = 0; n < NTW; ++n)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (32 * n + 8 * (i >> 2) + 4 * half + (i & 3) == dv) dp = c1[n][i];
-            const float den = sum_halves(dp) + eps;
-            float dot = 0.0f;
-#pragma unroll
-            for (int n = 0; n < NTW; ++n)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int c = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
-                    if (c < dv) dot += Elem<T>::load(do_r, c) * (c1[n][i] / den);
-                }
-            const float gd = -sum_halves(dot) / den;
-            float* gn = gnum + ((size_t)bh * N + rr) * dv;
-#pragma unroll
-            for (int n = 0; n < NTW; ++n)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int c = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
-                    const float wv_c = c < dv ? Elem<T>::load(do_r, c) / den : (c == dv ? gd : 0.0f);
-                    c1[n][i] = wv_c;
-                    if (ok && c < dv) gn[c] = wv_c;
-                }
-            if (ok && half == 0) gden[(size_t)bh * N + rr] = gd;
-        } else {
-            const T* v_r = v + ((size_t)bh * N + rr) * dv;
-            T* dvo = dv_out + ((size_t)bh * N + rr) * dv;
-#pragma unroll
-            for (int n = 0; n < NTW; ++n)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int c = 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
-                    if (ok && c < dv) Elem<T>::store(dvo, c, c1[n][i]);
-                    c1[n][i] = c < dv ? Elem<T>::load(v_r, c) : (c == dv ? 1.0f : 0.0f);
-                }
-        }
-        // C2 = St w^T: step (n, i) contracts column 32 n + 8 (i / 4) + 4 h + i % 4 of half h
-        f32x16 c2[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) c2[m][i] = 0.0f;
-#pragma unroll
-        for (int n = 0; n < NTW; ++n)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float* scol = sS + col * Ws + 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
-#pragma unroll
-                for (int m = 0; m < MT; ++m) c2[m] = mfma_f32(scol[32 * m * Ws], c1[n][i], c2[m]);
-            }
-        // dl = gamma (dgamma - gamma . dgamma)
-        float sp = 0.0f;
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sp += g[m][i] * c2[m][i];
-        const float s = sum_halves(sp);
-        if (ok) {
-            float* dl_r = dl_bh + rr * K;
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int k0 = 32 * m + 8 * q + 4 * half;
-                    float4 x;
-                    x.x = g[m][4 * q] * (c2[m][4 * q] - s);
-                    x.y = g[m][4 * q + 1] * (c2[m][4 * q + 1] - s);
-                    x.z = g[m][4 * q + 2] * (c2[m][4 * q + 2] - s);
-                    x.w = g[m][4 * q + 3] * (c2[m][4 * q + 3] - s);
-                    if (vec_k && k0 < K) {
-                        *reinterpret_cast<float4*>(dl_r + k0) = x;
-                    } else {
-                        if (k0 < K) dl_r[k0] = x.x;
-                        if (k0 + 1 < K) dl_r[k0 + 1] = x.y;
-                        if (k0 + 2 < K) dl_r[k0 + 2] = x.z;
-                        if (k0 + 3 < K) dl_r[k0 + 3] = x.w;
-                    }
-                }
-        }
-    }
+// Two fp32 values as their bf16 hi and lo pairs (element 0 in the low half): hi = rne(v),
+// lo = rne(v - hi), v to ~2^-17 relative.
+__device__ __forceinline__ void split_pair(float v0, float v1, uint32_t& hi, uint32_t& lo) {
+    hi = mf::pack_bf16(v0, v1);
+    lo = mf::pack_bf16(v0 - mf::bf16lo_to_f32(hi), v1 - mf::bf16hi_to_f32(hi));
 }
 
 // Causal rows in chunks of kCh positions (the chunked form of the walk, as the forward's
@@ -1965,23 +1816,6 @@ BwdLayout bwd_layout(const gma_desc& d) {
 
 // One pass over the rows: segment partials, their ordered starts, then the segment walks.
 template <typename T, int PASS, int MT, int NTW>
-hipError_t launch_bidir_mfma_t(const Args& a, const BwdArgs& g, const float* gamma, float* gnum, float* gden,
-                               float* dl, const float* start, const BwdLayout& L) {
-    const gma_desc& d = a.d;
-    const int BH = d.B * d.H;
-    const size_t lds = (size_t)(32 * MT) * (32 * NTW + 1) * sizeof(float);
-    hipError_t e;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_bidir_mfma<T, PASS, MT, NTW>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-        return e;
-    const int nb = (d.N + kMfRowBlock - 1) / kMfRowBlock;
-    bwd_bidir_mfma<T, PASS, MT, NTW><<<dim3((unsigned)(BH * nb)), dim3(kMfRowThreads), lds, a.stream>>>(
-        gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
-        start, BH, d.N, d.K, d.d_v, a.eps, L.seg, kMfRowBlock);
-    return hipGetLastError();
-}
-
-template <typename T, int PASS, int MT, int NTW>
 hipError_t launch_causal_mfma_t(const Args& a, const BwdArgs& g, const float* gamma, float* gnum, float* gden,
                                 float* dl, const float* start, const BwdLayout& L) {
     const gma_desc& d = a.d;
@@ -2032,12 +1866,299 @@ hipError_t launch_causal_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, 
     return hipErrorInvalidValue;
 }
 
+// Bidirectional rows on bf16 matrix cores (v_mfma_f32_32x32x16_bf16) with exact hi/lo
+// splits of the fp32 operands (products hi.hi + lo.hi + hi.lo).  Each wave takes 32 rows at
+// a time.  With G the rows' own gamma (32 x K) and St the head's total (K x W, W = d_v + 1):
+// C1 = St^T G^T (W x 32) is pass 1's [num | den - eps] of every row, pass 2's [dv | .]; the
+// per-row epilogue turns C1 into w (pass 1 [g_num | g_den], pass 2 [v | 1]); C2 = St w^T
+// (K x 32) is dgamma of every row; then dl = gamma (dgamma - gamma . dgamma).  St is staged
+// once per workgroup as bf16 hi and lo rows [Kp][Wp] (row stride 2 Wp + 16 bytes);
+//   C1 = St^T G^T: A = St^T (lane: column c, 8 consecutive k: transposed LDS reads of St),
+//                  B = G^T (lane: its row's gamma at 8 consecutive k, loaded from the row and
+//                  split in registers);
+//   C2 = St w^T:   A = St (lane: row k, 8 consecutive c: 16-byte LDS reads), B = w^T (the
+//                  epilogue's w, C layout, regrouped to 8 consecutive columns per lane by one
+//                  lane-half swap per register pair, then split).
+// Gamma in the C layout for dl is loaded after C2.  Grid (BH ceil(N / RB)).
+template <typename T, int PASS, int MT, int NTW>
+__global__ void __launch_bounds__(kMfRowThreads, 2)
+    bwd_bidir_bf16(const float* __restrict__ gamma, const T* __restrict__ v, const T* __restrict__ dout,
+                   float* __restrict__ gnum, float* __restrict__ gden, float* __restrict__ dl, T* __restrict__ dv_out,
+                   const float* __restrict__ start, int BH, int N, int K, int dv, float eps, int SEG, int RB) {
+    extern __shared__ double smem_d[];
+    constexpr int Kp = 32 * MT, Wp = 32 * NTW, SB = 2 * Wp + 16, KS = Kp / 16, CS = Wp / 16;
+    unsigned char* sSh = reinterpret_cast<unsigned char*>(smem_d);
+    unsigned char* sSl = sSh + (size_t)Kp * SB;
+    const int W = dv + 1;
+    const int NB = (N + RB - 1) / RB;
+    const int bs = blockIdx.x, bh = bs / NB, blk = bs % NB;
+    const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
+    const float* st0 = start + (size_t)bh * SEG * K * W;  // slot 0: the head's total
+    for (int e = t; e < Kp * Wp / 2; e += kMfRowThreads) {
+        const int k = e / (Wp / 2), c = 2 * (e % (Wp / 2));
+        const float v0 = (k < K && c < W) ? st0[(size_t)k * W + c] : 0.0f;
+        const float v1 = (k < K && c + 1 < W) ? st0[(size_t)k * W + c + 1] : 0.0f;
+        uint32_t hi, lo;
+        split_pair(v0, v1, hi, lo);
+        *reinterpret_cast<uint32_t*>(sSh + (size_t)k * SB + 2 * c) = hi;
+        *reinterpret_cast<uint32_t*>(sSl + (size_t)k * SB + 2 * c) = lo;
+    }
+    __syncthreads();
+    const size_t side = PASS == 1 ? 0 : (size_t)BH;
+    const float* g_bh = gamma + (side + bh) * N * K;
+    float* dl_bh = dl + (side + bh) * N * K;
+    const int i0 = blk * RB, i1 = min(N, i0 + RB);
+    const bool vec_k = (K & 3) == 0;
+    for (int tb = i0 + 32 * wv; tb < i1; tb += 32 * (kMfRowThreads / 64)) {
+        const int row = tb + col;
+        const bool ok = row < i1;
+        const size_t rr = (size_t)(ok ? row : i0);  // rows past the segment read a valid row
+        const float* grow = g_bh + rr * K;
+        // ---- C1 = St^T G^T, G^T from this lane's row: k = 16 ks + 8 half + 0..7
+        f32x16 c1[NTW];
+#pragma unroll
+        for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c1[n][i] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k0 = 16 * ks + 8 * half;
+            float x[8];
+            if (vec_k) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float4 f = k0 + 4 * q < K ? *reinterpret_cast<const float4*>(grow + k0 + 4 * q)
+                                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+                    x[4 * q] = f.x;
+                    x[4 * q + 1] = f.y;
+                    x[4 * q + 2] = f.z;
+                    x[4 * q + 3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = k0 + j < K ? grow[k0 + j] : 0.0f;
+            }
+            mf::u32x4 bh_, bl_;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t hi, lo;
+                split_pair(x[2 * j], x[2 * j + 1], hi, lo);
+                bh_[j] = hi;
+                bl_[j] = lo;
+            }
+            const mf::bf16x8 gbh = __builtin_bit_cast(mf::bf16x8, bh_), gbl = __builtin_bit_cast(mf::bf16x8, bl_);
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) {
+                const mf::bf16x8 ah = mf::lds_frag_tr(sSh, SB, 16 * ks, 32 * n);
+                const mf::bf16x8 al = mf::lds_frag_tr(sSl, SB, 16 * ks, 32 * n);
+                c1[n] = mf::mfma(ah, gbh, c1[n]);
+                c1[n] = mf::mfma(al, gbh, c1[n]);
+                c1[n] = mf::mfma(ah, gbl, c1[n]);
+            }
+        }
+        // epilogue: C1 register group q of tile n holds columns c0 = 32 n + 8 q + 4 h .. c0 + 3;
+        // with d_v a multiple of 4 (VEC) a group is all value columns or none, and its row
+        // values move as one 8-byte (bf16) or 16-byte (float) access
+        const bool vec_v = (dv & 3) == 0;
+        if constexpr (PASS == 1) {
+            const T* do_r = dout + ((size_t)bh * N + rr) * dv;
+            float dp = 0.0f;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * n + 8 * (i >> 2) + 4 * half + (i & 3) == dv) dp = c1[n][i];
+            const float den = sum_halves(dp) + eps;
+            const float rden = 1.0f / den;
+            // dO of this lane's row at its C-layout columns (0 past d_v)
+            float dov[NTW][16];
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c0 = 32 * n + 8 * q + 4 * half;
+                    if (vec_v) {
+                        const uint2 u = c0 < dv ? *reinterpret_cast<const uint2*>(do_r + c0) : make_uint2(0u, 0u);
+                        dov[n][4 * q] = mf::bf16lo_to_f32(u.x);
+                        dov[n][4 * q + 1] = mf::bf16hi_to_f32(u.x);
+                        dov[n][4 * q + 2] = mf::bf16lo_to_f32(u.y);
+                        dov[n][4 * q + 3] = mf::bf16hi_to_f32(u.y);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) dov[n][4 * q + j] = c0 + j < dv ? Elem<T>::load(do_r, c0 + j) : 0.0f;
+                    }
+                }
+            float dot = 0.0f;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dot += dov[n][i] * (c1[n][i] * rden);
+            const float gd = -sum_halves(dot) * rden;
+            float* gn = gnum + ((size_t)bh * N + rr) * dv;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c0 = 32 * n + 8 * q + 4 * half;
+                    float wq[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int c = c0 + j;
+                        wq[j] = c < dv ? dov[n][4 * q + j] * rden : (c == dv ? gd : 0.0f);
+                        c1[n][4 * q + j] = wq[j];
+                    }
+                    if (vec_v) {
+                        if (ok && c0 < dv) *reinterpret_cast<float4*>(gn + c0) = make_float4(wq[0], wq[1], wq[2], wq[3]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (ok && c0 + j < dv) gn[c0 + j] = wq[j];
+                    }
+                }
+            if (ok && half == 0) gden[(size_t)bh * N + rr] = gd;
+        } else {
+            const T* v_r = v + ((size_t)bh * N + rr) * dv;
+            T* dvo = dv_out + ((size_t)bh * N + rr) * dv;
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c0 = 32 * n + 8 * q + 4 * half;
+                    float cq[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) cq[j] = c1[n][4 * q + j];
+                    if (vec_v) {
+                        if (c0 < dv) {
+                            if (ok)
+                                *reinterpret_cast<uint2*>(dvo + c0) =
+                                    make_uint2(mf::pack_bf16(cq[0], cq[1]), mf::pack_bf16(cq[2], cq[3]));
+                            const uint2 u = *reinterpret_cast<const uint2*>(v_r + c0);
+                            cq[0] = mf::bf16lo_to_f32(u.x);
+                            cq[1] = mf::bf16hi_to_f32(u.x);
+                            cq[2] = mf::bf16lo_to_f32(u.y);
+                            cq[3] = mf::bf16hi_to_f32(u.y);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) cq[j] = c0 + j == dv ? 1.0f : 0.0f;
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int c = c0 + j;
+                            if (ok && c < dv) Elem<T>::store(dvo, c, cq[j]);
+                            cq[j] = c < dv ? Elem<T>::load(v_r, c) : (c == dv ? 1.0f : 0.0f);
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) c1[n][4 * q + j] = cq[j];
+                }
+        }
+        // ---- C2 = St w^T: per 16-column block cs = 2 n + b, w regrouped so that each lane holds
+        // columns 16 cs + 8 half + 0..7 of its row (registers 8 b .. 8 b + 7 of tile n hold
+        // columns 16 b + 4 half + 0..3 and 16 b + 8 + 4 half + 0..3), then split
+        f32x16 c2[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c2[m][i] = 0.0f;
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) {
+            const int n = cs >> 1, i0 = 8 * (cs & 1);
+            uint32_t ph[4], pl[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) split_pair(c1[n][i0 + 2 * j], c1[n][i0 + 2 * j + 1], ph[j], pl[j]);
+            // ph[0], ph[1]: columns +0..3 of this half's first group; ph[2], ph[3]: of its second
+            auto hx = __builtin_amdgcn_permlane32_swap(ph[0], ph[2], false, false);
+            auto hy = __builtin_amdgcn_permlane32_swap(ph[1], ph[3], false, false);
+            auto lx = __builtin_amdgcn_permlane32_swap(pl[0], pl[2], false, false);
+            auto ly = __builtin_amdgcn_permlane32_swap(pl[1], pl[3], false, false);
+            mf::u32x4 wh_, wl_;
+            wh_[0] = hx[0]; wh_[1] = hy[0]; wh_[2] = hx[1]; wh_[3] = hy[1];
+            wl_[0] = lx[0]; wl_[1] = ly[0]; wl_[2] = lx[1]; wl_[3] = ly[1];
+            const mf::bf16x8 wbh = __builtin_bit_cast(mf::bf16x8, wh_), wbl = __builtin_bit_cast(mf::bf16x8, wl_);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const size_t off = (size_t)(32 * m + col) * SB + 2 * (16 * cs + 8 * half);
+                const mf::bf16x8 ah = *reinterpret_cast<const mf::bf16x8*>(sSh + off);
+                const mf::bf16x8 al = *reinterpret_cast<const mf::bf16x8*>(sSl + off);
+                c2[m] = mf::mfma(ah, wbh, c2[m]);
+                c2[m] = mf::mfma(al, wbh, c2[m]);
+                c2[m] = mf::mfma(ah, wbl, c2[m]);
+            }
+        }
+        // gamma of this lane's row at its C-layout indices (zero past K), for dl
+        f32x16 g[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k0 = 32 * m + 8 * q + 4 * half;
+                if (vec_k && k0 < K) {
+                    const float4 x = *reinterpret_cast<const float4*>(grow + k0);
+                    g[m][4 * q] = x.x;
+                    g[m][4 * q + 1] = x.y;
+                    g[m][4 * q + 2] = x.z;
+                    g[m][4 * q + 3] = x.w;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) g[m][4 * q + j] = k0 + j < K ? grow[k0 + j] : 0.0f;
+                }
+            }
+        // dl = gamma (dgamma - gamma . dgamma)
+        float sp = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sp += g[m][i] * c2[m][i];
+        const float s = sum_halves(sp);
+        if (ok) {
+            float* dl_r = dl_bh + rr * K;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k0 = 32 * m + 8 * q + 4 * half;
+                    float4 x;
+                    x.x = g[m][4 * q] * (c2[m][4 * q] - s);
+                    x.y = g[m][4 * q + 1] * (c2[m][4 * q + 1] - s);
+                    x.z = g[m][4 * q + 2] * (c2[m][4 * q + 2] - s);
+                    x.w = g[m][4 * q + 3] * (c2[m][4 * q + 3] - s);
+                    if (vec_k && k0 < K) {
+                        *reinterpret_cast<float4*>(dl_r + k0) = x;
+                    } else {
+                        if (k0 < K) dl_r[k0] = x.x;
+                        if (k0 + 1 < K) dl_r[k0 + 1] = x.y;
+                        if (k0 + 2 < K) dl_r[k0 + 2] = x.z;
+                        if (k0 + 3 < K) dl_r[k0 + 3] = x.w;
+                    }
+                }
+        }
+    }
+}
+
+template <typename T, int PASS, int MT, int NTW>
+hipError_t launch_bidir_bf16_t(const Args& a, const BwdArgs& g, const float* gamma, float* gnum, float* gden,
+                               float* dl, const float* start, const BwdLayout& L) {
+    const gma_desc& d = a.d;
+    const int BH = d.B * d.H;
+    const size_t lds = (size_t)2 * (32 * MT) * (2 * 32 * NTW + 16);
+    hipError_t e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_bidir_bf16<T, PASS, MT, NTW>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    const int nb = (d.N + kMfRowBlock - 1) / kMfRowBlock;
+    bwd_bidir_bf16<T, PASS, MT, NTW><<<dim3((unsigned)(BH * nb)), dim3(kMfRowThreads), lds, a.stream>>>(
+        gamma, static_cast<const T*>(a.v), static_cast<const T*>(g.dout), gnum, gden, dl, static_cast<T*>(g.dv),
+        start, BH, d.N, d.K, d.d_v, a.eps, L.seg, kMfRowBlock);
+    return hipGetLastError();
+}
+
 // MT = 32-component tiles (1, 2 or 4), NTW = 32-column tiles of the state (1, 2 or 3).
 template <typename T, int PASS>
 hipError_t launch_bidir_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, const float* gamma, float* gnum,
                              float* gden, float* dl, const float* start, const BwdLayout& L) {
 #define GMA_BWD_MF(mt, ntw) \
-    if (MT == mt && NTW == ntw) return launch_bidir_mfma_t<T, PASS, mt, ntw>(a, g, gamma, gnum, gden, dl, start, L);
+    if (MT == mt && NTW == ntw) return launch_bidir_bf16_t<T, PASS, mt, ntw>(a, g, gamma, gnum, gden, dl, start, L);
     GMA_BWD_MF(1, 1) GMA_BWD_MF(1, 2) GMA_BWD_MF(1, 3)
     GMA_BWD_MF(2, 1) GMA_BWD_MF(2, 2) GMA_BWD_MF(2, 3)
     GMA_BWD_MF(4, 1) GMA_BWD_MF(4, 2) GMA_BWD_MF(4, 3)
@@ -2053,12 +2174,6 @@ hipError_t launch_bidir_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, c
 // row-major as bf16 (row strides padded by 32 bytes) and read as MFMA fragments with the
 // transposed LDS reads; the next block's values are loaded into registers while the current
 // block's products run.
-
-// Two fp32 values as their bf16 hi and lo pairs (element 0 in the low half).
-__device__ __forceinline__ void split_pair(float v0, float v1, uint32_t& hi, uint32_t& lo) {
-    hi = mf::pack_bf16(v0, v1);
-    lo = mf::pack_bf16(v0 - mf::bf16lo_to_f32(hi), v1 - mf::bf16hi_to_f32(hi));
-}
 
 // Segment partials: part[bs] = G^T U over the segment's rows (K x W),
 // G the weighting side's gamma rows (K columns), U = [v | 1] (pass 1: bf16 values, exact) or

@@ -68,6 +68,9 @@ SMALL = [
     (512, 128, 64, 64, True), (1000, 33, 100, 128, False),
     # ragged within the padded tiles on the matrix-core path (dims multiples of 8)
     (1000, 33, 104, 72, False), (777, 200, 24, 40, True),
+    # small tiles (K <= 64, d <= 64): the write at two workgroups per CU over 8 splits, a
+    # ragged last split, then the split reduce
+    (1000, 40, 48, 56, False),
 ]
 
 
