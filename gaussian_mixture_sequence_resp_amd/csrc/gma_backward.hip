@@ -417,6 +417,16 @@ __device__ __forceinline__ void split_pair(float v0, float v1, uint32_t& hi, uin
     lo = mf::pack_bf16(v0 - mf::bf16lo_to_f32(hi), v1 - mf::bf16hi_to_f32(hi));
 }
 
+// Two fp32 values as three bf16 pieces each, v = p1 + p2 + p3 exactly (8 + 8 + 8 significant
+// bits; every residual is exact in fp32): for sums whose terms cancel (the parameter
+// gradients, the states the chunk walks start from), where two pieces (~2^-17) lost accuracy.
+__device__ __forceinline__ void split3_pair(float v0, float v1, uint32_t& p1, uint32_t& p2, uint32_t& p3) {
+    p1 = mf::pack_bf16(v0, v1);
+    const float r0 = v0 - mf::bf16lo_to_f32(p1), r1 = v1 - mf::bf16hi_to_f32(p1);
+    p2 = mf::pack_bf16(r0, r1);
+    p3 = mf::pack_bf16(r0 - mf::bf16lo_to_f32(p2), r1 - mf::bf16hi_to_f32(p2));
+}
+
 // Causal rows in chunks of kCh positions (the chunked form of the walk, as the forward's
 // scan): with St the state before the chunk (pass 1: the prefix before it; pass 2: the
 // suffix after it), rows r of the chunk and the chunk's own rows j on the inclusive side
@@ -1866,13 +1876,15 @@ hipError_t launch_causal_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, 
     return hipErrorInvalidValue;
 }
 
-// Bidirectional rows on bf16 matrix cores (v_mfma_f32_32x32x16_bf16) with exact hi/lo
-// splits of the fp32 operands (products hi.hi + lo.hi + hi.lo).  Each wave takes 32 rows at
+// Bidirectional rows on bf16 matrix cores (v_mfma_f32_32x32x16_bf16) with the fp32 operands
+// in three exact bf16 pieces (split3_pair; the six products of order <= 2, or three against
+// an operand exact in bf16: the dl epilogue differences dgamma and its row sum, so the
+// products are kept to fp32 accuracy).  Each wave takes 32 rows at
 // a time.  With G the rows' own gamma (32 x K) and St the head's total (K x W, W = d_v + 1):
 // C1 = St^T G^T (W x 32) is pass 1's [num | den - eps] of every row, pass 2's [dv | .]; the
 // per-row epilogue turns C1 into w (pass 1 [g_num | g_den], pass 2 [v | 1]); C2 = St w^T
 // (K x 32) is dgamma of every row; then dl = gamma (dgamma - gamma . dgamma).  St is staged
-// once per workgroup as bf16 hi and lo rows [Kp][Wp] (row stride 2 Wp + 16 bytes);
+// once per workgroup as three bf16 piece rows [Kp][Wp] (row stride 2 Wp + 16 bytes);
 //   C1 = St^T G^T: A = St^T (lane: column c, 8 consecutive k: transposed LDS reads of St),
 //                  B = G^T (lane: its row's gamma at 8 consecutive k, loaded from the row and
 //                  split in registers);
@@ -1887,8 +1899,9 @@ __global__ void __launch_bounds__(kMfRowThreads, 2)
                    const float* __restrict__ start, int BH, int N, int K, int dv, float eps, int SEG, int RB) {
     extern __shared__ double smem_d[];
     constexpr int Kp = 32 * MT, Wp = 32 * NTW, SB = 2 * Wp + 16, KS = Kp / 16, CS = Wp / 16;
-    unsigned char* sSh = reinterpret_cast<unsigned char*>(smem_d);
-    unsigned char* sSl = sSh + (size_t)Kp * SB;
+    unsigned char* sS1 = reinterpret_cast<unsigned char*>(smem_d);
+    unsigned char* sS2 = sS1 + (size_t)Kp * SB;
+    unsigned char* sS3 = sS2 + (size_t)Kp * SB;
     const int W = dv + 1;
     const int NB = (N + RB - 1) / RB;
     const int bs = blockIdx.x, bh = bs / NB, blk = bs % NB;
@@ -1898,10 +1911,11 @@ __global__ void __launch_bounds__(kMfRowThreads, 2)
         const int k = e / (Wp / 2), c = 2 * (e % (Wp / 2));
         const float v0 = (k < K && c < W) ? st0[(size_t)k * W + c] : 0.0f;
         const float v1 = (k < K && c + 1 < W) ? st0[(size_t)k * W + c + 1] : 0.0f;
-        uint32_t hi, lo;
-        split_pair(v0, v1, hi, lo);
-        *reinterpret_cast<uint32_t*>(sSh + (size_t)k * SB + 2 * c) = hi;
-        *reinterpret_cast<uint32_t*>(sSl + (size_t)k * SB + 2 * c) = lo;
+        uint32_t a, b, d;
+        split3_pair(v0, v1, a, b, d);
+        *reinterpret_cast<uint32_t*>(sS1 + (size_t)k * SB + 2 * c) = a;
+        *reinterpret_cast<uint32_t*>(sS2 + (size_t)k * SB + 2 * c) = b;
+        *reinterpret_cast<uint32_t*>(sS3 + (size_t)k * SB + 2 * c) = d;
     }
     __syncthreads();
     const size_t side = PASS == 1 ? 0 : (size_t)BH;
@@ -1938,22 +1952,28 @@ __global__ void __launch_bounds__(kMfRowThreads, 2)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) x[j] = k0 + j < K ? grow[k0 + j] : 0.0f;
             }
-            mf::u32x4 bh_, bl_;
+            mf::u32x4 q1, q2, q3;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                uint32_t hi, lo;
-                split_pair(x[2 * j], x[2 * j + 1], hi, lo);
-                bh_[j] = hi;
-                bl_[j] = lo;
+                uint32_t a, b, d;
+                split3_pair(x[2 * j], x[2 * j + 1], a, b, d);
+                q1[j] = a;
+                q2[j] = b;
+                q3[j] = d;
             }
-            const mf::bf16x8 gbh = __builtin_bit_cast(mf::bf16x8, bh_), gbl = __builtin_bit_cast(mf::bf16x8, bl_);
+            const mf::bf16x8 g1 = __builtin_bit_cast(mf::bf16x8, q1), g2 = __builtin_bit_cast(mf::bf16x8, q2),
+                             g3 = __builtin_bit_cast(mf::bf16x8, q3);
 #pragma unroll
             for (int n = 0; n < NTW; ++n) {
-                const mf::bf16x8 ah = mf::lds_frag_tr(sSh, SB, 16 * ks, 32 * n);
-                const mf::bf16x8 al = mf::lds_frag_tr(sSl, SB, 16 * ks, 32 * n);
-                c1[n] = mf::mfma(ah, gbh, c1[n]);
-                c1[n] = mf::mfma(al, gbh, c1[n]);
-                c1[n] = mf::mfma(ah, gbl, c1[n]);
+                const mf::bf16x8 a1 = mf::lds_frag_tr(sS1, SB, 16 * ks, 32 * n);
+                const mf::bf16x8 a2 = mf::lds_frag_tr(sS2, SB, 16 * ks, 32 * n);
+                const mf::bf16x8 a3 = mf::lds_frag_tr(sS3, SB, 16 * ks, 32 * n);
+                c1[n] = mf::mfma(a3, g1, c1[n]);
+                c1[n] = mf::mfma(a2, g2, c1[n]);
+                c1[n] = mf::mfma(a1, g3, c1[n]);
+                c1[n] = mf::mfma(a2, g1, c1[n]);
+                c1[n] = mf::mfma(a1, g2, c1[n]);
+                c1[n] = mf::mfma(a1, g1, c1[n]);
             }
         }
         // epilogue: C1 register group q of tile n holds columns c0 = 32 n + 8 q + 4 h .. c0 + 3;
@@ -2064,26 +2084,39 @@ __global__ void __launch_bounds__(kMfRowThreads, 2)
 #pragma unroll
         for (int cs = 0; cs < CS; ++cs) {
             const int n = cs >> 1, i0 = 8 * (cs & 1);
-            uint32_t ph[4], pl[4];
+            // pass 1: w = [g_num | g_den] in three pieces; pass 2: w = [v | 1], exact in bf16
+            uint32_t p1[4], p2[4], p3[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) split_pair(c1[n][i0 + 2 * j], c1[n][i0 + 2 * j + 1], ph[j], pl[j]);
-            // ph[0], ph[1]: columns +0..3 of this half's first group; ph[2], ph[3]: of its second
-            auto hx = __builtin_amdgcn_permlane32_swap(ph[0], ph[2], false, false);
-            auto hy = __builtin_amdgcn_permlane32_swap(ph[1], ph[3], false, false);
-            auto lx = __builtin_amdgcn_permlane32_swap(pl[0], pl[2], false, false);
-            auto ly = __builtin_amdgcn_permlane32_swap(pl[1], pl[3], false, false);
-            mf::u32x4 wh_, wl_;
-            wh_[0] = hx[0]; wh_[1] = hy[0]; wh_[2] = hx[1]; wh_[3] = hy[1];
-            wl_[0] = lx[0]; wl_[1] = ly[0]; wl_[2] = lx[1]; wl_[3] = ly[1];
-            const mf::bf16x8 wbh = __builtin_bit_cast(mf::bf16x8, wh_), wbl = __builtin_bit_cast(mf::bf16x8, wl_);
+            for (int j = 0; j < 4; ++j) split3_pair(c1[n][i0 + 2 * j], c1[n][i0 + 2 * j + 1], p1[j], p2[j], p3[j]);
+            // p[0], p[1]: columns +0..3 of this half's first group; p[2], p[3]: of its second
+            auto regroup = [](const uint32_t (&p)[4]) {
+                auto x = __builtin_amdgcn_permlane32_swap(p[0], p[2], false, false);
+                auto y = __builtin_amdgcn_permlane32_swap(p[1], p[3], false, false);
+                mf::u32x4 r;
+                r[0] = x[0]; r[1] = y[0]; r[2] = x[1]; r[3] = y[1];
+                return __builtin_bit_cast(mf::bf16x8, r);
+            };
+            const mf::bf16x8 w1 = regroup(p1);
+            const mf::bf16x8 w2 = PASS == 1 ? regroup(p2) : w1;
+            const mf::bf16x8 w3 = PASS == 1 ? regroup(p3) : w1;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const size_t off = (size_t)(32 * m + col) * SB + 2 * (16 * cs + 8 * half);
-                const mf::bf16x8 ah = *reinterpret_cast<const mf::bf16x8*>(sSh + off);
-                const mf::bf16x8 al = *reinterpret_cast<const mf::bf16x8*>(sSl + off);
-                c2[m] = mf::mfma(ah, wbh, c2[m]);
-                c2[m] = mf::mfma(al, wbh, c2[m]);
-                c2[m] = mf::mfma(ah, wbl, c2[m]);
+                const mf::bf16x8 a1 = *reinterpret_cast<const mf::bf16x8*>(sS1 + off);
+                const mf::bf16x8 a2 = *reinterpret_cast<const mf::bf16x8*>(sS2 + off);
+                const mf::bf16x8 a3 = *reinterpret_cast<const mf::bf16x8*>(sS3 + off);
+                if (PASS == 1) {
+                    c2[m] = mf::mfma(a3, w1, c2[m]);
+                    c2[m] = mf::mfma(a2, w2, c2[m]);
+                    c2[m] = mf::mfma(a1, w3, c2[m]);
+                    c2[m] = mf::mfma(a2, w1, c2[m]);
+                    c2[m] = mf::mfma(a1, w2, c2[m]);
+                    c2[m] = mf::mfma(a1, w1, c2[m]);
+                } else {
+                    c2[m] = mf::mfma(a3, w1, c2[m]);
+                    c2[m] = mf::mfma(a2, w1, c2[m]);
+                    c2[m] = mf::mfma(a1, w1, c2[m]);
+                }
             }
         }
         // gamma of this lane's row at its C-layout indices (zero past K), for dl
@@ -2141,7 +2174,7 @@ hipError_t launch_bidir_bf16_t(const Args& a, const BwdArgs& g, const float* gam
                                float* dl, const float* start, const BwdLayout& L) {
     const gma_desc& d = a.d;
     const int BH = d.B * d.H;
-    const size_t lds = (size_t)2 * (32 * MT) * (2 * 32 * NTW + 16);
+    const size_t lds = (size_t)3 * (32 * MT) * (2 * 32 * NTW + 16);
     hipError_t e;
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_bidir_bf16<T, PASS, MT, NTW>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
@@ -2167,17 +2200,19 @@ hipError_t launch_bidir_mfma(const Args& a, const BwdArgs& g, int MT, int NTW, c
 }
 
 // ---- split-bf16 row contractions (bf16 inputs).  A sum over rows of G[r][k] U[r][c] with
-// fp32 G and U runs on v_mfma_f32_32x32x16_bf16: every fp32 value is staged as the bf16 pair
-// hi = rne(v), lo = rne(v - hi) (v to ~2^-17 relative), and a product as
-// hi.hi + lo.hi + hi.lo (the dropped lo.lo is ~2^-16 of it); an operand that is bf16 already
-// (the value rows, the routing rows) has no lo part.  Blocks of 32 rows are staged in LDS
+// fp32 G and U runs on v_mfma_f32_32x32x16_bf16: every fp32 value is staged as three bf16
+// pieces p1 + p2 + p3 that add up to it exactly (split3_pair), and a product as the six
+// piece products of order <= 2 (p1q1, p2q1, p1q2, p3q1, p2q2, p1q3: the dropped ones are
+// below 2^-24 of it); an operand that is bf16 already (the value rows, the routing rows) is
+// one piece, and its products with the three pieces of the other are exact.  Blocks of 32 rows are staged in LDS
 // row-major as bf16 (row strides padded by 32 bytes) and read as MFMA fragments with the
 // transposed LDS reads; the next block's values are loaded into registers while the current
 // block's products run.
 
 // Segment partials: part[bs] = G^T U over the segment's rows (K x W),
-// G the weighting side's gamma rows (K columns), U = [v | 1] (pass 1: bf16 values, exact) or
-// [g_num | g_den] (pass 2: fp32, split).  The MT x NTW output tiles are dealt over the 4 waves.
+// G the weighting side's gamma rows (K columns, three pieces), U = [v | 1] (pass 1: bf16
+// values, exact: three products) or [g_num | g_den] (pass 2: fp32, three pieces: six
+// products).  The MT x NTW output tiles are dealt over the 4 waves.
 // Staging in groups of 4 columns per thread; VEC (K and d_v multiples of 4): one 16-byte load
 // of gamma / g_num or one 8-byte load of v per group.  Grid (BH * SEG).
 template <typename T, int PASS, int MT, int NTW, bool VEC>
@@ -2189,14 +2224,16 @@ __global__ void __launch_bounds__(kMfRowThreads)
     extern __shared__ double smem_d[];
     constexpr int GC = 32 * MT, UC = 32 * NTW;       // staged columns
     constexpr int GB = 2 * GC + 32, UB = 2 * UC + 32;  // row strides, bytes
-    constexpr bool ULO = PASS == 2;                    // U needs a lo part
+    constexpr bool USPLIT = PASS == 2;                 // U in three pieces
     constexpr int NG = 32 * (GC / 4) / kMfRowThreads;  // column groups per thread and block
     constexpr int NU = 32 * (UC / 4) / kMfRowThreads;
     constexpr int kTiles = MT * NTW, kWaves = kMfRowThreads / 64, TPW = (kTiles + kWaves - 1) / kWaves;
-    unsigned char* sGh = reinterpret_cast<unsigned char*>(smem_d);
-    unsigned char* sGl = sGh + 32 * GB;
-    unsigned char* sUh = sGl + 32 * GB;
-    unsigned char* sUl = sUh + 32 * UB;
+    unsigned char* sG1 = reinterpret_cast<unsigned char*>(smem_d);
+    unsigned char* sG2 = sG1 + 32 * GB;
+    unsigned char* sG3 = sG2 + 32 * GB;
+    unsigned char* sU1 = sG3 + 32 * GB;
+    unsigned char* sU2 = sU1 + 32 * UB;
+    unsigned char* sU3 = sU2 + 32 * UB;
     const int W = dv + 1;
     const int bs = blockIdx.x, bh = bs / SEG, seg = bs % SEG;
     const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
@@ -2260,23 +2297,25 @@ __global__ void __launch_bounds__(kMfRowThreads)
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int e = t + kMfRowThreads * i, r = e / (GC / 4), c = 4 * (e % (GC / 4));
-            uint2 hi, lo;
-            split_pair(gv[i].x, gv[i].y, hi.x, lo.x);
-            split_pair(gv[i].z, gv[i].w, hi.y, lo.y);
-            *reinterpret_cast<uint2*>(sGh + r * GB + 2 * c) = hi;
-            *reinterpret_cast<uint2*>(sGl + r * GB + 2 * c) = lo;
+            uint2 a, b, d;
+            split3_pair(gv[i].x, gv[i].y, a.x, b.x, d.x);
+            split3_pair(gv[i].z, gv[i].w, a.y, b.y, d.y);
+            *reinterpret_cast<uint2*>(sG1 + r * GB + 2 * c) = a;
+            *reinterpret_cast<uint2*>(sG2 + r * GB + 2 * c) = b;
+            *reinterpret_cast<uint2*>(sG3 + r * GB + 2 * c) = d;
         }
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
             const int e = t + kMfRowThreads * i, r = e / (UC / 4), c = 4 * (e % (UC / 4));
             if constexpr (PASS == 1) {
-                *reinterpret_cast<uint2*>(sUh + r * UB + 2 * c) = ub[i];
+                *reinterpret_cast<uint2*>(sU1 + r * UB + 2 * c) = ub[i];
             } else {
-                uint2 hi, lo;
-                split_pair(uf[i].x, uf[i].y, hi.x, lo.x);
-                split_pair(uf[i].z, uf[i].w, hi.y, lo.y);
-                *reinterpret_cast<uint2*>(sUh + r * UB + 2 * c) = hi;
-                *reinterpret_cast<uint2*>(sUl + r * UB + 2 * c) = lo;
+                uint2 a, b, d;
+                split3_pair(uf[i].x, uf[i].y, a.x, b.x, d.x);
+                split3_pair(uf[i].z, uf[i].w, a.y, b.y, d.y);
+                *reinterpret_cast<uint2*>(sU1 + r * UB + 2 * c) = a;
+                *reinterpret_cast<uint2*>(sU2 + r * UB + 2 * c) = b;
+                *reinterpret_cast<uint2*>(sU3 + r * UB + 2 * c) = d;
             }
         }
     };
@@ -2297,12 +2336,24 @@ __global__ void __launch_bounds__(kMfRowThreads)
                 const int m = tau / NTW, n = tau % NTW;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const mf::bf16x8 ah = mf::lds_frag_tr(sGh, GB, 16 * ks, 32 * m);
-                    const mf::bf16x8 al = mf::lds_frag_tr(sGl, GB, 16 * ks, 32 * m);
-                    const mf::bf16x8 bh = mf::lds_frag_tr(sUh, UB, 16 * ks, 32 * n);
-                    acc[u] = mf::mfma(ah, bh, acc[u]);
-                    acc[u] = mf::mfma(al, bh, acc[u]);
-                    if (ULO) acc[u] = mf::mfma(ah, mf::lds_frag_tr(sUl, UB, 16 * ks, 32 * n), acc[u]);
+                    const mf::bf16x8 a1 = mf::lds_frag_tr(sG1, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 a2 = mf::lds_frag_tr(sG2, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 a3 = mf::lds_frag_tr(sG3, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 b1 = mf::lds_frag_tr(sU1, UB, 16 * ks, 32 * n);
+                    if (USPLIT) {
+                        const mf::bf16x8 b2 = mf::lds_frag_tr(sU2, UB, 16 * ks, 32 * n);
+                        const mf::bf16x8 b3 = mf::lds_frag_tr(sU3, UB, 16 * ks, 32 * n);
+                        acc[u] = mf::mfma(a3, b1, acc[u]);
+                        acc[u] = mf::mfma(a2, b2, acc[u]);
+                        acc[u] = mf::mfma(a1, b3, acc[u]);
+                        acc[u] = mf::mfma(a2, b1, acc[u]);
+                        acc[u] = mf::mfma(a1, b2, acc[u]);
+                        acc[u] = mf::mfma(a1, b1, acc[u]);
+                    } else {
+                        acc[u] = mf::mfma(a3, b1, acc[u]);
+                        acc[u] = mf::mfma(a2, b1, acc[u]);
+                        acc[u] = mf::mfma(a1, b1, acc[u]);
+                    }
                 }
             }
         }
@@ -2325,7 +2376,7 @@ __global__ void __launch_bounds__(kMfRowThreads)
 
 template <int MT, int NTW>
 constexpr size_t partial_bf16_lds() {
-    return (size_t)32 * (2 * (64 * MT + 32) + 2 * (64 * NTW + 32));
+    return (size_t)32 * (3 * (64 * MT + 32) + 3 * (64 * NTW + 32));
 }
 
 template <typename T, int PASS, int MT, int NTW>
@@ -2454,8 +2505,10 @@ hipError_t bwd_pass(const Args& a, const BwdArgs& g, const BwdLayout& L, A* gamm
 
 // Parameter-gradient sums on bf16 matrix cores (bf16 inputs, float dl; the split-bf16 form
 // of the row contractions above): for chunk c of head h, S1 = dl^T x, S2 = dl^T x^2 and
-// S0 = dl^T 1 over the chunk's rows (both sides, all b), dl split into hi/lo, x exact in
-// bf16, x^2 split exactly into hi/lo (x^2 of a bf16 value has at most 16 significant bits).
+// S0 = dl^T 1 over the chunk's rows (both sides, all b), dl in three exact pieces, x exact
+// in bf16 (S1, S0: exact products), x^2 split exactly into hi/lo (x^2 of a bf16 value has at
+// most 16 significant bits; S2: the five products of order <= 2).  The final gradients
+// difference these sums (dmu = lam (S1 - mu S0), ...), so they are kept to fp32 accuracy.
 // The MT x NTD tiles of S1 and S2 are dealt over the 4 waves; the wave of tile (m, 0) also
 // forms S0 of component tile m against a ones operand.  Staging in groups of 4 columns; VEC
 // (K and d_r multiples of 4): one 16-byte load of dl and one 8-byte load of x per group.
@@ -2471,9 +2524,10 @@ __global__ void __launch_bounds__(kMfRowThreads, 2)
     constexpr int GB = 2 * GC + 32, XB = 2 * XC + 32;
     constexpr int NG = 32 * (GC / 4) / kMfRowThreads, NX = (32 * (XC / 4) + kMfRowThreads - 1) / kMfRowThreads;
     constexpr int kTiles = MT * NTD, kWaves = kMfRowThreads / 64, TPW = (kTiles + kWaves - 1) / kWaves;
-    unsigned char* sGh = reinterpret_cast<unsigned char*>(smem_d);
-    unsigned char* sGl = sGh + 32 * GB;
-    unsigned char* sX = sGl + 32 * GB;
+    unsigned char* sG1 = reinterpret_cast<unsigned char*>(smem_d);
+    unsigned char* sG2 = sG1 + 32 * GB;
+    unsigned char* sG3 = sG2 + 32 * GB;
+    unsigned char* sX = sG3 + 32 * GB;
     unsigned char* sX2h = sX + 32 * XB;
     unsigned char* sX2l = sX2h + 32 * XB;
     const int t = threadIdx.x, l = t & 63, wv = t >> 6, col = l & 31, half = l >> 5;
@@ -2530,11 +2584,12 @@ __global__ void __launch_bounds__(kMfRowThreads, 2)
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const int e = t + kMfRowThreads * i, r = e / (GC / 4), k = 4 * (e % (GC / 4));
-            uint2 hi, lo;
-            split_pair(gv[i].x, gv[i].y, hi.x, lo.x);
-            split_pair(gv[i].z, gv[i].w, hi.y, lo.y);
-            *reinterpret_cast<uint2*>(sGh + r * GB + 2 * k) = hi;
-            *reinterpret_cast<uint2*>(sGl + r * GB + 2 * k) = lo;
+            uint2 a, b, d;
+            split3_pair(gv[i].x, gv[i].y, a.x, b.x, d.x);
+            split3_pair(gv[i].z, gv[i].w, a.y, b.y, d.y);
+            *reinterpret_cast<uint2*>(sG1 + r * GB + 2 * k) = a;
+            *reinterpret_cast<uint2*>(sG2 + r * GB + 2 * k) = b;
+            *reinterpret_cast<uint2*>(sG3 + r * GB + 2 * k) = d;
         }
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
@@ -2571,19 +2626,24 @@ __global__ void __launch_bounds__(kMfRowThreads, 2)
                 const int m = tau / NTD, n = tau % NTD;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const mf::bf16x8 ah = mf::lds_frag_tr(sGh, GB, 16 * ks, 32 * m);
-                    const mf::bf16x8 al = mf::lds_frag_tr(sGl, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 g1 = mf::lds_frag_tr(sG1, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 g2 = mf::lds_frag_tr(sG2, GB, 16 * ks, 32 * m);
+                    const mf::bf16x8 g3 = mf::lds_frag_tr(sG3, GB, 16 * ks, 32 * m);
                     const mf::bf16x8 bx = mf::lds_frag_tr(sX, XB, 16 * ks, 32 * n);
                     const mf::bf16x8 b2h = mf::lds_frag_tr(sX2h, XB, 16 * ks, 32 * n);
                     const mf::bf16x8 b2l = mf::lds_frag_tr(sX2l, XB, 16 * ks, 32 * n);
-                    a1[u] = mf::mfma(ah, bx, a1[u]);
-                    a1[u] = mf::mfma(al, bx, a1[u]);
-                    a2[u] = mf::mfma(ah, b2h, a2[u]);
-                    a2[u] = mf::mfma(al, b2h, a2[u]);
-                    a2[u] = mf::mfma(ah, b2l, a2[u]);
+                    a1[u] = mf::mfma(g3, bx, a1[u]);
+                    a1[u] = mf::mfma(g2, bx, a1[u]);
+                    a1[u] = mf::mfma(g1, bx, a1[u]);
+                    a2[u] = mf::mfma(g3, b2h, a2[u]);
+                    a2[u] = mf::mfma(g2, b2l, a2[u]);
+                    a2[u] = mf::mfma(g2, b2h, a2[u]);
+                    a2[u] = mf::mfma(g1, b2l, a2[u]);
+                    a2[u] = mf::mfma(g1, b2h, a2[u]);
                     if (n == 0) {
-                        a0[u] = mf::mfma(ah, ones, a0[u]);
-                        a0[u] = mf::mfma(al, ones, a0[u]);
+                        a0[u] = mf::mfma(g3, ones, a0[u]);
+                        a0[u] = mf::mfma(g2, ones, a0[u]);
+                        a0[u] = mf::mfma(g1, ones, a0[u]);
                     }
                 }
             }
@@ -2613,7 +2673,7 @@ template <typename T, int MT, int NTD>
 hipError_t launch_param_bf16_t(const Args& a, const BwdLayout& L, const float* dl, double* pmu, double* pvar,
                                double* ppi) {
     const gma_desc& d = a.d;
-    const size_t lds = (size_t)32 * (2 * (64 * MT + 32) + 3 * (64 * NTD + 32));
+    const size_t lds = (size_t)32 * (3 * (64 * MT + 32) + 3 * (64 * NTD + 32));
     const bool vec = d.K % 4 == 0 && d.d_r % 4 == 0;
     auto fn = vec ? &bwd_param_bf16<T, MT, NTD, true> : &bwd_param_bf16<T, MT, NTD, false>;
     hipError_t e;
