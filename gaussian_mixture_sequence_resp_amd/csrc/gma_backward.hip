@@ -68,7 +68,7 @@ namespace {
 
 constexpr int kBwdThreads = 256;
 constexpr size_t kScanLdsMax = 150 * 1024;  // dynamic LDS cap of the row, chunk and dx kernels
-constexpr int kParamChunks = 64;
+constexpr int kParamChunks = 64;  // most chunks of rows of the parameter sums
 
 // Sums over rows are split into SEG contiguous segments of L rows per head.  The state of a
 // pass is [K][W] (W = d_v + 1), kept in A: double for float32 inputs (gamma included: the
@@ -1727,18 +1727,28 @@ __global__ void __launch_bounds__(kBwdThreads)
         sdp[k] = a;
     }
     __syncthreads();
-    if (t == 0) {
-        // prior softmax: max, sum of exponentials, and the total of dlog pi, in order
-        double m = prior[(size_t)h * K];
-        for (int k = 1; k < K; ++k) m = fmax(m, (double)prior[(size_t)h * K + k]);
+    if (t < 64) {
+        // prior softmax: max, sum of exponentials, and the total of dlog pi, by the first wave
+        // (lanes strided over k, then a fixed butterfly order: deterministic)
+        double m = -INFINITY;
+        for (int k = t; k < K; k += 64) m = fmax(m, (double)prior[(size_t)h * K + k]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
         double se = 0.0, tot = 0.0;
-        for (int k = 0; k < K; ++k) {
+        for (int k = t; k < K; k += 64) {
             se += exp((double)prior[(size_t)h * K + k] - m);
             tot += sdp[k];
         }
-        sred[0] = m;
-        sred[1] = se;
-        sred[2] = tot;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            se += __shfl_xor(se, o, 64);
+            tot += __shfl_xor(tot, o, 64);
+        }
+        if (t == 0) {
+            sred[0] = m;
+            sred[1] = se;
+            sred[2] = tot;
+        }
     }
     __syncthreads();
     for (int k = t; k < K; k += kBwdThreads) {
@@ -1809,7 +1819,13 @@ BwdLayout bwd_layout(const gma_desc& d) {
     L.state = off;
     if (!state_in_lds(d)) off += align_up(segs);
     const int rows = 2 * d.B * d.N;
-    L.chunks = rows > 0 ? (rows < kParamChunks ? rows : kParamChunks) : 0;
+    // chunks of rows for the parameter sums: about 512 workgroups of the matrix-core sums
+    // (H chunks ceil(K / 128) of them), 16 to 64 chunks (each chunk's sums are read once more
+    // by bwd_param_final: fewer chunks, less traffic there)
+    const int kzs = (d.K + 127) / 128;
+    int nch = 512 / (d.H * kzs > 0 ? d.H * kzs : 1);
+    nch = nch < 16 ? 16 : (nch > kParamChunks ? kParamChunks : nch);
+    L.chunks = rows > 0 ? (rows < nch ? rows : nch) : 0;
     L.per_chunk = L.chunks ? (rows + L.chunks - 1) / L.chunks : 0;
     const size_t nc = L.chunks ? L.chunks : 1;
     L.pmu = off;

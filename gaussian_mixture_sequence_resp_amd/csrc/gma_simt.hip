@@ -26,47 +26,46 @@ namespace {
 
 constexpr int kBlock = 256;
 
-// One block per head: lam[h,k,d] = 1/var, cst[h,k] = log pi_k - 1/2 sum_d log var_kd.
-// Computed and stored in double.
-__global__ void __launch_bounds__(kBlock) params_kernel(const float* __restrict__ mu,
-                                                        const float* __restrict__ var_raw,
-                                                        const float* __restrict__ prior, int K,
-                                                        int dr, float var_floor,
-                                                        double* __restrict__ lam,
-                                                        double* __restrict__ cst) {
-    (void)mu;
-    const int h = blockIdx.x;
-    __shared__ double red[kBlock];
-    // log-sum-exp of the prior logits of this head (softmax priors)
-    double pmax = -INFINITY;
-    for (int k = threadIdx.x; k < K; k += kBlock) pmax = fmax(pmax, (double)prior[(size_t)h * K + k]);
-    red[threadIdx.x] = pmax;
-    __syncthreads();
-    for (int s = kBlock / 2; s > 0; s >>= 1) {
-        if (threadIdx.x < s) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + s]);
-        __syncthreads();
-    }
-    pmax = red[0];
-    __syncthreads();
-    double psum = 0.0;
-    for (int k = threadIdx.x; k < K; k += kBlock) psum += exp((double)prior[(size_t)h * K + k] - pmax);
-    red[threadIdx.x] = psum;
-    __syncthreads();
-    for (int s = kBlock / 2; s > 0; s >>= 1) {
-        if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-        __syncthreads();
-    }
-    const double lse = pmax + log(red[0]);
-    for (int k = threadIdx.x; k < K; k += kBlock) {
+// One wave per (h, k): lam[h,k,d] = 1/var, cst[h,k] = log pi_k - 1/2 sum_d log var_kd, in
+// double; lanes over the routing dims (and over the head's K prior logits for its log-sum-
+// exp), the sums over the wave in a fixed butterfly order (deterministic).  Blocks stride
+// over the H K pairs (grid min(H K, 2^20)).
+__device__ __forceinline__ double wave_max_d(double x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+__global__ void __launch_bounds__(64) params_kernel(const float* __restrict__ var_raw,
+                                                    const float* __restrict__ prior, int H, int K, int dr,
+                                                    float var_floor, double* __restrict__ lam,
+                                                    double* __restrict__ cst) {
+    const int lane = threadIdx.x;
+    for (int64_t p = blockIdx.x; p < (int64_t)H * K; p += gridDim.x) {
+        const int64_t h = p / K;
+        const int k = (int)(p % K);
+        const float* ph = prior + h * K;
+        // log-sum-exp of the prior logits of this head (softmax priors)
+        double pmax = -INFINITY;
+        for (int j = lane; j < K; j += 64) pmax = fmax(pmax, (double)ph[j]);
+        pmax = wave_max_d(pmax);
+        double psum = 0.0;
+        for (int j = lane; j < K; j += 64) psum += exp((double)ph[j] - pmax);
+        const double lse = pmax + log(wave_sum_d(psum));
         double half_logdet = 0.0;
-        for (int d = 0; d < dr; ++d) {
-            const size_t i = ((size_t)h * K + k) * dr + d;
+        for (int d = lane; d < dr; d += 64) {
+            const size_t i = (size_t)p * dr + d;
             const double r = var_raw[i];
             const double var = fmax(r, 0.0) + log1p(exp(-fabs(r))) + (double)var_floor;
             lam[i] = 1.0 / var;
             half_logdet += 0.5 * log(var);
         }
-        cst[(size_t)h * K + k] = (double)prior[(size_t)h * K + k] - lse - half_logdet;
+        half_logdet = wave_sum_d(half_logdet);
+        if (lane == 0) cst[p] = (double)ph[k] - lse - half_logdet;
     }
 }
 
@@ -281,8 +280,14 @@ size_t simt_workspace(const gma_desc& d, int /*causal*/, int Nk) { return simt_l
 
 hipError_t simt_params(const Args& a, double* lam, double* cst) {
     rec_begin(a, "simt_params");
-    params_kernel<<<dim3(a.d.H), dim3(kBlock), 0, a.stream>>>(a.mu, a.var_raw, a.prior, a.d.K, a.d.d_r,
-                                                              a.d.var_floor, lam, cst);
+    const int64_t pairs = (int64_t)a.d.H * a.d.K;
+    if (pairs == 0) {
+        rec_end(a);
+        return hipSuccess;
+    }
+    const unsigned grid = (unsigned)(pairs < (1 << 20) ? pairs : (1 << 20));
+    params_kernel<<<dim3(grid), dim3(64), 0, a.stream>>>(a.var_raw, a.prior, a.d.H, a.d.K, a.d.d_r, a.d.var_floor,
+                                                          lam, cst);
     rec_end(a);
     return hipGetLastError();
 }
