@@ -349,6 +349,190 @@ __global__ void __launch_bounds__(64 * kRespWaves, 2)
     }
 }
 
+// Component-parallel responsibilities, for a coefficient block too large for LDS (256
+// components of 128 routing dims: 266 KB of split coefficients, which gma_causal_resp would
+// restage from L2 in phases at every step).  Each of the eight waves owns 32 components and
+// keeps their split coefficients in registers for the whole launch; the workgroup walks its
+// positions in steps of kCpTiles 32-position tiles.  Per step the raw routing rows are split
+// once by the whole workgroup (x and the exact x^2 = x2h + x2l) into an LDS buffer (two
+// buffers: the next step's rows are loaded while the current step's products run and split
+// after them), and every wave forms its components' logits of all tiles of the step (the
+// same five products per 16-dim chunk as gma_causal_resp).  The softmax over all components is
+// assembled from per-wave statistics: each wave's per-position maximum m_w over its components
+// and the sum s_w of 2^(logit - m_w) go through LDS, and after one barrier each wave scales its
+// exponentials by 2^(m_w - M) / sum_w' s_w' 2^(m_w' - M), M the maximum over the waves.  The
+// output is the fragment layout of gma_causal_resp (wave w writes blocks 2w and 2w + 1), zero
+// past N.
+constexpr int kCpTiles = 2;
+template <int NC>
+struct CpLds {
+    static constexpr int Dp = 16 * NC;
+    static constexpr int xs = 2 * Dp + 16;                                  // bytes per staged row
+    static constexpr int piece = kTileT * kCpTiles * xs;                    // x, x2h or x2l of a step
+    static constexpr int buf = 3 * piece;
+    static constexpr int xch = 2 * kRespWaves * kTileT * kCpTiles * 8;    // two buffers of (m, s)
+    static constexpr size_t total = 2 * (size_t)buf + xch + 32 * kRespWaves * 4;
+};
+
+template <int NC>
+__global__ void __launch_bounds__(64 * kRespWaves, 1)
+    gma_causal_resp_cp(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ kr, const bf16_t* __restrict__ W,
+                       const float* __restrict__ cvec, bf16_t* __restrict__ GQ, bf16_t* __restrict__ GK,
+                       int* __restrict__ hard, int BH, int H, int N, int Np, int dr, int parts, int part_len, int K) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    using L = CpLds<NC>;
+    constexpr int Kp = 32 * kRespWaves, Dp = L::Dp, KS = Kp / 16;
+    constexpr int kStep = kTileT * kCpTiles;
+    constexpr int kNT = 64 * kRespWaves;
+    constexpr int VPR = Dp / 8;                // 16-byte vectors per staged row
+    constexpr int XV = kStep * VPR / kNT;      // raw vectors per thread per step
+    static_assert(XV >= 1 && kStep * VPR % kNT == 0, "step rows must split evenly over the threads");
+    unsigned char* sX = smem;
+    float2* sM = reinterpret_cast<float2*>(smem + 2 * L::buf);
+    float* sC = reinterpret_cast<float*>(smem + 2 * L::buf + L::xch);
+    int bh, part;
+    head_part(blockIdx.x, BH, parts, bh, part);
+    const int h = bh % H;
+    const int l = lane_id(), w = wave_id(), col = l & 31, half = l >> 5;
+    const int side = blockIdx.y;
+    const bf16_t* x = (side == 0 ? qr : kr) + (size_t)bh * N * dr;
+    bf16_t* G = (side == 0 ? GQ : GK) + (size_t)bh * Np * Kp + 8 * l;
+    const int n_begin = part * part_len;
+    const int n_end = min(Np, n_begin + part_len);
+    if (n_begin >= n_end) return;  // uniform over the workgroup
+
+    // this wave's coefficient fragments: component 32 w + col, dims 16 c + 8 half .. + 7
+    bf16x8 ca[NC], cal[NC], cb[NC], cbl[NC];
+    {
+        const bf16_t* wr = W + ((size_t)h * Kp + 32 * w + col) * 4 * Dp + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            ca[c] = *reinterpret_cast<const bf16x8*>(wr + 16 * c);
+            cal[c] = *reinterpret_cast<const bf16x8*>(wr + Dp + 16 * c);
+            cb[c] = *reinterpret_cast<const bf16x8*>(wr + 2 * Dp + 16 * c);
+            cbl[c] = *reinterpret_cast<const bf16x8*>(wr + 3 * Dp + 16 * c);
+        }
+    }
+    for (int i = threadIdx.x; i < Kp; i += kNT) sC[i] = cvec[(size_t)h * Kp + i];
+
+    // raw rows of a step: vector v = thread + kNT u is position v / VPR, dims 8 (v % VPR);
+    // positions past the sequence read its last row (their responsibilities are zeroed)
+    bf16x8 xraw[XV];
+    auto load_raw = [&](int b0) {
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int v = threadIdx.x + kNT * u;
+            const int t = min(b0 + v / VPR, N - 1), d0 = 8 * (v % VPR);
+            bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (d0 < dr) z = *reinterpret_cast<const bf16x8*>(x + (size_t)t * dr + d0);
+            xraw[u] = z;
+        }
+    };
+    auto store_split = [&](int b) {
+        unsigned char* base = sX + (size_t)b * L::buf;
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int v = threadIdx.x + kNT * u;
+            const int off = (v / VPR) * L::xs + 16 * (v % VPR);
+            XFrag f;
+            f.x1 = xraw[u];
+            split_square(f);
+            *reinterpret_cast<bf16x8*>(base + off) = f.x1;
+            *reinterpret_cast<bf16x8*>(base + L::piece + off) = f.x2h;
+            *reinterpret_cast<bf16x8*>(base + 2 * L::piece + off) = f.x2l;
+        }
+    };
+    load_raw(n_begin);
+    store_split(0);
+    __syncthreads();
+
+    int it = 0;
+    for (int b0 = n_begin; b0 < n_end; b0 += kStep, ++it) {
+        const int b = it & 1;
+        const bool more = b0 + kStep < n_end;
+        if (more) load_raw(b0 + kStep);
+        // register i of acc[j]: component 32 w + 8 (i / 4) + 4 half + i % 4, position 32 j + col
+        f32x16 acc[kCpTiles];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 cq = *reinterpret_cast<const float4*>(sC + 32 * w + 8 * q + 4 * half);
+#pragma unroll
+            for (int j = 0; j < kCpTiles; ++j) {
+                acc[j][4 * q] = cq.x;
+                acc[j][4 * q + 1] = cq.y;
+                acc[j][4 * q + 2] = cq.z;
+                acc[j][4 * q + 3] = cq.w;
+            }
+        }
+        const unsigned char* xb = sX + (size_t)b * L::buf + (size_t)col * L::xs + 16 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            bf16x8 p1[kCpTiles], p2h[kCpTiles], p2l[kCpTiles];
+#pragma unroll
+            for (int j = 0; j < kCpTiles; ++j) {
+                const unsigned char* pj = xb + (size_t)kTileT * j * L::xs + 32 * c;
+                p1[j] = *reinterpret_cast<const bf16x8*>(pj);
+                p2h[j] = *reinterpret_cast<const bf16x8*>(pj + L::piece);
+                p2l[j] = *reinterpret_cast<const bf16x8*>(pj + 2 * L::piece);
+            }
+#pragma unroll
+            for (int j = 0; j < kCpTiles; ++j) acc[j] = mfma(ca[c], p2h[j], acc[j]);
+#pragma unroll
+            for (int j = 0; j < kCpTiles; ++j) acc[j] = mfma(cb[c], p1[j], acc[j]);
+#pragma unroll
+            for (int j = 0; j < kCpTiles; ++j) acc[j] = mfma(cal[c], p2h[j], acc[j]);
+#pragma unroll
+            for (int j = 0; j < kCpTiles; ++j) acc[j] = mfma(cbl[c], p1[j], acc[j]);
+#pragma unroll
+            for (int j = 0; j < kCpTiles; ++j) acc[j] = mfma(ca[c], p2l[j], acc[j]);
+        }
+        // per-wave statistics of every position of the step
+        float mloc[kCpTiles];
+#pragma unroll
+        for (int j = 0; j < kCpTiles; ++j) {
+            float m0 = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, acc[j][i]);
+            // a wave whose components are all padding (logits -inf) keeps a finite maximum, so
+            // its exponentials and sum are 0 rather than 2^(-inf + inf)
+            m0 = fmaxf(max_halves(m0), -__FLT_MAX__);
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float e = fast_exp2(acc[j][i] - m0);
+                acc[j][i] = e;
+                s += e;
+            }
+            s = sum_halves(s);
+            mloc[j] = m0;
+            if (half == 0) sM[(b * kRespWaves + w) * kStep + kTileT * j + col] = make_float2(m0, s);
+        }
+        if (more) store_split(b ^ 1);  // the buffer read one step ago: every wave is past that
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < kCpTiles; ++j) {
+            const int t0 = b0 + kTileT * j;
+            float2 st[kRespWaves];
+            float M = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < kRespWaves; ++ww) {
+                st[ww] = sM[(b * kRespWaves + ww) * kStep + kTileT * j + col];
+                M = fmaxf(M, st[ww].x);
+            }
+            float S = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < kRespWaves; ++ww) S += st[ww].y * fast_exp2(st[ww].x - M);
+            // S >= 1 (the wave holding the maximum contributes at least 2^0)
+            const float inv = t0 + col < N ? fast_exp2(mloc[j] - M) * __builtin_amdgcn_rcpf(S) : 0.0f;
+            if (t0 < n_end) {
+                bf16_t* gt = G + (size_t)(t0 / kTileT) * KS * kFrag;
+                *reinterpret_cast<bf16x8*>(gt + (size_t)(2 * w) * kFrag) = pack8(acc[j], 0, inv);
+                *reinterpret_cast<bf16x8*>(gt + (size_t)(2 * w + 1) * kFrag) = pack8(acc[j], 8, inv);
+            }
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------- group staging
 // Register prefetch of one group: this thread's share of the Gamma_K fragments (the group's
 // four tiles are one contiguous block of 16 Kp 16-byte chunks; thread i takes chunks
@@ -742,9 +926,13 @@ RespFn select_resp_t(const Geo& g, int nph) {
     }
     return nullptr;
 }
+// Component-parallel form: eight 32-component tiles whose coefficients (in registers) would
+// otherwise be restaged in phases.
+bool resp_cp(const Geo& g, int nph, int mode) { return mode == kRespFrag && nph > 1 && g.MT == 8 && g.NC == 8; }
 RespFn select_resp(const Geo& g, int nph, int mode = kRespFrag) {
     if (mode == kRespStats) return select_resp_t<kRespStats>(g, nph);
     if (mode == kRespRows) return select_resp_t<kRespRows>(g, nph);
+    if (resp_cp(g, nph, mode)) return gma_causal_resp_cp<8>;
     return select_resp_t<kRespFrag>(g, nph);
 }
 // LDS of the responsibilities kernel with the routing dims staged in nph phases.
@@ -803,7 +991,8 @@ hipError_t launch_resp(const Args& a, const Geo& g, RespFn rf, int nph, int Np, 
     const int BH = d.B * d.H;
     int part_len = 0;
     const int parts = resp_parts(BH, Np, &part_len);
-    const size_t rl = resp_lds(g, nph);
+    const bool cp = rf == static_cast<RespFn>(gma_causal_resp_cp<8>);
+    const size_t rl = cp ? CpLds<8>::total : resp_lds(g, nph);
     hipError_t e;
     if ((e = set_lds(reinterpret_cast<const void*>(rf), rl)) != hipSuccess) return e;
     const bf16_t* kr = static_cast<const bf16_t*>(a.kr);

@@ -71,6 +71,9 @@ SMALL = [
     # small tiles (K <= 64, d <= 64): the write at two workgroups per CU over 8 splits, a
     # ragged last split, then the split reduce
     (1000, 40, 48, 56, False),
+    # 256 padded components of 128 padded routing dims, causal: the component-parallel
+    # responsibilities (one wave's 32 components all padding), four parts, a ragged tail
+    (1000, 200, 120, 64, True),
 ]
 
 
@@ -192,7 +195,7 @@ def test_causal_outputs_ignore_future_bitwise(cfg):
     assert not torch.equal(out1[:, :, cut + 1:], out2[:, :, cut + 1:])
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", [2, 3, 5])
 def test_deterministic_bitwise(cfg):
     w = WORKLOADS[cfg].with_(B=2, H=2, N=3000)
     inp = make_inputs(w)
