@@ -118,9 +118,13 @@ def traffic_from_profiles(kernel: str, workload: str):
     on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(p)).get(f"{workload}:{kernel}")
+        table = json.load(open(p))
     except Exception:
         return None
+    # a launch recorded under one name may run one of several kernel forms, which the
+    # profiler names apart (gma_causal_resp: gma_causal_resp or gma_causal_resp_cp)
+    forms = [k for k in table if k == f"{workload}:{kernel}" or k.startswith(f"{workload}:{kernel}_")]
+    rec = table[forms[0]] if len(forms) == 1 else None
     if not rec or rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
