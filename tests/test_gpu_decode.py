@@ -98,6 +98,25 @@ def test_memory_long_prefix(algo, K):
     np.testing.assert_allclose(state.cpu()[..., -1].sum(-1).numpy(), w.N, rtol=1e-4)
 
 
+@pytest.mark.parametrize("algo", ["auto", "mfma"])
+def test_memory_wide_routing(algo):
+    # 256 components of 128 routing dims: the prefill runs the component-parallel
+    # responsibilities on the key side only (one side per launch), then the totals kernels;
+    # a ragged prefix over several workgroup parts
+    w = WORKLOADS[3].with_(B=2, H=2, N=3000 + 45, K=256, d_r=128, d_v=64, seed=62)
+    inp = make_inputs(w)
+    _say("memory wide routing", algo, w)
+    d = {k: x.to(DEV) for k, x in inp.items()}
+    state = gma.memory(d["kr"], d["v"], d["mu"], d["var_raw"], d["prior_logits"], var_floor=w.var_floor,
+                       algo=algo)
+    torch.cuda.synchronize()
+    ref = oracle.memory(inp["kr"], inp["v"], inp["mu"], inp["var_raw"], inp["prior_logits"], w.var_floor)
+    err = metrics.rowrel(state.cpu(), ref)
+    _say("memory wide routing rowrel", err)
+    assert err <= metrics.tol_for(w.dtype)
+    np.testing.assert_allclose(state.cpu()[..., -1].sum(-1).numpy(), w.N, rtol=1e-4)
+
+
 def test_memory_of_empty_prefix_is_zero():
     w = WORKLOADS[3].with_(B=2, H=2, N=0, seed=62)
     inp = make_inputs(w)
