@@ -1,7 +1,8 @@
 // Backward of the GMA forward mixer (bidirectional and causal): SIMT kernels, with
-// matrix-core forms of the row passes, the segment partials, dx and the parameter sums for
-// bf16 inputs (fp32 matrix cores, or bf16 matrix cores on exact hi/lo splits of the fp32
-// operands).
+// matrix-core forms for bf16 inputs: the causal chunk walks on fp32 matrix cores; the
+// bidirectional row passes, the segment partials and the parameter sums on bf16 matrix cores
+// over exact three-piece bf16 splits of their fp32 operands; dqr, dkr on bf16 matrix cores
+// over exact hi/lo pairs.
 //
 // Method: Gaussian Mixture Attention (arXiv 2606.18283).  The mixture parameters are trained
 // end to end by backpropagation ("Core mechanism" item 3); the pages analyse the gradients'

@@ -258,8 +258,9 @@ int gma_decode_step_prepared(const void* qr, const void* kr, const void* v, cons
  * forward: see the kernels' source for the formulas.  For bf16 inputs the responsibilities
  * come from the matrix-core responsibilities kernel where it covers the shape (else the SIMT
  * one), and the passes over the rows, the segment partials, dqr/dkr and the parameter sums
- * run on the matrix cores (fp32 products, or bf16 products of exact hi/lo splits of the fp32
- * operands; shapes outside the tiles keep SIMT kernels); float32 inputs run SIMT kernels
+ * run on the matrix cores (fp32 products in the causal chunk walks, elsewhere bf16 products
+ * of exact two- or three-piece bf16 splits of the fp32 operands; shapes outside the tiles
+ * keep SIMT kernels); float32 inputs run SIMT kernels
  * throughout.  algo SIMT only makes bf16 inputs take their responsibilities from the SIMT
  * kernel (double logits); the other kernels are those of AUTO.  An explicit MFMA request
  * returns GMA_ERR_UNSUPPORTED.  Sums accumulate in
