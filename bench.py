@@ -144,7 +144,7 @@ def run_workload(w, steps, warmup, per_rep=True):
     need = gma.workspace_size_cross(desc, w.Nk) if cross else gma.workspace_size(desc, w.causal)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    max_k = 8
+    max_k = 24
     hip, evs = hip_events(2 * max_k * steps)
     names = (ctypes.c_char_p * max_k)()
 
@@ -182,7 +182,9 @@ def run_workload(w, steps, warmup, per_rep=True):
     for j in range(min(nk, max_k)):
         name = names[j].decode()
         ts = [elapsed_ms(hip, evs[2 * max_k * i + 2 * j], evs[2 * max_k * i + 2 * j + 1]) for i in range(steps)]
-        per_kernel[name] = sum(ts) / len(ts)
+        # a kernel launched several times per forward (one launch per slab of heads) counts once
+        # per step with the sum of its launches
+        per_kernel[name] = per_kernel.get(name, 0.0) + sum(ts) / len(ts)
     for e in evs:
         hip.hipEventDestroy(e)
     cold = rep_timing(step, torch, dev) if per_rep else None
