@@ -352,10 +352,14 @@ __global__ void __launch_bounds__(kFThreads, 2)
     // the eight waves' statistics combined (M = max, s = sum of ps_u 2^(pm_u - M)); this wave's
     // exponentials scaled by 2^(pm_w - M) / s: its normalised responsibilities, bf16, into LDS
     auto assemble = [&](const f32x16& t, int side, bool valid) {
-        const float4* xp = reinterpret_cast<const float4*>(xch + (size_t)(side * kGrp + col) * kFWaves * 2);
-        float pmv[kFWaves], psv[kFWaves];
+        // lanes l and l + 32 hold the same position: each half takes four waves' pairs, then
+        // the halves exchange (maximum, then the two partial sums)
+        constexpr int WH = kFWaves / 2;
+        const float4* xp = reinterpret_cast<const float4*>(xch + (size_t)(side * kGrp + col) * kFWaves * 2) +
+                           (WH / 2) * half;
+        float pmv[WH], psv[WH];
 #pragma unroll
-        for (int u = 0; u < kFWaves / 2; ++u) {
+        for (int u = 0; u < WH / 2; ++u) {
             const float4 a4 = xp[u];
             pmv[2 * u] = a4.x;
             psv[2 * u] = a4.y;
@@ -364,10 +368,12 @@ __global__ void __launch_bounds__(kFThreads, 2)
         }
         float M = pmv[0];
 #pragma unroll
-        for (int u = 1; u < kFWaves; ++u) M = fmaxf(M, pmv[u]);
+        for (int u = 1; u < WH; ++u) M = fmaxf(M, pmv[u]);
+        M = max_halves(M);
         float ssum = 0.0f;
 #pragma unroll
-        for (int u = 0; u < kFWaves; ++u) ssum += psv[u] * fast_exp2(pmv[u] - M);
+        for (int u = 0; u < WH; ++u) ssum += psv[u] * fast_exp2(pmv[u] - M);
+        ssum = sum_halves(ssum);
         // this wave's own maximum (a uniform LDS offset, not a dynamic register index)
         const float pmw = xch[((size_t)(side * kGrp + col) * kFWaves + w) * 2];
         // positions past the segment (keys) must not enter the state: zero responsibility

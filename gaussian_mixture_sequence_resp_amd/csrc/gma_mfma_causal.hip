@@ -512,16 +512,21 @@ __global__ void __launch_bounds__(64 * kRespWaves, 1)
 #pragma unroll
         for (int j = 0; j < kCpTiles; ++j) {
             const int t0 = b0 + kTileT * j;
-            float2 st[kRespWaves];
+            // lanes l and l + 32 hold the same position: each half takes four waves' terms,
+            // then the halves exchange (maximum, then the two partial sums in half order)
+            constexpr int WH = kRespWaves / 2;
+            float2 st[WH];
             float M = -INFINITY;
 #pragma unroll
-            for (int ww = 0; ww < kRespWaves; ++ww) {
-                st[ww] = sM[(b * kRespWaves + ww) * kStep + kTileT * j + col];
-                M = fmaxf(M, st[ww].x);
+            for (int u = 0; u < WH; ++u) {
+                st[u] = sM[(b * kRespWaves + WH * half + u) * kStep + kTileT * j + col];
+                M = fmaxf(M, st[u].x);
             }
+            M = max_halves(M);
             float S = 0.0f;
 #pragma unroll
-            for (int ww = 0; ww < kRespWaves; ++ww) S += st[ww].y * fast_exp2(st[ww].x - M);
+            for (int u = 0; u < WH; ++u) S += st[u].y * fast_exp2(st[u].x - M);
+            S = sum_halves(S);
             // S >= 1 (the wave holding the maximum contributes at least 2^0)
             const float inv = t0 + col < N ? fast_exp2(mloc[j] - M) * __builtin_amdgcn_rcpf(S) : 0.0f;
             if (t0 < n_end) {
